@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each check cites the passage of the Switch Transformers write-up it follows.
+Sources of truth: hand-worked fixtures (tests/golden/), closed forms the
+write-up states (the uniform-routing value of the loss), textbook routines
+that compute the same thing another way (stable sort ranks, scipy's softmax,
+explicit-loop matrix products), brute force over every routing of tiny
+batches, and invariants (conservation of tokens, monotonicity in the capacity
+factor).  The mutation tests at the end plant plausible mistakes in the oracle
+and check that some pin catches each one.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle.switch_oracle as so
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _hand_inputs():
+    g = _load("hand_layer_example.json")
+    inp = g["inputs"]
+    ln3 = math.log(3.0)
+    x = np.array(inp["x"], np.float64)
+    w_r = np.array(inp["w_router_over_ln3"], np.float64) * ln3
+    w_in = np.array(inp["w_in"], np.float64)
+    w_out = np.array(inp["w_out"], np.float64)
+    return g, x, w_r, w_in, w_out
+
+
+def _rand_layer(rng, T, d, f, N, scale=1.0):
+    x = rng.standard_normal((T, d))
+    w_r = rng.standard_normal((N, d)) * scale
+    w_in = rng.standard_normal((N, f, d)) * 0.3
+    w_out = rng.standard_normal((N, d, f)) * 0.3
+    return x, w_r, w_in, w_out
+
+
+# ---------------------------------------------------------------- pins -----
+def pin_capacity_table():
+    """Capacity equation ('Expert Capacity and the Capacity Factor'), by hand."""
+    for c in _load("capacity_table.json")["cases"]:
+        got = so.expert_capacity(c["tokens"], c["experts"], c["cf"])
+        assert got == c["capacity"], (c, got)
+
+
+def pin_hand_example():
+    """The whole hand-worked layer (tests/golden/hand_layer_example.json)."""
+    g, x, w_r, w_in, w_out = _hand_inputs()
+    exp = g["expected"]
+    C = so.expert_capacity(4, 2, g["inputs"]["capacity_factor"])
+    assert C == exp["capacity"]
+    out = so.forward(x, w_r, None, w_in, w_out, C)
+    np.testing.assert_allclose(out["probs"], exp["probs"], rtol=0, atol=1e-14)
+    assert out["expert_idx"].tolist() == exp["expert_idx"]
+    np.testing.assert_allclose(out["gate"], exp["gate"], rtol=0, atol=1e-14)
+    assert out["slot"].tolist() == exp["slot"]
+    assert out["dropped"].tolist() == exp["dropped"]
+    assert out["expert_count"].tolist() == exp["expert_count"]
+    assert abs(out["aux_loss"] - exp["aux_loss"]) < 1e-14
+    np.testing.assert_allclose(out["y_bare"], exp["y_bare"], rtol=0, atol=1e-14)
+    res = so.forward(x, w_r, None, w_in, w_out, C, add_residual=True)
+    np.testing.assert_allclose(res["y"], exp["y_residual"], rtol=0, atol=1e-14)
+    # the stage functions reproduce the same answer
+    buf, filled = so.dispatch(x, out["expert_idx"], out["slot"], out["dropped"], 2, C)
+    assert filled.tolist() == [[True, True], [True, False]]
+    eo = np.zeros_like(buf)
+    for i in range(2):
+        eo[i] = so.expert_ffn(buf[i], w_in[i], w_out[i])
+    y = so.combine(eo, out["expert_idx"], out["slot"], out["dropped"], out["gate"])
+    np.testing.assert_allclose(y, exp["y_bare"], rtol=0, atol=1e-14)
+
+
+def pin_softmax_library(rng):
+    """Softmax equation ('Switch Routing'): scipy's softmax, sum 1, gate bounds."""
+    h = rng.standard_normal((64, 9)) * 3
+    p = so.softmax(h)
+    np.testing.assert_allclose(p, scipy.special.softmax(h, axis=1), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    e, _ = so.top1(h)
+    gate = p[np.arange(64), e]
+    assert np.all(gate >= 1.0 / 9 - 1e-15) and np.all(gate <= 1.0)
+    # gate = 1 / sum_j e^{h_j - max h}, computed by an explicit loop
+    for t in range(64):
+        s = 0.0
+        for j in range(9):
+            s += math.exp(h[t, j] - max(h[t]))
+        assert abs(gate[t] - 1.0 / s) < 1e-14
+
+
+def pin_top1_bruteforce(rng):
+    """Top-1 selection ('Switch Routing: From Top-k to k = 1'), brute force."""
+    h = np.round(rng.standard_normal((200, 5)), 1)  # coarse values => many ties
+    e, gap = so.top1(h)
+    for t in range(200):
+        best = 0
+        for j in range(1, 5):
+            if h[t, j] > h[t, best]:
+                best = j
+        assert e[t] == best
+        srt = sorted(h[t])
+        assert abs(gap[t] - (srt[-1] - srt[-2])) < 1e-15
+    # equal router rows: every token is an exact tie -> expert 0
+    x = rng.standard_normal((10, 4))
+    w = np.tile(rng.standard_normal((1, 4)), (3, 1))
+    e, gap = so.top1(so.router_logits(x, w))
+    assert e.tolist() == [0] * 10 and np.all(gap == 0)
+
+
+def pin_router_logits_loops(rng):
+    """h(x) = W_r . x (+ b), against explicit loops with d != N."""
+    x = rng.standard_normal((5, 7))
+    w = rng.standard_normal((3, 7))
+    b = rng.standard_normal(3)
+    h = so.router_logits(x, w, b)
+    for t in range(5):
+        for i in range(3):
+            s = b[i]
+            for k in range(7):
+                s += w[i, k] * x[t, k]
+            assert abs(h[t, i] - s) < 1e-12
+
+
+def pin_slots_stable_sort(rng):
+    """Token-order slots equal ranks from a stable sort (textbook routine)."""
+    for N in (1, 2, 7, 128):
+        e = rng.integers(0, N, size=3000)
+        slot, dropped, count = so.assign_slots(e, N, 20)
+        order = np.argsort(e, kind="stable")
+        starts = np.concatenate([[0], np.cumsum(np.bincount(e, minlength=N))[:-1]])
+        rank = np.empty(len(e), np.int64)
+        rank[order] = np.arange(len(e)) - starts[e[order]]
+        assert np.array_equal(slot, rank)
+        assert np.array_equal(count, np.bincount(e, minlength=N))
+        assert np.array_equal(dropped, rank >= 20)
+
+
+def pin_slots_bruteforce():
+    """Every routing of T <= 6 tokens over N <= 3 experts: slots are a
+    bijection onto 0..count-1 per expert that preserves token order, and
+    conservation sum_i min(count_i, C) + #dropped = T holds."""
+    for N in (1, 2, 3):
+        for T in range(0, 7):
+            for e in itertools.product(range(N), repeat=T):
+                e = np.array(e, np.int64)
+                for C in (0, 1, 2, T):
+                    slot, dropped, count = so.assign_slots(e, N, C)
+                    for i in range(N):
+                        toks = [t for t in range(T) if e[t] == i]
+                        assert [slot[t] for t in toks] == list(range(len(toks)))
+                        assert count[i] == len(toks)
+                    assert sum(min(c, C) for c in count) + int(dropped.sum()) == T
+
+
+def pin_aux_uniform_closed_form():
+    """'The Load-Balancing Loss': under uniform routing sum_i f_i P_i = 1/N, so
+    N * sum f_i P_i = 1.  (a) f uniform: one-hot tokens x_t = e_{t mod N}
+    with W_r = [I 0]; (b) P uniform: W_r = 0 (all logits equal)."""
+    for N in (1, 2, 5, 16):
+        T, d = 3 * N, N + 3
+        x = np.zeros((T, d))
+        x[np.arange(T), np.arange(T) % N] = 1.0
+        w = np.zeros((N, d))
+        w[:, :N] = np.eye(N)
+        out = so.forward(x, w, None, np.zeros((N, 2, d)), np.zeros((N, d, 2)), 3)
+        assert abs(out["aux_loss"] - 1.0) < 1e-13
+        rng = np.random.default_rng(N)
+        x = rng.standard_normal((T, d))
+        out = so.forward(x, np.zeros((N, d)), None, np.zeros((N, 2, d)), np.zeros((N, d, 2)), 3)
+        assert abs(out["aux_loss"] - 1.0) < 1e-13
+        assert np.all(out["expert_idx"] == 0)  # all-tie routing -> expert 0
+
+
+def pin_ffn_loops(rng):
+    """E(x) = W_out . ReLU(W_in . x), against explicit loops; square dims so a
+    transposed operand would not fail on shape alone."""
+    for d, f in ((3, 3), (4, 6)):
+        x = rng.standard_normal((4, d))
+        wi = rng.standard_normal((f, d))
+        wo = rng.standard_normal((d, f))
+        y = so.expert_ffn(x, wi, wo)
+        for m in range(4):
+            hid = [max(0.0, sum(wi[j, k] * x[m, k] for k in range(d))) for j in range(f)]
+            for n in range(d):
+                assert abs(y[m, n] - sum(wo[n, j] * hid[j] for j in range(f))) < 1e-12
+
+
+def pin_single_expert_dense(rng):
+    """N = 1: softmax of one logit is 1 and cf >= 1 drops nothing, so the layer
+    is the dense ReLU FFN (explicit loops) on every token."""
+    T, d, f = 6, 3, 5
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, 1)
+    out = so.forward(x, w_r, None, w_in, w_out, so.expert_capacity(T, 1, 1.0))
+    assert np.all(out["gate"] == 1.0) and not out["dropped"].any()
+    for t in range(T):
+        hid = [max(0.0, sum(w_in[0, j, k] * x[t, k] for k in range(d))) for j in range(f)]
+        for n in range(d):
+            assert abs(out["y_bare"][t, n] - sum(w_out[0, n, j] * hid[j] for j in range(f))) < 1e-12
+
+
+def pin_layer_properties(rng):
+    """Invariants of the layer: capacity >= T drops nothing; kept sets grow with
+    cf; dropped rows are exactly 0 (bare) or exactly x (residual); doubling
+    W_out doubles y; y / gate = E_e(x); with no drops, permuting tokens
+    permutes every per-token output."""
+    T, d, f, N = 40, 6, 10, 4
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, N, scale=2.0)
+    b = np.array([1.5, 0.0, -0.5, 0.2])  # skew popularity to force drops
+    prev_kept = None
+    for cf in (0.25, 0.5, 1.0, 2.0, float(N)):
+        C = so.expert_capacity(T, N, cf)
+        out = so.forward(x, w_r, b, w_in, w_out, C)
+        kept = ~out["dropped"]
+        if prev_kept is not None:
+            assert np.all(kept[prev_kept])
+        prev_kept = kept
+        assert np.sum(np.minimum(out["expert_count"], C)) + out["dropped"].sum() == T
+        assert np.all(out["y_bare"][out["dropped"]] == 0.0)
+        res = so.forward(x, w_r, b, w_in, w_out, C, add_residual=True)
+        assert np.array_equal(res["y"][out["dropped"]], x[out["dropped"]])
+        dbl = so.forward(x, w_r, b, w_in, 2 * w_out, C)
+        assert np.array_equal(dbl["y_bare"], 2 * out["y_bare"])
+        for t in np.nonzero(kept)[0][:5]:
+            e = out["expert_idx"][t]
+            ref = so.expert_ffn(x[t:t + 1], w_in[e], w_out[e])[0]
+            np.testing.assert_allclose(out["y_bare"][t] / out["gate"][t], ref, rtol=1e-12, atol=1e-12)
+    assert prev_kept is not None and prev_kept.all()  # cf = N keeps all
+    perm = rng.permutation(T)
+    a = so.forward(x, w_r, b, w_in, w_out, T)
+    p = so.forward(x[perm], w_r, b, w_in, w_out, T)
+    for k in ("expert_idx", "gate", "y_bare"):
+        np.testing.assert_array_equal(p[k], a[k][perm])
+
+
+def pin_aux_counts_before_capacity():
+    """f_i follows the f equation (argmax indicator, before capacity): the
+    hand example's dropped token still counts (17/16, not 25/32)."""
+    g, x, w_r, w_in, w_out = _hand_inputs()
+    out = so.forward(x, w_r, None, w_in, w_out, 1)  # capacity 1 drops more
+    assert abs(out["aux_loss"] - 17 / 16) < 1e-14
+
+
+def pin_fed_mode():
+    """Fed routing: the oracle follows the given expert_idx for gates, slots,
+    drops, the loss and y."""
+    g, x, w_r, w_in, w_out = _hand_inputs()
+    out = so.forward(x, w_r, None, w_in, w_out, 2, expert_idx=np.array([1, 1, 1, 0]))
+    assert out["slot"].tolist() == [0, 1, 2, 0] and out["dropped"].tolist() == [False, False, True, False]
+    np.testing.assert_allclose(out["gate"], [0.25, 0.75, 0.25, 0.5], atol=1e-14)
+    # f = [1/4, 3/4], P = [9/16, 7/16] -> 2 * (9/64 + 21/64) = 15/16
+    assert abs(out["aux_loss"] - 15 / 16) < 1e-14
+    # token 3 -> expert 0 with input [1,1]: W_in0.[1,1] = [3,0,-3] -> ReLU [3,0,0] -> [3,9]; x 1/2
+    np.testing.assert_allclose(out["y_bare"][3], [1.5, 4.5], atol=1e-14)
+
+
+ALL_PINS = [
+    pin_capacity_table, pin_hand_example, pin_softmax_library, pin_top1_bruteforce,
+    pin_router_logits_loops, pin_slots_stable_sort, pin_slots_bruteforce,
+    pin_aux_uniform_closed_form, pin_ffn_loops, pin_single_expert_dense,
+    pin_layer_properties, pin_aux_counts_before_capacity, pin_fed_mode,
+]
+
+
+def _run(pin):
+    import inspect
+    if "rng" in inspect.signature(pin).parameters:
+        pin(np.random.default_rng(1234))
+    else:
+        pin()
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    _run(pin)
+
+
+# ------------------------------------------------------------ mutations -----
+def _mut_top1_last_tie(h):
+    e = (h.shape[1] - 1 - np.argmax(h[:, ::-1], axis=1)).astype(np.int64)
+    srt = np.sort(h, axis=1)
+    gap = srt[:, -1] - srt[:, -2] if h.shape[1] > 1 else np.full(h.shape[0], np.inf)
+    return e, gap
+
+
+def _mut_slots_reversed(expert_idx, num_experts, capacity):
+    T = len(expert_idx)
+    seen = [0] * num_experts
+    slot = np.empty(T, np.int64)
+    for t in reversed(range(T)):
+        i = int(expert_idx[t])
+        slot[t] = seen[i]
+        seen[i] += 1
+    return slot, slot >= capacity, np.asarray(seen, np.int64)
+
+
+def _mut_slots_off_by_one(expert_idx, num_experts, capacity):
+    slot, _, count = _ORIG["assign_slots"](expert_idx, num_experts, capacity)
+    return slot, slot > capacity, count
+
+
+def _mut_aux_after_capacity(expert_idx, probs, num_experts):
+    T = len(expert_idx)
+    if T == 0:
+        return 0.0
+    C = so.expert_capacity(T, num_experts, 1.0)
+    slot, dropped, _ = _ORIG["assign_slots"](expert_idx, num_experts, C)
+    f = np.array([np.count_nonzero((expert_idx == i) & ~dropped) / T for i in range(num_experts)])
+    return float(num_experts * np.sum(f * probs.sum(axis=0) / T))
+
+
+def _mut_aux_no_n(expert_idx, probs, num_experts):
+    return _ORIG["load_balancing_loss"](expert_idx, probs, num_experts) / num_experts
+
+
+def _mut_ffn_no_relu(x_e, w_in_e, w_out_e):
+    return (np.asarray(x_e) @ np.asarray(w_in_e).T) @ np.asarray(w_out_e).T
+
+
+def _mut_ffn_transposed(x_e, w_in_e, w_out_e):
+    hid = np.maximum(np.asarray(x_e) @ np.asarray(w_in_e).T, 0.0)
+    wo = np.asarray(w_out_e)
+    return hid @ (wo if wo.shape[0] == wo.shape[1] else wo.T)
+
+
+def _mut_softmax_wrong_axis(h):
+    m = h.max(axis=1, keepdims=True)
+    e = np.exp(h - m)
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def _mut_logits_no_bias(x, w_router, bias=None):
+    return np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+
+
+_ORIG = {k: getattr(so, k) for k in ("assign_slots", "load_balancing_loss", "top1", "expert_ffn",
+                                     "softmax", "router_logits")}
+
+MUTANTS = {
+    "top1_last_index_on_tie": ("top1", _mut_top1_last_tie),
+    "slots_later_token_wins": ("assign_slots", _mut_slots_reversed),
+    "drop_off_by_one": ("assign_slots", _mut_slots_off_by_one),
+    "f_after_capacity": ("load_balancing_loss", _mut_aux_after_capacity),
+    "loss_missing_N": ("load_balancing_loss", _mut_aux_no_n),
+    "ffn_without_relu": ("expert_ffn", _mut_ffn_no_relu),
+    "ffn_transposed_w_out": ("expert_ffn", _mut_ffn_transposed),
+    "softmax_wrong_axis": ("softmax", _mut_softmax_wrong_axis),
+    "router_bias_dropped": ("router_logits", _mut_logits_no_bias),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(so, attr, fn)
+    failures = 0
+    for pin in ALL_PINS:
+        try:
+            _run(pin)
+        except Exception:  # noqa: BLE001 - any failure of a pin counts
+            failures += 1
+    assert failures > 0, f"no pin catches the planted mistake {name}"
