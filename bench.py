@@ -1,0 +1,230 @@
+"""Benchmark of the Switch FFN layer forward on one MI355X.
+
+One step = one switch_layer_forward call (router, capacity assignment, aux
+loss, dispatch, expert FFN, combine) over the base workload: 16384 tokens
+(32 sequences x 512), d_model 768, d_ff 3072, 128 experts, capacity factor
+1.25, bf16 activations and expert weights, fp32 router, seeded synthetic
+inputs already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Switch-layer fwd tokens/sec on 1 MI355X; expert-FFN % MFMA peak; route/dispatch % HBM"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+PROFILES = os.path.join(ROOT, "profiles")
+FFN_SRC = os.path.join(ROOT, "sparse_mixture_experts_switch_amd", "csrc", "ffn.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(name: str, T: int, d: int, f: int, N: int, C: int, counts) -> float:
+    """Bytes each kernel must move at minimum (every input byte read once,
+    every output byte written once; no padding rows)."""
+    kept = int(sum(min(int(c), C) for c in counts))
+    active = int(sum(1 for c in counts if c > 0 and C > 0))
+    nb = (T + 31) // 32
+    if name == "router":
+        return T * d * 2 + N * d * 4 + T * 12 + nb * N * 8
+    if name == "assign_scan":
+        return nb * N * 12 + N * 8
+    if name == "assign_apply":
+        # slot/dropped/token map, plus the zero rows of dropped tokens
+        return T * 13 + T * 4 + N * 8 + (T - kept) * d * 2
+    if name == "dispatch":
+        return 2 * kept * d * 2 + T * 9
+    if name == "ffn_up":    # W_in of live experts, gathered x rows, H written
+        return active * f * d * 2 + kept * d * 2 + kept * f * 2 + kept * 4
+    if name == "ffn_down":  # W_out of live experts, H read, y rows written
+        return active * d * f * 2 + kept * f * 2 + kept * d * 2 + kept * 8
+    if name == "combine":
+        return kept * d * 2 + T * d * 2 + T * 13
+    return float("nan")
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"{kernel}_base_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"^(\w+)\s*=\s*(\S+)", line.strip())
+            if m:
+                vals[m.group(1)] = m.group(2)
+    if vals.get("source_sha256") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, C: int, sample_experts: int = 16) -> dict:
+    """The CPU oracle (numpy fp64) on a bounded sample of the same workload:
+    routing, assignment and loss for all tokens, the expert FFN for a seeded
+    sample of experts, extrapolated to every expert."""
+    import numpy as np
+    import torch
+
+    import oracle.switch_oracle as so
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    x, wr = f64(inp["x"]), f64(inp["w_router"])
+    N = wr.shape[0]
+    rng = np.random.default_rng(3)
+    sample = sorted(rng.choice(N, sample_experts, replace=False).tolist())
+    w = {i: (f64(inp["w_in"][i]), f64(inp["w_out"][i])) for i in sample}
+    t0 = time.perf_counter()
+    so.forward(x, wr, None, lambda i: w[i], None, C, experts=[])
+    t_route = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    so.forward(x, wr, None, lambda i: w[i], None, C, experts=sample)
+    t_both = time.perf_counter() - t0
+    t_ffn = max(t_both - t_route, 0.0) * N / len(sample)
+    total = t_route + t_ffn
+    T = x.shape[0]
+    return {"value": T / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"numpy fp64 oracle: routing, slots and loss for all {T} tokens ({t_route:.2f} s), "
+                       f"expert FFN for {len(sample)} of {N} experts ({t_both - t_route:.2f} s) "
+                       f"extrapolated to {N}; host cores available {len(os.sched_getaffinity(0))}")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", default="base", help="workload (the metric is quoted on 'base')")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sparse_mixture_experts_switch_amd as smx
+    from sparse_mixture_experts_switch_amd.inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: generating {cfg}")
+    inp = make_inputs(cfg, device=dev)
+    T, d, f, N = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts
+    C = smx.capacity(T, N, cfg.capacity_factor)
+    shape = smx.binding.make_shape(T, d, f, N, C, cfg.torch_dtype)
+    ws = torch.empty(smx.workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = smx.binding._route_outputs(T, N, dev)
+    out["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
+    call = lambda: smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],  # noqa: E731
+                                     inp["w_out"], C, workspace=ws, out=out)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"bench: warmup {args.warmup} done; timing {args.steps} steps")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+    counts = out["expert_count"].cpu().tolist()
+    drop_rate = float(out["dropped"].float().mean().item())
+
+    # per-kernel durations: HIP events recorded by the library on the stream
+    # it launches on, averaged over the same number of steps
+    sums: dict[str, float] = {}
+    for _ in range(args.steps):
+        _, per = smx.layer_forward_profiled(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],
+                                            inp["w_out"], C, workspace=ws, out=out)
+        for name, v in per:
+            sums[name] = sums.get(name, 0.0) + v
+    kern = {k: v / args.steps for k, v in sums.items()}
+    log("bench: per-kernel ms " + ", ".join(f"{k}={v:.4f}" for k, v in kern.items()))
+    per_kernel = {}
+    for k, v in kern.items():
+        b = algorithmic_bytes(k, T, d, f, N, C, counts)
+        per_kernel[k] = {"ms": round(v, 5), "alg_bytes": b, "GBps": round(b / (v * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(b / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    dom = max(("ffn_up", "ffn_down"), key=lambda k: kern.get(k, 0.0))
+    dom_b = algorithmic_bytes(dom, T, d, f, N, C, counts)
+    achieved = dom_b / (kern[dom] * 1e-3) / 1e9
+    kept = sum(min(c, C) for c in counts)
+    ffn_ms = kern["ffn_up"] + kern["ffn_down"]
+    ffn_tflops = 4.0 * kept * d * f / (ffn_ms * 1e-3) / 1e12
+    rdc = ("router", "assign_scan", "assign_apply")
+    rdc_b = sum(algorithmic_bytes(k, T, d, f, N, C, counts) for k in rdc)
+    rdc_ms = sum(kern[k] for k in rdc)
+    res = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, truncated-normal 0.1-scale weights; no dataset)",
+        "config": {"workload": f"{cfg.name}: {T} tokens (32 seqs x 512), d_model {d}, d_ff {f}, {N} experts, "
+                               f"capacity factor {cfg.capacity_factor} (capacity {C}), bf16 activations and "
+                               f"expert weights, fp32 router",
+                   "tokens": T, "d_model": d, "d_ff": f, "num_experts": N, "capacity": C,
+                   "drop_rate": round(drop_rate, 5)},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(dom, source_digest(FFN_SRC))},
+        "ffn": {"ms": round(ffn_ms, 4), "tflops": round(ffn_tflops, 1),
+                "mfma_frac": round(ffn_tflops / BF16_PEAK_TFLOPS, 4)},
+        "route": {"ms": round(rdc_ms, 4), "alg_bytes": rdc_b,
+                                   "hbm_frac": round(rdc_b / (rdc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "kernels": per_kernel,
+        "wall_s_timed": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(inp, C)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

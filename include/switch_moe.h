@@ -1,0 +1,171 @@
+/*
+ * switch_moe.h -- C ABI of the Switch FFN layer forward pass on one AMD
+ * MI355X GPU (gfx950), library libswitchmoe.so.
+ *
+ * The operation is the Switch layer of the Switch Transformer, as defined in
+ * the engineering write-up "Switch Transformers: Scaling to Trillion Parameter
+ * Models" (sections "Switch Routing: From Top-k to k = 1", "Expert Capacity
+ * and the Capacity Factor", "The Load-Balancing Loss", "The Architecture in
+ * Place", "Making Sparse Training Stable"):
+ *
+ *   h(x) = W_r x (+ b)                     router logits, fp32
+ *   p_i(x) = exp(h_i) / sum_j exp(h_j)     softmax gate, fp32
+ *   e(x) = argmax_i p_i(x)                 top-1 ("Switch") routing, k = 1
+ *   capacity = T / N * capacity_factor     per-expert buffer, overflow dropped
+ *   E_i(x) = W_out,i ReLU(W_in,i x)        N independent expert FFNs
+ *   y(x) = p_e(x) E_e(x)                   gate-scaled combine (0 if dropped)
+ *   aux = N sum_i f_i P_i                  load-balancing loss (no alpha)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Array arguments are DEVICE pointers owned by the caller; the library
+ *   allocates and frees nothing, keeps no state between calls and never
+ *   blocks the host (except switch_layer_forward_profiled).  All work is
+ *   enqueued on `stream` (a hipStream_t passed as void*; NULL = null stream).
+ * - Layouts are dense row-major.  T tokens are the caller's [batch][seq]
+ *   flattened in row-major order; that order is the "token order" that
+ *   decides which tokens overflow an expert.
+ * - Activation dtype (s->dtype) applies to x, W_in, W_out, dispatched,
+ *   expert_out and y: SWITCH_F32 (float) or SWITCH_BF16 (bfloat16, stored as
+ *   16-bit words).  The router (W_r, bias, logits, softmax, gate) is always
+ *   fp32, whatever the activation dtype.
+ * - Every call validates all of its arguments on the host before it enqueues
+ *   anything: a call that returns an error has enqueued nothing and left
+ *   every output untouched.  Device faults are asynchronous and surface at
+ *   the caller's next synchronisation of the stream.
+ * - Outputs must not alias inputs or each other.  Calls on different streams
+ *   with different buffers are independent; the library is reentrant.
+ * - Alignment: x, W_in, W_out, dispatched, expert_out, y, x_residual, W_r
+ *   must be 16-byte aligned; workspace 256-byte aligned; other arrays 4-byte
+ *   aligned (dropped: any).
+ * - Supported shapes: d_model and d_ff multiples of 64; 0 <= tokens <= 2^31-1;
+ *   num_experts >= 1; capacity >= 0.  Shapes outside that give
+ *   SWITCH_E_UNSUPPORTED.
+ */
+#ifndef SWITCH_MOE_H
+#define SWITCH_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWITCH_OK 0
+#define SWITCH_E_INVALID (-1)     /* NULL / misaligned pointer, negative or zero dimension, bad dtype */
+#define SWITCH_E_UNSUPPORTED (-2) /* shape outside the kernels' contract (see above) */
+#define SWITCH_E_WORKSPACE (-3)   /* workspace smaller than switch_workspace_bytes() */
+#define SWITCH_E_HIP (-4)         /* a HIP runtime / launch call failed; see switch_last_error() */
+
+enum { SWITCH_F32 = 0, SWITCH_BF16 = 1 };
+
+typedef struct switch_shape {
+  int64_t tokens;      /* T: tokens per batch (capacity equation)                      */
+  int32_t d_model;     /* d: token width                                               */
+  int32_t d_ff;        /* expert hidden width                                          */
+  int32_t num_experts; /* N                                                            */
+  int32_t capacity;    /* C: per-expert buffer rows, normally from switch_capacity()   */
+  int32_t dtype;       /* SWITCH_F32 or SWITCH_BF16 (activations and expert weights)   */
+} switch_shape;
+
+/* Expert capacity, "Expert Capacity and the Capacity Factor" (capacity
+ * equation): tokens per batch / number of experts x capacity factor, rounded
+ * up, computed exactly on the binary64 value of capacity_factor.  Host only.
+ * Errors: SWITCH_E_INVALID (tokens < 0, num_experts < 1, factor not finite
+ * and > 0, NULL out), SWITCH_E_UNSUPPORTED (result above 2^31-1). */
+int switch_capacity(int64_t tokens, int32_t num_experts, double capacity_factor, int32_t *capacity_out);
+
+/* Bytes of device workspace that every entry point below accepts for this
+ * shape (the largest need, which is switch_layer_forward's).  Host only.
+ * Smaller needs: switch_route needs the value reported for the same shape
+ * with capacity 0; switch_expert_ffn needs num_experts * capacity * d_ff *
+ * sizeof(activation) rounded up to 256 bytes. */
+int switch_workspace_bytes(const switch_shape *s, size_t *bytes_out);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char *switch_last_error(void);
+
+/* Routing: router logits, fp32 softmax, top-1 choice, gate, capacity
+ * assignment and the load-balancing loss ("Switch Routing", "Expert
+ * Capacity", "The Load-Balancing Loss").
+ *   x            [T][d]    activation dtype
+ *   w_router     [N][d]    fp32
+ *   router_bias  [N] fp32 or NULL (added to the logits)
+ * Outputs:
+ *   expert_idx   [T] int32  argmax of the logits; ties go to the lowest index
+ *   gate         [T] fp32   p_e(x) = 1 / sum_j exp(h_j - max_j h_j)
+ *   slot         [T] int32  number of earlier tokens routed to the same
+ *                           expert (also for dropped tokens)
+ *   dropped      [T] uint8  1 if slot >= capacity (overflow), else 0
+ *   expert_count [N] int32  tokens routed to each expert before capacity
+ *   aux_loss     [1] fp32   N * sum_i f_i P_i; f_i = expert_count_i / T,
+ *                           P_i = mean over all T tokens of p_i; 0 when T = 0
+ * Results are deterministic: integer slots, fixed-order float reductions. */
+int switch_route(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                 int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count,
+                 float *aux_loss, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Dispatch: copy every kept token's row into its expert's buffer,
+ * dispatched[expert_idx[t]][slot[t]][:] = x[t][:] ("Expert Capacity" figure:
+ * dispatch to the single top expert).  dispatched is [N][C][d]; rows at or
+ * past an expert's kept count are padding and left untouched. */
+int switch_dispatch(const switch_shape *s, const void *x, const int32_t *expert_idx, const int32_t *slot,
+                    const uint8_t *dropped, void *dispatched, void *stream);
+
+/* Expert FFNs ("The Core Idea": N independent FFNs; the expert form
+ * E(x) = W_out ReLU(W_in x) has no biases):
+ *   expert_out[i][r] = W_out,i ReLU(W_in,i dispatched[i][r])
+ * for r < min(expert_count[i], C).  w_in is [N][d_ff][d], w_out is
+ * [N][d][d_ff]; expert_out is [N][C][d].  In bf16 the hidden ReLU output is
+ * rounded to bf16; accumulation is fp32.  Padding rows are neither read nor
+ * written. */
+int switch_expert_ffn(const switch_shape *s, const void *dispatched, const int32_t *expert_count,
+                      const void *w_in, const void *w_out, void *expert_out, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Combine ("Switch Routing" combine equation with k = 1; "Expert Capacity":
+ * dropped tokens skip the expert):
+ *   y[t] = gate[t] * expert_out[expert_idx[t]][slot[t]]   (kept t)
+ *   y[t] = 0                                              (dropped t)
+ * plus x_residual[t] for every t when x_residual is not NULL.  fp32
+ * arithmetic, one rounding to the activation dtype. */
+int switch_combine(const switch_shape *s, const void *expert_out, const int32_t *expert_idx,
+                   const int32_t *slot, const uint8_t *dropped, const float *gate, const void *x_residual,
+                   void *y, void *stream);
+
+/* The whole layer in one stream-ordered call: the results of switch_route,
+ * switch_dispatch, switch_expert_ffn and switch_combine, fused.  The expert
+ * FFN reads each kept token's row of x directly (no dispatch copy) and
+ * writes y[t] = gate[t] * E_e(x_t) (+ x_t) straight from its fp32
+ * accumulators, so every output element is rounded once.  The workspace
+ * holds the router's partial results, the hidden activations and the
+ * slot -> token map.  add_residual != 0 returns y = x + layer output
+ * (dropped tokens then pass x through unchanged); 0 returns the bare layer
+ * output (0 for dropped tokens).  Outputs as for switch_route plus y [T][d]. */
+int switch_layer_forward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                         const void *w_in, const void *w_out, int32_t add_residual, void *y,
+                         int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
+                         int32_t *expert_count, float *aux_loss, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Measurement variant of switch_layer_forward: same arguments and results,
+ * plus the duration of each kernel launch in milliseconds, timed with HIP
+ * events recorded on `stream` around every launch.  BLOCKS until the stream
+ * has finished the call.  kernel_ms receives up to max_kernels values and
+ * *num_kernels the number of launches; switch_kernel_name(i) names launch i. */
+int switch_layer_forward_profiled(const switch_shape *s, const void *x, const float *w_router,
+                                  const float *router_bias, const void *w_in, const void *w_out,
+                                  int32_t add_residual, void *y, int32_t *expert_idx, float *gate,
+                                  int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,
+                                  void *workspace, size_t workspace_bytes, void *stream, float *kernel_ms,
+                                  int32_t max_kernels, int32_t *num_kernels);
+
+/* Name of launch `index` of switch_layer_forward ("" past the last). */
+const char *switch_kernel_name(int32_t index);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWITCH_MOE_H */

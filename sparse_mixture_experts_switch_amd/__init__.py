@@ -1,0 +1,24 @@
+"""Switch FFN layer forward for one AMD MI355X (gfx950), hand-written HIP.
+
+The layer runs in libswitchmoe.so (C ABI in include/switch_moe.h); this
+package holds its ctypes binding (`binding`), the build script (`build`) and
+the seeded synthetic input generator (`inputs`).  Importing the package does
+not load the library; the first binding call does, and fails loudly if the
+library has not been built.
+"""
+
+from .binding import (  # noqa: F401
+    SWITCH_BF16,
+    SWITCH_F32,
+    SwitchError,
+    capacity,
+    combine,
+    dispatch,
+    expert_ffn,
+    kernel_names,
+    layer_forward,
+    layer_forward_profiled,
+    load_library,
+    route,
+    workspace_bytes,
+)

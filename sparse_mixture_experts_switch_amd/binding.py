@@ -1,0 +1,252 @@
+"""Python binding of libswitchmoe.so (ctypes).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory (outputs and workspace are torch
+tensors) and the stream (torch's current stream on the tensors' device).
+There is no fallback: if the library or a GPU is missing, calls raise.
+The C contract of each function is in include/switch_moe.h.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SwitchError", "load_library", "capacity", "workspace_bytes", "route", "dispatch",
+    "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "kernel_names",
+    "SWITCH_F32", "SWITCH_BF16",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswitchmoe.so")
+
+SWITCH_OK, SWITCH_E_INVALID, SWITCH_E_UNSUPPORTED, SWITCH_E_WORKSPACE, SWITCH_E_HIP = 0, -1, -2, -3, -4
+SWITCH_F32, SWITCH_BF16 = 0, 1
+_CODES = {-1: "SWITCH_E_INVALID", -2: "SWITCH_E_UNSUPPORTED", -3: "SWITCH_E_WORKSPACE", -4: "SWITCH_E_HIP"}
+
+EXPORTED = [
+    "switch_capacity", "switch_workspace_bytes", "switch_last_error", "switch_route", "switch_dispatch",
+    "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
+    "switch_kernel_name",
+]
+
+
+class SwitchError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32), ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m sparse_mixture_experts_switch_amd.build`")
+    lib = ctypes.CDLL(path)
+    sp = ctypes.POINTER(Shape)
+    i32p, sz = ctypes.POINTER(ctypes.c_int32), ctypes.c_size_t
+    lib.switch_capacity.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_double, i32p]
+    lib.switch_workspace_bytes.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.switch_last_error.restype = ctypes.c_char_p
+    lib.switch_route.argtypes = [sp] + [_P] * 10 + [sz, _P]
+    lib.switch_dispatch.argtypes = [sp] + [_P] * 6
+    lib.switch_expert_ffn.argtypes = [sp] + [_P] * 6 + [sz, _P]
+    lib.switch_combine.argtypes = [sp] + [_P] * 8
+    lib.switch_layer_forward.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P]
+    lib.switch_layer_forward_profiled.argtypes = (
+        [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P, _P, ctypes.c_int32, _P])
+    lib.switch_kernel_name.argtypes = [ctypes.c_int32]
+    lib.switch_kernel_name.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name not in ("switch_last_error", "switch_kernel_name"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != SWITCH_OK:
+        raise SwitchError(rc, load_library().switch_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return SWITCH_BF16
+    if dt == torch.float32:
+        return SWITCH_F32
+    raise ValueError(f"activation dtype {dt} is not supported (float32 or bfloat16)")
+
+
+def _stream(dev: torch.device) -> int:
+    if dev.type != "cuda":
+        raise ValueError("the Switch layer runs on a GPU: tensors must be on a cuda device")
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def make_shape(tokens: int, d_model: int, d_ff: int, num_experts: int, capacity_: int, dtype: torch.dtype) -> Shape:
+    return Shape(tokens, d_model, d_ff, num_experts, capacity_, _dtype_code(dtype))
+
+
+def capacity(tokens: int, num_experts: int, capacity_factor: float) -> int:
+    """ceil(tokens / num_experts * capacity_factor) (exact)."""
+    out = ctypes.c_int32()
+    _check(load_library().switch_capacity(tokens, num_experts, float(capacity_factor), ctypes.byref(out)))
+    return out.value
+
+
+def workspace_bytes(shape: Shape) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().switch_workspace_bytes(ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(shape: Shape, dev: torch.device, ws: torch.Tensor | None) -> torch.Tensor:
+    need = workspace_bytes(shape)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    return ws
+
+
+def _route_outputs(T: int, N: int, dev: torch.device) -> dict:
+    return {
+        "expert_idx": torch.empty(T, dtype=torch.int32, device=dev),
+        "gate": torch.empty(T, dtype=torch.float32, device=dev),
+        "slot": torch.empty(T, dtype=torch.int32, device=dev),
+        "dropped": torch.empty(T, dtype=torch.uint8, device=dev),
+        "expert_count": torch.empty(N, dtype=torch.int32, device=dev),
+        "aux_loss": torch.empty(1, dtype=torch.float32, device=dev),
+    }
+
+
+def _shape_of(x, w_in, num_experts, capacity_, d_ff=None) -> Shape:
+    T, d = x.shape
+    f = d_ff if d_ff is not None else w_in.shape[1]
+    return make_shape(T, d, f, num_experts, capacity_, x.dtype)
+
+
+def route(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None, capacity_: int,
+          workspace: torch.Tensor | None = None, out: dict | None = None) -> dict:
+    """Router, top-1, capacity assignment and aux loss (switch_route)."""
+    T, d = x.shape
+    N = w_router.shape[0]
+    shape = make_shape(T, d, 64, N, capacity_, x.dtype)
+    dev = x.device
+    o = out if out is not None else _route_outputs(T, N, dev)
+    # routing needs the workspace of the same shape without expert buffers
+    ws = _workspace(make_shape(T, d, 64, N, 0, x.dtype), dev, workspace)
+    _check(load_library().switch_route(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(o["expert_idx"]), _ptr(o["gate"]),
+        _ptr(o["slot"]), _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]), _ptr(ws),
+        ws.numel(), _stream(dev)))
+    return o
+
+
+def dispatch(x: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tensor, dropped: torch.Tensor,
+             num_experts: int, capacity_: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Gather kept token rows into [N][C][d] expert buffers (switch_dispatch)."""
+    T, d = x.shape
+    shape = make_shape(T, d, 64, num_experts, capacity_, x.dtype)
+    buf = out if out is not None else torch.empty(num_experts, capacity_, d, dtype=x.dtype, device=x.device)
+    _check(load_library().switch_dispatch(ctypes.byref(shape), _ptr(x), _ptr(expert_idx), _ptr(slot),
+                                          _ptr(dropped), _ptr(buf), _stream(x.device)))
+    return buf
+
+
+def expert_ffn(dispatched: torch.Tensor, expert_count: torch.Tensor, w_in: torch.Tensor, w_out: torch.Tensor,
+               workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """expert_out[i][r] = W_out,i ReLU(W_in,i dispatched[i][r]) (switch_expert_ffn)."""
+    N, C, d = dispatched.shape
+    shape = make_shape(0, d, w_in.shape[1], N, C, dispatched.dtype)
+    dev = dispatched.device
+    eo = out if out is not None else torch.empty_like(dispatched)
+    ws = workspace
+    if ws is None:  # expert_ffn alone needs only the [N][C][d_ff] hidden buffer
+        ws = torch.empty(max(N * C * w_in.shape[1] * dispatched.element_size(), 256), dtype=torch.uint8,
+                         device=dev)
+    _check(load_library().switch_expert_ffn(ctypes.byref(shape), _ptr(dispatched), _ptr(expert_count), _ptr(w_in),
+                                            _ptr(w_out), _ptr(eo), _ptr(ws), ws.numel(), _stream(dev)))
+    return eo
+
+
+def combine(expert_out: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tensor, dropped: torch.Tensor,
+            gate: torch.Tensor, x_residual: torch.Tensor | None = None,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[t] = gate[t] expert_out[e[t]][slot[t]] (0 if dropped) (+ x) (switch_combine)."""
+    N, C, d = expert_out.shape
+    T = expert_idx.shape[0]
+    shape = make_shape(T, d, 64, N, C, expert_out.dtype)
+    y = out if out is not None else torch.empty(T, d, dtype=expert_out.dtype, device=expert_out.device)
+    _check(load_library().switch_combine(ctypes.byref(shape), _ptr(expert_out), _ptr(expert_idx), _ptr(slot),
+                                         _ptr(dropped), _ptr(gate), _ptr(x_residual), _ptr(y),
+                                         _stream(expert_out.device)))
+    return y
+
+
+def _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out):
+    T, d = x.shape
+    N, f = w_in.shape[0], w_in.shape[1]
+    shape = make_shape(T, d, f, N, capacity_, x.dtype)
+    dev = x.device
+    o = out if out is not None else _route_outputs(T, N, dev)
+    if "y" not in o:
+        o["y"] = torch.empty(T, d, dtype=x.dtype, device=dev)
+    ws = _workspace(shape, dev, workspace)
+    args = [ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_in), _ptr(w_out),
+            1 if add_residual else 0, _ptr(o["y"]), _ptr(o["expert_idx"]), _ptr(o["gate"]), _ptr(o["slot"]),
+            _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]), _ptr(ws), ws.numel(), _stream(dev)]
+    return shape, o, args
+
+
+def layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None, w_in: torch.Tensor,
+                  w_out: torch.Tensor, capacity_: int, add_residual: bool = False,
+                  workspace: torch.Tensor | None = None, out: dict | None = None) -> dict:
+    """The whole Switch layer forward (switch_layer_forward)."""
+    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
+    _check(load_library().switch_layer_forward(*args))
+    return o
+
+
+def kernel_names() -> list[str]:
+    lib = load_library()
+    names, i = [], 0
+    while True:
+        n = lib.switch_kernel_name(i).decode()
+        if not n:
+            return names
+        names.append(n)
+        i += 1
+
+
+def layer_forward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, add_residual=False,
+                           workspace=None, out=None):
+    """layer_forward plus per-launch durations (ms) from HIP events; blocks."""
+    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
+    ms = (ctypes.c_float * 16)()
+    n = ctypes.c_int32()
+    _check(load_library().switch_layer_forward_profiled(*args, ms, 16, ctypes.byref(n)))
+    names = kernel_names()
+    return o, [(names[i] if i < len(names) else f"k{i}", float(ms[i])) for i in range(n.value)]

@@ -1,0 +1,433 @@
+// C ABI of the Switch layer forward: host-side validation, workspace carving
+// and the stream-ordered launch sequence.  The contract of every entry point
+// is documented in include/switch_moe.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "../../include/switch_moe.h"
+#include "launch.h"
+
+using namespace smx;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(SWITCH_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Products of non-negative sizes; false on overflow past 2^62.
+bool mul(size_t &out, std::initializer_list<int64_t> xs) {
+  unsigned __int128 p = 1;
+  for (int64_t x : xs) {
+    if (x < 0) return false;
+    p *= (unsigned __int128)x;
+    if (p > ((unsigned __int128)1 << 62)) return false;
+  }
+  out = (size_t)p;
+  return true;
+}
+
+int esize(int dtype) { return dtype == SWITCH_BF16 ? 2 : 4; }
+
+struct Layout {
+  size_t bcount = 0, ppart = 0, psum = 0, logits = 0, route_end = 0;
+  size_t ffn_hidden = 0, ffn_end = 0;                             // switch_expert_ffn alone
+  size_t lf_hidden = 0, lf_tok = 0, total = 0;                  // layer forward
+};
+
+int check_shape(const switch_shape *s) {
+  if (!s) return fail(SWITCH_E_INVALID, "shape is NULL");
+  if (s->tokens < 0) return fail(SWITCH_E_INVALID, "tokens = %lld < 0", (long long)s->tokens);
+  if (s->d_model < 1 || s->d_ff < 1 || s->num_experts < 1)
+    return fail(SWITCH_E_INVALID, "d_model = %d, d_ff = %d, num_experts = %d must be >= 1", s->d_model, s->d_ff,
+                s->num_experts);
+  if (s->capacity < 0) return fail(SWITCH_E_INVALID, "capacity = %d < 0", s->capacity);
+  if (s->dtype != SWITCH_F32 && s->dtype != SWITCH_BF16) return fail(SWITCH_E_INVALID, "dtype = %d", s->dtype);
+  if (s->tokens > INT32_MAX)
+    return fail(SWITCH_E_UNSUPPORTED, "tokens = %lld above 2^31-1", (long long)s->tokens);
+  if (s->d_model % 64 || s->d_ff % 64)
+    return fail(SWITCH_E_UNSUPPORTED, "d_model = %d and d_ff = %d must be multiples of 64", s->d_model, s->d_ff);
+  return SWITCH_OK;
+}
+
+int layout(const switch_shape *s, Layout &L) {
+  const int64_t T = s->tokens, N = s->num_experts, C = s->capacity, d = s->d_model, f = s->d_ff;
+  const int64_t nb = router_blocks(T);
+  const int es = esize(s->dtype);
+  size_t bc, pp, ps, lg = 0, hid, act, tk;
+  bool ok = mul(bc, {nb, N, 4}) && mul(pp, {nb, N, 4}) && mul(ps, {N, 4}) &&
+            (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(hid, {N, C, f, es}) && mul(act, {N, C, d, es}) &&
+            mul(tk, {N, C, 4});
+  if (!ok) return fail(SWITCH_E_UNSUPPORTED, "buffer sizes overflow for this shape");
+  size_t o = 0;
+  L.bcount = o;
+  o = align_up(o + bc);
+  L.ppart = o;
+  o = align_up(o + pp);
+  L.psum = o;
+  o = align_up(o + ps);
+  L.logits = o;
+  o = align_up(o + lg);
+  L.route_end = o;
+  L.ffn_hidden = 0;
+  L.ffn_end = align_up(hid);
+  L.lf_hidden = o;
+  o = align_up(o + hid);
+  L.lf_tok = o;
+  o = align_up(o + tk);
+  L.total = o;
+  return SWITCH_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define NEED(ptr, al)                                                                            \
+  do {                                                                                           \
+    if (!(ptr)) return fail(SWITCH_E_INVALID, "%s is NULL", #ptr);                               \
+    if (!aligned((ptr), (al))) return fail(SWITCH_E_INVALID, "%s is not %d-byte aligned", #ptr, (int)(al)); \
+  } while (0)
+
+#define GUARD(...)                                            \
+  try {                                                       \
+    __VA_ARGS__                                               \
+  } catch (const std::exception &ex) {                        \
+    return fail(SWITCH_E_HIP, "internal error: %s", ex.what()); \
+  } catch (...) {                                             \
+    return fail(SWITCH_E_HIP, "internal error");              \
+  }
+
+int check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SWITCH_OK;
+  if (!ws) return fail(SWITCH_E_INVALID, "workspace is NULL");
+  if (!aligned(ws, kWsAlign)) return fail(SWITCH_E_INVALID, "workspace is not 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(SWITCH_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  return SWITCH_OK;
+}
+
+// ---------------------------------------------------------------- launches --
+// A launch sequence runs plainly, or with HIP events around each launch.
+struct Timer {
+  bool on = false;
+  int n = 0;
+  hipEvent_t ev[16] = {};
+  hipStream_t st = nullptr;
+  hipError_t err = hipSuccess;
+  const char *names[16];
+  void mark(const char *name) {
+    if (!on || err != hipSuccess) return;
+    if (n >= 15) return;
+    names[n] = name;
+    err = hipEventRecord(ev[n + 1], st);
+    ++n;
+  }
+};
+
+const char *const kKernelNames[] = {"router", "assign_scan", "assign_apply", "ffn_up", "ffn_down"};
+constexpr int kNumKernels = 5;
+
+int route_args(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+               int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count,
+               float *aux_loss, void *ws, size_t ws_bytes, const Layout &L, RouteArgs &a) {
+  const bool any = s->tokens > 0;
+  if (any) {
+    NEED(x, 16);
+    NEED(expert_idx, 4);
+    NEED(gate, 4);
+    NEED(slot, 4);
+    if (!dropped) return fail(SWITCH_E_INVALID, "dropped is NULL");
+  }
+  NEED(w_router, 16);
+  if (router_bias && !aligned(router_bias, 4)) return fail(SWITCH_E_INVALID, "router_bias is not 4-byte aligned");
+  NEED(expert_count, 4);
+  NEED(aux_loss, 4);
+  int rc = check_ws(ws, ws_bytes, L.route_end);
+  if (rc) return rc;
+  char *w = (char *)ws;
+  a.dtype = s->dtype;
+  a.T = s->tokens;
+  a.d = s->d_model;
+  a.N = s->num_experts;
+  a.C = s->capacity;
+  a.x = x;
+  a.w_r = w_router;
+  a.bias = router_bias;
+  a.logits = (float *)(w + L.logits);
+  a.expert_idx = expert_idx;
+  a.gate = gate;
+  a.slot = slot;
+  a.dropped = dropped;
+  a.expert_count = expert_count;
+  a.aux_loss = aux_loss;
+  a.bcount = (int32_t *)(w + L.bcount);
+  a.ppart = (float *)(w + L.ppart);
+  a.psum = (float *)(w + L.psum);
+  return SWITCH_OK;
+}
+
+// Routing kernels.  With tok set (layer path) the apply step also fills the
+// slot -> token map and the output rows of dropped tokens.
+int run_route(const RouteArgs &a, hipStream_t st, Timer &tm, int32_t *tok = nullptr, const void *xres = nullptr,
+              void *y = nullptr) {
+  hipError_t e;
+  if ((e = launch_router(a, st)) != hipSuccess) return hip_fail(e, "router launch");
+  tm.mark(kKernelNames[0]);
+  if ((e = launch_assign_scan(a, st)) != hipSuccess) return hip_fail(e, "assign_scan launch");
+  tm.mark(kKernelNames[1]);
+  e = tok ? launch_assign_apply_layer(a, tok, xres, y, st) : launch_assign_apply(a, st);
+  if (e != hipSuccess) return hip_fail(e, "assign_apply launch");
+  tm.mark(kKernelNames[2]);
+  return SWITCH_OK;
+}
+
+int layer_forward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                  const void *w_in, const void *w_out, int32_t add_residual, void *y, int32_t *expert_idx,
+                  float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,
+                  void *ws, size_t ws_bytes, void *stream, Timer &tm) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  Layout L;
+  if ((rc = layout(s, L))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
+  RouteArgs ra;
+  if ((rc = route_args(s, x, w_router, router_bias, expert_idx, gate, slot, dropped, expert_count, aux_loss, ws,
+                       ws_bytes, L, ra)))
+    return rc;
+  NEED(w_in, 16);
+  NEED(w_out, 16);
+  if (s->tokens > 0) NEED(y, 16);
+  hipStream_t st = (hipStream_t)stream;
+  char *w = (char *)ws;
+  if (tm.on) {
+    tm.st = st;
+    for (int i = 0; i <= kNumKernels; ++i)
+      if ((tm.err = hipEventCreate(&tm.ev[i])) != hipSuccess) return hip_fail(tm.err, "hipEventCreate");
+    if ((tm.err = hipEventRecord(tm.ev[0], st)) != hipSuccess) return hip_fail(tm.err, "hipEventRecord");
+  }
+  int32_t *tok = (int32_t *)(w + L.lf_tok);
+  const void *xres = add_residual ? x : nullptr;
+  if ((rc = run_route(ra, st, tm, tok, xres, y))) return rc;
+  hipError_t e;
+  GemmCall up{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w + L.lf_hidden,
+              expert_count, tok, nullptr, nullptr};
+  if ((e = launch_ffn_up_gather(up, st)) != hipSuccess) return hip_fail(e, "ffn_up launch");
+  tm.mark(kKernelNames[3]);
+  GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, y,
+                expert_count, tok, gate, xres};
+  if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
+  tm.mark(kKernelNames[4]);
+  return SWITCH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *switch_last_error(void) { return g_err.c_str(); }
+
+int switch_capacity(int64_t tokens, int32_t num_experts, double cf, int32_t *capacity_out) {
+  GUARD({
+    if (!capacity_out) return fail(SWITCH_E_INVALID, "capacity_out is NULL");
+    if (tokens < 0 || num_experts < 1 || !(cf > 0) || !std::isfinite(cf))
+      return fail(SWITCH_E_INVALID, "need tokens >= 0, num_experts >= 1 and a finite capacity_factor > 0");
+    if (tokens > INT32_MAX) return fail(SWITCH_E_UNSUPPORTED, "tokens above 2^31-1");
+    if (tokens == 0) {
+      *capacity_out = 0;
+      return SWITCH_OK;
+    }
+    // cf = mant * 2^sh exactly; capacity = ceil(tokens * mant * 2^sh / N).
+    int ex = 0;
+    const double fr = std::frexp(cf, &ex);
+    int64_t mant = (int64_t)std::ldexp(fr, 53);
+    int sh = ex - 53;
+    while ((mant & 1) == 0) {
+      mant >>= 1;
+      ++sh;
+    }
+    unsigned __int128 num = (unsigned __int128)tokens * (unsigned __int128)mant;  // < 2^84
+    unsigned __int128 den = (unsigned __int128)num_experts;
+    if (sh > 0) {
+      if (sh > 40) return fail(SWITCH_E_UNSUPPORTED, "capacity above 2^31-1");
+      num <<= sh;
+    } else if (sh < 0) {
+      if (-sh >= 90) {
+        *capacity_out = 1;  // 0 < T*cf/N < 1
+        return SWITCH_OK;
+      }
+      den <<= -sh;
+    }
+    unsigned __int128 q = num / den;
+    if (q * den != num) ++q;
+    if (q > (unsigned __int128)INT32_MAX) return fail(SWITCH_E_UNSUPPORTED, "capacity above 2^31-1");
+    *capacity_out = (int32_t)q;
+    return SWITCH_OK;
+  })
+}
+
+int switch_workspace_bytes(const switch_shape *s, size_t *bytes_out) {
+  GUARD({
+    if (!bytes_out) return fail(SWITCH_E_INVALID, "bytes_out is NULL");
+    int rc = check_shape(s);
+    if (rc) return rc;
+    Layout L;
+    if ((rc = layout(s, L))) return rc;
+    *bytes_out = L.total;
+    return SWITCH_OK;
+  })
+}
+
+int switch_route(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                 int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count,
+                 float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    Layout L;
+    if ((rc = layout(s, L))) return rc;
+    RouteArgs a;
+    if ((rc = route_args(s, x, w_router, router_bias, expert_idx, gate, slot, dropped, expert_count, aux_loss, ws,
+                         ws_bytes, L, a)))
+      return rc;
+    Timer tm;
+    return run_route(a, (hipStream_t)stream, tm);
+  })
+}
+
+int switch_dispatch(const switch_shape *s, const void *x, const int32_t *expert_idx, const int32_t *slot,
+                    const uint8_t *dropped, void *dispatched, void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (s->tokens > 0) {
+      NEED(x, 16);
+      NEED(expert_idx, 4);
+      NEED(slot, 4);
+      if (!dropped) return fail(SWITCH_E_INVALID, "dropped is NULL");
+      if (s->capacity > 0) NEED(dispatched, 16);
+    }
+    DispatchArgs a{s->dtype, s->tokens, s->d_model, s->num_experts, s->capacity, x,
+                   expert_idx, slot, dropped, dispatched};
+    hipError_t e = launch_dispatch(a, (hipStream_t)stream);
+    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "dispatch launch");
+  })
+}
+
+int switch_expert_ffn(const switch_shape *s, const void *dispatched, const int32_t *expert_count,
+                      const void *w_in, const void *w_out, void *expert_out, void *ws, size_t ws_bytes,
+                      void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    Layout L;
+    if ((rc = layout(s, L))) return rc;
+    NEED(expert_count, 4);
+    NEED(w_in, 16);
+    NEED(w_out, 16);
+    if (s->capacity > 0) {
+      NEED(dispatched, 16);
+      NEED(expert_out, 16);
+    }
+    if ((rc = check_ws(ws, ws_bytes, L.ffn_end))) return rc;
+    FfnArgs a{s->dtype, s->d_model, s->d_ff, s->num_experts, s->capacity, dispatched, expert_count,
+              w_in, w_out, (char *)ws + L.ffn_hidden, expert_out};
+    hipError_t e = launch_ffn_up(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ffn_up launch");
+    e = launch_ffn_down(a, (hipStream_t)stream);
+    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "ffn_down launch");
+  })
+}
+
+int switch_combine(const switch_shape *s, const void *expert_out, const int32_t *expert_idx, const int32_t *slot,
+                   const uint8_t *dropped, const float *gate, const void *x_residual, void *y, void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (s->tokens > 0) {
+      NEED(expert_idx, 4);
+      NEED(slot, 4);
+      NEED(gate, 4);
+      NEED(y, 16);
+      if (!dropped) return fail(SWITCH_E_INVALID, "dropped is NULL");
+      if (s->capacity > 0) NEED(expert_out, 16);
+      if (x_residual && !aligned(x_residual, 16))
+        return fail(SWITCH_E_INVALID, "x_residual is not 16-byte aligned");
+    }
+    CombineArgs a{s->dtype, s->tokens, s->d_model, s->num_experts, s->capacity, expert_out,
+                  expert_idx, slot, dropped, gate, x_residual, y};
+    hipError_t e = launch_combine(a, (hipStream_t)stream);
+    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "combine launch");
+  })
+}
+
+int switch_layer_forward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                         const void *w_in, const void *w_out, int32_t add_residual, void *y, int32_t *expert_idx,
+                         float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,
+                         void *ws, size_t ws_bytes, void *stream) {
+  GUARD({
+    Timer tm;
+    return layer_forward(s, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
+                         dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
+  })
+}
+
+int switch_layer_forward_profiled(const switch_shape *s, const void *x, const float *w_router,
+                                  const float *router_bias, const void *w_in, const void *w_out,
+                                  int32_t add_residual, void *y, int32_t *expert_idx, float *gate, int32_t *slot,
+                                  uint8_t *dropped, int32_t *expert_count, float *aux_loss, void *ws,
+                                  size_t ws_bytes, void *stream, float *kernel_ms, int32_t max_kernels,
+                                  int32_t *num_kernels) {
+  GUARD({
+    if (!kernel_ms || !num_kernels || max_kernels < 0)
+      return fail(SWITCH_E_INVALID, "kernel_ms / num_kernels is NULL or max_kernels < 0");
+    Timer tm;
+    tm.on = true;
+    int rc = layer_forward(s, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
+                           dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
+    if (rc == SWITCH_OK && tm.err != hipSuccess) rc = hip_fail(tm.err, "hipEventRecord");
+    if (rc == SWITCH_OK) {
+      hipError_t e = hipEventSynchronize(tm.ev[tm.n]);
+      if (e != hipSuccess) rc = hip_fail(e, "hipEventSynchronize");
+      for (int i = 0; rc == SWITCH_OK && i < tm.n; ++i) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, tm.ev[i], tm.ev[i + 1]);
+        if (e != hipSuccess) rc = hip_fail(e, "hipEventElapsedTime");
+        if (i < max_kernels) kernel_ms[i] = ms;
+      }
+      if (rc == SWITCH_OK) *num_kernels = tm.n;
+    }
+    if (tm.on)
+      for (int i = 0; i <= kNumKernels; ++i)
+        if (tm.ev[i]) (void)hipEventDestroy(tm.ev[i]);
+    return rc;
+  })
+}
+
+const char *switch_kernel_name(int32_t index) {
+  return (index >= 0 && index < kNumKernels) ? kKernelNames[index] : "";
+}
+
+}  // extern "C"

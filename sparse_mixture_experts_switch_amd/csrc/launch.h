@@ -1,0 +1,96 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace smx {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+constexpr int kRouterTokens = 32;    // tokens per router block
+constexpr int kRouterThreads = 256;  // 4 waves
+constexpr int kRouterChunk = 128;    // experts per logits chunk (4 waves x 32)
+
+struct RouteArgs {
+  int dtype;
+  int64_t T;
+  int d, N, C;
+  const void *x;
+  const float *w_r, *bias;
+  float *logits;  // [T][N] scratch, only used when N > kRouterChunk
+  int32_t *expert_idx;
+  float *gate;
+  int32_t *slot;  // in-block rank after the router, slot after assignment
+  uint8_t *dropped;
+  int32_t *expert_count;
+  float *aux_loss;
+  int32_t *bcount;  // [nb][N]: block counts, then exclusive block offsets
+  float *ppart;     // [nb][N]: block partial sums of p
+  float *psum;      // [N]
+};
+
+struct DispatchArgs {
+  int dtype;
+  int64_t T;
+  int d, N, C;
+  const void *x;
+  const int32_t *expert_idx, *slot;
+  const uint8_t *dropped;
+  void *dispatched;  // [N][C][d]
+};
+
+struct FfnArgs {
+  int dtype;
+  int d, dff, N, C;
+  const void *dispatched;  // [N][C][d]
+  const int32_t *expert_count;
+  const void *w_in;   // [N][dff][d]
+  const void *w_out;  // [N][d][dff]
+  void *hidden;       // [N][C][dff] scratch
+  void *expert_out;   // [N][C][d]
+};
+
+struct CombineArgs {
+  int dtype;
+  int64_t T;
+  int d, N, C;
+  const void *expert_out;
+  const int32_t *expert_idx, *slot;
+  const uint8_t *dropped;
+  const float *gate;
+  const void *x_residual;  // may be null
+  void *y;
+};
+
+// One grouped GEMM of the expert FFN (see ffn.hip).
+struct GemmCall {
+  int dtype, N, C, K, Nout;
+  const void *A;  // [N][C][K] buffer, or x [T][K] when rows are gathered through tok
+  const void *B;  // [N][Nout][K]
+  void *Out;      // [N][C][Nout] buffer, or y [T][Nout] for the combine epilogue
+  const int32_t *counts;
+  const int32_t *tok;  // [N][C]: token in each live slot (gather / combine)
+  const float *gate;   // [T] (combine)
+  const void *xres;    // [T][Nout] residual rows (combine), may be null
+};
+
+// Each launcher enqueues its kernels on `st` and returns the launch status.
+hipError_t launch_router(const RouteArgs &a, hipStream_t st);
+hipError_t launch_assign_scan(const RouteArgs &a, hipStream_t st);
+hipError_t launch_assign_apply(const RouteArgs &a, hipStream_t st);
+// Layer path: also records tok[e][slot] = t for kept tokens and writes the
+// y rows of dropped tokens (0, or x with a residual).
+hipError_t launch_assign_apply_layer(const RouteArgs &a, int32_t *tok, const void *xres, void *y,
+                                     hipStream_t st);
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st);
+hipError_t launch_ffn_up(const FfnArgs &a, hipStream_t st);
+hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st);
+hipError_t launch_ffn_up_gather(const GemmCall &c, hipStream_t st);
+hipError_t launch_ffn_down_combine(const GemmCall &c, hipStream_t st);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+
+inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
+
+}  // namespace smx

@@ -1,0 +1,112 @@
+// Dispatch (gather into per-expert buffers) and combine (gate-scaled scatter
+// back to token order).
+//
+// Switch Transformers write-up: the figure of "Expert Capacity and the
+// Capacity Factor" (dispatch each token to its single top expert, overflow
+// beyond capacity goes to the residual, combine scales each output by the gate
+// p_i(x)), and the combine equation y = sum_{i in T} p_i(x) E_i(x) of "Switch
+// Routing" with k = 1.  A dropped token's computation is skipped: its bare
+// output is 0, and with the residual it is x.
+//
+// Both kernels move whole rows with 16-byte vector accesses, one wave per
+// token; they are bound by HBM bandwidth.
+
+#include "common.h"
+#include "launch.h"
+
+namespace smx {
+
+constexpr int kMoveThreads = 256;
+constexpr int kMoveTokens = kMoveThreads / kWave;  // one wave per token
+
+__global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ expert_idx, const int32_t *__restrict__ slot,
+    const uint8_t *__restrict__ dropped, u32x4 *__restrict__ out, int64_t T, int row16, int C) {
+  const int64_t t = (int64_t)blockIdx.x * kMoveTokens + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (t >= T || dropped[t]) return;
+  const u32x4 *src = x + t * row16;
+  u32x4 *dst = out + ((int64_t)expert_idx[t] * C + slot[t]) * row16;
+  for (int c = lane; c < row16; c += kWave) dst[c] = src[c];
+}
+
+template <typename T_>
+__device__ __forceinline__ void combine_chunk(u32x4 &out, const u32x4 *eo, const u32x4 *xr, float g,
+                                              bool keep);
+
+template <>
+__device__ __forceinline__ void combine_chunk<bf16>(u32x4 &out, const u32x4 *eo, const u32x4 *xr, float g,
+                                                    bool keep) {
+  bf16x8 r;
+  bf16x8 e = keep ? as_bf16x8(*eo) : bf16x8{};
+  bf16x8 xv = xr ? as_bf16x8(*xr) : bf16x8{};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v = keep ? g * (float)e[i] : 0.f;
+    if (xr) v = (float)xv[i] + v;
+    r[i] = (bf16)v;
+  }
+  out = as_u32x4(r);
+}
+
+template <>
+__device__ __forceinline__ void combine_chunk<float>(u32x4 &out, const u32x4 *eo, const u32x4 *xr, float g,
+                                                     bool keep) {
+  f32x4 e = keep ? __builtin_bit_cast(f32x4, *eo) : f32x4{};
+  f32x4 xv = xr ? __builtin_bit_cast(f32x4, *xr) : f32x4{};
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = keep ? g * e[i] : 0.f;
+    if (xr) v = xv[i] + v;
+    r[i] = v;
+  }
+  out = __builtin_bit_cast(u32x4, r);
+}
+
+template <typename T_>
+__global__ __launch_bounds__(kMoveThreads) void combine_kernel(
+    const u32x4 *__restrict__ expert_out, const int32_t *__restrict__ expert_idx,
+    const int32_t *__restrict__ slot, const uint8_t *__restrict__ dropped, const float *__restrict__ gate,
+    const u32x4 *__restrict__ xres, u32x4 *__restrict__ y, int64_t T, int row16, int C) {
+  const int64_t t = (int64_t)blockIdx.x * kMoveTokens + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (t >= T) return;
+  const bool keep = !dropped[t];
+  const float g = keep ? gate[t] : 0.f;
+  const u32x4 *eo = keep ? expert_out + ((int64_t)expert_idx[t] * C + slot[t]) * row16 : nullptr;
+  const u32x4 *xr = xres ? xres + t * row16 : nullptr;
+  u32x4 *dst = y + t * row16;
+  for (int c = lane; c < row16; c += kWave) {
+    u32x4 o;
+    combine_chunk<T_>(o, keep ? eo + c : nullptr, xr ? xr + c : nullptr, g, keep);
+    dst[c] = o;
+  }
+}
+
+static inline int esize(int dtype) { return dtype == kBF16 ? 2 : 4; }
+
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st) {
+  if (a.T == 0 || a.C == 0) return hipSuccess;
+  const int row16 = a.d * esize(a.dtype) / 16;
+  dispatch_kernel<<<dim3((unsigned)ceil_div(a.T, kMoveTokens)), dim3(kMoveThreads), 0, st>>>(
+      (const u32x4 *)a.x, a.expert_idx, a.slot, a.dropped, (u32x4 *)a.dispatched, a.T, row16, a.C);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  const int row16 = a.d * esize(a.dtype) / 16;
+  dim3 grid((unsigned)ceil_div(a.T, kMoveTokens)), block(kMoveThreads);
+  if (a.dtype == kBF16)
+    combine_kernel<bf16><<<grid, block, 0, st>>>((const u32x4 *)a.expert_out, a.expert_idx, a.slot, a.dropped,
+                                                 a.gate, (const u32x4 *)a.x_residual, (u32x4 *)a.y, a.T, row16,
+                                                 a.C);
+  else
+    combine_kernel<float><<<grid, block, 0, st>>>((const u32x4 *)a.expert_out, a.expert_idx, a.slot,
+                                                  a.dropped, a.gate, (const u32x4 *)a.x_residual, (u32x4 *)a.y,
+                                                  a.T, row16, a.C);
+  return hipGetLastError();
+}
+
+}  // namespace smx

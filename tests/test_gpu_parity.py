@@ -1,0 +1,213 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs are the seeded synthetic workloads of inputs.CONFIGS (full sizes,
+in the launch configuration the benchmark times) plus small shapes that span
+several tiles with ragged tails, and the layer's degenerate cases.
+Tolerances are stated in parity_lib.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.switch_oracle as so
+import sparse_mixture_experts_switch_amd as smx
+from parity_lib import (check_routing, check_y, f64, gpu_outputs_numpy, oracle_run, say)
+from sparse_mixture_experts_switch_amd.inputs import CONFIGS, LayerConfig, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _run(cfg: LayerConfig, add_residual=False, bias=None):
+    say(f"case {cfg}")
+    inp = make_inputs(cfg, device=DEV)
+    if bias is not None:
+        inp["router_bias"] = bias.to(DEV)
+    C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+    assert C == so.expert_capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+    o = smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C,
+                          add_residual=add_residual)
+    torch.cuda.synchronize()
+    say("  gpu done")
+    return inp, C, gpu_outputs_numpy(o)
+
+
+def _check_full(cfg, experts=None, add_residual=False, bias=None):
+    inp, C, g = _run(cfg, add_residual=add_residual, bias=bias)
+    own = oracle_run(inp, C, experts=[] if experts is not None else [])  # routing only
+    fed = oracle_run(inp, C, expert_idx=g["expert_idx"], experts=experts)
+    rep = check_routing(g, own, fed, cfg.name)
+    x = f64(inp["x"]) if add_residual else None
+    rel = check_y(g["y"], fed, cfg.torch_dtype, cfg.name, x=x)
+    say(f"  {cfg.name}: C={C} {rep} max|err|/rms={rel:.3e}")
+    return inp, C, g, fed
+
+
+# --------------------------------------------------------------- edge cases --
+SMALL = LayerConfig("small", 1000, 128, 256, 16, 1.0, "bf16")
+EDGE = {
+    "ragged_tokens": SMALL,
+    "one_expert": SMALL.with_(num_experts=1, tokens=333),
+    "three_experts": SMALL.with_(num_experts=3, tokens=77),
+    "router_chunks_200_experts": SMALL.with_(num_experts=200, tokens=300, capacity_factor=2.0),
+    "fewer_tokens_than_experts": SMALL.with_(tokens=5, num_experts=128),
+    "capacity_37": SMALL.with_(tokens=37 * 16 - 5, capacity_factor=1.0),
+    "capacity_above_tile": SMALL.with_(num_experts=2, tokens=512, capacity_factor=2.0),
+    "no_drops_cf_eq_N": SMALL.with_(capacity_factor=16.0),
+    "small_capacity": SMALL.with_(capacity_factor=0.25),
+    "d_ff_64": SMALL.with_(d_ff=64, d_model=64),
+    "wide_d_ff": SMALL.with_(d_ff=2816 // 4 * 4, d_model=192),
+    "fp32_ragged": SMALL.with_(dtype="f32", tokens=531, num_experts=5, d_model=64, d_ff=192),
+    "fp32_many_experts": SMALL.with_(dtype="f32", tokens=400, num_experts=300, d_model=128, d_ff=128,
+                                     capacity_factor=3.0),
+    "zipf_bias": SMALL.with_(zipf_s=1.1, tokens=2048, num_experts=32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge(name):
+    _check_full(EDGE[name].with_(name=name))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_residual(dtype):
+    _check_full(SMALL.with_(name=f"residual_{dtype}", dtype=dtype, capacity_factor=0.5), add_residual=True)
+
+
+def test_all_tokens_one_expert():
+    cfg = SMALL.with_(name="one_hot_expert", tokens=700)
+    bias = torch.zeros(cfg.num_experts)
+    bias[5] = 50.0
+    inp, C, g, fed = _check_full(cfg, bias=bias)
+    assert np.all(g["expert_idx"] == 5) and g["expert_count"][5] == 700
+    assert g["dropped"].sum() == 700 - C
+
+
+def test_capacity_zero_drops_everything():
+    cfg = SMALL.with_(tokens=300)
+    inp = make_inputs(cfg, device=DEV)
+    o = smx.layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], 0)
+    torch.cuda.synchronize()
+    g = gpu_outputs_numpy(o)
+    assert g["dropped"].all() and np.all(g["y"] == 0.0)
+    fed = oracle_run(inp, 0, expert_idx=g["expert_idx"], experts=[])
+    assert np.array_equal(g["slot"].astype(np.int64), fed["slot"])
+
+
+def test_empty_batch():
+    cfg = SMALL.with_(tokens=0)
+    inp = make_inputs(cfg, device=DEV)
+    out = {"expert_count": torch.full((cfg.num_experts,), 7, dtype=torch.int32, device=DEV),
+           "aux_loss": torch.full((1,), 7.0, device=DEV)}
+    for k, dt in (("expert_idx", torch.int32), ("gate", torch.float32), ("slot", torch.int32),
+                  ("dropped", torch.uint8)):
+        out[k] = torch.empty(0, dtype=dt, device=DEV)
+    out["y"] = torch.empty(0, cfg.d_model, dtype=torch.bfloat16, device=DEV)
+    smx.layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], 0, out=out)
+    torch.cuda.synchronize()
+    assert out["expert_count"].sum().item() == 0 and out["aux_loss"].item() == 0.0
+
+
+def test_deterministic_across_runs_and_streams():
+    cfg = CONFIGS["base"].with_(tokens=4096)
+    inp = make_inputs(cfg, device=DEV)
+    C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+    ref = smx.layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], C)
+    s = torch.cuda.Stream()
+    for i in range(4):
+        with torch.cuda.stream(s if i % 2 else torch.cuda.current_stream()):
+            o = smx.layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], C)
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(o[k], ref[k]), f"run {i}: {k} differs"
+
+
+# -------------------------------------------------------- stage-wise calls --
+def test_stages_match_layer_and_oracle():
+    cfg = SMALL.with_(name="stages", tokens=1500, capacity_factor=0.75)
+    inp = make_inputs(cfg, device=DEV)
+    N, d = cfg.num_experts, cfg.d_model
+    C = smx.capacity(cfg.tokens, N, cfg.capacity_factor)
+    r = smx.route(inp["x"], inp["w_router"], None, C)
+    disp = torch.zeros(N, C, d, dtype=torch.bfloat16, device=DEV)
+    smx.dispatch(inp["x"], r["expert_idx"], r["slot"], r["dropped"], N, C, out=disp)
+    eo = smx.expert_ffn(disp, r["expert_count"], inp["w_in"], inp["w_out"])
+    y = smx.combine(eo, r["expert_idx"], r["slot"], r["dropped"], r["gate"])
+    lf = smx.layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], C)
+    torch.cuda.synchronize()
+    for k in ("expert_idx", "gate", "slot", "dropped", "expert_count", "aux_loss"):
+        assert torch.equal(r[k], lf[k]), k
+    # the stage path rounds expert_out to bf16 before the gate multiply; the
+    # layer path rounds once: they agree to one bf16 ulp
+    ys, yl = y.double(), lf["y"].double()
+    assert torch.all((ys - yl).abs() <= 2.0 ** -7 * yl.abs())
+    g = gpu_outputs_numpy(r)
+    e = g["expert_idx"].astype(np.int64)
+    # dispatch: bit-exact rows, padding untouched (still zero)
+    buf, filled = so.dispatch(f64(inp["x"]), e, g["slot"], g["dropped"], N, C)
+    d64 = f64(disp)
+    assert np.array_equal(d64[filled], buf[filled]) and np.all(d64[~filled] == 0.0)
+    # expert FFN on the live rows, against the oracle's FFN of the same rows
+    eo64 = f64(eo)
+    for i in range(N):
+        m = min(int(g["expert_count"][i]), C)
+        if m == 0:
+            continue
+        ref = so.expert_ffn(d64[i, :m], f64(inp["w_in"][i]), f64(inp["w_out"][i]))
+        rms = np.sqrt(np.mean(ref ** 2))
+        assert np.all(np.abs(eo64[i, :m] - ref) <= 2e-2 * rms + 2.0 ** -8 * np.abs(ref)), i
+    # combine of the GPU's own expert_out: one bf16 rounding of gate * value
+    ref = so.combine(eo64, e, g["slot"], g["dropped"], g["gate"].astype(np.float64))
+    yy = f64(y)
+    assert np.all(np.abs(yy - ref) <= 2.0 ** -8 * np.abs(ref))
+    assert np.all(yy[g["dropped"]] == 0.0)
+
+
+def test_route_feeds_oracle_routing():
+    """Stage calls take the oracle's routing as well: dispatch + combine fed
+    the oracle's slots reproduce the oracle's layout bit-exactly."""
+    cfg = SMALL.with_(tokens=800, capacity_factor=0.5)
+    inp = make_inputs(cfg, device=DEV)
+    N, d = cfg.num_experts, cfg.d_model
+    C = so.expert_capacity(cfg.tokens, N, cfg.capacity_factor)
+    own = oracle_run(inp, C, experts=[])
+    e = torch.tensor(own["expert_idx"], dtype=torch.int32, device=DEV)
+    sl = torch.tensor(own["slot"], dtype=torch.int32, device=DEV)
+    dr = torch.tensor(own["dropped"], dtype=torch.uint8, device=DEV)
+    disp = torch.zeros(N, C, d, dtype=torch.bfloat16, device=DEV)
+    smx.dispatch(inp["x"], e, sl, dr, N, C, out=disp)
+    torch.cuda.synchronize()
+    buf, filled = so.dispatch(f64(inp["x"]), own["expert_idx"], own["slot"], own["dropped"], N, C)
+    assert np.array_equal(f64(disp)[filled], buf[filled])
+
+
+def test_invalid_arguments_rejected():
+    cfg = SMALL.with_(tokens=64)
+    inp = make_inputs(cfg, device=DEV)
+    with pytest.raises(smx.SwitchError) as ei:
+        smx.layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], -1)
+    assert ei.value.code == smx.binding.SWITCH_E_INVALID
+    small_ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(smx.SwitchError) as ei:
+        smx.layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], 4, workspace=small_ws)
+    assert ei.value.code == smx.binding.SWITCH_E_WORKSPACE
+
+
+# ------------------------------------------------------------- full configs --
+@pytest.mark.parametrize("name", ["tiny", "base", "large"])
+def test_config_full(name):
+    _check_full(CONFIGS[name])
+
+
+def test_xxl_sampled_experts():
+    cfg = CONFIGS["xxl"]
+    rng = np.random.default_rng(7)
+    _check_full(cfg, experts=sorted(rng.choice(cfg.num_experts, 8, replace=False).tolist()))
+
+
+def test_many_sampled_experts():
+    cfg = CONFIGS["many"]
+    rng = np.random.default_rng(7)
+    _check_full(cfg, experts=sorted(rng.choice(cfg.num_experts, 32, replace=False).tolist()))
+    torch.cuda.empty_cache()
