@@ -33,7 +33,7 @@
 
 namespace smx {
 
-constexpr int kFfnThreads = 256;  // 4 waves
+constexpr int kFfnThreads = 256;  // fp32 kernel: 4 waves
 constexpr int kKC = 64;           // contraction chunk
 constexpr int kLdsStride = kKC + 8;
 
@@ -61,19 +61,21 @@ __device__ __forceinline__ int xcd_tile(int b, int grid) {
 }
 
 // bf16 grouped GEMM on v_mfma_f32_16x16x32_bf16.
-// MB: 16-row blocks per workgroup; NBW: 16-column blocks per wave
-// (workgroup columns = 4 * 16 * NBW); DEPTH: weight chunks in flight.
+// MB: 16-row blocks per workgroup; NBW: 16-column blocks per wave;
+// WAVES: waves per workgroup (workgroup columns = WAVES * 16 * NBW);
+// DEPTH: register ring of contraction chunks in flight.
 // Operand layout: lane l supplies row (l % 16) and 8 consecutive k starting
 // at 8 * (l / 16); result lane l holds column (l % 16), rows 4 * (l / 16) + i.
-template <int MB, int NBW, int DEPTH, bool kGather, int kEpi>
-__global__ __launch_bounds__(kFfnThreads) void ffn_gemm_bf16_kernel(const GemmArgs<bf16> p) {
+template <int MB, int NBW, int DEPTH, int WAVES, bool kGather, int kEpi>
+__global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArgs<bf16> p) {
+  constexpr int kFfnThreads = WAVES * 64;
   constexpr int kRows = MB * 16;
-  constexpr int kCols = 4 * NBW * 16;
+  constexpr int kCols = WAVES * NBW * 16;
   constexpr int kAChunks = kRows * (kKC / 8);  // 16-byte pieces of one A chunk
   constexpr int kAPer = (kAChunks + kFfnThreads - 1) / kFfnThreads;
   constexpr int kABytes = 2 * kRows * kLdsStride * 2;
   constexpr int kEStride = NBW * 16 + 4;  // fp32 staging row (per wave)
-  constexpr int kEBytes = 4 * 16 * kEStride * 4;
+  constexpr int kEBytes = WAVES * 16 * kEStride * 4;
   constexpr int kSmem = kABytes > kEBytes ? kABytes : kEBytes;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   __shared__ int s_tok[kRows];
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_bf16_kernel(const GemmAr
     __syncthreads();
   }
 
-  const bf16 *Aexp = p.A + ((int64_t)e * p.C + m0) * K;
+  // Weight rows of this wave (rows past Nout read row 0; never stored).
   const bf16 *bp[NBW];
   bool bval[NBW];
 #pragma unroll
@@ -114,6 +116,20 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_bf16_kernel(const GemmAr
     bval[nb] = n < Nout;
     bp[nb] = p.B + ((int64_t)e * Nout + (bval[nb] ? n : 0)) * K + kq;
   }
+  // Activation pieces this thread moves into LDS: row ar[q], 8 columns at
+  // ac[q].  Rows past the live ones re-read the last live row, so that every
+  // lane always loads (no divergent branches around the loads: the compiler
+  // can then count outstanding loads exactly and keep the prefetch in flight).
+  const bf16 *asrc[kAPer];
+  int aoff[kAPer];
+#pragma unroll
+  for (int q = 0; q < kAPer; ++q) {
+    const int i = (tid + q * kFfnThreads) % kAChunks;
+    const int r = i / (kKC / 8), c = i % (kKC / 8);
+    const int rr = min(r, mrows - 1);
+    asrc[q] = (kGather ? p.A + (int64_t)s_tok[rr] * K : p.A + ((int64_t)e * p.C + m0 + rr) * K) + c * 8;
+    aoff[q] = r * kLdsStride + c * 8;
+  }
 
   f32x4 acc[MB][NBW];
 #pragma unroll
@@ -121,36 +137,27 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_bf16_kernel(const GemmAr
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int nch = K / kKC;
   u32x4 areg[DEPTH][kAPer];
   u32x4 breg[DEPTH][2][NBW];
-  auto fetch = [&](int slot, int k0) {
+  // Loads of chunk `ch` (clamped to the last chunk past the end: re-reads
+  // that hit in cache and are never consumed).
+  auto fetch = [&](int slot, int ch) {
+    const int k0 = min(ch, nch - 1) * kKC;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) breg[slot][s][nb] = *(const u32x4 *)(bp[nb] + k0 + s * 32);
 #pragma unroll
-    for (int q = 0; q < kAPer; ++q) {
-      const int i = tid + q * kFfnThreads;
-      const int r = i / (kKC / 8), c = i % (kKC / 8);
-      if (i < kAChunks && r < mrows) {
-        const bf16 *src = kGather ? p.A + (int64_t)s_tok[r] * K : Aexp + (int64_t)r * K;
-        areg[slot][q] = *(const u32x4 *)(src + k0 + c * 8);
-      }
-    }
+    for (int q = 0; q < kAPer; ++q) areg[slot][q] = *(const u32x4 *)(asrc[q] + k0);
   };
   auto store_a = [&](int slot, int buf) {
 #pragma unroll
-    for (int q = 0; q < kAPer; ++q) {
-      const int i = tid + q * kFfnThreads;
-      const int r = i / (kKC / 8), c = i % (kKC / 8);
-      if (i < kAChunks && r < mrows) *(u32x4 *)(&sA[buf * kRows * kLdsStride + r * kLdsStride + c * 8]) = areg[slot][q];
-    }
+    for (int q = 0; q < kAPer; ++q) *(u32x4 *)(&sA[buf * kRows * kLdsStride + aoff[q]]) = areg[slot][q];
   };
 
-  const int nch = K / kKC;
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j)
-    if (j < nch) fetch(j, j * kKC);
+  for (int j = 0; j < DEPTH; ++j) fetch(j, j);
   store_a(0, 0);
   __syncthreads();
   for (int base = 0; base < nch; base += DEPTH) {
@@ -161,23 +168,25 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_bf16_kernel(const GemmAr
         const bf16 *abuf = sA + (ch & 1) * kRows * kLdsStride;
 #pragma clang loop unroll(full)
         for (int s = 0; s < 2; ++s) {
+          // every row block runs: rows past the live ones hold copies of the
+          // last live row and are never stored (straight-line MFMA stream;
+          // the kernel is bound by the weight stream, not by MFMA)
 #pragma clang loop unroll(full)
           for (int mb = 0; mb < MB; ++mb) {
-            if (mb < amb) {
-              const bf16x8 a = as_bf16x8(*(const u32x4 *)(&abuf[(mb * 16 + r16) * kLdsStride + s * 32 + kq]));
+            const bf16x8 a = as_bf16x8(*(const u32x4 *)(&abuf[(mb * 16 + r16) * kLdsStride + s * 32 + kq]));
 #pragma unroll
-              for (int nb = 0; nb < NBW; ++nb)
-                acc[mb][nb] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(breg[j][s][nb]), acc[mb][nb], 0, 0, 0);
-            }
+            for (int nb = 0; nb < NBW; ++nb)
+              acc[mb][nb] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(breg[j][s][nb]), acc[mb][nb], 0, 0, 0);
           }
         }
-        // next chunk's A into the other LDS buffer (its readers finished at
-        // the previous barrier), then refill this ring slot DEPTH ahead
-        if (ch + 1 < nch) store_a((j + 1) % DEPTH, (ch + 1) & 1);
-        if (ch + DEPTH < nch) fetch(j, (ch + DEPTH) * kKC);
-        __syncthreads();
       }
+      // refill this ring slot DEPTH chunks ahead, then move the next chunk's
+      // activations into the other LDS buffer (its readers finished at the
+      // previous barrier)
+      fetch(j, ch + DEPTH);
+      store_a((j + 1) % DEPTH, (ch + 1) & 1);
+      __syncthreads();
     }
   }
 
@@ -309,80 +318,55 @@ int pick_mb(int C) {
   return kMaxMB;
 }
 
-// Columns per wave: the widest choice whose tile count fills the 256 CUs
-// in whole rounds best.
-int pick_nbw(int64_t experts_x_mtiles, int Nout) {
-  int best = 4;
-  double best_eff = -1.0;
-  for (int nbw : {4, 3, 2}) {
-    const int64_t tiles = experts_x_mtiles * ceil_div(Nout, 64 * nbw);
-    const double eff = (double)tiles / (double)(ceil_div(tiles, 256) * 256);
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best = nbw;
-    }
-  }
-  return best;
-}
-
 template <typename T_>
-GemmArgs<T_> make_args(const void *A, const void *B, void *O, const int32_t *counts, const int32_t *tok,
-                       const float *gate, const void *xres, int N, int C, int K, int Nout, int rows, int cols) {
+GemmArgs<T_> make_args(const GemmCall &c, int rows, int cols) {
   GemmArgs<T_> g;
-  g.A = (const T_ *)A;
-  g.B = (const T_ *)B;
-  g.Out = (T_ *)O;
-  g.counts = counts;
-  g.tok = tok;
-  g.gate = gate;
-  g.xres = (const T_ *)xres;
-  g.C = C;
-  g.K = K;
-  g.Nout = Nout;
-  g.m_tiles = (int)ceil_div(C, rows);
-  g.n_tiles = (int)ceil_div(Nout, cols);
-  g.ntiles = N * g.m_tiles * g.n_tiles;
-  (void)N;
+  g.A = (const T_ *)c.A;
+  g.B = (const T_ *)c.B;
+  g.Out = (T_ *)c.Out;
+  g.counts = c.counts;
+  g.tok = c.tok;
+  g.gate = c.gate;
+  g.xres = (const T_ *)c.xres;
+  g.C = c.C;
+  g.K = c.K;
+  g.Nout = c.Nout;
+  g.m_tiles = (int)ceil_div(c.C, rows);
+  g.n_tiles = (int)ceil_div(c.Nout, cols);
+  g.ntiles = c.N * g.m_tiles * g.n_tiles;
   return g;
 }
 
 inline unsigned grid_of(int ntiles) { return (unsigned)(ceil_div(ntiles, 8) * 8); }
 
-template <int MB, int NBW, bool kGather, int kEpi>
-hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
-  constexpr int kDepth = 3;
-  auto g = make_args<bf16>(c.A, c.B, c.Out, c.counts, c.tok, c.gate, c.xres, c.N, c.C, c.K, c.Nout, MB * 16,
-                           64 * NBW);
-  ffn_gemm_bf16_kernel<MB, NBW, kDepth, kGather, kEpi><<<dim3(grid_of(g.ntiles)), dim3(kFfnThreads), 0, st>>>(g);
-  return hipGetLastError();
-}
+// Tile shape (measured on MI355X for the weight-streaming regime): every
+// live row of the expert (up to 160) x 384 output features per workgroup of
+// 8 waves (3 column blocks each), two contraction chunks in flight.
+constexpr int kNBW = 3, kWaves = 8, kDepth = 2;
 
 template <int MB, bool kGather, int kEpi>
-hipError_t run_bf16_nbw(int nbw, const GemmCall &c, hipStream_t st) {
-  switch (nbw) {
-    case 2: return run_bf16<MB, 2, kGather, kEpi>(c, st);
-    case 3: return run_bf16<MB, 3, kGather, kEpi>(c, st);
-    default: return run_bf16<MB, 4, kGather, kEpi>(c, st);
-  }
+hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
+  auto g = make_args<bf16>(c, MB * 16, kWaves * 16 * kNBW);
+  ffn_gemm_bf16_kernel<MB, kNBW, kDepth, kWaves, kGather, kEpi>
+      <<<dim3(grid_of(g.ntiles)), dim3(kWaves * 64), 0, st>>>(g);
+  return hipGetLastError();
 }
 
 template <bool kGather, int kEpi>
 hipError_t gemm(const GemmCall &c, hipStream_t st) {
   if (c.N == 0 || c.C == 0) return hipSuccess;
   if (c.dtype == kF32) {
-    auto g = make_args<float>(c.A, c.B, c.Out, c.counts, c.tok, c.gate, c.xres, c.N, c.C, c.K, c.Nout, 64, 64);
+    auto g = make_args<float>(c, 64, 64);
     ffn_gemm_f32_kernel<kGather, kEpi><<<dim3(grid_of(g.ntiles)), dim3(kFfnThreads), 0, st>>>(g);
     return hipGetLastError();
   }
-  const int mb = pick_mb(c.C);
-  const int nbw = pick_nbw((int64_t)c.N * ceil_div(c.C, mb * 16), c.Nout);
-  switch (mb) {
-    case 1: return run_bf16_nbw<1, kGather, kEpi>(nbw, c, st);
-    case 2: return run_bf16_nbw<2, kGather, kEpi>(nbw, c, st);
-    case 4: return run_bf16_nbw<4, kGather, kEpi>(nbw, c, st);
-    case 6: return run_bf16_nbw<6, kGather, kEpi>(nbw, c, st);
-    case 8: return run_bf16_nbw<8, kGather, kEpi>(nbw, c, st);
-    default: return run_bf16_nbw<10, kGather, kEpi>(nbw, c, st);
+  switch (pick_mb(c.C)) {
+    case 1: return run_bf16<1, kGather, kEpi>(c, st);
+    case 2: return run_bf16<2, kGather, kEpi>(c, st);
+    case 4: return run_bf16<4, kGather, kEpi>(c, st);
+    case 6: return run_bf16<6, kGather, kEpi>(c, st);
+    case 8: return run_bf16<8, kGather, kEpi>(c, st);
+    default: return run_bf16<10, kGather, kEpi>(c, st);
   }
 }
 
