@@ -38,7 +38,7 @@ def algorithmic_bytes(name: str, T: int, d: int, f: int, N: int, C: int, counts)
     every output byte written once; no padding rows)."""
     kept = int(sum(min(int(c), C) for c in counts))
     active = int(sum(1 for c in counts if c > 0 and C > 0))
-    nb = (T + 31) // 32
+    nb = (T + 63) // 64  # router blocks of 64 tokens
     if name == "router":
         return T * d * 2 + N * d * 4 + T * 12 + nb * N * 8
     if name == "assign_scan":

@@ -23,7 +23,11 @@ constexpr int kScanWaves = 16;
 // One workgroup per 64 experts (lane = expert).  Wave w owns a contiguous
 // segment of blocks: it sums its segment, the segment sums are scanned in LDS,
 // then the wave rewrites its segment as exclusive offsets.  The P partial sums
-// are reduced in the same fixed order (segment by segment).
+// are reduced in the same fixed order (segment by segment).  Loads are issued
+// kScanBatch at a time so that each wave waits for memory once per batch, not
+// once per block.
+constexpr int kScanBatch = 8;
+
 __global__ __launch_bounds__(kScanWaves *kWave) void assign_scan_kernel(
     int32_t *__restrict__ bcount, const float *__restrict__ ppart, int64_t nb, int N,
     int32_t *__restrict__ expert_count, float *__restrict__ psum) {
@@ -32,26 +36,43 @@ __global__ __launch_bounds__(kScanWaves *kWave) void assign_scan_kernel(
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int j = blockIdx.x * kWave + lane;
   const bool valid = j < N;
+  const int jj = valid ? j : N - 1;  // lanes past N read a valid column
   const int64_t seg = ceil_div(nb, kScanWaves);
   const int64_t b0 = min<int64_t>(nb, wave * seg), b1 = min<int64_t>(nb, b0 + seg);
   int c = 0;
   float p = 0.f;
-  if (valid)
-    for (int64_t b = b0; b < b1; ++b) {
-      c += bcount[b * N + j];
-      p += ppart[b * N + j];
+  for (int64_t b = b0; b < b1; b += kScanBatch) {
+    int cv[kScanBatch];
+    float pv[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) {
+      const int64_t bb = min(b + i, b1 - 1);
+      cv[i] = bcount[bb * N + jj];
+      pv[i] = ppart[bb * N + jj];
     }
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      if (b + i < b1) {
+        c += cv[i];
+        p += pv[i];
+      }
+  }
   s_cnt[wave][lane] = c;
   s_p[wave][lane] = p;
   __syncthreads();
   int run = 0;
   for (int w = 0; w < wave; ++w) run += s_cnt[w][lane];
-  if (valid)
-    for (int64_t b = b0; b < b1; ++b) {
-      const int v = bcount[b * N + j];
-      bcount[b * N + j] = run;
-      run += v;
-    }
+  for (int64_t b = b0; b < b1; b += kScanBatch) {
+    int cv[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) cv[i] = bcount[min(b + i, b1 - 1) * N + jj];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      if (b + i < b1) {
+        if (valid) bcount[(b + i) * N + j] = run;
+        run += cv[i];
+      }
+  }
   if (wave == 0 && valid) {
     int tot = 0;
     float ps = 0.f;

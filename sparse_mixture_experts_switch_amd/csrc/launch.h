@@ -9,7 +9,7 @@ namespace smx {
 
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
-constexpr int kRouterTokens = 32;    // tokens per router block
+constexpr int kRouterTokens = 64;    // tokens per router block
 constexpr int kRouterThreads = 256;  // 4 waves
 constexpr int kRouterChunk = 128;    // experts per logits chunk (4 waves x 32)
 
@@ -20,6 +20,7 @@ struct RouteArgs {
   const void *x;
   const float *w_r, *bias;
   float *logits;  // [T][N] scratch, only used when N > kRouterChunk
+  void *planes;   // [3][N][d] bf16 scratch: W_r split into hi/mid/lo planes
   int32_t *expert_idx;
   float *gate;
   int32_t *slot;  // in-block rank after the router, slot after assignment

@@ -19,8 +19,9 @@
 //
 // bf16 activations: the contraction runs on bf16 MFMA.  W_r (fp32) is split
 // exactly into three bf16 planes hi + mid + lo (each plane takes the next 8
-// significant bits), so every product x_k * plane_k is exact in fp32 and the
-// fp32 accumulation sees the same terms as an fp32 dot product.
+// significant bits; a small kernel does it once per call), so every product
+// x_k * plane_k is exact in fp32 and the fp32 accumulation sees the same
+// terms as an fp32 dot product.
 // fp32 activations: plain fp32 FMA on the vector ALUs.
 
 #include "common.h"
@@ -45,140 +46,204 @@ struct LogitRows {
 };
 
 // Softmax, argmax, gate, P partials, block counts and in-block ranks for the
-// block's tokens, from logits already complete in `lg`.
+// block's tokens, from logits already complete in `lg`.  Four consecutive
+// lanes share a token: each scans every fourth expert, then two butterfly
+// steps combine the four partial results in a fixed order.
 template <bool kLds>
 __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t t0, int64_t blk,
                                 int32_t *__restrict__ expert_idx, float *__restrict__ gate,
                                 int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
                                 float *__restrict__ ppart, float *s_max, float *s_inv, int *s_e) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  constexpr int kWaves = kRouterThreads / kWave;
-  for (int t = wave; t < nt; t += kWaves) {
+  static_assert(kRouterThreads == 4 * kRouterTokens, "4 lanes per token");
+  const int tid = threadIdx.x;
+  const int t = tid / 4, q = tid % 4;
+  if (t < nt) {
     float best = -INFINITY;
     int bi = 0x7fffffff;
-    for (int j = lane; j < N; j += kWave) {
-      float h = lg.at(t, j);
-      if (h > best) {  // ascending j per lane: first maximum kept
+    for (int j = q; j < N; j += 4) {
+      const float h = lg.at(t, j);
+      if (h > best) {  // ascending j: first maximum kept
         best = h;
         bi = j;
       }
     }
-    wave_argmax(best, bi);
-    float s = 0.f;
-    for (int j = lane; j < N; j += kWave) s += __expf(lg.at(t, j) - best);
-    s = wave_sum(s);
-    if (lane == 0) {
-      float inv = 1.0f / s;
+#pragma unroll
+    for (int off = 1; off < 4; off <<= 1) {
+      const float ov = __shfl_xor(best, off, kWave);
+      const int oi = __shfl_xor(bi, off, kWave);
+      if (ov > best || (ov == best && oi < bi)) {
+        best = ov;
+        bi = oi;
+      }
+    }
+    float sum = 0.f;
+    for (int j = q; j < N; j += 4) sum += __expf(lg.at(t, j) - best);
+    sum += __shfl_xor(sum, 1, kWave);
+    sum += __shfl_xor(sum, 2, kWave);
+    if (q == 0) {
+      const float inv = 1.0f / sum;
       s_max[t] = best;
       s_inv[t] = inv;
       s_e[t] = bi;
       expert_idx[t0 + t] = bi;
-      gate[t0 + t] = inv;  // p_e = exp(h_e - max) / s with h_e = max
+      gate[t0 + t] = inv;  // p_e = exp(h_e - max) / sum with h_e = max
     }
-  }
+  }  // the four lanes of a token are always on the same side of t < nt
   __syncthreads();
   for (int j = tid; j < N; j += kRouterThreads) {
     float p = 0.f;
     int c = 0;
-    for (int t = 0; t < nt; ++t) {
-      p += __expf(lg.at(t, j) - s_max[t]) * s_inv[t];
-      c += (s_e[t] == j);
+    for (int u = 0; u < nt; ++u) {
+      p += __expf(lg.at(u, j) - s_max[u]) * s_inv[u];
+      c += (s_e[u] == j);
     }
     ppart[blk * N + j] = p;
     bcount[blk * N + j] = c;
   }
-  for (int t = tid; t < nt; t += kRouterThreads) {
-    int e = s_e[t], r = 0;
-    for (int u = 0; u < t; ++u) r += (s_e[u] == e);
-    slot_rank[t0 + t] = r;
+  if (tid < nt) {
+    const int e = s_e[tid];
+    int r = 0;
+    for (int u = 0; u < tid; ++u) r += (s_e[u] == e);
+    slot_rank[t0 + tid] = r;
   }
 }
 
 // ---------------------------------------------------------------------------
 // bf16 activations, 3-plane bf16 MFMA (v_mfma_f32_16x16x32_bf16).
-// Wave w computes experts [c0 + 32w, c0 + 32w + 32) for all 32 tokens of the
-// block: 2 token tiles x 2 expert tiles of 16x16.
+// The block's 64 token rows and the 128-expert chunk of the three W_r planes
+// move through LDS 64 contraction columns at a time: global loads are
+// row-contiguous (8 lanes cover one 128-byte row piece, the access pattern
+// the L1/L2 path serves fastest), a register ring keeps kRouterDepth chunks
+// in flight, and the MFMA operands are then read from padded LDS rows.
+// Wave w computes experts [c0 + 32w, c0 + 32w + 32) for all 64 tokens: 4
+// token tiles x 2 expert tiles of 16x16, three planes each.
 // MFMA operand layout (16x16x32): lane l supplies row (l % 16) and the 8
 // consecutive k values starting at 8 * (l / 16); the result lane l holds
 // column (l % 16), rows 4 * (l / 16) + i.
 // ---------------------------------------------------------------------------
+constexpr int kRouterDepth = 2;
+constexpr int kTokTiles = kRouterTokens / 16;
+constexpr int kRKC = 64;                     // contraction columns per chunk
+constexpr int kRLS = kRKC + 8;               // padded LDS row (bf16)
+constexpr int kXPer = kRouterTokens * (kRKC / 8) / kRouterThreads;      // 16-byte x pieces per thread
+constexpr int kWPer = 3 * kRouterChunk * (kRKC / 8) / kRouterThreads;  // 16-byte plane pieces per thread
+constexpr int kXStage = kRouterTokens * kRLS;                          // bf16 per x stage
+constexpr int kWStage = 3 * kRouterChunk * kRLS;                       // bf16 per plane stage
+constexpr int kRouterStageBytes = 2 * (kXStage + kWStage) * 2;
+constexpr int kRouterLgBytes = kRouterTokens * (kRouterChunk + 1) * 4;
+constexpr int kRouterSmem = kRouterStageBytes > kRouterLgBytes ? kRouterStageBytes : kRouterLgBytes;
+
 template <bool kLds>
 __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
-    const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
+    const bf16 *__restrict__ x, const bf16 *__restrict__ planes, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
     float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
     float *__restrict__ ppart) {
-  static_assert(kRouterTokens == 32 && kRouterThreads == 256, "tile shape");
-  __shared__ float s_lg[kLds ? kRouterTokens * (kRouterChunk + 1) : 1];
+  static_assert(kRouterThreads == 256 && kRouterChunk == 128, "4 waves x 32 experts");
+  static_assert(kXPer * kRouterThreads == kRouterTokens * (kRKC / 8), "x pieces");
+  static_assert(kWPer * kRouterThreads == 3 * kRouterChunk * (kRKC / 8), "plane pieces");
+  __shared__ __attribute__((aligned(16))) char smem[kRouterSmem];
   __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
   __shared__ int s_e[kRouterTokens];
+  bf16 *xs = (bf16 *)smem;              // [2][64][kRLS]
+  bf16 *ws = xs + 2 * kXStage;          // [2][3][128][kRLS]
 
   const int64_t blk = blockIdx.x;
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int r16 = lane % 16, kq = (lane / 16) * 8;
+  const int64_t plane = (int64_t)N * d;
+  const int nk = d / kRKC;
 
   LogitRows<kLds> lg;
   if (kLds) {
-    lg.base = s_lg;
+    lg.base = (float *)smem;  // reuses the staging buffers after the contraction
     lg.stride = kRouterChunk + 1;
   } else {
     lg.base = logits_g + t0 * N;
     lg.stride = N;
   }
 
-  // token rows this lane feeds to the A operand (clamped inside the batch)
-  const int64_t ta0 = t0 + min(r16, nt - 1);
-  const int64_t ta1 = t0 + min(16 + r16, nt - 1);
-  const bf16 *xa0 = x + ta0 * d + kq;
-  const bf16 *xa1 = x + ta1 * d + kq;
+  // Row-contiguous load plan: piece i covers 16 bytes of row i / 8.
+  const bf16 *xsrc[kXPer];
+  int xoff[kXPer];
+#pragma unroll
+  for (int q = 0; q < kXPer; ++q) {
+    const int i = tid + q * kRouterThreads, r = i / 8, c = i % 8;
+    xsrc[q] = x + (t0 + min(r, nt - 1)) * d + c * 8;
+    xoff[q] = r * kRLS + c * 8;
+  }
 
   for (int c0 = 0; c0 < N; c0 += kRouterChunk) {
-    const int e0 = c0 + wave * 32 + r16;  // expert of B tile 0 for this lane
-    const int e1 = e0 + 16;
-    const bool v0 = e0 < N, v1 = e1 < N;
-    const float *wb0 = w_r + (int64_t)(v0 ? e0 : 0) * d + kq;
-    const float *wb1 = w_r + (int64_t)(v1 ? e1 : 0) * d + kq;
-    f32x4 acc[2][2] = {};
-    if (c0 + wave * 32 < N) {
-      for (int k = 0; k < d; k += 32) {
-        bf16x8 a0 = as_bf16x8(*(const u32x4 *)(xa0 + k));
-        bf16x8 a1 = as_bf16x8(*(const u32x4 *)(xa1 + k));
-        bf16x8 bh[2], bm[2], bl[2];
+    const bf16 *wsrc[kWPer];
+    int woff[kWPer];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float *wp = (q == 0 ? wb0 : wb1) + k;
-          const bool valid = q == 0 ? v0 : v1;
-          f32x4 w0 = *(const f32x4 *)wp;
-          f32x4 w1 = *(const f32x4 *)(wp + 4);
-          if (!valid) {
-            w0 = f32x4{0.f, 0.f, 0.f, 0.f};
-            w1 = w0;
-          }
+    for (int q = 0; q < kWPer; ++q) {
+      const int i = tid + q * kRouterThreads, row = i / 8, c = i % 8;  // row = plane * 128 + expert
+      const int pl = row / kRouterChunk, e = row % kRouterChunk;
+      wsrc[q] = planes + pl * plane + (int64_t)min(c0 + e, N - 1) * d + c * 8;
+      woff[q] = row * kRLS + c * 8;
+    }
+    u32x4 xr[kRouterDepth][kXPer], wr[kRouterDepth][kWPer];
+    auto fetch = [&](int slot, int ch) {
+      const int k0 = min(ch, nk - 1) * kRKC;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            bf16 h, m, l;
-            split3(i < 4 ? w0[i] : w1[i - 4], h, m, l);
-            bh[q][i] = h;
-            bm[q][i] = m;
-            bl[q][i] = l;
+      for (int q = 0; q < kXPer; ++q) xr[slot][q] = *(const u32x4 *)(xsrc[q] + k0);
+#pragma unroll
+      for (int q = 0; q < kWPer; ++q) wr[slot][q] = *(const u32x4 *)(wsrc[q] + k0);
+    };
+    auto store = [&](int slot, int buf) {
+#pragma unroll
+      for (int q = 0; q < kXPer; ++q) *(u32x4 *)(xs + buf * kXStage + xoff[q]) = xr[slot][q];
+#pragma unroll
+      for (int q = 0; q < kWPer; ++q) *(u32x4 *)(ws + buf * kWStage + woff[q]) = wr[slot][q];
+    };
+    f32x4 acc[kTokTiles][2];
+#pragma unroll
+    for (int tb = 0; tb < kTokTiles; ++tb) acc[tb][0] = acc[tb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();  // previous chunk's readers of the staging buffers are done
+#pragma unroll
+    for (int j = 0; j < kRouterDepth; ++j) fetch(j, j);
+    store(0, 0);
+    __syncthreads();
+    for (int base = 0; base < nk; base += kRouterDepth) {
+#pragma clang loop unroll(full)
+      for (int j = 0; j < kRouterDepth; ++j) {
+        const int ch = base + j;
+        if (ch < nk) {
+          const bf16 *xb = xs + (ch & 1) * kXStage;
+          const bf16 *wbuf = ws + (ch & 1) * kWStage;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            bf16x8 b[2][3];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+              for (int pl = 0; pl < 3; ++pl)
+                b[q][pl] = as_bf16x8(*(const u32x4 *)(
+                    wbuf + (pl * kRouterChunk + wave * 32 + q * 16 + r16) * kRLS + s * 32 + kq));
+#pragma unroll
+            for (int tb = 0; tb < kTokTiles; ++tb) {
+              const bf16x8 a = as_bf16x8(*(const u32x4 *)(xb + (tb * 16 + r16) * kRLS + s * 32 + kq));
+#pragma unroll
+              for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+                  acc[tb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[q][pl], acc[tb][q], 0, 0, 0);
+            }
           }
         }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh[q], acc[0][q], 0, 0, 0);
-          acc[1][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh[q], acc[1][q], 0, 0, 0);
-          acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bm[q], acc[0][q], 0, 0, 0);
-          acc[1][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bm[q], acc[1][q], 0, 0, 0);
-          acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl[q], acc[0][q], 0, 0, 0);
-          acc[1][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl[q], acc[1][q], 0, 0, 0);
-        }
+        fetch(j, ch + kRouterDepth);
+        store((j + 1) % kRouterDepth, (ch + 1) & 1);
+        __syncthreads();
       }
     }
-    // scatter the 32 x 32 logits tile of this wave
+    // scatter this wave's 64 x 32 logits tile (the staging buffers are free:
+    // the loop ended with a barrier)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < kTokTiles; ++tb)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int j = c0 + wave * 32 + q * 16 + r16;
@@ -187,7 +252,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = tb * 16 + (lane / 16) * 4 + i;
-            if (t < nt) lg.at(t, kLds ? j - c0 + 0 : j) = acc[tb][q][i] + b;
+            if (t < nt) lg.at(t, kLds ? j - c0 : j) = acc[tb][q][i] + b;
           }
         }
       }
@@ -196,6 +261,27 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
   __syncthreads();
   router_epilogue<kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, s_max, s_inv,
                         s_e);
+}
+
+// W_r split once per call into three bf16 planes [3][N][d] (hi, mid, lo),
+// 8 values per thread.
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ w_r, int64_t n8,
+                                                           u32x4 *__restrict__ planes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = ((const f32x4 *)w_r)[2 * i], b = ((const f32x4 *)w_r)[2 * i + 1];
+  bf16x8 h, m, l;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    bf16 hh, mm, ll;
+    split3(k < 4 ? a[k] : b[k - 4], hh, mm, ll);
+    h[k] = hh;
+    m[k] = mm;
+    l[k] = ll;
+  }
+  planes[i] = as_u32x4(h);
+  planes[n8 + i] = as_u32x4(m);
+  planes[2 * n8 + i] = as_u32x4(l);
 }
 
 // ---------------------------------------------------------------------------
@@ -271,14 +357,16 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
   const bool lds = a.N <= kRouterChunk;
   dim3 grid((unsigned)nb), block(kRouterThreads);
   if (a.dtype == kBF16) {
+    const int64_t n8 = (int64_t)a.N * a.d / 8;
+    router_split_kernel<<<dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, st>>>(a.w_r, n8, (u32x4 *)a.planes);
     if (lds)
-      router_bf16_kernel<true><<<grid, block, 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T, a.d, a.N,
-                                                       a.logits, a.expert_idx, a.gate, a.slot, a.bcount,
-                                                       a.ppart);
+      router_bf16_kernel<true><<<grid, block, 0, st>>>((const bf16 *)a.x, (const bf16 *)a.planes, a.bias, a.T,
+                                                       a.d, a.N, a.logits, a.expert_idx, a.gate, a.slot,
+                                                       a.bcount, a.ppart);
     else
-      router_bf16_kernel<false><<<grid, block, 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T, a.d, a.N,
-                                                        a.logits, a.expert_idx, a.gate, a.slot, a.bcount,
-                                                        a.ppart);
+      router_bf16_kernel<false><<<grid, block, 0, st>>>((const bf16 *)a.x, (const bf16 *)a.planes, a.bias, a.T,
+                                                        a.d, a.N, a.logits, a.expert_idx, a.gate, a.slot,
+                                                        a.bcount, a.ppart);
   } else {
     if (lds)
       router_f32_kernel<true><<<grid, block, 0, st>>>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N,
