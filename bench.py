@@ -82,11 +82,11 @@ def read_traffic(kernel: str, digest: str):
         return None
 
 
-def cpu_baseline(inp, C: int, sample_experts: int = 16) -> dict:
-    """The CPU oracle (numpy fp64) on a bounded sample of the same workload:
-    routing, assignment and loss for all tokens, the expert FFN for a seeded
-    sample of experts, extrapolated to every expert."""
-    import numpy as np
+def cpu_baseline(inp, C: int, min_seconds: float = 10.0) -> dict:
+    """The CPU oracle (numpy fp64, as it stands) timed on this host on the same
+    workload: the whole layer forward (routing, slots, loss and every expert's
+    FFN) for all tokens, repeated until at least min_seconds have elapsed.
+    Inputs are converted to fp64 on the host before the clock starts."""
     import torch
 
     import oracle.switch_oracle as so
@@ -98,23 +98,22 @@ def cpu_baseline(inp, C: int, sample_experts: int = 16) -> dict:
         threads = os.cpu_count() or 1
     f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
     x, wr = f64(inp["x"]), f64(inp["w_router"])
+    b = None if inp["router_bias"] is None else f64(inp["router_bias"])
     N = wr.shape[0]
-    rng = np.random.default_rng(3)
-    sample = sorted(rng.choice(N, sample_experts, replace=False).tolist())
-    w = {i: (f64(inp["w_in"][i]), f64(inp["w_out"][i])) for i in sample}
-    t0 = time.perf_counter()
-    so.forward(x, wr, None, lambda i: w[i], None, C, experts=[])
-    t_route = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    so.forward(x, wr, None, lambda i: w[i], None, C, experts=sample)
-    t_both = time.perf_counter() - t0
-    t_ffn = max(t_both - t_route, 0.0) * N / len(sample)
-    total = t_route + t_ffn
+    w = [(f64(inp["w_in"][i]), f64(inp["w_out"][i])) for i in range(N)]
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        so.forward(x, wr, b, lambda i: w[i], None, C)
+        runs += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= min_seconds:
+            break
     T = x.shape[0]
-    return {"value": T / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"numpy fp64 oracle: routing, slots and loss for all {T} tokens ({t_route:.2f} s), "
-                       f"expert FFN for {len(sample)} of {N} experts ({t_both - t_route:.2f} s) "
-                       f"extrapolated to {N}; host cores available {len(os.sched_getaffinity(0))}")}
+    per = elapsed / runs
+    return {"value": T / per, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"numpy fp64 oracle, whole layer forward on the full workload ({T} tokens, all {N} "
+                       f"experts), {runs} run(s) in {elapsed:.1f} s ({per:.2f} s each); BLAS threads "
+                       f"{threads}, host cores available {len(os.sched_getaffinity(0))}")}
 
 
 def main() -> int:
@@ -124,6 +123,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", default="base", help="workload (the metric is quoted on 'base')")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -217,6 +218,14 @@ def main() -> int:
         "kernels": per_kernel,
         "wall_s_timed": round(t_wall, 4),
     }
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(inp, C)

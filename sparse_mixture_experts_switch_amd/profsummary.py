@@ -1,0 +1,127 @@
+"""Text summaries of rocprofv3 runs (rocpd SQLite output) for profiles/.
+
+    python -m sparse_mixture_experts_switch_amd.profsummary trace DB OUT --cmd "..."
+        per-kernel dispatch count and average / min / max duration
+    python -m sparse_mixture_experts_switch_amd.profsummary traffic FETCH_DB WRITE_DB OUT \
+        --kernel NAME --cmd "..." --source FILE
+        HBM bytes per launch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB
+        per dispatch), each scaled by what the same counter reads for a plain
+        1 GiB device-to-device copy recorded in the same run
+
+Kernel names are the library's launch names: ffn_up / ffn_down are the
+grouped-GEMM instantiations that gather token rows (ReLU epilogue) and that
+scatter through the combine epilogue.
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import hashlib
+import sqlite3
+
+COPY_BYTES = 1 << 30
+KERNEL_KEYS = {
+    "ffn_up": ("ffn_gemm_bf16_kernel", "Lb1ELi0E"),
+    "ffn_down": ("ffn_gemm_bf16_kernel", "Lb0ELi2E"),
+    "router": ("router_bf16_kernel", ""),
+    "router_split": ("router_split_kernel", ""),
+    "assign_scan": ("assign_scan_kernel", ""),
+    "assign_apply": ("assign_apply_layer_kernel", ""),
+    "copy": ("__amd_rocclr_copyBuffer", ""),
+}
+
+
+def short_name(full: str) -> str:
+    for short, (a, b) in KERNEL_KEYS.items():
+        if a in full and b in full:
+            return short
+    return full[:60]
+
+
+def _trace(db_path: str):
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, start, end from kernels").fetchall()
+    agg = collections.defaultdict(list)
+    for name, s, e in rows:
+        agg[name].append((e - s) / 1e3)
+    return agg
+
+
+def _counter(db_path: str, counter: str):
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                      (counter,)).fetchall()
+    agg = collections.defaultdict(list)
+    for name, v in rows:
+        agg[name].append(float(v))
+    return agg
+
+
+def trace_summary(db: str, cmd: str) -> str:
+    agg = _trace(db)
+    lines = [f"# rocprofv3 kernel trace summary", f"# command: {cmd}",
+             "# kernel | dispatches | avg_us | min_us | max_us | full name"]
+    for name, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{short_name(name)} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | {name[:160]}")
+    return "\n".join(lines) + "\n"
+
+
+def traffic_summary(fetch_db: str, write_db: str, kernel: str, cmd: str, source: str) -> str:
+    fetch, write = _counter(fetch_db, "FETCH_SIZE"), _counter(write_db, "WRITE_SIZE")
+
+    def pick(agg, short):
+        vals = [v for name, vs in agg.items() if short_name(name) == short for v in vs]
+        return vals
+
+    kf, kw = pick(fetch, kernel), pick(write, kernel)
+    cf, cw = pick(fetch, "copy"), pick(write, "copy")
+    if not kf or not kw or not cf or not cw:
+        raise SystemExit(f"missing dispatches: kernel fetch {len(kf)} write {len(kw)}, copy {len(cf)} {len(cw)}")
+    fetch_factor = COPY_BYTES / (max(cf) * 1024.0)
+    write_factor = COPY_BYTES / (max(cw) * 1024.0)
+    f_kib, w_kib = sum(kf) / len(kf), sum(kw) / len(kw)
+    hbm = f_kib * 1024.0 * fetch_factor + w_kib * 1024.0 * write_factor
+    with open(source, "rb") as fh:
+        digest = hashlib.sha256(fh.read()).hexdigest()[:16]
+    return "\n".join([
+        f"# HBM traffic of {kernel} (base workload), rocprofv3 --pmc",
+        f"# command (FETCH_SIZE pass): {cmd.replace('COUNTER', 'FETCH_SIZE')}",
+        f"# command (WRITE_SIZE pass): {cmd.replace('COUNTER', 'WRITE_SIZE')}",
+        f"# calibration: a 1 GiB device-to-device copy in the same run reads {max(cf):.0f} KiB FETCH_SIZE",
+        f"#   and {max(cw):.0f} KiB WRITE_SIZE; factors = true bytes / counter bytes",
+        f"kernel = {kernel}",
+        f"source_sha256 = {digest}",
+        f"dispatches = {len(kf)}",
+        f"fetch_kib_per_dispatch = {f_kib:.1f}",
+        f"write_kib_per_dispatch = {w_kib:.1f}",
+        f"fetch_factor = {fetch_factor:.4f}",
+        f"write_factor = {write_factor:.4f}",
+        f"hbm_bytes_per_launch = {hbm:.0f}",
+    ]) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("out")
+    t.add_argument("--cmd", required=True)
+    c = sub.add_parser("traffic")
+    c.add_argument("fetch_db")
+    c.add_argument("write_db")
+    c.add_argument("out")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--source", required=True)
+    a = ap.parse_args()
+    text = trace_summary(a.db, a.cmd) if a.mode == "trace" else traffic_summary(
+        a.fetch_db, a.write_db, a.kernel, a.cmd, a.source)
+    with open(a.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()
