@@ -56,7 +56,7 @@ int esize(int dtype) { return dtype == SWITCH_BF16 ? 2 : 4; }
 struct Layout {
   size_t bcount = 0, ppart = 0, psum = 0, logits = 0, planes = 0, route_end = 0;
   size_t ffn_hidden = 0, ffn_end = 0;                             // switch_expert_ffn alone
-  size_t lf_hidden = 0, lf_tok = 0, total = 0;                  // layer forward
+  size_t lf_hidden = 0, lf_tok = 0, lf_gmap = 0, total = 0;     // layer forward
 };
 
 int check_shape(const switch_shape *s) {
@@ -101,6 +101,8 @@ int layout(const switch_shape *s, Layout &L) {
   L.lf_hidden = o;
   o = align_up(o + hid);
   L.lf_tok = o;
+  o = align_up(o + tk);
+  L.lf_gmap = o;
   o = align_up(o + tk);
   L.total = o;
   return SWITCH_OK;
@@ -195,14 +197,14 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
 
 // Routing kernels.  With tok set (layer path) the apply step also fills the
 // slot -> token map and the output rows of dropped tokens.
-int run_route(const RouteArgs &a, hipStream_t st, Timer &tm, int32_t *tok = nullptr, const void *xres = nullptr,
-              void *y = nullptr) {
+int run_route(const RouteArgs &a, hipStream_t st, Timer &tm, int32_t *tok = nullptr, float *gmap = nullptr,
+              const void *xres = nullptr, void *y = nullptr) {
   hipError_t e;
   if ((e = launch_router(a, st)) != hipSuccess) return hip_fail(e, "router launch");
   tm.mark(kKernelNames[0]);
   if ((e = launch_assign_scan(a, st)) != hipSuccess) return hip_fail(e, "assign_scan launch");
   tm.mark(kKernelNames[1]);
-  e = tok ? launch_assign_apply_layer(a, tok, xres, y, st) : launch_assign_apply(a, st);
+  e = tok ? launch_assign_apply_layer(a, tok, gmap, xres, y, st) : launch_assign_apply(a, st);
   if (e != hipSuccess) return hip_fail(e, "assign_apply launch");
   tm.mark(kKernelNames[2]);
   return SWITCH_OK;
@@ -233,15 +235,16 @@ int layer_forward(const switch_shape *s, const void *x, const float *w_router, c
     if ((tm.err = hipEventRecord(tm.ev[0], st)) != hipSuccess) return hip_fail(tm.err, "hipEventRecord");
   }
   int32_t *tok = (int32_t *)(w + L.lf_tok);
+  float *gmap = (float *)(w + L.lf_gmap);
   const void *xres = add_residual ? x : nullptr;
-  if ((rc = run_route(ra, st, tm, tok, xres, y))) return rc;
+  if ((rc = run_route(ra, st, tm, tok, gmap, xres, y))) return rc;
   hipError_t e;
   GemmCall up{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w + L.lf_hidden,
-              expert_count, tok, nullptr, nullptr};
+              expert_count, tok, nullptr, nullptr, nullptr};
   if ((e = launch_ffn_up_gather(up, st)) != hipSuccess) return hip_fail(e, "ffn_up launch");
   tm.mark(kKernelNames[3]);
   GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, y,
-                expert_count, tok, gate, xres};
+                expert_count, tok, gate, gmap, xres};
   if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
   tm.mark(kKernelNames[4]);
   return SWITCH_OK;

@@ -121,14 +121,16 @@ __global__ __launch_bounds__(256) void assign_apply_kernel(
 }
 
 // Layer path variant of the apply step: besides slot and dropped it records
-// which token sits in each live slot (tok[e][slot] = t) for the expert FFN to
-// gather from and scatter to, and writes the output rows of dropped tokens
-// (their computation is skipped: 0, or x when a residual is added).
+// which token sits in each live slot (tok[e][slot] = t) and its gate
+// (gmap[e][slot]) for the expert FFN to gather from and scatter to, and
+// writes the output rows of dropped tokens (their computation is skipped: 0,
+// or x when a residual is added).
 __global__ __launch_bounds__(256) void assign_apply_layer_kernel(
     const int32_t *__restrict__ expert_idx, int32_t *__restrict__ slot, uint8_t *__restrict__ dropped,
     const int32_t *__restrict__ boff, int64_t T, int N, int C, const int32_t *__restrict__ expert_count,
     const float *__restrict__ psum, float *__restrict__ aux_loss, int32_t *__restrict__ tok,
-    const u32x4 *__restrict__ xres, u32x4 *__restrict__ y, int row16) {
+    float *__restrict__ gmap, const float *__restrict__ gate, const u32x4 *__restrict__ xres,
+    u32x4 *__restrict__ y, int row16) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int lane = threadIdx.x % kWave;
   bool drop = false;
@@ -138,7 +140,10 @@ __global__ __launch_bounds__(256) void assign_apply_layer_kernel(
     slot[t] = s;
     drop = s >= C;
     dropped[t] = drop ? 1 : 0;
-    if (!drop) tok[(int64_t)e * C + s] = (int32_t)t;
+    if (!drop) {
+      tok[(int64_t)e * C + s] = (int32_t)t;
+      gmap[(int64_t)e * C + s] = gate[t];
+    }
   }
   unsigned long long mask = __ballot(drop);
   while (mask) {
@@ -174,13 +179,13 @@ hipError_t launch_assign_apply(const RouteArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_assign_apply_layer(const RouteArgs &a, int32_t *tok, const void *xres, void *y,
+hipError_t launch_assign_apply_layer(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y,
                                      hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const int row16 = a.d * (a.dtype == kBF16 ? 2 : 4) / 16;
   assign_apply_layer_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
-      a.expert_idx, a.slot, a.dropped, a.bcount, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss, tok,
-      (const u32x4 *)xres, (u32x4 *)y, row16);
+      a.expert_idx, a.slot, a.dropped, a.bcount, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss, tok, gmap,
+      a.gate, (const u32x4 *)xres, (u32x4 *)y, row16);
   return hipGetLastError();
 }
 

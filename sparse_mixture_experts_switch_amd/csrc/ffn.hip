@@ -46,7 +46,8 @@ struct GemmArgs {
   T_ *Out;              // [N][C][Nout], or y [T][Nout] for the combine epilogue
   const int32_t *counts;
   const int32_t *tok;   // [N][C] token of each live slot (gather / combine)
-  const float *gate;    // [T] (combine)
+  const float *gate;    // [T] (combine, fp32 path)
+  const float *gmap;    // [N][C] gate of the token in each live slot (combine, bf16 path)
   const T_ *xres;       // [T][Nout] residual rows (combine), or null
   int C, K, Nout, m_tiles, n_tiles, ntiles;
 };
@@ -60,174 +61,251 @@ __device__ __forceinline__ int xcd_tile(int b, int grid) {
   return (b % 8) * per + b / 8;
 }
 
-// bf16 grouped GEMM on v_mfma_f32_16x16x32_bf16.
-// MB: 16-row blocks per workgroup; NBW: 16-column blocks per wave;
-// WAVES: waves per workgroup (workgroup columns = WAVES * 16 * NBW);
-// DEPTH: register ring of contraction chunks in flight.
-// Operand layout: lane l supplies row (l % 16) and 8 consecutive k starting
-// at 8 * (l / 16); result lane l holds column (l % 16), rows 4 * (l / 16) + i.
-template <int MB, int NBW, int DEPTH, int WAVES, bool kGather, int kEpi>
+// bf16 grouped GEMM on v_mfma_f32_16x16x32_bf16, persistent.
+//
+// A workgroup stays resident and walks a list of tiles (one expert's live
+// rows [m0, m0 + mrows) x kCols output features).  XCD x (= blockIdx % 8,
+// workgroups are dealt to the 8 XCDs round-robin) owns a contiguous range of
+// tiles, so the tiles of one expert run together on one XCD and share its L2
+// for the expert's activation rows; empty tiles are skipped.
+//
+// The contraction runs in 64-column chunks.  Weight rows stream from global
+// memory straight into MFMA operand registers through a two-chunk register
+// ring; activation rows pass through a double-buffered padded LDS tile.  The
+// ring runs on across tile boundaries: the next tile's first chunks are in
+// flight while the current tile finishes and while its results are written,
+// so a tile change costs no pipeline refill.
+//
+// MB: 16-row blocks per tile; NBW: 16-column blocks per wave; WAVES: waves
+// per workgroup (kCols = WAVES * 16 * NBW).  Operand layout: lane l supplies
+// row (l % 16) and 8 consecutive k starting at 8 * (l / 16); result lane l
+// holds column (l % 16), rows 4 * (l / 16) + i.
+template <int MB, int NBW, int WAVES, bool kGather, int kEpi>
 __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArgs<bf16> p) {
-  constexpr int kFfnThreads = WAVES * 64;
+  constexpr int kThreads = WAVES * 64;
   constexpr int kRows = MB * 16;
   constexpr int kCols = WAVES * NBW * 16;
   constexpr int kAChunks = kRows * (kKC / 8);  // 16-byte pieces of one A chunk
-  constexpr int kAPer = (kAChunks + kFfnThreads - 1) / kFfnThreads;
-  constexpr int kABytes = 2 * kRows * kLdsStride * 2;
-  constexpr int kEStride = NBW * 16 + 4;  // fp32 staging row (per wave)
-  constexpr int kEBytes = WAVES * 16 * kEStride * 4;
-  constexpr int kSmem = kABytes > kEBytes ? kABytes : kEBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
-  __shared__ int s_tok[kRows];
-  __shared__ float s_gate[kRows];
-  bf16 *sA = (bf16 *)smem;
+  constexpr int kAPer = (kAChunks + kThreads - 1) / kThreads;
+  constexpr int kAStage = kRows * kLdsStride;  // bf16 per LDS buffer
+  constexpr int kEStride = NBW * 16 + 4;       // fp32 staging row (per wave)
+  constexpr int kPieces = NBW * 2;             // 8-column pieces per staged row
+  constexpr bool kTok = kGather || kEpi == kEpiCombine;
+  static_assert(kRows <= kThreads, "one row per thread for the tile's token map");
+  __shared__ __attribute__((aligned(16))) bf16 sA[2 * kAStage];
+  __shared__ __attribute__((aligned(16))) float sStage[WAVES * 16 * kEStride];
+  __shared__ int s_tok[2][kRows];
+  __shared__ float s_gate[2][kRows];
 
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  if (tile >= p.ntiles) return;
-  const int e = tile / (p.m_tiles * p.n_tiles);
-  const int rem = tile % (p.m_tiles * p.n_tiles);
-  const int mt = rem / p.n_tiles, nt = rem % p.n_tiles;
-  const int M = min(p.counts[e], p.C);
-  const int m0 = mt * kRows;
-  if (m0 >= M) return;
-  const int mrows = min(kRows, M - m0);
-  const int amb = (mrows + 15) / 16;
-  const int K = p.K, Nout = p.Nout;
-
+  const int K = p.K, Nout = p.Nout, C = p.C;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int r16 = lane % 16, kq = (lane / 16) * 8;
-  const int ncol0 = nt * kCols + wave * NBW * 16;
+  const int nch = K / kKC;
+  const int nchp = nch + (nch & 1);  // chunks per tile, padded to the ring depth
 
-  if (kGather || kEpi == kEpiCombine) {
-    for (int r = tid; r < mrows; r += kFfnThreads) {
-      const int t = p.tok[(int64_t)e * p.C + m0 + r];
-      s_tok[r] = t;
-      if (kEpi == kEpiCombine) s_gate[r] = p.gate[t];
+  // ---- tile schedule (uniform) ----
+  const int g8 = gridDim.x / 8, xcd = blockIdx.x % 8, lid = blockIdx.x / 8;
+  const int per = (p.ntiles + 7) / 8;
+  const int t_end = min(p.ntiles, (xcd + 1) * per);
+  int t_next = xcd * per + lid;
+  struct Tile {
+    int e, m0, n0, mrows;
+  };
+  auto next_tile = [&](Tile &t) -> bool {
+    while (t_next < t_end) {
+      const int id = t_next;
+      t_next += g8;
+      const int e = id / (p.m_tiles * p.n_tiles);
+      const int rem = id % (p.m_tiles * p.n_tiles);
+      const int m0 = (rem / p.n_tiles) * kRows;
+      const int M = min(p.counts[e], C);
+      if (m0 < M) {
+        t.e = e;
+        t.m0 = m0;
+        t.n0 = (rem % p.n_tiles) * kCols;
+        t.mrows = min(kRows, M - m0);
+        return true;
+      }
     }
-    __syncthreads();
-  }
+    return false;
+  };
 
-  // Weight rows of this wave (rows past Nout read row 0; never stored).
-  const bf16 *bp[NBW];
-  bool bval[NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int n = ncol0 + nb * 16 + r16;
-    bval[nb] = n < Nout;
-    bp[nb] = p.B + ((int64_t)e * Nout + (bval[nb] ? n : 0)) * K + kq;
-  }
-  // Activation pieces this thread moves into LDS: row ar[q], 8 columns at
-  // ac[q].  Rows past the live ones re-read the last live row, so that every
-  // lane always loads (no divergent branches around the loads: the compiler
-  // can then count outstanding loads exactly and keep the prefetch in flight).
-  const bf16 *asrc[kAPer];
-  int aoff[kAPer];
+  // ---- per-lane pieces of the activation chunk: row ar[q], columns ac[q] ----
+  int ar[kAPer], aoff[kAPer];
 #pragma unroll
   for (int q = 0; q < kAPer; ++q) {
-    const int i = (tid + q * kFfnThreads) % kAChunks;
-    const int r = i / (kKC / 8), c = i % (kKC / 8);
-    const int rr = min(r, mrows - 1);
-    asrc[q] = (kGather ? p.A + (int64_t)s_tok[rr] * K : p.A + ((int64_t)e * p.C + m0 + rr) * K) + c * 8;
-    aoff[q] = r * kLdsStride + c * 8;
+    const int i = (tid + q * kThreads) % kAChunks;
+    ar[q] = i / (kKC / 8);
+    aoff[q] = ar[q] * kLdsStride + (i % (kKC / 8)) * 8;
   }
+  // Token of each of this lane's activation rows, for the current and the
+  // next tile (gather); rows past the live ones re-read the last live row so
+  // that every lane always loads (branch-free loads keep the ring counted).
+  int atok[2][kAPer];
+  auto load_atok = [&](int which, const Tile &t) {
+#pragma unroll
+    for (int q = 0; q < kAPer; ++q) atok[which][q] = p.tok[(int64_t)t.e * C + t.m0 + min(ar[q], t.mrows - 1)];
+  };
+  // Token and gate of row `tid` of a tile (combine epilogue).
+  int ttok = 0;
+  float tgate = 0.f;
+  auto load_rowinfo = [&](const Tile &t) {
+    const int64_t sl = (int64_t)t.e * C + t.m0 + min(tid, t.mrows - 1);
+    ttok = p.tok[sl];
+    if (kEpi == kEpiCombine) tgate = p.gmap[sl];
+  };
+
+  Tile cur, nxt;
+  if (!next_tile(cur)) return;
+  bool have_nxt = next_tile(nxt);
 
   f32x4 acc[MB][NBW];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nch = K / kKC;
-  u32x4 areg[DEPTH][kAPer];
-  u32x4 breg[DEPTH][2][NBW];
-  // Loads of chunk `ch` (clamped to the last chunk past the end: re-reads
-  // that hit in cache and are never consumed).
-  auto fetch = [&](int slot, int ch) {
+  u32x4 areg[2][kAPer];
+  u32x4 breg[2][2][NBW];
+  // Loads of chunk `ch` of tile t (clamped to the tile's last chunk past its
+  // end: re-reads that hit in cache and are never consumed).  Activation rows
+  // are issued first: loads complete in issue order, and the activations are
+  // needed one iteration before the weights.
+  auto fetch = [&](int slot, const Tile &t, int which, int ch) {
     const int k0 = min(ch, nch - 1) * kKC;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int q = 0; q < kAPer; ++q) {
+      const int64_t row = kGather ? (int64_t)atok[which][q] : (int64_t)t.e * C + t.m0 + min(ar[q], t.mrows - 1);
+      areg[slot][q] = *(const u32x4 *)(p.A + row * K + (aoff[q] % kLdsStride) + k0);
+    }
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) breg[slot][s][nb] = *(const u32x4 *)(bp[nb] + k0 + s * 32);
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int n = min(t.n0 + wave * NBW * 16 + nb * 16 + r16, Nout - 1);
+      const bf16 *bp = p.B + ((int64_t)t.e * Nout + n) * K + kq + k0;
 #pragma unroll
-    for (int q = 0; q < kAPer; ++q) areg[slot][q] = *(const u32x4 *)(asrc[q] + k0);
+      for (int s = 0; s < 2; ++s) breg[slot][s][nb] = *(const u32x4 *)(bp + s * 32);
+    }
   };
   auto store_a = [&](int slot, int buf) {
 #pragma unroll
-    for (int q = 0; q < kAPer; ++q) *(u32x4 *)(&sA[buf * kRows * kLdsStride + aoff[q]]) = areg[slot][q];
+    for (int q = 0; q < kAPer; ++q) *(u32x4 *)(&sA[buf * kAStage + aoff[q]]) = areg[slot][q];
   };
 
-#pragma unroll
-  for (int j = 0; j < DEPTH; ++j) fetch(j, j);
+  // ---- prologue: token maps of the first two tiles, first two chunks ----
+  int cb = 0;  // s_tok / s_gate buffer of the current tile
+  if (kGather) {
+    load_atok(0, cur);
+    if (have_nxt) load_atok(1, nxt);
+  }
+  if (kTok) {
+    load_rowinfo(cur);
+    if (tid < kRows) {  // rows past mrows hold a valid copy of the last live row
+      s_tok[0][tid] = ttok;
+      if (kEpi == kEpiCombine) s_gate[0][tid] = tgate;
+    }
+    if (have_nxt) load_rowinfo(nxt);
+  }
+  fetch(0, cur, 0, 0);
+  fetch(1, cur, 0, 1);
   store_a(0, 0);
   __syncthreads();
-  for (int base = 0; base < nch; base += DEPTH) {
-#pragma clang loop unroll(full)
-    for (int j = 0; j < DEPTH; ++j) {
-      const int ch = base + j;
-      if (ch < nch) {
-        const bf16 *abuf = sA + (ch & 1) * kRows * kLdsStride;
-#pragma clang loop unroll(full)
-        for (int s = 0; s < 2; ++s) {
-          // every row block runs: rows past the live ones hold copies of the
-          // last live row and are never stored (straight-line MFMA stream;
-          // the kernel is bound by the weight stream, not by MFMA)
-#pragma clang loop unroll(full)
-          for (int mb = 0; mb < MB; ++mb) {
-            const bf16x8 a = as_bf16x8(*(const u32x4 *)(&abuf[(mb * 16 + r16) * kLdsStride + s * 32 + kq]));
+
+  while (true) {
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-              acc[mb][nb] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(breg[j][s][nb]), acc[mb][nb], 0, 0, 0);
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int base = 0; base < nchp; base += 2) {
+#pragma clang loop unroll(full)
+      for (int j = 0; j < 2; ++j) {
+        const int ch = base + j;
+        if (ch < nch) {
+          const bf16 *abuf = sA + j * kAStage;
+#pragma clang loop unroll(full)
+          for (int s = 0; s < 2; ++s) {
+            // every row block runs: rows past the live ones hold copies of
+            // the last live row and are never stored (straight-line MFMA
+            // stream; the kernel is bound by the weight stream)
+#pragma clang loop unroll(full)
+            for (int mb = 0; mb < MB; ++mb) {
+              const bf16x8 a = as_bf16x8(*(const u32x4 *)(&abuf[(mb * 16 + r16) * kLdsStride + s * 32 + kq]));
+#pragma unroll
+              for (int nb = 0; nb < NBW; ++nb)
+                acc[mb][nb] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(breg[j][s][nb]), acc[mb][nb], 0, 0, 0);
+            }
+          }
+        }
+        // refill this ring slot two chunks ahead (the next tile's first
+        // chunks once this tile's run out), then move the next chunk's
+        // activations into the other LDS buffer
+        if (ch + 2 < nchp || !have_nxt)
+          fetch(j, cur, 0, ch + 2);
+        else
+          fetch(j, nxt, 1, ch + 2 - nchp);
+        store_a(j ^ 1, j ^ 1);
+        __syncthreads();
+      }
+    }
+
+    // ---- epilogue of `cur`: each wave stages 16-row blocks of its columns
+    // in its own LDS region and writes whole 16-byte row pieces ----
+    float *stg = sStage + wave * 16 * kEStride;
+    const int ncol0 = cur.n0 + wave * NBW * 16;
+#pragma clang loop unroll(full)
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb * 16 >= cur.mrows) continue;
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stg[((lane / 16) * 4 + i) * kEStride + nb * 16 + r16] = acc[mb][nb][i];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes landed
+      __builtin_amdgcn_wave_barrier();
+      for (int c = lane; c < 16 * kPieces; c += kWave) {
+        const int rr = c / kPieces, pc = c % kPieces;
+        const int m = mb * 16 + rr;
+        const int n = ncol0 + pc * 8;
+        if (m < cur.mrows && n < Nout) {
+          const f32x4 v0 = *(const f32x4 *)&stg[rr * kEStride + pc * 8];
+          const f32x4 v1 = *(const f32x4 *)&stg[rr * kEStride + pc * 8 + 4];
+          const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          bf16x8 o;
+          if (kEpi == kEpiCombine) {
+            const int t = s_tok[cb][m];
+            const float g = s_gate[cb][m];
+            bf16x8 xv{};
+            if (p.xres) xv = as_bf16x8(*(const u32x4 *)(p.xres + (int64_t)t * Nout + n));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (bf16)(p.xres ? (float)xv[i] + g * v[i] : g * v[i]);
+            *(u32x4 *)(p.Out + (int64_t)t * Nout + n) = as_u32x4(o);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (bf16)(kEpi == kEpiRelu ? fmaxf(v[i], 0.f) : v[i]);
+            *(u32x4 *)(p.Out + ((int64_t)cur.e * C + cur.m0 + m) * Nout + n) = as_u32x4(o);
           }
         }
       }
-      // refill this ring slot DEPTH chunks ahead, then move the next chunk's
-      // activations into the other LDS buffer (its readers finished at the
-      // previous barrier)
-      fetch(j, ch + DEPTH);
-      store_a((j + 1) % DEPTH, (ch + 1) & 1);
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // staging reads done before the next block overwrites
+      __builtin_amdgcn_wave_barrier();
     }
-  }
 
-  // Epilogue: per 16-row block, each wave stages its 16 x (16 NBW) fp32 tile
-  // in LDS, then writes whole 16-byte row pieces.
-  float *stg = (float *)smem + wave * 16 * kEStride;
-  constexpr int kPieces = NBW * 2;  // 8-column pieces per staged row
-  // fully unrolled so that acc is only ever indexed by constants
-#pragma clang loop unroll(full)
-  for (int mb = 0; mb < MB; ++mb) {
-    if (mb >= amb) continue;
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) stg[((lane / 16) * 4 + i) * kEStride + nb * 16 + r16] = acc[mb][nb][i];
-    __syncthreads();
-    for (int c = lane; c < 16 * kPieces; c += kWave) {
-      const int rr = c / kPieces, pc = c % kPieces;
-      const int m = mb * 16 + rr;
-      const int n = ncol0 + pc * 8;
-      if (m < mrows && n < Nout) {
-        const f32x4 v0 = *(const f32x4 *)&stg[rr * kEStride + pc * 8];
-        const f32x4 v1 = *(const f32x4 *)&stg[rr * kEStride + pc * 8 + 4];
-        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        bf16x8 o;
-        if (kEpi == kEpiCombine) {
-          const int t = s_tok[m];
-          const float g = s_gate[m];
-          bf16x8 xv{};
-          if (p.xres) xv = as_bf16x8(*(const u32x4 *)(p.xres + (int64_t)t * Nout + n));
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = (bf16)(p.xres ? (float)xv[i] + g * v[i] : g * v[i]);
-          *(u32x4 *)(p.Out + (int64_t)t * Nout + n) = as_u32x4(o);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = (bf16)(kEpi == kEpiRelu ? fmaxf(v[i], 0.f) : v[i]);
-          *(u32x4 *)(p.Out + ((int64_t)e * p.C + m0 + m) * Nout + n) = as_u32x4(o);
-        }
+    if (!have_nxt) break;
+    // ---- advance: nxt becomes cur; look up the tile after it ----
+    cur = nxt;
+    cb ^= 1;
+    if (kTok) {
+      // rowinfo of the new cur was loaded a whole tile ago; publish it (the
+      // next barrier, inside the first chunk, makes it visible)
+      if (tid < kRows) {
+        s_tok[cb][tid] = ttok;
+        if (kEpi == kEpiCombine) s_gate[cb][tid] = tgate;
       }
     }
-    __syncthreads();
+    if (kGather) {
+#pragma unroll
+      for (int q = 0; q < kAPer; ++q) atok[0][q] = atok[1][q];
+    }
+    have_nxt = next_tile(nxt);
+    if (have_nxt) {
+      if (kGather) load_atok(1, nxt);
+      if (kTok) load_rowinfo(nxt);
+    }
   }
 }
 
@@ -327,6 +405,7 @@ GemmArgs<T_> make_args(const GemmCall &c, int rows, int cols) {
   g.counts = c.counts;
   g.tok = c.tok;
   g.gate = c.gate;
+  g.gmap = c.gmap;
   g.xres = (const T_ *)c.xres;
   g.C = c.C;
   g.K = c.K;
@@ -341,14 +420,25 @@ inline unsigned grid_of(int ntiles) { return (unsigned)(ceil_div(ntiles, 8) * 8)
 
 // Tile shape (measured on MI355X for the weight-streaming regime): every
 // live row of the expert (up to 160) x 384 output features per workgroup of
-// 8 waves (3 column blocks each), two contraction chunks in flight.
-constexpr int kNBW = 3, kWaves = 8, kDepth = 2;
+// 8 waves (3 column blocks each).
+constexpr int kNBW = 3, kWaves = 8;
+
+// Resident workgroups for a persistent launch: CUs x workgroups per CU.
+template <typename Kern>
+unsigned persistent_grid(Kern kern, int ntiles) {
+  int dev = 0, cus = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kWaves * 64, 0) != hipSuccess || occ < 1) occ = 1;
+  const int64_t want = std::min<int64_t>((int64_t)cus * occ, ceil_div(ntiles, 8) * 8);
+  return (unsigned)std::max<int64_t>(8, ceil_div(want, 8) * 8);
+}
 
 template <int MB, bool kGather, int kEpi>
 hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
   auto g = make_args<bf16>(c, MB * 16, kWaves * 16 * kNBW);
-  ffn_gemm_bf16_kernel<MB, kNBW, kDepth, kWaves, kGather, kEpi>
-      <<<dim3(grid_of(g.ntiles)), dim3(kWaves * 64), 0, st>>>(g);
+  auto kern = ffn_gemm_bf16_kernel<MB, kNBW, kWaves, kGather, kEpi>;
+  kern<<<dim3(persistent_grid(kern, g.ntiles)), dim3(kWaves * 64), 0, st>>>(g);
   return hipGetLastError();
 }
 
@@ -375,13 +465,13 @@ hipError_t gemm(const GemmCall &c, hipStream_t st) {
 // Stage call: dispatched buffer -> H -> expert_out buffer.
 hipError_t launch_ffn_up(const FfnArgs &a, hipStream_t st) {
   GemmCall c{a.dtype, a.N, a.C, a.d, a.dff, a.dispatched, a.w_in, a.hidden, a.expert_count,
-             nullptr, nullptr, nullptr};
+             nullptr, nullptr, nullptr, nullptr};
   return gemm<false, kEpiRelu>(c, st);
 }
 
 hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st) {
   GemmCall c{a.dtype, a.N, a.C, a.dff, a.d, a.hidden, a.w_out, a.expert_out, a.expert_count,
-             nullptr, nullptr, nullptr};
+             nullptr, nullptr, nullptr, nullptr};
   return gemm<false, kEpiPlain>(c, st);
 }
 

@@ -73,7 +73,8 @@ struct GemmCall {
   void *Out;      // [N][C][Nout] buffer, or y [T][Nout] for the combine epilogue
   const int32_t *counts;
   const int32_t *tok;  // [N][C]: token in each live slot (gather / combine)
-  const float *gate;   // [T] (combine)
+  const float *gate;   // [T] (combine, fp32 path)
+  const float *gmap;   // [N][C]: gate of the token in each live slot (combine)
   const void *xres;    // [T][Nout] residual rows (combine), may be null
 };
 
@@ -81,9 +82,10 @@ struct GemmCall {
 hipError_t launch_router(const RouteArgs &a, hipStream_t st);
 hipError_t launch_assign_scan(const RouteArgs &a, hipStream_t st);
 hipError_t launch_assign_apply(const RouteArgs &a, hipStream_t st);
-// Layer path: also records tok[e][slot] = t for kept tokens and writes the
-// y rows of dropped tokens (0, or x with a residual).
-hipError_t launch_assign_apply_layer(const RouteArgs &a, int32_t *tok, const void *xres, void *y,
+// Layer path: also records tok[e][slot] = t and gmap[e][slot] = gate[t] for
+// kept tokens and writes the y rows of dropped tokens (0, or x with a
+// residual).
+hipError_t launch_assign_apply_layer(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y,
                                      hipStream_t st);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st);
 hipError_t launch_ffn_up(const FfnArgs &a, hipStream_t st);
