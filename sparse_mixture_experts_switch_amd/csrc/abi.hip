@@ -54,7 +54,7 @@ bool mul(size_t &out, std::initializer_list<int64_t> xs) {
 int esize(int dtype) { return dtype == SWITCH_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t bcount = 0, ppart = 0, psum = 0, logits = 0, planes = 0, route_end = 0;
+  size_t bcount = 0, ppart = 0, psum = 0, logits = 0, route_end = 0;
   size_t ffn_hidden = 0, ffn_end = 0;                             // switch_expert_ffn alone
   size_t lf_hidden = 0, lf_tok = 0, lf_gmap = 0, total = 0;     // layer forward
 };
@@ -78,9 +78,8 @@ int layout(const switch_shape *s, Layout &L) {
   const int64_t T = s->tokens, N = s->num_experts, C = s->capacity, d = s->d_model, f = s->d_ff;
   const int64_t nb = router_blocks(T);
   const int es = esize(s->dtype);
-  size_t bc, pp, ps, lg = 0, pl = 0, hid, act, tk;
+  size_t bc, pp, ps, lg = 0, hid, act, tk;
   bool ok = mul(bc, {nb, N, 4}) && mul(pp, {nb, N, 4}) && mul(ps, {N, 4}) &&
-            (s->dtype != SWITCH_BF16 || mul(pl, {3, N, d, 2})) &&
             (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(hid, {N, C, f, es}) && mul(act, {N, C, d, es}) &&
             mul(tk, {N, C, 4});
   if (!ok) return fail(SWITCH_E_UNSUPPORTED, "buffer sizes overflow for this shape");
@@ -93,8 +92,6 @@ int layout(const switch_shape *s, Layout &L) {
   o = align_up(o + ps);
   L.logits = o;
   o = align_up(o + lg);
-  L.planes = o;
-  o = align_up(o + pl);
   L.route_end = o;
   L.ffn_hidden = 0;
   L.ffn_end = align_up(hid);
@@ -182,7 +179,6 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
   a.w_r = w_router;
   a.bias = router_bias;
   a.logits = (float *)(w + L.logits);
-  a.planes = w + L.planes;
   a.expert_idx = expert_idx;
   a.gate = gate;
   a.slot = slot;

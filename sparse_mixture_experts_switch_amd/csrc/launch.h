@@ -20,7 +20,6 @@ struct RouteArgs {
   const void *x;
   const float *w_r, *bias;
   float *logits;  // [T][N] scratch, only used when N > kRouterChunk
-  void *planes;   // [3][N][d] bf16 scratch: W_r split into hi/mid/lo planes
   int32_t *expert_idx;
   float *gate;
   int32_t *slot;  // in-block rank after the router, slot after assignment

@@ -19,9 +19,9 @@
 //
 // bf16 activations: the contraction runs on bf16 MFMA.  W_r (fp32) is split
 // exactly into three bf16 planes hi + mid + lo (each plane takes the next 8
-// significant bits; a small kernel does it once per call), so every product
-// x_k * plane_k is exact in fp32 and the fp32 accumulation sees the same
-// terms as an fp32 dot product.
+// significant bits; every block splits the fp32 rows as it stages them), so
+// every product x_k * plane_k is exact in fp32 and the fp32 accumulation sees
+// the same terms as an fp32 dot product.
 // fp32 activations: plain fp32 FMA on the vector ALUs.
 
 #include "common.h"
@@ -29,13 +29,32 @@
 
 namespace smx {
 
-// Exact split of an fp32 value into three bf16 values whose sum is the value.
-__device__ __forceinline__ void split3(float w, bf16 &hi, bf16 &mid, bf16 &lo) {
-  hi = (bf16)w;
-  float r1 = w - (float)hi;
-  mid = (bf16)r1;
-  float r2 = r1 - (float)mid;
-  lo = (bf16)r2;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Exact split of two fp32 values into three bf16 pairs whose sums are the
+// values: hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid), each
+// conversion rounding to nearest even (both differences are exact in fp32).
+// Each result holds the pair packed as two bf16 (first value in the low half).
+__device__ __forceinline__ void split3_pair(f32x2 w, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf16x2));
+  const f32x2 r1 = w - f32x2{__builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xffff0000u)};
+  mid = __builtin_bit_cast(uint32_t, __builtin_convertvector(r1, bf16x2));
+  const f32x2 r2 = r1 - f32x2{__builtin_bit_cast(float, mid << 16), __builtin_bit_cast(float, mid & 0xffff0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2));
+}
+
+// The three bf16x8 planes of 8 consecutive fp32 values.
+__device__ __forceinline__ void split3_x8(const f32x4 a, const f32x4 b, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    split3_pair(f32x2{a[2 * i], a[2 * i + 1]}, h[i], m[i], l[i]);
+    split3_pair(f32x2{b[2 * i], b[2 * i + 1]}, h[2 + i], m[2 + i], l[2 + i]);
+  }
+  hi = as_bf16x8(u32x4{h[0], h[1], h[2], h[3]});
+  mid = as_bf16x8(u32x4{m[0], m[1], m[2], m[3]});
+  lo = as_bf16x8(u32x4{l[0], l[1], l[2], l[3]});
 }
 
 template <bool kLds>
@@ -46,29 +65,51 @@ struct LogitRows {
 };
 
 // Softmax, argmax, gate, P partials, block counts and in-block ranks for the
-// block's tokens, from logits already complete in `lg`.  Four consecutive
-// lanes share a token: each scans every fourth expert, then two butterfly
-// steps combine the four partial results in a fixed order.
-template <bool kLds>
+// block's tokens, from logits already complete in `lg` (kThreads threads).
+//  - kThreads / 64 consecutive lanes share a token: each scans a strided
+//    subset of the experts, butterfly steps combine the partial results in a
+//    fixed order; exp(h_j - max) replaces h_j in `lg` on the way.
+//  - kThreads / 128 consecutive lanes share an expert: each sums p_j(t) and
+//    counts the choices of one contiguous run of the block's tokens, and the
+//    runs are combined by butterfly steps (fixed order: the same bits every
+//    call).
+template <int kThreads, bool kLds>
 __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t t0, int64_t blk,
                                 int32_t *__restrict__ expert_idx, float *__restrict__ gate,
                                 int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
                                 float *__restrict__ ppart, float *s_max, float *s_inv, int *s_e) {
-  static_assert(kRouterThreads == 4 * kRouterTokens, "4 lanes per token");
+  constexpr int kLpt = kThreads / kRouterTokens;   // lanes per token
+  constexpr int kTpe = kThreads / kRouterChunk;    // lanes per expert
+  constexpr int kUpt = kRouterTokens / kTpe;       // tokens per lane in the expert sums
+  static_assert(kLpt >= 1 && kLpt <= kWave && (kLpt & (kLpt - 1)) == 0, "lanes per token");
+  static_assert(kTpe >= 1 && kTpe <= kWave && (kTpe & (kTpe - 1)) == 0, "lanes per expert");
   const int tid = threadIdx.x;
-  const int t = tid / 4, q = tid % 4;
-  if (t < nt) {
+  const int t = tid / kLpt, q = tid % kLpt;
+  if (t < nt) {  // the lanes of a token are always on the same side of t < nt
     float best = -INFINITY;
     int bi = 0x7fffffff;
-    for (int j = q; j < N; j += 4) {
-      const float h = lg.at(t, j);
-      if (h > best) {  // ascending j: first maximum kept
-        best = h;
-        bi = j;
+    if (kLds) {  // N <= kRouterChunk: at most kJ values per lane, loaded together
+      constexpr int kJ = kRouterChunk / kLpt;
+      float h[kJ];
+#pragma unroll
+      for (int i = 0; i < kJ; ++i) h[i] = q + i * kLpt < N ? lg.at(t, q + i * kLpt) : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kJ; ++i)
+        if (h[i] > best) {  // ascending j: first maximum kept
+          best = h[i];
+          bi = q + i * kLpt;
+        }
+    } else {
+      for (int j = q; j < N; j += kLpt) {
+        const float h = lg.at(t, j);
+        if (h > best) {
+          best = h;
+          bi = j;
+        }
       }
     }
 #pragma unroll
-    for (int off = 1; off < 4; off <<= 1) {
+    for (int off = 1; off < kLpt; off <<= 1) {
       const float ov = __shfl_xor(best, off, kWave);
       const int oi = __shfl_xor(bi, off, kWave);
       if (ov > best || (ov == best && oi < bi)) {
@@ -77,9 +118,25 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       }
     }
     float sum = 0.f;
-    for (int j = q; j < N; j += 4) sum += __expf(lg.at(t, j) - best);
-    sum += __shfl_xor(sum, 1, kWave);
-    sum += __shfl_xor(sum, 2, kWave);
+    if (kLds) {
+      constexpr int kJ = kRouterChunk / kLpt;
+      float ev[kJ];
+#pragma unroll
+      for (int i = 0; i < kJ; ++i) ev[i] = q + i * kLpt < N ? __expf(lg.at(t, q + i * kLpt) - best) : 0.f;
+#pragma unroll
+      for (int i = 0; i < kJ; ++i) {
+        if (q + i * kLpt < N) lg.at(t, q + i * kLpt) = ev[i];
+        sum += ev[i];
+      }
+    } else {
+      for (int j = q; j < N; j += kLpt) {
+        const float ev = __expf(lg.at(t, j) - best);
+        lg.at(t, j) = ev;
+        sum += ev;
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < kLpt; off <<= 1) sum += __shfl_xor(sum, off, kWave);
     if (q == 0) {
       const float inv = 1.0f / sum;
       s_max[t] = best;
@@ -88,73 +145,104 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       expert_idx[t0 + t] = bi;
       gate[t0 + t] = inv;  // p_e = exp(h_e - max) / sum with h_e = max
     }
-  }  // the four lanes of a token are always on the same side of t < nt
+  }
   __syncthreads();
-  for (int j = tid; j < N; j += kRouterThreads) {
+  for (int j0 = 0; j0 < N; j0 += kRouterChunk) {
+    const int j = j0 + tid / kTpe, r = tid % kTpe;
     float p = 0.f;
     int c = 0;
-    for (int u = 0; u < nt; ++u) {
-      p += __expf(lg.at(u, j) - s_max[u]) * s_inv[u];
-      c += (s_e[u] == j);
+    if (j < N) {
+#pragma unroll
+      for (int i = 0; i < kUpt; ++i) {
+        const int u = r * kUpt + i;
+        if (u < nt) {
+          p += lg.at(u, j) * s_inv[u];
+          c += (s_e[u] == j);
+        }
+      }
     }
-    ppart[blk * N + j] = p;
-    bcount[blk * N + j] = c;
+#pragma unroll
+    for (int off = 1; off < kTpe; off <<= 1) {
+      p += __shfl_xor(p, off, kWave);
+      c += __shfl_xor(c, off, kWave);
+    }
+    if (r == 0 && j < N) {
+      ppart[blk * N + j] = p;
+      bcount[blk * N + j] = c;
+    }
   }
-  if (tid < nt) {
-    const int e = s_e[tid];
+  // rank among the block's earlier tokens with the same expert: wave 0 holds
+  // one token per lane and reads the others' choices lane by lane
+  static_assert(kRouterTokens == kWave, "one router block = one wave of tokens");
+  if (tid < kWave) {
+    const int e = tid < nt ? s_e[tid] : -1;
     int r = 0;
-    for (int u = 0; u < tid; ++u) r += (s_e[u] == e);
-    slot_rank[t0 + tid] = r;
+#pragma unroll
+    for (int u = 0; u < kWave; ++u) r += (u < tid) & (__builtin_amdgcn_readlane(e, u) == e);
+    if (tid < nt) slot_rank[t0 + tid] = r;
   }
 }
 
 // ---------------------------------------------------------------------------
 // bf16 activations, 3-plane bf16 MFMA (v_mfma_f32_16x16x32_bf16).
-// The block's 64 token rows and the 128-expert chunk of the three W_r planes
-// move through LDS 64 contraction columns at a time: global loads are
-// row-contiguous (8 lanes cover one 128-byte row piece, the access pattern
-// the L1/L2 path serves fastest), a register ring keeps kRouterDepth chunks
-// in flight, and the MFMA operands are then read from padded LDS rows.
-// Wave w computes experts [c0 + 32w, c0 + 32w + 32) for all 64 tokens: 4
-// token tiles x 2 expert tiles of 16x16, three planes each.
+// 8 waves in two roles, one of each on every SIMD, so that staging and
+// matrix work overlap instead of taking turns:
+//  - waves 4..7 stage: they load the block's 64 token rows (bf16) and the
+//    fp32 rows of a 128-expert chunk of W_r 64 contraction columns at a time
+//    (row-contiguous loads, a register ring up to two chunks ahead) and write
+//    them to a padded LDS buffer;
+//  - waves 0..3 multiply: wave w computes experts [c0 + 32w, c0 + 32w + 32)
+//    for all 64 tokens (4 token tiles x 2 expert tiles of 16x16) from the
+//    other LDS buffer, splitting its W_r operands into the three bf16 planes
+//    as it reads them (fp32 in LDS costs fewer bytes than three planes).
+// One barrier per chunk swaps the two buffers.  Every block reads the same
+// W_r rows (from L2); the blocks of one XCD start their walk over the
+// contraction at different chunks so that they do not all ask for the same
+// cache lines at once.
 // MFMA operand layout (16x16x32): lane l supplies row (l % 16) and the 8
 // consecutive k values starting at 8 * (l / 16); the result lane l holds
 // column (l % 16), rows 4 * (l / 16) + i.
 // ---------------------------------------------------------------------------
-constexpr int kRouterDepth = 2;
+constexpr int kRBThreads = 512;
+constexpr int kStageThreads = 256;           // waves 4..7
 constexpr int kTokTiles = kRouterTokens / 16;
 constexpr int kRKC = 64;                     // contraction columns per chunk
-constexpr int kRLS = kRKC + 8;               // padded LDS row (bf16)
-constexpr int kXPer = kRouterTokens * (kRKC / 8) / kRouterThreads;      // 16-byte x pieces per thread
-constexpr int kWPer = 3 * kRouterChunk * (kRKC / 8) / kRouterThreads;  // 16-byte plane pieces per thread
-constexpr int kXStage = kRouterTokens * kRLS;                          // bf16 per x stage
-constexpr int kWStage = 3 * kRouterChunk * kRLS;                       // bf16 per plane stage
-constexpr int kRouterStageBytes = 2 * (kXStage + kWStage) * 2;
+constexpr int kRLS = kRKC + 8;               // padded LDS row of x (bf16)
+constexpr int kWLS = kRKC + 4;               // padded LDS row of W_r (fp32)
+constexpr int kXPer = kRouterTokens * (kRKC / 8) / kStageThreads;  // 16-byte x pieces per staging thread
+constexpr int kWGrp = kRouterChunk * (kRKC / 8) / kStageThreads;   // 8-value W_r groups per staging thread
+constexpr int kXStage = kRouterTokens * kRLS * 2;                  // bytes per x stage
+constexpr int kWStage = kRouterChunk * kWLS * 4;                   // bytes per W_r stage
+constexpr int kRouterStageBytes = 2 * (kXStage + kWStage);
 constexpr int kRouterLgBytes = kRouterTokens * (kRouterChunk + 1) * 4;
 constexpr int kRouterSmem = kRouterStageBytes > kRouterLgBytes ? kRouterStageBytes : kRouterLgBytes;
 
 template <bool kLds>
-__global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
-    const bf16 *__restrict__ x, const bf16 *__restrict__ planes, const float *__restrict__ bias,
+__global__ __launch_bounds__(kRBThreads) void router_bf16_kernel(
+    const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
     float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
     float *__restrict__ ppart) {
-  static_assert(kRouterThreads == 256 && kRouterChunk == 128, "4 waves x 32 experts");
-  static_assert(kXPer * kRouterThreads == kRouterTokens * (kRKC / 8), "x pieces");
-  static_assert(kWPer * kRouterThreads == 3 * kRouterChunk * (kRKC / 8), "plane pieces");
+  static_assert(kRBThreads == 8 * kWave && kStageThreads == 4 * kWave && kRouterChunk == 128,
+                "4 MFMA waves x 32 experts + 4 staging waves");
+  static_assert(kXPer * kStageThreads == kRouterTokens * (kRKC / 8), "x pieces");
+  static_assert(kWGrp * kStageThreads == kRouterChunk * (kRKC / 8), "W_r groups");
   __shared__ __attribute__((aligned(16))) char smem[kRouterSmem];
   __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
   __shared__ int s_e[kRouterTokens];
-  bf16 *xs = (bf16 *)smem;              // [2][64][kRLS]
-  bf16 *ws = xs + 2 * kXStage;          // [2][3][128][kRLS]
+  char *xs = smem;                    // [2][64][kRLS] bf16
+  char *ws = smem + 2 * kXStage;      // [2][128][kWLS] fp32
 
+  constexpr int kRing = kLds ? 3 : 2;  // register ring depth of the staging waves
   const int64_t blk = blockIdx.x;
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const bool stager = wave >= 4;  // wave-uniform role
+  const int ptid = tid - kStageThreads;
   const int r16 = lane % 16, kq = (lane / 16) * 8;
-  const int64_t plane = (int64_t)N * d;
   const int nk = d / kRKC;
+  const int rot = (int)((blk / 8) % nk);  // first chunk of this block's walk (blocks b, b + 8, ... share an XCD)
 
   LogitRows<kLds> lg;
   if (kLds) {
@@ -165,123 +253,118 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
     lg.stride = N;
   }
 
-  // Row-contiguous load plan: piece i covers 16 bytes of row i / 8.
+  // Staging plan.  x: piece i covers 16 bytes of token row i / 8.  W_r:
+  // group g covers 8 consecutive fp32 values of expert row g / 8.
   const bf16 *xsrc[kXPer];
   int xoff[kXPer];
 #pragma unroll
   for (int q = 0; q < kXPer; ++q) {
-    const int i = tid + q * kRouterThreads, r = i / 8, c = i % 8;
+    const int i = max(ptid, 0) + q * kStageThreads, r = i / 8, c = i % 8;
     xsrc[q] = x + (t0 + min(r, nt - 1)) * d + c * 8;
-    xoff[q] = r * kRLS + c * 8;
+    xoff[q] = (r * kRLS + c * 8) * 2;
   }
 
   for (int c0 = 0; c0 < N; c0 += kRouterChunk) {
-    const bf16 *wsrc[kWPer];
-    int woff[kWPer];
+    const float *wsrc[kWGrp];
+    int woff[kWGrp];
 #pragma unroll
-    for (int q = 0; q < kWPer; ++q) {
-      const int i = tid + q * kRouterThreads, row = i / 8, c = i % 8;  // row = plane * 128 + expert
-      const int pl = row / kRouterChunk, e = row % kRouterChunk;
-      wsrc[q] = planes + pl * plane + (int64_t)min(c0 + e, N - 1) * d + c * 8;
-      woff[q] = row * kRLS + c * 8;
+    for (int q = 0; q < kWGrp; ++q) {
+      const int g = max(ptid, 0) + q * kStageThreads, e = g / 8, c = g % 8;
+      wsrc[q] = w_r + (int64_t)min(c0 + e, N - 1) * d + c * 8;
+      woff[q] = (e * kWLS + c * 8) * 4;
     }
-    u32x4 xr[kRouterDepth][kXPer], wr[kRouterDepth][kWPer];
+    u32x4 xr[kRing][kXPer];
+    f32x4 wr[kRing][kWGrp][2];
+    // chunk ch of the walk (ch >= nk: a repeat of the last one, never used)
     auto fetch = [&](int slot, int ch) {
-      const int k0 = min(ch, nk - 1) * kRKC;
+      int kc = min(ch, nk - 1) + rot;
+      kc = (kc >= nk ? kc - nk : kc) * kRKC;
 #pragma unroll
-      for (int q = 0; q < kXPer; ++q) xr[slot][q] = *(const u32x4 *)(xsrc[q] + k0);
+      for (int q = 0; q < kXPer; ++q) xr[slot][q] = *(const u32x4 *)(xsrc[q] + kc);
 #pragma unroll
-      for (int q = 0; q < kWPer; ++q) wr[slot][q] = *(const u32x4 *)(wsrc[q] + k0);
+      for (int q = 0; q < kWGrp; ++q) {
+        wr[slot][q][0] = *(const f32x4 *)(wsrc[q] + kc);
+        wr[slot][q][1] = *(const f32x4 *)(wsrc[q] + kc + 4);
+      }
     };
     auto store = [&](int slot, int buf) {
 #pragma unroll
       for (int q = 0; q < kXPer; ++q) *(u32x4 *)(xs + buf * kXStage + xoff[q]) = xr[slot][q];
 #pragma unroll
-      for (int q = 0; q < kWPer; ++q) *(u32x4 *)(ws + buf * kWStage + woff[q]) = wr[slot][q];
+      for (int q = 0; q < kWGrp; ++q) {
+        *(f32x4 *)(ws + buf * kWStage + woff[q]) = wr[slot][q][0];
+        *(f32x4 *)(ws + buf * kWStage + woff[q] + 16) = wr[slot][q][1];
+      }
     };
     f32x4 acc[kTokTiles][2];
 #pragma unroll
     for (int tb = 0; tb < kTokTiles; ++tb) acc[tb][0] = acc[tb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();  // previous chunk's readers of the staging buffers are done
+    if (stager) {
 #pragma unroll
-    for (int j = 0; j < kRouterDepth; ++j) fetch(j, j);
-    store(0, 0);
+      for (int j = 0; j < kRing; ++j) fetch(j, j);
+      store(0, 0);
+    }
     __syncthreads();
-    for (int base = 0; base < nk; base += kRouterDepth) {
+    for (int base = 0; base < nk; base += kRing) {
 #pragma clang loop unroll(full)
-      for (int j = 0; j < kRouterDepth; ++j) {
+      for (int j = 0; j < kRing; ++j) {
         const int ch = base + j;
-        if (ch < nk) {
-          const bf16 *xb = xs + (ch & 1) * kXStage;
-          const bf16 *wbuf = ws + (ch & 1) * kWStage;
+        if (stager) {
+          // slot j held chunk ch, already in LDS: refill it kRing chunks
+          // ahead, then move chunk ch + 1 into the other LDS buffer
+          fetch(j, ch + kRing);
+          store((j + 1) % kRing, (ch + 1) & 1);
+        } else if (ch < nk) {
+          const bf16 *xb = (const bf16 *)(xs + (ch & 1) * kXStage);
+          const float *wbuf = (const float *)(ws + (ch & 1) * kWStage);
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            bf16x8 b[2][3];
+            bf16x8 b[2][3], a[kTokTiles];
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q) {
+              const float *src = wbuf + (wave * 32 + q * 16 + r16) * kWLS + s * 32 + kq;
+              split3_x8(*(const f32x4 *)src, *(const f32x4 *)(src + 4), b[q][0], b[q][1], b[q][2]);
+            }
 #pragma unroll
-              for (int pl = 0; pl < 3; ++pl)
-                b[q][pl] = as_bf16x8(*(const u32x4 *)(
-                    wbuf + (pl * kRouterChunk + wave * 32 + q * 16 + r16) * kRLS + s * 32 + kq));
+            for (int tb = 0; tb < kTokTiles; ++tb)
+              a[tb] = as_bf16x8(*(const u32x4 *)(xb + (tb * 16 + r16) * kRLS + s * 32 + kq));
 #pragma unroll
-            for (int tb = 0; tb < kTokTiles; ++tb) {
-              const bf16x8 a = as_bf16x8(*(const u32x4 *)(xb + (tb * 16 + r16) * kRLS + s * 32 + kq));
+            for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
               for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int pl = 0; pl < 3; ++pl)
-                  acc[tb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[q][pl], acc[tb][q], 0, 0, 0);
-            }
+                for (int tb = 0; tb < kTokTiles; ++tb)
+                  acc[tb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], b[q][pl], acc[tb][q], 0, 0, 0);
           }
         }
-        fetch(j, ch + kRouterDepth);
-        store((j + 1) % kRouterDepth, (ch + 1) & 1);
         __syncthreads();
       }
     }
-    // scatter this wave's 64 x 32 logits tile (the staging buffers are free:
-    // the loop ended with a barrier)
-#pragma unroll
-    for (int tb = 0; tb < kTokTiles; ++tb)
+    // scatter each MFMA wave's 64 x 32 logits tile (the staging buffers are
+    // free: the loop ended with a barrier)
+    if (!stager) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int j = c0 + wave * 32 + q * 16 + r16;
         if (j < N) {
-          const float b = bias ? bias[j] : 0.f;
+          const float bj = bias ? bias[j] : 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = tb * 16 + (lane / 16) * 4 + i;
-            if (t < nt) lg.at(t, kLds ? j - c0 : j) = acc[tb][q][i] + b;
-          }
+          for (int tb = 0; tb < kTokTiles; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = tb * 16 + (lane / 16) * 4 + i;
+              if (t < nt) lg.at(t, kLds ? j - c0 : j) = acc[tb][q][i] + bj;
+            }
         }
       }
+    }
     if (kLds) break;  // N <= kRouterChunk: one chunk holds every expert
   }
   __syncthreads();
-  router_epilogue<kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, s_max, s_inv,
-                        s_e);
-}
-
-// W_r split once per call into three bf16 planes [3][N][d] (hi, mid, lo),
-// 8 values per thread.
-__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ w_r, int64_t n8,
-                                                           u32x4 *__restrict__ planes) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = ((const f32x4 *)w_r)[2 * i], b = ((const f32x4 *)w_r)[2 * i + 1];
-  bf16x8 h, m, l;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    bf16 hh, mm, ll;
-    split3(k < 4 ? a[k] : b[k - 4], hh, mm, ll);
-    h[k] = hh;
-    m[k] = mm;
-    l[k] = ll;
-  }
-  planes[i] = as_u32x4(h);
-  planes[n8 + i] = as_u32x4(m);
-  planes[2 * n8 + i] = as_u32x4(l);
+  router_epilogue<kRBThreads, kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, s_max,
+                                    s_inv, s_e);
 }
 
 // ---------------------------------------------------------------------------
@@ -347,8 +430,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
     if (kLds) break;
   }
   __syncthreads();
-  router_epilogue<kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, s_max, s_inv,
-                        s_e);
+  router_epilogue<kRouterThreads, kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, s_max,
+                                        s_inv, s_e);
 }
 
 hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
@@ -357,14 +440,12 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
   const bool lds = a.N <= kRouterChunk;
   dim3 grid((unsigned)nb), block(kRouterThreads);
   if (a.dtype == kBF16) {
-    const int64_t n8 = (int64_t)a.N * a.d / 8;
-    router_split_kernel<<<dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, st>>>(a.w_r, n8, (u32x4 *)a.planes);
     if (lds)
-      router_bf16_kernel<true><<<grid, block, 0, st>>>((const bf16 *)a.x, (const bf16 *)a.planes, a.bias, a.T,
+      router_bf16_kernel<true><<<grid, dim3(kRBThreads), 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T,
                                                        a.d, a.N, a.logits, a.expert_idx, a.gate, a.slot,
                                                        a.bcount, a.ppart);
     else
-      router_bf16_kernel<false><<<grid, block, 0, st>>>((const bf16 *)a.x, (const bf16 *)a.planes, a.bias, a.T,
+      router_bf16_kernel<false><<<grid, dim3(kRBThreads), 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T,
                                                         a.d, a.N, a.logits, a.expert_idx, a.gate, a.slot,
                                                         a.bcount, a.ppart);
   } else {
