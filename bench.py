@@ -46,6 +46,8 @@ def algorithmic_bytes(name: str, T: int, d: int, f: int, N: int, C: int, counts)
     if name == "assign_apply":
         # slot/dropped/token map, plus the zero rows of dropped tokens
         return T * 13 + T * 4 + N * 8 + (T - kept) * d * 2
+    if name == "assign":  # scan and apply in one launch
+        return sum(algorithmic_bytes(k, T, d, f, N, C, counts) for k in ("assign_scan", "assign_apply"))
     if name == "dispatch":
         return 2 * kept * d * 2 + T * 9
     if name == "ffn_up":    # W_in of live experts, gathered x rows, H written
@@ -187,7 +189,7 @@ def main() -> int:
     kept = sum(min(c, C) for c in counts)
     ffn_ms = kern["ffn_up"] + kern["ffn_down"]
     ffn_tflops = 4.0 * kept * d * f / (ffn_ms * 1e-3) / 1e12
-    rdc = ("router", "assign_scan", "assign_apply")
+    rdc = [k for k in ("router", "assign", "assign_scan", "assign_apply") if k in kern]
     rdc_b = sum(algorithmic_bytes(k, T, d, f, N, C, counts) for k in rdc)
     rdc_ms = sum(kern[k] for k in rdc)
     res = {

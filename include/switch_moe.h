@@ -152,17 +152,17 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
 /* Measurement variant of switch_layer_forward: same arguments and results,
  * plus the duration of each kernel launch in milliseconds, timed with HIP
  * events recorded on `stream` around every launch.  BLOCKS until the stream
- * has finished the call.  kernel_ms receives up to max_kernels values and
- * *num_kernels the number of launches; switch_kernel_name(i) names launch i. */
+ * has finished the call.  kernel_ms receives up to max_kernels values,
+ * kernel_names (may be NULL) the matching launch names (static strings:
+ * "route" for the one-launch routing step, or "router", "assign_scan",
+ * "assign_apply"; then "ffn_up", "ffn_down"), and *num_kernels the number of
+ * launches (at most 5). */
 int switch_layer_forward_profiled(const switch_shape *s, const void *x, const float *w_router,
                                   const float *router_bias, const void *w_in, const void *w_out,
                                   int32_t add_residual, void *y, int32_t *expert_idx, float *gate,
                                   int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,
                                   void *workspace, size_t workspace_bytes, void *stream, float *kernel_ms,
-                                  int32_t max_kernels, int32_t *num_kernels);
-
-/* Name of launch `index` of switch_layer_forward ("" past the last). */
-const char *switch_kernel_name(int32_t index);
+                                  const char **kernel_names, int32_t max_kernels, int32_t *num_kernels);
 
 #ifdef __cplusplus
 }

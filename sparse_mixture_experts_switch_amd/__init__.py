@@ -15,7 +15,6 @@ from .binding import (  # noqa: F401
     combine,
     dispatch,
     expert_ffn,
-    kernel_names,
     layer_forward,
     layer_forward_profiled,
     load_library,

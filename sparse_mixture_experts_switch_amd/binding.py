@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "SwitchError", "load_library", "capacity", "workspace_bytes", "route", "dispatch",
-    "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "kernel_names",
+    "expert_ffn", "combine", "layer_forward", "layer_forward_profiled",
     "SWITCH_F32", "SWITCH_BF16",
 ]
 
@@ -29,7 +29,6 @@ _CODES = {-1: "SWITCH_E_INVALID", -2: "SWITCH_E_UNSUPPORTED", -3: "SWITCH_E_WORK
 EXPORTED = [
     "switch_capacity", "switch_workspace_bytes", "switch_last_error", "switch_route", "switch_dispatch",
     "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
-    "switch_kernel_name",
 ]
 
 
@@ -70,11 +69,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.switch_combine.argtypes = [sp] + [_P] * 8
     lib.switch_layer_forward.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P]
     lib.switch_layer_forward_profiled.argtypes = (
-        [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P, _P, ctypes.c_int32, _P])
-    lib.switch_kernel_name.argtypes = [ctypes.c_int32]
-    lib.switch_kernel_name.restype = ctypes.c_char_p
+        [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P, _P, _P, ctypes.c_int32, _P])
     for name in EXPORTED:
-        if name not in ("switch_last_error", "switch_kernel_name"):
+        if name != "switch_last_error":
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -230,23 +227,12 @@ def layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Te
     return o
 
 
-def kernel_names() -> list[str]:
-    lib = load_library()
-    names, i = [], 0
-    while True:
-        n = lib.switch_kernel_name(i).decode()
-        if not n:
-            return names
-        names.append(n)
-        i += 1
-
-
 def layer_forward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, add_residual=False,
                            workspace=None, out=None):
     """layer_forward plus per-launch durations (ms) from HIP events; blocks."""
     _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
     ms = (ctypes.c_float * 16)()
+    names = (ctypes.c_char_p * 16)()
     n = ctypes.c_int32()
-    _check(load_library().switch_layer_forward_profiled(*args, ms, 16, ctypes.byref(n)))
-    names = kernel_names()
-    return o, [(names[i] if i < len(names) else f"k{i}", float(ms[i])) for i in range(n.value)]
+    _check(load_library().switch_layer_forward_profiled(*args, ms, names, 16, ctypes.byref(n)))
+    return o, [(names[i].decode(), float(ms[i])) for i in range(n.value)]

@@ -79,7 +79,8 @@ int layout(const switch_shape *s, Layout &L) {
   const int64_t nb = router_blocks(T);
   const int es = esize(s->dtype);
   size_t bc, pp, ps, lg = 0, hid, act, tk;
-  bool ok = mul(bc, {nb, N, 4}) && mul(pp, {nb, N, 4}) && mul(ps, {N, 4}) &&
+  const int64_t Np = count_stride((int)N);
+  bool ok = mul(bc, {nb, Np, 4}) && mul(pp, {nb, Np, 4}) && mul(ps, {N, 4}) &&
             (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(hid, {N, C, f, es}) && mul(act, {N, C, d, es}) &&
             mul(tk, {N, C, 4});
   if (!ok) return fail(SWITCH_E_UNSUPPORTED, "buffer sizes overflow for this shape");
@@ -149,8 +150,7 @@ struct Timer {
   }
 };
 
-const char *const kKernelNames[] = {"router", "assign_scan", "assign_apply", "ffn_up", "ffn_down"};
-constexpr int kNumKernels = 5;
+constexpr int kNumKernels = 5;  // most launches one call makes
 
 int route_args(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
                int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count,
@@ -191,18 +191,16 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
   return SWITCH_OK;
 }
 
-// Routing kernels.  With tok set (layer path) the apply step also fills the
-// slot -> token map and the output rows of dropped tokens.
+// Routing kernels: router, then the capacity assignment (one or two
+// launches).  With tok set (layer path) the assignment also fills the slot ->
+// token / gate maps and the output rows of dropped tokens.
 int run_route(const RouteArgs &a, hipStream_t st, Timer &tm, int32_t *tok = nullptr, float *gmap = nullptr,
               const void *xres = nullptr, void *y = nullptr) {
   hipError_t e;
   if ((e = launch_router(a, st)) != hipSuccess) return hip_fail(e, "router launch");
-  tm.mark(kKernelNames[0]);
-  if ((e = launch_assign_scan(a, st)) != hipSuccess) return hip_fail(e, "assign_scan launch");
-  tm.mark(kKernelNames[1]);
-  e = tok ? launch_assign_apply_layer(a, tok, gmap, xres, y, st) : launch_assign_apply(a, st);
-  if (e != hipSuccess) return hip_fail(e, "assign_apply launch");
-  tm.mark(kKernelNames[2]);
+  tm.mark("router");
+  LaunchMarks marks{[](void *ctx, const char *name) { static_cast<Timer *>(ctx)->mark(name); }, &tm};
+  if ((e = launch_assign(a, tok, gmap, xres, y, st, marks)) != hipSuccess) return hip_fail(e, "assignment launch");
   return SWITCH_OK;
 }
 
@@ -238,11 +236,11 @@ int layer_forward(const switch_shape *s, const void *x, const float *w_router, c
   GemmCall up{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w + L.lf_hidden,
               expert_count, tok, nullptr, nullptr, nullptr};
   if ((e = launch_ffn_up_gather(up, st)) != hipSuccess) return hip_fail(e, "ffn_up launch");
-  tm.mark(kKernelNames[3]);
+  tm.mark("ffn_up");
   GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, y,
                 expert_count, tok, gate, gmap, xres};
   if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
-  tm.mark(kKernelNames[4]);
+  tm.mark("ffn_down");
   return SWITCH_OK;
 }
 
@@ -401,8 +399,8 @@ int switch_layer_forward_profiled(const switch_shape *s, const void *x, const fl
                                   const float *router_bias, const void *w_in, const void *w_out,
                                   int32_t add_residual, void *y, int32_t *expert_idx, float *gate, int32_t *slot,
                                   uint8_t *dropped, int32_t *expert_count, float *aux_loss, void *ws,
-                                  size_t ws_bytes, void *stream, float *kernel_ms, int32_t max_kernels,
-                                  int32_t *num_kernels) {
+                                  size_t ws_bytes, void *stream, float *kernel_ms, const char **kernel_names,
+                                  int32_t max_kernels, int32_t *num_kernels) {
   GUARD({
     if (!kernel_ms || !num_kernels || max_kernels < 0)
       return fail(SWITCH_E_INVALID, "kernel_ms / num_kernels is NULL or max_kernels < 0");
@@ -418,7 +416,10 @@ int switch_layer_forward_profiled(const switch_shape *s, const void *x, const fl
         float ms = 0.f;
         e = hipEventElapsedTime(&ms, tm.ev[i], tm.ev[i + 1]);
         if (e != hipSuccess) rc = hip_fail(e, "hipEventElapsedTime");
-        if (i < max_kernels) kernel_ms[i] = ms;
+        if (i < max_kernels) {
+          kernel_ms[i] = ms;
+          if (kernel_names) kernel_names[i] = tm.names[i];
+        }
       }
       if (rc == SWITCH_OK) *num_kernels = tm.n;
     }
@@ -427,10 +428,6 @@ int switch_layer_forward_profiled(const switch_shape *s, const void *x, const fl
         if (tm.ev[i]) (void)hipEventDestroy(tm.ev[i]);
     return rc;
   })
-}
-
-const char *switch_kernel_name(int32_t index) {
-  return (index >= 0 && index < kNumKernels) ? kKernelNames[index] : "";
 }
 
 }  // extern "C"

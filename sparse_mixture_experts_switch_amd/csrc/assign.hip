@@ -37,6 +37,7 @@ __global__ __launch_bounds__(kScanWaves *kWave) void assign_scan_kernel(
   const int j = blockIdx.x * kWave + lane;
   const bool valid = j < N;
   const int jj = valid ? j : N - 1;  // lanes past N read a valid column
+  const int64_t Np = count_stride(N);
   const int64_t seg = ceil_div(nb, kScanWaves);
   const int64_t b0 = min<int64_t>(nb, wave * seg), b1 = min<int64_t>(nb, b0 + seg);
   int c = 0;
@@ -47,8 +48,8 @@ __global__ __launch_bounds__(kScanWaves *kWave) void assign_scan_kernel(
 #pragma unroll
     for (int i = 0; i < kScanBatch; ++i) {
       const int64_t bb = min(b + i, b1 - 1);
-      cv[i] = bcount[bb * N + jj];
-      pv[i] = ppart[bb * N + jj];
+      cv[i] = bcount[bb * Np + jj];
+      pv[i] = ppart[bb * Np + jj];
     }
 #pragma unroll
     for (int i = 0; i < kScanBatch; ++i)
@@ -65,11 +66,11 @@ __global__ __launch_bounds__(kScanWaves *kWave) void assign_scan_kernel(
   for (int64_t b = b0; b < b1; b += kScanBatch) {
     int cv[kScanBatch];
 #pragma unroll
-    for (int i = 0; i < kScanBatch; ++i) cv[i] = bcount[min(b + i, b1 - 1) * N + jj];
+    for (int i = 0; i < kScanBatch; ++i) cv[i] = bcount[min(b + i, b1 - 1) * Np + jj];
 #pragma unroll
     for (int i = 0; i < kScanBatch; ++i)
       if (b + i < b1) {
-        if (valid) bcount[(b + i) * N + j] = run;
+        if (valid) bcount[(b + i) * Np + j] = run;
         run += cv[i];
       }
   }
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void assign_apply_kernel(
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t < T) {
     const int e = expert_idx[t];
-    const int s = slot[t] + boff[(t / kRouterTokens) * N + e];
+    const int s = slot[t] + boff[(t / kRouterTokens) * count_stride(N) + e];
     slot[t] = s;
     dropped[t] = s >= C ? 1 : 0;
   }
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void assign_apply_layer_kernel(
   bool drop = false;
   if (t < T) {
     const int e = expert_idx[t];
-    const int s = slot[t] + boff[(t / kRouterTokens) * N + e];
+    const int s = slot[t] + boff[(t / kRouterTokens) * count_stride(N) + e];
     slot[t] = s;
     drop = s >= C;
     dropped[t] = drop ? 1 : 0;
@@ -161,32 +162,212 @@ __global__ void route_empty_kernel(int N, int32_t *__restrict__ expert_count, fl
   if (blockIdx.x == 0 && threadIdx.x == 0) aux_loss[0] = 0.f;
 }
 
-hipError_t launch_assign_scan(const RouteArgs &a, hipStream_t st) {
+// ---------------------------------------------------------------------------
+// One-launch assignment for batches whose block count is small.  Workgroup a
+// owns router blocks [4a, 4a + 4) (256 tokens).  It sums the counts of all
+// blocks before its own (16-byte loads, kAsBatch rows in flight per thread,
+// 16 row groups, then the group sums in ascending order: exact integers),
+// adds its own blocks' counts one by one for the offsets of each, and
+// assigns its tokens.  The workgroup holding the last block also reads the P
+// partials of every block and forms the totals, the P sums and the loss.
+// ---------------------------------------------------------------------------
+constexpr int kAsThreads = 512;
+constexpr int kAsBlocks = 4;                          // router blocks per workgroup
+constexpr int kAsTokens = kAsBlocks * kRouterTokens;  // tokens per workgroup
+constexpr int kAsGroups = kAsThreads / 32;            // row groups (32 lanes x 4 experts per row)
+constexpr int kAsChunk = 128;                         // experts per pass
+constexpr int kAsBatch = 16;
+
+struct AssignArgs {
+  const int32_t *expert_idx;
+  int32_t *slot;
+  uint8_t *dropped;
+  const int32_t *bcount;
+  const float *ppart;
+  int64_t T, nb;
+  int N, C;
+  int32_t *expert_count;
+  float *psum, *aux_loss;
+  const float *gate;
+  int32_t *tok;  // layer path, or null
+  float *gmap;
+  const u32x4 *xres;
+  u32x4 *y;
+  int row16;
+};
+
+size_t assign_one_smem(int N) {
+  return (size_t)kAsBlocks * N * 4 + (size_t)N * 4 + 2 * (size_t)kAsGroups * kAsChunk * 4 + kAsThreads * 8;
+}
+
+__global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int N = p.N;
+  int *s_off = (int *)dsm;                                 // [kAsBlocks][N]
+  float *s_q = (float *)(s_off + kAsBlocks * N);           // [N] P partial sums of the blocks before r0
+  int *s_part = (int *)(s_q + N);                          // [kAsGroups][kAsChunk]
+  float *s_pq = (float *)(s_part + kAsGroups * kAsChunk);  // [kAsGroups][kAsChunk]
+  double *s_acc = (double *)(s_pq + kAsGroups * kAsChunk); // [kAsThreads]
+  const int tid = threadIdx.x, jq = tid % 32, rg = tid / 32;
+  const int64_t Np = count_stride(N);
+  const int64_t r0 = (int64_t)blockIdx.x * kAsBlocks, r1 = min(r0 + kAsBlocks, p.nb);
+  const bool last = r1 == p.nb;
+
+  // 1. counts (and, for the last group, P partials) of blocks [0, r0)
+  for (int c0 = 0; c0 < N; c0 += kAsChunk) {
+    const int j4 = c0 + 4 * jq;
+    const bool act = j4 < N;  // Np % 4 == 0: the 4 columns from j4 lie inside the row
+    int c[4] = {0, 0, 0, 0};
+    float q[4] = {0.f, 0.f, 0.f, 0.f};
+    if (act) {
+      for (int64_t b = rg; b < r0; b += (int64_t)kAsGroups * kAsBatch) {
+        u32x4 cv[kAsBatch];
+#pragma unroll
+        for (int i = 0; i < kAsBatch; ++i)  // clamped past r0: a row that exists, never added
+          cv[i] = *(const u32x4 *)(p.bcount + min(b + (int64_t)i * kAsGroups, r0 - 1) * Np + j4);
+#pragma unroll
+        for (int i = 0; i < kAsBatch; ++i)
+          if (b + (int64_t)i * kAsGroups < r0) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) c[k] += (int)cv[i][k];
+          }
+      }
+      if (last) {
+        for (int64_t b = rg; b < r0; b += (int64_t)kAsGroups * kAsBatch) {
+          f32x4 pv[kAsBatch];
+#pragma unroll
+          for (int i = 0; i < kAsBatch; ++i)
+            pv[i] = *(const f32x4 *)(p.ppart + min(b + (int64_t)i * kAsGroups, r0 - 1) * Np + j4);
+#pragma unroll
+          for (int i = 0; i < kAsBatch; ++i)
+            if (b + (int64_t)i * kAsGroups < r0) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) q[k] += pv[i][k];
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s_part[rg * kAsChunk + 4 * jq + k] = c[k];
+      s_pq[rg * kAsChunk + 4 * jq + k] = q[k];
+    }
+    __syncthreads();
+    if (tid < kAsChunk && c0 + tid < N) {
+      int off = 0;
+      float qs = 0.f;
+#pragma unroll
+      for (int g = 0; g < kAsGroups; ++g) {
+        off += s_part[g * kAsChunk + tid];
+        qs += s_pq[g * kAsChunk + tid];
+      }
+      s_off[c0 + tid] = off;
+      s_q[c0 + tid] = qs;
+    }
+    __syncthreads();
+  }
+
+  // 2. offsets of each of this group's blocks; the last group's totals
+  double acc = 0.0;
+  for (int j = tid; j < N; j += kAsThreads) {
+    int run = s_off[j];
+    float qs = s_q[j];
+    for (int64_t b = r0; b < r1; ++b) {
+      s_off[(b - r0) * N + j] = run;
+      run += p.bcount[b * Np + j];
+      if (last) qs += p.ppart[b * Np + j];
+    }
+    if (last) {
+      p.expert_count[j] = run;
+      p.psum[j] = qs;
+      acc += (double)run * (double)qs;
+    }
+  }
+  if (last) s_acc[tid] = acc;
+  __syncthreads();
+
+  // 3. tokens: slot = offset of the token's block for its expert + in-block rank
+  const int64_t t = r0 * kRouterTokens + tid;
+  const int lane = tid % kWave;
+  bool drop = false;
+  if (tid < kAsTokens && t < p.T) {
+    const int e = p.expert_idx[t];
+    const int sl = s_off[(tid / kRouterTokens) * N + e] + p.slot[t];
+    p.slot[t] = sl;
+    drop = sl >= p.C;
+    p.dropped[t] = drop ? 1 : 0;
+    if (!drop && p.tok) {
+      p.tok[(int64_t)e * p.C + sl] = (int32_t)t;
+      p.gmap[(int64_t)e * p.C + sl] = p.gate[t];
+    }
+  }
+  if (p.y) {  // output rows of this wave's dropped tokens: 0, or x with a residual
+    unsigned long long mask = __ballot(drop);
+    while (mask) {
+      const int bb = __ffsll(mask) - 1;
+      mask &= mask - 1;
+      const int64_t tt = t - lane + bb;
+      for (int c = lane; c < p.row16; c += kWave)
+        p.y[tt * p.row16 + c] = p.xres ? p.xres[tt * p.row16 + c] : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // 4. loss = N * sum_i (count_i / T) (psum_i / T), reduced in double in a fixed order
+  if (last) {
+    for (int w = kAsThreads / 2; w > 0; w >>= 1) {
+      if (tid < w) s_acc[tid] += s_acc[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) {
+      const double tt = (double)p.T;
+      p.aux_loss[0] = (float)(s_acc[0] * (double)N / (tt * tt));
+    }
+  }
+}
+
+// One launch when the prefix reads of all workgroups together stay small.
+bool assign_one_ok(int64_t nb, int N) {
+  const int64_t groups = ceil_div(nb, kAsBlocks);
+  const double reads = 0.5 * (double)groups * (double)(groups * kAsBlocks) * (double)count_stride(N) * 4.0;
+  return nb > 0 && reads <= 16.0 * (1 << 20) && assign_one_smem(N) <= 64 * 1024;
+}
+
+hipError_t launch_assign(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y, hipStream_t st,
+                         LaunchMarks marks) {
+  auto mark = [&](const char *name) {
+    if (marks.fn) marks.fn(marks.ctx, name);
+  };
   const int64_t nb = router_blocks(a.T);
+  hipError_t e;
   if (nb == 0) {
     route_empty_kernel<<<dim3((unsigned)ceil_div(a.N, 256)), dim3(256), 0, st>>>(a.N, a.expert_count, a.aux_loss);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    mark("assign");
+    return hipSuccess;
+  }
+  const int row16 = a.d * (a.dtype == kBF16 ? 2 : 4) / 16;
+  if (assign_one_ok(nb, a.N)) {
+    AssignArgs p{a.expert_idx, a.slot, a.dropped, a.bcount, a.ppart, a.T, nb, a.N, a.C, a.expert_count,
+                 a.psum, a.aux_loss, a.gate, tok, gmap, (const u32x4 *)xres, (u32x4 *)y, row16};
+    assign_one_kernel<<<dim3((unsigned)ceil_div(nb, kAsBlocks)), dim3(kAsThreads), assign_one_smem(a.N), st>>>(p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    mark("assign");
+    return hipSuccess;
   }
   assign_scan_kernel<<<dim3((unsigned)ceil_div(a.N, kWave)), dim3(kScanWaves * kWave), 0, st>>>(
       a.bcount, a.ppart, nb, a.N, a.expert_count, a.psum);
-  return hipGetLastError();
-}
-
-hipError_t launch_assign_apply(const RouteArgs &a, hipStream_t st) {
-  if (a.T == 0) return hipSuccess;
-  assign_apply_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
-      a.expert_idx, a.slot, a.dropped, a.bcount, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss);
-  return hipGetLastError();
-}
-
-hipError_t launch_assign_apply_layer(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y,
-                                     hipStream_t st) {
-  if (a.T == 0) return hipSuccess;
-  const int row16 = a.d * (a.dtype == kBF16 ? 2 : 4) / 16;
-  assign_apply_layer_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
-      a.expert_idx, a.slot, a.dropped, a.bcount, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss, tok, gmap,
-      a.gate, (const u32x4 *)xres, (u32x4 *)y, row16);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mark("assign_scan");
+  if (tok)
+    assign_apply_layer_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
+        a.expert_idx, a.slot, a.dropped, a.bcount, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss, tok, gmap,
+        a.gate, (const u32x4 *)xres, (u32x4 *)y, row16);
+  else
+    assign_apply_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
+        a.expert_idx, a.slot, a.dropped, a.bcount, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mark("assign_apply");
+  return hipSuccess;
 }
 
 }  // namespace smx

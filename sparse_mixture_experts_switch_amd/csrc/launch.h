@@ -26,8 +26,8 @@ struct RouteArgs {
   uint8_t *dropped;
   int32_t *expert_count;
   float *aux_loss;
-  int32_t *bcount;  // [nb][N]: block counts, then exclusive block offsets
-  float *ppart;     // [nb][N]: block partial sums of p
+  int32_t *bcount;  // [nb][count_stride(N)]: block counts (then exclusive block offsets on the scan path)
+  float *ppart;     // [nb][count_stride(N)]: block partial sums of p
   float *psum;      // [N]
 };
 
@@ -79,13 +79,19 @@ struct GemmCall {
 
 // Each launcher enqueues its kernels on `st` and returns the launch status.
 hipError_t launch_router(const RouteArgs &a, hipStream_t st);
-hipError_t launch_assign_scan(const RouteArgs &a, hipStream_t st);
-hipError_t launch_assign_apply(const RouteArgs &a, hipStream_t st);
-// Layer path: also records tok[e][slot] = t and gmap[e][slot] = gate[t] for
-// kept tokens and writes the y rows of dropped tokens (0, or x with a
-// residual).
-hipError_t launch_assign_apply_layer(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y,
-                                     hipStream_t st);
+// Capacity assignment and loss after the router.  Small batches take one
+// launch (each workgroup sums the counts of the blocks before its own);
+// others a scan over blocks, then the apply step.  With tok set (layer path)
+// it also records tok[e][slot] = t and gmap[e][slot] = gate[t] for kept
+// tokens and writes the y rows of dropped tokens (0, or x with a residual).
+// `names` receives the kernel name of each launch (up to 2), `*n` their
+// number; `mark` (may be null) is called after each launch.
+struct LaunchMarks {
+  void (*fn)(void *ctx, const char *name);
+  void *ctx;
+};
+hipError_t launch_assign(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y, hipStream_t st,
+                         LaunchMarks marks);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st);
 hipError_t launch_ffn_up(const FfnArgs &a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st);
@@ -94,5 +100,8 @@ hipError_t launch_ffn_down_combine(const GemmCall &c, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 
 inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
+// Row stride (elements) of the per-block count and P-partial arrays: rows
+// start on 16-byte boundaries.
+__host__ __device__ inline int count_stride(int N) { return (N + 3) & ~3; }
 
 }  // namespace smx

@@ -167,8 +167,8 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       c += __shfl_xor(c, off, kWave);
     }
     if (r == 0 && j < N) {
-      ppart[blk * N + j] = p;
-      bcount[blk * N + j] = c;
+      ppart[blk * count_stride(N) + j] = p;
+      bcount[blk * count_stride(N) + j] = c;
     }
   }
   // rank among the block's earlier tokens with the same expert: wave 0 holds
@@ -217,24 +217,30 @@ constexpr int kRouterStageBytes = 2 * (kXStage + kWStage);
 constexpr int kRouterLgBytes = kRouterTokens * (kRouterChunk + 1) * 4;
 constexpr int kRouterSmem = kRouterStageBytes > kRouterLgBytes ? kRouterStageBytes : kRouterLgBytes;
 
+// LDS of one router block (bf16 path).
+struct RouterSmem {
+  __attribute__((aligned(16))) char stage[kRouterSmem];
+  float s_max[kRouterTokens], s_inv[kRouterTokens];
+  int s_e[kRouterTokens];
+};
+
+// Router work of block `blk` (tokens [64 blk, 64 blk + 64)).  Starts with a
+// barrier, so consecutive calls by one workgroup may reuse `sm`.
 template <bool kLds>
-__global__ __launch_bounds__(kRBThreads) void router_bf16_kernel(
+__device__ __forceinline__ void router_block_bf16(
     const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
     float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
-    float *__restrict__ ppart) {
+    float *__restrict__ ppart, int64_t blk, RouterSmem &sm) {
   static_assert(kRBThreads == 8 * kWave && kStageThreads == 4 * kWave && kRouterChunk == 128,
                 "4 MFMA waves x 32 experts + 4 staging waves");
   static_assert(kXPer * kStageThreads == kRouterTokens * (kRKC / 8), "x pieces");
   static_assert(kWGrp * kStageThreads == kRouterChunk * (kRKC / 8), "W_r groups");
-  __shared__ __attribute__((aligned(16))) char smem[kRouterSmem];
-  __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
-  __shared__ int s_e[kRouterTokens];
+  char *const smem = sm.stage;
   char *xs = smem;                    // [2][64][kRLS] bf16
   char *ws = smem + 2 * kXStage;      // [2][128][kWLS] fp32
 
   constexpr int kRing = kLds ? 3 : 2;  // register ring depth of the staging waves
-  const int64_t blk = blockIdx.x;
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -363,8 +369,19 @@ __global__ __launch_bounds__(kRBThreads) void router_bf16_kernel(
     if (kLds) break;  // N <= kRouterChunk: one chunk holds every expert
   }
   __syncthreads();
-  router_epilogue<kRBThreads, kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, s_max,
-                                    s_inv, s_e);
+  router_epilogue<kRBThreads, kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, sm.s_max,
+                                    sm.s_inv, sm.s_e);
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kRBThreads) void router_bf16_kernel(
+    const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
+    int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
+    float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
+    float *__restrict__ ppart) {
+  __shared__ RouterSmem sm;
+  router_block_bf16<kLds>(x, w_r, bias, T, d, N, logits_g, expert_idx, gate, slot_rank, bcount, ppart, blockIdx.x,
+                          sm);
 }
 
 // ---------------------------------------------------------------------------

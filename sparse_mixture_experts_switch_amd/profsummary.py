@@ -25,7 +25,7 @@ KERNEL_KEYS = {
     "ffn_up": ("ffn_gemm_bf16_kernel", "Lb1ELi0E"),
     "ffn_down": ("ffn_gemm_bf16_kernel", "Lb0ELi2E"),
     "router": ("router_bf16_kernel", ""),
-    "router_split": ("router_split_kernel", ""),
+    "assign": ("assign_one_kernel", ""),
     "assign_scan": ("assign_scan_kernel", ""),
     "assign_apply": ("assign_apply_layer_kernel", ""),
     "copy": ("__amd_rocclr_copyBuffer", ""),

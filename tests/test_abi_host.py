@@ -29,7 +29,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = smx.load_library()
     names = _declared()
-    assert len(names) >= 10, names
+    assert len(names) >= 9, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in switch_moe.h but not exported"
     assert sorted(B.EXPORTED) == names
@@ -124,9 +124,10 @@ def test_entry_points_reject_before_launch():
     assert rc == B.SWITCH_E_INVALID
     # profiled: NULL timing outputs
     rc = lib.switch_layer_forward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good, good,
-                                           good, good, good, good, 1 << 30, None, None, 0, None)
+                                           good, good, good, good, 1 << 30, None, None, None, 0, None)
     assert rc == B.SWITCH_E_INVALID
 
 
-def test_kernel_names():
-    assert smx.kernel_names() == ["router", "assign_scan", "assign_apply", "ffn_up", "ffn_down"]
+def test_no_kernel_name_lookup():
+    # launch names come back from the profiled call itself (they depend on the shape)
+    assert "switch_kernel_name" not in B.EXPORTED

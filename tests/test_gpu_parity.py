@@ -62,6 +62,9 @@ EDGE = {
     "fp32_many_experts": SMALL.with_(dtype="f32", tokens=400, num_experts=300, d_model=128, d_ff=128,
                                      capacity_factor=3.0),
     "zipf_bias": SMALL.with_(zipf_s=1.1, tokens=2048, num_experts=32),
+    # block count x experts large enough for the two-launch assignment (scan, then apply)
+    "scan_path_2048_experts": SMALL.with_(tokens=10000, num_experts=2048, d_model=64, d_ff=64,
+                                          capacity_factor=2.0),
 }
 
 
