@@ -80,7 +80,7 @@ __device__ __forceinline__ int xcd_tile(int b, int grid) {
 // per workgroup (kCols = WAVES * 16 * NBW).  Operand layout: lane l supplies
 // row (l % 16) and 8 consecutive k starting at 8 * (l / 16); result lane l
 // holds column (l % 16), rows 4 * (l / 16) + i.
-template <int MB, int NBW, int WAVES, bool kGather, int kEpi>
+template <int MB, int NBW, int WAVES, bool kGather, int kEpi, bool kSkipDead = true>
 __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArgs<bf16> p) {
   constexpr int kThreads = WAVES * 64;
   constexpr int kRows = MB * 16;
@@ -159,7 +159,6 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
   if (!next_tile(cur)) return;
   bool have_nxt = next_tile(nxt);
 
-  f32x4 acc[MB][NBW];
   u32x4 areg[2][kAPer];
   u32x4 breg[2][2][NBW];
   // Loads of chunk `ch` of tile t (clamped to the tile's last chunk past its
@@ -206,6 +205,9 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
   __syncthreads();
 
   while (true) {
+    // ---- one tile: `cur` ----
+    const int mlive = (cur.mrows + 15) / 16;  // row blocks holding live rows (uniform)
+    f32x4 acc[MB][NBW];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -219,16 +221,26 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
           const bf16 *abuf = sA + j * kAStage;
 #pragma clang loop unroll(full)
           for (int s = 0; s < 2; ++s) {
-            // every row block runs: rows past the live ones hold copies of
-            // the last live row and are never stored (straight-line MFMA
-            // stream; the kernel is bound by the weight stream)
+            auto blocks = [&](int mb0, int mb1) {
 #pragma clang loop unroll(full)
-            for (int mb = 0; mb < MB; ++mb) {
-              const bf16x8 a = as_bf16x8(*(const u32x4 *)(&abuf[(mb * 16 + r16) * kLdsStride + s * 32 + kq]));
+              for (int mb = mb0; mb < mb1; ++mb) {
+                const bf16x8 a = as_bf16x8(*(const u32x4 *)(&abuf[(mb * 16 + r16) * kLdsStride + s * 32 + kq]));
 #pragma unroll
-              for (int nb = 0; nb < NBW; ++nb)
-                acc[mb][nb] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(breg[j][s][nb]), acc[mb][nb], 0, 0, 0);
+                for (int nb = 0; nb < NBW; ++nb)
+                  acc[mb][nb] =
+                      __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(breg[j][s][nb]), acc[mb][nb], 0, 0, 0);
+              }
+            };
+            // Row blocks past the live ones hold copies of the last live row
+            // and are never stored.  The last two pairs of blocks run only
+            // when they hold live rows (two uniform branches; finer-grained
+            // skipping breaks up the MFMA stream and costs more than it saves).
+            if (kSkipDead && MB >= 6) {
+              blocks(0, MB - 4);
+              if (mlive > MB - 4) blocks(MB - 4, MB - 2);
+              if (mlive > MB - 2) blocks(MB - 2, MB);
+            } else {
+              blocks(0, MB);
             }
           }
         }
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
     const int ncol0 = cur.n0 + wave * NBW * 16;
 #pragma clang loop unroll(full)
     for (int mb = 0; mb < MB; ++mb) {
-      if (mb * 16 >= cur.mrows) continue;
+      if (mb >= mlive) continue;
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
