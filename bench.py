@@ -26,6 +26,7 @@ METRIC = "Switch-layer fwd tokens/sec on 1 MI355X; expert-FFN % MFMA peak; route
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
+MIN_WARMUP_S = 0.25        # untimed warmup floor (seconds of steps)
 FFN_SRC = os.path.join(ROOT, "sparse_mixture_experts_switch_amd", "csrc", "ffn.hip")
 
 
@@ -151,19 +152,31 @@ def main() -> int:
     out["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
     call = lambda: smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],  # noqa: E731
                                      inp["w_out"], C, workspace=ws, out=out)
-    for _ in range(args.warmup):
-        call()
+    # the layer runs on a stream of its own (the legacy default stream
+    # synchronises with every other stream at each launch)
+    stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
-    log(f"bench: warmup {args.warmup} done; timing {args.steps} steps")
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        call()
-    stop.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
+    with torch.cuda.stream(stream):
+        # untimed warmup: at least W steps and at least MIN_WARMUP_S seconds
+        # of steps (the GPU needs a fraction of a second of load to reach its
+        # steady clock; timing before that reads ~10% slow)
+        warm_run, t_warm = 0, time.perf_counter()
+        while warm_run < args.warmup or time.perf_counter() - t_warm < MIN_WARMUP_S:
+            call()
+            warm_run += 1
+            if warm_run % 50 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        log(f"bench: warmup {warm_run} steps done; timing {args.steps} steps")
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        start.record(stream)
+        for _ in range(args.steps):
+            call()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(stop) / args.steps
     counts = out["expert_count"].cpu().tolist()
     drop_rate = float(out["dropped"].float().mean().item())
@@ -171,11 +184,12 @@ def main() -> int:
     # per-kernel durations: HIP events recorded by the library on the stream
     # it launches on, averaged over the same number of steps
     sums: dict[str, float] = {}
-    for _ in range(args.steps):
-        _, per = smx.layer_forward_profiled(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],
-                                            inp["w_out"], C, workspace=ws, out=out)
-        for name, v in per:
-            sums[name] = sums.get(name, 0.0) + v
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            _, per = smx.layer_forward_profiled(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],
+                                                inp["w_out"], C, workspace=ws, out=out)
+            for name, v in per:
+                sums[name] = sums.get(name, 0.0) + v
     kern = {k: v / args.steps for k, v in sums.items()}
     log("bench: per-kernel ms " + ", ".join(f"{k}={v:.4f}" for k, v in kern.items()))
     per_kernel = {}
@@ -199,6 +213,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_run,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
