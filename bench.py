@@ -181,16 +181,31 @@ def main() -> int:
     counts = out["expert_count"].cpu().tolist()
     drop_rate = float(out["dropped"].float().mean().item())
 
-    # per-kernel durations: HIP events recorded by the library on the stream
-    # it launches on, averaged over the same number of steps
-    sums: dict[str, float] = {}
+    # per-kernel durations, live: K more ordinary steps in which HIP events
+    # (on the layer's stream) bracket kernel i alone -- kernels 0..i-1, event,
+    # kernel i, event, kernels i+1..n-1; no kernel of the layer modifies its
+    # inputs, so the split calls reproduce the ordinary step
+    names = smx.launch_names(shape)
+    n_k = len(names)
+    part = lambda lo, hi: smx.layer_forward_profiled(  # noqa: E731
+        inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C, first_kernel=lo,
+        last_kernel=hi, workspace=ws, out=out)
+    kern = {}
     with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            _, per = smx.layer_forward_profiled(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],
-                                                inp["w_out"], C, workspace=ws, out=out)
-            for name, v in per:
-                sums[name] = sums.get(name, 0.0) + v
-    kern = {k: v / args.steps for k, v in sums.items()}
+        for i, name in enumerate(names):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for a, b in evs:
+                if i > 0:
+                    part(0, i - 1)
+                a.record(stream)
+                part(i, i)
+                b.record(stream)
+                if i < n_k - 1:
+                    part(i + 1, n_k - 1)
+            torch.cuda.synchronize()
+            kern[name] = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     log("bench: per-kernel ms " + ", ".join(f"{k}={v:.4f}" for k, v in kern.items()))
     per_kernel = {}
     for k, v in kern.items():

@@ -149,20 +149,28 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
                          int32_t *expert_count, float *aux_loss, void *workspace, size_t workspace_bytes,
                          void *stream);
 
-/* Measurement variant of switch_layer_forward: same arguments and results,
- * plus the duration of each kernel launch in milliseconds, timed with HIP
- * events recorded on `stream` around every launch.  BLOCKS until the stream
- * has finished the call.  kernel_ms receives up to max_kernels values,
- * kernel_names (may be NULL) the matching launch names (static strings:
- * "route" for the one-launch routing step, or "router", "assign_scan",
- * "assign_apply"; then "ffn_up", "ffn_down"), and *num_kernels the number of
- * launches (at most 5). */
+/* Measurement variant of switch_layer_forward: same arguments and
+ * asynchrony, but it launches only the kernels numbered first_kernel ..
+ * last_kernel of the call (0-based, in the order switch_launch_names gives),
+ * each `times` (>= 1) times back to back.  Every kernel of the layer reads
+ * only the inputs and what earlier kernels of the call left in the
+ * workspace, and never its own outputs: after one full call, calls covering
+ * 0..i-1, then i..i, then i+1..n-1 reproduce the full call exactly, so a
+ * caller can bracket kernel i with its own events inside an otherwise
+ * ordinary step.  SWITCH_E_INVALID if the range is empty or past the last
+ * kernel of this shape. */
 int switch_layer_forward_profiled(const switch_shape *s, const void *x, const float *w_router,
                                   const float *router_bias, const void *w_in, const void *w_out,
                                   int32_t add_residual, void *y, int32_t *expert_idx, float *gate,
                                   int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,
-                                  void *workspace, size_t workspace_bytes, void *stream, float *kernel_ms,
-                                  const char **kernel_names, int32_t max_kernels, int32_t *num_kernels);
+                                  void *workspace, size_t workspace_bytes, void *stream, int32_t first_kernel,
+                                  int32_t last_kernel, int32_t times);
+
+/* Names of the kernels switch_layer_forward launches for this shape, in
+ * launch order (static strings: "router", then "assign" or "assign_scan" +
+ * "assign_apply", then "ffn_up", "ffn_down").  Up to max_names are stored in
+ * names[]; *num_names receives their number (at most 5).  Host only. */
+int switch_launch_names(const switch_shape *s, const char **names, int32_t max_names, int32_t *num_names);
 
 #ifdef __cplusplus
 }

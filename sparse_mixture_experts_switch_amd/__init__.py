@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     expert_ffn,
     layer_forward,
     layer_forward_profiled,
+    launch_names,
     load_library,
     route,
     workspace_bytes,

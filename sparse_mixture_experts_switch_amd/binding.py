@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "SwitchError", "load_library", "capacity", "workspace_bytes", "route", "dispatch",
-    "expert_ffn", "combine", "layer_forward", "layer_forward_profiled",
+    "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "launch_names",
     "SWITCH_F32", "SWITCH_BF16",
 ]
 
@@ -29,6 +29,7 @@ _CODES = {-1: "SWITCH_E_INVALID", -2: "SWITCH_E_UNSUPPORTED", -3: "SWITCH_E_WORK
 EXPORTED = [
     "switch_capacity", "switch_workspace_bytes", "switch_last_error", "switch_route", "switch_dispatch",
     "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
+    "switch_launch_names",
 ]
 
 
@@ -69,7 +70,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.switch_combine.argtypes = [sp] + [_P] * 8
     lib.switch_layer_forward.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P]
     lib.switch_layer_forward_profiled.argtypes = (
-        [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P, _P, _P, ctypes.c_int32, _P])
+        [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P, ctypes.c_int32, ctypes.c_int32,
+                                                               ctypes.c_int32])
+    lib.switch_launch_names.argtypes = [sp, _P, ctypes.c_int32, _P]
     for name in EXPORTED:
         if name != "switch_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -227,12 +230,18 @@ def layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Te
     return o
 
 
-def layer_forward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, add_residual=False,
-                           workspace=None, out=None):
-    """layer_forward plus per-launch durations (ms) from HIP events; blocks."""
+def layer_forward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, first_kernel: int, last_kernel: int,
+                           times: int = 1, add_residual=False, workspace=None, out=None) -> dict:
+    """Kernels first_kernel..last_kernel of layer_forward only, each launched
+    `times` times back to back (switch_layer_forward_profiled); asynchronous."""
     _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
-    ms = (ctypes.c_float * 16)()
-    names = (ctypes.c_char_p * 16)()
+    _check(load_library().switch_layer_forward_profiled(*args, int(first_kernel), int(last_kernel), int(times)))
+    return o
+
+
+def launch_names(shape: Shape) -> list[str]:
+    """Kernels switch_layer_forward launches for this shape, in order."""
+    names = (ctypes.c_char_p * 8)()
     n = ctypes.c_int32()
-    _check(load_library().switch_layer_forward_profiled(*args, ms, names, 16, ctypes.byref(n)))
-    return o, [(names[i].decode(), float(ms[i])) for i in range(n.value)]
+    _check(load_library().switch_launch_names(ctypes.byref(shape), names, 8, ctypes.byref(n)))
+    return [names[i].decode() for i in range(n.value)]

@@ -10,6 +10,7 @@
 #include <cstring>
 #include <exception>
 #include <string>
+#include <vector>
 
 #include "../../include/switch_moe.h"
 #include "launch.h"
@@ -54,7 +55,7 @@ bool mul(size_t &out, std::initializer_list<int64_t> xs) {
 int esize(int dtype) { return dtype == SWITCH_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t bcount = 0, ppart = 0, psum = 0, logits = 0, route_end = 0;
+  size_t bcount = 0, boff = 0, ppart = 0, psum = 0, rank = 0, logits = 0, route_end = 0;
   size_t ffn_hidden = 0, ffn_end = 0;                             // switch_expert_ffn alone
   size_t lf_hidden = 0, lf_tok = 0, lf_gmap = 0, total = 0;     // layer forward
 };
@@ -78,19 +79,23 @@ int layout(const switch_shape *s, Layout &L) {
   const int64_t T = s->tokens, N = s->num_experts, C = s->capacity, d = s->d_model, f = s->d_ff;
   const int64_t nb = router_blocks(T);
   const int es = esize(s->dtype);
-  size_t bc, pp, ps, lg = 0, hid, act, tk;
+  size_t bc, pp, ps, rk, lg = 0, hid, act, tk;
   const int64_t Np = count_stride((int)N);
-  bool ok = mul(bc, {nb, Np, 4}) && mul(pp, {nb, Np, 4}) && mul(ps, {N, 4}) &&
+  bool ok = mul(bc, {nb, Np, 4}) && mul(pp, {nb, Np, 4}) && mul(ps, {N, 4}) && mul(rk, {T, 4}) &&
             (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(hid, {N, C, f, es}) && mul(act, {N, C, d, es}) &&
             mul(tk, {N, C, 4});
   if (!ok) return fail(SWITCH_E_UNSUPPORTED, "buffer sizes overflow for this shape");
   size_t o = 0;
   L.bcount = o;
   o = align_up(o + bc);
+  L.boff = o;
+  o = align_up(o + bc);
   L.ppart = o;
   o = align_up(o + pp);
   L.psum = o;
   o = align_up(o + ps);
+  L.rank = o;
+  o = align_up(o + rk);
   L.logits = o;
   o = align_up(o + lg);
   L.route_end = o;
@@ -133,19 +138,19 @@ int check_ws(void *ws, size_t ws_bytes, size_t need) {
 }
 
 // ---------------------------------------------------------------- launches --
-// A launch sequence runs plainly, or with HIP events around each launch.
+// Launch sequence control: records the name of each kernel in launch order
+// and says how many times to issue it: once, or, for a measurement call, only
+// the kernels numbered first..last, each `times` times back to back (every
+// kernel of the layer reads only what earlier kernels wrote and never its own
+// outputs, so a repeat or a rerun on the same workspace changes no result).
 struct Timer {
-  bool on = false;
-  int n = 0;
-  hipEvent_t ev[16] = {};
-  hipStream_t st = nullptr;
-  hipError_t err = hipSuccess;
-  const char *names[16];
+  int first = 0, last = 1 << 30;
+  int times = 1;
+  int n = 0;  // kernels of this call passed so far
+  const char *names[16] = {};
+  int reps() const { return (n >= first && n <= last) ? times : 0; }
   void mark(const char *name) {
-    if (!on || err != hipSuccess) return;
-    if (n >= 15) return;
-    names[n] = name;
-    err = hipEventRecord(ev[n + 1], st);
+    if (n < 16) names[n] = name;
     ++n;
   }
 };
@@ -186,6 +191,8 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
   a.expert_count = expert_count;
   a.aux_loss = aux_loss;
   a.bcount = (int32_t *)(w + L.bcount);
+  a.boff = (int32_t *)(w + L.boff);
+  a.rank = (int32_t *)(w + L.rank);
   a.ppart = (float *)(w + L.ppart);
   a.psum = (float *)(w + L.psum);
   return SWITCH_OK;
@@ -197,9 +204,11 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
 int run_route(const RouteArgs &a, hipStream_t st, Timer &tm, int32_t *tok = nullptr, float *gmap = nullptr,
               const void *xres = nullptr, void *y = nullptr) {
   hipError_t e;
-  if ((e = launch_router(a, st)) != hipSuccess) return hip_fail(e, "router launch");
+  for (int r = tm.reps(); r > 0; --r)
+    if ((e = launch_router(a, st)) != hipSuccess) return hip_fail(e, "router launch");
   tm.mark("router");
-  LaunchMarks marks{[](void *ctx, const char *name) { static_cast<Timer *>(ctx)->mark(name); }, &tm};
+  LaunchMarks marks{[](void *ctx, const char *name) { static_cast<Timer *>(ctx)->mark(name); },
+                    [](void *ctx) { return static_cast<Timer *>(ctx)->reps(); }, &tm};
   if ((e = launch_assign(a, tok, gmap, xres, y, st, marks)) != hipSuccess) return hip_fail(e, "assignment launch");
   return SWITCH_OK;
 }
@@ -222,12 +231,6 @@ int layer_forward(const switch_shape *s, const void *x, const float *w_router, c
   if (s->tokens > 0) NEED(y, 16);
   hipStream_t st = (hipStream_t)stream;
   char *w = (char *)ws;
-  if (tm.on) {
-    tm.st = st;
-    for (int i = 0; i <= kNumKernels; ++i)
-      if ((tm.err = hipEventCreate(&tm.ev[i])) != hipSuccess) return hip_fail(tm.err, "hipEventCreate");
-    if ((tm.err = hipEventRecord(tm.ev[0], st)) != hipSuccess) return hip_fail(tm.err, "hipEventRecord");
-  }
   int32_t *tok = (int32_t *)(w + L.lf_tok);
   float *gmap = (float *)(w + L.lf_gmap);
   const void *xres = add_residual ? x : nullptr;
@@ -235,11 +238,13 @@ int layer_forward(const switch_shape *s, const void *x, const float *w_router, c
   hipError_t e;
   GemmCall up{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w + L.lf_hidden,
               expert_count, tok, nullptr, nullptr, nullptr};
-  if ((e = launch_ffn_up_gather(up, st)) != hipSuccess) return hip_fail(e, "ffn_up launch");
+  for (int r = tm.reps(); r > 0; --r)
+    if ((e = launch_ffn_up_gather(up, st)) != hipSuccess) return hip_fail(e, "ffn_up launch");
   tm.mark("ffn_up");
   GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, y,
                 expert_count, tok, gate, gmap, xres};
-  if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
+  for (int r = tm.reps(); r > 0; --r)
+    if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
   tm.mark("ffn_down");
   return SWITCH_OK;
 }
@@ -399,34 +404,45 @@ int switch_layer_forward_profiled(const switch_shape *s, const void *x, const fl
                                   const float *router_bias, const void *w_in, const void *w_out,
                                   int32_t add_residual, void *y, int32_t *expert_idx, float *gate, int32_t *slot,
                                   uint8_t *dropped, int32_t *expert_count, float *aux_loss, void *ws,
-                                  size_t ws_bytes, void *stream, float *kernel_ms, const char **kernel_names,
-                                  int32_t max_kernels, int32_t *num_kernels) {
+                                  size_t ws_bytes, void *stream, int32_t first_kernel, int32_t last_kernel,
+                                  int32_t times) {
   GUARD({
-    if (!kernel_ms || !num_kernels || max_kernels < 0)
-      return fail(SWITCH_E_INVALID, "kernel_ms / num_kernels is NULL or max_kernels < 0");
+    if (times < 1) return fail(SWITCH_E_INVALID, "times = %d < 1", times);
+    if (first_kernel < 0 || last_kernel < first_kernel)
+      return fail(SWITCH_E_INVALID, "kernel range %d..%d", first_kernel, last_kernel);
     Timer tm;
-    tm.on = true;
+    tm.first = first_kernel;
+    tm.last = last_kernel;
+    tm.times = times;
     int rc = layer_forward(s, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
                            dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
-    if (rc == SWITCH_OK && tm.err != hipSuccess) rc = hip_fail(tm.err, "hipEventRecord");
-    if (rc == SWITCH_OK) {
-      hipError_t e = hipEventSynchronize(tm.ev[tm.n]);
-      if (e != hipSuccess) rc = hip_fail(e, "hipEventSynchronize");
-      for (int i = 0; rc == SWITCH_OK && i < tm.n; ++i) {
-        float ms = 0.f;
-        e = hipEventElapsedTime(&ms, tm.ev[i], tm.ev[i + 1]);
-        if (e != hipSuccess) rc = hip_fail(e, "hipEventElapsedTime");
-        if (i < max_kernels) {
-          kernel_ms[i] = ms;
-          if (kernel_names) kernel_names[i] = tm.names[i];
-        }
-      }
-      if (rc == SWITCH_OK) *num_kernels = tm.n;
-    }
-    if (tm.on)
-      for (int i = 0; i <= kNumKernels; ++i)
-        if (tm.ev[i]) (void)hipEventDestroy(tm.ev[i]);
+    if (rc == SWITCH_OK && last_kernel >= tm.n)
+      return fail(SWITCH_E_INVALID, "kernel range %d..%d: the call launches %d kernels", first_kernel, last_kernel,
+                  tm.n);
     return rc;
+  })
+}
+
+int switch_launch_names(const switch_shape *s, const char **names, int32_t max_names, int32_t *num_names) {
+  GUARD({
+    if (!num_names || max_names < 0 || (max_names > 0 && !names))
+      return fail(SWITCH_E_INVALID, "names / num_names is NULL or max_names < 0");
+    int rc = check_shape(s);
+    if (rc) return rc;
+    const char *seq[kNumKernels];
+    int n = 0;
+    seq[n++] = "router";
+    if (s->tokens == 0 || assign_single_launch(router_blocks(s->tokens), s->num_experts)) {
+      seq[n++] = "assign";
+    } else {
+      seq[n++] = "assign_scan";
+      seq[n++] = "assign_apply";
+    }
+    seq[n++] = "ffn_up";
+    seq[n++] = "ffn_down";
+    for (int i = 0; i < n && i < max_names; ++i) names[i] = seq[i];
+    *num_names = n;
+    return SWITCH_OK;
   })
 }
 

@@ -10,8 +10,10 @@
 //
 // The router leaves, per block of kRouterTokens tokens, the block's count for
 // every expert (bcount[b][i]) and every token's rank inside its block.  The
-// scan turns bcount into exclusive offsets over blocks, in place, with integer
-// arithmetic only, so slots and drops are exact and independent of scheduling.
+// assignment turns the counts into exclusive offsets over blocks with integer
+// arithmetic only, so slots and drops are exact and independent of
+// scheduling.  No kernel here modifies its inputs: each one can be run again
+// on the same buffers with the same result.
 
 #include "common.h"
 #include "launch.h"
@@ -29,8 +31,8 @@ constexpr int kScanWaves = 16;
 constexpr int kScanBatch = 8;
 
 __global__ __launch_bounds__(kScanWaves *kWave) void assign_scan_kernel(
-    int32_t *__restrict__ bcount, const float *__restrict__ ppart, int64_t nb, int N,
-    int32_t *__restrict__ expert_count, float *__restrict__ psum) {
+    const int32_t *__restrict__ bcount, int32_t *__restrict__ boff, const float *__restrict__ ppart, int64_t nb,
+    int N, int32_t *__restrict__ expert_count, float *__restrict__ psum) {
   __shared__ int s_cnt[kScanWaves][kWave];
   __shared__ float s_p[kScanWaves][kWave];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(kScanWaves *kWave) void assign_scan_kernel(
 #pragma unroll
     for (int i = 0; i < kScanBatch; ++i)
       if (b + i < b1) {
-        if (valid) bcount[(b + i) * Np + j] = run;
+        if (valid) boff[(b + i) * Np + j] = run;
         run += cv[i];
       }
   }
@@ -108,13 +110,14 @@ __device__ void write_aux_loss(int64_t T, int N, const int32_t *__restrict__ exp
 // slot = in-block rank + the block's offset for the token's expert;
 // dropped = slot >= capacity.  Block 0 also forms the loss.
 __global__ __launch_bounds__(256) void assign_apply_kernel(
-    const int32_t *__restrict__ expert_idx, int32_t *__restrict__ slot, uint8_t *__restrict__ dropped,
+    const int32_t *__restrict__ expert_idx, const int32_t *__restrict__ rank, int32_t *__restrict__ slot,
+    uint8_t *__restrict__ dropped,
     const int32_t *__restrict__ boff, int64_t T, int N, int C, const int32_t *__restrict__ expert_count,
     const float *__restrict__ psum, float *__restrict__ aux_loss) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t < T) {
     const int e = expert_idx[t];
-    const int s = slot[t] + boff[(t / kRouterTokens) * count_stride(N) + e];
+    const int s = rank[t] + boff[(t / kRouterTokens) * count_stride(N) + e];
     slot[t] = s;
     dropped[t] = s >= C ? 1 : 0;
   }
@@ -127,7 +130,8 @@ __global__ __launch_bounds__(256) void assign_apply_kernel(
 // writes the output rows of dropped tokens (their computation is skipped: 0,
 // or x when a residual is added).
 __global__ __launch_bounds__(256) void assign_apply_layer_kernel(
-    const int32_t *__restrict__ expert_idx, int32_t *__restrict__ slot, uint8_t *__restrict__ dropped,
+    const int32_t *__restrict__ expert_idx, const int32_t *__restrict__ rank, int32_t *__restrict__ slot,
+    uint8_t *__restrict__ dropped,
     const int32_t *__restrict__ boff, int64_t T, int N, int C, const int32_t *__restrict__ expert_count,
     const float *__restrict__ psum, float *__restrict__ aux_loss, int32_t *__restrict__ tok,
     float *__restrict__ gmap, const float *__restrict__ gate, const u32x4 *__restrict__ xres,
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(256) void assign_apply_layer_kernel(
   bool drop = false;
   if (t < T) {
     const int e = expert_idx[t];
-    const int s = slot[t] + boff[(t / kRouterTokens) * count_stride(N) + e];
+    const int s = rank[t] + boff[(t / kRouterTokens) * count_stride(N) + e];
     slot[t] = s;
     drop = s >= C;
     dropped[t] = drop ? 1 : 0;
@@ -180,6 +184,7 @@ constexpr int kAsBatch = 16;
 
 struct AssignArgs {
   const int32_t *expert_idx;
+  const int32_t *rank;
   int32_t *slot;
   uint8_t *dropped;
   const int32_t *bcount;
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
   bool drop = false;
   if (tid < kAsTokens && t < p.T) {
     const int e = p.expert_idx[t];
-    const int sl = s_off[(tid / kRouterTokens) * N + e] + p.slot[t];
+    const int sl = s_off[(tid / kRouterTokens) * N + e] + p.rank[t];
     p.slot[t] = sl;
     drop = sl >= p.C;
     p.dropped[t] = drop ? 1 : 0;
@@ -326,7 +331,7 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
 }
 
 // One launch when the prefix reads of all workgroups together stay small.
-bool assign_one_ok(int64_t nb, int N) {
+bool assign_single_launch(int64_t nb, int N) {
   const int64_t groups = ceil_div(nb, kAsBlocks);
   const double reads = 0.5 * (double)groups * (double)(groups * kAsBlocks) * (double)count_stride(N) * 4.0;
   return nb > 0 && reads <= 16.0 * (1 << 20) && assign_one_smem(N) <= 64 * 1024;
@@ -337,34 +342,41 @@ hipError_t launch_assign(const RouteArgs &a, int32_t *tok, float *gmap, const vo
   auto mark = [&](const char *name) {
     if (marks.fn) marks.fn(marks.ctx, name);
   };
+  auto reps = [&]() { return marks.reps ? marks.reps(marks.ctx) : 1; };
   const int64_t nb = router_blocks(a.T);
   hipError_t e;
   if (nb == 0) {
-    route_empty_kernel<<<dim3((unsigned)ceil_div(a.N, 256)), dim3(256), 0, st>>>(a.N, a.expert_count, a.aux_loss);
+    for (int r = reps(); r > 0; --r)
+      route_empty_kernel<<<dim3((unsigned)ceil_div(a.N, 256)), dim3(256), 0, st>>>(a.N, a.expert_count,
+                                                                                   a.aux_loss);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     mark("assign");
     return hipSuccess;
   }
   const int row16 = a.d * (a.dtype == kBF16 ? 2 : 4) / 16;
-  if (assign_one_ok(nb, a.N)) {
-    AssignArgs p{a.expert_idx, a.slot, a.dropped, a.bcount, a.ppart, a.T, nb, a.N, a.C, a.expert_count,
+  if (assign_single_launch(nb, a.N)) {
+    AssignArgs p{a.expert_idx, a.rank, a.slot, a.dropped, a.bcount, a.ppart, a.T, nb, a.N, a.C, a.expert_count,
                  a.psum, a.aux_loss, a.gate, tok, gmap, (const u32x4 *)xres, (u32x4 *)y, row16};
-    assign_one_kernel<<<dim3((unsigned)ceil_div(nb, kAsBlocks)), dim3(kAsThreads), assign_one_smem(a.N), st>>>(p);
+    for (int r = reps(); r > 0; --r)
+      assign_one_kernel<<<dim3((unsigned)ceil_div(nb, kAsBlocks)), dim3(kAsThreads), assign_one_smem(a.N), st>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     mark("assign");
     return hipSuccess;
   }
-  assign_scan_kernel<<<dim3((unsigned)ceil_div(a.N, kWave)), dim3(kScanWaves * kWave), 0, st>>>(
-      a.bcount, a.ppart, nb, a.N, a.expert_count, a.psum);
+  for (int r = reps(); r > 0; --r)
+    assign_scan_kernel<<<dim3((unsigned)ceil_div(a.N, kWave)), dim3(kScanWaves * kWave), 0, st>>>(
+        a.bcount, a.boff, a.ppart, nb, a.N, a.expert_count, a.psum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mark("assign_scan");
-  if (tok)
-    assign_apply_layer_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
-        a.expert_idx, a.slot, a.dropped, a.bcount, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss, tok, gmap,
-        a.gate, (const u32x4 *)xres, (u32x4 *)y, row16);
-  else
-    assign_apply_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
-        a.expert_idx, a.slot, a.dropped, a.bcount, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss);
+  for (int r = reps(); r > 0; --r) {
+    if (tok)
+      assign_apply_layer_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
+          a.expert_idx, a.rank, a.slot, a.dropped, a.boff, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss, tok,
+          gmap, a.gate, (const u32x4 *)xres, (u32x4 *)y, row16);
+    else
+      assign_apply_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
+          a.expert_idx, a.rank, a.slot, a.dropped, a.boff, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mark("assign_apply");
   return hipSuccess;

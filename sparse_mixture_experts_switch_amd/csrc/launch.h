@@ -22,11 +22,13 @@ struct RouteArgs {
   float *logits;  // [T][N] scratch, only used when N > kRouterChunk
   int32_t *expert_idx;
   float *gate;
-  int32_t *slot;  // in-block rank after the router, slot after assignment
+  int32_t *slot;  // slot of each token (assignment output)
+  int32_t *rank;  // [T] workspace: rank of each token among its block's earlier tokens with the same expert
   uint8_t *dropped;
   int32_t *expert_count;
   float *aux_loss;
-  int32_t *bcount;  // [nb][count_stride(N)]: block counts (then exclusive block offsets on the scan path)
+  int32_t *bcount;  // [nb][count_stride(N)]: block counts
+  int32_t *boff;    // [nb][count_stride(N)]: exclusive block offsets (scan path)
   float *ppart;     // [nb][count_stride(N)]: block partial sums of p
   float *psum;      // [N]
 };
@@ -84,12 +86,16 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t st);
 // others a scan over blocks, then the apply step.  With tok set (layer path)
 // it also records tok[e][slot] = t and gmap[e][slot] = gate[t] for kept
 // tokens and writes the y rows of dropped tokens (0, or x with a residual).
-// `names` receives the kernel name of each launch (up to 2), `*n` their
-// number; `mark` (may be null) is called after each launch.
+// marks.fn (may be null) is called with each kernel's name after its
+// launches; marks.reps (may be null) says how many times to issue the next
+// kernel back to back (measurement only: no kernel modifies its inputs).
 struct LaunchMarks {
   void (*fn)(void *ctx, const char *name);
+  int (*reps)(void *ctx);
   void *ctx;
 };
+// Whether the assignment of nb router blocks and N experts takes one launch.
+bool assign_single_launch(int64_t nb, int N);
 hipError_t launch_assign(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y, hipStream_t st,
                          LaunchMarks marks);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st);

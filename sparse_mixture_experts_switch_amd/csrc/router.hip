@@ -14,7 +14,7 @@
 // max and first argmax of the logits, s = sum_j exp(h_j - max), gate = 1/s;
 // per block: P partial sums sum_t p_j(t) in token order, the number of the
 // block's tokens that chose each expert, and each token's rank among the
-// block's earlier tokens with the same expert (stored in slot[] and later
+// block's earlier tokens with the same expert (stored in rank[] and later
 // offset by the cross-block scan).
 //
 // bf16 activations: the contraction runs on bf16 MFMA.  W_r (fp32) is split
@@ -459,20 +459,20 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
   if (a.dtype == kBF16) {
     if (lds)
       router_bf16_kernel<true><<<grid, dim3(kRBThreads), 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T,
-                                                       a.d, a.N, a.logits, a.expert_idx, a.gate, a.slot,
+                                                       a.d, a.N, a.logits, a.expert_idx, a.gate, a.rank,
                                                        a.bcount, a.ppart);
     else
       router_bf16_kernel<false><<<grid, dim3(kRBThreads), 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T,
-                                                        a.d, a.N, a.logits, a.expert_idx, a.gate, a.slot,
+                                                        a.d, a.N, a.logits, a.expert_idx, a.gate, a.rank,
                                                         a.bcount, a.ppart);
   } else {
     if (lds)
       router_f32_kernel<true><<<grid, block, 0, st>>>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N,
-                                                      a.logits, a.expert_idx, a.gate, a.slot, a.bcount,
+                                                      a.logits, a.expert_idx, a.gate, a.rank, a.bcount,
                                                       a.ppart);
     else
       router_f32_kernel<false><<<grid, block, 0, st>>>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N,
-                                                       a.logits, a.expert_idx, a.gate, a.slot, a.bcount,
+                                                       a.logits, a.expert_idx, a.gate, a.rank, a.bcount,
                                                        a.ppart);
   }
   return hipGetLastError();

@@ -65,15 +65,15 @@ def test_workspace_bytes_layout():
     s = B.make_shape(16384, 768, 3072, 128, 160, torch.bfloat16)
     ws = smx.workspace_bytes(s)
     nb = 16384 // 64
-    # block counts + P partials, P sums, hidden, slot->token and slot->gate maps
-    expect_min = 2 * nb * 128 * 4 + 128 * 4 + 128 * 160 * 3072 * 2 + 2 * 128 * 160 * 4
+    # block counts, block offsets, P partials, P sums, ranks, hidden, slot->token and slot->gate maps
+    expect_min = 3 * nb * 128 * 4 + 128 * 4 + 16384 * 4 + 128 * 160 * 3072 * 2 + 2 * 128 * 160 * 4
     assert expect_min <= ws <= expect_min + 8 * 256
     # more experts than one router chunk adds the [T][N] logits scratch
     s2 = B.make_shape(1000, 64, 64, 300, 10, torch.float32)
     assert smx.workspace_bytes(s2) >= 1000 * 300 * 4
     # routing alone: the capacity-0 figure holds no expert buffers
     s3 = B.make_shape(16384, 768, 3072, 128, 0, torch.bfloat16)
-    assert smx.workspace_bytes(s3) < 2 * nb * 128 * 4 + 4096
+    assert smx.workspace_bytes(s3) < 3 * nb * 128 * 4 + 16384 * 4 + 4096
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -122,12 +122,22 @@ def test_entry_points_reject_before_launch():
     # dispatch: NULL dropped
     rc = lib.switch_dispatch(ctypes.byref(s), good, good, good, None, good, None)
     assert rc == B.SWITCH_E_INVALID
-    # profiled: NULL timing outputs
-    rc = lib.switch_layer_forward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good, good,
-                                           good, good, good, good, 1 << 30, None, None, None, 0, None)
-    assert rc == B.SWITCH_E_INVALID
+    # profiled: empty kernel range / times < 1
+    for first, last, times in ((0, 0, 0), (2, 1, 1), (-1, 0, 1)):
+        rc = lib.switch_layer_forward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good,
+                                               good, good, good, good, good, 1 << 30, None, first, last, times)
+        assert rc == B.SWITCH_E_INVALID
 
 
-def test_no_kernel_name_lookup():
-    # launch names come back from the profiled call itself (they depend on the shape)
-    assert "switch_kernel_name" not in B.EXPORTED
+def test_launch_names_follow_the_shape():
+    import torch
+    base = B.make_shape(16384, 768, 3072, 128, 160, torch.bfloat16)
+    assert smx.launch_names(base) == ["router", "assign", "ffn_up", "ffn_down"]
+    # many router blocks x many experts: scan over blocks, then apply
+    many = B.make_shape(32768, 2048, 6144, 2048, 16, torch.bfloat16)
+    assert smx.launch_names(many) == ["router", "assign_scan", "assign_apply", "ffn_up", "ffn_down"]
+    empty = B.make_shape(0, 64, 64, 8, 0, torch.float32)
+    assert smx.launch_names(empty) == ["router", "assign", "ffn_up", "ffn_down"]
+    bad = B.make_shape(16, 96, 64, 8, 2, torch.float32)
+    with pytest.raises(smx.SwitchError):
+        smx.launch_names(bad)

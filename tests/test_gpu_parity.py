@@ -214,3 +214,34 @@ def test_many_sampled_experts():
     rng = np.random.default_rng(7)
     _check_full(cfg, experts=sorted(rng.choice(cfg.num_experts, 32, replace=False).tolist()))
     torch.cuda.empty_cache()
+
+
+def test_profiled_call_matches_plain_call():
+    # every kernel of the layer can be launched again, alone or repeated,
+    # without changing a result
+    cfg = SMALL.with_(name="profiled", tokens=2000)
+    inp = make_inputs(cfg, device=DEV)
+    C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+    args = (inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C)
+    plain = gpu_outputs_numpy(smx.layer_forward(*args))
+    names = smx.launch_names(smx.binding.make_shape(cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts, C,
+                                                    cfg.torch_dtype))
+    assert names == ["router", "assign", "ffn_up", "ffn_down"]
+    ws = torch.empty(smx.workspace_bytes(smx.binding.make_shape(cfg.tokens, cfg.d_model, cfg.d_ff,
+                                                                cfg.num_experts, C, cfg.torch_dtype)),
+                     dtype=torch.uint8, device=DEV)
+    out = smx.binding._route_outputs(cfg.tokens, cfg.num_experts, torch.device(DEV))
+    out["y"] = torch.empty(cfg.tokens, cfg.d_model, dtype=cfg.torch_dtype, device=DEV)
+    smx.layer_forward(*args, workspace=ws, out=out)
+    n = len(names)
+    for k in range(n):
+        if k > 0:
+            smx.layer_forward_profiled(*args, first_kernel=0, last_kernel=k - 1, workspace=ws, out=out)
+        smx.layer_forward_profiled(*args, first_kernel=k, last_kernel=k, times=3, workspace=ws, out=out)
+        if k < n - 1:
+            smx.layer_forward_profiled(*args, first_kernel=k + 1, last_kernel=n - 1, workspace=ws, out=out)
+        timed = gpu_outputs_numpy(out)
+        for key in plain:
+            assert np.array_equal(plain[key], timed[key]), (names[k], key)
+    with pytest.raises(smx.SwitchError):
+        smx.layer_forward_profiled(*args, first_kernel=n, last_kernel=n, workspace=ws, out=out)
