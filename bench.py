@@ -85,11 +85,26 @@ def read_traffic(kernel: str, digest: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, C: int, min_seconds: float = 10.0) -> dict:
     """The CPU oracle (numpy fp64, as it stands) timed on this host on the same
     workload: the whole layer forward (routing, slots, loss and every expert's
     FFN) for all tokens, repeated until at least min_seconds have elapsed.
-    Inputs are converted to fp64 on the host before the clock starts."""
+    One more pass through the oracle's stage functions (routing + assignment
+    + loss, dispatch to [N][C][d] buffers, the per-expert FFN loop, combine)
+    gives a per-stage breakdown.  Inputs are converted to fp64 on the host
+    before the clock starts."""
+    import numpy as np
     import torch
 
     import oracle.switch_oracle as so
@@ -113,10 +128,35 @@ def cpu_baseline(inp, C: int, min_seconds: float = 10.0) -> dict:
             break
     T = x.shape[0]
     per = elapsed / runs
+
+    # stage breakdown (one pass)
+    st = {}
+    t = time.perf_counter()
+    h = so.router_logits(x, wr, b)
+    p = so.softmax(h)
+    idx, _ = so.top1(h)
+    gate = p[np.arange(T), idx]
+    slot, dropped, count = so.assign_slots(idx, N, C)
+    so.load_balancing_loss(idx, p, N)
+    st["route_assign_loss"] = time.perf_counter() - t
+    t = time.perf_counter()
+    buf, _ = so.dispatch(x, idx, slot, dropped, N, C)
+    st["dispatch"] = time.perf_counter() - t
+    t = time.perf_counter()
+    out = np.zeros_like(buf)
+    for i in range(N):
+        m = int(min(count[i], C))
+        if m:
+            out[i, :m] = so.expert_ffn(buf[i, :m], w[i][0], w[i][1])
+    st["expert_ffn"] = time.perf_counter() - t
+    t = time.perf_counter()
+    so.combine(out, idx, slot, dropped, gate)
+    st["combine"] = time.perf_counter() - t
     return {"value": T / per, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"numpy fp64 oracle, whole layer forward on the full workload ({T} tokens, all {N} "
                        f"experts), {runs} run(s) in {elapsed:.1f} s ({per:.2f} s each); BLAS threads "
-                       f"{threads}, host cores available {len(os.sched_getaffinity(0))}")}
+                       f"{threads}, host cores available {len(os.sched_getaffinity(0))}, CPU {cpu_model()}"),
+            "stages_s": {k: round(v, 4) for k, v in st.items()}}
 
 
 def main() -> int:
