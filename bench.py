@@ -247,6 +247,36 @@ def main() -> int:
             torch.cuda.synchronize()
             kern[name] = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     log("bench: per-kernel ms " + ", ".join(f"{k}={v:.4f}" for k, v in kern.items()))
+
+    # the stage entry points' data-movement kernels on the same routing (not
+    # on the layer path, which gathers and scatters inside the expert FFN):
+    # switch_dispatch (x rows -> [N][C][d]) and switch_combine ([N][C][d] ->
+    # y, here fed the dispatched buffer as expert output), K launches each
+    kept = int(sum(min(int(c), C) for c in counts))
+    disp = torch.empty(N, C, d, dtype=cfg.torch_dtype, device=dev)
+    ystage = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
+    stage_ms = {}
+    with torch.cuda.stream(stream):
+        for name, fn in (("dispatch", lambda: smx.dispatch(inp["x"], out["expert_idx"], out["slot"], out["dropped"],
+                                                           N, C, out=disp)),
+                         ("combine", lambda: smx.combine(disp, out["expert_idx"], out["slot"], out["dropped"],
+                                                         out["gate"], out=ystage))):
+            fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(args.steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            stage_ms[name] = a.elapsed_time(b) / args.steps
+    stage_bytes = {"dispatch": 2 * kept * d * 2 + T * 9,          # read kept x rows, write them; idx/slot/drop
+                   "combine": kept * d * 2 + T * d * 2 + T * 13}  # read kept rows, write every y row; + gate
+    stage_kernels = {k: {"ms": round(v, 5), "alg_bytes": stage_bytes[k],
+                         "GBps": round(stage_bytes[k] / (v * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(stage_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                     for k, v in stage_ms.items()}
+    log("bench: stage kernels " + ", ".join(f"{k}={v['GBps']} GB/s" for k, v in stage_kernels.items()))
     per_kernel = {}
     for k, v in kern.items():
         b = algorithmic_bytes(k, T, d, f, N, C, counts)
@@ -288,6 +318,7 @@ def main() -> int:
         "route": {"ms": round(rdc_ms, 4), "alg_bytes": rdc_b,
                                    "hbm_frac": round(rdc_b / (rdc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "kernels": per_kernel,
+        "stage_kernels": stage_kernels,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.calib_copy:

@@ -7,6 +7,10 @@
         HBM bytes per launch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB
         per dispatch), each scaled by what the same counter reads for a plain
         1 GiB device-to-device copy recorded in the same run
+    python -m sparse_mixture_experts_switch_amd.profsummary mfma DB OUT --cmd "..." --simds N --xcds X --source FILE
+        per kernel: MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES (summed over
+        SIMDs) / (GRBM_GUI_ACTIVE / X x SIMDs) and bf16 MFMA flops per
+        dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
 
 Kernel names are the library's launch names: ffn_up / ffn_down are the
 grouped-GEMM instantiations that gather token rows (ReLU epilogue) and that
@@ -28,6 +32,8 @@ KERNEL_KEYS = {
     "assign": ("assign_one_kernel", ""),
     "assign_scan": ("assign_scan_kernel", ""),
     "assign_apply": ("assign_apply_layer_kernel", ""),
+    "dispatch": ("dispatch_kernel", ""),
+    "combine": ("combine_kernel", ""),
     "copy": ("__amd_rocclr_copyBuffer", ""),
 }
 
@@ -101,6 +107,29 @@ def traffic_summary(fetch_db: str, write_db: str, kernel: str, cmd: str, source:
     ]) + "\n"
 
 
+def mfma_summary(db: str, cmd: str, simds: int, xcds: int, source: str) -> str:
+    busy = _counter(db, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _counter(db, "GRBM_GUI_ACTIVE")
+    mops = _counter(db, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    with open(source, "rb") as fh:
+        digest = hashlib.sha256(fh.read()).hexdigest()[:16]
+    lines = [f"# MFMA use per kernel (base workload), rocprofv3 --pmc", f"# command: {cmd}",
+             f"# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES (sum over SIMDs) / ((GRBM_GUI_ACTIVE / {xcds}) x {simds} SIMDs),",
+             f"#   averaged over dispatches (GRBM_GUI_ACTIVE is stored summed over the {xcds} XCDs' GRBM instances)",
+             f"# bf16_mfma_gflop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / 1e9 per dispatch",
+             f"source_sha256 = {digest}",
+             "# kernel | dispatches | mfma_busy | bf16_mfma_gflop"]
+    for name in sorted(busy, key=lambda n: -sum(busy[n])):
+        short = short_name(name)
+        if short not in KERNEL_KEYS or short == "copy" or name not in gui:
+            continue
+        b, g = busy[name], gui[name]
+        frac = sum(bi / (gi / xcds * simds) for bi, gi in zip(b, g) if gi > 0) / len(b)
+        gf = sum(mops.get(name, [0.0])) / max(len(mops.get(name, [])), 1) * 512 / 1e9
+        lines.append(f"{short} | {len(b)} | {frac:.4f} | {gf:.2f}")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -115,9 +144,20 @@ def main():
     c.add_argument("--kernel", required=True)
     c.add_argument("--cmd", required=True)
     c.add_argument("--source", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("db")
+    m.add_argument("out")
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--simds", type=int, required=True)
+    m.add_argument("--xcds", type=int, required=True)
+    m.add_argument("--source", required=True)
     a = ap.parse_args()
-    text = trace_summary(a.db, a.cmd) if a.mode == "trace" else traffic_summary(
-        a.fetch_db, a.write_db, a.kernel, a.cmd, a.source)
+    if a.mode == "trace":
+        text = trace_summary(a.db, a.cmd)
+    elif a.mode == "traffic":
+        text = traffic_summary(a.fetch_db, a.write_db, a.kernel, a.cmd, a.source)
+    else:
+        text = mfma_summary(a.db, a.cmd, a.simds, a.xcds, a.source)
     with open(a.out, "w") as fh:
         fh.write(text)
     print(text)
