@@ -24,7 +24,10 @@ function that takes it):
   N * sum_i f_i P_i with no alpha; T == 0 gives 0;
 * expert FFN E(x) = W_out . ReLU(W_in . x), no biases;
 * a dropped token's bare output is 0; with the residual flag the output is
-  x + bare output.
+  x + bare output;
+* the block's "Add + Normalize" after the layer is layer normalisation over
+  d_model of x + y (population variance, eps inside the square root, a
+  per-feature scale and shift).
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (hand-worked fixtures under tests/golden/, closed
@@ -234,3 +237,18 @@ def combine(expert_out: np.ndarray, expert_idx: np.ndarray, slot: np.ndarray,
     if x_residual is not None:
         y = y + np.asarray(x_residual, np.float64)
     return y
+
+
+# ---------------------------------------------------------------------------
+# Block epilogue ("The Architecture in Place": the Add + Normalize box after
+# the Switch FFN layer)
+# ---------------------------------------------------------------------------
+def add_normalize(x: np.ndarray, y: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float) -> np.ndarray:
+    """out[t] = (v[t] - mean v[t]) / sqrt(var v[t] + eps) * gamma + beta with
+    v = x + y (the residual add) and the mean and population variance taken
+    over d_model.  Reading: the write-up names the box only; it is taken to be
+    layer normalisation with a per-feature scale gamma and shift beta."""
+    v = np.asarray(x, np.float64) + np.asarray(y, np.float64)
+    mu = v.mean(axis=1, keepdims=True)
+    var = ((v - mu) ** 2).mean(axis=1, keepdims=True)
+    return (v - mu) / np.sqrt(var + eps) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)

@@ -265,11 +265,41 @@ def pin_fed_mode():
     np.testing.assert_allclose(out["y_bare"][3], [1.5, 4.5], atol=1e-14)
 
 
+def pin_add_norm_zscore(rng):
+    """Add + Normalize ('The Architecture in Place'): with eps = 0, unit scale
+    and zero shift it is scipy's z-score of x + y over d_model (population
+    standard deviation)."""
+    import scipy.stats
+    x, y = rng.standard_normal((7, 12)), rng.standard_normal((7, 12)) * 0.1
+    got = so.add_normalize(x, y, np.ones(12), np.zeros(12), 0.0)
+    np.testing.assert_allclose(got, scipy.stats.zscore(x + y, axis=1, ddof=0), rtol=0, atol=1e-12)
+
+
+def pin_add_norm_hand():
+    """A hand-worked row: x + y = [2, 2, 2, 4], mean 5/2, variance 3/4; with
+    eps = 1/4 the denominator is exactly 1, so out = (v - 5/2) * gamma + beta."""
+    out = so.add_normalize(np.array([[1.0, 2.0, 3.0, 4.0]]), np.array([[1.0, 0.0, -1.0, 0.0]]),
+                           np.array([1.0, 2.0, 1.0, 1.0]), np.array([0.0, 0.0, 1.0, 0.0]), 0.25)
+    assert out.tolist() == [[-0.5, -1.0, 0.5, 1.5]]
+
+
+def pin_add_norm_invariants(rng):
+    """Normalisation removes a per-row shift of x + y; scale and shift act per
+    feature after it."""
+    x, y = rng.standard_normal((5, 16)), rng.standard_normal((5, 16))
+    g, b = rng.standard_normal(16), rng.standard_normal(16)
+    base = so.add_normalize(x, y, np.ones(16), np.zeros(16), 1e-6)
+    shifted = so.add_normalize(x + rng.standard_normal((5, 1)) * 3.0, y, np.ones(16), np.zeros(16), 1e-6)
+    np.testing.assert_allclose(shifted, base, atol=1e-10)
+    np.testing.assert_allclose(so.add_normalize(x, y, g, b, 1e-6), base * g + b, atol=1e-12)
+
+
 ALL_PINS = [
     pin_capacity_table, pin_hand_example, pin_softmax_library, pin_top1_bruteforce,
     pin_router_logits_loops, pin_slots_stable_sort, pin_slots_bruteforce,
     pin_aux_uniform_closed_form, pin_ffn_loops, pin_single_expert_dense,
     pin_layer_properties, pin_aux_counts_before_capacity, pin_fed_mode,
+    pin_add_norm_zscore, pin_add_norm_hand, pin_add_norm_invariants,
 ]
 
 
@@ -344,8 +374,26 @@ def _mut_logits_no_bias(x, w_router, bias=None):
     return np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
 
 
+def _mut_norm_sample_variance(x, y, gamma, beta, eps):
+    v = np.asarray(x, np.float64) + np.asarray(y, np.float64)
+    mu = v.mean(axis=1, keepdims=True)
+    var = ((v - mu) ** 2).sum(axis=1, keepdims=True) / (v.shape[1] - 1)
+    return (v - mu) / np.sqrt(var + eps) * gamma + beta
+
+
+def _mut_norm_eps_outside(x, y, gamma, beta, eps):
+    v = np.asarray(x, np.float64) + np.asarray(y, np.float64)
+    mu = v.mean(axis=1, keepdims=True)
+    var = ((v - mu) ** 2).mean(axis=1, keepdims=True)
+    return (v - mu) / (np.sqrt(var) + eps) * gamma + beta
+
+
+def _mut_norm_no_residual(x, y, gamma, beta, eps):
+    return _ORIG["add_normalize"](np.zeros_like(np.asarray(x, np.float64)), y, gamma, beta, eps)
+
+
 _ORIG = {k: getattr(so, k) for k in ("assign_slots", "load_balancing_loss", "top1", "expert_ffn",
-                                     "softmax", "router_logits")}
+                                     "softmax", "router_logits", "add_normalize")}
 
 MUTANTS = {
     "top1_last_index_on_tie": ("top1", _mut_top1_last_tie),
@@ -357,6 +405,9 @@ MUTANTS = {
     "ffn_transposed_w_out": ("expert_ffn", _mut_ffn_transposed),
     "softmax_wrong_axis": ("softmax", _mut_softmax_wrong_axis),
     "router_bias_dropped": ("router_logits", _mut_logits_no_bias),
+    "norm_sample_variance": ("add_normalize", _mut_norm_sample_variance),
+    "norm_eps_outside_sqrt": ("add_normalize", _mut_norm_eps_outside),
+    "norm_without_residual": ("add_normalize", _mut_norm_no_residual),
 }
 
 
