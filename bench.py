@@ -251,16 +251,20 @@ def main() -> int:
     # the stage entry points' data-movement kernels on the same routing (not
     # on the layer path, which gathers and scatters inside the expert FFN):
     # switch_dispatch (x rows -> [N][C][d]) and switch_combine ([N][C][d] ->
-    # y, here fed the dispatched buffer as expert output), K launches each
+    # y, here fed the dispatched buffer as expert output), and the block's
+    # Add + Normalize after the layer (switch_add_norm), K launches each
     kept = int(sum(min(int(c), C) for c in counts))
     disp = torch.empty(N, C, d, dtype=cfg.torch_dtype, device=dev)
+    gamma = torch.ones(d, device=dev)
+    beta = torch.zeros(d, device=dev)
     ystage = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
     stage_ms = {}
     with torch.cuda.stream(stream):
         for name, fn in (("dispatch", lambda: smx.dispatch(inp["x"], out["expert_idx"], out["slot"], out["dropped"],
                                                            N, C, out=disp)),
                          ("combine", lambda: smx.combine(disp, out["expert_idx"], out["slot"], out["dropped"],
-                                                         out["gate"], out=ystage))):
+                                                         out["gate"], out=ystage)),
+                         ("add_norm", lambda: smx.add_norm(inp["x"], out["y"], gamma, beta, 1e-6, out=ystage))):
             fn()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -271,7 +275,8 @@ def main() -> int:
             torch.cuda.synchronize()
             stage_ms[name] = a.elapsed_time(b) / args.steps
     stage_bytes = {"dispatch": 2 * kept * d * 2 + T * 9,          # read kept x rows, write them; idx/slot/drop
-                   "combine": kept * d * 2 + T * d * 2 + T * 13}  # read kept rows, write every y row; + gate
+                   "combine": kept * d * 2 + T * d * 2 + T * 13,  # read kept rows, write every y row; + gate
+                   "add_norm": 3 * T * d * 2 + 2 * d * 4}         # read x and y, write the block output
     stage_kernels = {k: {"ms": round(v, 5), "alg_bytes": stage_bytes[k],
                          "GBps": round(stage_bytes[k] / (v * 1e-3) / 1e9, 1),
                          "hbm_frac": round(stage_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

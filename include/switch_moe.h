@@ -149,6 +149,21 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
                          int32_t *expert_count, float *aux_loss, void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/* The block's "Add + Normalize" after the layer (Switch Transformers
+ * write-up, "The Architecture in Place", the block figure): for every token t,
+ * out[t] = (v - mean v) / sqrt(var v + eps) * gamma + beta with v = x[t] +
+ * y[t] (layer normalisation over d_model: mean and population variance of the
+ * row; x may be NULL, then v = y[t]).  Typical use: y = the bare output of
+ * switch_layer_forward (add_residual = 0) and x its input, so the residual add
+ * happens in fp32 inside the normalisation.  Uses s->tokens, s->d_model,
+ * s->dtype: x, y, out [T][d] of that dtype (16-byte aligned); gamma, beta [d]
+ * fp32; eps finite and >= 0.  out may be y itself (in place); it must not
+ * overlap x or y otherwise.  Arithmetic in fp32, one rounding to the output
+ * dtype; deterministic.  SWITCH_E_UNSUPPORTED for d_model above 4096 (bf16) /
+ * 2048 (fp32). */
+int switch_add_norm(const switch_shape *s, const void *x, const void *y, const float *gamma, const float *beta,
+                    float eps, void *out, void *stream);
+
 /* Measurement variant of switch_layer_forward: same arguments and
  * asynchrony, but it launches only the kernels numbered first_kernel ..
  * last_kernel of the call (0-based, in the order switch_launch_names gives),

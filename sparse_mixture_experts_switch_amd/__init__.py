@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     SWITCH_BF16,
     SWITCH_F32,
     SwitchError,
+    add_norm,
     capacity,
     combine,
     dispatch,

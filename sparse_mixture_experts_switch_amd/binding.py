@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "SwitchError", "load_library", "capacity", "workspace_bytes", "route", "dispatch",
-    "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "launch_names",
+    "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "launch_names", "add_norm",
     "SWITCH_F32", "SWITCH_BF16",
 ]
 
@@ -29,7 +29,7 @@ _CODES = {-1: "SWITCH_E_INVALID", -2: "SWITCH_E_UNSUPPORTED", -3: "SWITCH_E_WORK
 EXPORTED = [
     "switch_capacity", "switch_workspace_bytes", "switch_last_error", "switch_route", "switch_dispatch",
     "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
-    "switch_launch_names",
+    "switch_launch_names", "switch_add_norm",
 ]
 
 
@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P, ctypes.c_int32, ctypes.c_int32,
                                                                ctypes.c_int32])
     lib.switch_launch_names.argtypes = [sp, _P, ctypes.c_int32, _P]
+    lib.switch_add_norm.argtypes = [sp, _P, _P, _P, _P, ctypes.c_float, _P, _P]
     for name in EXPORTED:
         if name != "switch_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -236,6 +237,18 @@ def layer_forward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, fir
     `times` times back to back (switch_layer_forward_profiled); asynchronous."""
     _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
     _check(load_library().switch_layer_forward_profiled(*args, int(first_kernel), int(last_kernel), int(times)))
+    return o
+
+
+def add_norm(x: torch.Tensor | None, y: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """Layer normalisation over d_model of x + y (x may be None): the block's
+    Add + Normalize after the layer (switch_add_norm).  out may be y."""
+    T, d = y.shape
+    shape = make_shape(T, d, 64, 1, 0, y.dtype)
+    o = out if out is not None else torch.empty_like(y)
+    _check(load_library().switch_add_norm(ctypes.byref(shape), _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta),
+                                          float(eps), _ptr(o), _stream(y.device)))
     return o
 
 

@@ -389,6 +389,28 @@ int switch_combine(const switch_shape *s, const void *expert_out, const int32_t 
   })
 }
 
+int switch_add_norm(const switch_shape *s, const void *x, const void *y, const float *gamma, const float *beta,
+                    float eps, void *out, void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(SWITCH_E_INVALID, "eps = %g: need a finite eps >= 0", eps);
+    if (s->d_model > add_norm_max_d(s->dtype))
+      return fail(SWITCH_E_UNSUPPORTED, "d_model = %d above %d for add_norm", s->d_model,
+                  add_norm_max_d(s->dtype));
+    if (s->tokens > 0) {
+      NEED(y, 16);
+      NEED(out, 16);
+      NEED(gamma, 4);
+      NEED(beta, 4);
+      if (x && !aligned(x, 16)) return fail(SWITCH_E_INVALID, "x is not 16-byte aligned");
+    }
+    AddNormArgs a{s->dtype, s->tokens, s->d_model, x, y, gamma, beta, eps, out};
+    hipError_t e = launch_add_norm(a, (hipStream_t)stream);
+    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "add_norm launch");
+  })
+}
+
 int switch_layer_forward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
                          const void *w_in, const void *w_out, int32_t add_residual, void *y, int32_t *expert_idx,
                          float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,

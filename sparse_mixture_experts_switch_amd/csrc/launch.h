@@ -66,6 +66,17 @@ struct CombineArgs {
   void *y;
 };
 
+struct AddNormArgs {
+  int dtype;
+  int64_t T;
+  int d;
+  const void *x;  // may be null
+  const void *y;
+  const float *gamma, *beta;
+  float eps;
+  void *out;  // may equal y
+};
+
 // One grouped GEMM of the expert FFN (see ffn.hip).
 struct GemmCall {
   int dtype, N, C, K, Nout;
@@ -104,6 +115,8 @@ hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st);
 hipError_t launch_ffn_up_gather(const GemmCall &c, hipStream_t st);
 hipError_t launch_ffn_down_combine(const GemmCall &c, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+hipError_t launch_add_norm(const AddNormArgs &a, hipStream_t st);
+int add_norm_max_d(int dtype);  // largest d_model the row-in-registers kernel takes
 
 inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
 // Row stride (elements) of the per-block count and P-partial arrays: rows

@@ -10,6 +10,10 @@
 //
 // Both kernels move whole rows with 16-byte vector accesses, one wave per
 // token; they are bound by HBM bandwidth.
+//
+// The block's Add + Normalize after the layer (the architecture figure of
+// "The Architecture in Place") is here too: layer normalisation over d_model
+// of x + y, one wave per row.
 
 #include "common.h"
 #include "launch.h"
@@ -85,6 +89,101 @@ __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
 }
 
 static inline int esize(int dtype) { return dtype == kBF16 ? 2 : 4; }
+
+// out[t] = (v - mean v) / sqrt(var v + eps) * gamma + beta, v = x[t] + y[t]
+// (x may be null), in fp32: the row stays in registers (P pieces of 16 bytes
+// per lane), the mean and then the sum of squared deviations are each summed
+// per lane in order and across the wave by fixed-order butterflies, so every
+// run gives the same bits.  One rounding to the output type.
+template <typename T_, int P>
+__global__ __launch_bounds__(kMoveThreads) void add_norm_kernel(const u32x4 *__restrict__ x, const u32x4 *y,
+                                                               const float *__restrict__ gamma,
+                                                               const float *__restrict__ beta, float eps,
+                                                               u32x4 *out, int64_t T, int d) {
+  constexpr int kE = 16 / sizeof(T_);  // values per 16-byte piece
+  const int64_t t = (int64_t)blockIdx.x * kMoveTokens + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (t >= T) return;
+  const int pieces = d / kE;
+  float v[P][kE];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int c = lane + i * kWave;
+    const bool in = c < pieces;
+    const int cc = in ? c : 0;
+    const u32x4 yv = y[t * pieces + cc];
+    const u32x4 xv = x ? x[t * pieces + cc] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kE; ++k) {
+      float a, b;
+      if constexpr (sizeof(T_) == 2) {
+        a = (float)as_bf16x8(yv)[k];
+        b = (float)as_bf16x8(xv)[k];
+      } else {
+        a = __builtin_bit_cast(f32x4, yv)[k];
+        b = __builtin_bit_cast(f32x4, xv)[k];
+      }
+      v[i][k] = in ? a + b : 0.f;
+      sum += v[i][k];
+    }
+  }
+  const float mean = wave_sum(sum) / (float)d;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (lane + i * kWave < pieces) {
+#pragma unroll
+      for (int k = 0; k < kE; ++k) {
+        const float dv = v[i][k] - mean;
+        sq += dv * dv;
+      }
+    }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int c = lane + i * kWave;
+    if (c >= pieces) continue;
+    u32x4 o;
+    if constexpr (sizeof(T_) == 2) {
+      bf16x8 r;
+#pragma unroll
+      for (int k = 0; k < kE; ++k) r[k] = (bf16)((v[i][k] - mean) * rstd * gamma[c * kE + k] + beta[c * kE + k]);
+      o = as_u32x4(r);
+    } else {
+      f32x4 r;
+#pragma unroll
+      for (int k = 0; k < kE; ++k) r[k] = (v[i][k] - mean) * rstd * gamma[c * kE + k] + beta[c * kE + k];
+      o = __builtin_bit_cast(u32x4, r);
+    }
+    out[t * pieces + c] = o;
+  }
+}
+
+template <typename T_, int P>
+hipError_t run_add_norm(const AddNormArgs &a, hipStream_t st) {
+  add_norm_kernel<T_, P><<<dim3((unsigned)ceil_div(a.T, kMoveTokens)), dim3(kMoveThreads), 0, st>>>(
+      (const u32x4 *)a.x, (const u32x4 *)a.y, a.gamma, a.beta, a.eps, (u32x4 *)a.out, a.T, a.d);
+  return hipGetLastError();
+}
+
+template <typename T_>
+hipError_t add_norm_dispatch(const AddNormArgs &a, hipStream_t st) {
+  const int pieces = a.d / (16 / (int)sizeof(T_));
+  const int per = (int)ceil_div(pieces, kWave);
+  if (per <= 1) return run_add_norm<T_, 1>(a, st);
+  if (per <= 2) return run_add_norm<T_, 2>(a, st);
+  if (per <= 4) return run_add_norm<T_, 4>(a, st);
+  if (per <= 8) return run_add_norm<T_, 8>(a, st);
+  return hipErrorInvalidValue;
+}
+
+int add_norm_max_d(int dtype) { return 8 * kWave * (dtype == kBF16 ? 8 : 4); }
+
+hipError_t launch_add_norm(const AddNormArgs &a, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  return a.dtype == kBF16 ? add_norm_dispatch<bf16>(a, st) : add_norm_dispatch<float>(a, st);
+}
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st) {
   if (a.T == 0 || a.C == 0) return hipSuccess;

@@ -122,6 +122,14 @@ def test_entry_points_reject_before_launch():
     # dispatch: NULL dropped
     rc = lib.switch_dispatch(ctypes.byref(s), good, good, good, None, good, None)
     assert rc == B.SWITCH_E_INVALID
+    # add_norm: negative / NaN eps, NULL gamma, misaligned out, d_model too large
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert lib.switch_add_norm(ctypes.byref(s), good, good, good, good, eps, good, None) == B.SWITCH_E_INVALID
+    assert lib.switch_add_norm(ctypes.byref(s), good, good, None, good, 1e-6, good, None) == B.SWITCH_E_INVALID
+    assert lib.switch_add_norm(ctypes.byref(s), good, good, good, good, 1e-6, odd, None) == B.SWITCH_E_INVALID
+    wide = B.make_shape(64, 8192, 256, 8, 16, torch.bfloat16)
+    assert lib.switch_add_norm(ctypes.byref(wide), good, good, good, good, 1e-6, good, None) == \
+        B.SWITCH_E_UNSUPPORTED
     # profiled: empty kernel range / times < 1
     for first, last, times in ((0, 0, 0), (2, 1, 1), (-1, 0, 1)):
         rc = lib.switch_layer_forward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good,

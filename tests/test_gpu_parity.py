@@ -245,3 +245,44 @@ def test_profiled_call_matches_plain_call():
             assert np.array_equal(plain[key], timed[key]), (names[k], key)
     with pytest.raises(smx.SwitchError):
         smx.layer_forward_profiled(*args, first_kernel=n, last_kernel=n, workspace=ws, out=out)
+
+
+# ------------------------------------------------ Add + Normalize after the layer --
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_add_norm_after_layer(dtype):
+    """The block's Add + Normalize ('The Architecture in Place') on the layer's
+    bare output: against the oracle's layer normalisation of x + y fed the
+    GPU's own y (the kernel's arithmetic alone), and end to end against the
+    oracle's y; in place equals out of place; repeat runs give the same bits."""
+    cfg = SMALL.with_(name=f"add_norm_{dtype}", dtype=dtype, tokens=777, d_model=192)
+    inp = make_inputs(cfg, device=DEV)
+    C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+    o = smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C)
+    gen = torch.Generator().manual_seed(5)
+    gamma = (1.0 + 0.1 * torch.randn(cfg.d_model, generator=gen)).to(DEV)
+    beta = (0.1 * torch.randn(cfg.d_model, generator=gen)).to(DEV)
+    eps = 1e-6
+    out = smx.add_norm(inp["x"], o["y"], gamma, beta, eps)
+    again = smx.add_norm(inp["x"], o["y"], gamma, beta, eps)
+    inplace = o["y"].clone()
+    smx.add_norm(inp["x"], inplace, gamma, beta, eps, out=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again) and torch.equal(out, inplace)
+    g = f64(out)
+    x, y, ga, be = f64(inp["x"]), f64(o["y"]), f64(gamma), f64(beta)
+    ref = so.add_normalize(x, y, ga, be, eps)
+    # fp32 arithmetic on O(1) normalised values, one rounding to the output type
+    rnd = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    err = np.abs(g - ref)
+    assert np.all(err <= 1e-5 + rnd * np.abs(ref)), err.max()
+    # end to end: the oracle's own bare output (the layer's tolerance moves y by
+    # far less than one bf16 step of x + y)
+    fed = oracle_run(inp, C, expert_idx=gpu_outputs_numpy(o)["expert_idx"])
+    ref2 = so.add_normalize(x, fed["y_bare"], ga, be, eps)
+    err2 = np.abs(g - ref2)
+    assert np.all(err2 <= 1e-4 + 2 * rnd * np.abs(ref2)), err2.max()
+    # without x: normalisation of y alone
+    only_y = f64(smx.add_norm(None, o["y"], gamma, beta, eps))
+    np.testing.assert_allclose(only_y, so.add_normalize(np.zeros_like(y), y, ga, be, eps),
+                               atol=1e-4, rtol=2 * rnd)
+    say(f"  add_norm {dtype}: max err {err.max():.3e} (vs fed), {err2.max():.3e} (end to end)")
