@@ -11,7 +11,8 @@ imports the HIP path, its binding or its library.
 
 Inputs are numpy arrays holding the exact values of the layer's inputs
 (bf16 / fp32 values widened to float64 without rounding).  Every step is in
-float64; numpy's matmul, exp and argmax are the only library primitives used.
+float64; numpy's matmul, exp, argmax and (top-k) stable argsort are the only
+library primitives used.
 
 Readings taken where the write-up leaves a step open (each is repeated at the
 function that takes it):
@@ -27,7 +28,14 @@ function that takes it):
   x + bare output;
 * the block's "Add + Normalize" after the layer is layer normalisation over
   d_model of x + y (population variance, eps inside the square root, a
-  per-feature scale and shift).
+  per-feature scale and shift);
+* classic top-k routing (the variant the Switch layer simplifies): a token's
+  k routes go to its k largest logits, in decreasing order (ties to the lower
+  index); each route's gate is the full softmax p_i(x), not renormalised over
+  the k chosen experts; routes claim capacity route-major (every token's
+  first choice, in token order, before any second choice); the capacity is
+  the caller's (k T / N x cf when each expert receives k routes' worth of
+  tokens); f_i is the fraction of the k T routes that choose expert i.
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (hand-worked fixtures under tests/golden/, closed
@@ -252,3 +260,94 @@ def add_normalize(x: np.ndarray, y: np.ndarray, gamma: np.ndarray, beta: np.ndar
     mu = v.mean(axis=1, keepdims=True)
     var = ((v - mu) ** 2).mean(axis=1, keepdims=True)
     return (v - mu) / np.sqrt(var + eps) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Classic top-k routing ("Switch Routing: From Top-k to k = 1": the router
+# sends each token to its top-k experts and the output is the gate-weighted
+# sum over that set)
+# ---------------------------------------------------------------------------
+def topk_choice(h: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """The k experts with the largest logits, best first: idx [k][T].
+
+    Order: larger logit first, the lower expert index first among equal
+    logits (a stable sort of -h).  Also returns, per token, the smallest gap
+    between consecutive logits among the min(k + 1, N) largest (+inf for
+    N == 1): below it a rounding difference can change the chosen set or its
+    order.
+    """
+    T, N = h.shape
+    if not 1 <= k <= N:
+        raise ValueError("need 1 <= k <= N")
+    order = np.argsort(-h, axis=1, kind="stable")
+    idx = order[:, :k].T.astype(np.int64).copy()
+    m = min(k + 1, N)
+    top = np.take_along_axis(h, order[:, :m], axis=1)
+    gap = np.min(top[:, :-1] - top[:, 1:], axis=1) if m > 1 else np.full(T, np.inf)
+    return idx, gap
+
+
+def assign_slots_topk(expert_idx: np.ndarray, num_experts: int, capacity: int):
+    """Slots of the k routes of every token, route-major.
+
+    The routes are ranked (route 0 of tokens 0..T-1, then route 1 of tokens
+    0..T-1, ...); a route's slot is the number of earlier-ranked routes to
+    the same expert and it is dropped when that reaches the capacity.  With
+    the routes laid out [k][T] that order is the flattened order, so this is
+    the token-order assignment applied to the k T routes.  Returns slot and
+    dropped [k][T] and count [N] (routes per expert before capacity).
+    """
+    k, T = expert_idx.shape
+    slot, dropped, count = assign_slots(expert_idx.reshape(-1), num_experts, capacity)
+    return slot.reshape(k, T), dropped.reshape(k, T), count
+
+
+def load_balancing_loss_topk(expert_idx: np.ndarray, probs: np.ndarray, num_experts: int) -> float:
+    """N * sum_i f_i P_i with f_i = (routes choosing i) / (k T) and P_i the
+    batch mean of p_i(x); k = 1 gives the Switch loss."""
+    k, T = expert_idx.shape
+    if T == 0:
+        return 0.0
+    f = np.zeros(num_experts)
+    for i in range(num_experts):
+        f[i] = np.count_nonzero(expert_idx == i) / (k * T)
+    P = probs.sum(axis=0) / T
+    return float(num_experts * np.sum(f * P))
+
+
+def forward_topk(x: np.ndarray, w_router: np.ndarray, router_bias, w_in, w_out, capacity: int, k: int,
+                 add_residual: bool = False, expert_idx: np.ndarray | None = None) -> dict:
+    """Top-k MoE layer: y[t] = sum over the token's kept routes r of
+    p_{e_r}(x) E_{e_r}(x) (+ x with the residual flag).
+
+    expert_idx [k][T], when given, replaces the oracle's own choice ("fed"
+    mode).  Outputs as forward(), with the routing arrays [k][T].
+    """
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    N = w_router.shape[0]
+    h = router_logits(x, w_router, router_bias)
+    p = softmax(h) if T else np.zeros((0, N))
+    own_idx, gap = topk_choice(h, k) if T else (np.zeros((k, 0), np.int64), np.zeros(0))
+    idx = own_idx if expert_idx is None else np.asarray(expert_idx, np.int64).reshape(k, T)
+    gate = np.empty((k, T))
+    for r in range(k):
+        gate[r] = p[np.arange(T), idx[r]]
+    slot, dropped, count = assign_slots_topk(idx, N, capacity)
+    aux = load_balancing_loss_topk(idx, p, N)
+
+    get = _weights(w_in, w_out)
+    y_bare = np.zeros((T, d))
+    for i in range(N):
+        for r in range(k):
+            rows = np.nonzero((idx[r] == i) & ~dropped[r])[0]
+            if len(rows) == 0:
+                continue
+            wi, wo = get(i)
+            y_bare[rows] += gate[r, rows, None] * expert_ffn(x[rows], wi, wo)
+    y = x + y_bare if add_residual else y_bare
+    return {
+        "logits": h, "probs": p, "expert_idx": idx, "own_expert_idx": own_idx,
+        "gap": gap, "gate": gate, "slot": slot, "dropped": dropped,
+        "expert_count": count, "aux_loss": aux, "y_bare": y_bare, "y": y,
+    }

@@ -34,6 +34,7 @@ KERNEL_KEYS = {
     "assign_apply": ("assign_apply_layer_kernel", ""),
     "dispatch": ("dispatch_kernel", ""),
     "combine": ("combine_kernel", ""),
+    "add_norm": ("add_norm_kernel", ""),
     "copy": ("__amd_rocclr_copyBuffer", ""),
 }
 

@@ -294,12 +294,128 @@ def pin_add_norm_invariants(rng):
     np.testing.assert_allclose(so.add_normalize(x, y, g, b, 1e-6), base * g + b, atol=1e-12)
 
 
+def _top2_hand_inputs():
+    g = _load("top2_hand_example.json")
+    inp = g["inputs"]
+    x = np.array(inp["x_over_ln2"], np.float64) * math.log(2.0)
+    w_r = np.array(inp["w_router"], np.float64)
+    w_in = np.stack([np.eye(3)] * 3)
+    w_out = np.stack([s * np.eye(3) for s in inp["w_out_scale"]])
+    return g, x, w_r, w_in, w_out
+
+
+def pin_topk_hand_example():
+    """The hand-worked top-2 layer (tests/golden/top2_hand_example.json):
+    choice order, un-renormalised gates, route-major capacity, the loss."""
+    g, x, w_r, w_in, w_out = _top2_hand_inputs()
+    exp = g["expected"]
+    for cap in (2, 3):
+        e = exp[f"capacity_{cap}"]
+        out = so.forward_topk(x, w_r, None, w_in, w_out, cap, 2)
+        np.testing.assert_allclose(out["probs"] * 7, exp["probs_times_7"], rtol=0, atol=1e-13)
+        assert out["expert_idx"].tolist() == exp["expert_idx"]
+        np.testing.assert_allclose(out["gate"] * 7, exp["gate_times_7"], rtol=0, atol=1e-13)
+        assert out["dropped"].tolist() == e["dropped"]
+        coef = np.array([n / d for n, d in e["y_over_x_num_den"]])
+        np.testing.assert_allclose(out["y_bare"], coef[:, None] * x, rtol=0, atol=1e-13)
+        if "slot" in e:
+            assert out["slot"].tolist() == e["slot"]
+            assert out["expert_count"].tolist() == e["expert_count"]
+            n, d = e["aux_loss_num_den"]
+            assert abs(out["aux_loss"] - n / d) < 1e-14
+
+
+def pin_topk_choice_loops(rng):
+    """Top-k selection ('Switch Routing: From Top-k to k = 1'): repeated
+    explicit-loop argmax with the chosen entries removed, on coarse values
+    with many ties; the near-tie gap by brute force over sorted values."""
+    for N, k in ((5, 2), (4, 4), (6, 3), (2, 1)):
+        h = np.round(rng.standard_normal((150, N)), 1)
+        idx, gap = so.topk_choice(h, k)
+        for t in range(150):
+            left = list(range(N))
+            for r in range(k):
+                best = left[0]
+                for j in left[1:]:
+                    if h[t, j] > h[t, best]:
+                        best = j
+                assert idx[r, t] == best
+                left.remove(best)
+            srt = sorted(h[t], reverse=True)[:min(k + 1, N)]
+            want = min(a - b for a, b in zip(srt, srt[1:])) if len(srt) > 1 else math.inf
+            assert gap[t] == want
+
+
+def pin_topk_k1_is_switch(rng):
+    """k = 1 is the Switch layer: every output equals the top-1 oracle's,
+    with drops (skewed bias) and with the residual."""
+    T, d, f, N = 30, 5, 7, 4
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, N, scale=2.0)
+    b = np.array([1.0, 0.0, -0.5, 0.3])
+    for cap in (3, 8, 30):
+        for res in (False, True):
+            a = so.forward(x, w_r, b, w_in, w_out, cap, add_residual=res)
+            t = so.forward_topk(x, w_r, b, w_in, w_out, cap, 1, add_residual=res)
+            for key in ("expert_idx", "gate", "slot", "dropped"):
+                np.testing.assert_array_equal(t[key][0], a[key])
+            np.testing.assert_array_equal(t["expert_count"], a["expert_count"])
+            assert t["aux_loss"] == a["aux_loss"]
+            np.testing.assert_allclose(t["y"], a["y"], rtol=0, atol=1e-13)
+
+
+def pin_topk_dense_mixture(rng):
+    """k = N with room for every route is the dense softmax mixture
+    sum_i p_i(x) E_i(x) over all experts (scipy's softmax, einsum experts)."""
+    T, d, f, N = 12, 4, 6, 3
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, N)
+    out = so.forward_topk(x, w_r, None, w_in, w_out, N * T, N)
+    p = scipy.special.softmax(x @ w_r.T, axis=1)
+    hid = np.maximum(np.einsum("td,nfd->ntf", x, w_in), 0.0)
+    e = np.einsum("ntf,ndf->ntd", hid, w_out)
+    np.testing.assert_allclose(out["y_bare"], np.einsum("tn,ntd->td", p, e), rtol=0, atol=1e-12)
+    assert not out["dropped"].any()
+    np.testing.assert_allclose(out["gate"].sum(axis=0), 1.0, rtol=0, atol=1e-14)
+
+
+def pin_topk_route_major_bruteforce():
+    """Route-major capacity over every top-2 routing of T <= 4 tokens over
+    N = 3 experts: route 0's slots are the top-1 slots of route 0 alone (a
+    second choice never displaces a first choice); each expert's slots run
+    0..count-1 in route-major order; conservation over the 2T routes."""
+    pairs = [(a, b) for a in range(3) for b in range(3) if a != b]
+    for T in range(0, 5):
+        for choice in itertools.product(pairs, repeat=T):
+            idx = np.array(choice, np.int64).reshape(T, 2).T if T else np.zeros((2, 0), np.int64)
+            for C in (0, 1, 2, 2 * T):
+                slot, dropped, count = so.assign_slots_topk(idx, 3, C)
+                s0, d0, _ = so.assign_slots(idx[0], 3, C)
+                assert np.array_equal(slot[0], s0) and np.array_equal(dropped[0], d0)
+                for i in range(3):
+                    seq = [slot[r, t] for r in range(2) for t in range(T) if idx[r, t] == i]
+                    assert seq == list(range(len(seq))) and count[i] == len(seq)
+                assert sum(min(c, C) for c in count) + int(dropped.sum()) == 2 * T
+
+
+def pin_topk_aux_uniform():
+    """'The Load-Balancing Loss' closed form carried to k routes: with every
+    p_i = 1/N (W_r = 0) the loss is sum_i f_i = 1 whatever the routing."""
+    rng = np.random.default_rng(7)
+    for N, k in ((2, 2), (5, 2), (8, 3)):
+        T, d = 4 * N, 6
+        x = rng.standard_normal((T, d))
+        out = so.forward_topk(x, np.zeros((N, d)), None, np.zeros((N, 2, d)), np.zeros((N, d, 2)), T, k)
+        assert abs(out["aux_loss"] - 1.0) < 1e-13
+        assert out["expert_idx"].tolist() == [[r] * T for r in range(k)]  # all-tie -> lowest indices
+
+
 ALL_PINS = [
     pin_capacity_table, pin_hand_example, pin_softmax_library, pin_top1_bruteforce,
     pin_router_logits_loops, pin_slots_stable_sort, pin_slots_bruteforce,
     pin_aux_uniform_closed_form, pin_ffn_loops, pin_single_expert_dense,
     pin_layer_properties, pin_aux_counts_before_capacity, pin_fed_mode,
     pin_add_norm_zscore, pin_add_norm_hand, pin_add_norm_invariants,
+    pin_topk_hand_example, pin_topk_choice_loops, pin_topk_k1_is_switch, pin_topk_dense_mixture,
+    pin_topk_route_major_bruteforce, pin_topk_aux_uniform,
 ]
 
 
@@ -392,8 +508,44 @@ def _mut_norm_no_residual(x, y, gamma, beta, eps):
     return _ORIG["add_normalize"](np.zeros_like(np.asarray(x, np.float64)), y, gamma, beta, eps)
 
 
+def _mut_topk_token_major(expert_idx, num_experts, capacity):
+    k, T = expert_idx.shape
+    slot, dropped, count = _ORIG["assign_slots"](expert_idx.T.reshape(-1), num_experts, capacity)
+    return slot.reshape(T, k).T, dropped.reshape(T, k).T, count
+
+
+def _mut_topk_last_tie(h, k):
+    N = h.shape[1]
+    order = (N - 1 - np.argsort(-h[:, ::-1], axis=1, kind="stable"))
+    idx = order[:, :k].T.astype(np.int64).copy()
+    return idx, _ORIG["topk_choice"](h, k)[1]
+
+
+def _mut_topk_f_over_T(expert_idx, probs, num_experts):
+    return _ORIG["load_balancing_loss_topk"](expert_idx, probs, num_experts) * expert_idx.shape[0]
+
+
+def _mut_topk_renormalised(*args, **kw):
+    out = _ORIG["forward_topk"](*args, **kw)
+    s = out["gate"].sum(axis=0)
+    out["y_bare"] = out["y_bare"] / s[:, None]
+    return out
+
+
+def _mut_topk_skips_second(*args, **kw):
+    out = _ORIG["forward_topk"](*args, **kw)
+    k = out["expert_idx"].shape[0]
+    if k > 1:
+        args = list(args)
+        x, w_r, b, w_in, w_out, cap = args[:6]
+        first = so.forward(x, w_r, b, w_in, w_out, cap, expert_idx=out["expert_idx"][0])
+        out["y_bare"] = first["y_bare"]
+    return out
+
+
 _ORIG = {k: getattr(so, k) for k in ("assign_slots", "load_balancing_loss", "top1", "expert_ffn",
-                                     "softmax", "router_logits", "add_normalize")}
+                                     "softmax", "router_logits", "add_normalize", "topk_choice",
+                                     "load_balancing_loss_topk", "forward_topk")}
 
 MUTANTS = {
     "top1_last_index_on_tie": ("top1", _mut_top1_last_tie),
@@ -408,6 +560,11 @@ MUTANTS = {
     "norm_sample_variance": ("add_normalize", _mut_norm_sample_variance),
     "norm_eps_outside_sqrt": ("add_normalize", _mut_norm_eps_outside),
     "norm_without_residual": ("add_normalize", _mut_norm_no_residual),
+    "topk_token_major_capacity": ("assign_slots_topk", _mut_topk_token_major),
+    "topk_last_index_on_tie": ("topk_choice", _mut_topk_last_tie),
+    "topk_f_over_T": ("load_balancing_loss_topk", _mut_topk_f_over_T),
+    "topk_renormalised_gates": ("forward_topk", _mut_topk_renormalised),
+    "topk_second_route_ignored": ("forward_topk", _mut_topk_skips_second),
 }
 
 
