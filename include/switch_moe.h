@@ -164,6 +164,37 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
 int switch_add_norm(const switch_shape *s, const void *x, const void *y, const float *gamma, const float *beta,
                     float eps, void *out, void *stream);
 
+/* Classic top-k MoE layer, the variant the Switch layer simplifies
+ * ("Switch Routing: From Top-k to k = 1": each token goes to its top-k
+ * experts and the output is the gate-weighted sum y = sum over the selected
+ * set of p_i(x) E_i(x)), for top_k = 1 or 2.  top_k = 1 gives exactly
+ * switch_layer_forward.  Readings of what the write-up leaves open:
+ *   - route r (0-based) of a token goes to its expert with the (r+1)-th
+ *     largest logit; equal logits rank the lower index first;
+ *   - gate[r][t] = p_i(x) of that expert (the full softmax, not renormalised
+ *     over the chosen experts);
+ *   - capacity is claimed route-major: all first routes in token order, then
+ *     all second routes; slot[r][t] = number of earlier routes in that order to
+ *     the same expert; dropped[r][t] = slot >= capacity (a dropped route adds
+ *     nothing; the token keeps its other routes).  s->capacity is the caller's
+ *     (switch_capacity(top_k * tokens, ...) gives k T / N x cf, room for k
+ *     routes' worth of tokens);
+ *   - expert_count[i] = routes to expert i before capacity; aux_loss = N sum_i
+ *     f_i P_i with f_i = expert_count[i] / (top_k T).
+ * Arguments as switch_layer_forward, except: expert_idx, gate, slot, dropped
+ * are [top_k][T] (route-major); workspace of switch_topk_workspace_bytes
+ * (for top_k = 2 it holds a [2][T][d_model] buffer of gate-scaled expert
+ * outputs that a last kernel sums per token, in route order, in fp32, with one
+ * rounding to y's dtype).  Errors: SWITCH_E_INVALID for top_k < 1 or above
+ * num_experts; SWITCH_E_UNSUPPORTED for top_k > 2 or top_k x tokens above
+ * 2^31-1. */
+int switch_topk_workspace_bytes(const switch_shape *s, int32_t top_k, size_t *bytes_out);
+int switch_topk_layer_forward(const switch_shape *s, int32_t top_k, const void *x, const float *w_router,
+                              const float *router_bias, const void *w_in, const void *w_out, int32_t add_residual,
+                              void *y, int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
+                              int32_t *expert_count, float *aux_loss, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* Measurement variant of switch_layer_forward: same arguments and
  * asynchrony, but it launches only the kernels numbered first_kernel ..
  * last_kernel of the call (0-based, in the order switch_launch_names gives),

@@ -21,5 +21,7 @@ from .binding import (  # noqa: F401
     launch_names,
     load_library,
     route,
+    topk_layer_forward,
+    topk_workspace_bytes,
     workspace_bytes,
 )

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "SwitchError", "load_library", "capacity", "workspace_bytes", "route", "dispatch",
     "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "launch_names", "add_norm",
-    "SWITCH_F32", "SWITCH_BF16",
+    "topk_workspace_bytes", "topk_layer_forward", "SWITCH_F32", "SWITCH_BF16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswitchmoe.so")
@@ -29,7 +29,7 @@ _CODES = {-1: "SWITCH_E_INVALID", -2: "SWITCH_E_UNSUPPORTED", -3: "SWITCH_E_WORK
 EXPORTED = [
     "switch_capacity", "switch_workspace_bytes", "switch_last_error", "switch_route", "switch_dispatch",
     "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
-    "switch_launch_names", "switch_add_norm",
+    "switch_launch_names", "switch_add_norm", "switch_topk_workspace_bytes", "switch_topk_layer_forward",
 ]
 
 
@@ -74,6 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                                ctypes.c_int32])
     lib.switch_launch_names.argtypes = [sp, _P, ctypes.c_int32, _P]
     lib.switch_add_norm.argtypes = [sp, _P, _P, _P, _P, ctypes.c_float, _P, _P]
+    lib.switch_topk_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.switch_topk_layer_forward.argtypes = (
+        [sp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P])
     for name in EXPORTED:
         if name != "switch_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -132,12 +135,13 @@ def _workspace(shape: Shape, dev: torch.device, ws: torch.Tensor | None) -> torc
     return ws
 
 
-def _route_outputs(T: int, N: int, dev: torch.device) -> dict:
+def _route_outputs(T: int, N: int, dev: torch.device, k: int | None = None) -> dict:
+    rt = (T,) if k is None else (k, T)
     return {
-        "expert_idx": torch.empty(T, dtype=torch.int32, device=dev),
-        "gate": torch.empty(T, dtype=torch.float32, device=dev),
-        "slot": torch.empty(T, dtype=torch.int32, device=dev),
-        "dropped": torch.empty(T, dtype=torch.uint8, device=dev),
+        "expert_idx": torch.empty(rt, dtype=torch.int32, device=dev),
+        "gate": torch.empty(rt, dtype=torch.float32, device=dev),
+        "slot": torch.empty(rt, dtype=torch.int32, device=dev),
+        "dropped": torch.empty(rt, dtype=torch.uint8, device=dev),
         "expert_count": torch.empty(N, dtype=torch.int32, device=dev),
         "aux_loss": torch.empty(1, dtype=torch.float32, device=dev),
     }
@@ -249,6 +253,35 @@ def add_norm(x: torch.Tensor | None, y: torch.Tensor, gamma: torch.Tensor, beta:
     o = out if out is not None else torch.empty_like(y)
     _check(load_library().switch_add_norm(ctypes.byref(shape), _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta),
                                           float(eps), _ptr(o), _stream(y.device)))
+    return o
+
+
+def topk_workspace_bytes(shape: Shape, top_k: int) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().switch_topk_workspace_bytes(ctypes.byref(shape), int(top_k), ctypes.byref(out)))
+    return out.value
+
+
+def topk_layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None,
+                       w_in: torch.Tensor, w_out: torch.Tensor, capacity_: int, top_k: int,
+                       add_residual: bool = False, workspace: torch.Tensor | None = None,
+                       out: dict | None = None) -> dict:
+    """Classic top-k MoE layer, k = 1 or 2 (switch_topk_layer_forward); the
+    routing outputs are [top_k][T]."""
+    T, d = x.shape
+    N, f = w_in.shape[0], w_in.shape[1]
+    shape = make_shape(T, d, f, N, capacity_, x.dtype)
+    dev = x.device
+    o = out if out is not None else _route_outputs(T, N, dev, top_k)
+    if "y" not in o:
+        o["y"] = torch.empty(T, d, dtype=x.dtype, device=dev)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(topk_workspace_bytes(shape, top_k), 256), dtype=torch.uint8, device=dev)
+    _check(load_library().switch_topk_layer_forward(
+        ctypes.byref(shape), int(top_k), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_in), _ptr(w_out),
+        1 if add_residual else 0, _ptr(o["y"]), _ptr(o["expert_idx"]), _ptr(o["gate"]), _ptr(o["slot"]),
+        _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]), _ptr(ws), ws.numel(), _stream(dev)))
     return o
 
 

@@ -56,8 +56,9 @@ int esize(int dtype) { return dtype == SWITCH_BF16 ? 2 : 4; }
 
 struct Layout {
   size_t bcount = 0, boff = 0, ppart = 0, psum = 0, rank = 0, logits = 0, route_end = 0;
-  size_t ffn_hidden = 0, ffn_end = 0;                             // switch_expert_ffn alone
+  size_t ffn_hidden = 0, ffn_end = 0;                           // switch_expert_ffn alone
   size_t lf_hidden = 0, lf_tok = 0, lf_gmap = 0, total = 0;     // layer forward
+  size_t lf_rows = 0, lf_routed = 0;                            // top-k layer forward (k > 1)
 };
 
 int check_shape(const switch_shape *s) {
@@ -75,15 +76,20 @@ int check_shape(const switch_shape *s) {
   return SWITCH_OK;
 }
 
-int layout(const switch_shape *s, Layout &L) {
+// Workspace of a call with k routes per token: the router's per-block
+// partials (k blocks per router block), the route ranks, the logits rows when
+// the experts do not fit one chunk, then the layer's hidden activations and
+// slot maps; k > 1 adds the slot -> output row map and the [k][T][d] buffer of
+// gate-scaled expert outputs per route.
+int layout(const switch_shape *s, Layout &L, int k = 1) {
   const int64_t T = s->tokens, N = s->num_experts, C = s->capacity, d = s->d_model, f = s->d_ff;
-  const int64_t nb = router_blocks(T);
+  const int64_t nb = router_blocks(T) * k, Tp = router_blocks(T) * kRouterTokens * k;
   const int es = esize(s->dtype);
-  size_t bc, pp, ps, rk, lg = 0, hid, act, tk;
+  size_t bc, pp, ps, rk, lg = 0, hid, act, tk, rt = 0;
   const int64_t Np = count_stride((int)N);
-  bool ok = mul(bc, {nb, Np, 4}) && mul(pp, {nb, Np, 4}) && mul(ps, {N, 4}) && mul(rk, {T, 4}) &&
+  bool ok = mul(bc, {nb, Np, 4}) && mul(pp, {nb, Np, 4}) && mul(ps, {N, 4}) && mul(rk, {Tp, 4}) &&
             (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(hid, {N, C, f, es}) && mul(act, {N, C, d, es}) &&
-            mul(tk, {N, C, 4});
+            mul(tk, {N, C, 4}) && (k == 1 || mul(rt, {k, T, d, es}));
   if (!ok) return fail(SWITCH_E_UNSUPPORTED, "buffer sizes overflow for this shape");
   size_t o = 0;
   L.bcount = o;
@@ -107,7 +113,25 @@ int layout(const switch_shape *s, Layout &L) {
   o = align_up(o + tk);
   L.lf_gmap = o;
   o = align_up(o + tk);
+  if (k > 1) {
+    L.lf_rows = o;
+    o = align_up(o + tk);
+    L.lf_routed = o;
+    o = align_up(o + rt);
+  }
   L.total = o;
+  return SWITCH_OK;
+}
+
+// Routes per token: 1 (Switch routing) or 2 (classic top-2), at most N, and
+// k * tokens rows must be indexable by int32.
+int check_topk(const switch_shape *s, int32_t top_k) {
+  if (top_k < 1) return fail(SWITCH_E_INVALID, "top_k = %d < 1", top_k);
+  if (top_k > s->num_experts)
+    return fail(SWITCH_E_INVALID, "top_k = %d above num_experts = %d", top_k, s->num_experts);
+  if (top_k > 2) return fail(SWITCH_E_UNSUPPORTED, "top_k = %d: only 1 and 2 are supported", top_k);
+  if ((int64_t)top_k * s->tokens > INT32_MAX)
+    return fail(SWITCH_E_UNSUPPORTED, "top_k x tokens = %lld above 2^31-1", (long long)top_k * s->tokens);
   return SWITCH_OK;
 }
 
@@ -176,6 +200,7 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
   if (rc) return rc;
   char *w = (char *)ws;
   a.dtype = s->dtype;
+  a.k = 1;
   a.T = s->tokens;
   a.d = s->d_model;
   a.N = s->num_experts;
@@ -199,53 +224,73 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
 }
 
 // Routing kernels: router, then the capacity assignment (one or two
-// launches).  With tok set (layer path) the assignment also fills the slot ->
-// token / gate maps and the output rows of dropped tokens.
-int run_route(const RouteArgs &a, hipStream_t st, Timer &tm, int32_t *tok = nullptr, float *gmap = nullptr,
-              const void *xres = nullptr, void *y = nullptr) {
+// launches).  With maps.tok set (layer path) the assignment also fills the
+// slot -> token / output row / gate maps and, for one route per token, the
+// output rows of dropped tokens.
+int run_route(const RouteArgs &a, hipStream_t st, Timer &tm, const LayerMaps &maps = LayerMaps{}) {
   hipError_t e;
   for (int r = tm.reps(); r > 0; --r)
     if ((e = launch_router(a, st)) != hipSuccess) return hip_fail(e, "router launch");
   tm.mark("router");
   LaunchMarks marks{[](void *ctx, const char *name) { static_cast<Timer *>(ctx)->mark(name); },
                     [](void *ctx) { return static_cast<Timer *>(ctx)->reps(); }, &tm};
-  if ((e = launch_assign(a, tok, gmap, xres, y, st, marks)) != hipSuccess) return hip_fail(e, "assignment launch");
+  if ((e = launch_assign(a, maps, st, marks)) != hipSuccess) return hip_fail(e, "assignment launch");
   return SWITCH_OK;
 }
 
-int layer_forward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
-                  const void *w_in, const void *w_out, int32_t add_residual, void *y, int32_t *expert_idx,
-                  float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,
-                  void *ws, size_t ws_bytes, void *stream, Timer &tm) {
+// The layer with k routes per token.  k = 1: the expert FFN's epilogue writes
+// y directly.  k = 2: it writes each kept route's gate-scaled output to row
+// r * T + t of a workspace buffer, and a last kernel adds the kept routes of
+// each token (and x with the residual) into y.
+int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *w_router,
+                  const float *router_bias, const void *w_in, const void *w_out, int32_t add_residual, void *y,
+                  int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count,
+                  float *aux_loss, void *ws, size_t ws_bytes, void *stream, Timer &tm) {
   int rc = check_shape(s);
   if (rc) return rc;
+  if ((rc = check_topk(s, k))) return rc;
   Layout L;
-  if ((rc = layout(s, L))) return rc;
+  if ((rc = layout(s, L, k))) return rc;
   if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
   RouteArgs ra;
   if ((rc = route_args(s, x, w_router, router_bias, expert_idx, gate, slot, dropped, expert_count, aux_loss, ws,
                        ws_bytes, L, ra)))
     return rc;
+  ra.k = k;
   NEED(w_in, 16);
   NEED(w_out, 16);
   if (s->tokens > 0) NEED(y, 16);
   hipStream_t st = (hipStream_t)stream;
   char *w = (char *)ws;
-  int32_t *tok = (int32_t *)(w + L.lf_tok);
-  float *gmap = (float *)(w + L.lf_gmap);
+  LayerMaps maps;
+  maps.tok = (int32_t *)(w + L.lf_tok);
+  maps.gmap = (float *)(w + L.lf_gmap);
   const void *xres = add_residual ? x : nullptr;
-  if ((rc = run_route(ra, st, tm, tok, gmap, xres, y))) return rc;
+  if (k == 1) {
+    maps.xres = xres;
+    maps.y = y;
+  } else {
+    maps.rows = (int32_t *)(w + L.lf_rows);
+  }
+  if ((rc = run_route(ra, st, tm, maps))) return rc;
   hipError_t e;
   GemmCall up{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w + L.lf_hidden,
-              expert_count, tok, nullptr, nullptr, nullptr};
+              expert_count, maps.tok, nullptr, nullptr, nullptr};
   for (int r = tm.reps(); r > 0; --r)
     if ((e = launch_ffn_up_gather(up, st)) != hipSuccess) return hip_fail(e, "ffn_up launch");
   tm.mark("ffn_up");
-  GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, y,
-                expert_count, tok, gate, gmap, xres};
+  void *routed = k == 1 ? y : (void *)(w + L.lf_routed);
+  GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, routed,
+                expert_count, k == 1 ? maps.tok : maps.rows, gate, maps.gmap, k == 1 ? xres : nullptr};
   for (int r = tm.reps(); r > 0; --r)
     if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
   tm.mark("ffn_down");
+  if (k > 1) {
+    TopkSumArgs sa{s->dtype, k, s->tokens, s->d_model, routed, dropped, xres, y};
+    for (int r = tm.reps(); r > 0; --r)
+      if ((e = launch_topk_sum(sa, st)) != hipSuccess) return hip_fail(e, "topk_sum launch");
+    tm.mark("topk_sum");
+  }
   return SWITCH_OK;
 }
 
@@ -417,7 +462,7 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
                          void *ws, size_t ws_bytes, void *stream) {
   GUARD({
     Timer tm;
-    return layer_forward(s, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
+    return layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
                          dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
   })
 }
@@ -436,12 +481,36 @@ int switch_layer_forward_profiled(const switch_shape *s, const void *x, const fl
     tm.first = first_kernel;
     tm.last = last_kernel;
     tm.times = times;
-    int rc = layer_forward(s, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
+    int rc = layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
                            dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
     if (rc == SWITCH_OK && last_kernel >= tm.n)
       return fail(SWITCH_E_INVALID, "kernel range %d..%d: the call launches %d kernels", first_kernel, last_kernel,
                   tm.n);
     return rc;
+  })
+}
+
+int switch_topk_workspace_bytes(const switch_shape *s, int32_t top_k, size_t *bytes_out) {
+  GUARD({
+    if (!bytes_out) return fail(SWITCH_E_INVALID, "bytes_out is NULL");
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if ((rc = check_topk(s, top_k))) return rc;
+    Layout L;
+    if ((rc = layout(s, L, top_k))) return rc;
+    *bytes_out = L.total;
+    return SWITCH_OK;
+  })
+}
+
+int switch_topk_layer_forward(const switch_shape *s, int32_t top_k, const void *x, const float *w_router,
+                              const float *router_bias, const void *w_in, const void *w_out, int32_t add_residual,
+                              void *y, int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
+                              int32_t *expert_count, float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
+  GUARD({
+    Timer tm;
+    return layer_forward(s, top_k, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
+                         dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
   })
 }
 

@@ -22,6 +22,16 @@ namespace smx {
 
 constexpr int kScanWaves = 16;
 
+// Virtual token j = r * Tp + t (route r of token t, Tp a multiple of the
+// router block): its token t and its index o = r * T + t in the per-route
+// outputs; false past the batch.  k <= 2.
+__device__ __forceinline__ bool virt_token(int64_t j, int64_t T, int64_t Tp, int k, int64_t &t, int64_t &o) {
+  const int r = (k > 1 && j >= Tp) ? 1 : 0;
+  t = j - r * Tp;
+  o = r * T + t;
+  return t < T;
+}
+
 // One workgroup per 64 experts (lane = expert).  Wave w owns a contiguous
 // segment of blocks: it sums its segment, the segment sums are scanned in LDS,
 // then the wave rewrites its segment as exclusive offsets.  The P partial sums
@@ -88,9 +98,9 @@ __global__ __launch_bounds__(kScanWaves *kWave) void assign_scan_kernel(
   }
 }
 
-// N * sum_i (count_i / T) (psum_i / T) by one 256-thread block, reduced in
-// double in a fixed order.
-__device__ void write_aux_loss(int64_t T, int N, const int32_t *__restrict__ expert_count,
+// N * sum_i (count_i / (k T)) (psum_i / T) by one 256-thread block, reduced
+// in double in a fixed order.
+__device__ void write_aux_loss(int64_t T, int k, int N, const int32_t *__restrict__ expert_count,
                                const float *__restrict__ psum, float *__restrict__ aux_loss) {
   __shared__ double s_acc[256];
   double acc = 0.0;
@@ -103,61 +113,69 @@ __device__ void write_aux_loss(int64_t T, int N, const int32_t *__restrict__ exp
   }
   if (threadIdx.x == 0) {
     const double tt = (double)T;
-    aux_loss[0] = T > 0 ? (float)(s_acc[0] * (double)N / (tt * tt)) : 0.f;
+    aux_loss[0] = T > 0 ? (float)(s_acc[0] * (double)N / ((double)k * tt * tt)) : 0.f;
   }
 }
 
-// slot = in-block rank + the block's offset for the token's expert;
-// dropped = slot >= capacity.  Block 0 also forms the loss.
+// slot = in-block rank + the block's offset for the route's expert;
+// dropped = slot >= capacity.  Block 0 also forms the loss.  One thread per
+// virtual token.
 __global__ __launch_bounds__(256) void assign_apply_kernel(
     const int32_t *__restrict__ expert_idx, const int32_t *__restrict__ rank, int32_t *__restrict__ slot,
     uint8_t *__restrict__ dropped,
-    const int32_t *__restrict__ boff, int64_t T, int N, int C, const int32_t *__restrict__ expert_count,
-    const float *__restrict__ psum, float *__restrict__ aux_loss) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t < T) {
-    const int e = expert_idx[t];
-    const int s = rank[t] + boff[(t / kRouterTokens) * count_stride(N) + e];
-    slot[t] = s;
-    dropped[t] = s >= C ? 1 : 0;
+    const int32_t *__restrict__ boff, int64_t T, int64_t Tp, int k, int N, int C,
+    const int32_t *__restrict__ expert_count, const float *__restrict__ psum, float *__restrict__ aux_loss) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t t, o;
+  if (virt_token(j, T, Tp, k, t, o)) {
+    const int e = expert_idx[o];
+    const int s = rank[j] + boff[(j / kRouterTokens) * count_stride(N) + e];
+    slot[o] = s;
+    dropped[o] = s >= C ? 1 : 0;
   }
-  if (blockIdx.x == 0) write_aux_loss(T, N, expert_count, psum, aux_loss);
+  if (blockIdx.x == 0) write_aux_loss(T, k, N, expert_count, psum, aux_loss);
 }
 
 // Layer path variant of the apply step: besides slot and dropped it records
-// which token sits in each live slot (tok[e][slot] = t) and its gate
-// (gmap[e][slot]) for the expert FFN to gather from and scatter to, and
-// writes the output rows of dropped tokens (their computation is skipped: 0,
-// or x when a residual is added).
+// which token sits in each live slot (tok[e][slot] = t), the route's output
+// row (rows[e][slot], when rows is set) and its gate (gmap[e][slot]) for the
+// expert FFN to gather from and scatter to, and, when y is set (one route per
+// token), writes the output rows of dropped tokens (their computation is
+// skipped: 0, or x when a residual is added).
 __global__ __launch_bounds__(256) void assign_apply_layer_kernel(
     const int32_t *__restrict__ expert_idx, const int32_t *__restrict__ rank, int32_t *__restrict__ slot,
     uint8_t *__restrict__ dropped,
-    const int32_t *__restrict__ boff, int64_t T, int N, int C, const int32_t *__restrict__ expert_count,
-    const float *__restrict__ psum, float *__restrict__ aux_loss, int32_t *__restrict__ tok,
-    float *__restrict__ gmap, const float *__restrict__ gate, const u32x4 *__restrict__ xres,
-    u32x4 *__restrict__ y, int row16) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int32_t *__restrict__ boff, int64_t T, int64_t Tp, int k, int N, int C,
+    const int32_t *__restrict__ expert_count, const float *__restrict__ psum, float *__restrict__ aux_loss,
+    int32_t *__restrict__ tok, int32_t *__restrict__ rows, float *__restrict__ gmap, const float *__restrict__ gate,
+    const u32x4 *__restrict__ xres, u32x4 *__restrict__ y, int row16) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int lane = threadIdx.x % kWave;
   bool drop = false;
-  if (t < T) {
-    const int e = expert_idx[t];
-    const int s = rank[t] + boff[(t / kRouterTokens) * count_stride(N) + e];
-    slot[t] = s;
+  int64_t t, o;
+  if (virt_token(j, T, Tp, k, t, o)) {
+    const int e = expert_idx[o];
+    const int s = rank[j] + boff[(j / kRouterTokens) * count_stride(N) + e];
+    slot[o] = s;
     drop = s >= C;
-    dropped[t] = drop ? 1 : 0;
+    dropped[o] = drop ? 1 : 0;
     if (!drop) {
       tok[(int64_t)e * C + s] = (int32_t)t;
-      gmap[(int64_t)e * C + s] = gate[t];
+      if (rows) rows[(int64_t)e * C + s] = (int32_t)o;
+      gmap[(int64_t)e * C + s] = gate[o];
     }
   }
-  unsigned long long mask = __ballot(drop);
-  while (mask) {
-    const int b = __ffsll(mask) - 1;
-    mask &= mask - 1;
-    const int64_t tt = t - lane + b;
-    for (int c = lane; c < row16; c += kWave) y[tt * row16 + c] = xres ? xres[tt * row16 + c] : u32x4{0, 0, 0, 0};
+  if (y) {  // one route per token: virtual token = token
+    unsigned long long mask = __ballot(drop);
+    while (mask) {
+      const int b = __ffsll(mask) - 1;
+      mask &= mask - 1;
+      const int64_t tt = j - lane + b;
+      for (int c = lane; c < row16; c += kWave)
+        y[tt * row16 + c] = xres ? xres[tt * row16 + c] : u32x4{0, 0, 0, 0};
+    }
   }
-  if (blockIdx.x == 0) write_aux_loss(T, N, expert_count, psum, aux_loss);
+  if (blockIdx.x == 0) write_aux_loss(T, k, N, expert_count, psum, aux_loss);
 }
 
 // Empty batch: every count is 0 and the loss is 0.
@@ -189,15 +207,16 @@ struct AssignArgs {
   uint8_t *dropped;
   const int32_t *bcount;
   const float *ppart;
-  int64_t T, nb;
-  int N, C;
+  int64_t T, Tp, nb;  // tokens, route stride of virtual tokens, blocks over all routes
+  int k, N, C;
   int32_t *expert_count;
   float *psum, *aux_loss;
   const float *gate;
-  int32_t *tok;  // layer path, or null
+  int32_t *tok;   // layer path, or null
+  int32_t *rows;  // layer path with k > 1, or null
   float *gmap;
   const u32x4 *xres;
-  u32x4 *y;
+  u32x4 *y;       // layer path with k = 1, or null
   int row16;
 };
 
@@ -291,33 +310,35 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
   if (last) s_acc[tid] = acc;
   __syncthreads();
 
-  // 3. tokens: slot = offset of the token's block for its expert + in-block rank
-  const int64_t t = r0 * kRouterTokens + tid;
+  // 3. routes: slot = offset of the route's block for its expert + in-block rank
+  const int64_t j = r0 * kRouterTokens + tid;
   const int lane = tid % kWave;
   bool drop = false;
-  if (tid < kAsTokens && t < p.T) {
-    const int e = p.expert_idx[t];
-    const int sl = s_off[(tid / kRouterTokens) * N + e] + p.rank[t];
-    p.slot[t] = sl;
+  int64_t t, o;
+  if (tid < kAsTokens && j < p.nb * kRouterTokens && virt_token(j, p.T, p.Tp, p.k, t, o)) {
+    const int e = p.expert_idx[o];
+    const int sl = s_off[(tid / kRouterTokens) * N + e] + p.rank[j];
+    p.slot[o] = sl;
     drop = sl >= p.C;
-    p.dropped[t] = drop ? 1 : 0;
+    p.dropped[o] = drop ? 1 : 0;
     if (!drop && p.tok) {
       p.tok[(int64_t)e * p.C + sl] = (int32_t)t;
-      p.gmap[(int64_t)e * p.C + sl] = p.gate[t];
+      if (p.rows) p.rows[(int64_t)e * p.C + sl] = (int32_t)o;
+      p.gmap[(int64_t)e * p.C + sl] = p.gate[o];
     }
   }
-  if (p.y) {  // output rows of this wave's dropped tokens: 0, or x with a residual
+  if (p.y) {  // one route per token: output rows of this wave's dropped tokens, 0 or x
     unsigned long long mask = __ballot(drop);
     while (mask) {
       const int bb = __ffsll(mask) - 1;
       mask &= mask - 1;
-      const int64_t tt = t - lane + bb;
+      const int64_t tt = j - lane + bb;
       for (int c = lane; c < p.row16; c += kWave)
         p.y[tt * p.row16 + c] = p.xres ? p.xres[tt * p.row16 + c] : u32x4{0, 0, 0, 0};
     }
   }
 
-  // 4. loss = N * sum_i (count_i / T) (psum_i / T), reduced in double in a fixed order
+  // 4. loss = N * sum_i (count_i / (k T)) (psum_i / T), reduced in double in a fixed order
   if (last) {
     for (int w = kAsThreads / 2; w > 0; w >>= 1) {
       if (tid < w) s_acc[tid] += s_acc[tid + w];
@@ -325,7 +346,7 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
     }
     if (tid == 0) {
       const double tt = (double)p.T;
-      p.aux_loss[0] = (float)(s_acc[0] * (double)N / (tt * tt));
+      p.aux_loss[0] = (float)(s_acc[0] * (double)N / ((double)p.k * tt * tt));
     }
   }
 }
@@ -337,13 +358,12 @@ bool assign_single_launch(int64_t nb, int N) {
   return nb > 0 && reads <= 16.0 * (1 << 20) && assign_one_smem(N) <= 64 * 1024;
 }
 
-hipError_t launch_assign(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y, hipStream_t st,
-                         LaunchMarks marks) {
+hipError_t launch_assign(const RouteArgs &a, const LayerMaps &m, hipStream_t st, LaunchMarks marks) {
   auto mark = [&](const char *name) {
     if (marks.fn) marks.fn(marks.ctx, name);
   };
   auto reps = [&]() { return marks.reps ? marks.reps(marks.ctx) : 1; };
-  const int64_t nb = router_blocks(a.T);
+  const int64_t nb1 = router_blocks(a.T), nb = a.k * nb1, Tp = nb1 * kRouterTokens;
   hipError_t e;
   if (nb == 0) {
     for (int r = reps(); r > 0; --r)
@@ -354,9 +374,10 @@ hipError_t launch_assign(const RouteArgs &a, int32_t *tok, float *gmap, const vo
     return hipSuccess;
   }
   const int row16 = a.d * (a.dtype == kBF16 ? 2 : 4) / 16;
+  u32x4 *y = a.k == 1 ? (u32x4 *)m.y : nullptr;
   if (assign_single_launch(nb, a.N)) {
-    AssignArgs p{a.expert_idx, a.rank, a.slot, a.dropped, a.bcount, a.ppart, a.T, nb, a.N, a.C, a.expert_count,
-                 a.psum, a.aux_loss, a.gate, tok, gmap, (const u32x4 *)xres, (u32x4 *)y, row16};
+    AssignArgs p{a.expert_idx, a.rank, a.slot, a.dropped, a.bcount, a.ppart, a.T, Tp, nb, a.k, a.N, a.C,
+                 a.expert_count, a.psum, a.aux_loss, a.gate, m.tok, m.rows, m.gmap, (const u32x4 *)m.xres, y, row16};
     for (int r = reps(); r > 0; --r)
       assign_one_kernel<<<dim3((unsigned)ceil_div(nb, kAsBlocks)), dim3(kAsThreads), assign_one_smem(a.N), st>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -368,14 +389,15 @@ hipError_t launch_assign(const RouteArgs &a, int32_t *tok, float *gmap, const vo
         a.bcount, a.boff, a.ppart, nb, a.N, a.expert_count, a.psum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mark("assign_scan");
+  const dim3 grid((unsigned)ceil_div(nb * kRouterTokens, 256));
   for (int r = reps(); r > 0; --r) {
-    if (tok)
-      assign_apply_layer_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
-          a.expert_idx, a.rank, a.slot, a.dropped, a.boff, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss, tok,
-          gmap, a.gate, (const u32x4 *)xres, (u32x4 *)y, row16);
+    if (m.tok)
+      assign_apply_layer_kernel<<<grid, dim3(256), 0, st>>>(
+          a.expert_idx, a.rank, a.slot, a.dropped, a.boff, a.T, Tp, a.k, a.N, a.C, a.expert_count, a.psum,
+          a.aux_loss, m.tok, m.rows, m.gmap, a.gate, (const u32x4 *)m.xres, y, row16);
     else
-      assign_apply_kernel<<<dim3((unsigned)ceil_div(a.T, 256)), dim3(256), 0, st>>>(
-          a.expert_idx, a.rank, a.slot, a.dropped, a.boff, a.T, a.N, a.C, a.expert_count, a.psum, a.aux_loss);
+      assign_apply_kernel<<<grid, dim3(256), 0, st>>>(a.expert_idx, a.rank, a.slot, a.dropped, a.boff, a.T, Tp,
+                                                      a.k, a.N, a.C, a.expert_count, a.psum, a.aux_loss);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mark("assign_apply");

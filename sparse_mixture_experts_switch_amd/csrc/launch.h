@@ -13,8 +13,14 @@ constexpr int kRouterTokens = 64;    // tokens per router block
 constexpr int kRouterThreads = 256;  // 4 waves
 constexpr int kRouterChunk = 128;    // experts per logits chunk (4 waves x 32)
 
+// Routing arguments.  k routes per token (1: Switch routing; 2: classic
+// top-2).  Route r of token t is "virtual token" r * Tp + t with Tp =
+// router_blocks(T) * kRouterTokens, so the router block b of route r is block
+// r * nb + b of the assignment; per-route outputs (expert_idx, gate, slot,
+// dropped) are [k][T].
 struct RouteArgs {
   int dtype;
+  int k;
   int64_t T;
   int d, N, C;
   const void *x;
@@ -23,13 +29,13 @@ struct RouteArgs {
   int32_t *expert_idx;
   float *gate;
   int32_t *slot;  // slot of each token (assignment output)
-  int32_t *rank;  // [T] workspace: rank of each token among its block's earlier tokens with the same expert
+  int32_t *rank;  // [k * Tp] workspace: rank of each route among its block's earlier routes to the same expert
   uint8_t *dropped;
   int32_t *expert_count;
   float *aux_loss;
-  int32_t *bcount;  // [nb][count_stride(N)]: block counts
-  int32_t *boff;    // [nb][count_stride(N)]: exclusive block offsets (scan path)
-  float *ppart;     // [nb][count_stride(N)]: block partial sums of p
+  int32_t *bcount;  // [k * nb][count_stride(N)]: block counts
+  int32_t *boff;    // [k * nb][count_stride(N)]: exclusive block offsets (scan path)
+  float *ppart;     // [k * nb][count_stride(N)]: block partial sums of p (route 0 rows; others 0)
   float *psum;      // [N]
 };
 
@@ -95,8 +101,10 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t st);
 // Capacity assignment and loss after the router.  Small batches take one
 // launch (each workgroup sums the counts of the blocks before its own);
 // others a scan over blocks, then the apply step.  With tok set (layer path)
-// it also records tok[e][slot] = t and gmap[e][slot] = gate[t] for kept
-// tokens and writes the y rows of dropped tokens (0, or x with a residual).
+// it also records, for each kept route of token t, tok[e][slot] = t, the
+// route's output row rows[e][slot] = r * T + t (rows may be null when k = 1:
+// the row is t) and its gate gmap[e][slot], and, when y is set (k = 1 only),
+// writes the y rows of dropped tokens (0, or x with a residual).
 // marks.fn (may be null) is called with each kernel's name after its
 // launches; marks.reps (may be null) says how many times to issue the next
 // kernel back to back (measurement only: no kernel modifies its inputs).
@@ -107,8 +115,25 @@ struct LaunchMarks {
 };
 // Whether the assignment of nb router blocks and N experts takes one launch.
 bool assign_single_launch(int64_t nb, int N);
-hipError_t launch_assign(const RouteArgs &a, int32_t *tok, float *gmap, const void *xres, void *y, hipStream_t st,
-                         LaunchMarks marks);
+struct LayerMaps {
+  int32_t *tok = nullptr;   // [N][C] token of each live slot (x row to gather)
+  int32_t *rows = nullptr;  // [N][C] output row of each live slot, or null (= tok)
+  float *gmap = nullptr;    // [N][C] gate of each live slot
+  const void *xres = nullptr;
+  void *y = nullptr;
+};
+hipError_t launch_assign(const RouteArgs &a, const LayerMaps &m, hipStream_t st, LaunchMarks marks);
+// Top-k combine: y[t] = sum over kept routes r of routed[r * T + t] (+ x[t]).
+struct TopkSumArgs {
+  int dtype, k;
+  int64_t T;
+  int d;
+  const void *routed;  // [k][T][d]
+  const uint8_t *dropped;  // [k][T]
+  const void *x;  // may be null
+  void *y;
+};
+hipError_t launch_topk_sum(const TopkSumArgs &a, hipStream_t st);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st);
 hipError_t launch_ffn_up(const FfnArgs &a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st);
@@ -118,7 +143,7 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_add_norm(const AddNormArgs &a, hipStream_t st);
 int add_norm_max_d(int dtype);  // largest d_model the row-in-registers kernel takes
 
-inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
+__host__ __device__ inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
 // Row stride (elements) of the per-block count and P-partial arrays: rows
 // start on 16-byte boundaries.
 __host__ __device__ inline int count_stride(int N) { return (N + 3) & ~3; }

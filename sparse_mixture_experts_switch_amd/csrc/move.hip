@@ -185,6 +185,74 @@ hipError_t launch_add_norm(const AddNormArgs &a, hipStream_t st) {
   return a.dtype == kBF16 ? add_norm_dispatch<bf16>(a, st) : add_norm_dispatch<float>(a, st);
 }
 
+// Top-k combine ("Switch Routing" combine equation: the output is the sum
+// over the token's selected experts of p_i(x) E_i(x)).  The expert FFN has
+// already written each kept route's gate-scaled output to its own row r * T +
+// t of `routed`; this adds the kept routes of every token in route order (and
+// x, with the residual) in fp32 and rounds once.  One thread per 16-byte
+// piece of an output row, consecutive threads on consecutive pieces.
+template <typename T_, int kK>
+__global__ __launch_bounds__(kMoveThreads) void topk_sum_kernel(const u32x4 *__restrict__ routed,
+                                                                const uint8_t *__restrict__ dropped,
+                                                                const u32x4 *__restrict__ x, u32x4 *__restrict__ y,
+                                                                int64_t T, int row16) {
+  constexpr int kE = 16 / sizeof(T_);
+  const int64_t i = (int64_t)blockIdx.x * kMoveThreads + threadIdx.x;
+  if (i >= T * row16) return;
+  const int64_t t = i / row16;
+  const int c = (int)(i - t * row16);
+  float v[kE];
+#pragma unroll
+  for (int q = 0; q < kE; ++q) v[q] = 0.f;
+#pragma unroll
+  for (int r = 0; r < kK; ++r) {
+    const int64_t row = r * T + t;
+    if (dropped[row]) continue;
+    const u32x4 w = routed[row * row16 + c];
+#pragma unroll
+    for (int q = 0; q < kE; ++q) {
+      if constexpr (sizeof(T_) == 2)
+        v[q] += (float)as_bf16x8(w)[q];
+      else
+        v[q] += __builtin_bit_cast(f32x4, w)[q];
+    }
+  }
+  if (x) {
+    const u32x4 w = x[t * row16 + c];
+#pragma unroll
+    for (int q = 0; q < kE; ++q) {
+      if constexpr (sizeof(T_) == 2)
+        v[q] = (float)as_bf16x8(w)[q] + v[q];
+      else
+        v[q] = __builtin_bit_cast(f32x4, w)[q] + v[q];
+    }
+  }
+  u32x4 o;
+  if constexpr (sizeof(T_) == 2) {
+    bf16x8 r;
+#pragma unroll
+    for (int q = 0; q < kE; ++q) r[q] = (bf16)v[q];
+    o = as_u32x4(r);
+  } else {
+    o = __builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]});
+  }
+  y[t * row16 + c] = o;
+}
+
+hipError_t launch_topk_sum(const TopkSumArgs &a, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  if (a.k != 2) return hipErrorInvalidValue;
+  const int row16 = a.d * esize(a.dtype) / 16;
+  const dim3 grid((unsigned)ceil_div(a.T * row16, kMoveThreads)), block(kMoveThreads);
+  if (a.dtype == kBF16)
+    topk_sum_kernel<bf16, 2><<<grid, block, 0, st>>>((const u32x4 *)a.routed, a.dropped, (const u32x4 *)a.x,
+                                                     (u32x4 *)a.y, a.T, row16);
+  else
+    topk_sum_kernel<float, 2><<<grid, block, 0, st>>>((const u32x4 *)a.routed, a.dropped, (const u32x4 *)a.x,
+                                                      (u32x4 *)a.y, a.T, row16);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st) {
   if (a.T == 0 || a.C == 0) return hipSuccess;
   const int row16 = a.d * esize(a.dtype) / 16;

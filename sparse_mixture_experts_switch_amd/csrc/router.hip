@@ -1,6 +1,8 @@
 // Router of the Switch layer: logits h = W_r . x (+ b), fp32 softmax, top-1
 // expert, gate p_e(x), and the per-block partial results that the capacity
-// assignment and the load-balancing loss are built from.
+// assignment and the load-balancing loss are built from.  The same kernels
+// also route each token to its two best experts (classic top-2 routing, the
+// variant the Switch layer simplifies), with the gate p_i(x) of each.
 //
 // Switch Transformers write-up, "Switch Routing: From Top-k to k = 1" (router
 // logits and the softmax gate equation), "Making Sparse Training Stable"
@@ -64,30 +66,62 @@ struct LogitRows {
   __device__ __forceinline__ float &at(int t, int j) const { return base[(int64_t)t * stride + j]; }
 };
 
-// Softmax, argmax, gate, P partials, block counts and in-block ranks for the
-// block's tokens, from logits already complete in `lg` (kThreads threads).
+// Softmax, top-k choice (k = 1 or 2), gates, P partials, block counts and
+// in-block ranks for the block's tokens, from logits already complete in `lg`
+// (kThreads threads).
 //  - kThreads / 64 consecutive lanes share a token: each scans a strided
 //    subset of the experts, butterfly steps combine the partial results in a
-//    fixed order; exp(h_j - max) replaces h_j in `lg` on the way.
+//    fixed order; exp(h_j - max) replaces h_j in `lg` on the way.  The order
+//    of the choice is larger logit first, lower expert index first on equal
+//    logits; it is a total order, so the butterfly partners agree exactly.
 //  - kThreads / 128 consecutive lanes share an expert: each sums p_j(t) and
 //    counts the choices of one contiguous run of the block's tokens, and the
 //    runs are combined by butterfly steps (fixed order: the same bits every
 //    call).
-template <int kThreads, bool kLds>
-__device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t t0, int64_t blk,
+// Route r of token t0 + t is written at r * T + t0 + t (expert_idx, gate) and
+// r * Tp + t0 + t (rank, Tp = nb * kRouterTokens); its block counts are row
+// r * nb + blk of bcount.  The P partials go to row blk; rows nb + blk of a
+// second route hold zeros (P does not depend on the route).
+struct TopK {
+  int64_t T, nb;  // tokens, router blocks
+};
+
+template <int kK>
+__device__ __forceinline__ void topk_take(float h, int j, float &b1, int &i1, float &b2, int &i2) {
+  // ascending j within one lane: strict comparisons keep the lower index
+  if (h > b1) {
+    if (kK == 2) {
+      b2 = b1;
+      i2 = i1;
+    }
+    b1 = h;
+    i1 = j;
+  } else if (kK == 2 && h > b2) {
+    b2 = h;
+    i2 = j;
+  }
+}
+
+__device__ __forceinline__ bool topk_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+template <int kThreads, bool kLds, int kK>
+__device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t t0, int64_t blk, TopK tk,
                                 int32_t *__restrict__ expert_idx, float *__restrict__ gate,
                                 int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
-                                float *__restrict__ ppart, float *s_max, float *s_inv, int *s_e) {
+                                float *__restrict__ ppart, float *s_max, float *s_inv, int *s_e, int *s_e2) {
   constexpr int kLpt = kThreads / kRouterTokens;   // lanes per token
   constexpr int kTpe = kThreads / kRouterChunk;    // lanes per expert
   constexpr int kUpt = kRouterTokens / kTpe;       // tokens per lane in the expert sums
   static_assert(kLpt >= 1 && kLpt <= kWave && (kLpt & (kLpt - 1)) == 0, "lanes per token");
   static_assert(kTpe >= 1 && kTpe <= kWave && (kTpe & (kTpe - 1)) == 0, "lanes per expert");
+  static_assert(kK == 1 || kK == 2, "one or two routes per token");
   const int tid = threadIdx.x;
   const int t = tid / kLpt, q = tid % kLpt;
   if (t < nt) {  // the lanes of a token are always on the same side of t < nt
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
+    float best = -INFINITY, sec = -INFINITY;
+    int bi = 0x7fffffff, si = 0x7fffffff;
     if (kLds) {  // N <= kRouterChunk: at most kJ values per lane, loaded together
       constexpr int kJ = kRouterChunk / kLpt;
       float h[kJ];
@@ -95,24 +129,29 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       for (int i = 0; i < kJ; ++i) h[i] = q + i * kLpt < N ? lg.at(t, q + i * kLpt) : -INFINITY;
 #pragma unroll
       for (int i = 0; i < kJ; ++i)
-        if (h[i] > best) {  // ascending j: first maximum kept
-          best = h[i];
-          bi = q + i * kLpt;
-        }
+        if (q + i * kLpt < N) topk_take<kK>(h[i], q + i * kLpt, best, bi, sec, si);
     } else {
-      for (int j = q; j < N; j += kLpt) {
-        const float h = lg.at(t, j);
-        if (h > best) {
-          best = h;
-          bi = j;
-        }
-      }
+      for (int j = q; j < N; j += kLpt) topk_take<kK>(lg.at(t, j), j, best, bi, sec, si);
     }
 #pragma unroll
     for (int off = 1; off < kLpt; off <<= 1) {
       const float ov = __shfl_xor(best, off, kWave);
       const int oi = __shfl_xor(bi, off, kWave);
-      if (ov > best || (ov == best && oi < bi)) {
+      if (kK == 2) {
+        // top two of the union of two ordered pairs
+        const float ov2 = __shfl_xor(sec, off, kWave);
+        const int oi2 = __shfl_xor(si, off, kWave);
+        if (topk_before(ov, oi, best, bi)) {  // theirs first; second: my first or their second
+          const bool mine = topk_before(best, bi, ov2, oi2);
+          sec = mine ? best : ov2;
+          si = mine ? bi : oi2;
+          best = ov;
+          bi = oi;
+        } else if (topk_before(ov, oi, sec, si)) {  // mine first; second: their first or my second
+          sec = ov;
+          si = oi;
+        }
+      } else if (topk_before(ov, oi, best, bi)) {
         best = ov;
         bi = oi;
       }
@@ -144,13 +183,19 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       s_e[t] = bi;
       expert_idx[t0 + t] = bi;
       gate[t0 + t] = inv;  // p_e = exp(h_e - max) / sum with h_e = max
+      if (kK == 2) {
+        s_e2[t] = si;
+        expert_idx[tk.T + t0 + t] = si;
+        gate[tk.T + t0 + t] = __expf(sec - best) * inv;
+      }
     }
   }
   __syncthreads();
+  const int64_t Np = count_stride(N);
   for (int j0 = 0; j0 < N; j0 += kRouterChunk) {
     const int j = j0 + tid / kTpe, r = tid % kTpe;
     float p = 0.f;
-    int c = 0;
+    int c = 0, c2 = 0;
     if (j < N) {
 #pragma unroll
       for (int i = 0; i < kUpt; ++i) {
@@ -158,6 +203,7 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
         if (u < nt) {
           p += lg.at(u, j) * s_inv[u];
           c += (s_e[u] == j);
+          if (kK == 2) c2 += (s_e2[u] == j);
         }
       }
     }
@@ -165,21 +211,29 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
     for (int off = 1; off < kTpe; off <<= 1) {
       p += __shfl_xor(p, off, kWave);
       c += __shfl_xor(c, off, kWave);
+      if (kK == 2) c2 += __shfl_xor(c2, off, kWave);
     }
     if (r == 0 && j < N) {
-      ppart[blk * count_stride(N) + j] = p;
-      bcount[blk * count_stride(N) + j] = c;
+      ppart[blk * Np + j] = p;
+      bcount[blk * Np + j] = c;
+      if (kK == 2) {
+        ppart[(tk.nb + blk) * Np + j] = 0.f;
+        bcount[(tk.nb + blk) * Np + j] = c2;
+      }
     }
   }
-  // rank among the block's earlier tokens with the same expert: wave 0 holds
-  // one token per lane and reads the others' choices lane by lane
+  // rank among the block's earlier tokens with the same expert, per route:
+  // wave 0 holds one token per lane and reads the others' choices lane by lane
   static_assert(kRouterTokens == kWave, "one router block = one wave of tokens");
   if (tid < kWave) {
-    const int e = tid < nt ? s_e[tid] : -1;
-    int r = 0;
+#pragma unroll 1
+    for (int rt = 0; rt < kK; ++rt) {
+      const int e = tid < nt ? (rt == 0 ? s_e[tid] : s_e2[tid]) : -1;
+      int r = 0;
 #pragma unroll
-    for (int u = 0; u < kWave; ++u) r += (u < tid) & (__builtin_amdgcn_readlane(e, u) == e);
-    if (tid < nt) slot_rank[t0 + tid] = r;
+      for (int u = 0; u < kWave; ++u) r += (u < tid) & (__builtin_amdgcn_readlane(e, u) == e);
+      if (tid < nt) slot_rank[rt * tk.nb * kRouterTokens + t0 + tid] = r;
+    }
   }
 }
 
@@ -221,12 +275,12 @@ constexpr int kRouterSmem = kRouterStageBytes > kRouterLgBytes ? kRouterStageByt
 struct RouterSmem {
   __attribute__((aligned(16))) char stage[kRouterSmem];
   float s_max[kRouterTokens], s_inv[kRouterTokens];
-  int s_e[kRouterTokens];
+  int s_e[kRouterTokens], s_e2[kRouterTokens];
 };
 
 // Router work of block `blk` (tokens [64 blk, 64 blk + 64)).  Starts with a
 // barrier, so consecutive calls by one workgroup may reuse `sm`.
-template <bool kLds>
+template <bool kLds, int kK>
 __device__ __forceinline__ void router_block_bf16(
     const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
@@ -369,36 +423,36 @@ __device__ __forceinline__ void router_block_bf16(
     if (kLds) break;  // N <= kRouterChunk: one chunk holds every expert
   }
   __syncthreads();
-  router_epilogue<kRBThreads, kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, sm.s_max,
-                                    sm.s_inv, sm.s_e);
+  router_epilogue<kRBThreads, kLds, kK>(lg, nt, N, t0, blk, TopK{T, router_blocks(T)}, expert_idx, gate, slot_rank,
+                                        bcount, ppart, sm.s_max, sm.s_inv, sm.s_e, sm.s_e2);
 }
 
-template <bool kLds>
+template <bool kLds, int kK>
 __global__ __launch_bounds__(kRBThreads) void router_bf16_kernel(
     const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
     float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
     float *__restrict__ ppart) {
   __shared__ RouterSmem sm;
-  router_block_bf16<kLds>(x, w_r, bias, T, d, N, logits_g, expert_idx, gate, slot_rank, bcount, ppart, blockIdx.x,
-                          sm);
+  router_block_bf16<kLds, kK>(x, w_r, bias, T, d, N, logits_g, expert_idx, gate, slot_rank, bcount, ppart,
+                              blockIdx.x, sm);
 }
 
 // ---------------------------------------------------------------------------
 // fp32 activations: fp32 FMA.  The block's x rows are staged in LDS in
 // k-slices; each thread owns (token, expert) pairs of the current chunk.
 // ---------------------------------------------------------------------------
-template <bool kLds>
+template <bool kLds, int kK>
 __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
     float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
     float *__restrict__ ppart) {
-  constexpr int kK = 64;
+  constexpr int kKc = 64;  // contraction columns per LDS slice
   __shared__ float s_lg[kLds ? kRouterTokens * (kRouterChunk + 1) : 1];
-  __shared__ float s_x[kRouterTokens][kK + 1];
+  __shared__ float s_x[kRouterTokens][kKc + 1];
   __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
-  __shared__ int s_e[kRouterTokens];
+  __shared__ int s_e[kRouterTokens], s_e2[kRouterTokens];
 
   const int64_t blk = blockIdx.x;
   const int64_t t0 = blk * kRouterTokens;
@@ -418,10 +472,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
     float acc[kPer];
 #pragma unroll
     for (int p = 0; p < kPer; ++p) acc[p] = 0.f;
-    for (int k0 = 0; k0 < d; k0 += kK) {
+    for (int k0 = 0; k0 < d; k0 += kKc) {
       __syncthreads();
-      for (int i = tid; i < kRouterTokens * kK; i += kRouterThreads) {
-        int t = i / kK, k = i % kK;
+      for (int i = tid; i < kRouterTokens * kKc; i += kRouterThreads) {
+        int t = i / kKc, k = i % kKc;
         s_x[t][k] = (t < nt && k0 + k < d) ? x[(t0 + t) * d + k0 + k] : 0.f;
       }
       __syncthreads();
@@ -431,7 +485,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
         const int t = pair / kRouterChunk, j = c0 + pair % kRouterChunk;
         if (j < N) {
           const float *w = w_r + (int64_t)j * d + k0;
-          const int kn = min(kK, d - k0);
+          const int kn = min(kKc, d - k0);
           float a = acc[p];
           for (int k = 0; k < kn; ++k) a = __builtin_fmaf(s_x[t][k], w[k], a);
           acc[p] = a;
@@ -447,35 +501,30 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
     if (kLds) break;
   }
   __syncthreads();
-  router_epilogue<kRouterThreads, kLds>(lg, nt, N, t0, blk, expert_idx, gate, slot_rank, bcount, ppart, s_max,
-                                        s_inv, s_e);
+  router_epilogue<kRouterThreads, kLds, kK>(lg, nt, N, t0, blk, TopK{T, router_blocks(T)}, expert_idx, gate,
+                                            slot_rank, bcount, ppart, s_max, s_inv, s_e, s_e2);
+}
+
+template <int kK>
+hipError_t run_router(const RouteArgs &a, hipStream_t st) {
+  const int64_t nb = router_blocks(a.T);
+  const bool lds = a.N <= kRouterChunk;
+  const dim3 grid((unsigned)nb);
+  if (a.dtype == kBF16) {
+    auto kern = lds ? router_bf16_kernel<true, kK> : router_bf16_kernel<false, kK>;
+    kern<<<grid, dim3(kRBThreads), 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits,
+                                            a.expert_idx, a.gate, a.rank, a.bcount, a.ppart);
+  } else {
+    auto kern = lds ? router_f32_kernel<true, kK> : router_f32_kernel<false, kK>;
+    kern<<<grid, dim3(kRouterThreads), 0, st>>>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits,
+                                                a.expert_idx, a.gate, a.rank, a.bcount, a.ppart);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
-  const int64_t nb = ceil_div(a.T, kRouterTokens);
-  if (nb == 0) return hipSuccess;
-  const bool lds = a.N <= kRouterChunk;
-  dim3 grid((unsigned)nb), block(kRouterThreads);
-  if (a.dtype == kBF16) {
-    if (lds)
-      router_bf16_kernel<true><<<grid, dim3(kRBThreads), 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T,
-                                                       a.d, a.N, a.logits, a.expert_idx, a.gate, a.rank,
-                                                       a.bcount, a.ppart);
-    else
-      router_bf16_kernel<false><<<grid, dim3(kRBThreads), 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T,
-                                                        a.d, a.N, a.logits, a.expert_idx, a.gate, a.rank,
-                                                        a.bcount, a.ppart);
-  } else {
-    if (lds)
-      router_f32_kernel<true><<<grid, block, 0, st>>>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N,
-                                                      a.logits, a.expert_idx, a.gate, a.rank, a.bcount,
-                                                      a.ppart);
-    else
-      router_f32_kernel<false><<<grid, block, 0, st>>>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N,
-                                                       a.logits, a.expert_idx, a.gate, a.rank, a.bcount,
-                                                       a.ppart);
-  }
-  return hipGetLastError();
+  if (router_blocks(a.T) == 0) return hipSuccess;
+  return a.k == 2 ? run_router<2>(a, st) : run_router<1>(a, st);
 }
 
 }  // namespace smx

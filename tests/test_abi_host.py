@@ -149,3 +149,39 @@ def test_launch_names_follow_the_shape():
     bad = B.make_shape(16, 96, 64, 8, 2, torch.float32)
     with pytest.raises(smx.SwitchError):
         smx.launch_names(bad)
+
+
+def test_topk_validation_and_workspace():
+    """top_k outside 1..min(2, N) is rejected on the host; top_k = 1 needs the
+    Switch layer's workspace; top_k = 2 doubles the per-block partials and
+    ranks and adds the slot -> row map and the [2][T][d] buffer of routed
+    outputs."""
+    import torch
+    lib = smx.load_library()
+    s = B.make_shape(16384, 768, 3072, 128, 320, torch.bfloat16)
+    assert smx.topk_workspace_bytes(s, 1) == smx.workspace_bytes(s)
+    w2 = smx.topk_workspace_bytes(s, 2)
+    nb = 16384 // 64
+    expect_min = (3 * 2 * nb * 128 * 4 + 128 * 4 + 2 * 16384 * 4 + 128 * 320 * 3072 * 2 + 3 * 128 * 320 * 4
+                  + 2 * 16384 * 768 * 2)
+    assert expect_min <= w2 <= expect_min + 10 * 256
+    out = ctypes.c_size_t()
+    for k, code in ((0, B.SWITCH_E_INVALID), (-1, B.SWITCH_E_INVALID), (3, B.SWITCH_E_UNSUPPORTED),
+                    (129, B.SWITCH_E_INVALID)):
+        assert lib.switch_topk_workspace_bytes(ctypes.byref(s), k, ctypes.byref(out)) == code, k
+    one = B.make_shape(64, 128, 256, 1, 16, torch.bfloat16)
+    assert lib.switch_topk_workspace_bytes(ctypes.byref(one), 2, ctypes.byref(out)) == B.SWITCH_E_INVALID
+    big = B.make_shape(2 ** 30 + 1, 128, 256, 8, 16, torch.bfloat16)
+    assert lib.switch_topk_workspace_bytes(ctypes.byref(big), 2, ctypes.byref(out)) == B.SWITCH_E_UNSUPPORTED
+    P = ctypes.c_void_p
+    good = P(1 << 20)
+    small = B.make_shape(64, 128, 256, 8, 16, torch.bfloat16)
+    rc = lib.switch_topk_layer_forward(ctypes.byref(small), 3, good, good, None, good, good, 0, good, good, good,
+                                       good, good, good, good, good, 1 << 30, None)
+    assert rc == B.SWITCH_E_UNSUPPORTED
+    rc = lib.switch_topk_layer_forward(ctypes.byref(small), 2, None, good, None, good, good, 0, good, good, good,
+                                       good, good, good, good, good, 1 << 30, None)
+    assert rc == B.SWITCH_E_INVALID
+    rc = lib.switch_topk_layer_forward(ctypes.byref(small), 2, good, good, None, good, good, 0, good, good, good,
+                                       good, good, good, good, good, 64, None)
+    assert rc == B.SWITCH_E_WORKSPACE
