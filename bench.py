@@ -282,6 +282,34 @@ def main() -> int:
                          "hbm_frac": round(stage_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                      for k, v in stage_ms.items()}
     log("bench: stage kernels " + ", ".join(f"{k}={v['GBps']} GB/s" for k, v in stage_kernels.items()))
+    # classic top-2 routing on the same workload (switch_topk_layer_forward,
+    # capacity from 2 T so that both routes have room): whole-call time
+    C2 = smx.capacity(2 * T, N, cfg.capacity_factor)
+    shape2 = smx.binding.make_shape(T, d, f, N, C2, cfg.torch_dtype)
+    ws2 = torch.empty(smx.topk_workspace_bytes(shape2, 2), dtype=torch.uint8, device=dev)
+    out2 = smx.binding._route_outputs(T, N, dev, 2)
+    out2["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
+    call2 = lambda: smx.topk_layer_forward(inp["x"], inp["w_router"], inp["router_bias"],  # noqa: E731
+                                           inp["w_in"], inp["w_out"], C2, 2, workspace=ws2, out=out2)
+    with torch.cuda.stream(stream):
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < MIN_WARMUP_S:
+            for _ in range(20):
+                call2()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            call2()
+        b.record(stream)
+        torch.cuda.synchronize()
+    ms2 = a.elapsed_time(b) / args.steps
+    kept2 = int(sum(min(int(c), C2) for c in out2["expert_count"].cpu().tolist()))
+    top2 = {"ms": round(ms2, 4), "tokens_per_s": round(T / (ms2 * 1e-3), 1), "capacity": C2,
+            "route_drop_rate": round(float(out2["dropped"].float().mean().item()), 5),
+            "ffn_tflop_per_s_whole_call": round(4.0 * kept2 * d * f / (ms2 * 1e-3) / 1e12, 1)}
+    log(f"bench: top-2 layer {ms2:.4f} ms ({T / (ms2 * 1e-3) / 1e6:.2f} Mtok/s)")
+    del ws2, out2
     per_kernel = {}
     for k, v in kern.items():
         b = algorithmic_bytes(k, T, d, f, N, C, counts)
@@ -324,6 +352,7 @@ def main() -> int:
                                    "hbm_frac": round(rdc_b / (rdc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "kernels": per_kernel,
         "stage_kernels": stage_kernels,
+        "top2": top2,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.calib_copy:
