@@ -29,6 +29,10 @@ function that takes it):
 * the block's "Add + Normalize" after the layer is layer normalisation over
   d_model of x + y (population variance, eps inside the square root, a
   per-feature scale and shift);
+* the backward pass differentiates L = <dy, y> + d_aux * aux with the routing
+  (expert choice, f_i, capacity drops) held fixed: f_i is a hard count with no
+  gradient, so the loss reaches the router only through P_i, and the output
+  reaches it only through the gate of each kept token;
 * classic top-k routing (the variant the Switch layer simplifies): a token's
   k routes go to its k largest logits, in decreasing order (ties to the lower
   index); each route's gate is the full softmax p_i(x), not renormalised over
@@ -351,3 +355,86 @@ def forward_topk(x: np.ndarray, w_router: np.ndarray, router_bias, w_in, w_out, 
         "gap": gap, "gate": gate, "slot": slot, "dropped": dropped,
         "expert_count": count, "aux_loss": aux, "y_bare": y_bare, "y": y,
     }
+
+
+# ---------------------------------------------------------------------------
+# Backward pass ("Switch Routing": the gate multiplies the expert output, so
+# the router stays differentiable with one expert; "The Load-Balancing Loss":
+# f_i is a hard count with no gradient, P_i is differentiable)
+# ---------------------------------------------------------------------------
+def softmax_backward(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """dL/dh from dL/dp through p = softmax(h): p * (dp - <dp, p>) per row
+    (the softmax Jacobian diag(p) - p p^T applied to dp)."""
+    return p * (dp - np.sum(dp * p, axis=1, keepdims=True))
+
+
+def expert_backward(x_e: np.ndarray, w_in_e: np.ndarray, w_out_e: np.ndarray, dy_e: np.ndarray,
+                    gate_e: np.ndarray):
+    """Backward of y = g W_out ReLU(W_in x) for the rows of one expert.
+
+    Returns (dL/dg per row, dW_in, dW_out, dL/dx rows): with u = W_in x,
+    h = ReLU(u), o = W_out h: dL/dg = <dy, o>, dL/do = g dy, dW_out =
+    sum (g dy) h^T, dL/du = (W_out^T g dy) * [u > 0], dW_in = sum dL/du x^T,
+    dL/dx = W_in^T dL/du.
+    """
+    u = x_e @ w_in_e.T
+    h = np.maximum(u, 0.0)
+    o = h @ w_out_e.T
+    dgate = np.sum(dy_e * o, axis=1)
+    do = gate_e[:, None] * dy_e
+    du = (do @ w_out_e) * (u > 0)
+    return dgate, du.T @ x_e, do.T @ h, du @ w_in_e
+
+
+def backward(x: np.ndarray, w_router: np.ndarray, router_bias, w_in, w_out, capacity: int,
+             dy: np.ndarray, d_aux: float, add_residual: bool = False,
+             expert_idx: np.ndarray | None = None) -> dict:
+    """Gradients of L = sum_t <dy_t, y_t> + d_aux * aux with respect to x,
+    W_r, the router bias, W_in and W_out, for the Switch layer (k = 1).
+
+    The routing (expert choice, capacity drops, the counts f_i) is held fixed
+    at the forward's values; expert_idx, when given, replaces the oracle's own
+    choice as in forward().  Kept tokens go through expert_backward with their
+    expert's weights.  Router: dL/dp_i(x_t) = d_aux N f_i / T (from P_i)
+    + [i = e, kept] dL/dg; dL/dh_t = softmax_backward(p, dL/dp); dW_r = sum_t
+    dL/dh_t x_t^T, dbias = sum_t dL/dh_t, dx_t += W_r^T dL/dh_t.  A dropped
+    token's bare output is 0, so only the loss term reaches its router.  With
+    the residual, dx_t += dy_t.
+    """
+    fwd = forward(x, w_router, router_bias, w_in, w_out, capacity, add_residual=add_residual,
+                  expert_idx=expert_idx)
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    T, d = x.shape
+    N = w_router.shape[0]
+    get = _weights(w_in, w_out)
+    idx, dropped, gate, p = fwd["expert_idx"], fwd["dropped"], fwd["gate"], fwd["probs"]
+    dx = dy.copy() if add_residual else np.zeros((T, d))
+    dgate = np.zeros(T)
+    dw_in, dw_out = [], []
+    for i in range(N):
+        wi, wo = get(i)
+        wi = np.asarray(wi, np.float64)
+        wo = np.asarray(wo, np.float64)
+        rows = np.nonzero((idx == i) & ~dropped)[0]
+        if len(rows):
+            dg, gi, go, dxr = expert_backward(x[rows], wi, wo, dy[rows], gate[rows])
+            dgate[rows] = dg
+            dx[rows] += dxr
+        else:
+            gi, go = np.zeros_like(wi), np.zeros_like(wo)
+        dw_in.append(gi)
+        dw_out.append(go)
+    if T:
+        f = np.bincount(idx, minlength=N) / T
+        dp = np.tile(d_aux * N * f / T, (T, 1))
+        kept = np.nonzero(~dropped)[0]
+        dp[kept, idx[kept]] += dgate[kept]
+        dh = softmax_backward(p, dp)
+    else:
+        dh = np.zeros((0, N))
+    dw_r = dh.T @ x
+    db = dh.sum(axis=0)
+    dx += dh @ np.asarray(w_router, np.float64)
+    return {"dx": dx, "dw_router": dw_r, "d_router_bias": db, "dw_in": dw_in, "dw_out": dw_out,
+            "dgate": dgate, "dlogits": dh, "forward": fwd}

@@ -408,6 +408,105 @@ def pin_topk_aux_uniform():
         assert out["expert_idx"].tolist() == [[r] * T for r in range(k)]  # all-tie -> lowest indices
 
 
+def _bwd_loss(x, w_r, b, w_in, w_out, C, dy, d_aux, res):
+    out = so.forward(x, w_r, b, w_in, w_out, C, add_residual=res)
+    return float(np.sum(dy * out["y"]) + d_aux * out["aux_loss"]), out
+
+
+def pin_backward_finite_differences(rng):
+    """Backward pass against central finite differences of the forward
+    oracle's L = <dy, y> + d_aux aux, for every scalar of x, W_r, b, W_in and
+    W_out, with drops and with and without the residual.  The routing must not
+    change under the perturbation (checked), so f_i stays fixed as the
+    write-up's hard count."""
+    T, d, f, N = 9, 4, 5, 3
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, N, scale=1.5)
+    b = np.array([0.7, 0.0, -0.4])
+    dy = rng.standard_normal((T, d))
+    eps = 1e-6
+    for res, C in ((False, 2), (True, 3)):
+        g = so.backward(x, w_r, b, w_in, w_out, C, dy, 0.37, add_residual=res)
+        base = g["forward"]
+        assert base["dropped"].any()
+        params = [("x", x, g["dx"]), ("w_r", w_r, g["dw_router"]), ("b", b, g["d_router_bias"]),
+                  ("w_in", w_in, np.stack(g["dw_in"])), ("w_out", w_out, np.stack(g["dw_out"]))]
+        for name, arr, grad in params:
+            for i in np.ndindex(arr.shape):
+                old = arr[i]
+                arr[i] = old + eps
+                lp, op = _bwd_loss(x, w_r, b, w_in, w_out, C, dy, 0.37, res)
+                arr[i] = old - eps
+                lm, om = _bwd_loss(x, w_r, b, w_in, w_out, C, dy, 0.37, res)
+                arr[i] = old
+                for o in (op, om):
+                    assert np.array_equal(o["expert_idx"], base["expert_idx"])
+                    assert np.array_equal(o["dropped"], base["dropped"])
+                fd = (lp - lm) / (2 * eps)
+                assert abs(fd - grad[i]) <= 2e-6 * (1 + abs(fd)), (name, i, fd, grad[i], res)
+
+
+def pin_backward_aux_closed_form():
+    """'The Load-Balancing Loss': with W_r = 0 every p_i = 1/N and every token
+    ties to expert 0, so f = e_0; with dy = 0 and d_aux = 1 the logit gradient
+    is (e_0 - 1/N) / T for every token, dW_r = (e_0 - 1/N) (sum_t x_t)^T / T,
+    dbias = e_0 - 1/N, and nothing reaches the experts or x."""
+    rng = np.random.default_rng(3)
+    for N in (2, 5):
+        T, d, f = 6, 3, 4
+        x = rng.standard_normal((T, d))
+        w_in, w_out = rng.standard_normal((N, f, d)), rng.standard_normal((N, d, f))
+        g = so.backward(x, np.zeros((N, d)), None, w_in, w_out, T, np.zeros((T, d)), 1.0)
+        v = -np.full(N, 1.0 / N)
+        v[0] += 1.0
+        np.testing.assert_allclose(g["dlogits"], np.tile(v / T, (T, 1)), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(g["dw_router"], np.outer(v, x.sum(axis=0)) / T, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(g["d_router_bias"], v, rtol=0, atol=1e-14)
+        assert np.all(g["dx"] == 0.0)
+        assert all(np.all(a == 0.0) for a in g["dw_in"] + g["dw_out"])
+
+
+def pin_backward_single_expert_dense(rng):
+    """N = 1: the gate is 1 and the softmax of one logit has no gradient, so
+    the router gets nothing and the experts' gradients are the dense ReLU
+    FFN's, written out with explicit loops."""
+    T, d, f = 5, 3, 4
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, 1)
+    dy = rng.standard_normal((T, d))
+    g = so.backward(x, w_r, None, w_in, w_out, T, dy, 0.5)
+    assert np.all(g["dw_router"] == 0.0) and np.all(g["d_router_bias"] == 0.0)
+    wi, wo = w_in[0], w_out[0]
+    dwi, dwo, dx = np.zeros_like(wi), np.zeros_like(wo), np.zeros_like(x)
+    for t in range(T):
+        u = [sum(wi[j, k] * x[t, k] for k in range(d)) for j in range(f)]
+        h = [max(0.0, v) for v in u]
+        dh = [sum(wo[n, j] * dy[t, n] for n in range(d)) for j in range(f)]
+        du = [dh[j] if u[j] > 0 else 0.0 for j in range(f)]
+        for n in range(d):
+            for j in range(f):
+                dwo[n, j] += dy[t, n] * h[j]
+        for j in range(f):
+            for k in range(d):
+                dwi[j, k] += du[j] * x[t, k]
+                dx[t, k] += wi[j, k] * du[j]
+    np.testing.assert_allclose(g["dw_out"][0], dwo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dw_in"][0], dwi, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dx"], dx, rtol=0, atol=1e-12)
+
+
+def pin_backward_dropped_tokens(rng):
+    """A dropped token's bare output is 0: with no loss term its gradient is
+    exactly 0 (bare) or exactly dy (residual), and its logits get nothing."""
+    T, d, f, N = 12, 4, 5, 3
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, N, scale=2.0)
+    dy = rng.standard_normal((T, d))
+    for res in (False, True):
+        g = so.backward(x, w_r, np.array([2.0, 0.0, 0.0]), w_in, w_out, 2, dy, 0.0, add_residual=res)
+        drop = g["forward"]["dropped"]
+        assert drop.sum() >= 3
+        assert np.all(g["dlogits"][drop] == 0.0)
+        assert np.array_equal(g["dx"][drop], dy[drop] if res else np.zeros_like(dy[drop]))
+
+
 ALL_PINS = [
     pin_capacity_table, pin_hand_example, pin_softmax_library, pin_top1_bruteforce,
     pin_router_logits_loops, pin_slots_stable_sort, pin_slots_bruteforce,
@@ -416,6 +515,8 @@ ALL_PINS = [
     pin_add_norm_zscore, pin_add_norm_hand, pin_add_norm_invariants,
     pin_topk_hand_example, pin_topk_choice_loops, pin_topk_k1_is_switch, pin_topk_dense_mixture,
     pin_topk_route_major_bruteforce, pin_topk_aux_uniform,
+    pin_backward_finite_differences, pin_backward_aux_closed_form, pin_backward_single_expert_dense,
+    pin_backward_dropped_tokens,
 ]
 
 
@@ -543,7 +644,45 @@ def _mut_topk_skips_second(*args, **kw):
     return out
 
 
-_ORIG = {k: getattr(so, k) for k in ("assign_slots", "load_balancing_loss", "top1", "expert_ffn",
+def _mut_softmax_bwd_no_mean(p, dp):
+    return p * dp
+
+
+def _mut_expert_bwd_no_relu_mask(x_e, w_in_e, w_out_e, dy_e, gate_e):
+    o = np.maximum(x_e @ w_in_e.T, 0.0) @ w_out_e.T
+    do = gate_e[:, None] * dy_e
+    du = do @ w_out_e
+    return np.sum(dy_e * o, axis=1), du.T @ x_e, do.T @ np.maximum(x_e @ w_in_e.T, 0.0), du @ w_in_e
+
+
+def _mut_expert_bwd_no_gate(x_e, w_in_e, w_out_e, dy_e, gate_e):
+    return _ORIG["expert_backward"](x_e, w_in_e, w_out_e, dy_e, np.ones_like(gate_e))
+
+
+def _mut_expert_bwd_pre_relu(x_e, w_in_e, w_out_e, dy_e, gate_e):
+    dg, gi, go, dx = _ORIG["expert_backward"](x_e, w_in_e, w_out_e, dy_e, gate_e)
+    return dg, gi, (gate_e[:, None] * dy_e).T @ (x_e @ w_in_e.T), dx
+
+
+def _mut_bwd_aux_ignored(*args, **kw):
+    args = list(args)
+    if len(args) > 7:
+        args[7] = 0.0
+    else:
+        kw["d_aux"] = 0.0
+    return _ORIG["backward"](*args, **kw)
+
+
+def _mut_bwd_residual_ignored(*args, **kw):
+    out = _ORIG["backward"](*args, **kw)
+    res = kw.get("add_residual", args[8] if len(args) > 8 else False)
+    if res:
+        dy = args[6] if len(args) > 6 else kw["dy"]
+        out["dx"] = out["dx"] - dy
+    return out
+
+
+_ORIG = {k: getattr(so, k) for k in ("softmax_backward", "expert_backward", "backward","assign_slots", "load_balancing_loss", "top1", "expert_ffn",
                                      "softmax", "router_logits", "add_normalize", "topk_choice",
                                      "load_balancing_loss_topk", "forward_topk")}
 
@@ -565,6 +704,12 @@ MUTANTS = {
     "topk_f_over_T": ("load_balancing_loss_topk", _mut_topk_f_over_T),
     "topk_renormalised_gates": ("forward_topk", _mut_topk_renormalised),
     "topk_second_route_ignored": ("forward_topk", _mut_topk_skips_second),
+    "bwd_softmax_without_mean": ("softmax_backward", _mut_softmax_bwd_no_mean),
+    "bwd_no_relu_mask": ("expert_backward", _mut_expert_bwd_no_relu_mask),
+    "bwd_gate_ignored": ("expert_backward", _mut_expert_bwd_no_gate),
+    "bwd_w_out_grad_pre_relu": ("expert_backward", _mut_expert_bwd_pre_relu),
+    "bwd_aux_ignored": ("backward", _mut_bwd_aux_ignored),
+    "bwd_residual_ignored": ("backward", _mut_bwd_residual_ignored),
 }
 
 
