@@ -195,6 +195,56 @@ int switch_topk_layer_forward(const switch_shape *s, int32_t top_k, const void *
                               int32_t *expert_count, float *aux_loss, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* Backward pass of the Switch layer (k = 1): the gradients of a loss
+ * L = <dy, y> + d_aux * aux_loss with respect to the layer's inputs, for the
+ * routing of the preceding switch_layer_forward call ("Switch Routing: From
+ * Top-k to k = 1": the gate multiplies the expert output, which keeps the
+ * router differentiable; "The Load-Balancing Loss": f_i is a hard count with
+ * no gradient, P_i is differentiable; "Making Sparse Training Stable": the
+ * router's arithmetic stays in fp32).  The routing is held fixed: expert
+ * choices, drops and f_i are the forward's.  For a kept token t with expert
+ * e, gate g, u = W_in,e x, h = ReLU(u) and z = W_out,e^T dy_t:
+ *   dL/dg = <z, h>,  du = g z [h > 0],
+ *   dW_out,e += (g dy_t) h^T,  dW_in,e += du x_t^T,  dx_t += W_in,e^T du;
+ * router, every token: dL/dp_i = d_aux N f_i / T + [i = e, t kept] dL/dg,
+ *   dL/dh = p (dL/dp - <dL/dp, p>),  dW_r += dL/dh x_t^T,
+ *   dbias += dL/dh,  dx_t += W_r^T dL/dh;  with add_residual, dx_t += dy_t.
+ * Inputs: the forward's shape, x, w_router, router_bias, w_in, w_out and
+ * add_residual; its outputs expert_idx [T], dropped [T], expert_count [N];
+ * fwd_workspace: the workspace the forward call used, unmodified since (it
+ * holds the hidden activations H and the slot maps); dy [T][d] (activation
+ * dtype); d_aux (host scalar, finite: the weight of aux_loss in L, e.g. the
+ * alpha of the write-up).
+ * Outputs (device, caller-owned, overwritten): dx [T][d] and dw_in
+ * [N][d_ff][d], dw_out [N][d][d_ff] in the activation dtype; dw_router [N][d]
+ * and d_router_bias [N] (may be NULL) in fp32.  An expert that received no
+ * kept token gets exact zeros.  Arithmetic: bf16 MFMA with fp32 accumulation
+ * for the expert products (du and g dy rounded to bf16 as operands), fp32 for
+ * the router; dx summed in fp32 and rounded once.  Deterministic.
+ * workspace: switch_backward_workspace_bytes bytes (256-byte aligned).
+ * Errors: as switch_layer_forward; SWITCH_E_WORKSPACE if fwd_workspace_bytes
+ * is below the forward's workspace size. */
+int switch_backward_workspace_bytes(const switch_shape *s, size_t *bytes_out);
+int switch_layer_backward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                          const void *w_in, const void *w_out, int32_t add_residual, const int32_t *expert_idx,
+                          const uint8_t *dropped, const int32_t *expert_count, const void *fwd_workspace,
+                          size_t fwd_workspace_bytes, const void *dy, float d_aux, void *dx, float *dw_router,
+                          float *d_router_bias, void *dw_in, void *dw_out, void *workspace, size_t workspace_bytes,
+                          void *stream);
+/* Measurement variant of switch_layer_backward, with the contract of
+ * switch_layer_forward_profiled: kernels first_kernel..last_kernel only, each
+ * `times` times.  The backward launches 7 kernels, in order: "bwd_dz",
+ * "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_w",
+ * "bwd_router_w_sum"; none modifies its own inputs. */
+int switch_layer_backward_profiled(const switch_shape *s, const void *x, const float *w_router,
+                                   const float *router_bias, const void *w_in, const void *w_out,
+                                   int32_t add_residual, const int32_t *expert_idx, const uint8_t *dropped,
+                                   const int32_t *expert_count, const void *fwd_workspace,
+                                   size_t fwd_workspace_bytes, const void *dy, float d_aux, void *dx,
+                                   float *dw_router, float *d_router_bias, void *dw_in, void *dw_out,
+                                   void *workspace, size_t workspace_bytes, void *stream, int32_t first_kernel,
+                                   int32_t last_kernel, int32_t times);
+
 /* Measurement variant of switch_layer_forward: same arguments and
  * asynchrony, but it launches only the kernels numbered first_kernel ..
  * last_kernel of the call (0-based, in the order switch_launch_names gives),

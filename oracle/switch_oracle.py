@@ -388,7 +388,7 @@ def expert_backward(x_e: np.ndarray, w_in_e: np.ndarray, w_out_e: np.ndarray, dy
 
 def backward(x: np.ndarray, w_router: np.ndarray, router_bias, w_in, w_out, capacity: int,
              dy: np.ndarray, d_aux: float, add_residual: bool = False,
-             expert_idx: np.ndarray | None = None) -> dict:
+             expert_idx: np.ndarray | None = None, weight_grads_for: Sequence[int] | None = None) -> dict:
     """Gradients of L = sum_t <dy_t, y_t> + d_aux * aux with respect to x,
     W_r, the router bias, W_in and W_out, for the Switch layer (k = 1).
 
@@ -399,7 +399,15 @@ def backward(x: np.ndarray, w_router: np.ndarray, router_bias, w_in, w_out, capa
     + [i = e, kept] dL/dg; dL/dh_t = softmax_backward(p, dL/dp); dW_r = sum_t
     dL/dh_t x_t^T, dbias = sum_t dL/dh_t, dx_t += W_r^T dL/dh_t.  A dropped
     token's bare output is 0, so only the loss term reaches its router.  With
-    the residual, dx_t += dy_t.
+    the residual, dx_t += dy_t.  weight_grads_for, when given, keeps the
+    weight gradients of those experts only (the others are None); every
+    expert's rows still feed dx and the router.
+
+    Also returned, for the gradients that are sums over tokens, the root sum
+    of squares of their terms (d_router_bias_rss, dw_router_rss, dw_in_rss,
+    dw_out_rss): the scale of the rounding error such a sum can carry when its
+    terms carry independent relative errors, whatever cancellation the sum
+    itself has.
     """
     fwd = forward(x, w_router, router_bias, w_in, w_out, capacity, add_residual=add_residual,
                   expert_idx=expert_idx)
@@ -411,20 +419,29 @@ def backward(x: np.ndarray, w_router: np.ndarray, router_bias, w_in, w_out, capa
     idx, dropped, gate, p = fwd["expert_idx"], fwd["dropped"], fwd["gate"], fwd["probs"]
     dx = dy.copy() if add_residual else np.zeros((T, d))
     dgate = np.zeros(T)
-    dw_in, dw_out = [], []
+    dw_in, dw_out, dw_in_rss, dw_out_rss = [], [], [], []
     for i in range(N):
         wi, wo = get(i)
         wi = np.asarray(wi, np.float64)
         wo = np.asarray(wo, np.float64)
         rows = np.nonzero((idx == i) & ~dropped)[0]
+        keep = weight_grads_for is None or i in weight_grads_for
         if len(rows):
             dg, gi, go, dxr = expert_backward(x[rows], wi, wo, dy[rows], gate[rows])
             dgate[rows] = dg
             dx[rows] += dxr
+            if keep:  # term scales: du_t x_t^T and (g dy_t) h_t^T
+                u = x[rows] @ wi.T
+                du = ((gate[rows, None] * dy[rows]) @ wo) * (u > 0)
+                ri = np.sqrt((du ** 2).T @ (x[rows] ** 2))
+                ro = np.sqrt(((gate[rows, None] * dy[rows]) ** 2).T @ (np.maximum(u, 0.0) ** 2))
         else:
             gi, go = np.zeros_like(wi), np.zeros_like(wo)
-        dw_in.append(gi)
-        dw_out.append(go)
+            ri, ro = np.zeros_like(wi), np.zeros_like(wo)
+        dw_in.append(gi if keep else None)
+        dw_out.append(go if keep else None)
+        dw_in_rss.append(ri if keep else None)
+        dw_out_rss.append(ro if keep else None)
     if T:
         f = np.bincount(idx, minlength=N) / T
         dp = np.tile(d_aux * N * f / T, (T, 1))
@@ -437,4 +454,6 @@ def backward(x: np.ndarray, w_router: np.ndarray, router_bias, w_in, w_out, capa
     db = dh.sum(axis=0)
     dx += dh @ np.asarray(w_router, np.float64)
     return {"dx": dx, "dw_router": dw_r, "d_router_bias": db, "dw_in": dw_in, "dw_out": dw_out,
-            "dgate": dgate, "dlogits": dh, "forward": fwd}
+            "dgate": dgate, "dlogits": dh, "forward": fwd,
+            "d_router_bias_rss": np.sqrt((dh ** 2).sum(axis=0)), "dw_router_rss": np.sqrt((dh ** 2).T @ (x ** 2)),
+            "dw_in_rss": dw_in_rss, "dw_out_rss": dw_out_rss}

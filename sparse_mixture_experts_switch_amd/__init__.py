@@ -8,14 +8,18 @@ library has not been built.
 """
 
 from .binding import (  # noqa: F401
+    BACKWARD_KERNELS,
     SWITCH_BF16,
     SWITCH_F32,
     SwitchError,
     add_norm,
+    backward_workspace_bytes,
     capacity,
     combine,
     dispatch,
     expert_ffn,
+    layer_backward,
+    layer_backward_profiled,
     layer_forward,
     layer_forward_profiled,
     launch_names,

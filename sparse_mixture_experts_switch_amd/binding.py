@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "SwitchError", "load_library", "capacity", "workspace_bytes", "route", "dispatch",
     "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "launch_names", "add_norm",
-    "topk_workspace_bytes", "topk_layer_forward", "SWITCH_F32", "SWITCH_BF16",
+    "topk_workspace_bytes", "topk_layer_forward", "backward_workspace_bytes", "layer_backward",
+    "layer_backward_profiled", "BACKWARD_KERNELS", "SWITCH_F32", "SWITCH_BF16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswitchmoe.so")
@@ -30,7 +31,10 @@ EXPORTED = [
     "switch_capacity", "switch_workspace_bytes", "switch_last_error", "switch_route", "switch_dispatch",
     "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
     "switch_launch_names", "switch_add_norm", "switch_topk_workspace_bytes", "switch_topk_layer_forward",
+    "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
 ]
+BACKWARD_KERNELS = ["bwd_dz", "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_w",
+                    "bwd_router_w_sum"]
 
 
 class SwitchError(RuntimeError):
@@ -75,6 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.switch_launch_names.argtypes = [sp, _P, ctypes.c_int32, _P]
     lib.switch_add_norm.argtypes = [sp, _P, _P, _P, _P, ctypes.c_float, _P, _P]
     lib.switch_topk_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    bwd = [sp, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, sz, _P, ctypes.c_float] + [_P] * 6 + [sz, _P]
+    lib.switch_backward_workspace_bytes.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.switch_layer_backward.argtypes = bwd
+    lib.switch_layer_backward_profiled.argtypes = bwd + [ctypes.c_int32] * 3
     lib.switch_topk_layer_forward.argtypes = (
         [sp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P])
     for name in EXPORTED:
@@ -282,6 +290,56 @@ def topk_layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: tor
         ctypes.byref(shape), int(top_k), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_in), _ptr(w_out),
         1 if add_residual else 0, _ptr(o["y"]), _ptr(o["expert_idx"]), _ptr(o["gate"]), _ptr(o["slot"]),
         _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]), _ptr(ws), ws.numel(), _stream(dev)))
+    return o
+
+
+def backward_workspace_bytes(shape: Shape) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().switch_backward_workspace_bytes(ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
+
+
+def _bwd_args(x, w_router, router_bias, w_in, w_out, capacity_, fwd: dict, fwd_workspace, dy, d_aux,
+              add_residual, workspace, out):
+    T, d = x.shape
+    N, f = w_in.shape[0], w_in.shape[1]
+    shape = make_shape(T, d, f, N, capacity_, x.dtype)
+    dev = x.device
+    o = out if out is not None else {}
+    o.setdefault("dx", torch.empty(T, d, dtype=x.dtype, device=dev))
+    o.setdefault("dw_router", torch.empty(N, d, dtype=torch.float32, device=dev))
+    o.setdefault("d_router_bias", torch.empty(N, dtype=torch.float32, device=dev))
+    o.setdefault("dw_in", torch.empty_like(w_in))
+    o.setdefault("dw_out", torch.empty_like(w_out))
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(backward_workspace_bytes(shape), 256), dtype=torch.uint8, device=dev)
+    args = [ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_in), _ptr(w_out),
+            1 if add_residual else 0, _ptr(fwd["expert_idx"]), _ptr(fwd["dropped"]), _ptr(fwd["expert_count"]),
+            _ptr(fwd_workspace), fwd_workspace.numel(), _ptr(dy), float(d_aux), _ptr(o["dx"]), _ptr(o["dw_router"]),
+            _ptr(o["d_router_bias"]), _ptr(o["dw_in"]), _ptr(o["dw_out"]), _ptr(ws), ws.numel(), _stream(dev)]
+    return o, args
+
+
+def layer_backward(x, w_router, router_bias, w_in, w_out, capacity_: int, fwd: dict, fwd_workspace: torch.Tensor,
+                   dy: torch.Tensor, d_aux: float, add_residual: bool = False, workspace=None, out=None) -> dict:
+    """Gradients of <dy, y> + d_aux aux_loss for the routing of the forward
+    call whose outputs are `fwd` and whose workspace is `fwd_workspace`
+    (switch_layer_backward)."""
+    o, args = _bwd_args(x, w_router, router_bias, w_in, w_out, capacity_, fwd, fwd_workspace, dy, d_aux,
+                        add_residual, workspace, out)
+    _check(load_library().switch_layer_backward(*args))
+    return o
+
+
+def layer_backward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, fwd, fwd_workspace, dy, d_aux,
+                            first_kernel: int, last_kernel: int, times: int = 1, add_residual=False,
+                            workspace=None, out=None) -> dict:
+    """Kernels first_kernel..last_kernel of layer_backward only (names in
+    BACKWARD_KERNELS), each `times` times (switch_layer_backward_profiled)."""
+    o, args = _bwd_args(x, w_router, router_bias, w_in, w_out, capacity_, fwd, fwd_workspace, dy, d_aux,
+                        add_residual, workspace, out)
+    _check(load_library().switch_layer_backward_profiled(*args, int(first_kernel), int(last_kernel), int(times)))
     return o
 
 

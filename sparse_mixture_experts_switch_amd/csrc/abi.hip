@@ -294,6 +294,95 @@ int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *
   return SWITCH_OK;
 }
 
+// Workspace of switch_layer_backward: du [N][C][d_ff], the per-token partial
+// dots [T][n_dg], the experts' part of dx [T][d] (fp32), dL/dh [T][N], the
+// logits scratch when N > kRouterChunk, and the split partial sums of dW_r
+// and the bias gradient.
+struct BwdLayout {
+  size_t du = 0, dgpart = 0, dxe = 0, dh = 0, logits = 0, wpart = 0, bpart = 0, total = 0;
+  int n_dg = 0, splits = 1;
+};
+
+int bwd_layout(const switch_shape *s, BwdLayout &B) {
+  const int64_t T = s->tokens, N = s->num_experts, C = s->capacity, d = s->d_model, f = s->d_ff;
+  const int es = esize(s->dtype);
+  B.n_dg = bwd_dz_tiles(s->dtype, (int)f);
+  B.splits = router_wgrad_splits(T, (int)N, (int)d);
+  size_t du, dg, dxe, dh, lg = 0, wp, bp;
+  bool ok = mul(du, {N, C, f, es}) && mul(dg, {T, B.n_dg, 4}) && mul(dxe, {T, d, 4}) && mul(dh, {T, N, 4}) &&
+            (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(wp, {B.splits, N, d, 4}) && mul(bp, {B.splits, N, 4});
+  if (!ok) return fail(SWITCH_E_UNSUPPORTED, "backward buffer sizes overflow for this shape");
+  size_t o = 0;
+  B.du = o;
+  o = align_up(o + du);
+  B.dgpart = o;
+  o = align_up(o + dg);
+  B.dxe = o;
+  o = align_up(o + dxe);
+  B.dh = o;
+  o = align_up(o + dh);
+  B.logits = o;
+  o = align_up(o + lg);
+  B.wpart = o;
+  o = align_up(o + wp);
+  B.bpart = o;
+  o = align_up(o + bp);
+  B.total = o;
+  return SWITCH_OK;
+}
+
+int layer_backward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                   const void *w_in, const void *w_out, int32_t add_residual, const int32_t *expert_idx,
+                   const uint8_t *dropped, const int32_t *expert_count, const void *fwd_ws, size_t fwd_ws_bytes,
+                   const void *dy, float d_aux, void *dx, float *dw_router, float *d_router_bias, void *dw_in,
+                   void *dw_out, void *ws, size_t ws_bytes, void *stream, Timer &tm) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!std::isfinite(d_aux)) return fail(SWITCH_E_INVALID, "d_aux = %g is not finite", d_aux);
+  Layout L;
+  if ((rc = layout(s, L))) return rc;
+  BwdLayout B;
+  if ((rc = bwd_layout(s, B))) return rc;
+  if (!fwd_ws) return fail(SWITCH_E_INVALID, "fwd_workspace is NULL");
+  if (!aligned(fwd_ws, kWsAlign)) return fail(SWITCH_E_INVALID, "fwd_workspace is not 256-byte aligned");
+  if (fwd_ws_bytes < L.total)
+    return fail(SWITCH_E_WORKSPACE, "fwd_workspace of %zu bytes, the forward needs %zu", fwd_ws_bytes, L.total);
+  if ((rc = check_ws(ws, ws_bytes, B.total))) return rc;
+  NEED(w_router, 16);
+  if (router_bias && !aligned(router_bias, 4)) return fail(SWITCH_E_INVALID, "router_bias is not 4-byte aligned");
+  NEED(w_in, 16);
+  NEED(w_out, 16);
+  NEED(expert_count, 4);
+  NEED(dw_router, 16);
+  if (d_router_bias && !aligned(d_router_bias, 4))
+    return fail(SWITCH_E_INVALID, "d_router_bias is not 4-byte aligned");
+  NEED(dw_in, 16);
+  NEED(dw_out, 16);
+  if (s->tokens > 0) {
+    NEED(x, 16);
+    NEED(dy, 16);
+    NEED(dx, 16);
+    NEED(expert_idx, 4);
+    if (!dropped) return fail(SWITCH_E_INVALID, "dropped is NULL");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const char *fw = (const char *)fwd_ws;
+  char *w = (char *)ws;
+  BwdLaunch bl{s->dtype, s->tokens, s->d_model, s->d_ff, s->num_experts, s->capacity, x, w_in, w_out, dy,
+               expert_count, (const int32_t *)(fw + L.lf_tok), (const float *)(fw + L.lf_gmap),
+               fw + L.lf_hidden, w + B.du, (float *)(w + B.dgpart), (float *)(w + B.dxe), dw_in, dw_out};
+  LaunchMarks marks{[](void *ctx, const char *name) { static_cast<Timer *>(ctx)->mark(name); },
+                    [](void *ctx) { return static_cast<Timer *>(ctx)->reps(); }, &tm};
+  hipError_t e;
+  if ((e = launch_bwd_experts(bl, st, marks)) != hipSuccess) return hip_fail(e, "backward expert launch");
+  RouterBwdArgs ra{s->dtype, s->tokens, s->d_model, s->num_experts, x, w_router, router_bias,
+                   (float *)(w + B.logits), expert_idx, dropped, expert_count, (const float *)(w + B.dgpart),
+                   B.n_dg, d_aux, (const float *)(w + B.dxe), dy, add_residual ? 1 : 0, (float *)(w + B.dh), dx,
+                   dw_router, d_router_bias, (float *)(w + B.wpart), (float *)(w + B.bpart), B.splits};
+  if ((e = launch_router_bwd(ra, st, marks)) != hipSuccess) return hip_fail(e, "backward router launch");
+  return SWITCH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -511,6 +600,58 @@ int switch_topk_layer_forward(const switch_shape *s, int32_t top_k, const void *
     Timer tm;
     return layer_forward(s, top_k, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
                          dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
+  })
+}
+
+int switch_backward_workspace_bytes(const switch_shape *s, size_t *bytes_out) {
+  GUARD({
+    if (!bytes_out) return fail(SWITCH_E_INVALID, "bytes_out is NULL");
+    int rc = check_shape(s);
+    if (rc) return rc;
+    BwdLayout B;
+    if ((rc = bwd_layout(s, B))) return rc;
+    *bytes_out = B.total;
+    return SWITCH_OK;
+  })
+}
+
+int switch_layer_backward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                          const void *w_in, const void *w_out, int32_t add_residual, const int32_t *expert_idx,
+                          const uint8_t *dropped, const int32_t *expert_count, const void *fwd_workspace,
+                          size_t fwd_workspace_bytes, const void *dy, float d_aux, void *dx, float *dw_router,
+                          float *d_router_bias, void *dw_in, void *dw_out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  GUARD({
+    Timer tm;
+    return layer_backward(s, x, w_router, router_bias, w_in, w_out, add_residual, expert_idx, dropped, expert_count,
+                          fwd_workspace, fwd_workspace_bytes, dy, d_aux, dx, dw_router, d_router_bias, dw_in,
+                          dw_out, workspace, workspace_bytes, stream, tm);
+  })
+}
+
+int switch_layer_backward_profiled(const switch_shape *s, const void *x, const float *w_router,
+                                   const float *router_bias, const void *w_in, const void *w_out,
+                                   int32_t add_residual, const int32_t *expert_idx, const uint8_t *dropped,
+                                   const int32_t *expert_count, const void *fwd_workspace,
+                                   size_t fwd_workspace_bytes, const void *dy, float d_aux, void *dx,
+                                   float *dw_router, float *d_router_bias, void *dw_in, void *dw_out,
+                                   void *workspace, size_t workspace_bytes, void *stream, int32_t first_kernel,
+                                   int32_t last_kernel, int32_t times) {
+  GUARD({
+    if (times < 1) return fail(SWITCH_E_INVALID, "times = %d < 1", times);
+    if (first_kernel < 0 || last_kernel < first_kernel)
+      return fail(SWITCH_E_INVALID, "kernel range %d..%d", first_kernel, last_kernel);
+    Timer tm;
+    tm.first = first_kernel;
+    tm.last = last_kernel;
+    tm.times = times;
+    int rc = layer_backward(s, x, w_router, router_bias, w_in, w_out, add_residual, expert_idx, dropped,
+                            expert_count, fwd_workspace, fwd_workspace_bytes, dy, d_aux, dx, dw_router,
+                            d_router_bias, dw_in, dw_out, workspace, workspace_bytes, stream, tm);
+    if (rc == SWITCH_OK && last_kernel >= tm.n)
+      return fail(SWITCH_E_INVALID, "kernel range %d..%d: the call launches %d kernels", first_kernel, last_kernel,
+                  tm.n);
+    return rc;
   })
 }
 

@@ -1,0 +1,560 @@
+// Backward pass of the Switch layer: the grouped GEMMs of the experts.
+//
+// Switch Transformers write-up, "Switch Routing: From Top-k to k = 1": the
+// gate p_e(x) multiplies the chosen expert's output, which keeps the router
+// differentiable; "Making Sparse Training Stable" (selective precision: the
+// router's arithmetic stays in fp32, the experts run in bf16).  With L the
+// caller's loss and dy = dL/dy, for a kept token t of expert e with gate g,
+// u = W_in,e x, h = ReLU(u) (the forward's saved H) and z = W_out,e^T dy:
+//   dL/dg = <z, h>               (= <dy, W_out,e h>)
+//   du    = g z * [h > 0]        (dL/du)
+//   dW_out,e += (g dy) h^T,  dW_in,e += du x^T,  dx_t += W_in,e^T du.
+// Per expert, with the expert's kept rows stacked in slot order:
+//   DZ: Z = DY W_out,e           rows x d_ff, contraction d     (B k-major)
+//   DX: DX_e = DU W_in,e         rows x d,    contraction d_ff  (B k-major)
+//   DWO: dW_out,e = (G DY)^T H   d x d_ff,    contraction rows  (A, B k-major)
+//   DWI: dW_in,e = DU^T X        d_ff x d,    contraction rows  (A, B k-major)
+// "k-major" operands are stored with the contraction index as the row; the
+// MFMA wants 8 consecutive contraction values per lane, so those tiles are
+// staged in LDS as stored (16-byte row pieces) and read with the gfx950 LDS
+// transpose load (ds_read_b64_tr_b16): within each group of 16 lanes, lane
+// 4r + q reads 4 consecutive elements of LDS row r at column 4q, and lane j
+// receives element j % 4 of the reads of lanes j / 4, 4 + j / 4, 8 + j / 4,
+// 12 + j / 4 -- that is, column j of the 4-row block, rows 0..3.  Two such
+// loads give a lane its 8 contraction values.
+//
+// One workgroup computes one (expert, row tile, column tile); both operands
+// pass through a double-buffered LDS tile (registers prefetch the next
+// 64-wide contraction chunk while the MFMAs consume the current one).  Rows
+// of an expert past its kept count are never stored; contraction rows past it
+// (DWO / DWI) are zero, so an expert with no kept token gets exact zero
+// gradients.  Results are deterministic: fixed tiles, fixed reduction order.
+
+#include "common.h"
+#include "launch.h"
+
+namespace smx {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+namespace {
+
+constexpr int kBKC = 64;           // contraction columns per chunk
+constexpr int kKcStride = kBKC + 8;  // LDS row of a k-contiguous tile (bf16)
+
+// Two transposed LDS loads -> the 8 contraction values of one MFMA operand.
+__device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int stride, int k0, int c0, int lane) {
+  const int g = lane / 16, i = lane % 16;
+  const bf16 *p = tile + (k0 + 8 * g + i / 4) * stride + c0 + 4 * (i % 4);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 4 * stride));
+  const u32x4 v{__builtin_bit_cast(u32x2v, lo)[0], __builtin_bit_cast(u32x2v, lo)[1],
+                __builtin_bit_cast(u32x2v, hi)[0], __builtin_bit_cast(u32x2v, hi)[1]};
+  return as_bf16x8(v);
+}
+
+}  // namespace
+
+// Operand tile loader.  A tile covers R rows (output rows for A, output
+// columns for B) and kBKC contraction columns.
+//  KM = false (k-contiguous): element (r, k) at base + row(r) * ld + k; LDS
+//    [R][kKcStride]; rows r past the live count re-read the last live row.
+//  KM = true (k-major): element (r, k) at base + krow(k) * ld + r; LDS
+//    [kBKC][R + 8]; contraction rows past `klive` are zero.
+// Rows come through the slot -> token map when G (gathered rows of a [T][ld]
+// array); k-major gathered rows may be scaled by the slot's gate (S).
+template <int R, int kThreads, bool KM, bool G, bool S>
+struct TileLoader {
+  static constexpr int kPieces = R * kBKC / 8;
+  static constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
+  static constexpr int kStride = KM ? R + 8 : kKcStride;
+  static constexpr int kElems = KM ? kBKC * kStride : R * kStride;
+  u32x4 reg[kPer];
+  int off[kPer];     // LDS element offset of each piece
+  int rk[kPer];      // row (KC) or contraction row within the chunk (KM)
+  int col[kPer];     // column element offset within the row piece
+  bool act[kPer];
+
+  __device__ __forceinline__ void plan(int tid) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = tid + q * kThreads;
+      act[q] = i < kPieces;
+      const int ii = act[q] ? i : 0;
+      if (KM) {
+        rk[q] = ii / (R / 8);
+        col[q] = (ii % (R / 8)) * 8;
+        off[q] = rk[q] * kStride + col[q];
+      } else {
+        rk[q] = ii / (kBKC / 8);
+        col[q] = (ii % (kBKC / 8)) * 8;
+        off[q] = rk[q] * kStride + col[q];
+      }
+    }
+  }
+
+  // KC: rows r0 + rk of the expert (live count `live`); chunk at k0.
+  // KM: contraction rows k0 + rk (live count `live`), columns c0 + col.
+  __device__ __forceinline__ void fetch(const bf16 *base, int64_t estride, int ld, const int32_t *tok,
+                                        const float *gmap, int64_t eC, int r0, int c0, int live, int k0, int rmax) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      if (!act[q]) continue;
+      if (KM) {
+        const int k = k0 + rk[q];
+        const bool ok = k < live;
+        const int kk = ok ? k : max(live - 1, 0);
+        const int64_t row = G ? (int64_t)tok[eC + kk] : kk;
+        const int c = min(c0 + col[q], rmax - 8);
+        u32x4 v = *(const u32x4 *)(base + (G ? 0 : estride) + row * ld + c);
+        if (S) {
+          const float g = gmap[eC + kk];
+          bf16x8 b = as_bf16x8(v);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) b[j] = (bf16)(g * (float)b[j]);
+          v = as_u32x4(b);
+        }
+        reg[q] = ok ? v : u32x4{0, 0, 0, 0};
+      } else {
+        const int r = min(r0 + rk[q], max(live - 1, 0));
+        const int64_t row = G ? (int64_t)tok[eC + r] : r;
+        reg[q] = *(const u32x4 *)(base + (G ? 0 : estride) + row * ld + k0 + col[q]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16 *lds) const {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if (act[q]) *(u32x4 *)(lds + off[q]) = reg[q];
+  }
+};
+
+enum BwdEpi { kEpiDU = 0, kEpiDX = 1, kEpiDW = 2 };
+
+template <typename T_>
+struct BwdArgs {
+  int C;
+  const int32_t *counts;  // [N] routed tokens per expert (kept = min(count, C))
+  const int32_t *tok;     // [N][C] token of each live slot
+  const float *gmap;      // [N][C] gate of each live slot
+  const T_ *A;
+  int64_t a_estride;      // elements per expert (non-gathered operands)
+  int lda;
+  const T_ *B;
+  int64_t b_estride;
+  int ldb;
+  int M, Nout, K;         // fixed dimensions (the live row count replaces M for DU / DX, K for DW)
+  void *Out;
+  int64_t o_estride;
+  int ldo;
+  const T_ *H;            // [N][C][Nout] forward hidden activations (DU)
+  float *dgpart;          // [T][n_tiles] partial <z, h> per token (DU)
+  int m_tiles, n_tiles;
+  int64_t ntiles;
+};
+
+// MBW x NBW MFMA blocks per wave, WM x WN waves.
+template <int MBW, int NBW, int WM, int WN, bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
+__global__ __launch_bounds__(WM *WN * 64) void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
+  constexpr int kThreads = WM * WN * 64;
+  constexpr int BM = WM * MBW * 16, BN = WN * NBW * 16;
+  constexpr bool kRaggedM = EPI != kEpiDW;
+  using LA = TileLoader<BM, kThreads, AKM, AG, AS>;
+  using LB = TileLoader<BN, kThreads, BKM, BG, false>;
+  constexpr int kStageStride = NBW * 16 + 4;  // fp32 epilogue staging row (per wave)
+  constexpr int kOperandElems = 2 * (LA::kElems + LB::kElems);
+  constexpr int kStageElems = WM * WN * 16 * kStageStride * 2;  // in bf16 units
+  constexpr int kSmem = kOperandElems > kStageElems ? kOperandElems : kStageElems;
+  __shared__ __attribute__((aligned(16))) bf16 smem[kSmem];
+  __shared__ float s_dg[WN][BM];
+
+  // XCD-aware tile order: blocks b, b + 8, ... run on one XCD; XCD x takes
+  // the contiguous tile range [x per, (x + 1) per) so that the tiles of an
+  // expert share one L2.
+  const int64_t per = (p.ntiles + 7) / 8;
+  const int64_t id = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (id >= p.ntiles || blockIdx.x / 8 >= per) return;
+  const int e = (int)(id / ((int64_t)p.m_tiles * p.n_tiles));
+  const int rem = (int)(id % ((int64_t)p.m_tiles * p.n_tiles));
+  const int mt = rem / p.n_tiles, nt = rem % p.n_tiles;
+  const int live = min(p.counts[e], p.C);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int Mt = kRaggedM ? live : p.M;
+  if (m0 >= Mt) return;  // dead tile (ragged rows)
+  const int Kt = kRaggedM ? p.K : live;
+  const int64_t eC = (int64_t)e * p.C;
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / WN, wn = wave % WN;
+  const int r16 = lane % 16, kq = (lane / 16) * 8;
+
+  LA la;
+  LB lb;
+  la.plan(tid);
+  lb.plan(tid);
+  auto sA = [&](int b) { return smem + b * LA::kElems; };
+  auto sB = [&](int b) { return smem + 2 * LA::kElems + b * LB::kElems; };
+  const bf16 *Ab = p.A + (AG ? 0 : (int64_t)e * p.a_estride);
+  const bf16 *Bb = p.B + (BG ? 0 : (int64_t)e * p.b_estride);
+
+  // A rows: output rows (KC: live count Mt) or output rows with contraction
+  // rows live up to Kt (KM).  B likewise with the output columns.
+  auto fetch = [&](int k0) {
+    if (AKM)
+      la.fetch(Ab, 0, p.lda, p.tok, p.gmap, eC, 0, m0, Kt, k0, p.M);
+    else
+      la.fetch(Ab, 0, p.lda, p.tok, p.gmap, eC, m0, 0, Mt, k0, 0);
+    if (BKM)
+      lb.fetch(Bb, 0, p.ldb, p.tok, p.gmap, eC, 0, n0, Kt, k0, p.Nout);
+    else
+      lb.fetch(Bb, 0, p.ldb, p.tok, p.gmap, eC, n0, 0, p.Nout, k0, 0);
+  };
+
+  f32x4 acc[MBW][NBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nch = (int)ceil_div(Kt, kBKC);
+  if (nch > 0) {
+    fetch(0);
+    la.store(sA(0));
+    lb.store(sB(0));
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+      const int cur = ch & 1;
+      if (ch + 1 < nch) fetch((ch + 1) * kBKC);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 a[MBW], b[NBW];
+#pragma unroll
+        for (int i = 0; i < MBW; ++i) {
+          const int r = wm * MBW * 16 + i * 16;
+          if (AKM)
+            a[i] = tr_operand(sA(cur), LA::kStride, s * 32, r, lane);
+          else
+            a[i] = as_bf16x8(*(const u32x4 *)(sA(cur) + (r + r16) * LA::kStride + s * 32 + kq));
+        }
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const int c = wn * NBW * 16 + j * 16;
+          if (BKM)
+            b[j] = tr_operand(sB(cur), LB::kStride, s * 32, c, lane);
+          else
+            b[j] = as_bf16x8(*(const u32x4 *)(sB(cur) + (c + r16) * LB::kStride + s * 32 + kq));
+        }
+#pragma unroll
+        for (int i = 0; i < MBW; ++i)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+      if (ch + 1 < nch) {
+        la.store(sA(cur ^ 1));
+        lb.store(sB(cur ^ 1));
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: each wave stages one 16-row block at a time as fp32 in its
+  // own LDS region (the operand buffers are free after the last barrier) and
+  // writes whole row pieces ----
+  float *stg = (float *)smem + wave * 16 * kStageStride;
+  constexpr int kPieces = NBW * 2;  // 8-column pieces of a wave's staged row
+  static_assert(16 * kPieces <= 2 * kWave, "a wave's staged block in two passes");
+  float dgrow[MBW][2];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) dgrow[i][0] = dgrow[i][1] = 0.f;
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) stg[((lane / 16) * 4 + v) * kStageStride + j * 16 + r16] = acc[i][j][v];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    const int mrow0 = m0 + wm * MBW * 16 + i * 16;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int c = lane + c2 * kWave;  // 16 rows x kPieces pieces
+      const int rr = c / kPieces, pc = c % kPieces;
+      const int m = mrow0 + rr;
+      const int n = n0 + wn * NBW * 16 + pc * 8;
+      const bool in = c < 16 * kPieces && m < Mt && n < p.Nout;
+      float v[8];
+      if (c < 16 * kPieces) {
+        const f32x4 v0 = *(const f32x4 *)&stg[rr * kStageStride + pc * 8];
+        const f32x4 v1 = *(const f32x4 *)&stg[rr * kStageStride + pc * 8 + 4];
+        v[0] = v0[0]; v[1] = v0[1]; v[2] = v0[2]; v[3] = v0[3];
+        v[4] = v1[0]; v[5] = v1[1]; v[6] = v1[2]; v[7] = v1[3];
+      }
+      if (EPI == kEpiDW) {
+        if (in) {
+          bf16x8 o;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) o[q] = (bf16)v[q];
+          *(u32x4 *)((bf16 *)p.Out + (int64_t)e * p.o_estride + (int64_t)m * p.ldo + n) = as_u32x4(o);
+        }
+      } else if (EPI == kEpiDX) {
+        if (in) {
+          const int64_t t = p.tok[eC + m];
+          float *o = (float *)p.Out + t * p.ldo + n;
+          *(f32x4 *)o = f32x4{v[0], v[1], v[2], v[3]};
+          *(f32x4 *)(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        }
+      } else {  // kEpiDU: du = g z [h > 0], partial <z, h>
+        float dot = 0.f;
+        if (in) {
+          const bf16x8 h = as_bf16x8(*(const u32x4 *)(p.H + (eC + m) * (int64_t)p.Nout + n));
+          const float g = p.gmap[eC + m];
+          bf16x8 o;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float hv = (float)h[q];
+            dot += v[q] * hv;
+            o[q] = (bf16)(hv > 0.f ? g * v[q] : 0.f);
+          }
+          *(u32x4 *)((bf16 *)p.Out + (eC + m) * (int64_t)p.Nout + n) = as_u32x4(o);
+        }
+        // sum the kPieces pieces of each row (consecutive lanes, fixed order)
+#pragma unroll
+        for (int off = 1; off < kPieces; off <<= 1) dot += __shfl_xor(dot, off, kWave);
+        dgrow[i][c2] = dot;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (EPI == kEpiDU) {
+    static_assert(kPieces * 16 <= 2 * kWave && (kPieces & (kPieces - 1)) == 0, "row pieces per lane pair");
+    // per row: this wave's partial, then the WN waves' partials in order
+#pragma unroll
+    for (int i = 0; i < MBW; ++i)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int c = lane + c2 * kWave;
+        if (c < 16 * kPieces && c % kPieces == 0) s_dg[wn][wm * MBW * 16 + i * 16 + c / kPieces] = dgrow[i][c2];
+      }
+    __syncthreads();
+    if (tid < BM) {
+      const int m = m0 + tid;
+      if (m < Mt) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WN; ++w) s += s_dg[w][tid];
+        p.dgpart[(int64_t)p.tok[eC + m] * p.n_tiles + nt] = s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 layers: the same products on the vector ALUs.  64 x 64 output tile,
+// 256 threads with 4 x 4 outputs each, contraction chunks of 16 staged in LDS
+// k-major for both operands (element loads, any layout).
+// ---------------------------------------------------------------------------
+template <bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
+__global__ __launch_bounds__(256) void bwd_gemm_f32_kernel(const BwdArgs<float> p) {
+  constexpr int kT = 64, kKs = 16;
+  constexpr bool kRaggedM = EPI != kEpiDW;
+  __shared__ float sA[kKs][kT + 1], sB[kKs][kT + 1];
+  const int64_t id = blockIdx.x;
+  if (id >= p.ntiles) return;
+  const int e = (int)(id / ((int64_t)p.m_tiles * p.n_tiles));
+  const int rem = (int)(id % ((int64_t)p.m_tiles * p.n_tiles));
+  const int mt = rem / p.n_tiles, nt = rem % p.n_tiles;
+  const int live = min(p.counts[e], p.C);
+  const int m0 = mt * kT, n0 = nt * kT;
+  const int Mt = kRaggedM ? live : p.M;
+  if (m0 >= Mt) return;
+  const int Kt = kRaggedM ? p.K : live;
+  const int64_t eC = (int64_t)e * p.C;
+  const float *Ab = p.A + (AG ? 0 : (int64_t)e * p.a_estride);
+  const float *Bb = p.B + (BG ? 0 : (int64_t)e * p.b_estride);
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  // element (r, k) of an operand; r is a row of the tile, k a contraction index
+  auto elem = [&](const float *base, int ld, bool km, bool g, bool sc, int r, int rlive, int k) -> float {
+    if (km) {
+      if (k >= Kt || r >= rlive) return 0.f;
+      const int64_t row = g ? (int64_t)p.tok[eC + k] : k;
+      const float v = base[row * ld + r];
+      return sc ? p.gmap[eC + k] * v : v;
+    }
+    if (r >= rlive) return 0.f;
+    const int64_t row = g ? (int64_t)p.tok[eC + r] : r;
+    return base[row * ld + k];
+  };
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < Kt; k0 += kKs) {
+    for (int i = tid; i < kKs * kT; i += 256) {
+      const int k = i / kT, r = i % kT;
+      sA[k][r] = elem(Ab, p.lda, AKM, AG, AS, m0 + r, Mt, k0 + k);
+      sB[k][r] = elem(Bb, p.ldb, BKM, BG, false, n0 + r, p.Nout, k0 + k);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kKs; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = sA[k][ty * 4 + i];
+        b[i] = sB[k][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (m >= Mt || n >= p.Nout) continue;
+      const float v = acc[i][j];
+      if (EPI == kEpiDW) {
+        ((float *)p.Out)[(int64_t)e * p.o_estride + (int64_t)m * p.ldo + n] = v;
+      } else if (EPI == kEpiDX) {
+        ((float *)p.Out)[(int64_t)p.tok[eC + m] * p.ldo + n] = v;
+      } else {
+        const float h = p.H[(eC + m) * (int64_t)p.Nout + n];
+        dot += v * h;
+        ((float *)p.Out)[(eC + m) * (int64_t)p.Nout + n] = h > 0.f ? p.gmap[eC + m] * v : 0.f;
+      }
+    }
+    if (EPI == kEpiDU) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) dot += __shfl_xor(dot, off, kWave);
+      if (tx == 0 && m < Mt) p.dgpart[(int64_t)p.tok[eC + m] * p.n_tiles + nt] = dot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+// Tile shapes: rows of an expert (up to 160) x 256 columns for the products
+// with a ragged row count; 128 x 256 for the weight gradients.
+constexpr int kRowMBW = 5, kWgtMBW = 4, kNBWb = 4, kWMb = 2, kWNb = 4;
+constexpr int kBNb = kWNb * kNBWb * 16;
+
+template <typename T_>
+BwdArgs<T_> bwd_args(const BwdLaunch &L, const void *A, int64_t ae, int lda, const void *B, int64_t be, int ldb,
+                     int M, int Nout, int K, void *Out, int64_t oe, int ldo, int bm, int bn) {
+  BwdArgs<T_> a;
+  a.C = L.C;
+  a.counts = L.counts;
+  a.tok = L.tok;
+  a.gmap = L.gmap;
+  a.A = (const T_ *)A;
+  a.a_estride = ae;
+  a.lda = lda;
+  a.B = (const T_ *)B;
+  a.b_estride = be;
+  a.ldb = ldb;
+  a.M = M;
+  a.Nout = Nout;
+  a.K = K;
+  a.Out = Out;
+  a.o_estride = oe;
+  a.ldo = ldo;
+  a.H = (const T_ *)L.hidden;
+  a.dgpart = L.dgpart;
+  a.m_tiles = (int)ceil_div(M, bm);
+  a.n_tiles = (int)ceil_div(Nout, bn);
+  a.ntiles = (int64_t)L.N * a.m_tiles * a.n_tiles;
+  return a;
+}
+
+template <int MBW, bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
+hipError_t run_bf16(const BwdArgs<bf16> &a, hipStream_t st) {
+  if (a.ntiles == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(ceil_div(a.ntiles, 8) * 8);
+  bwd_gemm_bf16_kernel<MBW, kNBWb, kWMb, kWNb, AKM, AG, AS, BKM, BG, EPI>
+      <<<dim3(grid), dim3(kWMb * kWNb * 64), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
+hipError_t run_f32(const BwdArgs<float> &a, hipStream_t st) {
+  if (a.ntiles == 0) return hipSuccess;
+  bwd_gemm_f32_kernel<AKM, AG, AS, BKM, BG, EPI><<<dim3((unsigned)a.ntiles), dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_dz_tiles(int dtype, int dff) { return (int)ceil_div(dff, dtype == kBF16 ? kBNb : 64); }
+
+// The four products, in order: DZ (needs dy, W_out, H), DX (needs DU),
+// DWO (needs dy, H), DWI (needs DU, x).
+hipError_t launch_bwd_experts(const BwdLaunch &L, hipStream_t st, LaunchMarks marks) {
+  auto mark = [&](const char *name) {
+    if (marks.fn) marks.fn(marks.ctx, name);
+  };
+  auto reps = [&]() { return marks.reps ? marks.reps(marks.ctx) : 1; };
+  const int d = L.d, f = L.dff, C = L.C;
+  const int64_t ein = (int64_t)f * d;  // elements of one expert's W_in / W_out
+  const int64_t eh = (int64_t)C * f;   // elements of one expert's H / DU rows
+  hipError_t e = hipSuccess;
+  if (L.C == 0 || L.N == 0) {
+    // no kept rows: the weight gradients are zero, nothing else runs
+  }
+  if (L.dtype == kBF16) {
+    const int bm_rows = kWMb * kRowMBW * 16, bm_w = kWMb * kWgtMBW * 16;
+    // DZ: A = dy rows through tok (k-contiguous), B = W_out,e [d][d_ff] (k-major)
+    auto dz = bwd_args<bf16>(L, L.dy, 0, d, L.w_out, ein, f, C, f, d, L.du, eh, f, bm_rows, kBNb);
+    for (int r = reps(); r > 0 && e == hipSuccess; --r)
+      e = run_bf16<kRowMBW, false, true, false, true, false, kEpiDU>(dz, st);
+    if (e != hipSuccess) return e;
+    mark("bwd_dz");
+    // DX: A = DU,e [rows][d_ff] (k-contiguous), B = W_in,e [d_ff][d] (k-major)
+    auto dx = bwd_args<bf16>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, bm_rows, kBNb);
+    for (int r = reps(); r > 0 && e == hipSuccess; --r)
+      e = run_bf16<kRowMBW, false, false, false, true, false, kEpiDX>(dx, st);
+    if (e != hipSuccess) return e;
+    mark("bwd_dx");
+    // DWO: A = g dy rows through tok (k-major, gate-scaled), B = H,e [rows][d_ff] (k-major)
+    auto dwo = bwd_args<bf16>(L, L.dy, 0, d, L.hidden, eh, f, d, f, 0, L.dw_out, ein, f, bm_w, kBNb);
+    for (int r = reps(); r > 0 && e == hipSuccess; --r)
+      e = run_bf16<kWgtMBW, true, true, true, true, false, kEpiDW>(dwo, st);
+    if (e != hipSuccess) return e;
+    mark("bwd_dw_out");
+    // DWI: A = DU,e [rows][d_ff] (k-major), B = x rows through tok (k-major)
+    auto dwi = bwd_args<bf16>(L, L.du, eh, f, L.x, 0, d, f, d, 0, L.dw_in, ein, d, bm_w, kBNb);
+    for (int r = reps(); r > 0 && e == hipSuccess; --r)
+      e = run_bf16<kWgtMBW, true, false, false, true, true, kEpiDW>(dwi, st);
+    if (e != hipSuccess) return e;
+    mark("bwd_dw_in");
+    return hipSuccess;
+  }
+  auto dz = bwd_args<float>(L, L.dy, 0, d, L.w_out, ein, f, C, f, d, L.du, eh, f, 64, 64);
+  for (int r = reps(); r > 0 && e == hipSuccess; --r) e = run_f32<false, true, false, true, false, kEpiDU>(dz, st);
+  if (e != hipSuccess) return e;
+  mark("bwd_dz");
+  auto dx = bwd_args<float>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, 64, 64);
+  for (int r = reps(); r > 0 && e == hipSuccess; --r) e = run_f32<false, false, false, true, false, kEpiDX>(dx, st);
+  if (e != hipSuccess) return e;
+  mark("bwd_dx");
+  auto dwo = bwd_args<float>(L, L.dy, 0, d, L.hidden, eh, f, d, f, 0, L.dw_out, ein, f, 64, 64);
+  for (int r = reps(); r > 0 && e == hipSuccess; --r) e = run_f32<true, true, true, true, false, kEpiDW>(dwo, st);
+  if (e != hipSuccess) return e;
+  mark("bwd_dw_out");
+  auto dwi = bwd_args<float>(L, L.du, eh, f, L.x, 0, d, f, d, 0, L.dw_in, ein, d, 64, 64);
+  for (int r = reps(); r > 0 && e == hipSuccess; --r) e = run_f32<true, false, false, true, true, kEpiDW>(dwi, st);
+  if (e != hipSuccess) return e;
+  mark("bwd_dw_in");
+  return hipSuccess;
+}
+
+}  // namespace smx

@@ -143,6 +143,55 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_add_norm(const AddNormArgs &a, hipStream_t st);
 int add_norm_max_d(int dtype);  // largest d_model the row-in-registers kernel takes
 
+// ---- backward pass ----
+// Expert products of the backward (backward.hip), all on the forward's saved
+// slot maps and hidden activations.
+struct BwdLaunch {
+  int dtype;
+  int64_t T;
+  int d, dff, N, C;
+  const void *x, *w_in, *w_out, *dy;
+  const int32_t *counts;  // expert_count from the forward
+  const int32_t *tok;     // [N][C] slot -> token (forward workspace)
+  const float *gmap;      // [N][C] slot -> gate (forward workspace)
+  const void *hidden;     // [N][C][dff] H (forward workspace)
+  void *du;               // [N][C][dff] out: g z [H > 0]
+  float *dgpart;          // [T][bwd_dz_tiles] out: partial <z, H> per token
+  float *dxe;             // [T][d] out: W_in^T du for kept tokens (fp32)
+  void *dw_in, *dw_out;   // out: weight gradients, activation dtype
+};
+int bwd_dz_tiles(int dtype, int dff);
+hipError_t launch_bwd_experts(const BwdLaunch &a, hipStream_t st, LaunchMarks marks);
+
+// Router part of the backward (router.hip): recomputes the logits, forms
+// dL/dh (softmax Jacobian of dL/dp = d_aux N f / T + [kept, chosen] dL/dg),
+// writes dh and the whole dx; then dW_r and the bias gradient by a split sum
+// over tokens.
+struct RouterBwdArgs {
+  int dtype;
+  int64_t T;
+  int d, N;
+  const void *x;
+  const float *w_r, *bias;
+  float *logits;  // [T][N] scratch when N > kRouterChunk
+  const int32_t *expert_idx;
+  const uint8_t *dropped;
+  const int32_t *expert_count;
+  const float *dgpart;  // [T][n_dg]
+  int n_dg;
+  float d_aux;
+  const float *dxe;  // [T][d]
+  const void *dy;
+  int add_residual;
+  float *dh;  // [T][N] out
+  void *dx;   // [T][d] out
+  float *dw_r, *dbias;    // out ([N][d], [N] or null)
+  float *wpart, *bpart;   // [S][N][d], [S][N] scratch
+  int splits;
+};
+int router_wgrad_splits(int64_t T, int N, int d);
+hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st, LaunchMarks marks);
+
 __host__ __device__ inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
 // Row stride (elements) of the per-block count and P-partial arrays: rows
 // start on 16-byte boundaries.

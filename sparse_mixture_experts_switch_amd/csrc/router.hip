@@ -26,6 +26,8 @@
 // the same terms as an fp32 dot product.
 // fp32 activations: plain fp32 FMA on the vector ALUs.
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -278,14 +280,14 @@ struct RouterSmem {
   int s_e[kRouterTokens], s_e2[kRouterTokens];
 };
 
-// Router work of block `blk` (tokens [64 blk, 64 blk + 64)).  Starts with a
-// barrier, so consecutive calls by one workgroup may reuse `sm`.
-template <bool kLds, int kK>
-__device__ __forceinline__ void router_block_bf16(
+// Logits (+ bias) of block `blk` (tokens [64 blk, 64 blk + 64)) into LDS
+// (N <= kRouterChunk) or the block's rows of the global scratch; returns
+// after a barrier with the logits complete.  Starts with a barrier, so
+// consecutive calls by one workgroup may reuse `sm`.
+template <bool kLds>
+__device__ __forceinline__ LogitRows<kLds> router_contract_bf16(
     const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
-    int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
-    float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
-    float *__restrict__ ppart, int64_t blk, RouterSmem &sm) {
+    int64_t T, int d, int N, float *__restrict__ logits_g, int64_t blk, RouterSmem &sm) {
   static_assert(kRBThreads == 8 * kWave && kStageThreads == 4 * kWave && kRouterChunk == 128,
                 "4 MFMA waves x 32 experts + 4 staging waves");
   static_assert(kXPer * kStageThreads == kRouterTokens * (kRKC / 8), "x pieces");
@@ -423,6 +425,19 @@ __device__ __forceinline__ void router_block_bf16(
     if (kLds) break;  // N <= kRouterChunk: one chunk holds every expert
   }
   __syncthreads();
+  return lg;
+}
+
+// Router work of block `blk`: logits, then the forward epilogue.
+template <bool kLds, int kK>
+__device__ __forceinline__ void router_block_bf16(
+    const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
+    int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
+    float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
+    float *__restrict__ ppart, int64_t blk, RouterSmem &sm) {
+  const LogitRows<kLds> lg = router_contract_bf16<kLds>(x, w_r, bias, T, d, N, logits_g, blk, sm);
+  const int64_t t0 = blk * kRouterTokens;
+  const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
   router_epilogue<kRBThreads, kLds, kK>(lg, nt, N, t0, blk, TopK{T, router_blocks(T)}, expert_idx, gate, slot_rank,
                                         bcount, ppart, sm.s_max, sm.s_inv, sm.s_e, sm.s_e2);
 }
@@ -442,23 +457,16 @@ __global__ __launch_bounds__(kRBThreads) void router_bf16_kernel(
 // fp32 activations: fp32 FMA.  The block's x rows are staged in LDS in
 // k-slices; each thread owns (token, expert) pairs of the current chunk.
 // ---------------------------------------------------------------------------
-template <bool kLds, int kK>
-__global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
-    const float *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
-    int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
-    float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
-    float *__restrict__ ppart) {
+// fp32 logits (+ bias) of block `blk` into `lg` (LDS rows s_lg when
+// N <= kRouterChunk, else the global scratch); ends with a barrier.
+template <bool kLds>
+__device__ __forceinline__ LogitRows<kLds> router_contract_f32(
+    const float *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias, int64_t T, int d,
+    int N, float *__restrict__ logits_g, int64_t blk, float *s_lg, float (*s_x)[65]) {
   constexpr int kKc = 64;  // contraction columns per LDS slice
-  __shared__ float s_lg[kLds ? kRouterTokens * (kRouterChunk + 1) : 1];
-  __shared__ float s_x[kRouterTokens][kKc + 1];
-  __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
-  __shared__ int s_e[kRouterTokens], s_e2[kRouterTokens];
-
-  const int64_t blk = blockIdx.x;
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
   const int tid = threadIdx.x;
-
   LogitRows<kLds> lg;
   if (kLds) {
     lg.base = s_lg;
@@ -471,7 +479,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
   for (int c0 = 0; c0 < N; c0 += kRouterChunk) {
     float acc[kPer];
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) acc[p] = 0.f;
+    for (int q = 0; q < kPer; ++q) acc[q] = 0.f;
     for (int k0 = 0; k0 < d; k0 += kKc) {
       __syncthreads();
       for (int i = tid; i < kRouterTokens * kKc; i += kRouterThreads) {
@@ -480,29 +488,262 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
       }
       __syncthreads();
 #pragma unroll
-      for (int p = 0; p < kPer; ++p) {
-        const int pair = tid + p * kRouterThreads;
+      for (int q = 0; q < kPer; ++q) {
+        const int pair = tid + q * kRouterThreads;
         const int t = pair / kRouterChunk, j = c0 + pair % kRouterChunk;
         if (j < N) {
           const float *w = w_r + (int64_t)j * d + k0;
           const int kn = min(kKc, d - k0);
-          float a = acc[p];
+          float a = acc[q];
           for (int k = 0; k < kn; ++k) a = __builtin_fmaf(s_x[t][k], w[k], a);
-          acc[p] = a;
+          acc[q] = a;
         }
       }
     }
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int pair = tid + p * kRouterThreads;
+    for (int q = 0; q < kPer; ++q) {
+      const int pair = tid + q * kRouterThreads;
       const int t = pair / kRouterChunk, j = c0 + pair % kRouterChunk;
-      if (j < N && t < nt) lg.at(t, kLds ? j - c0 : j) = acc[p] + (bias ? bias[j] : 0.f);
+      if (j < N && t < nt) lg.at(t, kLds ? j - c0 : j) = acc[q] + (bias ? bias[j] : 0.f);
     }
     if (kLds) break;
   }
   __syncthreads();
+  return lg;
+}
+
+template <bool kLds, int kK>
+__global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
+    const float *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
+    int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
+    float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
+    float *__restrict__ ppart) {
+  __shared__ float s_lg[kLds ? kRouterTokens * (kRouterChunk + 1) : 1];
+  __shared__ float s_x[kRouterTokens][65];
+  __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
+  __shared__ int s_e[kRouterTokens], s_e2[kRouterTokens];
+  const int64_t blk = blockIdx.x;
+  const int64_t t0 = blk * kRouterTokens;
+  const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
+  const LogitRows<kLds> lg = router_contract_f32<kLds>(x, w_r, bias, T, d, N, logits_g, blk, s_lg, s_x);
   router_epilogue<kRouterThreads, kLds, kK>(lg, nt, N, t0, blk, TopK{T, router_blocks(T)}, expert_idx, gate,
                                             slot_rank, bcount, ppart, s_max, s_inv, s_e, s_e2);
+}
+
+// ---------------------------------------------------------------------------
+// Backward ("Switch Routing": the gate keeps the router differentiable; "The
+// Load-Balancing Loss": f_i is a hard count without gradient, P_i carries the
+// loss's gradient).  One router block per workgroup: the block's logits are
+// recomputed exactly as in the forward, then per token
+//   dL/dp_j = d_aux N count_j / T^2 + [j = e_t, t kept] dL/dg_t
+//   dL/dh_j = p_j (dL/dp_j - sum_i dL/dp_i p_i)
+// (dL/dg_t = sum of the expert backward's partial dots <z, H> of token t, in
+// a fixed order), written to dh [T][N]; then
+//   dx_t = W_r^T dL/dh_t + (W_in^T du)_t (kept t) + dy_t (residual)
+// in fp32, one rounding.
+// ---------------------------------------------------------------------------
+template <typename T_, int kThreads, bool kLds>
+__device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0, const RouterBwdArgs &a) {
+  constexpr int kLpt = kThreads / kRouterTokens;  // lanes per token
+  const int N = a.N, d = a.d;
+  const int tid = threadIdx.x, t = tid / kLpt, q = tid % kLpt;
+  const float caux = a.d_aux * (float)N / ((float)a.T * (float)a.T);
+  if (t < nt) {
+    const int64_t tt = t0 + t;
+    float mx = -INFINITY;
+    for (int j = q; j < N; j += kLpt) mx = fmaxf(mx, lg.at(t, j));
+#pragma unroll
+    for (int off = 1; off < kLpt; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    float sum = 0.f;
+    for (int j = q; j < N; j += kLpt) sum += __expf(lg.at(t, j) - mx);
+#pragma unroll
+    for (int off = 1; off < kLpt; off <<= 1) sum += __shfl_xor(sum, off, kWave);
+    const float inv = 1.0f / sum;
+    const int e = a.expert_idx[tt];
+    float dg = 0.f;
+    if (!a.dropped[tt])
+      for (int i = 0; i < a.n_dg; ++i) dg += a.dgpart[tt * a.n_dg + i];
+    float sdp = 0.f;
+    for (int j = q; j < N; j += kLpt) {
+      const float pj = __expf(lg.at(t, j) - mx) * inv;
+      const float dp = caux * (float)a.expert_count[j] + (j == e ? dg : 0.f);
+      lg.at(t, j) = pj;
+      sdp += dp * pj;
+    }
+#pragma unroll
+    for (int off = 1; off < kLpt; off <<= 1) sdp += __shfl_xor(sdp, off, kWave);
+    for (int j = q; j < N; j += kLpt) {
+      const float pj = lg.at(t, j);
+      const float dp = caux * (float)a.expert_count[j] + (j == e ? dg : 0.f);
+      const float dh = pj * (dp - sdp);
+      lg.at(t, j) = dh;
+      a.dh[tt * N + j] = dh;
+    }
+  }
+  __syncthreads();
+  // dx: wave w owns tokens w, w + W, ...; lane = column within a 64-column chunk
+  constexpr int kW = kThreads / kWave, kTpw = kRouterTokens / kW;
+  const int lane = tid % kWave, w = tid / kWave;
+  const T_ *dy = (const T_ *)a.dy;
+  T_ *dx = (T_ *)a.dx;
+  for (int c0 = 0; c0 < d; c0 += kWave) {
+    const int k = c0 + lane;
+    float acc[kTpw];
+#pragma unroll
+    for (int u = 0; u < kTpw; ++u) acc[u] = 0.f;
+    for (int j = 0; j < N; ++j) {
+      const float wv = a.w_r[(int64_t)j * d + k];
+#pragma unroll
+      for (int u = 0; u < kTpw; ++u) acc[u] = __builtin_fmaf(lg.at(min(w + u * kW, nt - 1), j), wv, acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kTpw; ++u) {
+      const int tl = w + u * kW;
+      if (tl >= nt) continue;
+      const int64_t tt = t0 + tl;
+      float v = acc[u];
+      if (!a.dropped[tt]) v += a.dxe[tt * d + k];
+      if (a.add_residual) v += to_f32(dy[tt * d + k]);
+      dx[tt * d + k] = from_f32<T_>(v);
+    }
+  }
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kRBThreads) void router_bwd_bf16_kernel(const RouterBwdArgs a) {
+  __shared__ RouterSmem sm;
+  const int64_t blk = blockIdx.x, t0 = blk * kRouterTokens;
+  const int nt = (int)min<int64_t>(kRouterTokens, a.T - t0);
+  const LogitRows<kLds> lg =
+      router_contract_bf16<kLds>((const bf16 *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, sm);
+  router_bwd_epilogue<bf16, kRBThreads, kLds>(lg, nt, t0, a);
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kRouterThreads) void router_bwd_f32_kernel(const RouterBwdArgs a) {
+  __shared__ float s_lg[kLds ? kRouterTokens * (kRouterChunk + 1) : 1];
+  __shared__ float s_x[kRouterTokens][65];
+  const int64_t blk = blockIdx.x, t0 = blk * kRouterTokens;
+  const int nt = (int)min<int64_t>(kRouterTokens, a.T - t0);
+  const LogitRows<kLds> lg =
+      router_contract_f32<kLds>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, s_lg, s_x);
+  router_bwd_epilogue<float, kRouterThreads, kLds>(lg, nt, t0, a);
+}
+
+// dW_r = sum_t dh_t x_t^T and dbias = sum_t dh_t: workgroup (j tile, k tile,
+// split s) sums tokens [s ts, (s + 1) ts) for a 64 x 64 tile of dW_r (4 x 4
+// per thread, token chunks of 16 through LDS); the k-tile-0 workgroups also
+// sum dh for the bias.  fp32 throughout; the splits are added in order by
+// router_wgrad_sum_kernel.
+template <typename T_>
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restrict__ dh, const T_ *__restrict__ x,
+                                                           int64_t T, int N, int d, int64_t ts,
+                                                           float *__restrict__ wpart, float *__restrict__ bpart) {
+  __shared__ float sD[16][65], sX[16][65];
+  const int j0 = blockIdx.x * 64, k0 = blockIdx.y * 64, sp = blockIdx.z;
+  const int64_t ta = min<int64_t>(T, (int64_t)sp * ts), tb = min<int64_t>(T, ta + ts);
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  float bacc = 0.f;
+  for (int64_t c = ta; c < tb; c += 16) {
+    for (int i = tid; i < 16 * 64; i += 256) {
+      const int r = i / 64, col = i % 64;
+      const int64_t t = c + r;
+      sD[r][col] = (t < tb && j0 + col < N) ? dh[t * N + j0 + col] : 0.f;
+      sX[r][col] = t < tb ? to_f32(x[t * d + k0 + col]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = sD[k][ty * 4 + i];
+        bv[i] = sX[k][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+    }
+    if (blockIdx.y == 0 && tid < 64) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) bacc += sD[k][tid];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = j0 + ty * 4 + i;
+    if (j >= N) continue;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wpart[((int64_t)sp * N + j) * d + k0 + tx * 4 + jj] = acc[i][jj];
+  }
+  if (blockIdx.y == 0 && tid < 64 && j0 + tid < N) bpart[(int64_t)sp * N + j0 + tid] = bacc;
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float *__restrict__ wpart,
+                                                               const float *__restrict__ bpart, int N, int d,
+                                                               int splits, float *__restrict__ dw_r,
+                                                               float *__restrict__ dbias) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nd = (int64_t)N * d;
+  if (i < nd) {
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += wpart[(int64_t)sp * nd + i];
+    dw_r[i] = s;
+  }
+  if (dbias && i < N) {
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += bpart[(int64_t)sp * N + i];
+    dbias[i] = s;
+  }
+}
+
+int router_wgrad_splits(int64_t T, int N, int d) {
+  const int64_t tiles = ceil_div(N, 64) * (d / 64);
+  int64_t s = ceil_div(512, tiles);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(T, 256)));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
+
+hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st, LaunchMarks marks) {
+  auto mark = [&](const char *name) {
+    if (marks.fn) marks.fn(marks.ctx, name);
+  };
+  auto reps = [&]() { return marks.reps ? marks.reps(marks.ctx) : 1; };
+  const int64_t nb = router_blocks(a.T);
+  const bool lds = a.N <= kRouterChunk;
+  for (int r = reps(); r > 0 && nb > 0; --r) {
+    if (a.dtype == kBF16)
+      (lds ? router_bwd_bf16_kernel<true> : router_bwd_bf16_kernel<false>)<<<dim3((unsigned)nb), dim3(kRBThreads), 0,
+                                                                              st>>>(a);
+    else
+      (lds ? router_bwd_f32_kernel<true> : router_bwd_f32_kernel<false>)<<<dim3((unsigned)nb), dim3(kRouterThreads),
+                                                                            0, st>>>(a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  mark("bwd_router");
+  const int64_t ts = ceil_div(ceil_div(a.T, a.splits), 16) * 16;
+  const dim3 g((unsigned)ceil_div(a.N, 64), (unsigned)(a.d / 64), (unsigned)a.splits);
+  for (int r = reps(); r > 0; --r) {
+    if (a.dtype == kBF16)
+      router_wgrad_kernel<bf16><<<g, dim3(256), 0, st>>>(a.dh, (const bf16 *)a.x, a.T, a.N, a.d, ts, a.wpart,
+                                                         a.bpart);
+    else
+      router_wgrad_kernel<float><<<g, dim3(256), 0, st>>>(a.dh, (const float *)a.x, a.T, a.N, a.d, ts, a.wpart,
+                                                          a.bpart);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mark("bwd_router_w");
+  const int64_t nd = (int64_t)a.N * a.d;
+  for (int r = reps(); r > 0; --r)
+    router_wgrad_sum_kernel<<<dim3((unsigned)ceil_div(std::max<int64_t>(nd, a.N), 256)), dim3(256), 0, st>>>(
+        a.wpart, a.bpart, a.N, a.d, a.splits, a.dw_r, a.dbias);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mark("bwd_router_w_sum");
+  return hipSuccess;
 }
 
 template <int kK>

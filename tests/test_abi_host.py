@@ -185,3 +185,31 @@ def test_topk_validation_and_workspace():
     rc = lib.switch_topk_layer_forward(ctypes.byref(small), 2, good, good, None, good, good, 0, good, good, good,
                                        good, good, good, good, good, 64, None)
     assert rc == B.SWITCH_E_WORKSPACE
+
+
+def test_backward_rejects_before_launch():
+    """switch_layer_backward validates on the host (through the binding's
+    argument types): NULL forward workspace, a forward workspace smaller than
+    the forward's, a non-finite d_aux, misaligned dx, a short workspace."""
+    import torch
+    lib = smx.load_library()
+    s = B.make_shape(64, 128, 256, 8, 16, torch.bfloat16)
+    P = ctypes.c_void_p
+    good, odd = P(1 << 20), P((1 << 20) + 2)
+    fwd_need = smx.workspace_bytes(s)
+    bwd_need = smx.backward_workspace_bytes(s)
+    assert bwd_need > 0
+
+    def call(fwd_ws=good, fwd_bytes=fwd_need, d_aux=0.5, dx=good, ws_bytes=bwd_need):
+        return lib.switch_layer_backward(ctypes.byref(s), good, good, None, good, good, 0, good, good, good, fwd_ws,
+                                         fwd_bytes, good, d_aux, dx, good, None, good, good, good, ws_bytes, None)
+
+    assert call(fwd_ws=None) == B.SWITCH_E_INVALID
+    assert call(fwd_bytes=fwd_need - 1) == B.SWITCH_E_WORKSPACE
+    assert call(d_aux=float("nan")) == B.SWITCH_E_INVALID
+    assert call(dx=odd) == B.SWITCH_E_INVALID
+    assert call(ws_bytes=bwd_need - 1) == B.SWITCH_E_WORKSPACE
+    rc = lib.switch_layer_backward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good, good,
+                                            fwd_need, good, 0.5, good, good, None, good, good, good, bwd_need, None,
+                                            2, 1, 1)
+    assert rc == B.SWITCH_E_INVALID
