@@ -159,6 +159,79 @@ def cpu_baseline(inp, C: int, min_seconds: float = 10.0) -> dict:
             "stages_s": {k: round(v, 4) for k, v in st.items()}}
 
 
+def backward_alg_bytes(T: int, d: int, f: int, N: int, C: int, counts, splits: int) -> dict:
+    """Algorithmic HBM bytes of each backward kernel: every input byte once and
+    every output byte once, padding rows excluded.  R = kept rows, Ea = experts
+    with a kept row (their weights are read), n_dg = partial dots per token."""
+    R = sum(min(int(c), C) for c in counts)
+    Ea = sum(1 for c in counts if min(int(c), C) > 0)
+    n_dg = (f + 255) // 256
+    return {
+        "bwd_dz": Ea * d * f * 2 + R * d * 2 + R * f * 2 + R * f * 2 + R * n_dg * 4 + R * 8,
+        "bwd_dx": Ea * f * d * 2 + R * f * 2 + R * d * 4 + R * 4,
+        "bwd_dw_out": R * d * 2 + R * f * 2 + R * 8 + N * d * f * 2,
+        "bwd_dw_in": R * f * 2 + R * d * 2 + R * 4 + N * f * d * 2,
+        "bwd_router": T * d * 2 + N * d * 4 + R * n_dg * 4 + R * d * 4 + T * 9 + N * 4 + T * N * 4 + T * d * 2,
+        "bwd_router_w": T * N * 4 + T * d * 2 + splits * (N * d + N) * 4,
+        "bwd_router_w_sum": splits * (N * d + N) * 4 + (N * d + N) * 4,
+    }
+
+
+def backward_bench(smx, torch, inp, out, ws, C, cfg, stream, steps: int) -> dict:
+    T, d, f, N = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts
+    dev = inp["x"].device
+    shape = smx.binding.make_shape(T, d, f, N, C, cfg.torch_dtype)
+    bws = torch.empty(smx.backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    g = torch.Generator().manual_seed(5)
+    dy = torch.randn(T, d, generator=g).to(cfg.torch_dtype).to(dev)
+    grads = {}
+    args = (inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C, out, ws, dy, 0.01)
+    call = lambda: smx.layer_backward(*args, workspace=bws, out=grads)  # noqa: E731
+    with torch.cuda.stream(stream):
+        call()
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < MIN_WARMUP_S:
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        names = smx.BACKWARD_KERNELS
+        part = lambda lo, hi: smx.layer_backward_profiled(*args, first_kernel=lo, last_kernel=hi,  # noqa: E731
+                                                          workspace=bws, out=grads)
+        kern = {}
+        for i, name in enumerate(names):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                if i > 0:
+                    part(0, i - 1)
+                e0.record(stream)
+                part(i, i)
+                e1.record(stream)
+                if i < len(names) - 1:
+                    part(i + 1, len(names) - 1)
+            torch.cuda.synchronize()
+            kern[name] = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    counts = out["expert_count"].cpu().tolist()
+    splits = max(1, min(64, -(-512 // ((-(-N // 64)) * (d // 64)))))
+    splits = min(splits, max(1, -(-T // 256)))
+    alg = backward_alg_bytes(T, d, f, N, C, counts, splits)
+    kept = sum(min(int(c), C) for c in counts)
+    flops = 2 * 4 * kept * d * f  # dz, dx, dW_out, dW_in: 2 kept d f each
+    return {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "expert_tflop_per_s": round(flops / (sum(kern[k] for k in names[:4]) * 1e-3) / 1e12, 1),
+            "kernels": {k: {"ms": round(v, 5), "alg_bytes": alg[k],
+                            "GBps": round(alg[k] / (v * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(alg[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                        for k, v in kern.items()}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,6 +383,12 @@ def main() -> int:
             "ffn_tflop_per_s_whole_call": round(4.0 * kept2 * d * f / (ms2 * 1e-3) / 1e12, 1)}
     log(f"bench: top-2 layer {ms2:.4f} ms ({T / (ms2 * 1e-3) / 1e6:.2f} Mtok/s)")
     del ws2, out2
+    # backward pass of the same step (switch_layer_backward on the forward's
+    # routing and saved workspace; dy ~ N(0, 1), d_aux = 0.01): whole-call
+    # time, then each kernel bracketed by events as for the forward
+    bwd = backward_bench(smx, torch, inp, out, ws, C, cfg, stream, args.steps)
+    log("bench: backward " + f"{bwd['ms']:.4f} ms; per-kernel ms " +
+        ", ".join(f"{k}={v['ms']:.4f}" for k, v in bwd["kernels"].items()))
     per_kernel = {}
     for k, v in kern.items():
         b = algorithmic_bytes(k, T, d, f, N, C, counts)
@@ -353,6 +432,7 @@ def main() -> int:
         "kernels": per_kernel,
         "stage_kernels": stage_kernels,
         "top2": top2,
+        "backward": bwd,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.calib_copy:

@@ -307,10 +307,11 @@ int bwd_layout(const switch_shape *s, BwdLayout &B) {
   const int64_t T = s->tokens, N = s->num_experts, C = s->capacity, d = s->d_model, f = s->d_ff;
   const int es = esize(s->dtype);
   B.n_dg = bwd_dz_tiles(s->dtype, (int)f);
-  B.splits = router_wgrad_splits(T, (int)N, (int)d);
+  B.splits = router_wgrad_split(T, (int)N, (int)d).splits;
   size_t du, dg, dxe, dh, lg = 0, wp, bp;
   bool ok = mul(du, {N, C, f, es}) && mul(dg, {T, B.n_dg, 4}) && mul(dxe, {T, d, 4}) && mul(dh, {T, N, 4}) &&
-            (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(wp, {B.splits, N, d, 4}) && mul(bp, {B.splits, N, 4});
+            (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(wp, {B.splits, N, d, 4}) &&
+            mul(bp, {router_blocks(T), N, 4});
   if (!ok) return fail(SWITCH_E_UNSUPPORTED, "backward buffer sizes overflow for this shape");
   size_t o = 0;
   B.du = o;
@@ -378,7 +379,7 @@ int layer_backward(const switch_shape *s, const void *x, const float *w_router, 
   RouterBwdArgs ra{s->dtype, s->tokens, s->d_model, s->num_experts, x, w_router, router_bias,
                    (float *)(w + B.logits), expert_idx, dropped, expert_count, (const float *)(w + B.dgpart),
                    B.n_dg, d_aux, (const float *)(w + B.dxe), dy, add_residual ? 1 : 0, (float *)(w + B.dh), dx,
-                   dw_router, d_router_bias, (float *)(w + B.wpart), (float *)(w + B.bpart), B.splits};
+                   dw_router, d_router_bias, (float *)(w + B.wpart), (float *)(w + B.bpart)};
   if ((e = launch_router_bwd(ra, st, marks)) != hipSuccess) return hip_fail(e, "backward router launch");
   return SWITCH_OK;
 }

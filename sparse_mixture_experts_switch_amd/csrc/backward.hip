@@ -439,6 +439,117 @@ __global__ __launch_bounds__(256) void bwd_gemm_f32_kernel(const BwdArgs<float> 
 }
 
 // ---------------------------------------------------------------------------
+// Router weight gradient dW_r = sum_t dL/dh_t x_t^T on bf16 MFMA, fp32-exact
+// products ("Making Sparse Training Stable": the router stays in fp32): dL/dh
+// (fp32) is split while staging into three bf16 planes hi + mid + lo that sum
+// to it exactly, x is bf16, so each plane product is exact in fp32 and the
+// accumulation sees the terms of an fp32 dot product.  Workgroup (64 experts,
+// 128 columns, token range [s ts, (s + 1) ts)) writes its partial sum; both
+// operands are k-major (token = contraction) and read with the LDS transpose
+// load.  4 waves, each 32 experts x 64 columns.
+// ---------------------------------------------------------------------------
+constexpr int kWgJ = 64, kWgK = 128, kWgT = 64;
+
+__device__ __forceinline__ void split3(float w, bf16 &hi, bf16 &mid, bf16 &lo) {
+  hi = (bf16)w;
+  const float r = w - (float)hi;  // exact
+  mid = (bf16)r;
+  lo = (bf16)(r - (float)mid);  // exact, and representable in bf16
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_bf16_kernel(const float *__restrict__ dh,
+                                                                const bf16 *__restrict__ x, int64_t T, int N, int d,
+                                                                int64_t ts, float *__restrict__ wpart) {
+  constexpr int kSA = kWgJ + 8, kSB = kWgK + 8;
+  __shared__ __attribute__((aligned(16))) bf16 sA[3 * kWgT * kSA];
+  __shared__ __attribute__((aligned(16))) bf16 sB[kWgT * kSB];
+  const int j0 = blockIdx.x * kWgJ, k0 = blockIdx.y * kWgK, sp = blockIdx.z;
+  const int64_t ta = min<int64_t>(T, (int64_t)sp * ts), tb = min<int64_t>(T, ta + ts);
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wj = wave / 2, wk = wave % 2;
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // staging: dh chunk 64 tokens x 64 experts (pieces of 4 fp32), x chunk 64
+  // tokens x 128 columns (pieces of 8 bf16); 4 pieces of each per thread
+  float rA[4][4];
+  u32x4 rB[4];
+  auto fetch = [&](int64_t c) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pc = tid + q * 256, t = pc / 16;
+      const int64_t tt = c + t;
+      const int jc = (pc % 16) * 4, kc = (pc % 16) * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rA[q][e] = (tt < tb && j0 + jc + e < N) ? dh[tt * N + j0 + jc + e] : 0.f;
+      rB[q] = (tt < tb && k0 + kc < d) ? *(const u32x4 *)(x + tt * d + k0 + kc) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pc = tid + q * 256, t = pc / 16;
+      const int jc = (pc % 16) * 4, kc = (pc % 16) * 8;
+      bf16 h[4], m[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split3(rA[q][e], h[e], m[e], l[e]);
+      bf16 *a = sA + t * kSA + jc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = h[e];
+        a[kWgT * kSA + e] = m[e];
+        a[2 * kWgT * kSA + e] = l[e];
+      }
+      *(u32x4 *)(sB + t * kSB + kc) = rB[q];
+    }
+  };
+  if (ta < tb) fetch(ta);
+  for (int64_t c = ta; c < tb; c += kWgT) {
+    __syncthreads();  // the previous chunk's readers are done
+    store();
+    __syncthreads();
+    if (c + kWgT < tb) fetch(c + kWgT);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 a[2][3], b[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) a[i][pl] = tr_operand(sA + pl * kWgT * kSA, kSA, s2 * 32, wj * 32 + i * 16, lane);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) b[jb] = tr_operand(sB, kSB, s2 * 32, wk * 64 + jb * 16, lane);
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb)
+            acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][pl], b[jb], acc[i][jb], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const int k = k0 + wk * 64 + jb * 16 + lane % 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + wj * 32 + i * 16 + (lane / 16) * 4 + r;
+        if (j < N && k < d) wpart[((int64_t)sp * N + j) * d + k] = acc[i][jb][r];
+      }
+    }
+}
+
+hipError_t launch_router_wgrad_bf16(const float *dh, const void *x, int64_t T, int N, int d, WgradSplit sp,
+                                    float *wpart, hipStream_t st) {
+  const dim3 g((unsigned)ceil_div(N, kWgJ), (unsigned)ceil_div(d, kWgK), (unsigned)sp.splits);
+  router_wgrad_bf16_kernel<<<g, dim3(256), 0, st>>>(dh, (const bf16 *)x, T, N, d, sp.ts, wpart);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 namespace {

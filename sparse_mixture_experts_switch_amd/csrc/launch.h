@@ -186,11 +186,20 @@ struct RouterBwdArgs {
   float *dh;  // [T][N] out
   void *dx;   // [T][d] out
   float *dw_r, *dbias;    // out ([N][d], [N] or null)
-  float *wpart, *bpart;   // [S][N][d], [S][N] scratch
-  int splits;
+  float *wpart;           // [splits][N][d] scratch: dW_r partial sums
+  float *bpart;           // [router blocks][N] scratch: bias partial sums
 };
-int router_wgrad_splits(int64_t T, int N, int d);
+// Token split of the dW_r sum: `splits` ranges of `ts` tokens (a multiple of 64).
+struct WgradSplit {
+  int splits;
+  int64_t ts;
+};
+WgradSplit router_wgrad_split(int64_t T, int N, int d);
 hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st, LaunchMarks marks);
+// dW_r partial sums on bf16 MFMA (backward.hip): dh split exactly into three
+// bf16 planes, x bf16, so every product is exact and accumulates in fp32.
+hipError_t launch_router_wgrad_bf16(const float *dh, const void *x, int64_t T, int N, int d, WgradSplit sp,
+                                    float *wpart, hipStream_t st);
 
 __host__ __device__ inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
 // Row stride (elements) of the per-block count and P-partial arrays: rows

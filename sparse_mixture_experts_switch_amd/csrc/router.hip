@@ -542,12 +542,30 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
 //   dx_t = W_r^T dL/dh_t + (W_in^T du)_t (kept t) + dy_t (residual)
 // in fp32, one rounding.
 // ---------------------------------------------------------------------------
+// LDS of the backward epilogue beyond the logit rows: the loss term of dL/dp
+// per expert, and per wave a group of kBwdWrCols columns of W_r rows for the
+// dx product.
+constexpr int kBwdWrCols = 8;
+template <int kThreads>
+constexpr int bwd_lds_floats() {
+  return kRouterChunk + (kThreads / kWave) * kRouterChunk * kBwdWrCols;
+}
+
 template <typename T_, int kThreads, bool kLds>
-__device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0, const RouterBwdArgs &a) {
+__device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0, const RouterBwdArgs &a,
+                                    float *s_extra) {
   constexpr int kLpt = kThreads / kRouterTokens;  // lanes per token
+  constexpr int kW = kThreads / kWave;
   const int N = a.N, d = a.d;
   const int tid = threadIdx.x, t = tid / kLpt, q = tid % kLpt;
   const float caux = a.d_aux * (float)N / ((float)a.T * (float)a.T);
+  float *s_aux = s_extra;                // [kRouterChunk] (N <= kRouterChunk)
+  float *s_wr = s_extra + kRouterChunk;  // [kW][kRouterChunk][kBwdWrCols]
+  if (kLds) {
+    for (int j = tid; j < N; j += kThreads) s_aux[j] = caux * (float)a.expert_count[j];
+    __syncthreads();
+  }
+  auto aux = [&](int j) { return kLds ? s_aux[j] : caux * (float)a.expert_count[j]; };
   if (t < nt) {
     const int64_t tt = t0 + t;
     float mx = -INFINITY;
@@ -560,13 +578,17 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
     for (int off = 1; off < kLpt; off <<= 1) sum += __shfl_xor(sum, off, kWave);
     const float inv = 1.0f / sum;
     const int e = a.expert_idx[tt];
+    // dL/dg: the token's partial dots, lane q taking q, q + kLpt, ..., then
+    // butterfly steps (the same bits on every lane of the token)
     float dg = 0.f;
     if (!a.dropped[tt])
-      for (int i = 0; i < a.n_dg; ++i) dg += a.dgpart[tt * a.n_dg + i];
+      for (int i = q; i < a.n_dg; i += kLpt) dg += a.dgpart[tt * a.n_dg + i];
+#pragma unroll
+    for (int off = 1; off < kLpt; off <<= 1) dg += __shfl_xor(dg, off, kWave);
     float sdp = 0.f;
     for (int j = q; j < N; j += kLpt) {
       const float pj = __expf(lg.at(t, j) - mx) * inv;
-      const float dp = caux * (float)a.expert_count[j] + (j == e ? dg : 0.f);
+      const float dp = aux(j) + (j == e ? dg : 0.f);
       lg.at(t, j) = pj;
       sdp += dp * pj;
     }
@@ -574,37 +596,70 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
     for (int off = 1; off < kLpt; off <<= 1) sdp += __shfl_xor(sdp, off, kWave);
     for (int j = q; j < N; j += kLpt) {
       const float pj = lg.at(t, j);
-      const float dp = caux * (float)a.expert_count[j] + (j == e ? dg : 0.f);
+      const float dp = aux(j) + (j == e ? dg : 0.f);
       const float dh = pj * (dp - sdp);
       lg.at(t, j) = dh;
       a.dh[tt * N + j] = dh;
     }
   }
   __syncthreads();
-  // dx: wave w owns tokens w, w + W, ...; lane = column within a 64-column chunk
-  constexpr int kW = kThreads / kWave, kTpw = kRouterTokens / kW;
-  const int lane = tid % kWave, w = tid / kWave;
+  // bias partial of the block: sum over its tokens of dL/dh, in token order
+  for (int j = tid; j < N; j += kThreads) {
+    float b = 0.f;
+    for (int u = 0; u < nt; ++u) b += lg.at(u, j);
+    a.bpart[(t0 / kRouterTokens) * N + j] = b;
+  }
+  // dx: lane = token of the block; wave w takes the column groups w, w + W,
+  // ... of kBwdWrCols columns.  With the logits in LDS the wave first copies
+  // its group's W_r rows to its own LDS region (each lane then reads them as
+  // broadcasts); otherwise the W_r values come straight from memory.
+  const int lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int tl = min(lane, nt - 1);
+  const int64_t tt = t0 + tl;
+  const bool live = lane < nt;
+  const bool kept = live && !a.dropped[tt];
   const T_ *dy = (const T_ *)a.dy;
   T_ *dx = (T_ *)a.dx;
-  for (int c0 = 0; c0 < d; c0 += kWave) {
-    const int k = c0 + lane;
-    float acc[kTpw];
-#pragma unroll
-    for (int u = 0; u < kTpw; ++u) acc[u] = 0.f;
-    for (int j = 0; j < N; ++j) {
-      const float wv = a.w_r[(int64_t)j * d + k];
-#pragma unroll
-      for (int u = 0; u < kTpw; ++u) acc[u] = __builtin_fmaf(lg.at(min(w + u * kW, nt - 1), j), wv, acc[u]);
+  float *wr = s_wr + w * kRouterChunk * kBwdWrCols;
+  for (int c0 = w * kBwdWrCols; c0 < d; c0 += kW * kBwdWrCols) {
+    if (kLds) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the previous group's reads are done
+      __builtin_amdgcn_wave_barrier();
+      for (int j = lane; j < N; j += kWave) {
+        const float *src = a.w_r + (int64_t)j * d + c0;
+        *(f32x4 *)(wr + j * kBwdWrCols) = *(const f32x4 *)src;
+        *(f32x4 *)(wr + j * kBwdWrCols + 4) = *(const f32x4 *)(src + 4);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
     }
+    float acc[kBwdWrCols];
 #pragma unroll
-    for (int u = 0; u < kTpw; ++u) {
-      const int tl = w + u * kW;
-      if (tl >= nt) continue;
-      const int64_t tt = t0 + tl;
-      float v = acc[u];
-      if (!a.dropped[tt]) v += a.dxe[tt * d + k];
-      if (a.add_residual) v += to_f32(dy[tt * d + k]);
-      dx[tt * d + k] = from_f32<T_>(v);
+    for (int i = 0; i < kBwdWrCols; ++i) acc[i] = 0.f;
+#pragma unroll 4
+    for (int j = 0; j < N; ++j) {
+      const float h = lg.at(tl, j);
+      float wv[kBwdWrCols];
+      if (kLds) {
+        const f32x4 w0 = *(const f32x4 *)(wr + j * kBwdWrCols), w1 = *(const f32x4 *)(wr + j * kBwdWrCols + 4);
+        wv[0] = w0[0]; wv[1] = w0[1]; wv[2] = w0[2]; wv[3] = w0[3];
+        wv[4] = w1[0]; wv[5] = w1[1]; wv[6] = w1[2]; wv[7] = w1[3];
+      } else {
+#pragma unroll
+        for (int i = 0; i < kBwdWrCols; ++i) wv[i] = a.w_r[(int64_t)j * d + c0 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < kBwdWrCols; ++i) acc[i] = __builtin_fmaf(h, wv[i], acc[i]);
+    }
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < kBwdWrCols; ++i) {
+        float v = acc[i];
+        if (kept) v += a.dxe[tt * d + c0 + i];
+        if (a.add_residual) v += to_f32(dy[tt * d + c0 + i]);
+        dx[tt * d + c0 + i] = from_f32<T_>(v);
+      }
     }
   }
 }
@@ -616,7 +671,10 @@ __global__ __launch_bounds__(kRBThreads) void router_bwd_bf16_kernel(const Route
   const int nt = (int)min<int64_t>(kRouterTokens, a.T - t0);
   const LogitRows<kLds> lg =
       router_contract_bf16<kLds>((const bf16 *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, sm);
-  router_bwd_epilogue<bf16, kRBThreads, kLds>(lg, nt, t0, a);
+  static_assert(kRouterTokens * (kRouterChunk + 1) + bwd_lds_floats<kRBThreads>() <= kRouterSmem / 4,
+                "logit rows + backward scratch fit the staging area");
+  router_bwd_epilogue<bf16, kRBThreads, kLds>(lg, nt, t0, a,
+                                              (float *)sm.stage + kRouterTokens * (kRouterChunk + 1));
 }
 
 template <bool kLds>
@@ -627,30 +685,28 @@ __global__ __launch_bounds__(kRouterThreads) void router_bwd_f32_kernel(const Ro
   const int nt = (int)min<int64_t>(kRouterTokens, a.T - t0);
   const LogitRows<kLds> lg =
       router_contract_f32<kLds>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, s_lg, s_x);
-  router_bwd_epilogue<float, kRouterThreads, kLds>(lg, nt, t0, a);
+  __shared__ __attribute__((aligned(16))) float s_extra[bwd_lds_floats<kRouterThreads>()];
+  router_bwd_epilogue<float, kRouterThreads, kLds>(lg, nt, t0, a, s_extra);
 }
 
-// dW_r = sum_t dh_t x_t^T and dbias = sum_t dh_t: workgroup (j tile, k tile,
-// split s) sums tokens [s ts, (s + 1) ts) for a 64 x 64 tile of dW_r (4 x 4
-// per thread, token chunks of 16 through LDS); the k-tile-0 workgroups also
-// sum dh for the bias.  fp32 throughout; the splits are added in order by
+// dW_r = sum_t dh_t x_t^T for fp32 layers: workgroup (j tile, k tile, split
+// s) sums tokens [s ts, (s + 1) ts) for a 64 x 64 tile (4 x 4 per thread,
+// token chunks of 16 through LDS).  The splits are added in order by
 // router_wgrad_sum_kernel.
-template <typename T_>
-__global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restrict__ dh, const T_ *__restrict__ x,
-                                                           int64_t T, int N, int d, int64_t ts,
-                                                           float *__restrict__ wpart, float *__restrict__ bpart) {
+__global__ __launch_bounds__(256) void router_wgrad_f32_kernel(const float *__restrict__ dh,
+                                                               const float *__restrict__ x, int64_t T, int N, int d,
+                                                               int64_t ts, float *__restrict__ wpart) {
   __shared__ float sD[16][65], sX[16][65];
   const int j0 = blockIdx.x * 64, k0 = blockIdx.y * 64, sp = blockIdx.z;
   const int64_t ta = min<int64_t>(T, (int64_t)sp * ts), tb = min<int64_t>(T, ta + ts);
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   float acc[4][4] = {};
-  float bacc = 0.f;
   for (int64_t c = ta; c < tb; c += 16) {
     for (int i = tid; i < 16 * 64; i += 256) {
       const int r = i / 64, col = i % 64;
       const int64_t t = c + r;
       sD[r][col] = (t < tb && j0 + col < N) ? dh[t * N + j0 + col] : 0.f;
-      sX[r][col] = t < tb ? to_f32(x[t * d + k0 + col]) : 0.f;
+      sX[r][col] = t < tb ? x[t * d + k0 + col] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -666,10 +722,6 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restri
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
     }
-    if (blockIdx.y == 0 && tid < 64) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) bacc += sD[k][tid];
-    }
     __syncthreads();
   }
 #pragma unroll
@@ -679,32 +731,37 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restri
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) wpart[((int64_t)sp * N + j) * d + k0 + tx * 4 + jj] = acc[i][jj];
   }
-  if (blockIdx.y == 0 && tid < 64 && j0 + tid < N) bpart[(int64_t)sp * N + j0 + tid] = bacc;
 }
 
+// dW_r = sum over the splits of wpart, in order; dbias = sum over the router
+// blocks of bpart, in order.
 __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float *__restrict__ wpart,
                                                                const float *__restrict__ bpart, int N, int d,
-                                                               int splits, float *__restrict__ dw_r,
+                                                               int splits, int64_t nb, float *__restrict__ dw_r,
                                                                float *__restrict__ dbias) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t nd = (int64_t)N * d;
   if (i < nd) {
     float s = 0.f;
+#pragma unroll 8
     for (int sp = 0; sp < splits; ++sp) s += wpart[(int64_t)sp * nd + i];
     dw_r[i] = s;
   }
   if (dbias && i < N) {
     float s = 0.f;
-    for (int sp = 0; sp < splits; ++sp) s += bpart[(int64_t)sp * N + i];
+#pragma unroll 16
+    for (int64_t b = 0; b < nb; ++b) s += bpart[b * N + i];
     dbias[i] = s;
   }
 }
 
-int router_wgrad_splits(int64_t T, int N, int d) {
-  const int64_t tiles = ceil_div(N, 64) * (d / 64);
-  int64_t s = ceil_div(512, tiles);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(T, 256)));
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+WgradSplit router_wgrad_split(int64_t T, int N, int d) {
+  const int64_t tiles = ceil_div(N, 64) * ceil_div(d, 128);
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(ceil_div(512, tiles), ceil_div(T, 64)));
+  WgradSplit w;
+  w.ts = std::max<int64_t>(64, ceil_div(ceil_div(T, want), 64) * 64);
+  w.splits = (int)std::max<int64_t>(1, ceil_div(T, w.ts));
+  return w;
 }
 
 hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st, LaunchMarks marks) {
@@ -725,22 +782,22 @@ hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st, LaunchMarks
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark("bwd_router");
-  const int64_t ts = ceil_div(ceil_div(a.T, a.splits), 16) * 16;
-  const dim3 g((unsigned)ceil_div(a.N, 64), (unsigned)(a.d / 64), (unsigned)a.splits);
-  for (int r = reps(); r > 0; --r) {
-    if (a.dtype == kBF16)
-      router_wgrad_kernel<bf16><<<g, dim3(256), 0, st>>>(a.dh, (const bf16 *)a.x, a.T, a.N, a.d, ts, a.wpart,
-                                                         a.bpart);
-    else
-      router_wgrad_kernel<float><<<g, dim3(256), 0, st>>>(a.dh, (const float *)a.x, a.T, a.N, a.d, ts, a.wpart,
-                                                          a.bpart);
+  const WgradSplit sp = router_wgrad_split(a.T, a.N, a.d);
+  for (int r = reps(); r > 0 && e == hipSuccess; --r) {
+    if (a.dtype == kBF16) {
+      e = launch_router_wgrad_bf16(a.dh, a.x, a.T, a.N, a.d, sp, a.wpart, st);
+    } else {
+      const dim3 g((unsigned)ceil_div(a.N, 64), (unsigned)(a.d / 64), (unsigned)sp.splits);
+      router_wgrad_f32_kernel<<<g, dim3(256), 0, st>>>(a.dh, (const float *)a.x, a.T, a.N, a.d, sp.ts, a.wpart);
+      e = hipGetLastError();
+    }
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (e != hipSuccess) return e;
   mark("bwd_router_w");
   const int64_t nd = (int64_t)a.N * a.d;
   for (int r = reps(); r > 0; --r)
     router_wgrad_sum_kernel<<<dim3((unsigned)ceil_div(std::max<int64_t>(nd, a.N), 256)), dim3(256), 0, st>>>(
-        a.wpart, a.bpart, a.N, a.d, a.splits, a.dw_r, a.dbias);
+        a.wpart, a.bpart, a.N, a.d, sp.splits, nb, a.dw_r, a.dbias);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mark("bwd_router_w_sum");
   return hipSuccess;

@@ -35,6 +35,14 @@ KERNEL_KEYS = {
     "dispatch": ("dispatch_kernel", ""),
     "combine": ("combine_kernel", ""),
     "add_norm": ("add_norm_kernel", ""),
+    "topk_sum": ("topk_sum_kernel", ""),
+    "bwd_dz": ("bwd_gemm_bf16_kernel", "Lb0ELb1ELb0ELb1ELb0ELi0E"),
+    "bwd_dx": ("bwd_gemm_bf16_kernel", "Lb0ELb0ELb0ELb1ELb0ELi1E"),
+    "bwd_dw_out": ("bwd_gemm_bf16_kernel", "Lb1ELb1ELb1ELb1ELb0ELi2E"),
+    "bwd_dw_in": ("bwd_gemm_bf16_kernel", "Lb1ELb0ELb0ELb1ELb1ELi2E"),
+    "bwd_router": ("router_bwd_bf16_kernel", ""),
+    "bwd_router_w": ("router_wgrad_kernel", ""),
+    "bwd_router_w_sum": ("router_wgrad_sum_kernel", ""),
     "copy": ("__amd_rocclr_copyBuffer", ""),
 }
 
