@@ -30,6 +30,8 @@
 // (DWO / DWI) are zero, so an expert with no kept token gets exact zero
 // gradients.  Results are deterministic: fixed tiles, fixed reduction order.
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -60,21 +62,26 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int stride, int k
 // Operand tile loader.  A tile covers R rows (output rows for A, output
 // columns for B) and kBKC contraction columns.
 //  KM = false (k-contiguous): element (r, k) at base + row(r) * ld + k; LDS
-//    [R][kKcStride]; rows r past the live count re-read the last live row.
+//    [R][kKcStride]; rows past the live count re-read the last live row.
 //  KM = true (k-major): element (r, k) at base + krow(k) * ld + r; LDS
-//    [kBKC][R + 8]; contraction rows past `klive` are zero.
-// Rows come through the slot -> token map when G (gathered rows of a [T][ld]
-// array); k-major gathered rows may be scaled by the slot's gate (S).
+//    [kBKC][R + 8]; contraction rows past the live count are stored as zero.
+// With G, rows (KC) or contraction rows (KM) go through the slot -> token
+// map, read from an LDS copy (`rows`, indexed from the tile's first row or
+// the segment's first contraction row), so that a fetch issues its global
+// loads without waiting for any; S scales k-major rows by the slot's gate
+// (LDS copy `gates`) when they are stored.  fetch() only issues loads: every
+// use of the loaded data (zeroing, scaling) happens in store(), so loads of
+// later chunks stay in flight.
 template <int R, int kThreads, bool KM, bool G, bool S>
 struct TileLoader {
   static constexpr int kPieces = R * kBKC / 8;
   static constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
   static constexpr int kStride = KM ? R + 8 : kKcStride;
   static constexpr int kElems = KM ? kBKC * kStride : R * kStride;
-  u32x4 reg[kPer];
-  int off[kPer];     // LDS element offset of each piece
-  int rk[kPer];      // row (KC) or contraction row within the chunk (KM)
-  int col[kPer];     // column element offset within the row piece
+  using Regs = u32x4[kPer];
+  int off[kPer];  // LDS element offset of each piece
+  int rk[kPer];   // row (KC) or contraction row within the chunk (KM)
+  int col[kPer];  // column element offset within the row piece
   bool act[kPer];
 
   __device__ __forceinline__ void plan(int tid) {
@@ -82,53 +89,57 @@ struct TileLoader {
     for (int q = 0; q < kPer; ++q) {
       const int i = tid + q * kThreads;
       act[q] = i < kPieces;
-      const int ii = act[q] ? i : 0;
+      const int ii = act[q] ? i : 0;  // idle pieces load a duplicate of piece 0 and store nothing
       if (KM) {
         rk[q] = ii / (R / 8);
         col[q] = (ii % (R / 8)) * 8;
-        off[q] = rk[q] * kStride + col[q];
       } else {
         rk[q] = ii / (kBKC / 8);
         col[q] = (ii % (kBKC / 8)) * 8;
-        off[q] = rk[q] * kStride + col[q];
+      }
+      off[q] = rk[q] * kStride + col[q];
+    }
+  }
+
+  // KC: rows r0 + rk (live count `live`), contraction chunk at k0.
+  // KM: contraction rows k0 + rk (live count `live`, segment start ks),
+  //     columns c0 + col (clamped below rmax).
+  __device__ __forceinline__ void fetch(Regs &reg, const bf16 *base, int ld, const int *rows, int r0, int c0,
+                                        int live, int k0, int ks, int rmax) const {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      if (KM) {
+        const int kk = min(k0 + rk[q], live - 1);
+        const int64_t row = G ? (int64_t)rows[kk - ks] : kk;
+        const int c = min(c0 + col[q], rmax - 8);
+        reg[q] = *(const u32x4 *)(base + row * ld + c);
+      } else {
+        const int r = min(r0 + rk[q], live - 1);
+        const int64_t row = G ? (int64_t)rows[r - r0] : r;
+        reg[q] = *(const u32x4 *)(base + row * ld + k0 + col[q]);
       }
     }
   }
 
-  // KC: rows r0 + rk of the expert (live count `live`); chunk at k0.
-  // KM: contraction rows k0 + rk (live count `live`), columns c0 + col.
-  __device__ __forceinline__ void fetch(const bf16 *base, int64_t estride, int ld, const int32_t *tok,
-                                        const float *gmap, int64_t eC, int r0, int c0, int live, int k0, int rmax) {
+  __device__ __forceinline__ void store(const Regs &reg, bf16 *lds, int k0, int live, int ks,
+                                        const float *gates) const {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       if (!act[q]) continue;
+      u32x4 v = reg[q];
       if (KM) {
         const int k = k0 + rk[q];
-        const bool ok = k < live;
-        const int kk = ok ? k : max(live - 1, 0);
-        const int64_t row = G ? (int64_t)tok[eC + kk] : kk;
-        const int c = min(c0 + col[q], rmax - 8);
-        u32x4 v = *(const u32x4 *)(base + (G ? 0 : estride) + row * ld + c);
         if (S) {
-          const float g = gmap[eC + kk];
+          const float g = gates[min(k, live - 1) - ks];
           bf16x8 b = as_bf16x8(v);
 #pragma unroll
           for (int j = 0; j < 8; ++j) b[j] = (bf16)(g * (float)b[j]);
           v = as_u32x4(b);
         }
-        reg[q] = ok ? v : u32x4{0, 0, 0, 0};
-      } else {
-        const int r = min(r0 + rk[q], max(live - 1, 0));
-        const int64_t row = G ? (int64_t)tok[eC + r] : r;
-        reg[q] = *(const u32x4 *)(base + (G ? 0 : estride) + row * ld + k0 + col[q]);
+        if (k >= live) v = u32x4{0, 0, 0, 0};
       }
+      *(u32x4 *)(lds + off[q]) = v;
     }
-  }
-
-  __device__ __forceinline__ void store(bf16 *lds) const {
-#pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if (act[q]) *(u32x4 *)(lds + off[q]) = reg[q];
   }
 };
 
@@ -156,16 +167,24 @@ struct BwdArgs {
   int64_t ntiles;
 };
 
-// MBW x NBW MFMA blocks per wave, WM x WN waves.
-template <int MBW, int NBW, int WM, int WN, bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
-__global__ __launch_bounds__(WM *WN * 64) void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
+// MBW x NBW MFMA blocks per wave, WM x WN waves.  kBufs LDS operand buffers
+// and kPre register sets: (2, 2) keeps two contraction chunks in flight while
+// the MFMAs consume a third (long contractions); (1, 1) stages one chunk at a
+// time and leaves LDS for a second workgroup per CU (short contractions, whose
+// workgroups overlap each other instead).  kWavesPerEU (0: none) caps the
+// registers so that many waves fit.
+template <int MBW, int NBW, int WM, int WN, bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI, int kBufs,
+          int kPre, int kWavesPerEU>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU > 0 ? kWavesPerEU : 1)))
+void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
   constexpr int kThreads = WM * WN * 64;
   constexpr int BM = WM * MBW * 16, BN = WN * NBW * 16;
   constexpr bool kRaggedM = EPI != kEpiDW;
+  static_assert((kBufs == 2 && (kPre == 1 || kPre == 2)) || (kBufs == 1 && kPre == 1), "pipeline shape");
   using LA = TileLoader<BM, kThreads, AKM, AG, AS>;
   using LB = TileLoader<BN, kThreads, BKM, BG, false>;
   constexpr int kStageStride = NBW * 16 + 4;  // fp32 epilogue staging row (per wave)
-  constexpr int kOperandElems = 2 * (LA::kElems + LB::kElems);
+  constexpr int kOperandElems = kBufs * (LA::kElems + LB::kElems);
   constexpr int kStageElems = WM * WN * 16 * kStageStride * 2;  // in bf16 units
   constexpr int kSmem = kOperandElems > kStageElems ? kOperandElems : kStageElems;
   __shared__ __attribute__((aligned(16))) bf16 smem[kSmem];
@@ -196,21 +215,46 @@ __global__ __launch_bounds__(WM *WN * 64) void bwd_gemm_bf16_kernel(const BwdArg
   la.plan(tid);
   lb.plan(tid);
   auto sA = [&](int b) { return smem + b * LA::kElems; };
-  auto sB = [&](int b) { return smem + 2 * LA::kElems + b * LB::kElems; };
+  auto sB = [&](int b) { return smem + kBufs * LA::kElems + b * LB::kElems; };
   const bf16 *Ab = p.A + (AG ? 0 : (int64_t)e * p.a_estride);
   const bf16 *Bb = p.B + (BG ? 0 : (int64_t)e * p.b_estride);
 
+  // slot -> token copies in LDS: the tile's rows (k-contiguous gathered
+  // operands) and one segment of contraction rows with their gates (k-major
+  // gathered operands)
+  constexpr bool kRowG = (AG && !AKM) || (BG && !BKM);
+  constexpr bool kKG = (AG && AKM) || (BG && BKM);
+  constexpr int kSeg = 1024;  // contraction rows per segment
+  __shared__ int s_rtok[kRowG ? (BM > BN ? BM : BN) : 1];
+  __shared__ int s_ktok[kKG ? kSeg : 1];
+  __shared__ float s_kgate[(kKG && AS) ? kSeg : 1];
+  if (kRowG) {
+    const int r0 = (AG && !AKM) ? m0 : n0, lv = (AG && !AKM) ? Mt : p.Nout;
+    for (int r = tid; r < ((AG && !AKM) ? BM : BN); r += kThreads) s_rtok[r] = p.tok[eC + min(r0 + r, lv - 1)];
+    __syncthreads();
+  }
+
+  typename LA::Regs ra[kPre];
+  typename LB::Regs rb[kPre];
+  int ks = 0;  // first contraction row of the current segment
   // A rows: output rows (KC: live count Mt) or output rows with contraction
   // rows live up to Kt (KM).  B likewise with the output columns.
-  auto fetch = [&](int k0) {
+  auto fetch = [&](auto slot, int k0) {
+    constexpr int sl = decltype(slot)::value;
     if (AKM)
-      la.fetch(Ab, 0, p.lda, p.tok, p.gmap, eC, 0, m0, Kt, k0, p.M);
+      la.fetch(ra[sl], Ab, p.lda, s_ktok, 0, m0, Kt, k0, ks, p.M);
     else
-      la.fetch(Ab, 0, p.lda, p.tok, p.gmap, eC, m0, 0, Mt, k0, 0);
+      la.fetch(ra[sl], Ab, p.lda, s_rtok, m0, 0, Mt, k0, ks, 0);
     if (BKM)
-      lb.fetch(Bb, 0, p.ldb, p.tok, p.gmap, eC, 0, n0, Kt, k0, p.Nout);
+      lb.fetch(rb[sl], Bb, p.ldb, s_ktok, 0, n0, Kt, k0, ks, p.Nout);
     else
-      lb.fetch(Bb, 0, p.ldb, p.tok, p.gmap, eC, n0, 0, p.Nout, k0, 0);
+      lb.fetch(rb[sl], Bb, p.ldb, s_rtok, n0, 0, p.Nout, k0, ks, 0);
+  };
+  int kst = 0;  // contraction row of the chunk being stored
+  auto store = [&](auto slot, int buf) {
+    constexpr int sl = decltype(slot)::value;
+    la.store(ra[sl], sA(buf), kst, Kt, ks, s_kgate);
+    lb.store(rb[sl], sB(buf), kst, Kt, ks, s_kgate);
   };
 
   f32x4 acc[MBW][NBW];
@@ -219,45 +263,90 @@ __global__ __launch_bounds__(WM *WN * 64) void bwd_gemm_bf16_kernel(const BwdArg
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nch = (int)ceil_div(Kt, kBKC);
-  if (nch > 0) {
-    fetch(0);
-    la.store(sA(0));
-    lb.store(sB(0));
-    __syncthreads();
-    for (int ch = 0; ch < nch; ++ch) {
-      const int cur = ch & 1;
-      if (ch + 1 < nch) fetch((ch + 1) * kBKC);
+  auto compute = [&](int buf) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 a[MBW], b[NBW];
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 a[MBW], b[NBW];
 #pragma unroll
-        for (int i = 0; i < MBW; ++i) {
-          const int r = wm * MBW * 16 + i * 16;
-          if (AKM)
-            a[i] = tr_operand(sA(cur), LA::kStride, s * 32, r, lane);
-          else
-            a[i] = as_bf16x8(*(const u32x4 *)(sA(cur) + (r + r16) * LA::kStride + s * 32 + kq));
-        }
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const int c = wn * NBW * 16 + j * 16;
-          if (BKM)
-            b[j] = tr_operand(sB(cur), LB::kStride, s * 32, c, lane);
-          else
-            b[j] = as_bf16x8(*(const u32x4 *)(sB(cur) + (c + r16) * LB::kStride + s * 32 + kq));
-        }
-#pragma unroll
-        for (int i = 0; i < MBW; ++i)
-#pragma unroll
-          for (int j = 0; j < NBW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < MBW; ++i) {
+        const int r = wm * MBW * 16 + i * 16;
+        if (AKM)
+          a[i] = tr_operand(sA(buf), LA::kStride, s * 32, r, lane);
+        else
+          a[i] = as_bf16x8(*(const u32x4 *)(sA(buf) + (r + r16) * LA::kStride + s * 32 + kq));
       }
-      if (ch + 1 < nch) {
-        la.store(sA(cur ^ 1));
-        lb.store(sB(cur ^ 1));
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int c = wn * NBW * 16 + j * 16;
+        if (BKM)
+          b[j] = tr_operand(sB(buf), LB::kStride, s * 32, c, lane);
+        else
+          b[j] = as_bf16x8(*(const u32x4 *)(sB(buf) + (c + r16) * LB::kStride + s * 32 + kq));
+      }
+#pragma unroll
+      for (int i = 0; i < MBW; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // contraction segments: one for fixed contractions; k-major gathered
+  // operands take kSeg rows at a time (their token copy is per segment)
+  for (ks = 0; ks < Kt; ks += kSeg) {
+    const int kend = kKG ? min(Kt, ks + kSeg) : Kt;
+    if (kKG) {
+      __syncthreads();  // the previous segment's readers are done
+      for (int i = tid; i < kend - ks; i += kThreads) {
+        s_ktok[i] = p.tok[eC + ks + i];
+        if (AS) s_kgate[i] = p.gmap[eC + ks + i];
       }
       __syncthreads();
     }
+    const int nch = (int)ceil_div(kend - ks, kBKC);
+    if constexpr (kBufs == 2) {
+      fetch(I0{}, ks);
+      kst = ks;
+      store(I0{}, 0);
+      if (kPre == 2 && nch > 1) fetch(I1{}, ks + kBKC);
+      __syncthreads();
+      // chunk ch is in LDS buffer ch & 1; with two register sets, set ch & 1
+      // is free (its chunk is in LDS) and refills with chunk ch + 2, while set
+      // (ch + 1) & 1 holds chunk ch + 1 for the other buffer.  Every step
+      // issues its loads unconditionally (past the end: the last chunk again,
+      // cache hits never stored) so that the compiler counts the loads in
+      // flight exactly and waits only for the chunk it stores.
+      auto step = [&](int ch, auto par) {
+        constexpr int c = decltype(par)::value;
+        if (kPre == 2)
+          fetch(std::integral_constant<int, c>{}, ks + min(ch + 2, nch - 1) * kBKC);
+        else
+          fetch(I0{}, ks + min(ch + 1, nch - 1) * kBKC);
+        if (ch < nch) compute(c);
+        if (ch + 1 < nch) {
+          kst = ks + (ch + 1) * kBKC;
+          store(std::integral_constant<int, kPre == 2 ? 1 - c : 0>{}, 1 - c);
+        }
+        __syncthreads();
+      };
+      for (int ch = 0; ch < nch; ch += 2) {
+        step(ch, I0{});
+        step(ch + 1, I1{});
+      }
+    } else {
+      fetch(I0{}, ks);
+      for (int ch = 0; ch < nch; ++ch) {
+        if (ch > 0) __syncthreads();  // the previous chunk's readers are done
+        kst = ks + ch * kBKC;
+        store(I0{}, 0);
+        __syncthreads();
+        fetch(I0{}, ks + min(ch + 1, nch - 1) * kBKC);  // unconditional, as above
+        compute(0);
+      }
+      __syncthreads();  // the next segment / the epilogue reuse the LDS
+    }
+    if (!kKG) break;
   }
 
   // ---- epilogue: each wave stages one 16-row block at a time as fp32 in its
@@ -554,10 +643,13 @@ hipError_t launch_router_wgrad_bf16(const float *dh, const void *x, int64_t T, i
 // ---------------------------------------------------------------------------
 namespace {
 
-// Tile shapes: rows of an expert (up to 160) x 256 columns for the products
-// with a ragged row count; 128 x 256 for the weight gradients.
-constexpr int kRowMBW = 5, kWgtMBW = 4, kNBWb = 4, kWMb = 2, kWNb = 4;
-constexpr int kBNb = kWNb * kNBWb * 16;
+// Tile shapes: rows of an expert (up to 160) x 256 columns, 8 waves, a deep
+// pipeline for the products with a long contraction (DZ, DX); 128 x 128, 4
+// waves, single-buffered, several workgroups per CU for the weight gradients
+// (contraction = an expert's rows, short).
+constexpr int kRowMBW = 5, kRowNBW = 4, kRowWM = 2, kRowWN = 4;
+constexpr int kWgtMBW = 4, kWgtNBW = 4, kWgtWM = 2, kWgtWN = 2;
+constexpr int kBNb = kRowWN * kRowNBW * 16;
 
 template <typename T_>
 BwdArgs<T_> bwd_args(const BwdLaunch &L, const void *A, int64_t ae, int lda, const void *B, int64_t be, int ldb,
@@ -587,12 +679,16 @@ BwdArgs<T_> bwd_args(const BwdLaunch &L, const void *A, int64_t ae, int lda, con
   return a;
 }
 
-template <int MBW, bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
+template <bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
 hipError_t run_bf16(const BwdArgs<bf16> &a, hipStream_t st) {
   if (a.ntiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)(ceil_div(a.ntiles, 8) * 8);
-  bwd_gemm_bf16_kernel<MBW, kNBWb, kWMb, kWNb, AKM, AG, AS, BKM, BG, EPI>
-      <<<dim3(grid), dim3(kWMb * kWNb * 64), 0, st>>>(a);
+  if constexpr (EPI != kEpiDW)
+    bwd_gemm_bf16_kernel<kRowMBW, kRowNBW, kRowWM, kRowWN, AKM, AG, AS, BKM, BG, EPI, 2, 2, 0>
+        <<<dim3(grid), dim3(kRowWM * kRowWN * 64), 0, st>>>(a);
+  else
+    bwd_gemm_bf16_kernel<kWgtMBW, kWgtNBW, kWgtWM, kWgtWN, AKM, AG, AS, BKM, BG, EPI, 1, 1, 3>
+        <<<dim3(grid), dim3(kWgtWM * kWgtWN * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -622,29 +718,29 @@ hipError_t launch_bwd_experts(const BwdLaunch &L, hipStream_t st, LaunchMarks ma
     // no kept rows: the weight gradients are zero, nothing else runs
   }
   if (L.dtype == kBF16) {
-    const int bm_rows = kWMb * kRowMBW * 16, bm_w = kWMb * kWgtMBW * 16;
+    const int bm_rows = kRowWM * kRowMBW * 16, bm_w = kWgtWM * kWgtMBW * 16, bn_w = kWgtWN * kWgtNBW * 16;
     // DZ: A = dy rows through tok (k-contiguous), B = W_out,e [d][d_ff] (k-major)
     auto dz = bwd_args<bf16>(L, L.dy, 0, d, L.w_out, ein, f, C, f, d, L.du, eh, f, bm_rows, kBNb);
     for (int r = reps(); r > 0 && e == hipSuccess; --r)
-      e = run_bf16<kRowMBW, false, true, false, true, false, kEpiDU>(dz, st);
+      e = run_bf16<false, true, false, true, false, kEpiDU>(dz, st);
     if (e != hipSuccess) return e;
     mark("bwd_dz");
     // DX: A = DU,e [rows][d_ff] (k-contiguous), B = W_in,e [d_ff][d] (k-major)
     auto dx = bwd_args<bf16>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, bm_rows, kBNb);
     for (int r = reps(); r > 0 && e == hipSuccess; --r)
-      e = run_bf16<kRowMBW, false, false, false, true, false, kEpiDX>(dx, st);
+      e = run_bf16<false, false, false, true, false, kEpiDX>(dx, st);
     if (e != hipSuccess) return e;
     mark("bwd_dx");
     // DWO: A = g dy rows through tok (k-major, gate-scaled), B = H,e [rows][d_ff] (k-major)
-    auto dwo = bwd_args<bf16>(L, L.dy, 0, d, L.hidden, eh, f, d, f, 0, L.dw_out, ein, f, bm_w, kBNb);
+    auto dwo = bwd_args<bf16>(L, L.dy, 0, d, L.hidden, eh, f, d, f, 0, L.dw_out, ein, f, bm_w, bn_w);
     for (int r = reps(); r > 0 && e == hipSuccess; --r)
-      e = run_bf16<kWgtMBW, true, true, true, true, false, kEpiDW>(dwo, st);
+      e = run_bf16<true, true, true, true, false, kEpiDW>(dwo, st);
     if (e != hipSuccess) return e;
     mark("bwd_dw_out");
     // DWI: A = DU,e [rows][d_ff] (k-major), B = x rows through tok (k-major)
-    auto dwi = bwd_args<bf16>(L, L.du, eh, f, L.x, 0, d, f, d, 0, L.dw_in, ein, d, bm_w, kBNb);
+    auto dwi = bwd_args<bf16>(L, L.du, eh, f, L.x, 0, d, f, d, 0, L.dw_in, ein, d, bm_w, bn_w);
     for (int r = reps(); r > 0 && e == hipSuccess; --r)
-      e = run_bf16<kWgtMBW, true, false, false, true, true, kEpiDW>(dwi, st);
+      e = run_bf16<true, false, false, true, true, kEpiDW>(dwi, st);
     if (e != hipSuccess) return e;
     mark("bwd_dw_in");
     return hipSuccess;
