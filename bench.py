@@ -166,12 +166,16 @@ def backward_alg_bytes(T: int, d: int, f: int, N: int, C: int, counts, splits: i
     R = sum(min(int(c), C) for c in counts)
     Ea = sum(1 for c in counts if min(int(c), C) > 0)
     n_dg = (f + 255) // 256
+    kp = -(-6 * N // 64) * 64
     return {
         "bwd_dz": Ea * d * f * 2 + R * d * 2 + R * f * 2 + R * f * 2 + R * n_dg * 4 + R * 8,
         "bwd_dx": Ea * f * d * 2 + R * f * 2 + R * d * 4 + R * 4,
         "bwd_dw_out": R * d * 2 + R * f * 2 + R * 8 + N * d * f * 2,
         "bwd_dw_in": R * f * 2 + R * d * 2 + R * 4 + N * f * d * 2,
-        "bwd_router": T * d * 2 + N * d * 4 + R * n_dg * 4 + R * d * 4 + T * 9 + N * 4 + T * N * 4 + T * d * 2,
+        # logits recomputed (x, W_r), dL/dh written fp32 and as six bf16 planes (Kp = 6 N padded to 64)
+        "bwd_router": T * d * 2 + N * d * 4 + R * n_dg * 4 + T * 5 + N * 4 + T * N * 4 + T * kp * 2,
+        # W_r split to planes, then dx = planes . planes + experts' part (kept rows) -> bf16
+        "bwd_router_dx": N * d * 4 + kp * d * 2 + T * kp * 2 + kp * d * 2 + R * d * 4 + T + T * d * 2,
         "bwd_router_w": T * N * 4 + T * d * 2 + splits * (N * d + N) * 4,
         "bwd_router_w_sum": splits * (N * d + N) * 4 + (N * d + N) * 4,
     }

@@ -220,7 +220,10 @@ int switch_topk_layer_forward(const switch_shape *s, int32_t top_k, const void *
  * and d_router_bias [N] (may be NULL) in fp32.  An expert that received no
  * kept token gets exact zeros.  Arithmetic: bf16 MFMA with fp32 accumulation
  * for the expert products (du and g dy rounded to bf16 as operands), fp32 for
- * the router; dx summed in fp32 and rounded once.  Deterministic.
+ * the router (in bf16 layers the router's matrix products run on bf16 MFMA
+ * from exact three-way bf16 splits of their fp32 operands: dW_r with all
+ * products exact, W_r^T dL/dh with the six plane products above 2^-24 of the
+ * result); dx summed in fp32 and rounded once.  Deterministic.
  * workspace: switch_backward_workspace_bytes bytes (256-byte aligned).
  * Errors: as switch_layer_forward; SWITCH_E_WORKSPACE if fwd_workspace_bytes
  * is below the forward's workspace size. */
@@ -233,9 +236,11 @@ int switch_layer_backward(const switch_shape *s, const void *x, const float *w_r
                           void *stream);
 /* Measurement variant of switch_layer_backward, with the contract of
  * switch_layer_forward_profiled: kernels first_kernel..last_kernel only, each
- * `times` times.  The backward launches 7 kernels, in order: "bwd_dz",
- * "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_w",
- * "bwd_router_w_sum"; none modifies its own inputs. */
+ * `times` times.  The backward's launch steps, in order: "bwd_dz",
+ * "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_dx" (bf16
+ * layers: the router's part of dx on matrix cores, two launches; fp32 layers:
+ * none, dx is formed in "bwd_router"), "bwd_router_w", "bwd_router_w_sum";
+ * none modifies its own inputs. */
 int switch_layer_backward_profiled(const switch_shape *s, const void *x, const float *w_router,
                                    const float *router_bias, const void *w_in, const void *w_out,
                                    int32_t add_residual, const int32_t *expert_idx, const uint8_t *dropped,

@@ -33,7 +33,7 @@ EXPORTED = [
     "switch_launch_names", "switch_add_norm", "switch_topk_workspace_bytes", "switch_topk_layer_forward",
     "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
 ]
-BACKWARD_KERNELS = ["bwd_dz", "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_w",
+BACKWARD_KERNELS = ["bwd_dz", "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
                     "bwd_router_w_sum"]
 
 

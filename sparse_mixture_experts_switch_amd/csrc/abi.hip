@@ -299,8 +299,9 @@ int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *
 // logits scratch when N > kRouterChunk, and the split partial sums of dW_r
 // and the bias gradient.
 struct BwdLayout {
-  size_t du = 0, dgpart = 0, dxe = 0, dh = 0, logits = 0, wpart = 0, bpart = 0, total = 0;
-  int n_dg = 0, splits = 1;
+  size_t du = 0, dgpart = 0, dxe = 0, dh = 0, logits = 0, wpart = 0, bpart = 0, aplanes = 0, bplanes = 0,
+         total = 0;
+  int n_dg = 0, splits = 1, kp = 0;
 };
 
 int bwd_layout(const switch_shape *s, BwdLayout &B) {
@@ -308,10 +309,12 @@ int bwd_layout(const switch_shape *s, BwdLayout &B) {
   const int es = esize(s->dtype);
   B.n_dg = bwd_dz_tiles(s->dtype, (int)f);
   B.splits = router_wgrad_split(T, (int)N, (int)d).splits;
-  size_t du, dg, dxe, dh, lg = 0, wp, bp;
+  B.kp = router_dx_kp((int)N);
+  size_t du, dg, dxe, dh, lg = 0, wp, bp, ap = 0, bq = 0;
+  const bool planes = s->dtype == SWITCH_BF16;  // the MFMA dx product of bf16 layers
   bool ok = mul(du, {N, C, f, es}) && mul(dg, {T, B.n_dg, 4}) && mul(dxe, {T, d, 4}) && mul(dh, {T, N, 4}) &&
             (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(wp, {B.splits, N, d, 4}) &&
-            mul(bp, {router_blocks(T), N, 4});
+            mul(bp, {router_blocks(T), N, 4}) && (!planes || (mul(ap, {T, B.kp, 2}) && mul(bq, {B.kp, d, 2})));
   if (!ok) return fail(SWITCH_E_UNSUPPORTED, "backward buffer sizes overflow for this shape");
   size_t o = 0;
   B.du = o;
@@ -328,6 +331,10 @@ int bwd_layout(const switch_shape *s, BwdLayout &B) {
   o = align_up(o + wp);
   B.bpart = o;
   o = align_up(o + bp);
+  B.aplanes = o;
+  o = align_up(o + ap);
+  B.bplanes = o;
+  o = align_up(o + bq);
   B.total = o;
   return SWITCH_OK;
 }
@@ -379,7 +386,8 @@ int layer_backward(const switch_shape *s, const void *x, const float *w_router, 
   RouterBwdArgs ra{s->dtype, s->tokens, s->d_model, s->num_experts, x, w_router, router_bias,
                    (float *)(w + B.logits), expert_idx, dropped, expert_count, (const float *)(w + B.dgpart),
                    B.n_dg, d_aux, (const float *)(w + B.dxe), dy, add_residual ? 1 : 0, (float *)(w + B.dh), dx,
-                   dw_router, d_router_bias, (float *)(w + B.wpart), (float *)(w + B.bpart)};
+                   dw_router, d_router_bias, (float *)(w + B.wpart), (float *)(w + B.bpart), w + B.aplanes,
+                   w + B.bplanes, B.kp};
   if ((e = launch_router_bwd(ra, st, marks)) != hipSuccess) return hip_fail(e, "backward router launch");
   return SWITCH_OK;
 }

@@ -143,7 +143,11 @@ struct TileLoader {
   }
 };
 
-enum BwdEpi { kEpiDU = 0, kEpiDX = 1, kEpiDW = 2 };
+// Epilogues: DU (du = g z [H > 0] and the partial dots <z, H>), DX (the
+// experts' part of dx, fp32 rows through the slot -> token map), DW (a weight
+// gradient tile), DXR (the router's part of dx plus the experts' part for kept
+// tokens plus dy with the residual, rounded once: the whole dx).
+enum BwdEpi { kEpiDU = 0, kEpiDX = 1, kEpiDW = 2, kEpiDXR = 3 };
 
 template <typename T_>
 struct BwdArgs {
@@ -163,6 +167,9 @@ struct BwdArgs {
   int ldo;
   const T_ *H;            // [N][C][Nout] forward hidden activations (DU)
   float *dgpart;          // [T][n_tiles] partial <z, h> per token (DU)
+  const float *dxe;       // [T][Nout] experts' part of dx (DXR)
+  const uint8_t *dropped; // [T] (DXR)
+  const T_ *dyres;        // [T][Nout] dy when the residual is added, or null (DXR)
   int m_tiles, n_tiles;
   int64_t ntiles;
 };
@@ -179,7 +186,8 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(kWa
 void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
   constexpr int kThreads = WM * WN * 64;
   constexpr int BM = WM * MBW * 16, BN = WN * NBW * 16;
-  constexpr bool kRaggedM = EPI != kEpiDW;
+  constexpr bool kRaggedM = EPI == kEpiDU || EPI == kEpiDX;  // rows = an expert's kept slots
+  constexpr bool kRaggedK = EPI == kEpiDW;                   // contraction = an expert's kept slots
   static_assert((kBufs == 2 && (kPre == 1 || kPre == 2)) || (kBufs == 1 && kPre == 1), "pipeline shape");
   using LA = TileLoader<BM, kThreads, AKM, AG, AS>;
   using LB = TileLoader<BN, kThreads, BKM, BG, false>;
@@ -199,11 +207,11 @@ void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
   const int e = (int)(id / ((int64_t)p.m_tiles * p.n_tiles));
   const int rem = (int)(id % ((int64_t)p.m_tiles * p.n_tiles));
   const int mt = rem / p.n_tiles, nt = rem % p.n_tiles;
-  const int live = min(p.counts[e], p.C);
+  const int live = (kRaggedM || kRaggedK) ? min(p.counts[e], p.C) : 0;
   const int m0 = mt * BM, n0 = nt * BN;
   const int Mt = kRaggedM ? live : p.M;
   if (m0 >= Mt) return;  // dead tile (ragged rows)
-  const int Kt = kRaggedM ? p.K : live;
+  const int Kt = kRaggedK ? live : p.K;
   const int64_t eC = (int64_t)e * p.C;
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -394,6 +402,24 @@ void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
           float *o = (float *)p.Out + t * p.ldo + n;
           *(f32x4 *)o = f32x4{v[0], v[1], v[2], v[3]};
           *(f32x4 *)(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        }
+      } else if (EPI == kEpiDXR) {
+        if (in) {
+          const int64_t row = (int64_t)m * p.ldo + n;
+          if (!p.dropped[m]) {
+            const f32x4 e0 = *(const f32x4 *)(p.dxe + row), e1 = *(const f32x4 *)(p.dxe + row + 4);
+            v[0] += e0[0]; v[1] += e0[1]; v[2] += e0[2]; v[3] += e0[3];
+            v[4] += e1[0]; v[5] += e1[1]; v[6] += e1[2]; v[7] += e1[3];
+          }
+          if (p.dyres) {
+            const bf16x8 r = as_bf16x8(*(const u32x4 *)(p.dyres + row));
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] += (float)r[q];
+          }
+          bf16x8 o;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) o[q] = (bf16)v[q];
+          *(u32x4 *)((bf16 *)p.Out + row) = as_u32x4(o);
         }
       } else {  // kEpiDU: du = g z [h > 0], partial <z, h>
         float dot = 0.f;
@@ -639,6 +665,35 @@ hipError_t launch_router_wgrad_bf16(const float *dh, const void *x, int64_t T, i
 }
 
 // ---------------------------------------------------------------------------
+// The router's part of dx, dx_t += W_r^T dL/dh_t, on bf16 MFMA.  Both fp32
+// operands are split exactly into three bf16 planes (hi + mid + lo); the six
+// plane products that carry more than 2^-24 of the result -- (hi, hi), (hi,
+// mid), (mid, hi), (hi, lo), (lo, hi), (mid, mid) -- are one contraction of
+// length 6 N: A' [T][Kp] holds the dL/dh planes in the order hi, hi, mid, hi,
+// lo, mid (written by the router kernel), B' [Kp][d] the W_r planes in the
+// order hi, mid, hi, lo, hi, mid (rows p N + j; Kp = 6 N rounded up to the
+// chunk, padding rows and columns zero).  Each dropped product is below
+// 2^-24 of |dL/dh| |W_r| per term, so the sum is fp32-accurate.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_wr_planes_kernel(const float *__restrict__ w_r, int N, int d, int kp,
+                                                               bf16 *__restrict__ planes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)kp * d) return;
+  const int row = (int)(i / d), k = (int)(i % d);
+  bf16 out = (bf16)0.f;
+  if (row < 6 * N) {
+    const int pl = row / N, j = row % N;
+    bf16 hi, mid, lo;
+    split3(w_r[(int64_t)j * d + k], hi, mid, lo);
+    static constexpr int kWhich[6] = {0, 1, 0, 2, 0, 1};  // B' order: hi, mid, hi, lo, hi, mid
+    out = kWhich[pl] == 0 ? hi : (kWhich[pl] == 1 ? mid : lo);
+  }
+  planes[i] = out;
+}
+
+int router_dx_kp(int N) { return (int)ceil_div(6 * (int64_t)N, kBKC) * kBKC; }
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 namespace {
@@ -648,8 +703,9 @@ namespace {
 // waves, single-buffered, several workgroups per CU for the weight gradients
 // (contraction = an expert's rows, short).
 constexpr int kRowMBW = 5, kRowNBW = 4, kRowWM = 2, kRowWN = 4;
+constexpr int kDxNBW = 2;  // DX: 128 columns per tile (d_model / 128 tiles per expert)
 constexpr int kWgtMBW = 4, kWgtNBW = 4, kWgtWM = 2, kWgtWN = 2;
-constexpr int kBNb = kRowWN * kRowNBW * 16;
+constexpr int kBNb = kRowWN * kRowNBW * 16, kBNdx = kRowWN * kDxNBW * 16;
 
 template <typename T_>
 BwdArgs<T_> bwd_args(const BwdLaunch &L, const void *A, int64_t ae, int lda, const void *B, int64_t be, int ldb,
@@ -683,8 +739,11 @@ template <bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
 hipError_t run_bf16(const BwdArgs<bf16> &a, hipStream_t st) {
   if (a.ntiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)(ceil_div(a.ntiles, 8) * 8);
-  if constexpr (EPI != kEpiDW)
+  if constexpr (EPI == kEpiDU)
     bwd_gemm_bf16_kernel<kRowMBW, kRowNBW, kRowWM, kRowWN, AKM, AG, AS, BKM, BG, EPI, 2, 2, 0>
+        <<<dim3(grid), dim3(kRowWM * kRowWN * 64), 0, st>>>(a);
+  else if constexpr (EPI == kEpiDX)
+    bwd_gemm_bf16_kernel<kRowMBW, kDxNBW, kRowWM, kRowWN, AKM, AG, AS, BKM, BG, EPI, 2, 2, 0>
         <<<dim3(grid), dim3(kRowWM * kRowWN * 64), 0, st>>>(a);
   else
     bwd_gemm_bf16_kernel<kWgtMBW, kWgtNBW, kWgtWM, kWgtWN, AKM, AG, AS, BKM, BG, EPI, 1, 1, 3>
@@ -700,6 +759,36 @@ hipError_t run_f32(const BwdArgs<float> &a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_router_dx_bf16(const RouterDxArgs &r, hipStream_t st) {
+  hipError_t e;
+  const int64_t n = (int64_t)r.kp * r.d;
+  router_wr_planes_kernel<<<dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st>>>(r.w_r, r.N, r.d, r.kp,
+                                                                                   (bf16 *)r.bplanes);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (r.T == 0) return hipSuccess;
+  BwdArgs<bf16> a{};
+  a.C = 0;
+  a.A = (const bf16 *)r.aplanes;
+  a.lda = r.kp;
+  a.B = (const bf16 *)r.bplanes;
+  a.ldb = r.d;
+  a.M = (int)r.T;
+  a.Nout = r.d;
+  a.K = r.kp;
+  a.Out = r.dx;
+  a.ldo = r.d;
+  a.dxe = r.dxe;
+  a.dropped = r.dropped;
+  a.dyres = (const bf16 *)r.dyres;
+  a.m_tiles = (int)ceil_div(r.T, kRowWM * kRowMBW * 16);
+  a.n_tiles = (int)ceil_div(r.d, kBNdx);
+  a.ntiles = (int64_t)a.m_tiles * a.n_tiles;
+  const unsigned grid = (unsigned)(ceil_div(a.ntiles, 8) * 8);
+  bwd_gemm_bf16_kernel<kRowMBW, kDxNBW, kRowWM, kRowWN, false, false, false, true, false, kEpiDXR, 2, 2, 0>
+      <<<dim3(grid), dim3(kRowWM * kRowWN * 64), 0, st>>>(a);
+  return hipGetLastError();
+}
 
 int bwd_dz_tiles(int dtype, int dff) { return (int)ceil_div(dff, dtype == kBF16 ? kBNb : 64); }
 
@@ -726,7 +815,7 @@ hipError_t launch_bwd_experts(const BwdLaunch &L, hipStream_t st, LaunchMarks ma
     if (e != hipSuccess) return e;
     mark("bwd_dz");
     // DX: A = DU,e [rows][d_ff] (k-contiguous), B = W_in,e [d_ff][d] (k-major)
-    auto dx = bwd_args<bf16>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, bm_rows, kBNb);
+    auto dx = bwd_args<bf16>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, bm_rows, kBNdx);
     for (int r = reps(); r > 0 && e == hipSuccess; --r)
       e = run_bf16<false, false, false, true, false, kEpiDX>(dx, st);
     if (e != hipSuccess) return e;

@@ -188,7 +188,25 @@ struct RouterBwdArgs {
   float *dw_r, *dbias;    // out ([N][d], [N] or null)
   float *wpart;           // [splits][N][d] scratch: dW_r partial sums
   float *bpart;           // [router blocks][N] scratch: bias partial sums
+  void *aplanes;          // bf16 layers: [T][kp] dL/dh planes for the dx product
+  void *bplanes;          // bf16 layers: [kp][d] W_r planes
+  int kp;
 };
+// The router's part of dx on bf16 MFMA (backward.hip), with the experts' part
+// and dy added: the whole dx of a bf16 layer.
+struct RouterDxArgs {
+  int64_t T;
+  int d, N, kp;
+  const float *w_r;
+  const void *aplanes;
+  void *bplanes;
+  const float *dxe;
+  const uint8_t *dropped;
+  const void *dyres;  // dy with the residual, or null
+  void *dx;
+};
+int router_dx_kp(int N);  // contraction length of the plane products, padded
+hipError_t launch_router_dx_bf16(const RouterDxArgs &r, hipStream_t st);
 // Token split of the dW_r sum: `splits` ranges of `ts` tokens (a multiple of 64).
 struct WgradSplit {
   int splits;

@@ -551,7 +551,9 @@ constexpr int bwd_lds_floats() {
   return kRouterChunk + (kThreads / kWave) * kRouterChunk * kBwdWrCols;
 }
 
-template <typename T_, int kThreads, bool kLds>
+// kDxHere: form dx in this kernel (fp32 layers, vector ALUs); otherwise
+// write the exact bf16 planes of dL/dh for the MFMA dx product (bf16 layers).
+template <typename T_, int kThreads, bool kLds, bool kDxHere>
 __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0, const RouterBwdArgs &a,
                                     float *s_extra) {
   constexpr int kLpt = kThreads / kRouterTokens;  // lanes per token
@@ -600,7 +602,22 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
       const float dh = pj * (dp - sdp);
       lg.at(t, j) = dh;
       a.dh[tt * N + j] = dh;
+      if (!kDxHere) {  // planes in the order hi, hi, mid, hi, lo, mid
+        bf16 *ap = (bf16 *)a.aplanes + tt * a.kp + j;
+        const bf16 hi = (bf16)dh;
+        const float r1 = dh - (float)hi;
+        const bf16 mid = (bf16)r1;
+        const bf16 lo = (bf16)(r1 - (float)mid);
+        ap[0] = hi;
+        ap[N] = hi;
+        ap[2 * N] = mid;
+        ap[3 * N] = hi;
+        ap[4 * N] = lo;
+        ap[5 * N] = mid;
+      }
     }
+    if (!kDxHere)  // zero padding of the plane row
+      for (int c = 6 * N + q; c < a.kp; c += kLpt) ((bf16 *)a.aplanes)[tt * a.kp + c] = (bf16)0.f;
   }
   __syncthreads();
   // bias partial of the block: sum over its tokens of dL/dh, in token order
@@ -609,6 +626,7 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
     for (int u = 0; u < nt; ++u) b += lg.at(u, j);
     a.bpart[(t0 / kRouterTokens) * N + j] = b;
   }
+  if (!kDxHere) return;
   // dx: lane = token of the block; wave w takes the column groups w, w + W,
   // ... of kBwdWrCols columns.  With the logits in LDS the wave first copies
   // its group's W_r rows to its own LDS region (each lane then reads them as
@@ -673,7 +691,7 @@ __global__ __launch_bounds__(kRBThreads) void router_bwd_bf16_kernel(const Route
       router_contract_bf16<kLds>((const bf16 *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, sm);
   static_assert(kRouterTokens * (kRouterChunk + 1) + bwd_lds_floats<kRBThreads>() <= kRouterSmem / 4,
                 "logit rows + backward scratch fit the staging area");
-  router_bwd_epilogue<bf16, kRBThreads, kLds>(lg, nt, t0, a,
+  router_bwd_epilogue<bf16, kRBThreads, kLds, false>(lg, nt, t0, a,
                                               (float *)sm.stage + kRouterTokens * (kRouterChunk + 1));
 }
 
@@ -686,7 +704,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bwd_f32_kernel(const Ro
   const LogitRows<kLds> lg =
       router_contract_f32<kLds>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, s_lg, s_x);
   __shared__ __attribute__((aligned(16))) float s_extra[bwd_lds_floats<kRouterThreads>()];
-  router_bwd_epilogue<float, kRouterThreads, kLds>(lg, nt, t0, a, s_extra);
+  router_bwd_epilogue<float, kRouterThreads, kLds, true>(lg, nt, t0, a, s_extra);
 }
 
 // dW_r = sum_t dh_t x_t^T for fp32 layers: workgroup (j tile, k tile, split
@@ -782,6 +800,13 @@ hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st, LaunchMarks
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark("bwd_router");
+  if (a.dtype == kBF16) {
+    RouterDxArgs rd{a.T, a.d, a.N, a.kp, a.w_r, a.aplanes, a.bplanes, a.dxe, a.dropped,
+                    a.add_residual ? a.dy : nullptr, a.dx};
+    for (int r = reps(); r > 0 && e == hipSuccess; --r) e = launch_router_dx_bf16(rd, st);
+    if (e != hipSuccess) return e;
+  }
+  mark("bwd_router_dx");
   const WgradSplit sp = router_wgrad_split(a.T, a.N, a.d);
   for (int r = reps(); r > 0 && e == hipSuccess; --r) {
     if (a.dtype == kBF16) {
