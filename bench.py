@@ -236,6 +236,38 @@ def backward_bench(smx, torch, inp, out, ws, C, cfg, stream, steps: int) -> dict
                         for k, v in kern.items()}}
 
 
+def top2_bench(smx, torch, inp, cfg, stream, steps: int) -> dict:
+    """Classic top-2 routing on the same workload (switch_topk_layer_forward,
+    capacity from 2 T so that both routes have room): whole-call time."""
+    T, d, f, N = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts
+    dev = inp["x"].device
+    C2 = smx.capacity(2 * T, N, cfg.capacity_factor)
+    shape2 = smx.binding.make_shape(T, d, f, N, C2, cfg.torch_dtype)
+    ws2 = torch.empty(smx.topk_workspace_bytes(shape2, 2), dtype=torch.uint8, device=dev)
+    out2 = smx.binding._route_outputs(T, N, dev, 2)
+    out2["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
+    call2 = lambda: smx.topk_layer_forward(inp["x"], inp["w_router"], inp["router_bias"],  # noqa: E731
+                                           inp["w_in"], inp["w_out"], C2, 2, workspace=ws2, out=out2)
+    with torch.cuda.stream(stream):
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < MIN_WARMUP_S:
+            for _ in range(20):
+                call2()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            call2()
+        b.record(stream)
+        torch.cuda.synchronize()
+    ms2 = a.elapsed_time(b) / steps
+    kept2 = int(sum(min(int(c), C2) for c in out2["expert_count"].cpu().tolist()))
+    log(f"bench: top-2 layer {ms2:.4f} ms ({T / (ms2 * 1e-3) / 1e6:.2f} Mtok/s)")
+    return {"ms": round(ms2, 4), "tokens_per_s": round(T / (ms2 * 1e-3), 1), "capacity": C2,
+            "route_drop_rate": round(float(out2["dropped"].float().mean().item()), 5),
+            "ffn_tflop_per_s_whole_call": round(4.0 * kept2 * d * f / (ms2 * 1e-3) / 1e12, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,9 +275,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", default="base", help="workload (the metric is quoted on 'base')")
+    ap.add_argument("--sections", default="stages,top2,backward",
+                    help="extra measurements after the layer forward: any of stages, top2, backward")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
+    sections = set(filter(None, args.sections.split(",")))
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -336,12 +371,14 @@ def main() -> int:
     beta = torch.zeros(d, device=dev)
     ystage = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
     stage_ms = {}
+    stage_fns = () if "stages" not in sections else (
+        ("dispatch", lambda: smx.dispatch(inp["x"], out["expert_idx"], out["slot"], out["dropped"], N, C,
+                                          out=disp)),
+        ("combine", lambda: smx.combine(disp, out["expert_idx"], out["slot"], out["dropped"], out["gate"],
+                                        out=ystage)),
+        ("add_norm", lambda: smx.add_norm(inp["x"], out["y"], gamma, beta, 1e-6, out=ystage)))
     with torch.cuda.stream(stream):
-        for name, fn in (("dispatch", lambda: smx.dispatch(inp["x"], out["expert_idx"], out["slot"], out["dropped"],
-                                                           N, C, out=disp)),
-                         ("combine", lambda: smx.combine(disp, out["expert_idx"], out["slot"], out["dropped"],
-                                                         out["gate"], out=ystage)),
-                         ("add_norm", lambda: smx.add_norm(inp["x"], out["y"], gamma, beta, 1e-6, out=ystage))):
+        for name, fn in stage_fns:
             fn()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -359,40 +396,15 @@ def main() -> int:
                          "hbm_frac": round(stage_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                      for k, v in stage_ms.items()}
     log("bench: stage kernels " + ", ".join(f"{k}={v['GBps']} GB/s" for k, v in stage_kernels.items()))
-    # classic top-2 routing on the same workload (switch_topk_layer_forward,
-    # capacity from 2 T so that both routes have room): whole-call time
-    C2 = smx.capacity(2 * T, N, cfg.capacity_factor)
-    shape2 = smx.binding.make_shape(T, d, f, N, C2, cfg.torch_dtype)
-    ws2 = torch.empty(smx.topk_workspace_bytes(shape2, 2), dtype=torch.uint8, device=dev)
-    out2 = smx.binding._route_outputs(T, N, dev, 2)
-    out2["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
-    call2 = lambda: smx.topk_layer_forward(inp["x"], inp["w_router"], inp["router_bias"],  # noqa: E731
-                                           inp["w_in"], inp["w_out"], C2, 2, workspace=ws2, out=out2)
-    with torch.cuda.stream(stream):
-        t_warm = time.perf_counter()
-        while time.perf_counter() - t_warm < MIN_WARMUP_S:
-            for _ in range(20):
-                call2()
-            torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(args.steps):
-            call2()
-        b.record(stream)
-        torch.cuda.synchronize()
-    ms2 = a.elapsed_time(b) / args.steps
-    kept2 = int(sum(min(int(c), C2) for c in out2["expert_count"].cpu().tolist()))
-    top2 = {"ms": round(ms2, 4), "tokens_per_s": round(T / (ms2 * 1e-3), 1), "capacity": C2,
-            "route_drop_rate": round(float(out2["dropped"].float().mean().item()), 5),
-            "ffn_tflop_per_s_whole_call": round(4.0 * kept2 * d * f / (ms2 * 1e-3) / 1e12, 1)}
-    log(f"bench: top-2 layer {ms2:.4f} ms ({T / (ms2 * 1e-3) / 1e6:.2f} Mtok/s)")
-    del ws2, out2
+    top2 = top2_bench(smx, torch, inp, cfg, stream, args.steps) if "top2" in sections else None
     # backward pass of the same step (switch_layer_backward on the forward's
     # routing and saved workspace; dy ~ N(0, 1), d_aux = 0.01): whole-call
     # time, then each kernel bracketed by events as for the forward
-    bwd = backward_bench(smx, torch, inp, out, ws, C, cfg, stream, args.steps)
-    log("bench: backward " + f"{bwd['ms']:.4f} ms; per-kernel ms " +
-        ", ".join(f"{k}={v['ms']:.4f}" for k, v in bwd["kernels"].items()))
+    bwd = None
+    if "backward" in sections:
+        bwd = backward_bench(smx, torch, inp, out, ws, C, cfg, stream, args.steps)
+        log("bench: backward " + f"{bwd['ms']:.4f} ms; per-kernel ms " +
+            ", ".join(f"{k}={v['ms']:.4f}" for k, v in bwd["kernels"].items()))
     per_kernel = {}
     for k, v in kern.items():
         b = algorithmic_bytes(k, T, d, f, N, C, counts)

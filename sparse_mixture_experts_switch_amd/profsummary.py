@@ -41,7 +41,9 @@ KERNEL_KEYS = {
     "bwd_dw_out": ("bwd_gemm_bf16_kernel", "Lb1ELb1ELb1ELb1ELb0ELi2E"),
     "bwd_dw_in": ("bwd_gemm_bf16_kernel", "Lb1ELb0ELb0ELb1ELb1ELi2E"),
     "bwd_router": ("router_bwd_bf16_kernel", ""),
-    "bwd_router_w": ("router_wgrad_kernel", ""),
+    "bwd_router_dx": ("bwd_gemm_bf16_kernel", "Lb0ELb0ELb0ELb1ELb0ELi3E"),
+    "bwd_router_planes": ("router_wr_planes_kernel", ""),
+    "bwd_router_w": ("router_wgrad_bf16_kernel", ""),
     "bwd_router_w_sum": ("router_wgrad_sum_kernel", ""),
     "copy": ("__amd_rocclr_copyBuffer", ""),
 }
