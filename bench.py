@@ -268,6 +268,55 @@ def top2_bench(smx, torch, inp, cfg, stream, steps: int) -> dict:
             "ffn_tflop_per_s_whole_call": round(4.0 * kept2 * d * f / (ms2 * 1e-3) / 1e12, 1)}
 
 
+def mfma_diag_bench(smx, torch, cfg, stream, steps: int) -> dict:
+    """Unranked diagnostic of the expert FFN's matrix-core use: the same
+    dimensions with 4x the tokens (512 per expert, capacity 640), where each
+    weight byte feeds more multiply-adds than the HBM/MFMA ridge (~315 flop/B)
+    and the grouped GEMMs are bound by MFMA rather than by the weight stream.
+    ffn_up / ffn_down are timed live by the event split of the layer call."""
+    from sparse_mixture_experts_switch_amd.inputs import make_inputs
+    dcfg = cfg.with_(name="mfma_diag", tokens=4 * cfg.tokens)
+    dev = torch.device("cuda:0")
+    inp = make_inputs(dcfg, device=dev)
+    T, d, f, N = dcfg.tokens, dcfg.d_model, dcfg.d_ff, dcfg.num_experts
+    C = smx.capacity(T, N, dcfg.capacity_factor)
+    shape = smx.binding.make_shape(T, d, f, N, C, dcfg.torch_dtype)
+    ws = torch.empty(smx.workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = smx.binding._route_outputs(T, N, dev)
+    out["y"] = torch.empty(T, d, dtype=dcfg.torch_dtype, device=dev)
+    names = smx.launch_names(shape)
+    part = lambda lo, hi: smx.layer_forward_profiled(  # noqa: E731
+        inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C, first_kernel=lo,
+        last_kernel=hi, workspace=ws, out=out)
+    kern = {}
+    with torch.cuda.stream(stream):
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < MIN_WARMUP_S:
+            part(0, len(names) - 1)
+            torch.cuda.synchronize()
+        for i, name in enumerate(names):
+            if name not in ("ffn_up", "ffn_down"):
+                continue
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for e0, e1 in evs:
+                part(0, i - 1)
+                e0.record(stream)
+                part(i, i)
+                e1.record(stream)
+                if i < len(names) - 1:
+                    part(i + 1, len(names) - 1)
+            torch.cuda.synchronize()
+            kern[name] = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    kept = sum(min(int(c), C) for c in out["expert_count"].cpu().tolist())
+    ffn_ms = kern["ffn_up"] + kern["ffn_down"]
+    tflops = 4.0 * kept * d * f / (ffn_ms * 1e-3) / 1e12
+    log(f"bench: MFMA diagnostic ({T} tokens, capacity {C}): ffn {ffn_ms:.4f} ms, {tflops:.1f} TFLOP/s")
+    return {"tokens": T, "capacity": C, "ffn_up_ms": round(kern["ffn_up"], 5),
+            "ffn_down_ms": round(kern["ffn_down"], 5), "ffn_tflop_per_s": round(tflops, 1),
+            "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "note": "unranked: 512 tokens per expert puts the expert FFN above the HBM/MFMA ridge"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,8 +324,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", default="base", help="workload (the metric is quoted on 'base')")
-    ap.add_argument("--sections", default="stages,top2,backward",
-                    help="extra measurements after the layer forward: any of stages, top2, backward")
+    ap.add_argument("--sections", default="stages,top2,mfma_diag,backward",
+                    help="extra measurements after the layer forward: any of stages, top2, mfma_diag, backward")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -332,6 +381,27 @@ def main() -> int:
     ms = start.elapsed_time(stop) / args.steps
     counts = out["expert_count"].cpu().tolist()
     drop_rate = float(out["dropped"].float().mean().item())
+
+    # cold-cache steps: before each, a 1 GiB read evicts L2 and the 256 MB
+    # MALL (a read leaves clean lines; a fill would leave ~290 MB of dirty
+    # lines whose write-back the next step would pay); events bracket the
+    # layer call only.  The back-to-back figure above is the headline: each
+    # step streams 1.2 GB of expert weights, far more than the caches hold, so
+    # only x, W_r and the small arrays can stay warm.
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            scratch.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            cold.append((e0, e1))
+        torch.cuda.synchronize()
+    ms_cold = sum(a.elapsed_time(b) for a, b in cold) / args.steps
+    del scratch
+    log(f"bench: cold-cache step {ms_cold:.4f} ms (back-to-back {ms:.4f} ms)")
 
     # per-kernel durations, live: K more ordinary steps in which HIP events
     # (on the layer's stream) bracket kernel i alone -- kernels 0..i-1, event,
@@ -400,6 +470,7 @@ def main() -> int:
     # backward pass of the same step (switch_layer_backward on the forward's
     # routing and saved workspace; dy ~ N(0, 1), d_aux = 0.01): whole-call
     # time, then each kernel bracketed by events as for the forward
+    diag = mfma_diag_bench(smx, torch, cfg, stream, args.steps) if "mfma_diag" in sections else None
     bwd = None
     if "backward" in sections:
         bwd = backward_bench(smx, torch, inp, out, ws, C, cfg, stream, args.steps)
@@ -448,8 +519,11 @@ def main() -> int:
         "kernels": per_kernel,
         "stage_kernels": stage_kernels,
         "top2": top2,
+        "mfma_diagnostic": diag,
         "backward": bwd,
         "wall_s_timed": round(t_wall, 4),
+        "cold_cache": {"ms_per_step": round(ms_cold, 4), "tokens_per_s": round(T / (ms_cold * 1e-3), 1),
+                       "note": "each step after a 1 GiB read (L2 and MALL evicted); events around the layer only"},
     }
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -704,7 +704,7 @@ namespace {
 // (contraction = an expert's rows, short).
 constexpr int kRowMBW = 5, kRowNBW = 4, kRowWM = 2, kRowWN = 4;
 constexpr int kDxNBW = 2;  // DX: 128 columns per tile (d_model / 128 tiles per expert)
-constexpr int kWgtMBW = 4, kWgtNBW = 4, kWgtWM = 2, kWgtWN = 2;
+constexpr int kWgtMBW = 4, kWgtNBW = 4, kWgtWM = 1, kWgtWN = 4;
 constexpr int kBNb = kRowWN * kRowNBW * 16, kBNdx = kRowWN * kDxNBW * 16;
 
 template <typename T_>
