@@ -24,11 +24,14 @@
 // loads give a lane its 8 contraction values.
 //
 // One workgroup computes one (expert, row tile, column tile); both operands
-// pass through a double-buffered LDS tile (registers prefetch the next
-// 64-wide contraction chunk while the MFMAs consume the current one).  Rows
-// of an expert past its kept count are never stored; contraction rows past it
-// (DWO / DWI) are zero, so an expert with no kept token gets exact zero
-// gradients.  Results are deterministic: fixed tiles, fixed reduction order.
+// pass through LDS (double-buffered with a two-deep register prefetch for the
+// long contractions, single-buffered with several workgroups per CU for the
+// weight gradients).  Rows of an expert past its kept count are never stored;
+// contraction rows past it (DWO / DWI) are zero, so an expert with no kept
+// token gets exact zero gradients.  The router's matrix products of the
+// backward (W_r^T dL/dh and dW_r) are here too, on exact bf16 plane splits of
+// their fp32 operands.  Results are deterministic: fixed tiles, fixed
+// reduction order.
 
 #include <type_traits>
 
@@ -803,9 +806,8 @@ hipError_t launch_bwd_experts(const BwdLaunch &L, hipStream_t st, LaunchMarks ma
   const int64_t ein = (int64_t)f * d;  // elements of one expert's W_in / W_out
   const int64_t eh = (int64_t)C * f;   // elements of one expert's H / DU rows
   hipError_t e = hipSuccess;
-  if (L.C == 0 || L.N == 0) {
-    // no kept rows: the weight gradients are zero, nothing else runs
-  }
+  // with no kept rows (C = 0) the row-tiled products launch no tile and the
+  // weight-gradient tiles write zeros
   if (L.dtype == kBF16) {
     const int bm_rows = kRowWM * kRowMBW * 16, bm_w = kWgtWM * kWgtMBW * 16, bn_w = kWgtWN * kWgtNBW * 16;
     // DZ: A = dy rows through tok (k-contiguous), B = W_out,e [d][d_ff] (k-major)

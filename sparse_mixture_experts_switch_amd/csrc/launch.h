@@ -165,8 +165,10 @@ hipError_t launch_bwd_experts(const BwdLaunch &a, hipStream_t st, LaunchMarks ma
 
 // Router part of the backward (router.hip): recomputes the logits, forms
 // dL/dh (softmax Jacobian of dL/dp = d_aux N f / T + [kept, chosen] dL/dg),
-// writes dh and the whole dx; then dW_r and the bias gradient by a split sum
-// over tokens.
+// writes dh and the bias partials, and the whole dx (fp32 layers: in the
+// same kernel; bf16 layers: the exact bf16 planes of dL/dh, then the MFMA dx
+// product of backward.hip); then dW_r by a split sum over tokens and the
+// ordered sums of the partials.
 struct RouterBwdArgs {
   int dtype;
   int64_t T;
