@@ -629,9 +629,9 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
   if (!kDxHere) return;
   // dx (fp32 layers): lane = token of the block; wave w takes the column
   // groups w, w + W, ... of kBwdWrCols columns.  With the logits in LDS the
-  // wave first copies
-  // its group's W_r rows to its own LDS region (each lane then reads them as
-  // broadcasts); otherwise the W_r values come straight from memory.
+  // wave first copies its group's W_r rows to its own LDS region (each lane
+  // then reads them as broadcasts); otherwise the W_r values come straight
+  // from memory.
   const int lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int tl = min(lane, nt - 1);
