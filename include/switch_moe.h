@@ -250,6 +250,20 @@ int switch_layer_backward_profiled(const switch_shape *s, const void *x, const f
                                    void *workspace, size_t workspace_bytes, void *stream, int32_t first_kernel,
                                    int32_t last_kernel, int32_t times);
 
+/* Combine and the block's Add + Normalize in one pass (stage API; the
+ * write-up's block figure puts "Add + Normalize" right after the combine):
+ *   out[t] = LayerNorm(x[t] + y[t]),  y[t] = gate[t] * expert_out[expert_idx[t]][slot[t]]
+ * (y[t] = 0 for a dropped token), with the statistics and the
+ * definitions of switch_add_norm.  The sum is formed in fp32 from the expert
+ * output and rounded once (switch_combine followed by switch_add_norm
+ * rounds y first).  Arguments as switch_combine (expert_out [N][C][d], the
+ * routing arrays [T]) plus x [T][d] (required), gamma, beta [d] fp32, eps;
+ * out [T][d] must not overlap the inputs.  SWITCH_E_UNSUPPORTED for d_model
+ * above 4096 (bf16) / 2048 (fp32). */
+int switch_combine_add_norm(const switch_shape *s, const void *expert_out, const int32_t *expert_idx,
+                            const int32_t *slot, const uint8_t *dropped, const float *gate, const void *x,
+                            const float *gamma, const float *beta, float eps, void *out, void *stream);
+
 /* Measurement variant of switch_layer_forward: same arguments and
  * asynchrony, but it launches only the kernels numbered first_kernel ..
  * last_kernel of the call (0-based, in the order switch_launch_names gives),

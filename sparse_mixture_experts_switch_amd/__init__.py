@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     backward_workspace_bytes,
     capacity,
     combine,
+    combine_add_norm,
     dispatch,
     expert_ffn,
     layer_backward,

@@ -18,7 +18,7 @@ __all__ = [
     "SwitchError", "load_library", "capacity", "workspace_bytes", "route", "dispatch",
     "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "launch_names", "add_norm",
     "topk_workspace_bytes", "topk_layer_forward", "backward_workspace_bytes", "layer_backward",
-    "layer_backward_profiled", "BACKWARD_KERNELS", "SWITCH_F32", "SWITCH_BF16",
+    "layer_backward_profiled", "BACKWARD_KERNELS", "combine_add_norm", "SWITCH_F32", "SWITCH_BF16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswitchmoe.so")
@@ -32,6 +32,7 @@ EXPORTED = [
     "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
     "switch_launch_names", "switch_add_norm", "switch_topk_workspace_bytes", "switch_topk_layer_forward",
     "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
+    "switch_combine_add_norm",
 ]
 BACKWARD_KERNELS = ["bwd_dz", "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
                     "bwd_router_w_sum"]
@@ -78,6 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                                ctypes.c_int32])
     lib.switch_launch_names.argtypes = [sp, _P, ctypes.c_int32, _P]
     lib.switch_add_norm.argtypes = [sp, _P, _P, _P, _P, ctypes.c_float, _P, _P]
+    lib.switch_combine_add_norm.argtypes = [sp] + [_P] * 8 + [ctypes.c_float, _P, _P]
     lib.switch_topk_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     bwd = [sp, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, sz, _P, ctypes.c_float] + [_P] * 6 + [sz, _P]
     lib.switch_backward_workspace_bytes.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
@@ -340,6 +342,20 @@ def layer_backward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, fw
     o, args = _bwd_args(x, w_router, router_bias, w_in, w_out, capacity_, fwd, fwd_workspace, dy, d_aux,
                         add_residual, workspace, out)
     _check(load_library().switch_layer_backward_profiled(*args, int(first_kernel), int(last_kernel), int(times)))
+    return o
+
+
+def combine_add_norm(expert_out: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tensor,
+                     dropped: torch.Tensor, gate: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor,
+                     beta: torch.Tensor, eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
+    """LayerNorm(x + combine) in one pass (switch_combine_add_norm)."""
+    N, C, d = expert_out.shape
+    T = expert_idx.shape[0]
+    shape = make_shape(T, d, 64, N, C, expert_out.dtype)
+    o = out if out is not None else torch.empty(T, d, dtype=expert_out.dtype, device=expert_out.device)
+    _check(load_library().switch_combine_add_norm(
+        ctypes.byref(shape), _ptr(expert_out), _ptr(expert_idx), _ptr(slot), _ptr(dropped), _ptr(gate), _ptr(x),
+        _ptr(gamma), _ptr(beta), float(eps), _ptr(o), _stream(expert_out.device)))
     return o
 
 

@@ -548,9 +548,37 @@ int switch_add_norm(const switch_shape *s, const void *x, const void *y, const f
       NEED(beta, 4);
       if (x && !aligned(x, 16)) return fail(SWITCH_E_INVALID, "x is not 16-byte aligned");
     }
-    AddNormArgs a{s->dtype, s->tokens, s->d_model, x, y, gamma, beta, eps, out};
+    AddNormArgs a{s->dtype, s->tokens, s->d_model, x, y, gamma, beta, eps, out, CombineRows{}};
     hipError_t e = launch_add_norm(a, (hipStream_t)stream);
     return e == hipSuccess ? SWITCH_OK : hip_fail(e, "add_norm launch");
+  })
+}
+
+int switch_combine_add_norm(const switch_shape *s, const void *expert_out, const int32_t *expert_idx,
+                            const int32_t *slot, const uint8_t *dropped, const float *gate, const void *x,
+                            const float *gamma, const float *beta, float eps, void *out, void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(SWITCH_E_INVALID, "eps = %g: need a finite eps >= 0", eps);
+    if (s->d_model > add_norm_max_d(s->dtype))
+      return fail(SWITCH_E_UNSUPPORTED, "d_model = %d above %d for add_norm", s->d_model,
+                  add_norm_max_d(s->dtype));
+    if (s->tokens > 0) {
+      NEED(x, 16);
+      NEED(out, 16);
+      NEED(expert_idx, 4);
+      NEED(slot, 4);
+      NEED(gate, 4);
+      NEED(gamma, 4);
+      NEED(beta, 4);
+      if (!dropped) return fail(SWITCH_E_INVALID, "dropped is NULL");
+      if (s->capacity > 0) NEED(expert_out, 16);
+    }
+    CombineRows rows{expert_idx, slot, dropped, gate, s->capacity};
+    AddNormArgs a{s->dtype, s->tokens, s->d_model, x, expert_out, gamma, beta, eps, out, rows};
+    hipError_t e = launch_add_norm(a, (hipStream_t)stream);
+    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "combine_add_norm launch");
   })
 }
 

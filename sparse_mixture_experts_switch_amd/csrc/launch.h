@@ -72,15 +72,24 @@ struct CombineArgs {
   void *y;
 };
 
+// Rows of the stage API's combine (gate * expert_out[e][slot], 0 if dropped).
+struct CombineRows {
+  const int32_t *expert_idx = nullptr, *slot = nullptr;
+  const uint8_t *dropped = nullptr;
+  const float *gate = nullptr;
+  int C = 0;
+};
+
 struct AddNormArgs {
   int dtype;
   int64_t T;
   int d;
   const void *x;  // may be null
-  const void *y;
+  const void *y;  // [T][d], or expert_out [N][C][d] when rows.expert_idx is set
   const float *gamma, *beta;
   float eps;
-  void *out;  // may equal y
+  void *out;  // may equal y (dense rows only)
+  CombineRows rows;
 };
 
 // One grouped GEMM of the expert FFN (see ffn.hip).

@@ -95,16 +95,29 @@ static inline int esize(int dtype) { return dtype == kBF16 ? 2 : 4; }
 // per lane), the mean and then the sum of squared deviations are each summed
 // per lane in order and across the wave by fixed-order butterflies, so every
 // run gives the same bits.  One rounding to the output type.
-template <typename T_, int P>
+// With kCombine the row y[t] is the combine of the layer's stage API instead
+// of a dense row: gate[t] * expert_out[expert_idx[t]][slot[t]] for a kept
+// token, 0 for a dropped one, so that the block's output LayerNorm(x + y)
+// is formed from the expert output in one pass (fp32 throughout, one
+// rounding).
+template <typename T_, int P, bool kCombine>
 __global__ __launch_bounds__(kMoveThreads) void add_norm_kernel(const u32x4 *__restrict__ x, const u32x4 *y,
                                                                const float *__restrict__ gamma,
                                                                const float *__restrict__ beta, float eps,
-                                                               u32x4 *out, int64_t T, int d) {
+                                                               u32x4 *out, int64_t T, int d, CombineRows cr) {
   constexpr int kE = 16 / sizeof(T_);  // values per 16-byte piece
   const int64_t t = (int64_t)blockIdx.x * kMoveTokens + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (t >= T) return;
   const int pieces = d / kE;
+  bool keep = true;
+  float g = 1.f;
+  const u32x4 *yrow = y + t * pieces;
+  if (kCombine) {
+    keep = !cr.dropped[t];
+    g = keep ? cr.gate[t] : 0.f;
+    yrow = y + (keep ? (int64_t)cr.expert_idx[t] * cr.C + cr.slot[t] : 0) * pieces;
+  }
   float v[P][kE];
   float sum = 0.f;
 #pragma unroll
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(kMoveThreads) void add_norm_kernel(const u32x4 *__r
     const int c = lane + i * kWave;
     const bool in = c < pieces;
     const int cc = in ? c : 0;
-    const u32x4 yv = y[t * pieces + cc];
+    const u32x4 yv = keep ? yrow[cc] : u32x4{0, 0, 0, 0};
     const u32x4 xv = x ? x[t * pieces + cc] : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < kE; ++k) {
@@ -124,7 +137,7 @@ __global__ __launch_bounds__(kMoveThreads) void add_norm_kernel(const u32x4 *__r
         a = __builtin_bit_cast(f32x4, yv)[k];
         b = __builtin_bit_cast(f32x4, xv)[k];
       }
-      v[i][k] = in ? a + b : 0.f;
+      v[i][k] = in ? (kCombine ? b + g * a : a + b) : 0.f;
       sum += v[i][k];
     }
   }
@@ -162,8 +175,13 @@ __global__ __launch_bounds__(kMoveThreads) void add_norm_kernel(const u32x4 *__r
 
 template <typename T_, int P>
 hipError_t run_add_norm(const AddNormArgs &a, hipStream_t st) {
-  add_norm_kernel<T_, P><<<dim3((unsigned)ceil_div(a.T, kMoveTokens)), dim3(kMoveThreads), 0, st>>>(
-      (const u32x4 *)a.x, (const u32x4 *)a.y, a.gamma, a.beta, a.eps, (u32x4 *)a.out, a.T, a.d);
+  const dim3 grid((unsigned)ceil_div(a.T, kMoveTokens)), block(kMoveThreads);
+  if (a.rows.expert_idx)
+    add_norm_kernel<T_, P, true><<<grid, block, 0, st>>>((const u32x4 *)a.x, (const u32x4 *)a.y, a.gamma, a.beta,
+                                                         a.eps, (u32x4 *)a.out, a.T, a.d, a.rows);
+  else
+    add_norm_kernel<T_, P, false><<<grid, block, 0, st>>>((const u32x4 *)a.x, (const u32x4 *)a.y, a.gamma,
+                                                          a.beta, a.eps, (u32x4 *)a.out, a.T, a.d, a.rows);
   return hipGetLastError();
 }
 

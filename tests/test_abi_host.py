@@ -130,6 +130,14 @@ def test_entry_points_reject_before_launch():
     wide = B.make_shape(64, 8192, 256, 8, 16, torch.bfloat16)
     assert lib.switch_add_norm(ctypes.byref(wide), good, good, good, good, 1e-6, good, None) == \
         B.SWITCH_E_UNSUPPORTED
+    # combine_add_norm: NULL x, misaligned out, non-finite eps
+    rc = lib.switch_combine_add_norm(ctypes.byref(s), good, good, good, good, good, None, good, good, 1e-6, good, None)
+    assert rc == B.SWITCH_E_INVALID
+    rc = lib.switch_combine_add_norm(ctypes.byref(s), good, good, good, good, good, good, good, good, 1e-6, odd, None)
+    assert rc == B.SWITCH_E_INVALID
+    rc = lib.switch_combine_add_norm(ctypes.byref(s), good, good, good, good, good, good, good, good,
+                                     float("inf"), good, None)
+    assert rc == B.SWITCH_E_INVALID
     # profiled: empty kernel range / times < 1
     for first, last, times in ((0, 0, 0), (2, 1, 1), (-1, 0, 1)):
         rc = lib.switch_layer_forward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good,

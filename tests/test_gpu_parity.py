@@ -286,3 +286,41 @@ def test_add_norm_after_layer(dtype):
     np.testing.assert_allclose(only_y, so.add_normalize(np.zeros_like(y), y, ga, be, eps),
                                atol=1e-4, rtol=2 * rnd)
     say(f"  add_norm {dtype}: max err {err.max():.3e} (vs fed), {err2.max():.3e} (end to end)")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_combine_add_norm_stage(dtype):
+    """Combine and the block's Add + Normalize in one pass on the stage API:
+    route -> dispatch -> expert FFN -> switch_combine_add_norm, against the
+    oracle's layer normalisation of x + combine(expert_out) fed the GPU's
+    expert outputs, gates and routing (the fused kernel's arithmetic alone),
+    with drops; and close to the unfused combine then add_norm."""
+    cfg = SMALL.with_(name=f"combine_add_norm_{dtype}", dtype=dtype, tokens=901, d_model=192,
+                      capacity_factor=0.5)
+    inp = make_inputs(cfg, device=DEV)
+    C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+    r = smx.route(inp["x"], inp["w_router"], inp["router_bias"], C)
+    disp = smx.dispatch(inp["x"], r["expert_idx"], r["slot"], r["dropped"], cfg.num_experts, C)
+    eo = smx.expert_ffn(disp, r["expert_count"], inp["w_in"], inp["w_out"])
+    gen = torch.Generator().manual_seed(7)
+    gamma = (1.0 + 0.1 * torch.randn(cfg.d_model, generator=gen)).to(DEV)
+    beta = (0.1 * torch.randn(cfg.d_model, generator=gen)).to(DEV)
+    eps = 1e-5
+    fused = smx.combine_add_norm(eo, r["expert_idx"], r["slot"], r["dropped"], r["gate"], inp["x"], gamma, beta, eps)
+    again = smx.combine_add_norm(eo, r["expert_idx"], r["slot"], r["dropped"], r["gate"], inp["x"], gamma, beta,
+                                 eps)
+    y = smx.combine(eo, r["expert_idx"], r["slot"], r["dropped"], r["gate"])
+    unfused = smx.add_norm(inp["x"], y, gamma, beta, eps)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, again)
+    g = gpu_outputs_numpy(r)
+    assert g["dropped"].any() and not g["dropped"].all()
+    ybare = so.combine(f64(eo), g["expert_idx"], g["slot"], g["dropped"], r["gate"].cpu().double().numpy())
+    ref = so.add_normalize(f64(inp["x"]), ybare, f64(gamma), f64(beta), eps)
+    rnd = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    got = f64(fused)
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-5 + rnd * np.abs(ref)), err.max()
+    # the unfused path rounds y once more before the sum
+    np.testing.assert_allclose(f64(unfused), got, atol=1e-4, rtol=2 * rnd)
+    say(f"  combine_add_norm {dtype}: max err {err.max():.3e} vs fed oracle; drops {int(g['dropped'].sum())}")
