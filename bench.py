@@ -440,13 +440,22 @@ def main() -> int:
     gamma = torch.ones(d, device=dev)
     beta = torch.zeros(d, device=dev)
     ystage = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
+    rstage = {k: torch.empty_like(v) for k, v in out.items() if k != "y"}
     stage_ms = {}
     stage_fns = () if "stages" not in sections else (
         ("dispatch", lambda: smx.dispatch(inp["x"], out["expert_idx"], out["slot"], out["dropped"], N, C,
                                           out=disp)),
         ("combine", lambda: smx.combine(disp, out["expert_idx"], out["slot"], out["dropped"], out["gate"],
                                         out=ystage)),
-        ("add_norm", lambda: smx.add_norm(inp["x"], out["y"], gamma, beta, 1e-6, out=ystage)))
+        ("add_norm", lambda: smx.add_norm(inp["x"], out["y"], gamma, beta, 1e-6, out=ystage)),
+        ("combine_add_norm", lambda: smx.combine_add_norm(disp, out["expert_idx"], out["slot"], out["dropped"],
+                                                          out["gate"], inp["x"], gamma, beta, 1e-6, out=ystage)),
+        # routing alone (router + assignment), and routing with the dispatch
+        # copy in one pass over x (its workspace's ordering state is cleared
+        # by a small kernel inside each call)
+        ("route", lambda: smx.route(inp["x"], inp["w_router"], inp["router_bias"], C, workspace=ws, out=rstage)),
+        ("route_dispatch", lambda: smx.route_dispatch(inp["x"], inp["w_router"], inp["router_bias"], C,
+                                                      workspace=ws, out=rstage, dispatched=disp)))
     with torch.cuda.stream(stream):
         for name, fn in stage_fns:
             fn()
@@ -460,7 +469,12 @@ def main() -> int:
             stage_ms[name] = a.elapsed_time(b) / args.steps
     stage_bytes = {"dispatch": 2 * kept * d * 2 + T * 9,          # read kept x rows, write them; idx/slot/drop
                    "combine": kept * d * 2 + T * d * 2 + T * 13,  # read kept rows, write every y row; + gate
-                   "add_norm": 3 * T * d * 2 + 2 * d * 4}         # read x and y, write the block output
+                   "add_norm": 3 * T * d * 2 + 2 * d * 4,         # read x and y, write the block output
+                   # read kept expert rows and x, write the block output; + gate and routing
+                   "combine_add_norm": kept * d * 2 + 2 * T * d * 2 + 2 * d * 4 + T * 13,
+                   # read x and W_r, write expert_idx, gate, slot, dropped (+ the kept rows)
+                   "route": T * d * 2 + N * d * 4 + T * 13 + N * 8,
+                   "route_dispatch": T * d * 2 + N * d * 4 + T * 13 + N * 8 + kept * d * 2}
     stage_kernels = {k: {"ms": round(v, 5), "alg_bytes": stage_bytes[k],
                          "GBps": round(stage_bytes[k] / (v * 1e-3) / 1e9, 1),
                          "hbm_frac": round(stage_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -113,6 +113,28 @@ int switch_route(const switch_shape *s, const void *x, const float *w_router, co
 int switch_dispatch(const switch_shape *s, const void *x, const int32_t *expert_idx, const int32_t *slot,
                     const uint8_t *dropped, void *dispatched, void *stream);
 
+/* Routing and dispatch in one pass over x (the router, "Expert Capacity and
+ * the Capacity Factor" and "The Load-Balancing Loss" of the Switch
+ * Transformers write-up): the outputs of switch_route followed by
+ * switch_dispatch, from a single kernel that reads each row of x once.  Every
+ * router block assigns its own tokens' slots after adding the expert counts of
+ * the blocks before it in token order, which it finds by a look-back over
+ * their published partial results in the workspace (a small clearing kernel
+ * runs first), and copies each kept row to dispatched[expert_idx[t]][slot[t]]
+ * while the row is still in cache.  expert_idx, gate, slot, dropped,
+ * expert_count and dispatched equal those of switch_route + switch_dispatch
+ * bit for bit; aux_loss sums P_i in 2^-32 fixed point (deterministic, within
+ * 1e-6 relative of switch_route's value; NaN would report a failed internal
+ * wait, which a correct launch never reaches).  dispatched is [N][C][d] of
+ * s->dtype (may be NULL when C = 0); padding rows are left untouched.
+ * Workspace: switch_workspace_bytes(s).  SWITCH_E_UNSUPPORTED for more than
+ * 2048 experts or N x C above 2^31-1.  Two calls must not share a workspace
+ * concurrently (the same holds for every call here). */
+int switch_route_dispatch(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                          int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
+                          int32_t *expert_count, float *aux_loss, void *dispatched, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Expert FFNs ("The Core Idea": N independent FFNs; the expert form
  * E(x) = W_out ReLU(W_in x) has no biases):
  *   expert_out[i][r] = W_out,i ReLU(W_in,i dispatched[i][r])

@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     launch_names,
     load_library,
     route,
+    route_dispatch,
     topk_layer_forward,
     topk_workspace_bytes,
     workspace_bytes,

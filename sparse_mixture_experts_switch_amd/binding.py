@@ -32,7 +32,7 @@ EXPORTED = [
     "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
     "switch_launch_names", "switch_add_norm", "switch_topk_workspace_bytes", "switch_topk_layer_forward",
     "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
-    "switch_combine_add_norm",
+    "switch_combine_add_norm", "switch_route_dispatch",
 ]
 BACKWARD_KERNELS = ["bwd_dz", "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
                     "bwd_router_w_sum"]
@@ -71,6 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.switch_last_error.restype = ctypes.c_char_p
     lib.switch_route.argtypes = [sp] + [_P] * 10 + [sz, _P]
     lib.switch_dispatch.argtypes = [sp] + [_P] * 6
+    lib.switch_route_dispatch.argtypes = [sp] + [_P] * 11 + [sz, _P]
     lib.switch_expert_ffn.argtypes = [sp] + [_P] * 6 + [sz, _P]
     lib.switch_combine.argtypes = [sp] + [_P] * 8
     lib.switch_layer_forward.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P]
@@ -177,6 +178,26 @@ def route(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | N
         ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(o["expert_idx"]), _ptr(o["gate"]),
         _ptr(o["slot"]), _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]), _ptr(ws),
         ws.numel(), _stream(dev)))
+    return o
+
+
+def route_dispatch(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None, capacity_: int,
+                   workspace: torch.Tensor | None = None, out: dict | None = None,
+                   dispatched: torch.Tensor | None = None) -> dict:
+    """Routing and dispatch in one pass over x (switch_route_dispatch): the
+    outputs of route() plus o["dispatched"] [N][C][d]."""
+    T, d = x.shape
+    N = w_router.shape[0]
+    shape = make_shape(T, d, 64, N, capacity_, x.dtype)
+    dev = x.device
+    o = out if out is not None else _route_outputs(T, N, dev)
+    ws = _workspace(make_shape(T, d, 64, N, 0, x.dtype), dev, workspace)
+    buf = dispatched if dispatched is not None else torch.empty(N, capacity_, d, dtype=x.dtype, device=dev)
+    _check(load_library().switch_route_dispatch(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(o["expert_idx"]), _ptr(o["gate"]),
+        _ptr(o["slot"]), _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]),
+        _ptr(buf) if buf.numel() else None, _ptr(ws), ws.numel(), _stream(dev)))
+    o["dispatched"] = buf
     return o
 
 

@@ -56,6 +56,9 @@ int esize(int dtype) { return dtype == SWITCH_BF16 ? 2 : 4; }
 
 struct Layout {
   size_t bcount = 0, boff = 0, ppart = 0, psum = 0, rank = 0, logits = 0, route_end = 0;
+  size_t fz_sync = 0, fz_aggc = 0, fz_aggp = 0, fz_incc = 0, fz_incp = 0;  // single-pass routing
+  size_t fz_clear = 0;
+  int64_t fz_stride = 0;
   size_t ffn_hidden = 0, ffn_end = 0;                           // switch_expert_ffn alone
   size_t lf_hidden = 0, lf_tok = 0, lf_gmap = 0, total = 0;     // layer forward
   size_t lf_rows = 0, lf_routed = 0;                            // top-k layer forward (k > 1)
@@ -85,9 +88,10 @@ int layout(const switch_shape *s, Layout &L, int k = 1) {
   const int64_t T = s->tokens, N = s->num_experts, C = s->capacity, d = s->d_model, f = s->d_ff;
   const int64_t nb = router_blocks(T) * k, Tp = router_blocks(T) * kRouterTokens * k;
   const int es = esize(s->dtype);
-  size_t bc, pp, ps, rk, lg = 0, hid, act, tk, rt = 0;
-  const int64_t Np = count_stride((int)N);
+  size_t bc, pp, ps, rk, lg = 0, hid, act, tk, rt = 0, sy, r32, r64;
+  const int64_t Np = count_stride((int)N), Ns = (N + 63) / 64 * 64;
   bool ok = mul(bc, {nb, Np, 4}) && mul(pp, {nb, Np, 4}) && mul(ps, {N, 4}) && mul(rk, {Tp, 4}) &&
+            mul(sy, {nb + 4, 4}) && mul(r32, {nb, Ns, 4}) && mul(r64, {nb, Ns, 8}) &&
             (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(hid, {N, C, f, es}) && mul(act, {N, C, d, es}) &&
             mul(tk, {N, C, 4}) && (k == 1 || mul(rt, {k, T, d, es}));
   if (!ok) return fail(SWITCH_E_UNSUPPORTED, "buffer sizes overflow for this shape");
@@ -104,6 +108,18 @@ int layout(const switch_shape *s, Layout &L, int k = 1) {
   o = align_up(o + rk);
   L.logits = o;
   o = align_up(o + lg);
+  L.fz_sync = o;  // ticket, error word and block states; then the look-back rows
+  L.fz_clear = (sy + 15) / 16 * 16;
+  o = align_up(o + sy);
+  L.fz_stride = Ns;
+  L.fz_aggc = o;
+  o = align_up(o + r32);
+  L.fz_incc = o;
+  o = align_up(o + r32);
+  L.fz_aggp = o;
+  o = align_up(o + r64);
+  L.fz_incp = o;
+  o = align_up(o + r64);
   L.route_end = o;
   L.ffn_hidden = 0;
   L.ffn_end = align_up(hid);
@@ -463,6 +479,41 @@ int switch_route(const switch_shape *s, const void *x, const float *w_router, co
       return rc;
     Timer tm;
     return run_route(a, (hipStream_t)stream, tm);
+  })
+}
+
+int switch_route_dispatch(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
+                          int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
+                          int32_t *expert_count, float *aux_loss, void *dispatched, void *ws, size_t ws_bytes,
+                          void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (s->num_experts > kFusedMaxExperts)
+      return fail(SWITCH_E_UNSUPPORTED, "num_experts = %d above %d", s->num_experts, kFusedMaxExperts);
+    if ((int64_t)s->num_experts * s->capacity > INT32_MAX)
+      return fail(SWITCH_E_UNSUPPORTED, "num_experts x capacity above 2^31-1");
+    Layout L;
+    if ((rc = layout(s, L))) return rc;
+    FusedRouteArgs a;
+    if ((rc = route_args(s, x, w_router, router_bias, expert_idx, gate, slot, dropped, expert_count, aux_loss, ws,
+                         ws_bytes, L, a.r)))
+      return rc;
+    if (s->tokens > 0 && s->capacity > 0) NEED(dispatched, 16);
+    char *w = (char *)ws;
+    a.sync = (int32_t *)(w + L.fz_sync);
+    a.clear_bytes = L.fz_clear;
+    a.row_stride = L.fz_stride;
+    a.agg_c = (int32_t *)(w + L.fz_aggc);
+    a.inc_c = (int32_t *)(w + L.fz_incc);
+    a.agg_p = (int64_t *)(w + L.fz_aggp);
+    a.inc_p = (int64_t *)(w + L.fz_incp);
+    a.dispatched = s->capacity > 0 ? dispatched : nullptr;
+    Timer tm;
+    LaunchMarks marks{[](void *ctx, const char *name) { static_cast<Timer *>(ctx)->mark(name); },
+                      [](void *ctx) { return static_cast<Timer *>(ctx)->reps(); }, &tm};
+    hipError_t e = launch_route_fused(a, (hipStream_t)stream, marks);
+    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "route_dispatch launch");
   })
 }
 

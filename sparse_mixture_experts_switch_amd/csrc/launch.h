@@ -132,6 +132,26 @@ struct LayerMaps {
   void *y = nullptr;
 };
 hipError_t launch_assign(const RouteArgs &a, const LayerMaps &m, hipStream_t st, LaunchMarks marks);
+
+// Single-pass routing with one route per token: the router kernel also
+// assigns the capacity slots (each block adds the counts of the blocks before
+// it, found by a look-back in token order), forms the totals and the loss,
+// and, with dispatched set, copies each kept token's row of x to
+// dispatched[e][slot].  r.bcount / r.ppart receive the block counts and P
+// sums; r.logits is used as for launch_router.  A small kernel clears the
+// first clear_bytes at `sync` (ticket, error word, block states) first; the
+// two launches count as one step for LaunchMarks.
+constexpr int kFusedMaxExperts = 2048;
+struct FusedRouteArgs {
+  RouteArgs r;
+  int32_t *sync;          // [4 + nb]: block ticket, error word, 2 unused, then one state per block
+  size_t clear_bytes;     // (4 + nb) * 4 rounded up to 16
+  int64_t row_stride;     // of the rows below: N rounded up to 64
+  int32_t *agg_c, *inc_c; // [nb][row_stride] block counts, counts of blocks 0..b
+  int64_t *agg_p, *inc_p; // [nb][row_stride] P sums (2^-31 fixed point), the same
+  void *dispatched;       // [N][C][d], or null
+};
+hipError_t launch_route_fused(const FusedRouteArgs &a, hipStream_t st, LaunchMarks marks);
 // Top-k combine: y[t] = sum over kept routes r of routed[r * T + t] (+ x[t]).
 struct TopkSumArgs {
   int dtype, k;

@@ -27,6 +27,7 @@
 // fp32 activations: plain fp32 FMA on the vector ALUs.
 
 #include <algorithm>
+#include <climits>
 
 #include "common.h"
 #include "launch.h"
@@ -88,6 +89,12 @@ struct TopK {
   int64_t T, nb;  // tokens, router blocks
 };
 
+// A block's P partial sum (fp32, at most 64) in 2^-31 fixed point: exact for
+// sums of at least 2^-8, rounded to nearest below.  Integer sums of these are
+// independent of their order, so totals formed in any grouping agree bit for
+// bit.
+__device__ __forceinline__ int64_t p_fixed(float p) { return __double2ll_rn((double)p * 0x1p31); }
+
 template <int kK>
 __device__ __forceinline__ void topk_take(float h, int j, float &b1, int &i1, float &b2, int &i2) {
   // ascending j within one lane: strict comparisons keep the lower index
@@ -108,11 +115,15 @@ __device__ __forceinline__ bool topk_before(float va, int ia, float vb, int ib) 
   return va > vb || (va == vb && ia < ib);
 }
 
+// With s_cnt set (one route per token) the block's counts and P partial sums
+// also go to LDS, the sums as 2^-31 fixed point (s_pfix), for the single-pass
+// assignment that follows in the same kernel.
 template <int kThreads, bool kLds, int kK>
 __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t t0, int64_t blk, TopK tk,
                                 int32_t *__restrict__ expert_idx, float *__restrict__ gate,
                                 int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
-                                float *__restrict__ ppart, float *s_max, float *s_inv, int *s_e, int *s_e2) {
+                                float *__restrict__ ppart, float *s_max, float *s_inv, int *s_e, int *s_e2,
+                                int *s_cnt = nullptr, int64_t *s_pfix = nullptr) {
   constexpr int kLpt = kThreads / kRouterTokens;   // lanes per token
   constexpr int kTpe = kThreads / kRouterChunk;    // lanes per expert
   constexpr int kUpt = kRouterTokens / kTpe;       // tokens per lane in the expert sums
@@ -218,6 +229,10 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
     if (r == 0 && j < N) {
       ppart[blk * Np + j] = p;
       bcount[blk * Np + j] = c;
+      if (kK == 1 && s_cnt) {
+        s_cnt[j] = c;
+        s_pfix[j] = p_fixed(p);
+      }
       if (kK == 2) {
         ppart[(tk.nb + blk) * Np + j] = 0.f;
         bcount[(tk.nb + blk) * Np + j] = c2;
@@ -849,6 +864,315 @@ hipError_t run_router(const RouteArgs &a, hipStream_t st) {
 hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
   if (router_blocks(a.T) == 0) return hipSuccess;
   return a.k == 2 ? run_router<2>(a, st) : run_router<1>(a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Single-pass routing ("Expert Capacity and the Capacity Factor": slots in
+// token order; "The Load-Balancing Loss"), one route per token: each block
+// routes its 64 tokens as above, then assigns their slots itself, so x is
+// read once and, with a dispatch buffer, each kept row is copied to
+// dispatched[e][slot] from the copy of it the block loaded before it waited.
+//
+// Token order across blocks comes from a decoupled look-back.  Block b
+// (state[b]: 0 nothing yet, 1 aggregate, 2 inclusive prefix):
+//   1. writes its counts and P sums (aggregate) and sets state 1;
+//   2. wave 0 reads the states of the 64 nearest earlier blocks at once and,
+//      once every block up to the nearest inclusive one (or the whole window)
+//      has published, all threads add those rows; repeated until an
+//      inclusive prefix or block 0 is reached;
+//   3. writes exclusive + aggregate as its inclusive prefix, state 2;
+//   4. slot = exclusive count of the expert + in-block rank, dropped, and the
+//      dispatch stores;
+//   5. the last block forms the totals and the loss from its inclusive row.
+// Visibility across the XCDs without cache maintenance: every row is written
+// once per launch with device-coherent (write-through) stores, which complete
+// before the state word that announces them is stored; states are read with
+// device-coherent loads; a row is read with ordinary cached loads only after
+// its state was seen, so no cache can hold an older copy of it (rows are
+// padded to 256 bytes, so no cache line spans two of them, and caches start
+// each launch clean).  Counts are integers and P sums 2^-31 fixed-point
+// integers, so every total is independent of how the look-back grouped the
+// blocks.  A workgroup takes its router block from an atomic ticket, so every
+// block it waits for belongs to a workgroup that is already running and never
+// waits for a later one: the chain always drains.  Each wait is bounded: one
+// that gives up (not reached by a correct launch) sets the error word and the
+// loss to NaN and goes on, so the kernel always ends.  A small kernel clears
+// the ticket, the error word and the states before every launch.
+// ---------------------------------------------------------------------------
+constexpr int kSpinLimit = 1 << 20;  // polls (~1 s)
+
+__global__ __launch_bounds__(256) void route_sync_clear_kernel(u32x4 *__restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = u32x4{0, 0, 0, 0};
+}
+
+template <typename V>
+__device__ __forceinline__ void store_through(V *p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS of the single-pass tail (after the logit rows, which the epilogue
+// reads until its end).
+struct TailLds {
+  int64_t *p, *xp;  // [N] block P sums, exclusive P sums (fixed point)
+  int *c, *xc;      // [N] block counts, exclusive counts
+  int *dst;         // [kRouterTokens] destination row e * C + slot, or -1
+  double *red;      // [16] loss partials of the waves
+  int *win;         // [2] look-back window: rows to add, last one inclusive
+};
+__host__ __device__ constexpr int fused_tail_bytes(int N) { return N * 24 + kRouterTokens * 4 + 16 * 8 + 16; }
+__device__ __forceinline__ TailLds tail_lds(char *base, int N) {
+  TailLds L;
+  L.p = (int64_t *)base;
+  L.xp = L.p + N;
+  L.red = (double *)(L.xp + N);
+  L.c = (int *)(L.red + 16);
+  L.xc = L.c + N;
+  L.dst = L.xc + N;
+  L.win = L.dst + kRouterTokens;
+  return L;
+}
+
+// Wave 0: states of blocks lo - 1 - lane.  Returns how many of them to add
+// (through the nearest one with an inclusive prefix, else all of the window)
+// once each of those has published; `found` says the last of them is
+// inclusive.  Every decision is a ballot, so the loop is wave-uniform.
+__device__ int lookback_window(const int32_t *state, int64_t lo, int32_t *err, bool &found) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t j = lo - 1 - lane;
+  const int nvalid = (int)min<int64_t>(lo, kWave);
+  for (int it = 0;; ++it) {
+    const int st = __hip_atomic_load(state + (j > 0 ? j : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long inc = __ballot(lane < nvalid && st == 2);
+    const int n = inc ? __ffsll(inc) : nvalid;
+    const unsigned long long miss = __ballot(lane < n && st == 0);
+    if (!miss) {
+      found = inc != 0;
+      return n;
+    }
+    // give up after kSpinLimit polls, or at once when another wait already did
+    const bool quit = it == kSpinLimit ||
+                      ((it & 255) == 255 &&
+                       __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+    if (quit) {
+      if (lane == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      found = false;
+      return n;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Steps 1-5 for block blk (its tokens' experts in s_e, in-block ranks in
+// r.slot, counts and P sums in L.c / L.p).
+template <int kThreads>
+__device__ void route_fused_tail(const FusedRouteArgs &a, int64_t blk, int64_t nb, int nt, const int *s_e,
+                                 const TailLds L) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int N = a.r.N;
+  const int64_t Ns = a.row_stride, t0 = blk * kRouterTokens;
+  int32_t *const state = a.sync + 4;
+
+  __syncthreads();  // the epilogue's LDS rows are complete
+  // 1. aggregate (block 0: its inclusive prefix)
+  {
+    int32_t *rc = (blk == 0 ? a.inc_c : a.agg_c) + blk * Ns;
+    int64_t *rp = (blk == 0 ? a.inc_p : a.agg_p) + blk * Ns;
+    for (int e = tid; e < N; e += kThreads) {
+      store_through(rc + e, L.c[e]);
+      store_through(rp + e, L.p[e]);
+      L.xc[e] = 0;
+      L.xp[e] = 0;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(state + blk, blk == 0 ? 2 : 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // the dispatch copy's first kU pieces per thread, loaded now so that they
+  // arrive while the block waits for the blocks before it
+  constexpr int kU = 12;
+  const int row16 = a.r.d * (a.r.dtype == kBF16 ? 2 : 4) / 16;
+  const u32x4 *xs = (const u32x4 *)a.r.x + t0 * row16;
+  u32x4 *ds = (u32x4 *)a.dispatched;
+  const int items = nt * row16;
+  u32x4 v[kU];
+  if (ds) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = xs[min(u * kThreads + tid, items - 1)];
+  }
+
+  // 2. look-back: G threads per expert share a window's rows
+  const int G = N >= kThreads ? 1 : kThreads / N;
+  const int q = tid / min(N, kThreads);
+  int64_t lo = blk;
+  while (lo > 0) {
+    if (wave == 0) {
+      bool found;
+      const int n = lookback_window(state, lo, a.sync + 1, found);
+      if (lane == 0) {
+        L.win[0] = n;
+        L.win[1] = found ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    const int n = L.win[0];
+    const bool found = L.win[1] != 0;
+    if (q < G) {
+      for (int e = tid % min(N, kThreads); e < N; e += kThreads) {
+        int c = 0;
+        int64_t p = 0;
+#pragma unroll 4
+        for (int l = q; l < n; l += G) {
+          const int64_t j = lo - 1 - l;
+          const bool inc = found && l == n - 1;
+          c += (inc ? a.inc_c : a.agg_c)[j * Ns + e];
+          p += (inc ? a.inc_p : a.agg_p)[j * Ns + e];
+        }
+        if (c) atomicAdd(&L.xc[e], c);
+        if (p) atomicAdd((unsigned long long *)&L.xp[e], (unsigned long long)p);
+      }
+    }
+    __syncthreads();
+    lo = found ? 0 : lo - n;
+  }
+
+  // 3. inclusive prefix of this block
+  if (blk > 0) {
+    for (int e = tid; e < N; e += kThreads) {
+      store_through(a.inc_c + blk * Ns + e, L.xc[e] + L.c[e]);
+      store_through(a.inc_p + blk * Ns + e, L.xp[e] + L.p[e]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(state + blk, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // slots and drops
+  const int C = a.r.C;
+  if (tid < nt) {
+    const int e = s_e[tid];
+    const int sl = L.xc[e] + a.r.slot[t0 + tid];  // the epilogue left the in-block rank there
+    const bool drop = sl >= C;
+    a.r.slot[t0 + tid] = sl;
+    a.r.dropped[t0 + tid] = drop ? 1 : 0;
+    L.dst[tid] = drop ? -1 : e * C + sl;
+  }
+  __syncthreads();
+
+  // dispatch: the loaded pieces, then the rest of the block's rows
+  if (ds) {
+    for (int b = 0; b < items; b += kThreads * kU) {
+      if (b > 0) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = xs[min(b + u * kThreads + tid, items - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = b + u * kThreads + tid;
+        if (i < items) {
+          const int t = i / row16;
+          const int dst = L.dst[t];
+          if (dst >= 0) ds[(int64_t)dst * row16 + (i - t * row16)] = v[u];
+        }
+      }
+    }
+  }
+
+  // totals and loss: N sum_i (count_i / T) (P_i / T), in double, fixed order
+  if (blk == nb - 1) {
+    double acc = 0.0;
+    for (int e = tid; e < N; e += kThreads) {
+      const int tot = L.xc[e] + L.c[e];
+      a.r.expert_count[e] = tot;
+      acc += (double)tot * (double)(L.xp[e] + L.p[e]);
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) acc += __shfl_xor(acc, off, kWave);
+    if (lane == 0) L.red[wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      double sum = 0.0;
+      for (int w = 0; w < kThreads / kWave; ++w) sum += L.red[w];
+      const double tt = (double)a.r.T;
+      const bool bad = __hip_atomic_load(a.sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      a.r.aux_loss[0] = bad ? __builtin_nanf("") : (float)(sum * 0x1p-31 * (double)N / (tt * tt));
+    }
+  }
+}
+
+// The block's ticket; past the grid (a launch whose ticket was not cleared)
+// the workgroup does nothing.
+__device__ __forceinline__ int64_t route_ticket(int32_t *ticket, int *s_blk) {
+  if (threadIdx.x == 0) *s_blk = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return *s_blk;
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kRBThreads) void route_fused_bf16_kernel(const FusedRouteArgs a) {
+  static_assert(kRouterLgBytes + fused_tail_bytes(kFusedMaxExperts) <= kRouterSmem, "tail LDS");
+  __shared__ RouterSmem sm;
+  __shared__ int s_blk;
+  const int64_t T = a.r.T, nb = router_blocks(T);
+  const int64_t blk = route_ticket(a.sync, &s_blk);
+  if (blk >= nb) return;
+  const int N = a.r.N;
+  const LogitRows<kLds> lg =
+      router_contract_bf16<kLds>((const bf16 *)a.r.x, a.r.w_r, a.r.bias, T, a.r.d, N, a.r.logits, blk, sm);
+  const int64_t t0 = blk * kRouterTokens;
+  const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
+  const TailLds L = tail_lds(sm.stage + kRouterLgBytes, N);
+  router_epilogue<kRBThreads, kLds, 1>(lg, nt, N, t0, blk, TopK{T, nb}, a.r.expert_idx, a.r.gate, a.r.slot,
+                                       a.r.bcount, a.r.ppart, sm.s_max, sm.s_inv, sm.s_e, sm.s_e2, L.c, L.p);
+  route_fused_tail<kRBThreads>(a, blk, nb, nt, sm.s_e, L);
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kRouterThreads) void route_fused_f32_kernel(const FusedRouteArgs a) {
+  constexpr int kLg = kLds ? kRouterTokens * (kRouterChunk + 1) * 4 : 0;
+  constexpr int kX = kRouterTokens * 65 * 4;
+  constexpr int kTail = fused_tail_bytes(kFusedMaxExperts);
+  __shared__ __attribute__((aligned(16))) char s_buf[kLg + (kX > kTail ? kX : kTail)];
+  __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
+  __shared__ int s_e[kRouterTokens], s_e2[kRouterTokens];
+  __shared__ int s_blk;
+  const int64_t T = a.r.T, nb = router_blocks(T);
+  const int64_t blk = route_ticket(a.sync, &s_blk);
+  if (blk >= nb) return;
+  const int N = a.r.N;
+  const int64_t t0 = blk * kRouterTokens;
+  const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
+  const LogitRows<kLds> lg = router_contract_f32<kLds>((const float *)a.r.x, a.r.w_r, a.r.bias, T, a.r.d, N,
+                                                       a.r.logits, blk, (float *)s_buf,
+                                                       (float(*)[65])(s_buf + kLg));
+  const TailLds L = tail_lds(s_buf + kLg, N);  // the x slices are dead after the contraction
+  router_epilogue<kRouterThreads, kLds, 1>(lg, nt, N, t0, blk, TopK{T, nb}, a.r.expert_idx, a.r.gate, a.r.slot,
+                                           a.r.bcount, a.r.ppart, s_max, s_inv, s_e, s_e2, L.c, L.p);
+  route_fused_tail<kRouterThreads>(a, blk, nb, nt, s_e, L);
+}
+
+hipError_t launch_route_fused(const FusedRouteArgs &a, hipStream_t st, LaunchMarks marks) {
+  const int64_t nb = router_blocks(a.r.T);
+  if (nb == 0) return launch_assign(a.r, LayerMaps{}, st, marks);  // no tokens: zero totals and loss
+  const bool lds = a.r.N <= kRouterChunk;
+  const int64_t n16 = (int64_t)(a.clear_bytes / 16);
+  const int reps = marks.reps ? marks.reps(marks.ctx) : 1;
+  for (int r = reps; r > 0; --r) {
+    route_sync_clear_kernel<<<dim3((unsigned)std::min<int64_t>(ceil_div(n16, 256), 2048)), dim3(256), 0, st>>>(
+        (u32x4 *)a.sync, n16);
+    if (a.r.dtype == kBF16) {
+      auto kern = lds ? route_fused_bf16_kernel<true> : route_fused_bf16_kernel<false>;
+      kern<<<dim3((unsigned)nb), dim3(kRBThreads), 0, st>>>(a);
+    } else {
+      auto kern = lds ? route_fused_f32_kernel<true> : route_fused_f32_kernel<false>;
+      kern<<<dim3((unsigned)nb), dim3(kRouterThreads), 0, st>>>(a);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (marks.fn) marks.fn(marks.ctx, "route_fused");
+  return hipSuccess;
 }
 
 }  // namespace smx

@@ -65,15 +65,19 @@ def test_workspace_bytes_layout():
     s = B.make_shape(16384, 768, 3072, 128, 160, torch.bfloat16)
     ws = smx.workspace_bytes(s)
     nb = 16384 // 64
-    # block counts, block offsets, P partials, P sums, ranks, hidden, slot->token and slot->gate maps
-    expect_min = 3 * nb * 128 * 4 + 128 * 4 + 16384 * 4 + 128 * 160 * 3072 * 2 + 2 * 128 * 160 * 4
-    assert expect_min <= ws <= expect_min + 8 * 256
+    # block counts, block offsets, P partials, P sums, ranks, the single-pass routing's ordering state
+    # (ticket, error word and one state word per block; then per block and expert the aggregate and
+    # inclusive counts (4 bytes each) and P sums (8 bytes each)), hidden, slot->token and slot->gate maps
+    single_pass = (nb + 4) * 4 + nb * 128 * 24
+    expect_min = (3 * nb * 128 * 4 + 128 * 4 + 16384 * 4 + single_pass + 128 * 160 * 3072 * 2
+                  + 2 * 128 * 160 * 4)
+    assert expect_min <= ws <= expect_min + 12 * 256
     # more experts than one router chunk adds the [T][N] logits scratch
     s2 = B.make_shape(1000, 64, 64, 300, 10, torch.float32)
     assert smx.workspace_bytes(s2) >= 1000 * 300 * 4
     # routing alone: the capacity-0 figure holds no expert buffers
     s3 = B.make_shape(16384, 768, 3072, 128, 0, torch.bfloat16)
-    assert smx.workspace_bytes(s3) < 3 * nb * 128 * 4 + 16384 * 4 + 4096
+    assert smx.workspace_bytes(s3) < 3 * nb * 128 * 4 + 16384 * 4 + single_pass + 4096
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -138,6 +142,17 @@ def test_entry_points_reject_before_launch():
     rc = lib.switch_combine_add_norm(ctypes.byref(s), good, good, good, good, good, good, good, good,
                                      float("inf"), good, None)
     assert rc == B.SWITCH_E_INVALID
+    # route_dispatch: NULL dispatched, small workspace, more experts than the single pass supports
+    rc = lib.switch_route_dispatch(ctypes.byref(s), good, good, None, good, good, good, good, good, good, None,
+                                   good, 1 << 30, None)
+    assert rc == B.SWITCH_E_INVALID and b"dispatched" in lib.switch_last_error()
+    rc = lib.switch_route_dispatch(ctypes.byref(s), good, good, None, good, good, good, good, good, good, good,
+                                   good, 16, None)
+    assert rc == B.SWITCH_E_WORKSPACE
+    many = B.make_shape(64, 128, 256, 4096, 16, torch.bfloat16)
+    rc = lib.switch_route_dispatch(ctypes.byref(many), good, good, None, good, good, good, good, good, good, good,
+                                   good, 1 << 40, None)
+    assert rc == B.SWITCH_E_UNSUPPORTED
     # profiled: empty kernel range / times < 1
     for first, last, times in ((0, 0, 0), (2, 1, 1), (-1, 0, 1)):
         rc = lib.switch_layer_forward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good,
@@ -170,9 +185,10 @@ def test_topk_validation_and_workspace():
     assert smx.topk_workspace_bytes(s, 1) == smx.workspace_bytes(s)
     w2 = smx.topk_workspace_bytes(s, 2)
     nb = 16384 // 64
-    expect_min = (3 * 2 * nb * 128 * 4 + 128 * 4 + 2 * 16384 * 4 + 128 * 320 * 3072 * 2 + 3 * 128 * 320 * 4
-                  + 2 * 16384 * 768 * 2)
-    assert expect_min <= w2 <= expect_min + 10 * 256
+    single_pass = (2 * nb + 4) * 4 + 2 * nb * 128 * 24  # sized for k blocks per router block
+    expect_min = (3 * 2 * nb * 128 * 4 + 128 * 4 + 2 * 16384 * 4 + single_pass + 128 * 320 * 3072 * 2
+                  + 3 * 128 * 320 * 4 + 2 * 16384 * 768 * 2)
+    assert expect_min <= w2 <= expect_min + 14 * 256
     out = ctypes.c_size_t()
     for k, code in ((0, B.SWITCH_E_INVALID), (-1, B.SWITCH_E_INVALID), (3, B.SWITCH_E_UNSUPPORTED),
                     (129, B.SWITCH_E_INVALID)):
