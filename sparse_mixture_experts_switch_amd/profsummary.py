@@ -34,7 +34,11 @@ KERNEL_KEYS = {
     "assign_apply": ("assign_apply_layer_kernel", ""),
     "dispatch": ("dispatch_kernel", ""),
     "combine": ("combine_kernel", ""),
-    "add_norm": ("add_norm_kernel", ""),
+    "add_norm": ("add_norm_kernel", "Lb0E"),
+    # the combine instantiation (its name has come back demangled without the bool value)
+    "combine_add_norm": ("add_norm_kernel", ""),
+    "route_fused": ("route_fused_bf16_kernel", ""),
+    "route_clear": ("route_sync_clear_kernel", ""),
     "topk_sum": ("topk_sum_kernel", ""),
     "bwd_dz": ("bwd_gemm_bf16_kernel", "Lb0ELb1ELb0ELb1ELb0ELi0E"),
     "bwd_dx": ("bwd_gemm_bf16_kernel", "Lb0ELb0ELb0ELb1ELb0ELi1E"),
