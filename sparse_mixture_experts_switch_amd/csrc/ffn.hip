@@ -432,8 +432,9 @@ inline unsigned grid_of(int ntiles) { return (unsigned)(ceil_div(ntiles, 8) * 8)
 
 // Tile shape (measured on MI355X for the weight-streaming regime): every
 // live row of the expert (up to 160) x 384 output features per workgroup of
-// 8 waves (3 column blocks each).
-constexpr int kNBW = 3, kWaves = 8;
+// 8 waves (3 column blocks each), or x 256 features (2 column blocks) when
+// that spreads the output features more evenly over the CUs.
+constexpr int kWaves = 8;
 
 // Resident workgroups for a persistent launch: CUs x workgroups per CU.
 template <typename Kern>
@@ -446,12 +447,36 @@ unsigned persistent_grid(Kern kern, int ntiles) {
   return (unsigned)std::max<int64_t>(8, ceil_div(want, 8) * 8);
 }
 
-template <int MB, bool kGather, int kEpi>
+template <int MB, int NBW, bool kGather, int kEpi>
 hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
-  auto g = make_args<bf16>(c, MB * 16, kWaves * 16 * kNBW);
-  auto kern = ffn_gemm_bf16_kernel<MB, kNBW, kWaves, kGather, kEpi>;
+  auto g = make_args<bf16>(c, MB * 16, kWaves * 16 * NBW);
+  auto kern = ffn_gemm_bf16_kernel<MB, NBW, kWaves, kGather, kEpi>;
   kern<<<dim3(persistent_grid(kern, g.ntiles)), dim3(kWaves * 64), 0, st>>>(g);
   return hipGetLastError();
+}
+
+// Column blocks per wave.  Both widths stream every weight byte once and run
+// at the same speed per output feature (measured); what differs is how many
+// feature columns the busiest CU gets when the tiles are dealt out (e.g. 1024
+// features: 3 tiles of 384 per expert leave half the CUs with two tiles,
+// 4 tiles of 256 give every CU the same).  Ties keep the wider tile, which
+// re-reads each expert's activation rows fewer times.
+int pick_nbw(const GemmCall &c, int rows) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  auto span = [&](int nbw) {
+    const int64_t cols = (int64_t)kWaves * 16 * nbw;
+    const int64_t tiles = (int64_t)c.N * ceil_div(c.C, rows) * ceil_div(c.Nout, cols);
+    return ceil_div(tiles, cus) * cols;
+  };
+  return span(2) < span(3) ? 2 : 3;
+}
+
+template <int MB, bool kGather, int kEpi>
+hipError_t run_bf16_mb(const GemmCall &c, hipStream_t st) {
+  return pick_nbw(c, MB * 16) == 2 ? run_bf16<MB, 2, kGather, kEpi>(c, st) : run_bf16<MB, 3, kGather, kEpi>(c, st);
 }
 
 template <bool kGather, int kEpi>
@@ -463,12 +488,12 @@ hipError_t gemm(const GemmCall &c, hipStream_t st) {
     return hipGetLastError();
   }
   switch (pick_mb(c.C)) {
-    case 1: return run_bf16<1, kGather, kEpi>(c, st);
-    case 2: return run_bf16<2, kGather, kEpi>(c, st);
-    case 4: return run_bf16<4, kGather, kEpi>(c, st);
-    case 6: return run_bf16<6, kGather, kEpi>(c, st);
-    case 8: return run_bf16<8, kGather, kEpi>(c, st);
-    default: return run_bf16<10, kGather, kEpi>(c, st);
+    case 1: return run_bf16_mb<1, kGather, kEpi>(c, st);
+    case 2: return run_bf16_mb<2, kGather, kEpi>(c, st);
+    case 4: return run_bf16_mb<4, kGather, kEpi>(c, st);
+    case 6: return run_bf16_mb<6, kGather, kEpi>(c, st);
+    case 8: return run_bf16_mb<8, kGather, kEpi>(c, st);
+    default: return run_bf16_mb<10, kGather, kEpi>(c, st);
   }
 }
 
