@@ -701,10 +701,10 @@ int router_dx_kp(int N) { return (int)ceil_div(6 * (int64_t)N, kBKC) * kBKC; }
 // ---------------------------------------------------------------------------
 namespace {
 
-// Tile shapes: rows of an expert (up to 160) x 256 columns, 8 waves, a deep
-// pipeline for the products with a long contraction (DZ, DX); 128 x 128, 4
-// waves, single-buffered, several workgroups per CU for the weight gradients
-// (contraction = an expert's rows, short).
+// Tile shapes: rows of an expert (up to 160) x 256 columns (DZ) or x 128
+// columns (DX), 8 waves, a deep pipeline for the products with a long
+// contraction; 64 x 256, 4 waves, single-buffered, three workgroups per CU
+// for the weight gradients (contraction = an expert's rows, short).
 constexpr int kRowMBW = 5, kRowNBW = 4, kRowWM = 2, kRowWN = 4;
 constexpr int kDxNBW = 2;  // DX: 128 columns per tile (d_model / 128 tiles per expert)
 constexpr int kWgtMBW = 4, kWgtNBW = 4, kWgtWM = 1, kWgtWN = 4;
