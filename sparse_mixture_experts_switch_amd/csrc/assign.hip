@@ -327,14 +327,27 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
       p.gmap[(int64_t)e * p.C + sl] = p.gate[o];
     }
   }
-  if (p.y) {  // one route per token: output rows of this wave's dropped tokens, 0 or x
-    unsigned long long mask = __ballot(drop);
-    while (mask) {
-      const int bb = __ffsll(mask) - 1;
-      mask &= mask - 1;
-      const int64_t tt = j - lane + bb;
-      for (int c = lane; c < p.row16; c += kWave)
-        p.y[tt * p.row16 + c] = p.xres ? p.xres[tt * p.row16 + c] : u32x4{0, 0, 0, 0};
+  if (p.y) {
+    // one route per token: the output rows of this group's dropped tokens
+    // (0, or x with the residual), listed in LDS and written by all threads
+    // of the group (16-byte pieces, consecutive threads along a row)
+    __shared__ int s_nd;
+    int *s_drop = s_part;  // free after step 1
+    if (tid == 0) s_nd = 0;
+    __syncthreads();
+    const unsigned long long mask = __ballot(drop);
+    if (mask) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_nd, (int)__popcll(mask));
+      base = __shfl(base, 0, kWave);
+      if (drop) s_drop[base + (int)__popcll(mask & ((1ull << lane) - 1))] = (int)t;
+    }
+    __syncthreads();
+    const int nd = s_nd;
+    for (int it = tid; it < nd * p.row16; it += kAsThreads) {
+      const int r = it / p.row16, c = it - r * p.row16;
+      const int64_t tt = s_drop[r];
+      p.y[tt * p.row16 + c] = p.xres ? p.xres[tt * p.row16 + c] : u32x4{0, 0, 0, 0};
     }
   }
 
