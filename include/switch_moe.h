@@ -123,7 +123,7 @@ int switch_dispatch(const switch_shape *s, const void *x, const int32_t *expert_
  * runs first), and copies each kept row to dispatched[expert_idx[t]][slot[t]]
  * while the row is still in cache.  expert_idx, gate, slot, dropped,
  * expert_count and dispatched equal those of switch_route + switch_dispatch
- * bit for bit; aux_loss sums P_i in 2^-32 fixed point (deterministic, within
+ * bit for bit; aux_loss sums P_i in 2^-31 fixed point (deterministic, within
  * 1e-6 relative of switch_route's value; NaN would report a failed internal
  * wait, which a correct launch never reaches).  dispatched is [N][C][d] of
  * s->dtype (may be NULL when C = 0); padding rows are left untouched.

@@ -3,7 +3,7 @@
 Its routing outputs and dispatch rows must equal those of switch_route
 followed by switch_dispatch bit for bit (both are deterministic and share
 the router's arithmetic), its aux loss must agree with switch_route's to
-1e-6 relative (P sums in 2^-32 fixed point instead of fp32) and with the
+1e-6 relative (P sums in 2^-31 fixed point instead of fp32) and with the
 oracle to the layer's 1e-4, and the routing must pass the same oracle checks
 as the layer.  Shapes span one and many router blocks (up to 2048 blocks, far
 more than run at once, so later blocks wait on earlier ones), the LDS and
