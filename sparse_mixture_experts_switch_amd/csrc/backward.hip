@@ -707,6 +707,7 @@ namespace {
 // for the weight gradients (contraction = an expert's rows, short).
 constexpr int kRowMBW = 5, kRowNBW = 4, kRowWM = 2, kRowWN = 4;
 constexpr int kDxNBW = 2;  // DX: 128 columns per tile (d_model / 128 tiles per expert)
+constexpr int kDxrMBW = 4;  // router dx: 128 token rows per tile (T / 128 x d / 128 tiles, even over the CUs)
 constexpr int kWgtMBW = 4, kWgtNBW = 4, kWgtWM = 1, kWgtWN = 4;
 constexpr int kBNb = kRowWN * kRowNBW * 16, kBNdx = kRowWN * kDxNBW * 16;
 
@@ -784,11 +785,11 @@ hipError_t launch_router_dx_bf16(const RouterDxArgs &r, hipStream_t st) {
   a.dxe = r.dxe;
   a.dropped = r.dropped;
   a.dyres = (const bf16 *)r.dyres;
-  a.m_tiles = (int)ceil_div(r.T, kRowWM * kRowMBW * 16);
+  a.m_tiles = (int)ceil_div(r.T, kRowWM * kDxrMBW * 16);
   a.n_tiles = (int)ceil_div(r.d, kBNdx);
   a.ntiles = (int64_t)a.m_tiles * a.n_tiles;
   const unsigned grid = (unsigned)(ceil_div(a.ntiles, 8) * 8);
-  bwd_gemm_bf16_kernel<kRowMBW, kDxNBW, kRowWM, kRowWN, false, false, false, true, false, kEpiDXR, 2, 2, 0>
+  bwd_gemm_bf16_kernel<kDxrMBW, kDxNBW, kRowWM, kRowWN, false, false, false, true, false, kEpiDXR, 2, 2, 0>
       <<<dim3(grid), dim3(kRowWM * kRowWN * 64), 0, st>>>(a);
   return hipGetLastError();
 }
