@@ -471,6 +471,180 @@ void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
 }
 
 // ---------------------------------------------------------------------------
+// Weight gradients with a resident operand.  dW_out,e = (G DY)^T H and
+// dW_in,e = DU^T X have a short contraction (the expert's kept rows) and a
+// large output (d_model x d_ff per expert), so the time goes to writing the
+// output and to re-reading operands, not to the MFMAs.  A unit of work is one
+// expert and 128 of its d_model columns: the gathered rows of that operand
+// (g dy or x, through the slot -> token map, gate-scaled as in the general
+// kernel) are staged once and then held in registers as MFMA operands for the
+// whole unit; the unit walks d_ff in 128-wide chunks of the expert's H or DU
+// rows (contiguous, double-buffered in LDS, the next chunk's loads in flight
+// while a chunk is multiplied) and writes each 128 x 128 output tile once, as
+// whole 256-byte row pieces staged through LDS.  The MFMA's row operand is
+// the one that indexes output columns, so each lane holds four consecutive
+// outputs of one row.  Per output element the contraction runs over the kept
+// rows in steps of 32, in order, as in the general kernel.  Persistent: one
+// workgroup per CU; XCD x takes a contiguous range of units, so the units of
+// an expert run side by side and read its H / DU rows through one L2.
+// ---------------------------------------------------------------------------
+constexpr int kWrKmax = 160;         // largest contraction (capacity) this kernel takes
+constexpr int kWrW = 128;            // resident columns per unit = streamed columns per chunk
+constexpr int kWrStride = kWrW + 8;  // LDS row of a panel (bf16)
+constexpr int kWrThreads = 512;
+constexpr int kWrPer = kWrKmax * (kWrW / 8) / kWrThreads;  // 16-byte panel pieces per thread
+static_assert(kWrKmax * (kWrW / 8) % kWrThreads == 0 && kWrKmax % 32 == 0, "panel pieces");
+
+struct WgradArgs {
+  int C;
+  const int32_t *counts;  // [N] routed tokens per expert (kept = min(count, C))
+  const int32_t *tok;     // [N][C] token of each live slot
+  const float *gmap;      // [N][C] gate of each live slot (scaled resident rows)
+  const bf16 *R;          // resident operand rows: R[token * nres + c], c < nres
+  int nres;
+  const bf16 *S;          // streamed operand rows: S[(e C + k) * nstr + c], c < nstr
+  int nstr;
+  bf16 *Out;              // [N] blocks of o_estride elements
+  int64_t o_estride;
+  int rblocks, schunks, nunits;
+};
+
+// kResRows: the resident operand indexes output rows (dW_out [d][d_ff]),
+// else output columns (dW_in [d_ff][d]).  kScale: resident rows are scaled
+// by the slot's gate.
+template <bool kResRows, bool kScale>
+__global__ __launch_bounds__(kWrThreads) void wgrad_res_bf16_kernel(const WgradArgs p) {
+  __shared__ __attribute__((aligned(16))) bf16 s_str[2][kWrKmax * kWrStride];
+  __shared__ __attribute__((aligned(16))) bf16 s_stg[2][kWrW * kWrStride];
+  static_assert(kWrKmax * kWrStride <= 2 * kWrW * kWrStride, "resident panel fits the staging area");
+  bf16 *const s_res = &s_stg[0][0];  // resident panel, only while a unit starts
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wr = wave / 4, wc = wave % 4;  // 64 resident x 32 streamed columns per wave
+  const int nres = p.nres, nstr = p.nstr;
+  const int ldo = kResRows ? nstr : nres;
+
+  // panel piece q of this thread: contraction row pk[q], column pc (x 8)
+  int pk[kWrPer];
+  const int pc = (tid % (kWrW / 8)) * 8;
+#pragma unroll
+  for (int q = 0; q < kWrPer; ++q) pk[q] = (tid + q * kWrThreads) / (kWrW / 8);
+
+  const int g8 = gridDim.x / 8, xcd = blockIdx.x % 8;
+  const int per = (p.nunits + 7) / 8;
+  const int u_end = min(p.nunits, (xcd + 1) * per);
+  for (int u = xcd * per + blockIdx.x / 8; u < u_end; u += g8) {
+    const int e = u / p.rblocks, rb = u % p.rblocks;
+    const int live = min(p.counts[e], p.C);
+    const int kp = (live + 31) & ~31, nks = kp / 32;
+    const int64_t eC = (int64_t)e * p.C;
+    const int r0 = rb * kWrW;
+    const bf16 *Se = p.S + eC * nstr;
+
+    // loads of the resident panel and of streamed chunk `sc` (rows past the
+    // live ones re-read the last live row and are stored as zero)
+    u32x4 rr[kWrPer], rs[kWrPer];
+    float rg[kWrPer];
+    auto fetch_str = [&](int sc) {
+      if (live == 0) return;
+      const int c = min(sc * kWrW + pc, nstr - 8);
+#pragma unroll
+      for (int q = 0; q < kWrPer; ++q)
+        rs[q] = *(const u32x4 *)(Se + (int64_t)min(pk[q], live - 1) * nstr + c);
+    };
+    auto store_str = [&](int b) {
+#pragma unroll
+      for (int q = 0; q < kWrPer; ++q)
+        if (pk[q] < kp) *(u32x4 *)(&s_str[b][pk[q] * kWrStride + pc]) = pk[q] < live ? rs[q] : u32x4{0, 0, 0, 0};
+    };
+    if (live > 0) {
+      const int c = min(r0 + pc, nres - 8);
+#pragma unroll
+      for (int q = 0; q < kWrPer; ++q) {
+        const int64_t slot = eC + min(pk[q], live - 1);
+        rr[q] = *(const u32x4 *)(p.R + (int64_t)p.tok[slot] * nres + c);
+        if (kScale) rg[q] = p.gmap[slot];
+      }
+    }
+    fetch_str(0);
+    __syncthreads();  // the previous unit's last tile has left the staging area
+#pragma unroll
+    for (int q = 0; q < kWrPer; ++q) {
+      if (pk[q] >= kp) continue;
+      u32x4 v = rr[q];
+      if (kScale) {
+        bf16x8 b = as_bf16x8(v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = (bf16)(rg[q] * (float)b[j]);
+        v = as_u32x4(b);
+      }
+      *(u32x4 *)(&s_res[pk[q] * kWrStride + pc]) = pk[q] < live ? v : u32x4{0, 0, 0, 0};
+    }
+    store_str(0);
+    fetch_str(min(1, p.schunks - 1));
+    __syncthreads();
+    bf16x8 res[kWrKmax / 32][4];
+#pragma unroll
+    for (int ks = 0; ks < kWrKmax / 32; ++ks)
+      if (ks < nks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) res[ks][i] = tr_operand(s_res, kWrStride, ks * 32, wr * 64 + i * 16, lane);
+    __syncthreads();  // every wave holds its resident operands before the staging area is reused
+
+    for (int sc = 0; sc < p.schunks; ++sc) {
+      const int b = sc & 1;
+      f32x4 acc[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kWrKmax / 32; ++ks) {
+        if (ks < nks) {
+          const bf16x8 s0 = tr_operand(s_str[b], kWrStride, ks * 32, wc * 32, lane);
+          const bf16x8 s1 = tr_operand(s_str[b], kWrStride, ks * 32, wc * 32 + 16, lane);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (kResRows) {
+              acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s0, res[ks][i], acc[i][0], 0, 0, 0);
+              acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s1, res[ks][i], acc[i][1], 0, 0, 0);
+            } else {
+              acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(res[ks][i], s0, acc[i][0], 0, 0, 0);
+              acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(res[ks][i], s1, acc[i][1], 0, 0, 0);
+            }
+          }
+        }
+      }
+      // lane: output row (16 x block + lane % 16), four consecutive columns
+      bf16 *stg = s_stg[b];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int ri = wr * 64 + i * 16, sj = wc * 32 + j * 16;
+          const int row = (kResRows ? ri : sj) + lane % 16, col = (kResRows ? sj : ri) + (lane / 16) * 4;
+          typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 o{(bf16)acc[i][j][0], (bf16)acc[i][j][1], (bf16)acc[i][j][2], (bf16)acc[i][j][3]};
+          *(bf16x4 *)(&stg[row * kWrStride + col]) = o;
+        }
+      if (sc + 1 < p.schunks) {
+        store_str(b ^ 1);
+        fetch_str(min(sc + 2, p.schunks - 1));
+      }
+      __syncthreads();
+      // the tile: 128 rows x 16 pieces of 16 bytes
+      const int row0 = kResRows ? r0 : sc * kWrW, col0 = kResRows ? sc * kWrW : r0;
+      const int rows = kResRows ? nres : nstr, cols = kResRows ? nstr : nres;
+      bf16 *Oe = p.Out + (int64_t)e * p.o_estride;
+#pragma unroll
+      for (int q = 0; q < kWrW * (kWrW / 8) / kWrThreads; ++q) {
+        const int i = tid + q * kWrThreads, row = i / (kWrW / 8), col = (i % (kWrW / 8)) * 8;
+        if (row0 + row < rows && col0 + col < cols)
+          *(u32x4 *)(Oe + (int64_t)(row0 + row) * ldo + col0 + col) = *(const u32x4 *)(&stg[row * kWrStride + col]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 layers: the same products on the vector ALUs.  64 x 64 output tile,
 // 256 threads with 4 x 4 outputs each, contraction chunks of 16 staged in LDS
 // k-major for both operands (element loads, any layout).
@@ -755,6 +929,39 @@ hipError_t run_bf16(const BwdArgs<bf16> &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Resident operand rows R (through the slot -> token map, width d), streamed
+// rows S ([N][C][d_ff]), output [N][d][d_ff] or [N][d_ff][d].
+WgradArgs wgrad_args(const BwdLaunch &L, const void *R, const void *S, void *Out) {
+  WgradArgs a;
+  a.C = L.C;
+  a.counts = L.counts;
+  a.tok = L.tok;
+  a.gmap = L.gmap;
+  a.R = (const bf16 *)R;
+  a.nres = L.d;
+  a.S = (const bf16 *)S;
+  a.nstr = L.dff;
+  a.Out = (bf16 *)Out;
+  a.o_estride = (int64_t)L.d * L.dff;
+  a.rblocks = (int)ceil_div(L.d, kWrW);
+  a.schunks = (int)ceil_div(L.dff, kWrW);
+  a.nunits = L.N * a.rblocks;
+  return a;
+}
+
+template <bool kResRows, bool kScale>
+hipError_t run_wgrad(const WgradArgs &a, hipStream_t st) {
+  if (a.nunits == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  // one workgroup per CU (the panels take most of the LDS), a multiple of 8
+  const int64_t grid = std::min<int64_t>(cus / 8 * 8, ceil_div(a.nunits, 8) * 8);
+  wgrad_res_bf16_kernel<kResRows, kScale><<<dim3((unsigned)grid), dim3(kWrThreads), 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <bool AKM, bool AG, bool AS, bool BKM, bool BG, int EPI>
 hipError_t run_f32(const BwdArgs<float> &a, hipStream_t st) {
   if (a.ntiles == 0) return hipSuccess;
@@ -823,6 +1030,18 @@ hipError_t launch_bwd_experts(const BwdLaunch &L, hipStream_t st, LaunchMarks ma
       e = run_bf16<false, false, false, true, false, kEpiDX>(dx, st);
     if (e != hipSuccess) return e;
     mark("bwd_dx");
+    if (C <= kWrKmax) {
+      // capacity up to 160: resident-operand kernel (g dy or x rows kept in registers)
+      for (int r = reps(); r > 0 && e == hipSuccess; --r)
+        e = run_wgrad<true, true>(wgrad_args(L, L.dy, L.hidden, L.dw_out), st);
+      if (e != hipSuccess) return e;
+      mark("bwd_dw_out");
+      for (int r = reps(); r > 0 && e == hipSuccess; --r)
+        e = run_wgrad<false, false>(wgrad_args(L, L.x, L.du, L.dw_in), st);
+      if (e != hipSuccess) return e;
+      mark("bwd_dw_in");
+      return hipSuccess;
+    }
     // DWO: A = g dy rows through tok (k-major, gate-scaled), B = H,e [rows][d_ff] (k-major)
     auto dwo = bwd_args<bf16>(L, L.dy, 0, d, L.hidden, eh, f, d, f, 0, L.dw_out, ein, f, bm_w, bn_w);
     for (int r = reps(); r > 0 && e == hipSuccess; --r)

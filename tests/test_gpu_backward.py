@@ -166,6 +166,9 @@ CASES = {
     "router_chunks_200_experts": SMALL.with_(num_experts=200, tokens=300, capacity_factor=2.0),
     "wide_d_ff": SMALL.with_(d_ff=2816 // 4 * 4, d_model=192, tokens=700),
     "capacity_above_tile": SMALL.with_(num_experts=2, tokens=512, capacity_factor=2.0),
+    # the weight gradients' resident-operand kernel takes capacities up to 160
+    "capacity_160": SMALL.with_(num_experts=4, tokens=640),
+    "capacity_161": SMALL.with_(num_experts=4, tokens=644),
     "fp32_ragged": SMALL.with_(dtype="f32", tokens=531, num_experts=5, d_model=64, d_ff=192),
     "fp32_many_experts": SMALL.with_(dtype="f32", tokens=400, num_experts=300, d_model=128, d_ff=128,
                                      capacity_factor=3.0),
