@@ -475,25 +475,34 @@ void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
 // dW_in,e = DU^T X have a short contraction (the expert's kept rows) and a
 // large output (d_model x d_ff per expert), so the time goes to writing the
 // output and to re-reading operands, not to the MFMAs.  A unit of work is one
-// expert and 128 of its d_model columns: the gathered rows of that operand
-// (g dy or x, through the slot -> token map, gate-scaled as in the general
-// kernel) are staged once and then held in registers as MFMA operands for the
-// whole unit; the unit walks d_ff in 128-wide chunks of the expert's H or DU
-// rows (contiguous, double-buffered in LDS, the next chunk's loads in flight
-// while a chunk is multiplied) and writes each 128 x 128 output tile once, as
-// whole 256-byte row pieces staged through LDS.  The MFMA's row operand is
-// the one that indexes output columns, so each lane holds four consecutive
-// outputs of one row.  Per output element the contraction runs over the kept
-// rows in steps of 32, in order, as in the general kernel.  Persistent: one
-// workgroup per CU; XCD x takes a contiguous range of units, so the units of
-// an expert run side by side and read its H / DU rows through one L2.
+// expert, 128 of its d_model columns and a range of its d_ff columns: the
+// gathered rows of the d_model operand (g dy or x, through the slot -> token
+// map, gate-scaled as in the general kernel) are staged once and then held in
+// registers as MFMA operands for the whole unit; the unit walks its d_ff range
+// in 64-wide chunks of the expert's H or DU rows (contiguous, double-buffered
+// in LDS, the loads two chunks ahead in flight) and writes each 128 x 64
+// output tile once, as whole row pieces staged through LDS.  The MFMA's row
+// operand is the one that indexes output columns, so each lane holds four
+// consecutive outputs of one row.  Per output element the contraction runs
+// over the kept rows in steps of 32, in order, as in the general kernel.
+// Four waves and 63 KB of LDS per workgroup, two workgroups per CU: while one
+// waits for its tile's stores to drain, the other multiplies.  Persistent;
+// XCD x takes a contiguous range of units, and the units that share an
+// expert's d_ff range are adjacent, so they run side by side and read its H /
+// DU rows through one L2.
 // ---------------------------------------------------------------------------
-constexpr int kWrKmax = 160;         // largest contraction (capacity) this kernel takes
-constexpr int kWrW = 128;            // resident columns per unit = streamed columns per chunk
-constexpr int kWrStride = kWrW + 8;  // LDS row of a panel (bf16)
-constexpr int kWrThreads = 512;
-constexpr int kWrPer = kWrKmax * (kWrW / 8) / kWrThreads;  // 16-byte panel pieces per thread
-static_assert(kWrKmax * (kWrW / 8) % kWrThreads == 0 && kWrKmax % 32 == 0, "panel pieces");
+constexpr int kWrKmax = 160;          // largest contraction (capacity) this kernel takes
+constexpr int kWrR = 128;             // resident (d_model) columns per unit
+constexpr int kWrS = 64;              // streamed (d_ff) columns per chunk
+constexpr int kWrRS = kWrR + 8;       // LDS row of the resident panel (bf16)
+constexpr int kWrSP = kWrS + 8;       // LDS row of a streamed panel (bf16)
+constexpr int kWrThreads = 256;       // 2 x 2 waves, each 64 resident x 32 streamed columns
+constexpr int kWrWgPerCu = 2;
+constexpr int kWrRPer = kWrKmax * (kWrR / 8) / kWrThreads;  // 16-byte resident pieces per thread
+constexpr int kWrSPer = kWrKmax * (kWrS / 8) / kWrThreads;  // 16-byte streamed pieces per thread
+constexpr int kWrOut = kWrR * kWrS / 8 / kWrThreads;        // 16-byte output pieces per thread
+static_assert(kWrKmax * (kWrS / 8) % kWrThreads == 0 && kWrKmax % 32 == 0, "panel pieces");
+static_assert(kWrKmax * kWrRS <= 2 * kWrKmax * kWrSP, "resident panel fits the streamed buffers");
 
 struct WgradArgs {
   int C;
@@ -506,7 +515,11 @@ struct WgradArgs {
   int nstr;
   bf16 *Out;              // [N] blocks of o_estride elements
   int64_t o_estride;
-  int rblocks, schunks, nunits;
+  int rblocks;            // resident column blocks per expert
+  int schunks;            // streamed chunks per expert
+  int cpu;                // streamed chunks per unit (the last range may be shorter)
+  int splits;             // d_ff ranges per expert
+  int nunits;             // N * splits * rblocks
 };
 
 // kResRows: the resident operand indexes output rows (dW_out [d][d_ff]),
@@ -514,93 +527,107 @@ struct WgradArgs {
 // by the slot's gate.
 template <bool kResRows, bool kScale>
 __global__ __launch_bounds__(kWrThreads) void wgrad_res_bf16_kernel(const WgradArgs p) {
-  __shared__ __attribute__((aligned(16))) bf16 s_str[2][kWrKmax * kWrStride];
-  __shared__ __attribute__((aligned(16))) bf16 s_stg[2][kWrW * kWrStride];
-  static_assert(kWrKmax * kWrStride <= 2 * kWrW * kWrStride, "resident panel fits the staging area");
-  bf16 *const s_res = &s_stg[0][0];  // resident panel, only while a unit starts
+  // output tile: 128 rows x 64 columns (dW_out) or 64 rows x 128 columns (dW_in)
+  constexpr int kTR = kResRows ? kWrR : kWrS, kTC = kResRows ? kWrS : kWrR, kSS = kTC + 8;
+  __shared__ __attribute__((aligned(16))) bf16 s_str[2][kWrKmax * kWrSP];
+  __shared__ __attribute__((aligned(16))) bf16 s_stg[kTR * kSS];
+  bf16 *const s_res = &s_str[0][0];  // resident panel, only while a unit starts
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int wr = wave / 4, wc = wave % 4;  // 64 resident x 32 streamed columns per wave
+  const int wr = wave / 2, wc = wave % 2;
   const int nres = p.nres, nstr = p.nstr;
   const int ldo = kResRows ? nstr : nres;
 
-  // panel piece q of this thread: contraction row pk[q], column pc (x 8)
-  int pk[kWrPer];
-  const int pc = (tid % (kWrW / 8)) * 8;
+  // resident piece q: contraction row rk[q], column rcol; streamed piece q: row sk[q], column scol
+  int rk[kWrRPer], sk[kWrSPer];
+  const int rcol = (tid % (kWrR / 8)) * 8, scol = (tid % (kWrS / 8)) * 8;
 #pragma unroll
-  for (int q = 0; q < kWrPer; ++q) pk[q] = (tid + q * kWrThreads) / (kWrW / 8);
+  for (int q = 0; q < kWrRPer; ++q) rk[q] = (tid + q * kWrThreads) / (kWrR / 8);
+#pragma unroll
+  for (int q = 0; q < kWrSPer; ++q) sk[q] = (tid + q * kWrThreads) / (kWrS / 8);
 
   const int g8 = gridDim.x / 8, xcd = blockIdx.x % 8;
   const int per = (p.nunits + 7) / 8;
   const int u_end = min(p.nunits, (xcd + 1) * per);
   for (int u = xcd * per + blockIdx.x / 8; u < u_end; u += g8) {
-    const int e = u / p.rblocks, rb = u % p.rblocks;
+    const int rb = u % p.rblocks, es = u / p.rblocks;
+    const int e = es / p.splits, c_lo = (es % p.splits) * p.cpu;
+    const int nc = min(p.cpu, p.schunks - c_lo);  // >= 1
     const int live = min(p.counts[e], p.C);
     const int kp = (live + 31) & ~31, nks = kp / 32;
     const int64_t eC = (int64_t)e * p.C;
-    const int r0 = rb * kWrW;
+    const int r0 = rb * kWrR;
     const bf16 *Se = p.S + eC * nstr;
 
-    // loads of the resident panel and of streamed chunk `sc` (rows past the
-    // live ones re-read the last live row and are stored as zero)
-    u32x4 rr[kWrPer], rs[kWrPer];
-    float rg[kWrPer];
-    auto fetch_str = [&](int sc) {
-      if (live == 0) return;
-      const int c = min(sc * kWrW + pc, nstr - 8);
+    // Every load and store of the pipeline is unconditional, so that the
+    // compiler counts the memory operations in flight exactly and a wait for
+    // one chunk's loads never waits for later stores: rows past the live ones
+    // re-read a live row (row 0 of the expert, token 0, when it has none) and
+    // are stored as zero.
+    u32x4 rs[kWrSPer];
+    auto fetch_str = [&](int c) {  // chunk c of the expert
+      const int col = min(c * kWrS + scol, nstr - 8);
 #pragma unroll
-      for (int q = 0; q < kWrPer; ++q)
-        rs[q] = *(const u32x4 *)(Se + (int64_t)min(pk[q], live - 1) * nstr + c);
+      for (int q = 0; q < kWrSPer; ++q)
+        rs[q] = *(const u32x4 *)(Se + (int64_t)max(min(sk[q], live - 1), 0) * nstr + col);
     };
     auto store_str = [&](int b) {
 #pragma unroll
-      for (int q = 0; q < kWrPer; ++q)
-        if (pk[q] < kp) *(u32x4 *)(&s_str[b][pk[q] * kWrStride + pc]) = pk[q] < live ? rs[q] : u32x4{0, 0, 0, 0};
+      for (int q = 0; q < kWrSPer; ++q)
+        *(u32x4 *)(&s_str[b][sk[q] * kWrSP + scol]) = sk[q] < live ? rs[q] : u32x4{0, 0, 0, 0};
     };
-    if (live > 0) {
-      const int c = min(r0 + pc, nres - 8);
+    bf16x8 res[kWrKmax / 32][4];
+    {
+      u32x4 rr[kWrRPer];
+      float rg[kWrRPer];
+      const int col = min(r0 + rcol, nres - 8);
 #pragma unroll
-      for (int q = 0; q < kWrPer; ++q) {
-        const int64_t slot = eC + min(pk[q], live - 1);
-        rr[q] = *(const u32x4 *)(p.R + (int64_t)p.tok[slot] * nres + c);
+      for (int q = 0; q < kWrRPer; ++q) {
+        const int64_t slot = eC + max(min(rk[q], live - 1), 0);
+        const int32_t t = p.tok[slot];
+        rr[q] = *(const u32x4 *)(p.R + (int64_t)(live > 0 ? t : 0) * nres + col);
         if (kScale) rg[q] = p.gmap[slot];
       }
-    }
-    fetch_str(0);
-    __syncthreads();  // the previous unit's last tile has left the staging area
+      fetch_str(c_lo);
+      __syncthreads();  // the previous unit's last chunk has left the panels
 #pragma unroll
-    for (int q = 0; q < kWrPer; ++q) {
-      if (pk[q] >= kp) continue;
-      u32x4 v = rr[q];
-      if (kScale) {
-        bf16x8 b = as_bf16x8(v);
+      for (int q = 0; q < kWrRPer; ++q) {
+        u32x4 v = rr[q];
+        if (kScale) {
+          bf16x8 b = as_bf16x8(v);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b[j] = (bf16)(rg[q] * (float)b[j]);
-        v = as_u32x4(b);
+          for (int j = 0; j < 8; ++j) b[j] = (bf16)(rg[q] * (float)b[j]);
+          v = as_u32x4(b);
+        }
+        *(u32x4 *)(&s_res[rk[q] * kWrRS + rcol]) = rk[q] < live ? v : u32x4{0, 0, 0, 0};
       }
-      *(u32x4 *)(&s_res[pk[q] * kWrStride + pc]) = pk[q] < live ? v : u32x4{0, 0, 0, 0};
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < kWrKmax / 32; ++ks)
+        if (ks < nks)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) res[ks][i] = tr_operand(s_res, kWrRS, ks * 32, wr * 64 + i * 16, lane);
+      __syncthreads();  // every wave holds its resident operands before chunk 0 overwrites them
     }
     store_str(0);
-    fetch_str(min(1, p.schunks - 1));
+    fetch_str(c_lo + min(1, nc - 1));
     __syncthreads();
-    bf16x8 res[kWrKmax / 32][4];
-#pragma unroll
-    for (int ks = 0; ks < kWrKmax / 32; ++ks)
-      if (ks < nks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) res[ks][i] = tr_operand(s_res, kWrStride, ks * 32, wr * 64 + i * 16, lane);
-    __syncthreads();  // every wave holds its resident operands before the staging area is reused
 
-    for (int sc = 0; sc < p.schunks; ++sc) {
-      const int b = sc & 1;
+    // one chunk: multiply, stage the tile (after every wave has written the
+    // previous one out), move the next chunk into LDS, issue the loads two
+    // chunks ahead, write the tile.  The first call is peeled off the loop so
+    // that the loop is entered with the same memory operations in flight as
+    // its back edge carries (loads, then the last tile's stores).
+    auto step = [&](const int j) {
+      const int b = j & 1;
       f32x4 acc[4][2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kWrKmax / 32; ++ks) {
         if (ks < nks) {
-          const bf16x8 s0 = tr_operand(s_str[b], kWrStride, ks * 32, wc * 32, lane);
-          const bf16x8 s1 = tr_operand(s_str[b], kWrStride, ks * 32, wc * 32 + 16, lane);
+          const bf16x8 s0 = tr_operand(s_str[b], kWrSP, ks * 32, wc * 32, lane);
+          const bf16x8 s1 = tr_operand(s_str[b], kWrSP, ks * 32, wc * 32 + 16, lane);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (kResRows) {
@@ -613,34 +640,38 @@ __global__ __launch_bounds__(kWrThreads) void wgrad_res_bf16_kernel(const WgradA
           }
         }
       }
+      __syncthreads();  // the previous tile has left the staging area
       // lane: output row (16 x block + lane % 16), four consecutive columns
-      bf16 *stg = s_stg[b];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int ri = wr * 64 + i * 16, sj = wc * 32 + j * 16;
+        for (int jb = 0; jb < 2; ++jb) {
+          const int ri = wr * 64 + i * 16, sj = wc * 32 + jb * 16;
           const int row = (kResRows ? ri : sj) + lane % 16, col = (kResRows ? sj : ri) + (lane / 16) * 4;
           typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const bf16x4 o{(bf16)acc[i][j][0], (bf16)acc[i][j][1], (bf16)acc[i][j][2], (bf16)acc[i][j][3]};
-          *(bf16x4 *)(&stg[row * kWrStride + col]) = o;
+          const bf16x4 o{(bf16)acc[i][jb][0], (bf16)acc[i][jb][1], (bf16)acc[i][jb][2], (bf16)acc[i][jb][3]};
+          *(bf16x4 *)(&s_stg[row * kSS + col]) = o;
         }
-      if (sc + 1 < p.schunks) {
-        store_str(b ^ 1);
-        fetch_str(min(sc + 2, p.schunks - 1));
-      }
+      // the next chunk into the other buffer (after the last chunk: a copy of
+      // it that nothing reads), then loads two chunks ahead
+      store_str(b ^ 1);
+      fetch_str(c_lo + min(j + 2, nc - 1));
       __syncthreads();
-      // the tile: 128 rows x 16 pieces of 16 bytes
-      const int row0 = kResRows ? r0 : sc * kWrW, col0 = kResRows ? sc * kWrW : r0;
-      const int rows = kResRows ? nres : nstr, cols = kResRows ? nstr : nres;
-      bf16 *Oe = p.Out + (int64_t)e * p.o_estride;
+      // the tile, in 16-byte row pieces; pieces past the output's edge write
+      // the nearest piece inside it again (same value)
+      const int sc = c_lo + j;
+      const int row0 = kResRows ? r0 : sc * kWrS, col0 = kResRows ? sc * kWrS : r0;
+      const int rlim = (kResRows ? nres : nstr) - row0 - 1, clim = (kResRows ? nstr : nres) - col0 - 8;
+      bf16 *Ot = p.Out + (int64_t)e * p.o_estride + (int64_t)row0 * ldo + col0;
 #pragma unroll
-      for (int q = 0; q < kWrW * (kWrW / 8) / kWrThreads; ++q) {
-        const int i = tid + q * kWrThreads, row = i / (kWrW / 8), col = (i % (kWrW / 8)) * 8;
-        if (row0 + row < rows && col0 + col < cols)
-          *(u32x4 *)(Oe + (int64_t)(row0 + row) * ldo + col0 + col) = *(const u32x4 *)(&stg[row * kWrStride + col]);
+      for (int q = 0; q < kWrOut; ++q) {
+        const int i = tid + q * kWrThreads;
+        const int row = min(i / (kTC / 8), rlim), col = min((i % (kTC / 8)) * 8, clim);
+        *(u32x4 *)(Ot + (int64_t)row * ldo + col) = *(const u32x4 *)(&s_stg[row * kSS + col]);
       }
-    }
+    };
+    step(0);
+    for (int j = 1; j < nc; ++j) step(j);
   }
 }
 
@@ -931,6 +962,19 @@ hipError_t run_bf16(const BwdArgs<bf16> &a, hipStream_t st) {
 
 // Resident operand rows R (through the slot -> token map, width d), streamed
 // rows S ([N][C][d_ff]), output [N][d][d_ff] or [N][d_ff][d].
+int wgrad_grid_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  return cus;
+}
+
+// Resident operand rows R (through the slot -> token map, width d), streamed
+// rows S ([N][C][d_ff]), output [N][d][d_ff] or [N][d_ff][d].  Each expert's
+// d_ff chunks are split into `splits` ranges so that the units deal out
+// evenly over the workgroups: the split count minimises the chunks (plus
+// two for a unit's start) of the busiest workgroup.
 WgradArgs wgrad_args(const BwdLaunch &L, const void *R, const void *S, void *Out) {
   WgradArgs a;
   a.C = L.C;
@@ -943,21 +987,28 @@ WgradArgs wgrad_args(const BwdLaunch &L, const void *R, const void *S, void *Out
   a.nstr = L.dff;
   a.Out = (bf16 *)Out;
   a.o_estride = (int64_t)L.d * L.dff;
-  a.rblocks = (int)ceil_div(L.d, kWrW);
-  a.schunks = (int)ceil_div(L.dff, kWrW);
-  a.nunits = L.N * a.rblocks;
+  a.rblocks = (int)ceil_div(L.d, kWrR);
+  a.schunks = (int)ceil_div(L.dff, kWrS);
+  const int64_t wgs = (int64_t)wgrad_grid_cus() * kWrWgPerCu;
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int sp = 1; sp <= 4 && sp <= a.schunks; ++sp) {
+    const int64_t cpu = ceil_div(a.schunks, sp);
+    const int64_t units = (int64_t)L.N * a.rblocks * ceil_div(a.schunks, cpu);
+    const int64_t cost = ceil_div(units, wgs) * (cpu + 2);
+    if (best_cost < 0 || cost < best_cost) best = sp, best_cost = cost;
+  }
+  a.cpu = (int)ceil_div(a.schunks, best);
+  a.splits = (int)ceil_div(a.schunks, a.cpu);  // every range non-empty
+  a.nunits = L.N * a.splits * a.rblocks;
   return a;
 }
 
 template <bool kResRows, bool kScale>
 hipError_t run_wgrad(const WgradArgs &a, hipStream_t st) {
   if (a.nunits == 0) return hipSuccess;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-    cus = 256;
-  // one workgroup per CU (the panels take most of the LDS), a multiple of 8
-  const int64_t grid = std::min<int64_t>(cus / 8 * 8, ceil_div(a.nunits, 8) * 8);
+  const int64_t wgs = (int64_t)wgrad_grid_cus() / 8 * 8 * kWrWgPerCu;
+  const int64_t grid = std::min<int64_t>(wgs, ceil_div(a.nunits, 8) * 8);
   wgrad_res_bf16_kernel<kResRows, kScale><<<dim3((unsigned)grid), dim3(kWrThreads), 0, st>>>(a);
   return hipGetLastError();
 }
@@ -1030,7 +1081,7 @@ hipError_t launch_bwd_experts(const BwdLaunch &L, hipStream_t st, LaunchMarks ma
       e = run_bf16<false, false, false, true, false, kEpiDX>(dx, st);
     if (e != hipSuccess) return e;
     mark("bwd_dx");
-    if (C <= kWrKmax) {
+    if (C > 0 && C <= kWrKmax && L.T > 0) {
       // capacity up to 160: resident-operand kernel (g dy or x rows kept in registers)
       for (int r = reps(); r > 0 && e == hipSuccess; --r)
         e = run_wgrad<true, true>(wgrad_args(L, L.dy, L.hidden, L.dw_out), st);

@@ -42,8 +42,12 @@ KERNEL_KEYS = {
     "topk_sum": ("topk_sum_kernel", ""),
     "bwd_dz": ("bwd_gemm_bf16_kernel", "Lb0ELb1ELb0ELb1ELb0ELi0E"),
     "bwd_dx": ("bwd_gemm_bf16_kernel", "Lb0ELb0ELb0ELb1ELb0ELi1E"),
-    "bwd_dw_out": ("bwd_gemm_bf16_kernel", "Lb1ELb1ELb1ELb1ELb0ELi2E"),
-    "bwd_dw_in": ("bwd_gemm_bf16_kernel", "Lb1ELb0ELb0ELb1ELb1ELi2E"),
+    # weight gradients: the resident-operand kernel (capacity <= 160; its name
+    # comes back demangled or mangled), else the general tile kernel
+    "bwd_dw_out": ("wgrad_res_bf16_kernel", ("<true, true>", "ILb1ELb1EE")),
+    "bwd_dw_in": ("wgrad_res_bf16_kernel", ("<false, false>", "ILb0ELb0EE")),
+    "bwd_dw_out_general": ("bwd_gemm_bf16_kernel", "Lb1ELb1ELb1ELb1ELb0ELi2E"),
+    "bwd_dw_in_general": ("bwd_gemm_bf16_kernel", "Lb1ELb0ELb0ELb1ELb1ELi2E"),
     "bwd_router": ("router_bwd_bf16_kernel", ""),
     "bwd_router_dx": ("bwd_gemm_bf16_kernel", "Lb0ELb0ELb0ELb1ELb0ELi3E"),
     "bwd_router_planes": ("router_wr_planes_kernel", ""),
@@ -55,7 +59,7 @@ KERNEL_KEYS = {
 
 def short_name(full: str) -> str:
     for short, (a, b) in KERNEL_KEYS.items():
-        if a in full and b in full:
+        if a in full and any(x in full for x in (b if isinstance(b, tuple) else (b,))):
             return short
     return full[:60]
 

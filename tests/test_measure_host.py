@@ -44,6 +44,8 @@ def test_short_names():
     assert ps.short_name(NORM_C) == "combine_add_norm"
     assert ps.short_name("void smx::route_fused_bf16_kernel<true>(smx::FusedRouteArgs)") == "route_fused"
     assert ps.short_name("smx::assign_one_kernel(smx::AssignArgs)") == "assign"
+    assert ps.short_name("void smx::wgrad_res_bf16_kernel<true, true>(smx::WgradArgs)") == "bwd_dw_out"
+    assert ps.short_name("_ZN3smx21wgrad_res_bf16_kernelILb0ELb0EEEvNS_9WgradArgsE") == "bwd_dw_in"
     assert ps.short_name("something_else") == "something_else"
 
 
