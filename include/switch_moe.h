@@ -259,7 +259,7 @@ int switch_layer_backward(const switch_shape *s, const void *x, const float *w_r
 /* Measurement variant of switch_layer_backward, with the contract of
  * switch_layer_forward_profiled: kernels first_kernel..last_kernel only, each
  * `times` times.  The backward's launch steps, in order: "bwd_dz",
- * "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_dx" (bf16
+ * "bwd_dw_out", "bwd_dx", "bwd_dw_in", "bwd_router", "bwd_router_dx" (bf16
  * layers: the router's part of dx on matrix cores, two launches; fp32 layers:
  * none, dx is formed in "bwd_router"), "bwd_router_w", "bwd_router_w_sum";
  * none modifies its own inputs. */

@@ -34,7 +34,7 @@ EXPORTED = [
     "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
     "switch_combine_add_norm", "switch_route_dispatch",
 ]
-BACKWARD_KERNELS = ["bwd_dz", "bwd_dx", "bwd_dw_out", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
+BACKWARD_KERNELS = ["bwd_dz", "bwd_dw_out", "bwd_dx", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
                     "bwd_router_w_sum"]
 
 

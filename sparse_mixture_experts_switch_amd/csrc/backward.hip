@@ -407,9 +407,11 @@ void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
       } else if (EPI == kEpiDX) {
         if (in) {
           const int64_t t = p.tok[eC + m];
+          // nontemporal, like the weight streams: DU stays in the last-level
+          // cache for dW_in (the router's dx reads these 50 MB once, later)
           float *o = (float *)p.Out + t * p.ldo + n;
-          *(f32x4 *)o = f32x4{v[0], v[1], v[2], v[3]};
-          *(f32x4 *)(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, (f32x4 *)o);
+          __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, (f32x4 *)(o + 4));
         }
       } else if (EPI == kEpiDXR) {
         if (in) {
@@ -505,7 +507,6 @@ constexpr int kWrThreads = 256;       // 2 x 2 waves, each 64 resident x 32 stre
 constexpr int kWrWgPerCu = 2;
 constexpr int kWrRPer = kWrKmax * (kWrR / 8) / kWrThreads;  // 16-byte resident pieces per thread
 constexpr int kWrSPer = kWrKmax * (kWrS / 8) / kWrThreads;  // 16-byte streamed pieces per thread
-constexpr int kWrOut = kWrR * kWrS / 8 / kWrThreads;        // 16-byte output pieces per thread
 static_assert(kWrKmax * (kWrS / 8) % kWrThreads == 0 && kWrKmax % 32 == 0, "panel pieces");
 static_assert(kWrKmax * kWrRS <= 2 * kWrKmax * kWrSP, "resident panel fits the streamed buffers");
 
@@ -532,10 +533,13 @@ struct WgradArgs {
 // by the slot's gate.
 template <bool kResRows, bool kScale>
 __global__ __launch_bounds__(kWrThreads) void wgrad_res_bf16_kernel(const WgradArgs p) {
-  // output tile: 128 rows x 64 columns (dW_out) or 64 rows x 128 columns (dW_in)
-  constexpr int kTR = kResRows ? kWrR : kWrS, kTC = kResRows ? kWrS : kWrR, kSS = kTC + 8;
+  // Two consecutive chunks' tiles are staged side by side and written
+  // together as one 128 x 128 tile: whole 256-byte row pieces for both
+  // gradients (a chunk alone is 128 rows x 64 columns of dW_out).
+  constexpr int kSS = kWrR + 8;
+  static_assert(2 * kWrS == kWrR, "a chunk pair spans the resident width");
   __shared__ __attribute__((aligned(16))) bf16 s_str[2][kWrKmax * kWrSP];
-  __shared__ __attribute__((aligned(16))) bf16 s_stg[kTR * kSS];
+  __shared__ __attribute__((aligned(16))) bf16 s_stg[kWrR * kSS];
   bf16 *const s_res = &s_str[0][0];  // resident panel, only while a unit starts
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -618,12 +622,17 @@ __global__ __launch_bounds__(kWrThreads) void wgrad_res_bf16_kernel(const WgradA
     fetch_str(c_lo + min(1, nc - 1));
     __syncthreads();
 
-    // one chunk: multiply, stage the tile (after every wave has written the
-    // previous one out), move the next chunk into LDS, issue the loads two
-    // chunks ahead, write the tile.  The first call is peeled off the loop so
-    // that the loop is entered with the same memory operations in flight as
-    // its back edge carries (loads, then the last tile's stores).
-    auto step = [&](const int j) {
+    // One chunk: multiply, stage its tile into half `kHalf` of the pair
+    // (the pair's first chunk waits until every wave has written the
+    // previous pair out), move the next chunk into LDS, issue the loads two
+    // chunks ahead, and, with kWrite halves, write the pair.  The loop takes
+    // chunks in pairs so that every store sits at a fixed place in the code,
+    // and the first pair is peeled off it: the loop is entered with the same
+    // memory operations in flight as its back edge carries (loads, then the
+    // last pair's stores), and a wait for a chunk's loads never includes
+    // those stores.
+    auto step = [&](auto half_c, auto write_c, const int j) {
+      constexpr int kHalf = decltype(half_c)::value, kWrite = decltype(write_c)::value;
       const int b = j & 1;
       f32x4 acc[4][2];
 #pragma unroll
@@ -645,13 +654,15 @@ __global__ __launch_bounds__(kWrThreads) void wgrad_res_bf16_kernel(const WgradA
           }
         }
       }
-      __syncthreads();  // the previous tile has left the staging area
-      // lane: output row (16 x block + lane % 16), four consecutive columns
+      if (kHalf == 0) __syncthreads();  // the previous pair has left the staging area
+      // lane: output row (16 x block + lane % 16), four consecutive columns;
+      // the chunk's streamed columns are the pair tile's columns (dW_out) or
+      // rows (dW_in) kHalf * 64 ...
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-          const int ri = wr * 64 + i * 16, sj = wc * 32 + jb * 16;
+          const int ri = wr * 64 + i * 16, sj = kHalf * kWrS + wc * 32 + jb * 16;
           const int row = (kResRows ? ri : sj) + lane % 16, col = (kResRows ? sj : ri) + (lane / 16) * 4;
           typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
           const bf16x4 o{(bf16)acc[i][jb][0], (bf16)acc[i][jb][1], (bf16)acc[i][jb][2], (bf16)acc[i][jb][3]};
@@ -662,25 +673,39 @@ __global__ __launch_bounds__(kWrThreads) void wgrad_res_bf16_kernel(const WgradA
       store_str(b ^ 1);
       fetch_str(c_lo + min(j + 2, nc - 1));
       __syncthreads();
-      // the tile, in 16-byte row pieces; pieces past the output's edge write
-      // the nearest piece inside it again (same value)
-      const int sc = c_lo + j;
-      const int row0 = kResRows ? r0 : sc * kWrS, col0 = kResRows ? sc * kWrS : r0;
-      const int rlim = (kResRows ? nres : nstr) - row0 - 1, clim = (kResRows ? nstr : nres) - col0 - 8;
-      bf16 *Ot = p.Out + (int64_t)e * p.o_estride + (int64_t)row0 * ldo + col0;
+      if (kWrite > 0) {
+        // the pair (kWrite chunks), in 16-byte row pieces; pieces past the
+        // output's edge write the nearest piece inside it again (same value)
+        const int sc = c_lo + j - kHalf;  // the pair's first chunk
+        const int row0 = kResRows ? r0 : sc * kWrS, col0 = kResRows ? sc * kWrS : r0;
+        constexpr int kRows = kResRows ? kWrR : kWrite * kWrS, kCols = kResRows ? kWrite * kWrS : kWrR;
+        const int rlim = min((kResRows ? nres : nstr) - row0, kRows) - 1;
+        const int clim = min((kResRows ? nstr : nres) - col0, kCols) - 8;
+        bf16 *Ot = p.Out + (int64_t)e * p.o_estride + (int64_t)row0 * ldo + col0;
 #pragma unroll
-      for (int q = 0; q < kWrOut; ++q) {
-        const int i = tid + q * kWrThreads;
-        const int row = min(i / (kTC / 8), rlim), col = min((i % (kTC / 8)) * 8, clim);
-        // nontemporal: the gradient is written once, and keeping it out of
-        // the last-level cache leaves DU there for dW_in (base workload:
-        // dW_in 203 -> 184 us, dW_out 198 -> 211 us, the pass 898 -> 872 us)
-        __builtin_nontemporal_store(*(const u32x4 *)(&s_stg[row * kSS + col]),
-                                    (u32x4 *)(Ot + (int64_t)row * ldo + col));
+        for (int q = 0; q < kRows * kCols / 8 / kWrThreads; ++q) {
+          const int i = tid + q * kWrThreads;
+          const int row = min(i / (kCols / 8), rlim), col = min((i % (kCols / 8)) * 8, clim);
+          // nontemporal: the gradient is written once, and keeping it out of
+          // the last-level cache leaves H and DU there for the other kernels
+          __builtin_nontemporal_store(*(const u32x4 *)(&s_stg[row * kSS + col]),
+                                      (u32x4 *)(Ot + (int64_t)row * ldo + col));
+        }
       }
     };
-    step(0);
-    for (int j = 1; j < nc; ++j) step(j);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    int j = 0;
+    if (nc >= 2) {
+      step(I0{}, I0{}, 0);
+      step(I1{}, I2{}, 1);
+      for (j = 2; j + 1 < nc; j += 2) {
+        step(I0{}, I0{}, j);
+        step(I1{}, I2{}, j + 1);
+      }
+    }
+    if (j < nc) step(I0{}, I1{}, j);  // an odd chunk count: the last chunk alone
   }
 }
 
@@ -1063,8 +1088,8 @@ hipError_t launch_router_dx_bf16(const RouterDxArgs &r, hipStream_t st) {
 
 int bwd_dz_tiles(int dtype, int dff) { return (int)ceil_div(dff, dtype == kBF16 ? kBNb : 64); }
 
-// The four products, in order: DZ (needs dy, W_out, H), DX (needs DU),
-// DWO (needs dy, H), DWI (needs DU, x).
+// The four products, in order: DZ (needs dy, W_out, H), DWO (needs dy, H),
+// DX (needs DU), DWI (needs DU, x).
 hipError_t launch_bwd_experts(const BwdLaunch &L, hipStream_t st, LaunchMarks marks) {
   auto mark = [&](const char *name) {
     if (marks.fn) marks.fn(marks.ctx, name);
@@ -1074,64 +1099,50 @@ hipError_t launch_bwd_experts(const BwdLaunch &L, hipStream_t st, LaunchMarks ma
   const int64_t ein = (int64_t)f * d;  // elements of one expert's W_in / W_out
   const int64_t eh = (int64_t)C * f;   // elements of one expert's H / DU rows
   hipError_t e = hipSuccess;
-  // with no kept rows (C = 0) the row-tiled products launch no tile and the
-  // weight-gradient tiles write zeros
+  auto run = [&](const char *name, auto &&launch) {
+    for (int r = reps(); r > 0 && e == hipSuccess; --r) e = launch();
+    if (e == hipSuccess) mark(name);
+    return e == hipSuccess;
+  };
+  // Order DZ, dW_out, DX, dW_in: each weight gradient runs right after the
+  // kernel that last touched its streamed operand (DZ reads H, DZ writes and
+  // DX reads DU), and the weight streams and gradient stores in between are
+  // nontemporal, so H and DU are read from the last-level cache.  With no
+  // kept rows (C = 0) the row-tiled products launch no tile and the
+  // weight-gradient tiles write zeros.
   if (L.dtype == kBF16) {
     const int bm_rows = kRowWM * kRowMBW * 16, bm_w = kWgtWM * kWgtMBW * 16, bn_w = kWgtWN * kWgtNBW * 16;
+    const bool resident = C > 0 && C <= kWrKmax && L.T > 0;  // resident-operand weight gradients
     // DZ: A = dy rows through tok (k-contiguous), B = W_out,e [d][d_ff] (k-major)
     auto dz = bwd_args<bf16>(L, L.dy, 0, d, L.w_out, ein, f, C, f, d, L.du, eh, f, bm_rows, kBNb);
-    for (int r = reps(); r > 0 && e == hipSuccess; --r)
-      e = run_bf16<false, true, false, true, false, kEpiDU>(dz, st);
-    if (e != hipSuccess) return e;
-    mark("bwd_dz");
-    // DX: A = DU,e [rows][d_ff] (k-contiguous), B = W_in,e [d_ff][d] (k-major)
-    auto dx = bwd_args<bf16>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, bm_rows, kBNdx);
-    for (int r = reps(); r > 0 && e == hipSuccess; --r)
-      e = run_bf16<false, false, false, true, false, kEpiDX>(dx, st);
-    if (e != hipSuccess) return e;
-    mark("bwd_dx");
-    if (C > 0 && C <= kWrKmax && L.T > 0) {
-      // capacity up to 160: resident-operand kernel (g dy or x rows kept in registers)
-      for (int r = reps(); r > 0 && e == hipSuccess; --r)
-        e = run_wgrad<true, true>(wgrad_args(L, L.dy, L.hidden, L.dw_out), st);
-      if (e != hipSuccess) return e;
-      mark("bwd_dw_out");
-      for (int r = reps(); r > 0 && e == hipSuccess; --r)
-        e = run_wgrad<false, false>(wgrad_args(L, L.x, L.du, L.dw_in), st);
-      if (e != hipSuccess) return e;
-      mark("bwd_dw_in");
-      return hipSuccess;
-    }
+    if (!run("bwd_dz", [&] { return run_bf16<false, true, false, true, false, kEpiDU>(dz, st); })) return e;
     // DWO: A = g dy rows through tok (k-major, gate-scaled), B = H,e [rows][d_ff] (k-major)
     auto dwo = bwd_args<bf16>(L, L.dy, 0, d, L.hidden, eh, f, d, f, 0, L.dw_out, ein, f, bm_w, bn_w);
-    for (int r = reps(); r > 0 && e == hipSuccess; --r)
-      e = run_bf16<true, true, true, true, false, kEpiDW>(dwo, st);
-    if (e != hipSuccess) return e;
-    mark("bwd_dw_out");
+    if (!run("bwd_dw_out", [&] {
+          return resident ? run_wgrad<true, true>(wgrad_args(L, L.dy, L.hidden, L.dw_out), st)
+                          : run_bf16<true, true, true, true, false, kEpiDW>(dwo, st);
+        }))
+      return e;
+    // DX: A = DU,e [rows][d_ff] (k-contiguous), B = W_in,e [d_ff][d] (k-major)
+    auto dx = bwd_args<bf16>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, bm_rows, kBNdx);
+    if (!run("bwd_dx", [&] { return run_bf16<false, false, false, true, false, kEpiDX>(dx, st); })) return e;
     // DWI: A = DU,e [rows][d_ff] (k-major), B = x rows through tok (k-major)
     auto dwi = bwd_args<bf16>(L, L.du, eh, f, L.x, 0, d, f, d, 0, L.dw_in, ein, d, bm_w, bn_w);
-    for (int r = reps(); r > 0 && e == hipSuccess; --r)
-      e = run_bf16<true, false, false, true, true, kEpiDW>(dwi, st);
-    if (e != hipSuccess) return e;
-    mark("bwd_dw_in");
+    if (!run("bwd_dw_in", [&] {
+          return resident ? run_wgrad<false, false>(wgrad_args(L, L.x, L.du, L.dw_in), st)
+                          : run_bf16<true, false, false, true, true, kEpiDW>(dwi, st);
+        }))
+      return e;
     return hipSuccess;
   }
   auto dz = bwd_args<float>(L, L.dy, 0, d, L.w_out, ein, f, C, f, d, L.du, eh, f, 64, 64);
-  for (int r = reps(); r > 0 && e == hipSuccess; --r) e = run_f32<false, true, false, true, false, kEpiDU>(dz, st);
-  if (e != hipSuccess) return e;
-  mark("bwd_dz");
-  auto dx = bwd_args<float>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, 64, 64);
-  for (int r = reps(); r > 0 && e == hipSuccess; --r) e = run_f32<false, false, false, true, false, kEpiDX>(dx, st);
-  if (e != hipSuccess) return e;
-  mark("bwd_dx");
+  if (!run("bwd_dz", [&] { return run_f32<false, true, false, true, false, kEpiDU>(dz, st); })) return e;
   auto dwo = bwd_args<float>(L, L.dy, 0, d, L.hidden, eh, f, d, f, 0, L.dw_out, ein, f, 64, 64);
-  for (int r = reps(); r > 0 && e == hipSuccess; --r) e = run_f32<true, true, true, true, false, kEpiDW>(dwo, st);
-  if (e != hipSuccess) return e;
-  mark("bwd_dw_out");
+  if (!run("bwd_dw_out", [&] { return run_f32<true, true, true, true, false, kEpiDW>(dwo, st); })) return e;
+  auto dx = bwd_args<float>(L, L.du, eh, f, L.w_in, ein, d, C, d, f, L.dxe, 0, d, 64, 64);
+  if (!run("bwd_dx", [&] { return run_f32<false, false, false, true, false, kEpiDX>(dx, st); })) return e;
   auto dwi = bwd_args<float>(L, L.du, eh, f, L.x, 0, d, f, d, 0, L.dw_in, ein, d, 64, 64);
-  for (int r = reps(); r > 0 && e == hipSuccess; --r) e = run_f32<true, false, false, true, true, kEpiDW>(dwi, st);
-  if (e != hipSuccess) return e;
-  mark("bwd_dw_in");
+  if (!run("bwd_dw_in", [&] { return run_f32<true, false, false, true, true, kEpiDW>(dwi, st); })) return e;
   return hipSuccess;
 }
 
