@@ -206,6 +206,15 @@ def test_backward_base_sampled_experts():
     _check(CONFIGS["base"].with_(name="base_bwd"), d_aux=0.01, sample_experts=[0, 17, 42, 63, 100, 127])
 
 
+def test_backward_xxl_sampled_experts():
+    """The XXL-shaped layer (8192 tokens, d_model 4096, d_ff 10240, 64
+    experts, capacity 160): 32 resident column blocks and 160 d_ff chunks per
+    expert in the weight-gradient kernel; dx and the router gradients in full,
+    the weight gradients of 3 sampled experts."""
+    _check(CONFIGS["xxl"].with_(name="xxl_bwd"), d_aux=0.01, sample_experts=[0, 31, 63])
+    torch.cuda.empty_cache()
+
+
 def test_backward_deterministic_and_profiled_split():
     cfg = CONFIGS["base"].with_(tokens=4096)
     inp, C, fwd, ws, dy, a = _run(cfg)
