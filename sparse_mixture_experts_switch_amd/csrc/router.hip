@@ -767,26 +767,34 @@ __global__ __launch_bounds__(256) void router_wgrad_f32_kernel(const float *__re
   }
 }
 
-// dW_r = sum over the splits of wpart, in order; dbias = sum over the router
-// blocks of bpart, in order.
+// dW_r = sum over the splits of wpart, in order (workgroups [0, wblocks), one
+// element per thread, 16 loads in flight); dbias = sum over the router blocks
+// of bpart (the following workgroups, one wave per expert: lane l adds blocks
+// l, l + 64, ... in order, then the 64 partials meet in a butterfly, which
+// every lane evaluates in the same order).  Both are fixed-order sums.
 __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float *__restrict__ wpart,
                                                                const float *__restrict__ bpart, int N, int d,
-                                                               int splits, int64_t nb, float *__restrict__ dw_r,
-                                                               float *__restrict__ dbias) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nd = (int64_t)N * d;
-  if (i < nd) {
-    float s = 0.f;
-#pragma unroll 8
-    for (int sp = 0; sp < splits; ++sp) s += wpart[(int64_t)sp * nd + i];
-    dw_r[i] = s;
-  }
-  if (dbias && i < N) {
-    float s = 0.f;
+                                                               int splits, int64_t nb, int64_t wblocks,
+                                                               float *__restrict__ dw_r, float *__restrict__ dbias) {
+  if (blockIdx.x < wblocks) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nd = (int64_t)N * d;
+    if (i < nd) {
+      float s = 0.f;
 #pragma unroll 16
-    for (int64_t b = 0; b < nb; ++b) s += bpart[b * N + i];
-    dbias[i] = s;
+      for (int sp = 0; sp < splits; ++sp) s += wpart[(int64_t)sp * nd + i];
+      dw_r[i] = s;
+    }
+    return;
   }
+  const int j = (int)((blockIdx.x - wblocks) * 4 + threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  if (j >= N) return;  // whole waves
+  float s = 0.f;
+#pragma unroll 4
+  for (int64_t b = lane; b < nb; b += kWave) s += bpart[b * N + j];
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) s += __shfl_xor(s, off, kWave);
+  if (lane == 0) dbias[j] = s;
 }
 
 WgradSplit router_wgrad_split(int64_t T, int N, int d) {
@@ -836,9 +844,10 @@ hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st, LaunchMarks
   if (e != hipSuccess) return e;
   mark("bwd_router_w");
   const int64_t nd = (int64_t)a.N * a.d;
+  const int64_t wblocks = ceil_div(nd, 256), bblocks = a.dbias ? ceil_div(a.N, 4) : 0;
   for (int r = reps(); r > 0; --r)
-    router_wgrad_sum_kernel<<<dim3((unsigned)ceil_div(std::max<int64_t>(nd, a.N), 256)), dim3(256), 0, st>>>(
-        a.wpart, a.bpart, a.N, a.d, sp.splits, nb, a.dw_r, a.dbias);
+    router_wgrad_sum_kernel<<<dim3((unsigned)(wblocks + bblocks)), dim3(256), 0, st>>>(
+        a.wpart, a.bpart, a.N, a.d, sp.splits, nb, wblocks, a.dw_r, a.dbias);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mark("bwd_router_w_sum");
   return hipSuccess;
