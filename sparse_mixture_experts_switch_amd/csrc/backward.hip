@@ -487,13 +487,14 @@ void bwd_gemm_bf16_kernel(const BwdArgs<bf16> p) {
 // map, gate-scaled as in the general kernel) are staged once and then held in
 // registers as MFMA operands for the whole unit; the unit walks its d_ff range
 // in 64-wide chunks of the expert's H or DU rows (contiguous, double-buffered
-// in LDS, the loads two chunks ahead in flight) and writes each 128 x 64
-// output tile once, as whole row pieces staged through LDS.  The MFMA's row
-// operand is the one that indexes output columns, so each lane holds four
-// consecutive outputs of one row.  Per output element the contraction runs
-// over the kept rows in steps of 32, in order, as in the general kernel.
-// Four waves and 63 KB of LDS per workgroup, two workgroups per CU: while one
-// waits for its tile's stores to drain, the other multiplies.  Persistent;
+// in LDS, the loads two chunks ahead in flight) and writes the output once,
+// two chunks at a time as 128 x 128 tiles of whole 256-byte row pieces
+// staged through LDS.  The MFMA's row operand is the one that indexes output
+// columns, so each lane holds four consecutive outputs of one row.  Per
+// output element the contraction runs over the kept rows in steps of 32, in
+// order, as in the general kernel.  Four waves and 79 KB of LDS per
+// workgroup, two workgroups per CU: while one waits for its stores to drain,
+// the other multiplies.  Persistent;
 // XCD x takes a contiguous range of units, and the units that share an
 // expert's d_ff range are adjacent, so they run side by side and read its H /
 // DU rows through one L2.
