@@ -169,6 +169,8 @@ CASES = {
     # the weight gradients' resident-operand kernel takes capacities up to 160
     "capacity_160": SMALL.with_(num_experts=4, tokens=640),
     "capacity_161": SMALL.with_(num_experts=4, tokens=644),
+    # d_model and d_ff of 64: half a resident block, one d_ff chunk (no pair)
+    "narrow_64": SMALL.with_(num_experts=5, tokens=300, d_model=64, d_ff=64),
     # 600 (expert, 128-column) units: workgroups take several, each with an odd number of d_ff chunks
     "odd_chunks_many_units": SMALL.with_(num_experts=300, tokens=3000, d_model=256, d_ff=384),
     "fp32_ragged": SMALL.with_(dtype="f32", tokens=531, num_experts=5, d_model=64, d_ff=192),
