@@ -22,6 +22,8 @@ Tolerances (stated once here, used by every parity test):
 
 from __future__ import annotations
 
+import json
+import os
 import sys
 import time
 
@@ -94,27 +96,46 @@ def check_routing(g: dict, own: dict, fed: dict, label: str) -> dict:
         fed["dropped"]) else 0.0, "aux_rel": float(aux_rel), "gate_err": float(gate_err.max(initial=0.0))}
 
 
-def check_y(y_gpu: np.ndarray, fed: dict, dtype: torch.dtype, label: str, x: np.ndarray | None = None) -> float:
+def report(label: str, rec: dict) -> None:
+    """Append one parity record (JSON line) to the file SMX_PARITY_REPORT
+    names, if set: the per-config error statistics of a GPU test run."""
+    path = os.environ.get("SMX_PARITY_REPORT")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps({"case": label, **rec}) + "\n")
+
+
+def check_y(y_gpu: np.ndarray, fed: dict, dtype: torch.dtype, label: str, x: np.ndarray | None = None,
+            expect_rows: int | None = None) -> dict:
     """Bare (or residual, when x is given) output parity on the rows the
-    oracle computed (rows it skipped are NaN there)."""
+    oracle computed (rows it skipped are NaN there).
+
+    Fails when no kept row was compared, or, with expect_rows, when the number
+    of kept rows compared differs from it (a sampled check must compare
+    exactly the kept tokens of its sampled experts).  Returns the number of
+    kept rows compared, max |err| / rms, and how many elements exceed the
+    bound without the rounding term (tol * rms alone)."""
     ref = fed["y_bare"]
     rows = ~np.isnan(ref).any(axis=1)
     dropped = fed["dropped"]
     if x is None:
         assert np.all(y_gpu[dropped] == 0.0), f"{label}: dropped rows not exactly 0"
-        got, want = y_gpu[rows], ref[rows]
     else:
         assert np.array_equal(y_gpu[dropped], x[dropped]), f"{label}: dropped rows differ from x"
-        got, want = y_gpu[rows], x[rows] + ref[rows]
-    if got.size == 0:
-        return 0.0
     kept = rows & ~dropped
-    if not kept.any():
-        return 0.0
+    n_rows = int(kept.sum())
+    if expect_rows is not None:
+        assert expect_rows > 0, f"{label}: the sample holds no kept token"
+        assert n_rows == expect_rows, f"{label}: compared {n_rows} kept rows, expected {expect_rows}"
+    assert n_rows > 0, f"{label}: no kept row compared"
+    got = y_gpu[kept]
+    want = ref[kept] if x is None else x[kept] + ref[kept]
     rms = float(np.sqrt(np.mean(ref[kept] ** 2)))
     diff = np.abs(got - want)
     lim = Y_TOL[dtype] * rms + Y_ROUND[dtype] * np.abs(want)
     worst = np.unravel_index(np.argmax(diff - lim), diff.shape)
     assert np.all(diff <= lim), (f"{label}: |y err| {diff[worst]:.3e} > {lim[worst]:.3e} at {worst} "
                                  f"(value {want[worst]:.3e}, rms {rms:.3e})")
-    return float(diff.max() / rms) if rms > 0 else 0.0
+    return {"rows": n_rows, "elements": int(diff.size),
+            "max_err_over_rms": float(diff.max() / rms) if rms > 0 else 0.0,
+            "over_strict": int(np.sum(diff > Y_TOL[dtype] * rms)), "strict_tol": Y_TOL[dtype]}

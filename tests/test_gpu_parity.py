@@ -12,7 +12,7 @@ import torch
 
 import oracle.switch_oracle as so
 import sparse_mixture_experts_switch_amd as smx
-from parity_lib import (check_routing, check_y, f64, gpu_outputs_numpy, oracle_run, say)
+from parity_lib import (check_routing, check_y, f64, gpu_outputs_numpy, oracle_run, report, say)
 from sparse_mixture_experts_switch_amd.inputs import CONFIGS, LayerConfig, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -35,12 +35,16 @@ def _run(cfg: LayerConfig, add_residual=False, bias=None):
 
 def _check_full(cfg, experts=None, add_residual=False, bias=None):
     inp, C, g = _run(cfg, add_residual=add_residual, bias=bias)
-    own = oracle_run(inp, C, experts=[] if experts is not None else [])  # routing only
+    own = oracle_run(inp, C, experts=[])  # routing only
     fed = oracle_run(inp, C, expert_idx=g["expert_idx"], experts=experts)
     rep = check_routing(g, own, fed, cfg.name)
     x = f64(inp["x"]) if add_residual else None
-    rel = check_y(g["y"], fed, cfg.torch_dtype, cfg.name, x=x)
-    say(f"  {cfg.name}: C={C} {rep} max|err|/rms={rel:.3e}")
+    # a sampled check compares exactly the kept tokens of the sampled experts
+    # (counted from the GPU's own counts)
+    want = None if experts is None else int(sum(min(int(g["expert_count"][i]), C) for i in experts))
+    yrep = check_y(g["y"], fed, cfg.torch_dtype, cfg.name, x=x, expect_rows=want)
+    report(cfg.name, {"capacity": C, **rep, **yrep, "sampled_experts": None if experts is None else len(experts)})
+    say(f"  {cfg.name}: C={C} {rep} y {yrep}")
     return inp, C, g, fed
 
 

@@ -507,6 +507,127 @@ def pin_backward_dropped_tokens(rng):
         assert np.array_equal(g["dx"][drop], dy[drop] if res else np.zeros_like(dy[drop]))
 
 
+def pin_forward_sampled_experts(rng):
+    """forward(experts=S) restricts the expert FFN to the experts in S (what
+    the parity tests of the largest layers use): the routing outputs do not
+    change; the rows of kept tokens routed to S are the full forward's rows
+    bit for bit; every other kept row is NaN (so a comparison skips it);
+    dropped rows are exactly 0 ('Expert Capacity': a dropped token's
+    computation is skipped); weights of experts outside S are never asked
+    for; S = every expert is the full forward."""
+    T, d, f, N = 48, 5, 7, 6
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, N, scale=2.0)
+    b = np.array([1.0, 0.5, 0.0, 0.0, -0.5, 0.0])  # skewed: forces drops
+    C = so.expert_capacity(T, N, 1.0)
+    full = so.forward(x, w_r, b, w_in, w_out, C)
+    kept = ~full["dropped"]
+    assert full["dropped"].any() and kept.any()
+    for S in ([], [2], [0, 3, 5], list(range(N))):
+        asked = []
+
+        def source(i, asked=asked):
+            asked.append(i)
+            return w_in[i], w_out[i]
+
+        part = so.forward(x, w_r, b, source, None, C, experts=S)
+        assert set(asked) <= set(S)
+        for k in ("expert_idx", "gate", "slot", "dropped", "expert_count"):
+            assert np.array_equal(part[k], full[k]), k
+        assert part["aux_loss"] == full["aux_loss"]
+        in_s = np.isin(full["expert_idx"], S)
+        assert np.array_equal(part["y_bare"][kept & in_s], full["y_bare"][kept & in_s])
+        assert np.all(np.isnan(part["y_bare"][kept & ~in_s]))
+        assert np.all(part["y_bare"][~kept] == 0.0)
+        if S == [0, 3, 5]:
+            assert (kept & in_s).sum() >= 10  # the sample is not empty
+    np.testing.assert_array_equal(so.forward(x, w_r, b, w_in, w_out, C, experts=list(range(N)))["y_bare"],
+                                  full["y_bare"])
+
+
+def pin_combine_residual():
+    """combine with x_residual: every row is x + the bare combined row and a
+    dropped row is exactly x ('Expert Capacity': a dropped token continues
+    through the residual; 'Switch Routing': y = p_e(x) E_e(x) for k = 1), on
+    the hand-worked layer with the expert outputs worked by hand there
+    (expert 0 maps [1, 0] to [1, 3]; expert 1 maps [0, 1] to [2, 1])."""
+    g, x, w_r, w_in, w_out = _hand_inputs()
+    exp = g["expected"]
+    e = np.array(exp["expert_idx"])
+    slot = np.array(exp["slot"])
+    dropped = np.array(exp["dropped"])
+    gate = np.array(exp["gate"])
+    eo = np.zeros((2, 2, 2))
+    eo[0, 0] = eo[0, 1] = [1.0, 3.0]  # tokens 0 and 2 (slots 0 and 1 of expert 0)
+    eo[1, 0] = [2.0, 1.0]             # token 1
+    np.testing.assert_allclose(so.combine(eo, e, slot, dropped, gate), exp["y_bare"], rtol=0, atol=1e-14)
+    y = so.combine(eo, e, slot, dropped, gate, x_residual=x)
+    np.testing.assert_allclose(y, exp["y_residual"], rtol=0, atol=1e-14)
+    assert np.array_equal(y[dropped], x[dropped])
+
+
+def pin_combine_residual_matches_layer(rng):
+    """Stage path with the residual: dispatch, the expert FFN of each buffer
+    and combine(x_residual=x) give the layer's y with add_residual, rows of
+    dropped tokens exactly x."""
+    T, d, f, N = 30, 4, 6, 3
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, N, scale=2.0)
+    b = np.array([1.0, 0.0, -1.0])
+    C = so.expert_capacity(T, N, 0.75)
+    lay = so.forward(x, w_r, b, w_in, w_out, C, add_residual=True)
+    assert lay["dropped"].any()
+    buf, filled = so.dispatch(x, lay["expert_idx"], lay["slot"], lay["dropped"], N, C)
+    eo = np.stack([so.expert_ffn(buf[i], w_in[i], w_out[i]) for i in range(N)])
+    y = so.combine(eo, lay["expert_idx"], lay["slot"], lay["dropped"], lay["gate"], x_residual=x)
+    np.testing.assert_allclose(y, lay["y"], rtol=1e-13, atol=1e-13)
+    assert np.array_equal(y[lay["dropped"]], x[lay["dropped"]])
+
+
+def pin_backward_rss_loops(rng):
+    """The root-sum-square scales backward reports beside each gradient that
+    sums over tokens are sqrt(sum_t term_t^2) over that sum's terms, written
+    here as explicit loops from quantities recomputed by loops: dbias_i sums
+    dh[t, i]; dW_r[i, k] sums dh[t, i] x[t, k]; dW_in[e][j, k] sums du[t, j]
+    x[t, k] and dW_out[e][n, j] sums g_t dy[t, n] h[t, j] over e's kept
+    tokens, with u = W_in x, h = ReLU(u), du = [u > 0] W_out^T (g dy).  dh
+    is the oracle's dL/dh (pinned to finite differences above).  Also: the
+    magnitude of a sum of n terms is at most sqrt(n) times the scale
+    (Cauchy-Schwarz), and equals the scale when one token contributes."""
+    T, d, f, N = 9, 3, 4, 3
+    x, w_r, w_in, w_out = _rand_layer(rng, T, d, f, N, scale=1.5)
+    dy = rng.standard_normal((T, d))
+    C = so.expert_capacity(T, N, 1.0)
+    g = so.backward(x, w_r, np.array([0.3, 0.0, -0.2]), w_in, w_out, C, dy, 0.7)
+    fw = g["forward"]
+    dh = g["dlogits"]
+    for i in range(N):
+        assert abs(g["d_router_bias_rss"][i] - math.sqrt(sum(dh[t, i] ** 2 for t in range(T)))) < 1e-12
+        for k in range(d):
+            ref = math.sqrt(sum((dh[t, i] * x[t, k]) ** 2 for t in range(T)))
+            assert abs(g["dw_router_rss"][i, k] - ref) < 1e-12
+    for e in range(N):
+        rows = [t for t in range(T) if fw["expert_idx"][t] == e and not fw["dropped"][t]]
+        u = {t: [sum(w_in[e, j, k] * x[t, k] for k in range(d)) for j in range(f)] for t in rows}
+        gd = {t: [fw["gate"][t] * dy[t, n] for n in range(d)] for t in rows}
+        du = {t: [(u[t][j] > 0) * sum(w_out[e, n, j] * gd[t][n] for n in range(d)) for j in range(f)] for t in rows}
+        for j in range(f):
+            for k in range(d):
+                ref = math.sqrt(sum((du[t][j] * x[t, k]) ** 2 for t in rows))
+                assert abs(g["dw_in_rss"][e][j, k] - ref) < 1e-12
+        for n in range(d):
+            for j in range(f):
+                ref = math.sqrt(sum((gd[t][n] * max(u[t][j], 0.0)) ** 2 for t in rows))
+                assert abs(g["dw_out_rss"][e][n, j] - ref) < 1e-12
+        if len(rows) == 1:
+            np.testing.assert_allclose(g["dw_in_rss"][e], np.abs(g["dw_in"][e]), rtol=1e-12, atol=1e-15)
+    # Cauchy-Schwarz: |sum of n terms| <= sqrt(n) * their root sum of squares
+    assert np.all(math.sqrt(T) * g["d_router_bias_rss"] >= np.abs(g["d_router_bias"]) - 1e-15)
+    assert np.all(math.sqrt(T) * g["dw_router_rss"] >= np.abs(g["dw_router"]) - 1e-15)
+    for e in range(N):
+        n = max(1, int(np.sum((fw["expert_idx"] == e) & ~fw["dropped"])))
+        assert np.all(math.sqrt(n) * g["dw_in_rss"][e] >= np.abs(g["dw_in"][e]) - 1e-15)
+        assert np.all(math.sqrt(n) * g["dw_out_rss"][e] >= np.abs(g["dw_out"][e]) - 1e-15)
+
+
 ALL_PINS = [
     pin_capacity_table, pin_hand_example, pin_softmax_library, pin_top1_bruteforce,
     pin_router_logits_loops, pin_slots_stable_sort, pin_slots_bruteforce,
@@ -516,7 +637,8 @@ ALL_PINS = [
     pin_topk_hand_example, pin_topk_choice_loops, pin_topk_k1_is_switch, pin_topk_dense_mixture,
     pin_topk_route_major_bruteforce, pin_topk_aux_uniform,
     pin_backward_finite_differences, pin_backward_aux_closed_form, pin_backward_single_expert_dense,
-    pin_backward_dropped_tokens,
+    pin_backward_dropped_tokens, pin_forward_sampled_experts, pin_combine_residual,
+    pin_combine_residual_matches_layer, pin_backward_rss_loops,
 ]
 
 
@@ -682,9 +804,77 @@ def _mut_bwd_residual_ignored(*args, **kw):
     return out
 
 
+def _mut_forward_sample_all_nan(*args, **kw):
+    out = _ORIG["forward"](*args, **kw)
+    if kw.get("experts") is not None:
+        out["y_bare"][~out["dropped"]] = np.nan
+        out["y"] = out["y_bare"]
+    return out
+
+
+def _mut_forward_sample_zero_rows(*args, **kw):
+    out = _ORIG["forward"](*args, **kw)
+    if kw.get("experts") is not None:
+        out["y_bare"] = np.nan_to_num(out["y_bare"], nan=0.0)
+        out["y"] = out["y_bare"]
+    return out
+
+
+def _mut_forward_sample_shifted(*args, **kw):
+    # computes the sampled rows with the next expert's weights
+    S = kw.get("experts")
+    if S is None:
+        return _ORIG["forward"](*args, **kw)
+    x, w_r, b, w_in, w_out, cap = args[:6]
+    n = np.asarray(w_r).shape[0]
+    get = _ORIG["_weights"](w_in, w_out)
+    kw = dict(kw)
+    return _ORIG["forward"](x, w_r, b, lambda i: get((i + 1) % n), None, cap, *args[6:], **kw)
+
+
+def _mut_combine_residual_kept_only(expert_out, expert_idx, slot, dropped, gate, x_residual=None):
+    y = _ORIG["combine"](expert_out, expert_idx, slot, dropped, gate)
+    if x_residual is not None:
+        y[~dropped] += np.asarray(x_residual, np.float64)[~dropped]
+    return y
+
+
+def _mut_combine_residual_ignored(expert_out, expert_idx, slot, dropped, gate, x_residual=None):
+    return _ORIG["combine"](expert_out, expert_idx, slot, dropped, gate)
+
+
+def _mut_bwd_rss_squared(*args, **kw):
+    out = _ORIG["backward"](*args, **kw)
+    out["d_router_bias_rss"] = out["d_router_bias_rss"] ** 2
+    out["dw_router_rss"] = out["dw_router_rss"] ** 2
+    out["dw_in_rss"] = [None if r is None else r ** 2 for r in out["dw_in_rss"]]
+    out["dw_out_rss"] = [None if r is None else r ** 2 for r in out["dw_out_rss"]]
+    return out
+
+
+def _mut_bwd_rss_router_without_x(*args, **kw):
+    out = _ORIG["backward"](*args, **kw)
+    out["dw_router_rss"] = np.broadcast_to(out["d_router_bias_rss"][:, None], out["dw_router_rss"].shape).copy()
+    return out
+
+
+def _mut_bwd_rss_out_pre_relu(*args, **kw):
+    out = _ORIG["backward"](*args, **kw)
+    x, w_r, b, w_in, w_out, cap, dy = args[:7]
+    fw = out["forward"]
+    for e in range(len(out["dw_out_rss"])):
+        rows = np.nonzero((fw["expert_idx"] == e) & ~fw["dropped"])[0]
+        if len(rows) and out["dw_out_rss"][e] is not None:
+            u = np.asarray(x)[rows] @ np.asarray(w_in[e]).T
+            gd = fw["gate"][rows, None] * np.asarray(dy)[rows]
+            out["dw_out_rss"][e] = np.sqrt((gd ** 2).T @ (u ** 2))
+    return out
+
+
 _ORIG = {k: getattr(so, k) for k in ("softmax_backward", "expert_backward", "backward","assign_slots", "load_balancing_loss", "top1", "expert_ffn",
                                      "softmax", "router_logits", "add_normalize", "topk_choice",
-                                     "load_balancing_loss_topk", "forward_topk")}
+                                     "load_balancing_loss_topk", "forward_topk", "forward", "combine",
+                                     "_weights")}
 
 MUTANTS = {
     "top1_last_index_on_tie": ("top1", _mut_top1_last_tie),
@@ -710,6 +900,14 @@ MUTANTS = {
     "bwd_w_out_grad_pre_relu": ("expert_backward", _mut_expert_bwd_pre_relu),
     "bwd_aux_ignored": ("backward", _mut_bwd_aux_ignored),
     "bwd_residual_ignored": ("backward", _mut_bwd_residual_ignored),
+    "sampled_experts_all_nan": ("forward", _mut_forward_sample_all_nan),
+    "sampled_experts_zero_rows": ("forward", _mut_forward_sample_zero_rows),
+    "sampled_experts_wrong_weights": ("forward", _mut_forward_sample_shifted),
+    "combine_residual_on_kept_rows_only": ("combine", _mut_combine_residual_kept_only),
+    "combine_residual_ignored": ("combine", _mut_combine_residual_ignored),
+    "bwd_rss_without_sqrt": ("backward", _mut_bwd_rss_squared),
+    "bwd_rss_router_without_x": ("backward", _mut_bwd_rss_router_without_x),
+    "bwd_rss_w_out_pre_relu": ("backward", _mut_bwd_rss_out_pre_relu),
 }
 
 
