@@ -55,7 +55,7 @@ bool mul(size_t &out, std::initializer_list<int64_t> xs) {
 int esize(int dtype) { return dtype == SWITCH_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t bcount = 0, boff = 0, ppart = 0, psum = 0, rank = 0, logits = 0, route_end = 0;
+  size_t bcount = 0, boff = 0, ppart = 0, psum = 0, rank = 0, logits = 0, wplanes = 0, route_end = 0;
   size_t fz_sync = 0, fz_aggc = 0, fz_aggp = 0, fz_incc = 0, fz_incp = 0;  // single-pass routing
   size_t fz_clear = 0;
   int64_t fz_stride = 0;
@@ -81,7 +81,8 @@ int check_shape(const switch_shape *s) {
 
 // Workspace of a call with k routes per token: the router's per-block
 // partials (k blocks per router block), the route ranks, the logits rows when
-// the experts do not fit one chunk, then the layer's hidden activations and
+// the experts do not fit one chunk, W_r's bf16 planes (bf16 layers), then the
+// layer's hidden activations and
 // slot maps; k > 1 adds the slot -> output row map and the [k][T][d] buffer of
 // gate-scaled expert outputs per route.
 int layout(const switch_shape *s, Layout &L, int k = 1) {
@@ -89,6 +90,7 @@ int layout(const switch_shape *s, Layout &L, int k = 1) {
   const int64_t nb = router_blocks(T) * k, Tp = router_blocks(T) * kRouterTokens * k;
   const int es = esize(s->dtype);
   size_t bc, pp, ps, rk, lg = 0, hid, act, tk, rt = 0, sy, r32, r64;
+  const size_t wpl = s->dtype == SWITCH_BF16 ? (size_t)router_planes_bytes((int)N, (int)d) : 0;
   const int64_t Np = count_stride((int)N), Ns = (N + 63) / 64 * 64;
   bool ok = mul(bc, {nb, Np, 4}) && mul(pp, {nb, Np, 4}) && mul(ps, {N, 4}) && mul(rk, {Tp, 4}) &&
             mul(sy, {nb + 4, 4}) && mul(r32, {nb, Ns, 4}) && mul(r64, {nb, Ns, 8}) &&
@@ -108,6 +110,8 @@ int layout(const switch_shape *s, Layout &L, int k = 1) {
   o = align_up(o + rk);
   L.logits = o;
   o = align_up(o + lg);
+  L.wplanes = o;
+  o = align_up(o + wpl);
   L.fz_sync = o;  // ticket, error word and block states; then the look-back rows
   L.fz_clear = (sy + 15) / 16 * 16;
   o = align_up(o + sy);
@@ -225,6 +229,7 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
   a.w_r = w_router;
   a.bias = router_bias;
   a.logits = (float *)(w + L.logits);
+  a.wplanes = w + L.wplanes;
   a.expert_idx = expert_idx;
   a.gate = gate;
   a.slot = slot;
@@ -312,11 +317,12 @@ int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *
 
 // Workspace of switch_layer_backward: du [N][C][d_ff], the per-token partial
 // dots [T][n_dg], the experts' part of dx [T][d] (fp32), dL/dh [T][N], the
-// logits scratch when N > kRouterChunk, and the split partial sums of dW_r
-// and the bias gradient.
+// logits scratch when N > kRouterChunk, W_r's bf16 planes for the logits
+// (bf16 layers), the split partial sums of dW_r and the bias gradient, and the
+// bf16 planes of the dx product.
 struct BwdLayout {
-  size_t du = 0, dgpart = 0, dxe = 0, dh = 0, logits = 0, wpart = 0, bpart = 0, aplanes = 0, bplanes = 0,
-         total = 0;
+  size_t du = 0, dgpart = 0, dxe = 0, dh = 0, logits = 0, wplanes = 0, wpart = 0, bpart = 0, aplanes = 0,
+         bplanes = 0, total = 0;
   int n_dg = 0, splits = 1, kp = 0;
 };
 
@@ -328,6 +334,7 @@ int bwd_layout(const switch_shape *s, BwdLayout &B) {
   B.kp = router_dx_kp((int)N);
   size_t du, dg, dxe, dh, lg = 0, wp, bp, ap = 0, bq = 0;
   const bool planes = s->dtype == SWITCH_BF16;  // the MFMA dx product of bf16 layers
+  const size_t wpl = planes ? (size_t)router_planes_bytes((int)N, (int)d) : 0;  // the logits' W_r planes
   bool ok = mul(du, {N, C, f, es}) && mul(dg, {T, B.n_dg, 4}) && mul(dxe, {T, d, 4}) && mul(dh, {T, N, 4}) &&
             (N <= kRouterChunk || mul(lg, {T, N, 4})) && mul(wp, {B.splits, N, d, 4}) &&
             mul(bp, {router_blocks(T), N, 4}) && (!planes || (mul(ap, {T, B.kp, 2}) && mul(bq, {B.kp, d, 2})));
@@ -343,6 +350,8 @@ int bwd_layout(const switch_shape *s, BwdLayout &B) {
   o = align_up(o + dh);
   B.logits = o;
   o = align_up(o + lg);
+  B.wplanes = o;
+  o = align_up(o + wpl);
   B.wpart = o;
   o = align_up(o + wp);
   B.bpart = o;
@@ -400,7 +409,8 @@ int layer_backward(const switch_shape *s, const void *x, const float *w_router, 
   hipError_t e;
   if ((e = launch_bwd_experts(bl, st, marks)) != hipSuccess) return hip_fail(e, "backward expert launch");
   RouterBwdArgs ra{s->dtype, s->tokens, s->d_model, s->num_experts, x, w_router, router_bias,
-                   (float *)(w + B.logits), expert_idx, dropped, expert_count, (const float *)(w + B.dgpart),
+                   (float *)(w + B.logits), w + B.wplanes, expert_idx, dropped, expert_count,
+                   (const float *)(w + B.dgpart),
                    B.n_dg, d_aux, (const float *)(w + B.dxe), dy, add_residual ? 1 : 0, (float *)(w + B.dh), dx,
                    dw_router, d_router_bias, (float *)(w + B.wpart), (float *)(w + B.bpart), w + B.aplanes,
                    w + B.bplanes, B.kp};

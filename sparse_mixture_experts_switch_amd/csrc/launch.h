@@ -26,6 +26,7 @@ struct RouteArgs {
   const void *x;
   const float *w_r, *bias;
   float *logits;  // [T][N] scratch, only used when N > kRouterChunk
+  void *wplanes;  // bf16 layers: W_r split into bf16 planes in MFMA fragment order (router_planes_bytes)
   int32_t *expert_idx;
   float *gate;
   int32_t *slot;  // slot of each token (assignment output)
@@ -205,6 +206,7 @@ struct RouterBwdArgs {
   const void *x;
   const float *w_r, *bias;
   float *logits;  // [T][N] scratch when N > kRouterChunk
+  void *wplanes;  // bf16 layers: router_planes_bytes of scratch for the logits' W_r planes
   const int32_t *expert_idx;
   const uint8_t *dropped;
   const int32_t *expert_count;
@@ -251,6 +253,12 @@ hipError_t launch_router_wgrad_bf16(const float *dh, const void *x, int64_t T, i
                                     float *wpart, hipStream_t st);
 
 __host__ __device__ inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
+// Bytes of W_r split into three bf16 planes, laid out in the order the bf16
+// router's MFMA waves load them: [ceil(N / 16)][d / 32][3 planes][64 lanes]
+// pieces of 16 bytes (the router writes them, then reads them, each call).
+__host__ __device__ inline int64_t router_planes_bytes(int N, int d) {
+  return (int64_t)((N + 15) / 16) * (d / 32) * 3 * 64 * 16;
+}
 // Row stride (elements) of the per-block count and P-partial arrays: rows
 // start on 16-byte boundaries.
 __host__ __device__ inline int count_stride(int N) { return (N + 3) & ~3; }

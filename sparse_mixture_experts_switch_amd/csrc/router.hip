@@ -21,9 +21,11 @@
 //
 // bf16 activations: the contraction runs on bf16 MFMA.  W_r (fp32) is split
 // exactly into three bf16 planes hi + mid + lo (each plane takes the next 8
-// significant bits; every block splits the fp32 rows as it stages them), so
-// every product x_k * plane_k is exact in fp32 and the fp32 accumulation sees
-// the same terms as an fp32 dot product.
+// significant bits), once per call by a small kernel that also lays them out
+// in MFMA fragment order, so every product x_k * plane_k is exact in fp32 and
+// the fp32 accumulation sees the same terms as an fp32 dot product.  The
+// softmax uses the accurate expf (not the fast exp intrinsic) and an IEEE
+// division for the gate.
 // fp32 activations: plain fp32 FMA on the vector ALUs.
 
 #include <algorithm>
@@ -119,7 +121,7 @@ __device__ __forceinline__ bool topk_before(float va, int ia, float vb, int ib) 
 // also go to LDS, the sums as 2^-31 fixed point (s_pfix), for the single-pass
 // assignment that follows in the same kernel.
 template <int kThreads, bool kLds, int kK>
-__device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t t0, int64_t blk, TopK tk,
+__device__ __forceinline__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t t0, int64_t blk, TopK tk,
                                 int32_t *__restrict__ expert_idx, float *__restrict__ gate,
                                 int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
                                 float *__restrict__ ppart, float *s_max, float *s_inv, int *s_e, int *s_e2,
@@ -174,7 +176,7 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       constexpr int kJ = kRouterChunk / kLpt;
       float ev[kJ];
 #pragma unroll
-      for (int i = 0; i < kJ; ++i) ev[i] = q + i * kLpt < N ? __expf(lg.at(t, q + i * kLpt) - best) : 0.f;
+      for (int i = 0; i < kJ; ++i) ev[i] = q + i * kLpt < N ? expf(lg.at(t, q + i * kLpt) - best) : 0.f;
 #pragma unroll
       for (int i = 0; i < kJ; ++i) {
         if (q + i * kLpt < N) lg.at(t, q + i * kLpt) = ev[i];
@@ -182,7 +184,7 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       }
     } else {
       for (int j = q; j < N; j += kLpt) {
-        const float ev = __expf(lg.at(t, j) - best);
+        const float ev = expf(lg.at(t, j) - best);
         lg.at(t, j) = ev;
         sum += ev;
       }
@@ -199,7 +201,7 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       if (kK == 2) {
         s_e2[t] = si;
         expert_idx[tk.T + t0 + t] = si;
-        gate[tk.T + t0 + t] = __expf(sec - best) * inv;
+        gate[tk.T + t0 + t] = expf(sec - best) * inv;
       }
     }
   }
@@ -209,7 +211,7 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
     const int j = j0 + tid / kTpe, r = tid % kTpe;
     float p = 0.f;
     int c = 0, c2 = 0;
-    if (j < N) {
+    if (j < N && tid < kThreads) {
 #pragma unroll
       for (int i = 0; i < kUpt; ++i) {
         const int u = r * kUpt + i;
@@ -226,7 +228,7 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
       c += __shfl_xor(c, off, kWave);
       if (kK == 2) c2 += __shfl_xor(c2, off, kWave);
     }
-    if (r == 0 && j < N) {
+    if (r == 0 && j < N && tid < kThreads) {
       ppart[blk * Np + j] = p;
       bcount[blk * Np + j] = c;
       if (kK == 1 && s_cnt) {
@@ -254,218 +256,487 @@ __device__ void router_epilogue(const LogitRows<kLds> lg, int nt, int N, int64_t
   }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 activations, 3-plane bf16 MFMA (v_mfma_f32_16x16x32_bf16).
-// 8 waves in two roles, one of each on every SIMD, so that staging and
-// matrix work overlap instead of taking turns:
-//  - waves 4..7 stage: they load the block's 64 token rows (bf16) and the
-//    fp32 rows of a 128-expert chunk of W_r 64 contraction columns at a time
-//    (row-contiguous loads, a register ring up to two chunks ahead) and write
-//    them to a padded LDS buffer;
-//  - waves 0..3 multiply: wave w computes experts [c0 + 32w, c0 + 32w + 32)
-//    for all 64 tokens (4 token tiles x 2 expert tiles of 16x16) from the
-//    other LDS buffer, splitting its W_r operands into the three bf16 planes
-//    as it reads them (fp32 in LDS costs fewer bytes than three planes).
-// One barrier per chunk swaps the two buffers.  Every block reads the same
-// W_r rows (from L2); the blocks of one XCD start their walk over the
-// contraction at different chunks so that they do not all ask for the same
-// cache lines at once.
-// MFMA operand layout (16x16x32): lane l supplies row (l % 16) and the 8
-// consecutive k values starting at 8 * (l / 16); the result lane l holds
-// column (l % 16), rows 4 * (l / 16) + i.
-// ---------------------------------------------------------------------------
+// Threads of the router epilogue (8 waves: 8 lanes per token, 4 per expert),
+// 16-token MFMA tiles per router block, and the LDS logit rows of a block
+// when every expert fits one chunk: 160 floats per token (a row starts 32
+// banks after the previous one, so the epilogue's 16-byte row reads and its
+// column reads are free of bank conflicts).
 constexpr int kRBThreads = 512;
-constexpr int kStageThreads = 256;           // waves 4..7
 constexpr int kTokTiles = kRouterTokens / 16;
-constexpr int kRKC = 64;                     // contraction columns per chunk
-constexpr int kRLS = kRKC + 8;               // padded LDS row of x (bf16)
-constexpr int kWLS = kRKC + 4;               // padded LDS row of W_r (fp32)
-constexpr int kXPer = kRouterTokens * (kRKC / 8) / kStageThreads;  // 16-byte x pieces per staging thread
-constexpr int kWGrp = kRouterChunk * (kRKC / 8) / kStageThreads;   // 8-value W_r groups per staging thread
-constexpr int kXStage = kRouterTokens * kRLS * 2;                  // bytes per x stage
-constexpr int kWStage = kRouterChunk * kWLS * 4;                   // bytes per W_r stage
-constexpr int kRouterStageBytes = 2 * (kXStage + kWStage);
-constexpr int kRouterLgBytes = kRouterTokens * (kRouterChunk + 1) * 4;
-constexpr int kRouterSmem = kRouterStageBytes > kRouterLgBytes ? kRouterStageBytes : kRouterLgBytes;
+constexpr int kLgStride = 160;
+constexpr int kRouterLgBytes = kRouterTokens * kLgStride * 4;
 
-// LDS of one router block (bf16 path).
-struct RouterSmem {
-  __attribute__((aligned(16))) char stage[kRouterSmem];
+// ---------------------------------------------------------------------------
+// Forward router, bf16 activations: the layer's routing step.  Each
+// workgroup owns one router block (64 tokens) and runs 12 waves in two roles:
+//  - waves 8..11 stream the block's rows of x through LDS in chunks of 256
+//    contraction columns (double-buffered: chunk 0 is requested alone so
+//    that it arrives first, then each thread keeps the next two chunks in
+//    registers);
+//  - waves 0..7 multiply: wave w owns experts [c0 + 16 w, c0 + 16 w + 16) of
+//    a 128-expert chunk for all 64 tokens.  Its W_r operands come straight
+//    from global memory (the 393 KB of W_r stay in every XCD's L2) into
+//    registers, 8 fp32 per lane per 32-column step, four steps ahead, and
+//    are split there into the three bf16 planes; the x operands are 16-byte
+//    LDS reads.  Each plane has its own fp32 accumulator (the small planes
+//    accumulate apart from the large one) and the logit is
+//    hi + (mid + lo) at the end.
+// x in LDS: piece-major ([32 pieces][64 tokens + 1] slots of 16 bytes), so
+// the 16 lanes of an MFMA row group read 256 contiguous bytes and the
+// staging stores of consecutive pieces fall on different banks.  One barrier
+// per chunk.  When d_model is a multiple of 256 every chunk is full: its 8
+// steps are unrolled without branches (the W_r operands 4 steps ahead come
+// from this chunk or, by fixed offsets, the next), so the compiler overlaps
+// one step's split and loads with the previous step's MFMAs; blocks on one
+// XCD then also start their walk over the contraction at different chunks.
+// Other widths take a general loop.
+// MFMA operand layout (16x16x32 bf16): lane l supplies row (l % 16) and the 8
+// consecutive k values starting at 8 * (l / 16); result lane l holds column
+// (l % 16), rows 4 * (l / 16) + i.
+// ---------------------------------------------------------------------------
+constexpr int kFwMfmaWaves = 8;
+constexpr int kFwStageThreads = 4 * kWave;
+constexpr int kFwThreads = kFwMfmaWaves * kWave + kFwStageThreads;  // 768
+constexpr int kFwKc = 256;                                          // contraction columns per x chunk
+constexpr int kFwPieces = kFwKc / 8;                                // 16-byte pieces of a row per chunk
+constexpr int kFwPitch = kRouterTokens + 1;                         // slots per piece (one pad slot)
+constexpr int kFwBuf = kFwPieces * kFwPitch * 16;                   // bytes per x buffer
+constexpr int kFwStagePer = kRouterTokens * kFwPieces / kFwStageThreads;  // pieces per staging thread
+constexpr int kFwRing = 4;                                          // W_r steps in flight per wave
+
+// LDS bytes of the single-pass tail (see route_fused_tail) for N experts
+__host__ __device__ constexpr int fused_tail_bytes(int N) { return N * 24 + kRouterTokens * 4 + 16 * 8 + 16; }
+
+// x buffers; after the contraction the logit rows, then (single pass) the
+// look-back tail's LDS or (backward) the dx scratch reuse the same bytes
+constexpr int kFwSmemX = 2 * kFwBuf > kRouterLgBytes + fused_tail_bytes(kFusedMaxExperts)
+                             ? 2 * kFwBuf
+                             : (kRouterLgBytes + fused_tail_bytes(kFusedMaxExperts) + 15) / 16 * 16;
+struct RouterFwSmem {
+  __attribute__((aligned(16))) char x[kFwSmemX];
+  uint64_t mask[2][kRouterChunk];  // per route and expert: the block's tokens that chose it (bit t)
+  float red[4][kRouterChunk];      // P partial sums of four 16-token groups
   float s_max[kRouterTokens], s_inv[kRouterTokens];
   int s_e[kRouterTokens], s_e2[kRouterTokens];
 };
+static_assert(kRouterLgBytes <= 2 * kFwBuf, "logit rows fit in the x buffers");
 
-// Logits (+ bias) of block `blk` (tokens [64 blk, 64 blk + 64)) into LDS
-// (N <= kRouterChunk) or the block's rows of the global scratch; returns
-// after a barrier with the logits complete.  Starts with a barrier, so
-// consecutive calls by one workgroup may reuse `sm`.
+// Workgroup barrier that orders LDS traffic only: each wave waits for its own
+// LDS (and scalar memory) operations, then meets the others.  Unlike
+// __syncthreads it does not wait for the wave's global loads in flight
+// (gfx9 counts loads and stores together, so a release fence would drain the
+// W_r register ring and the staging loads at every chunk).  The memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 12 MFMAs of one 32-column step: 4 token tiles x 3 planes.
+__device__ __forceinline__ void fw_step_mfma(f32x4 (&acc)[3][kTokTiles], const bf16x8 (&a)[kTokTiles],
+                                             const bf16x8 (&pln)[3]) {
+#pragma unroll
+  for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+    for (int tb = 0; tb < kTokTiles; ++tb)
+      acc[pl][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], pln[pl], acc[pl][tb], 0, 0, 0);
+}
+
 template <bool kLds>
-__device__ __forceinline__ LogitRows<kLds> router_contract_bf16(
-    const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
-    int64_t T, int d, int N, float *__restrict__ logits_g, int64_t blk, RouterSmem &sm) {
-  static_assert(kRBThreads == 8 * kWave && kStageThreads == 4 * kWave && kRouterChunk == 128,
-                "4 MFMA waves x 32 experts + 4 staging waves");
-  static_assert(kXPer * kStageThreads == kRouterTokens * (kRKC / 8), "x pieces");
-  static_assert(kWGrp * kStageThreads == kRouterChunk * (kRKC / 8), "W_r groups");
-  char *const smem = sm.stage;
-  char *xs = smem;                    // [2][64][kRLS] bf16
-  char *ws = smem + 2 * kXStage;      // [2][128][kWLS] fp32
-
-  constexpr int kRing = kLds ? 3 : 2;  // register ring depth of the staging waves
+__device__ __forceinline__ LogitRows<kLds> router_fwd_contract_bf16(
+    const bf16 *__restrict__ x, const u32x4 *__restrict__ wplanes, const float *__restrict__ bias,
+    int64_t T, int d, int N, float *__restrict__ logits_g, int64_t blk, RouterFwSmem &sm) {
+  static_assert(kFwStagePer * kFwStageThreads == kRouterTokens * kFwPieces, "staging plan");
+  static_assert(kFwMfmaWaves * 16 == kRouterChunk, "16 experts per MFMA wave");
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const bool stager = wave >= 4;  // wave-uniform role
-  const int ptid = tid - kStageThreads;
-  const int r16 = lane % 16, kq = (lane / 16) * 8;
-  const int nk = d / kRKC;
-  const int rot = (int)((blk / 8) % nk);  // first chunk of this block's walk (blocks b, b + 8, ... share an XCD)
+  const int nkc = (int)ceil_div(d, kFwKc);            // x chunks per expert chunk
+  const int nec = kLds ? 1 : (int)ceil_div(N, kRouterChunk);
+  const int Q = nkc * nec;                            // chunks in the walk
+  const int S = d / 32;                               // 32-column steps per expert chunk
+  const bool full = d % kFwKc == 0;                   // every chunk 8 steps
+  const int rot = full ? (int)((blk / 8) % nkc) : 0;
 
   LogitRows<kLds> lg;
   if (kLds) {
-    lg.base = (float *)smem;  // reuses the staging buffers after the contraction
-    lg.stride = kRouterChunk + 1;
+    lg.base = (float *)sm.x;
+    lg.stride = kLgStride;
   } else {
     lg.base = logits_g + t0 * N;
     lg.stride = N;
   }
 
-  // Staging plan.  x: piece i covers 16 bytes of token row i / 8.  W_r:
-  // group g covers 8 consecutive fp32 values of expert row g / 8.
-  const bf16 *xsrc[kXPer];
-  int xoff[kXPer];
+  if (wave >= kFwMfmaWaves) {
+    // ---- staging: chunk q of the walk holds columns [kc * 256, ...) of x,
+    // kc = (q mod nkc + rot) mod nkc; thread piece u covers row i / 32,
+    // piece i mod 32 (i = st + 256 u); pieces past a short chunk's width
+    // are loaded clamped and stored to slots no one reads.
+    const int st = tid - kFwMfmaWaves * kWave;
+    const bf16 *src[kFwStagePer];
+    int off[kFwStagePer], pc[kFwStagePer];
 #pragma unroll
-  for (int q = 0; q < kXPer; ++q) {
-    const int i = max(ptid, 0) + q * kStageThreads, r = i / 8, c = i % 8;
-    xsrc[q] = x + (t0 + min(r, nt - 1)) * d + c * 8;
-    xoff[q] = (r * kRLS + c * 8) * 2;
-  }
-
-  for (int c0 = 0; c0 < N; c0 += kRouterChunk) {
-    const float *wsrc[kWGrp];
-    int woff[kWGrp];
-#pragma unroll
-    for (int q = 0; q < kWGrp; ++q) {
-      const int g = max(ptid, 0) + q * kStageThreads, e = g / 8, c = g % 8;
-      wsrc[q] = w_r + (int64_t)min(c0 + e, N - 1) * d + c * 8;
-      woff[q] = (e * kWLS + c * 8) * 4;
+    for (int u = 0; u < kFwStagePer; ++u) {
+      const int i = st + u * kFwStageThreads, r = i / kFwPieces;
+      pc[u] = i % kFwPieces;
+      src[u] = x + (t0 + min(r, nt - 1)) * d;
+      off[u] = (pc[u] * kFwPitch + r) * 16;
     }
-    u32x4 xr[kRing][kXPer];
-    f32x4 wr[kRing][kWGrp][2];
-    // chunk ch of the walk (ch >= nk: a repeat of the last one, never used)
-    auto fetch = [&](int slot, int ch) {
-      int kc = min(ch, nk - 1) + rot;
-      kc = (kc >= nk ? kc - nk : kc) * kRKC;
+    u32x4 ring[2][kFwStagePer];
+    auto load = [&](int slot, int q) {
+      q = min(q, Q - 1);
+      int kc = q % nkc + rot;
+      kc = kc >= nkc ? kc - nkc : kc;
+      const int c0 = kc * kFwKc, np = min(kFwKc, d - c0) / 8;
 #pragma unroll
-      for (int q = 0; q < kXPer; ++q) xr[slot][q] = *(const u32x4 *)(xsrc[q] + kc);
-#pragma unroll
-      for (int q = 0; q < kWGrp; ++q) {
-        wr[slot][q][0] = *(const f32x4 *)(wsrc[q] + kc);
-        wr[slot][q][1] = *(const f32x4 *)(wsrc[q] + kc + 4);
-      }
+      for (int u = 0; u < kFwStagePer; ++u) ring[slot][u] = *(const u32x4 *)(src[u] + c0 + min(pc[u], np - 1) * 8);
     };
     auto store = [&](int slot, int buf) {
 #pragma unroll
-      for (int q = 0; q < kXPer; ++q) *(u32x4 *)(xs + buf * kXStage + xoff[q]) = xr[slot][q];
-#pragma unroll
-      for (int q = 0; q < kWGrp; ++q) {
-        *(f32x4 *)(ws + buf * kWStage + woff[q]) = wr[slot][q][0];
-        *(f32x4 *)(ws + buf * kWStage + woff[q] + 16) = wr[slot][q][1];
-      }
+      for (int u = 0; u < kFwStagePer; ++u) *(u32x4 *)(sm.x + buf * kFwBuf + off[u]) = ring[slot][u];
     };
-    f32x4 acc[kTokTiles][2];
-#pragma unroll
-    for (int tb = 0; tb < kTokTiles; ++tb) acc[tb][0] = acc[tb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    __syncthreads();  // previous chunk's readers of the staging buffers are done
-    if (stager) {
-#pragma unroll
-      for (int j = 0; j < kRing; ++j) fetch(j, j);
-      store(0, 0);
-    }
-    __syncthreads();
-    for (int base = 0; base < nk; base += kRing) {
-#pragma clang loop unroll(full)
-      for (int j = 0; j < kRing; ++j) {
-        const int ch = base + j;
-        if (stager) {
-          // slot j held chunk ch, already in LDS: refill it kRing chunks
-          // ahead, then move chunk ch + 1 into the other LDS buffer
-          fetch(j, ch + kRing);
-          store((j + 1) % kRing, (ch + 1) & 1);
-        } else if (ch < nk) {
-          const bf16 *xb = (const bf16 *)(xs + (ch & 1) * kXStage);
-          const float *wbuf = (const float *)(ws + (ch & 1) * kWStage);
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            bf16x8 b[2][3], a[kTokTiles];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const float *src = wbuf + (wave * 32 + q * 16 + r16) * kWLS + s * 32 + kq;
-              split3_x8(*(const f32x4 *)src, *(const f32x4 *)(src + 4), b[q][0], b[q][1], b[q][2]);
-            }
-#pragma unroll
-            for (int tb = 0; tb < kTokTiles; ++tb)
-              a[tb] = as_bf16x8(*(const u32x4 *)(xb + (tb * 16 + r16) * kRLS + s * 32 + kq));
-#pragma unroll
-            for (int pl = 0; pl < 3; ++pl)
-#pragma unroll
-              for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int tb = 0; tb < kTokTiles; ++tb)
-                  acc[tb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], b[q][pl], acc[tb][q], 0, 0, 0);
-          }
+    load(0, 0);
+    store(0, 0);
+    load(1, 1);
+    load(0, 2);
+    for (int q = 0; q < Q; ++q) {
+      lds_barrier();  // chunk q is in buffer q & 1; buffer (q + 1) & 1 is free
+      if (q + 1 < Q) {
+        if (q & 1) {
+          store(0, 0);
+          load(0, q + 3);
+        } else {
+          store(1, 1);
+          load(1, q + 3);
         }
-        __syncthreads();
       }
     }
-    // scatter each MFMA wave's 64 x 32 logits tile (the staging buffers are
-    // free: the loop ended with a barrier)
-    if (!stager) {
+    __syncthreads();  // every MFMA wave is past its last x read
+    if (kLds) {       // clear the rank masks for the epilogue
+      for (int i = tid - kFwMfmaWaves * kWave; i < 2 * kRouterChunk; i += kFwStageThreads)
+        (&sm.mask[0][0])[i] = 0;
+    }
+  } else {
+    // ---- multiply
+    const int r16 = lane % 16, kg = lane / 16;
+    f32x4 acc[3][kTokTiles];
+    u32x4 pring[kFwRing][3];
+    // planes of step g of expert chunk ec: tile ec * 8 + w (the last tile
+    // again past the experts), three contiguous 1 KB pieces, 16 bytes a lane
+    const int ntile = (N + 15) / 16;
+    auto pl_ptr = [&](int ec, int g) -> const u32x4 * {
+      const int m = min(ec * 8 + wave, ntile - 1);
+      return wplanes + ((int64_t)m * S + g) * 3 * kWave + lane;
+    };
+    auto pld = [&](int slot, const u32x4 *p) {
+      pring[slot][0] = p[0];
+      pring[slot][1] = p[kWave];
+      pring[slot][2] = p[2 * kWave];
+    };
+    auto planes = [&](int slot, bf16x8 (&pln)[3]) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int j = c0 + wave * 32 + q * 16 + r16;
-        if (j < N) {
-          const float bj = bias ? bias[j] : 0.f;
+      for (int pl = 0; pl < 3; ++pl) pln[pl] = as_bf16x8(pring[slot][pl]);
+    };
+    auto write_logits = [&](int ec) {
+      // chunk ec's logits (+ bias); in LDS, experts past N get -inf
+      const int j = ec * kRouterChunk + wave * 16 + r16;
+      const float bj = bias && j < N ? bias[j] : 0.f;
+#pragma unroll
+      for (int tb = 0; tb < kTokTiles; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tb * 16 + kg * 4 + i;
+          const float v = acc[0][tb][i] + (acc[1][tb][i] + acc[2][tb][i]) + bj;
+          if (kLds)
+            lg.at(t, j) = j < N ? v : -INFINITY;
+          else if (t < nt && j < N)
+            lg.at(t, j) = v;
+        }
+    };
+    auto zero_acc = [&]() {
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int tb = 0; tb < kTokTiles; ++tb) acc[pl][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    if (full) {
+      // chunk q: expert chunk q / nkc, contraction chunk (q mod nkc + rot)
+      // mod nkc, whose 8 steps' planes are consecutive
+      auto chunk_ptr = [&](int q) -> const u32x4 * {
+        q = min(q, Q - 1);
+        const int ec = q / nkc;
+        int kc = q - ec * nkc + rot;
+        kc = kc >= nkc ? kc - nkc : kc;
+        return pl_ptr(ec, kc * 8);
+      };
+      constexpr int kStep = 3 * kWave;  // u32x4 pieces per step
+      const u32x4 *cur = chunk_ptr(0);
+#pragma unroll
+      for (int r = 0; r < kFwRing; ++r) pld(r, cur + r * kStep);
+      int kcw = 0, ec = 0;  // position in the expert chunk's walk
+      for (int q = 0; q < Q; ++q) {
+        const u32x4 *nxt = chunk_ptr(q + 1);  // past the end: this chunk again (never used)
+        if (kcw == 0) zero_acc();
+        lds_barrier();  // x chunk q is in LDS
+        const char *xb = sm.x + (q & 1) * kFwBuf + (kg * kFwPitch + r16) * 16;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          bf16x8 pln[3];
+          planes(s % kFwRing, pln);
+          pld(s % kFwRing, s + kFwRing < 8 ? cur + (s + kFwRing) * kStep : nxt + (s + kFwRing - 8) * kStep);
+          __builtin_amdgcn_sched_barrier(0);  // the refill issues here, 4 steps before its use
+          bf16x8 a[kTokTiles];
 #pragma unroll
           for (int tb = 0; tb < kTokTiles; ++tb)
+            a[tb] = as_bf16x8(*(const u32x4 *)(xb + (s * 4 * kFwPitch + tb * 16) * 16));
+          fw_step_mfma(acc, a, pln);
+        }
+        cur = nxt;
+        if (++kcw == nkc) {
+          if (!kLds) write_logits(ec);
+          kcw = 0;
+          ++ec;
+        }
+      }
+    } else {
+      // general widths: x chunk g / 8 of the walk, the last one of each
+      // expert chunk short
+      int gn = 0, ecn = 0;  // next step to fetch (past the last one: the last one again)
+      auto fetch_next = [&](int slot) {
+        pld(slot, pl_ptr(ecn, gn));
+        if (++gn == S) {
+          if (ecn + 1 < nec) {
+            gn = 0;
+            ++ecn;
+          } else {
+            gn = S - 1;
+          }
+        }
+      };
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = tb * 16 + (lane / 16) * 4 + i;
-              if (t < nt) lg.at(t, kLds ? j - c0 : j) = acc[tb][q][i] + bj;
+      for (int r = 0; r < kFwRing; ++r) fetch_next(r);
+      const int total = nec * S;
+      int g = 0, ec = 0, q = 0;  // step within the expert chunk, expert chunk, x chunks started
+      for (int G0 = 0; G0 < total; G0 += kFwRing) {
+#pragma unroll
+        for (int r = 0; r < kFwRing; ++r) {
+          if (G0 + r < total) {
+            if (g == 0) zero_acc();
+            if ((g & 7) == 0) {
+              lds_barrier();  // x chunk q is in LDS
+              ++q;
             }
+            bf16x8 pln[3];
+            planes(r, pln);
+            fetch_next(r);
+            const char *xb = sm.x + ((q - 1) & 1) * kFwBuf + (((g & 7) * 4 + kg) * kFwPitch + r16) * 16;
+            bf16x8 a[kTokTiles];
+#pragma unroll
+            for (int tb = 0; tb < kTokTiles; ++tb) a[tb] = as_bf16x8(*(const u32x4 *)(xb + tb * 16 * 16));
+            fw_step_mfma(acc, a, pln);
+            if (g == S - 1 && !kLds) write_logits(ec);
+            if (++g == S) {
+              g = 0;
+              ++ec;
+            }
+          }
         }
       }
     }
-    if (kLds) break;  // N <= kRouterChunk: one chunk holds every expert
+    __syncthreads();  // every MFMA wave is past its last x read
+    if (kLds) write_logits(0);
   }
   __syncthreads();
   return lg;
 }
 
-// Router work of block `blk`: logits, then the forward epilogue.
-template <bool kLds, int kK>
-__device__ __forceinline__ void router_block_bf16(
-    const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
-    int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
-    float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
-    float *__restrict__ ppart, int64_t blk, RouterSmem &sm) {
-  const LogitRows<kLds> lg = router_contract_bf16<kLds>(x, w_r, bias, T, d, N, logits_g, blk, sm);
-  const int64_t t0 = blk * kRouterTokens;
-  const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
-  router_epilogue<kRBThreads, kLds, kK>(lg, nt, N, t0, blk, TopK{T, router_blocks(T)}, expert_idx, gate, slot_rank,
-                                        bcount, ppart, sm.s_max, sm.s_inv, sm.s_e, sm.s_e2);
+// W_r split into its three exact bf16 planes (hi + mid + lo, each taking the
+// next 8 significant bits) and laid out in MFMA fragment order, once per
+// call: piece (tile m, step g, plane p, lane l) holds the 8 values of expert
+// 16 m + l mod 16 (zeros past N) at contraction columns 32 g + 8 (l / 16) ..
+// + 8, so each router wave loads its operands of a step as three contiguous
+// 1 KB pieces (loads whose consecutive lanes read different rows of W_r
+// reach a fraction of the cache bandwidth).  One thread per (m, g, l).
+__global__ __launch_bounds__(256) void router_wplanes_kernel(const float *__restrict__ w_r, int N, int d,
+                                                             u32x4 *__restrict__ out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int S = d / 32;
+  const int l = (int)(i % kWave);
+  const int64_t mg = i / kWave;  // m * S + g
+  const int g = (int)(mg % S), m = (int)(mg / S);
+  const int row = m * 16 + l % 16;
+  f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, b = a;
+  if (row < N) {
+    const float *src = w_r + (int64_t)row * d + g * 32 + (l / 16) * 8;
+    a = *(const f32x4 *)src;
+    b = *(const f32x4 *)(src + 4);
+  }
+  bf16x8 hi, mid, lo;
+  split3_x8(a, b, hi, mid, lo);
+  u32x4 *o = out + mg * 3 * kWave + l;
+  o[0] = as_u32x4(hi);
+  o[kWave] = as_u32x4(mid);
+  o[2 * kWave] = as_u32x4(lo);
+}
+
+hipError_t launch_router_planes(const float *w_r, int N, int d, void *wplanes, hipStream_t st) {
+  const int64_t n = (int64_t)((N + 15) / 16) * (d / 32) * kWave;
+  router_wplanes_kernel<<<dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st>>>(w_r, N, d, (u32x4 *)wplanes, n);
+  return hipGetLastError();
+}
+
+// DPP moves within rows of 16 lanes: swap neighbours, swap pairs, mirror the
+// 8-lane halves (together a butterfly over each group of 8 lanes).
+__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_hmirror(int v) { return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false); }
+template <int kStep>
+__device__ __forceinline__ int dpp8(int v) {
+  return kStep == 0 ? dpp_xor1(v) : kStep == 1 ? dpp_xor2(v) : dpp_hmirror(v);
+}
+template <int kStep>
+__device__ __forceinline__ float dpp8f(float v) {
+  return __builtin_bit_cast(float, dpp8<kStep>(__builtin_bit_cast(int, v)));
+}
+
+// Epilogue of a router block whose logits (+ bias) sit in LDS rows of
+// kLgStride floats, experts past N holding -inf (N <= 128), run by the
+// first 512 threads:
+//  A. 8 lanes per token, lane q holding experts 32 c + 4 q + i (c, i < 4,
+//     four 16-byte reads): the best (and second best) logit and its expert
+//     (larger logit first, the lower index on equal logits), the sum of
+//     exp(h_j - max) and the probabilities p_j = exp(h_j - max) / sum,
+//     written back over the logits; reductions over the 8 lanes by DPP
+//     steps (every lane ends with the same bits); each route's choice sets
+//     the token's bit in the expert's mask;
+//  B. per expert: the block's P partial sum (four 16-token groups, then
+//     their sum in a fixed order), its count (bits of the mask) and, per
+//     token, the rank among the block's earlier tokens with the same expert
+//     (bits of the mask below the token's).
+// With s_cnt set (one route per token) the block's counts and P partial sums
+// also go to LDS, the sums as 2^-31 fixed point, for the single-pass
+// assignment.
+template <int kK>
+__device__ __forceinline__ void router_epilogue_lds(float *lg, RouterFwSmem &sm, int nt, int N, int64_t t0,
+                                                    int64_t blk, TopK tk, int32_t *__restrict__ expert_idx,
+                                                    float *__restrict__ gate, int32_t *__restrict__ slot_rank,
+                                                    int32_t *__restrict__ bcount, float *__restrict__ ppart,
+                                                    int *s_cnt = nullptr, int64_t *s_pfix = nullptr) {
+  static_assert(kK == 1 || kK == 2, "one or two routes per token");
+  const int tid = threadIdx.x;
+  if (tid < kRBThreads) {
+    const int t = tid >> 3, q = tid & 7;
+    float *row = lg + t * kLgStride + 4 * q;
+    float h[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 v = *(const f32x4 *)(row + 32 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[4 * c + i] = v[i];
+    }
+    float best = -INFINITY, sec = -INFINITY;
+    int bi = 0x7fffffff, si = 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) topk_take<kK>(h[4 * c + i], 32 * c + 4 * q + i, best, bi, sec, si);
+    auto merge = [&](float ov, int oi, float ov2, int oi2) {
+      if (kK == 2) {
+        if (topk_before(ov, oi, best, bi)) {  // theirs first; second: my first or their second
+          const bool mine = topk_before(best, bi, ov2, oi2);
+          sec = mine ? best : ov2;
+          si = mine ? bi : oi2;
+          best = ov;
+          bi = oi;
+        } else if (topk_before(ov, oi, sec, si)) {  // mine first; second: their first or my second
+          sec = ov;
+          si = oi;
+        }
+      } else if (topk_before(ov, oi, best, bi)) {
+        best = ov;
+        bi = oi;
+      }
+    };
+    merge(dpp8f<0>(best), dpp8<0>(bi), kK == 2 ? dpp8f<0>(sec) : 0.f, kK == 2 ? dpp8<0>(si) : 0);
+    merge(dpp8f<1>(best), dpp8<1>(bi), kK == 2 ? dpp8f<1>(sec) : 0.f, kK == 2 ? dpp8<1>(si) : 0);
+    merge(dpp8f<2>(best), dpp8<2>(bi), kK == 2 ? dpp8f<2>(sec) : 0.f, kK == 2 ? dpp8<2>(si) : 0);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      h[k] = expf(h[k] - best);  // exp(-inf) = 0 for the experts past N
+      sum += h[k];
+    }
+    sum += dpp8f<0>(sum);
+    sum += dpp8f<1>(sum);
+    sum += dpp8f<2>(sum);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *(f32x4 *)(row + 32 * c) = f32x4{h[4 * c] * inv, h[4 * c + 1] * inv, h[4 * c + 2] * inv, h[4 * c + 3] * inv};
+    if (q == 0 && t < nt) {
+      sm.s_e[t] = bi;
+      expert_idx[t0 + t] = bi;
+      gate[t0 + t] = inv;  // p_e = exp(h_e - max) / sum with h_e = max
+      __hip_atomic_fetch_or(&sm.mask[0][bi], 1ull << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (kK == 2) {
+        sm.s_e2[t] = si;
+        expert_idx[tk.T + t0 + t] = si;
+        gate[tk.T + t0 + t] = expf(sec - best) * inv;
+        __hip_atomic_fetch_or(&sm.mask[1][si], 1ull << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    // B1: P partial sums of 16-token groups (column reads of 64 consecutive experts)
+  }
+  __syncthreads();
+  if (tid < kRBThreads) {
+    const int j = tid & (kRouterChunk - 1), r = tid >> 7;
+    float p = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int tt = r * 16 + u;
+      if (tt < nt) p += lg[tt * kLgStride + j];
+    }
+    sm.red[r][j] = p;
+  }
+  __syncthreads();
+  const int64_t Np = count_stride(N);
+  if (tid < N) {
+    const int j = tid;
+    const float p = ((sm.red[0][j] + sm.red[1][j]) + sm.red[2][j]) + sm.red[3][j];
+    const int c = __popcll(sm.mask[0][j]);
+    ppart[blk * Np + j] = p;
+    bcount[blk * Np + j] = c;
+    if (kK == 1 && s_cnt) {
+      s_cnt[j] = c;
+      s_pfix[j] = p_fixed(p);
+    }
+    if (kK == 2) {
+      ppart[(tk.nb + blk) * Np + j] = 0.f;
+      bcount[(tk.nb + blk) * Np + j] = __popcll(sm.mask[1][j]);
+    }
+  }
+  if (tid < nt) {
+    const uint64_t below = (1ull << tid) - 1;
+    slot_rank[t0 + tid] = __popcll(sm.mask[0][sm.s_e[tid]] & below);
+    if (kK == 2) slot_rank[tk.nb * kRouterTokens + t0 + tid] = __popcll(sm.mask[1][sm.s_e2[tid]] & below);
+  }
 }
 
 template <bool kLds, int kK>
-__global__ __launch_bounds__(kRBThreads) void router_bf16_kernel(
-    const bf16 *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias,
+__global__ __launch_bounds__(kFwThreads) void router_fwd_bf16_kernel(
+    const bf16 *__restrict__ x, const u32x4 *__restrict__ wplanes, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
     float *__restrict__ gate, int32_t *__restrict__ slot_rank, int32_t *__restrict__ bcount,
     float *__restrict__ ppart) {
-  __shared__ RouterSmem sm;
-  router_block_bf16<kLds, kK>(x, w_r, bias, T, d, N, logits_g, expert_idx, gate, slot_rank, bcount, ppart,
-                              blockIdx.x, sm);
+  __shared__ RouterFwSmem sm;
+  const int64_t blk = blockIdx.x;
+  const LogitRows<kLds> lg = router_fwd_contract_bf16<kLds>(x, wplanes, bias, T, d, N, logits_g, blk, sm);
+  const int64_t t0 = blk * kRouterTokens;
+  const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
+  if (kLds)
+    router_epilogue_lds<kK>(lg.base, sm, nt, N, t0, blk, TopK{T, router_blocks(T)}, expert_idx, gate, slot_rank,
+                            bcount, ppart);
+  else
+    router_epilogue<kRBThreads, kLds, kK>(lg, nt, N, t0, blk, TopK{T, router_blocks(T)}, expert_idx, gate,
+                                          slot_rank, bcount, ppart, sm.s_max, sm.s_inv, sm.s_e, sm.s_e2);
 }
 
 // ---------------------------------------------------------------------------
@@ -569,7 +840,7 @@ constexpr int bwd_lds_floats() {
 // kDxHere: form dx in this kernel (fp32 layers, vector ALUs); otherwise
 // write the exact bf16 planes of dL/dh for the MFMA dx product (bf16 layers).
 template <typename T_, int kThreads, bool kLds, bool kDxHere>
-__device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0, const RouterBwdArgs &a,
+__device__ __forceinline__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0, const RouterBwdArgs &a,
                                     float *s_extra) {
   constexpr int kLpt = kThreads / kRouterTokens;  // lanes per token
   constexpr int kW = kThreads / kWave;
@@ -579,7 +850,8 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
   float *s_aux = s_extra;                // [kRouterChunk] (N <= kRouterChunk)
   float *s_wr = s_extra + kRouterChunk;  // [kW][kRouterChunk][kBwdWrCols]
   if (kLds) {
-    for (int j = tid; j < N; j += kThreads) s_aux[j] = caux * (float)a.expert_count[j];
+    if (tid < kThreads)
+      for (int j = tid; j < N; j += kThreads) s_aux[j] = caux * (float)a.expert_count[j];
     __syncthreads();
   }
   auto aux = [&](int j) { return kLds ? s_aux[j] : caux * (float)a.expert_count[j]; };
@@ -590,7 +862,7 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
 #pragma unroll
     for (int off = 1; off < kLpt; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
     float sum = 0.f;
-    for (int j = q; j < N; j += kLpt) sum += __expf(lg.at(t, j) - mx);
+    for (int j = q; j < N; j += kLpt) sum += expf(lg.at(t, j) - mx);
 #pragma unroll
     for (int off = 1; off < kLpt; off <<= 1) sum += __shfl_xor(sum, off, kWave);
     const float inv = 1.0f / sum;
@@ -604,7 +876,7 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
     for (int off = 1; off < kLpt; off <<= 1) dg += __shfl_xor(dg, off, kWave);
     float sdp = 0.f;
     for (int j = q; j < N; j += kLpt) {
-      const float pj = __expf(lg.at(t, j) - mx) * inv;
+      const float pj = expf(lg.at(t, j) - mx) * inv;
       const float dp = aux(j) + (j == e ? dg : 0.f);
       lg.at(t, j) = pj;
       sdp += dp * pj;
@@ -636,7 +908,7 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
   }
   __syncthreads();
   // bias partial of the block: sum over its tokens of dL/dh, in token order
-  for (int j = tid; j < N; j += kThreads) {
+  for (int j = tid; j < N && tid < kThreads; j += kThreads) {
     float b = 0.f;
     for (int u = 0; u < nt; ++u) b += lg.at(u, j);
     a.bpart[(t0 / kRouterTokens) * N + j] = b;
@@ -698,17 +970,19 @@ __device__ void router_bwd_epilogue(const LogitRows<kLds> lg, int nt, int64_t t0
   }
 }
 
+// The logits are recomputed with the forward router's contraction, so they
+// are the forward's bits; the epilogue runs on the first 512 threads.
 template <bool kLds>
-__global__ __launch_bounds__(kRBThreads) void router_bwd_bf16_kernel(const RouterBwdArgs a) {
-  __shared__ RouterSmem sm;
+__global__ __launch_bounds__(kFwThreads) void router_bwd_bf16_kernel(const RouterBwdArgs a) {
+  __shared__ RouterFwSmem sm;
   const int64_t blk = blockIdx.x, t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, a.T - t0);
   const LogitRows<kLds> lg =
-      router_contract_bf16<kLds>((const bf16 *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, sm);
-  static_assert(kRouterTokens * (kRouterChunk + 1) + bwd_lds_floats<kRBThreads>() <= kRouterSmem / 4,
+      router_fwd_contract_bf16<kLds>((const bf16 *)a.x, (const u32x4 *)a.wplanes, a.bias, a.T, a.d, a.N, a.logits,
+                                     blk, sm);
+  static_assert(kRouterLgBytes / 4 + bwd_lds_floats<kRBThreads>() <= kFwSmemX / 4,
                 "logit rows + backward scratch fit the staging area");
-  router_bwd_epilogue<bf16, kRBThreads, kLds, false>(lg, nt, t0, a,
-                                              (float *)sm.stage + kRouterTokens * (kRouterChunk + 1));
+  router_bwd_epilogue<bf16, kRBThreads, kLds, false>(lg, nt, t0, a, (float *)sm.x + kRouterLgBytes / 4);
 }
 
 template <bool kLds>
@@ -814,9 +1088,12 @@ hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st, LaunchMarks
   const int64_t nb = router_blocks(a.T);
   const bool lds = a.N <= kRouterChunk;
   for (int r = reps(); r > 0 && nb > 0; --r) {
-    if (a.dtype == kBF16)
-      (lds ? router_bwd_bf16_kernel<true> : router_bwd_bf16_kernel<false>)<<<dim3((unsigned)nb), dim3(kRBThreads), 0,
+    if (a.dtype == kBF16) {
+      hipError_t e = launch_router_planes(a.w_r, a.N, a.d, a.wplanes, st);
+      if (e != hipSuccess) return e;
+      (lds ? router_bwd_bf16_kernel<true> : router_bwd_bf16_kernel<false>)<<<dim3((unsigned)nb), dim3(kFwThreads), 0,
                                                                               st>>>(a);
+    }
     else
       (lds ? router_bwd_f32_kernel<true> : router_bwd_f32_kernel<false>)<<<dim3((unsigned)nb), dim3(kRouterThreads),
                                                                             0, st>>>(a);
@@ -859,9 +1136,11 @@ hipError_t run_router(const RouteArgs &a, hipStream_t st) {
   const bool lds = a.N <= kRouterChunk;
   const dim3 grid((unsigned)nb);
   if (a.dtype == kBF16) {
-    auto kern = lds ? router_bf16_kernel<true, kK> : router_bf16_kernel<false, kK>;
-    kern<<<grid, dim3(kRBThreads), 0, st>>>((const bf16 *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits,
-                                            a.expert_idx, a.gate, a.rank, a.bcount, a.ppart);
+    hipError_t e = launch_router_planes(a.w_r, a.N, a.d, a.wplanes, st);
+    if (e != hipSuccess) return e;
+    auto kern = lds ? router_fwd_bf16_kernel<true, kK> : router_fwd_bf16_kernel<false, kK>;
+    kern<<<grid, dim3(kFwThreads), 0, st>>>((const bf16 *)a.x, (const u32x4 *)a.wplanes, a.bias, a.T, a.d, a.N,
+                                            a.logits, a.expert_idx, a.gate, a.rank, a.bcount, a.ppart);
   } else {
     auto kern = lds ? router_f32_kernel<true, kK> : router_f32_kernel<false, kK>;
     kern<<<grid, dim3(kRouterThreads), 0, st>>>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits,
@@ -929,7 +1208,6 @@ struct TailLds {
   double *red;      // [16] loss partials of the waves
   int *win;         // [2] look-back window: rows to add, last one inclusive
 };
-__host__ __device__ constexpr int fused_tail_bytes(int N) { return N * 24 + kRouterTokens * 4 + 16 * 8 + 16; }
 __device__ __forceinline__ TailLds tail_lds(char *base, int N) {
   TailLds L;
   L.p = (int64_t *)base;
@@ -946,7 +1224,7 @@ __device__ __forceinline__ TailLds tail_lds(char *base, int N) {
 // (through the nearest one with an inclusive prefix, else all of the window)
 // once each of those has published; `found` says the last of them is
 // inclusive.  Every decision is a ballot, so the loop is wave-uniform.
-__device__ int lookback_window(const int32_t *state, int64_t lo, int32_t *err, bool &found) {
+__device__ __forceinline__ int lookback_window(const int32_t *state, int64_t lo, int32_t *err, bool &found) {
   const int lane = threadIdx.x % kWave;
   const int64_t j = lo - 1 - lane;
   const int nvalid = (int)min<int64_t>(lo, kWave);
@@ -975,7 +1253,7 @@ __device__ int lookback_window(const int32_t *state, int64_t lo, int32_t *err, b
 // Steps 1-5 for block blk (its tokens' experts in s_e, in-block ranks in
 // r.slot, counts and P sums in L.c / L.p).
 template <int kThreads>
-__device__ void route_fused_tail(const FusedRouteArgs &a, int64_t blk, int64_t nb, int nt, const int *s_e,
+__device__ __forceinline__ void route_fused_tail(const FusedRouteArgs &a, int64_t blk, int64_t nb, int nt, const int *s_e,
                                  const TailLds L) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int N = a.r.N;
@@ -1119,22 +1397,27 @@ __device__ __forceinline__ int64_t route_ticket(int32_t *ticket, int *s_blk) {
 }
 
 template <bool kLds>
-__global__ __launch_bounds__(kRBThreads) void route_fused_bf16_kernel(const FusedRouteArgs a) {
-  static_assert(kRouterLgBytes + fused_tail_bytes(kFusedMaxExperts) <= kRouterSmem, "tail LDS");
-  __shared__ RouterSmem sm;
+__global__ __launch_bounds__(kFwThreads) void route_fused_bf16_kernel(const FusedRouteArgs a) {
+  static_assert(kRouterLgBytes + fused_tail_bytes(kFusedMaxExperts) <= kFwSmemX, "tail LDS");
+  __shared__ RouterFwSmem sm;
   __shared__ int s_blk;
   const int64_t T = a.r.T, nb = router_blocks(T);
   const int64_t blk = route_ticket(a.sync, &s_blk);
   if (blk >= nb) return;
   const int N = a.r.N;
   const LogitRows<kLds> lg =
-      router_contract_bf16<kLds>((const bf16 *)a.r.x, a.r.w_r, a.r.bias, T, a.r.d, N, a.r.logits, blk, sm);
+      router_fwd_contract_bf16<kLds>((const bf16 *)a.r.x, (const u32x4 *)a.r.wplanes, a.r.bias, T, a.r.d, N,
+                                     a.r.logits, blk, sm);
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
-  const TailLds L = tail_lds(sm.stage + kRouterLgBytes, N);
-  router_epilogue<kRBThreads, kLds, 1>(lg, nt, N, t0, blk, TopK{T, nb}, a.r.expert_idx, a.r.gate, a.r.slot,
-                                       a.r.bcount, a.r.ppart, sm.s_max, sm.s_inv, sm.s_e, sm.s_e2, L.c, L.p);
-  route_fused_tail<kRBThreads>(a, blk, nb, nt, sm.s_e, L);
+  const TailLds L = tail_lds(sm.x + kRouterLgBytes, N);
+  if (kLds)
+    router_epilogue_lds<1>(lg.base, sm, nt, N, t0, blk, TopK{T, nb}, a.r.expert_idx, a.r.gate, a.r.slot,
+                           a.r.bcount, a.r.ppart, L.c, L.p);
+  else
+    router_epilogue<kRBThreads, kLds, 1>(lg, nt, N, t0, blk, TopK{T, nb}, a.r.expert_idx, a.r.gate, a.r.slot,
+                                         a.r.bcount, a.r.ppart, sm.s_max, sm.s_inv, sm.s_e, sm.s_e2, L.c, L.p);
+  route_fused_tail<kFwThreads>(a, blk, nb, nt, sm.s_e, L);
 }
 
 template <bool kLds>
@@ -1171,8 +1454,10 @@ hipError_t launch_route_fused(const FusedRouteArgs &a, hipStream_t st, LaunchMar
     route_sync_clear_kernel<<<dim3((unsigned)std::min<int64_t>(ceil_div(n16, 256), 2048)), dim3(256), 0, st>>>(
         (u32x4 *)a.sync, n16);
     if (a.r.dtype == kBF16) {
+      hipError_t e = launch_router_planes(a.r.w_r, a.r.N, a.r.d, a.r.wplanes, st);
+      if (e != hipSuccess) return e;
       auto kern = lds ? route_fused_bf16_kernel<true> : route_fused_bf16_kernel<false>;
-      kern<<<dim3((unsigned)nb), dim3(kRBThreads), 0, st>>>(a);
+      kern<<<dim3((unsigned)nb), dim3(kFwThreads), 0, st>>>(a);
     } else {
       auto kern = lds ? route_fused_f32_kernel<true> : route_fused_f32_kernel<false>;
       kern<<<dim3((unsigned)nb), dim3(kRouterThreads), 0, st>>>(a);

@@ -28,7 +28,8 @@ COPY_BYTES = 1 << 30
 KERNEL_KEYS = {
     "ffn_up": ("ffn_gemm_bf16_kernel", "Lb1ELi0E"),
     "ffn_down": ("ffn_gemm_bf16_kernel", "Lb0ELi2E"),
-    "router": ("router_bf16_kernel", ""),
+    "router": ("router_fwd_bf16_kernel", ""),
+    "router_planes": ("router_wplanes_kernel", ""),
     "assign": ("assign_one_kernel", ""),
     "assign_scan": ("assign_scan_kernel", ""),
     "assign_apply": ("assign_apply_layer_kernel", ""),

@@ -65,19 +65,21 @@ def test_workspace_bytes_layout():
     s = B.make_shape(16384, 768, 3072, 128, 160, torch.bfloat16)
     ws = smx.workspace_bytes(s)
     nb = 16384 // 64
-    # block counts, block offsets, P partials, P sums, ranks, the single-pass routing's ordering state
-    # (ticket, error word and one state word per block; then per block and expert the aggregate and
-    # inclusive counts (4 bytes each) and P sums (8 bytes each)), hidden, slot->token and slot->gate maps
+    # block counts, block offsets, P partials, P sums, ranks, W_r's three bf16 planes (bf16 layers), the
+    # single-pass routing's ordering state (ticket, error word and one state word per block; then per
+    # block and expert the aggregate and inclusive counts (4 bytes each) and P sums (8 bytes each)),
+    # hidden, slot->token and slot->gate maps
     single_pass = (nb + 4) * 4 + nb * 128 * 24
-    expect_min = (3 * nb * 128 * 4 + 128 * 4 + 16384 * 4 + single_pass + 128 * 160 * 3072 * 2
+    planes = 128 * 768 * 3 * 2
+    expect_min = (3 * nb * 128 * 4 + 128 * 4 + 16384 * 4 + planes + single_pass + 128 * 160 * 3072 * 2
                   + 2 * 128 * 160 * 4)
-    assert expect_min <= ws <= expect_min + 12 * 256
+    assert expect_min <= ws <= expect_min + 13 * 256
     # more experts than one router chunk adds the [T][N] logits scratch
     s2 = B.make_shape(1000, 64, 64, 300, 10, torch.float32)
     assert smx.workspace_bytes(s2) >= 1000 * 300 * 4
     # routing alone: the capacity-0 figure holds no expert buffers
     s3 = B.make_shape(16384, 768, 3072, 128, 0, torch.bfloat16)
-    assert smx.workspace_bytes(s3) < 3 * nb * 128 * 4 + 16384 * 4 + single_pass + 4096
+    assert smx.workspace_bytes(s3) < 3 * nb * 128 * 4 + 16384 * 4 + planes + single_pass + 4096
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -186,9 +188,10 @@ def test_topk_validation_and_workspace():
     w2 = smx.topk_workspace_bytes(s, 2)
     nb = 16384 // 64
     single_pass = (2 * nb + 4) * 4 + 2 * nb * 128 * 24  # sized for k blocks per router block
-    expect_min = (3 * 2 * nb * 128 * 4 + 128 * 4 + 2 * 16384 * 4 + single_pass + 128 * 320 * 3072 * 2
+    planes = 128 * 768 * 3 * 2                           # W_r's bf16 planes
+    expect_min = (3 * 2 * nb * 128 * 4 + 128 * 4 + 2 * 16384 * 4 + planes + single_pass + 128 * 320 * 3072 * 2
                   + 3 * 128 * 320 * 4 + 2 * 16384 * 768 * 2)
-    assert expect_min <= w2 <= expect_min + 14 * 256
+    assert expect_min <= w2 <= expect_min + 15 * 256
     out = ctypes.c_size_t()
     for k, code in ((0, B.SWITCH_E_INVALID), (-1, B.SWITCH_E_INVALID), (3, B.SWITCH_E_UNSUPPORTED),
                     (129, B.SWITCH_E_INVALID)):
