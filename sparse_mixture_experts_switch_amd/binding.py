@@ -108,6 +108,70 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return t.data_ptr()
 
 
+def _expect(t, name: str, shape, dtype: torch.dtype, dev: torch.device) -> None:
+    """Raise ValueError unless t is a contiguous tensor with this shape and
+    dtype on the call's device (the C ABI takes raw pointers and cannot tell
+    a short, mistyped or host buffer from a good one)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}; the call runs on {dev}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_acts(x, name: str = "x") -> torch.device:
+    """A 2-D activation tensor of a supported dtype; returns its device (that
+    it is a GPU is checked when the stream is taken, right before the call)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor [tokens][d_model]")
+    _dtype_code(x.dtype)
+    return x.device
+
+
+def _check_router(x, w_router, router_bias) -> None:
+    dev = _check_acts(x)
+    if not isinstance(w_router, torch.Tensor) or w_router.dim() != 2:
+        raise ValueError("w_router must be a 2-D tensor [num_experts][d_model]")
+    N = w_router.shape[0]
+    _expect(w_router, "w_router", (N, x.shape[1]), torch.float32, dev)
+    if router_bias is not None:
+        _expect(router_bias, "router_bias", (N,), torch.float32, dev)
+
+
+def _check_experts(w_in, w_out, N: int, d: int, dtype: torch.dtype, dev: torch.device) -> None:
+    if not isinstance(w_in, torch.Tensor) or w_in.dim() != 3:
+        raise ValueError("w_in must be a 3-D tensor [num_experts][d_ff][d_model]")
+    f = w_in.shape[1]
+    _expect(w_in, "w_in", (N, f, d), dtype, dev)
+    _expect(w_out, "w_out", (N, d, f), dtype, dev)
+
+
+def _check_layer_inputs(x, w_router, router_bias, w_in, w_out) -> None:
+    _check_router(x, w_router, router_bias)
+    _check_experts(w_in, w_out, w_router.shape[0], x.shape[1], x.dtype, x.device)
+
+
+def _check_route_outputs(o: dict, T: int, N: int, dev: torch.device, k: int | None = None) -> None:
+    rt = (T,) if k is None else (k, T)
+    for key, dt, shp in (("expert_idx", torch.int32, rt), ("gate", torch.float32, rt), ("slot", torch.int32, rt),
+                         ("dropped", torch.uint8, rt), ("expert_count", torch.int32, (N,)),
+                         ("aux_loss", torch.float32, (1,))):
+        if key not in o:
+            raise ValueError(f"out is missing {key}")
+        _expect(o[key], key, shp, dt, dev)
+
+
+def _check_ws(ws, dev: torch.device) -> None:
+    if not isinstance(ws, torch.Tensor) or ws.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    _expect(ws, "workspace", (ws.numel(),), torch.uint8, dev)
+
+
 def _dtype_code(dt: torch.dtype) -> int:
     if dt == torch.bfloat16:
         return SWITCH_BF16
@@ -143,6 +207,7 @@ def _workspace(shape: Shape, dev: torch.device, ws: torch.Tensor | None) -> torc
     need = workspace_bytes(shape)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check_ws(ws, dev)
     return ws
 
 
@@ -167,11 +232,13 @@ def _shape_of(x, w_in, num_experts, capacity_, d_ff=None) -> Shape:
 def route(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None, capacity_: int,
           workspace: torch.Tensor | None = None, out: dict | None = None) -> dict:
     """Router, top-1, capacity assignment and aux loss (switch_route)."""
+    _check_router(x, w_router, router_bias)
     T, d = x.shape
     N = w_router.shape[0]
     shape = make_shape(T, d, 64, N, capacity_, x.dtype)
     dev = x.device
     o = out if out is not None else _route_outputs(T, N, dev)
+    _check_route_outputs(o, T, N, dev)
     # routing needs the workspace of the same shape without expert buffers
     ws = _workspace(make_shape(T, d, 64, N, 0, x.dtype), dev, workspace)
     _check(load_library().switch_route(
@@ -186,13 +253,16 @@ def route_dispatch(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.T
                    dispatched: torch.Tensor | None = None) -> dict:
     """Routing and dispatch in one pass over x (switch_route_dispatch): the
     outputs of route() plus o["dispatched"] [N][C][d]."""
+    _check_router(x, w_router, router_bias)
     T, d = x.shape
     N = w_router.shape[0]
     shape = make_shape(T, d, 64, N, capacity_, x.dtype)
     dev = x.device
     o = out if out is not None else _route_outputs(T, N, dev)
+    _check_route_outputs(o, T, N, dev)
     ws = _workspace(make_shape(T, d, 64, N, 0, x.dtype), dev, workspace)
     buf = dispatched if dispatched is not None else torch.empty(N, capacity_, d, dtype=x.dtype, device=dev)
+    _expect(buf, "dispatched", (N, capacity_, d), x.dtype, dev)
     _check(load_library().switch_route_dispatch(
         ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(o["expert_idx"]), _ptr(o["gate"]),
         _ptr(o["slot"]), _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]),
@@ -204,9 +274,14 @@ def route_dispatch(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.T
 def dispatch(x: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tensor, dropped: torch.Tensor,
              num_experts: int, capacity_: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """Gather kept token rows into [N][C][d] expert buffers (switch_dispatch)."""
+    dev = _check_acts(x)
     T, d = x.shape
+    _expect(expert_idx, "expert_idx", (T,), torch.int32, dev)
+    _expect(slot, "slot", (T,), torch.int32, dev)
+    _expect(dropped, "dropped", (T,), torch.uint8, dev)
     shape = make_shape(T, d, 64, num_experts, capacity_, x.dtype)
     buf = out if out is not None else torch.empty(num_experts, capacity_, d, dtype=x.dtype, device=x.device)
+    _expect(buf, "out", (num_experts, capacity_, d), x.dtype, dev)
     _check(load_library().switch_dispatch(ctypes.byref(shape), _ptr(x), _ptr(expert_idx), _ptr(slot),
                                           _ptr(dropped), _ptr(buf), _stream(x.device)))
     return buf
@@ -215,14 +290,20 @@ def dispatch(x: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tensor, drop
 def expert_ffn(dispatched: torch.Tensor, expert_count: torch.Tensor, w_in: torch.Tensor, w_out: torch.Tensor,
                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
     """expert_out[i][r] = W_out,i ReLU(W_in,i dispatched[i][r]) (switch_expert_ffn)."""
+    if not isinstance(dispatched, torch.Tensor) or dispatched.dim() != 3:
+        raise ValueError("dispatched must be a 3-D tensor [num_experts][capacity][d_model]")
     N, C, d = dispatched.shape
+    dev = _check_acts(dispatched.reshape(N * C, d), "dispatched")
+    _expect(expert_count, "expert_count", (N,), torch.int32, dev)
+    _check_experts(w_in, w_out, N, d, dispatched.dtype, dev)
     shape = make_shape(0, d, w_in.shape[1], N, C, dispatched.dtype)
-    dev = dispatched.device
     eo = out if out is not None else torch.empty_like(dispatched)
+    _expect(eo, "out", (N, C, d), dispatched.dtype, dev)
     ws = workspace
     if ws is None:  # expert_ffn alone needs only the [N][C][d_ff] hidden buffer
         ws = torch.empty(max(N * C * w_in.shape[1] * dispatched.element_size(), 256), dtype=torch.uint8,
                          device=dev)
+    _check_ws(ws, dev)
     _check(load_library().switch_expert_ffn(ctypes.byref(shape), _ptr(dispatched), _ptr(expert_count), _ptr(w_in),
                                             _ptr(w_out), _ptr(eo), _ptr(ws), ws.numel(), _stream(dev)))
     return eo
@@ -232,10 +313,19 @@ def combine(expert_out: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tens
             gate: torch.Tensor, x_residual: torch.Tensor | None = None,
             out: torch.Tensor | None = None) -> torch.Tensor:
     """y[t] = gate[t] expert_out[e[t]][slot[t]] (0 if dropped) (+ x) (switch_combine)."""
+    if not isinstance(expert_out, torch.Tensor) or expert_out.dim() != 3:
+        raise ValueError("expert_out must be a 3-D tensor [num_experts][capacity][d_model]")
     N, C, d = expert_out.shape
+    dev = _check_acts(expert_out.reshape(N * C, d), "expert_out")
     T = expert_idx.shape[0]
+    for t_, name, dt in ((expert_idx, "expert_idx", torch.int32), (slot, "slot", torch.int32),
+                         (dropped, "dropped", torch.uint8), (gate, "gate", torch.float32)):
+        _expect(t_, name, (T,), dt, dev)
+    if x_residual is not None:
+        _expect(x_residual, "x_residual", (T, d), expert_out.dtype, dev)
     shape = make_shape(T, d, 64, N, C, expert_out.dtype)
     y = out if out is not None else torch.empty(T, d, dtype=expert_out.dtype, device=expert_out.device)
+    _expect(y, "out", (T, d), expert_out.dtype, dev)
     _check(load_library().switch_combine(ctypes.byref(shape), _ptr(expert_out), _ptr(expert_idx), _ptr(slot),
                                          _ptr(dropped), _ptr(gate), _ptr(x_residual), _ptr(y),
                                          _stream(expert_out.device)))
@@ -243,6 +333,7 @@ def combine(expert_out: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tens
 
 
 def _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out):
+    _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
     T, d = x.shape
     N, f = w_in.shape[0], w_in.shape[1]
     shape = make_shape(T, d, f, N, capacity_, x.dtype)
@@ -250,6 +341,8 @@ def _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, wor
     o = out if out is not None else _route_outputs(T, N, dev)
     if "y" not in o:
         o["y"] = torch.empty(T, d, dtype=x.dtype, device=dev)
+    _check_route_outputs(o, T, N, dev)
+    _expect(o["y"], "y", (T, d), x.dtype, dev)
     ws = _workspace(shape, dev, workspace)
     args = [ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_in), _ptr(w_out),
             1 if add_residual else 0, _ptr(o["y"]), _ptr(o["expert_idx"]), _ptr(o["gate"]), _ptr(o["slot"]),
@@ -279,9 +372,15 @@ def add_norm(x: torch.Tensor | None, y: torch.Tensor, gamma: torch.Tensor, beta:
              out: torch.Tensor | None = None) -> torch.Tensor:
     """Layer normalisation over d_model of x + y (x may be None): the block's
     Add + Normalize after the layer (switch_add_norm).  out may be y."""
+    dev = _check_acts(y, "y")
     T, d = y.shape
+    if x is not None:
+        _expect(x, "x", (T, d), y.dtype, dev)
+    _expect(gamma, "gamma", (d,), torch.float32, dev)
+    _expect(beta, "beta", (d,), torch.float32, dev)
     shape = make_shape(T, d, 64, 1, 0, y.dtype)
     o = out if out is not None else torch.empty_like(y)
+    _expect(o, "out", (T, d), y.dtype, dev)
     _check(load_library().switch_add_norm(ctypes.byref(shape), _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta),
                                           float(eps), _ptr(o), _stream(y.device)))
     return o
@@ -299,6 +398,7 @@ def topk_layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: tor
                        out: dict | None = None) -> dict:
     """Classic top-k MoE layer, k = 1 or 2 (switch_topk_layer_forward); the
     routing outputs are [top_k][T]."""
+    _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
     T, d = x.shape
     N, f = w_in.shape[0], w_in.shape[1]
     shape = make_shape(T, d, f, N, capacity_, x.dtype)
@@ -306,9 +406,12 @@ def topk_layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: tor
     o = out if out is not None else _route_outputs(T, N, dev, top_k)
     if "y" not in o:
         o["y"] = torch.empty(T, d, dtype=x.dtype, device=dev)
+    _check_route_outputs(o, T, N, dev, int(top_k))
+    _expect(o["y"], "y", (T, d), x.dtype, dev)
     ws = workspace
     if ws is None:
         ws = torch.empty(max(topk_workspace_bytes(shape, top_k), 256), dtype=torch.uint8, device=dev)
+    _check_ws(ws, dev)
     _check(load_library().switch_topk_layer_forward(
         ctypes.byref(shape), int(top_k), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_in), _ptr(w_out),
         1 if add_residual else 0, _ptr(o["y"]), _ptr(o["expert_idx"]), _ptr(o["gate"]), _ptr(o["slot"]),
@@ -324,19 +427,31 @@ def backward_workspace_bytes(shape: Shape) -> int:
 
 def _bwd_args(x, w_router, router_bias, w_in, w_out, capacity_, fwd: dict, fwd_workspace, dy, d_aux,
               add_residual, workspace, out):
+    _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
     T, d = x.shape
     N, f = w_in.shape[0], w_in.shape[1]
     shape = make_shape(T, d, f, N, capacity_, x.dtype)
     dev = x.device
+    _expect(fwd["expert_idx"], "fwd expert_idx", (T,), torch.int32, dev)
+    _expect(fwd["dropped"], "fwd dropped", (T,), torch.uint8, dev)
+    _expect(fwd["expert_count"], "fwd expert_count", (N,), torch.int32, dev)
+    _check_ws(fwd_workspace, dev)
+    _expect(dy, "dy", (T, d), x.dtype, dev)
     o = out if out is not None else {}
     o.setdefault("dx", torch.empty(T, d, dtype=x.dtype, device=dev))
     o.setdefault("dw_router", torch.empty(N, d, dtype=torch.float32, device=dev))
     o.setdefault("d_router_bias", torch.empty(N, dtype=torch.float32, device=dev))
     o.setdefault("dw_in", torch.empty_like(w_in))
     o.setdefault("dw_out", torch.empty_like(w_out))
+    _expect(o["dx"], "dx", (T, d), x.dtype, dev)
+    _expect(o["dw_router"], "dw_router", (N, d), torch.float32, dev)
+    _expect(o["d_router_bias"], "d_router_bias", (N,), torch.float32, dev)
+    _expect(o["dw_in"], "dw_in", tuple(w_in.shape), x.dtype, dev)
+    _expect(o["dw_out"], "dw_out", tuple(w_out.shape), x.dtype, dev)
     ws = workspace
     if ws is None:
         ws = torch.empty(max(backward_workspace_bytes(shape), 256), dtype=torch.uint8, device=dev)
+    _check_ws(ws, dev)
     args = [ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_in), _ptr(w_out),
             1 if add_residual else 0, _ptr(fwd["expert_idx"]), _ptr(fwd["dropped"]), _ptr(fwd["expert_count"]),
             _ptr(fwd_workspace), fwd_workspace.numel(), _ptr(dy), float(d_aux), _ptr(o["dx"]), _ptr(o["dw_router"]),
@@ -370,10 +485,20 @@ def combine_add_norm(expert_out: torch.Tensor, expert_idx: torch.Tensor, slot: t
                      dropped: torch.Tensor, gate: torch.Tensor, x: torch.Tensor, gamma: torch.Tensor,
                      beta: torch.Tensor, eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
     """LayerNorm(x + combine) in one pass (switch_combine_add_norm)."""
+    if not isinstance(expert_out, torch.Tensor) or expert_out.dim() != 3:
+        raise ValueError("expert_out must be a 3-D tensor [num_experts][capacity][d_model]")
     N, C, d = expert_out.shape
+    dev = _check_acts(expert_out.reshape(N * C, d), "expert_out")
     T = expert_idx.shape[0]
+    for t_, name, dt in ((expert_idx, "expert_idx", torch.int32), (slot, "slot", torch.int32),
+                         (dropped, "dropped", torch.uint8), (gate, "gate", torch.float32)):
+        _expect(t_, name, (T,), dt, dev)
+    _expect(x, "x", (T, d), expert_out.dtype, dev)
+    _expect(gamma, "gamma", (d,), torch.float32, dev)
+    _expect(beta, "beta", (d,), torch.float32, dev)
     shape = make_shape(T, d, 64, N, C, expert_out.dtype)
     o = out if out is not None else torch.empty(T, d, dtype=expert_out.dtype, device=expert_out.device)
+    _expect(o, "out", (T, d), expert_out.dtype, dev)
     _check(load_library().switch_combine_add_norm(
         ctypes.byref(shape), _ptr(expert_out), _ptr(expert_idx), _ptr(slot), _ptr(dropped), _ptr(gate), _ptr(x),
         _ptr(gamma), _ptr(beta), float(eps), _ptr(o), _stream(expert_out.device)))

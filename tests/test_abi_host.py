@@ -240,3 +240,47 @@ def test_backward_rejects_before_launch():
                                             fwd_need, good, 0.5, good, good, None, good, good, good, bwd_need, None,
                                             2, 1, 1)
     assert rc == B.SWITCH_E_INVALID
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python binding checks every tensor's dtype, shape and device (and
+    each output buffer's) before calling the library, which takes raw pointers
+    and could not tell: a bf16 router weight, a short bias, a transposed
+    expert weight, a mistyped output, a host workspace or a tensor on another
+    device is a ValueError, never a launch.  On this GPU-less host a call with
+    every argument right stops at the stream lookup (no device)."""
+    import torch
+    T, d, f, N, C = 64, 128, 256, 8, 16
+    x = torch.zeros(T, d, dtype=torch.bfloat16)
+    wr = torch.zeros(N, d)
+    w_in = torch.zeros(N, f, d, dtype=torch.bfloat16)
+    w_out = torch.zeros(N, d, f, dtype=torch.bfloat16)
+
+    def raises(fn, text):
+        with pytest.raises(ValueError) as ei:
+            fn()
+        assert text in str(ei.value), str(ei.value)
+
+    raises(lambda: smx.route(x, wr.to(torch.bfloat16), None, C), "w_router has dtype")
+    raises(lambda: smx.route(x, wr[:, :64].contiguous(), None, C), "w_router has shape")
+    raises(lambda: smx.route(x, wr, torch.zeros(N - 1), C), "router_bias has shape")
+    raises(lambda: smx.layer_forward(x, wr, None, w_in.transpose(1, 2).contiguous(), w_out, C), "w_in has shape")
+    raises(lambda: smx.layer_forward(x, wr, None, w_in, w_out.float(), C), "w_out has dtype")
+    raises(lambda: smx.layer_forward(x, wr, None, w_in, w_out, C, workspace=torch.zeros(1 << 20, dtype=torch.int32)),
+           "workspace has dtype")
+    out = B._route_outputs(T, N, torch.device("cpu"))
+    out["gate"] = torch.zeros(T, dtype=torch.float64)
+    raises(lambda: smx.layer_forward(x, wr, None, w_in, w_out, C, out=out), "gate has dtype")
+    out = B._route_outputs(T, N, torch.device("cpu"))
+    out["y"] = torch.zeros(T, d + 64, dtype=torch.bfloat16)
+    raises(lambda: smx.layer_forward(x, wr, None, w_in, w_out, C, out=out), "y has shape")
+    raises(lambda: smx.layer_forward(x, wr, None, w_in.to("meta"), w_out, C), "w_in is on meta")
+    raises(lambda: smx.dispatch(x, torch.zeros(T, dtype=torch.int64), torch.zeros(T, dtype=torch.int32),
+                                torch.zeros(T, dtype=torch.uint8), N, C), "expert_idx has dtype")
+    raises(lambda: smx.add_norm(x, x, torch.ones(d + 1), torch.zeros(d), 1e-6), "gamma has shape")
+    raises(lambda: smx.combine(torch.zeros(N, C, d, dtype=torch.bfloat16), torch.zeros(T, dtype=torch.int32),
+                               torch.zeros(T, dtype=torch.int32), torch.zeros(T, dtype=torch.uint8),
+                               torch.zeros(T, dtype=torch.float16)), "gate has dtype")
+    # every argument right: the call stops where it would need the GPU
+    raises(lambda: smx.layer_forward(x, wr, None, w_in, w_out, C), "cuda device")
+
