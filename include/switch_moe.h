@@ -171,6 +171,29 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
                          int32_t *expert_count, float *aux_loss, void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/* switch_layer_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace in a static
+ * device array of switch_noalloc_scratch_bytes (128 MiB) that the library
+ * holds on every GPU it runs on until the process ends.  Nothing is allocated
+ * or freed by the call.  Arguments as switch_layer_forward without the
+ * workspace; SWITCH_E_WORKSPACE (nothing launched) when the shape needs more
+ * workspace than the array holds (switch_workspace_bytes tells; the base and
+ * large layers fit).  The array keeps the last call's contents, and no kernel
+ * of the layer reads workspace it has not written in the same call.  Every
+ * call on one GPU uses that GPU's one array: calls whose work overlaps on the
+ * GPU (on different streams, or from several threads) race and give
+ * undefined results; serialise them.  The first call on each device looks up
+ * the array's device address (hipGetSymbolAddress) with that device current;
+ * SWITCH_E_HIP if that fails. */
+int switch_layer_forward_noalloc(const switch_shape *s, const void *x, const float *w_router,
+                                 const float *router_bias, const void *w_in, const void *w_out,
+                                 int32_t add_residual, void *y, int32_t *expert_idx, float *gate, int32_t *slot,
+                                 uint8_t *dropped, int32_t *expert_count, float *aux_loss, void *stream);
+
+/* Bytes of the static workspace switch_layer_forward_noalloc uses.  Host only. */
+int switch_noalloc_scratch_bytes(size_t *bytes_out);
+
 /* The block's "Add + Normalize" after the layer (Switch Transformers
  * write-up, "The Architecture in Place", the block figure): for every token t,
  * out[t] = (v - mean v) / sqrt(var v + eps) * gamma + beta with v = x[t] +

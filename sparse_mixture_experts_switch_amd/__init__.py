@@ -22,9 +22,11 @@ from .binding import (  # noqa: F401
     layer_backward,
     layer_backward_profiled,
     layer_forward,
+    layer_forward_noalloc,
     layer_forward_profiled,
     launch_names,
     load_library,
+    noalloc_scratch_bytes,
     route,
     route_dispatch,
     topk_layer_forward,

@@ -19,6 +19,7 @@ __all__ = [
     "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "launch_names", "add_norm",
     "topk_workspace_bytes", "topk_layer_forward", "backward_workspace_bytes", "layer_backward",
     "layer_backward_profiled", "BACKWARD_KERNELS", "combine_add_norm", "SWITCH_F32", "SWITCH_BF16",
+    "layer_forward_noalloc", "noalloc_scratch_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswitchmoe.so")
@@ -32,7 +33,8 @@ EXPORTED = [
     "switch_expert_ffn", "switch_combine", "switch_layer_forward", "switch_layer_forward_profiled",
     "switch_launch_names", "switch_add_norm", "switch_topk_workspace_bytes", "switch_topk_layer_forward",
     "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
-    "switch_combine_add_norm", "switch_route_dispatch",
+    "switch_combine_add_norm", "switch_route_dispatch", "switch_layer_forward_noalloc",
+    "switch_noalloc_scratch_bytes",
 ]
 BACKWARD_KERNELS = ["bwd_dz", "bwd_dw_out", "bwd_dx", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
                     "bwd_router_w_sum"]
@@ -88,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.switch_layer_backward_profiled.argtypes = bwd + [ctypes.c_int32] * 3
     lib.switch_topk_layer_forward.argtypes = (
         [sp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P])
+    lib.switch_layer_forward_noalloc.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 7 + [_P]
+    lib.switch_noalloc_scratch_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
     for name in EXPORTED:
         if name != "switch_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -365,6 +369,38 @@ def layer_forward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, fir
     `times` times back to back (switch_layer_forward_profiled); asynchronous."""
     _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
     _check(load_library().switch_layer_forward_profiled(*args, int(first_kernel), int(last_kernel), int(times)))
+    return o
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static workspace of layer_forward_noalloc."""
+    out = ctypes.c_size_t()
+    _check(load_library().switch_noalloc_scratch_bytes(ctypes.byref(out)))
+    return out.value
+
+
+def layer_forward_noalloc(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None,
+                          w_in: torch.Tensor, w_out: torch.Tensor, capacity_: int, add_residual: bool = False,
+                          out: dict | None = None) -> dict:
+    """The layer forward on the library's static workspace
+    (switch_layer_forward_noalloc): no device memory is allocated by the call.
+    `out` holds the output tensors (expert_idx, gate, slot, dropped,
+    expert_count, aux_loss, y); when it is None they are allocated here, by
+    the caller's side, before the call."""
+    T, d = x.shape
+    N, f = w_in.shape[0], w_in.shape[1]
+    shape = make_shape(T, d, f, N, capacity_, x.dtype)
+    dev = x.device
+    _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
+    o = out if out is not None else _route_outputs(T, N, dev)
+    if "y" not in o:
+        o["y"] = torch.empty(T, d, dtype=x.dtype, device=dev)
+    _check_route_outputs(o, T, N, dev)
+    _expect(o["y"], "y", (T, d), x.dtype, dev)
+    _check(load_library().switch_layer_forward_noalloc(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_in), _ptr(w_out),
+        1 if add_residual else 0, _ptr(o["y"]), _ptr(o["expert_idx"]), _ptr(o["gate"]), _ptr(o["slot"]),
+        _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]), _stream(dev)))
     return o
 
 

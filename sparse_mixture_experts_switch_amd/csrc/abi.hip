@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -16,6 +17,13 @@
 #include "launch.h"
 
 using namespace smx;
+
+// Workspace of switch_layer_forward_noalloc: a file-scope device array, one
+// copy on every GPU the library runs on, held until the process ends.  Host
+// code never uses its name as a device address: each device's address comes
+// from hipGetSymbolAddress (scratch_address).
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 27;  // 128 MiB
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -34,6 +42,37 @@ int fail(int code, const char *fmt, ...) {
 
 int hip_fail(hipError_t e, const char *what) {
   return fail(SWITCH_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; null with the error text set
+// when the lookup fails.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+void *scratch_address() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(SWITCH_E_HIP, "device %d beyond the %d the no-allocation workspace serves", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 constexpr size_t kWsAlign = 256;
@@ -651,6 +690,34 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
     Timer tm;
     return layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
                          dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
+  })
+}
+
+int switch_layer_forward_noalloc(const switch_shape *s, const void *x, const float *w_router,
+                                 const float *router_bias, const void *w_in, const void *w_out, int32_t add_residual,
+                                 void *y, int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
+                                 int32_t *expert_count, float *aux_loss, void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    Layout L;
+    if ((rc = layout(s, L))) return rc;
+    if (L.total > kNoAllocScratchBytes)
+      return fail(SWITCH_E_WORKSPACE, "this shape needs %zu bytes of workspace; the no-allocation call has %zu",
+                  L.total, kNoAllocScratchBytes);
+    void *ws = scratch_address();
+    if (!ws) return SWITCH_E_HIP;
+    Timer tm;
+    return layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
+                         dropped, expert_count, aux_loss, ws, kNoAllocScratchBytes, stream, tm);
+  })
+}
+
+int switch_noalloc_scratch_bytes(size_t *bytes_out) {
+  GUARD({
+    if (!bytes_out) return fail(SWITCH_E_INVALID, "bytes_out is NULL");
+    *bytes_out = kNoAllocScratchBytes;
+    return SWITCH_OK;
   })
 }
 

@@ -275,6 +275,7 @@ def test_binding_rejects_mismatched_tensors():
     out["y"] = torch.zeros(T, d + 64, dtype=torch.bfloat16)
     raises(lambda: smx.layer_forward(x, wr, None, w_in, w_out, C, out=out), "y has shape")
     raises(lambda: smx.layer_forward(x, wr, None, w_in.to("meta"), w_out, C), "w_in is on meta")
+    raises(lambda: smx.layer_forward_noalloc(x, wr, None, w_in, w_out.to("meta"), C), "w_out is on meta")
     raises(lambda: smx.dispatch(x, torch.zeros(T, dtype=torch.int64), torch.zeros(T, dtype=torch.int32),
                                 torch.zeros(T, dtype=torch.uint8), N, C), "expert_idx has dtype")
     raises(lambda: smx.add_norm(x, x, torch.ones(d + 1), torch.zeros(d), 1e-6), "gamma has shape")
@@ -283,4 +284,21 @@ def test_binding_rejects_mismatched_tensors():
                                torch.zeros(T, dtype=torch.float16)), "gate has dtype")
     # every argument right: the call stops where it would need the GPU
     raises(lambda: smx.layer_forward(x, wr, None, w_in, w_out, C), "cuda device")
+    raises(lambda: smx.layer_forward_noalloc(x, wr, None, w_in, w_out, C), "cuda device")
 
+
+def test_noalloc_rejects_shapes_beyond_its_workspace():
+    """switch_layer_forward_noalloc refuses a shape whose workspace exceeds
+    its static array (the XXL-shaped layer) with SWITCH_E_WORKSPACE and a
+    message, before touching any pointer; the base layer fits."""
+    import torch
+    lib = smx.load_library()
+    cap = smx.noalloc_scratch_bytes()
+    assert cap == 1 << 27
+    assert smx.workspace_bytes(B.make_shape(16384, 768, 3072, 128, 160, torch.bfloat16)) <= cap
+    s = B.make_shape(8192, 4096, 10240, 64, 160, torch.bfloat16)
+    assert smx.workspace_bytes(s) > cap
+    rc = lib.switch_layer_forward_noalloc(ctypes.byref(s), None, None, None, None, None, 0, None, None, None, None,
+                                          None, None, None, None)
+    assert rc == B.SWITCH_E_WORKSPACE
+    assert b"no-allocation" in lib.switch_last_error()
