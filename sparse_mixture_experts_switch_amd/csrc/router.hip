@@ -1172,13 +1172,13 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
 //   4. slot = exclusive count of the expert + in-block rank, dropped, and the
 //      dispatch stores;
 //   5. the last block forms the totals and the loss from its inclusive row.
-// Visibility across the XCDs without cache maintenance: every row is written
-// once per launch with device-coherent (write-through) stores, which complete
-// before the state word that announces them is stored; states are read with
-// device-coherent loads; a row is read with ordinary cached loads only after
-// its state was seen, so no cache can hold an older copy of it (rows are
-// padded to 256 bytes, so no cache line spans two of them, and caches start
-// each launch clean).  Counts are integers and P sums 2^-31 fixed-point
+// Ordering across the XCDs follows the HIP memory model at agent scope: a
+// block's row stores happen before (a workgroup barrier, then) thread 0's
+// release store of the state word that announces them; the look-back reads
+// state words with relaxed agent-scope loads and, once it has seen every
+// state it needs, runs an agent-scope acquire fence before any thread reads
+// those rows (a relaxed load that reads a released value, then an acquire
+// fence, synchronises with the release).  Counts are integers and P sums 2^-31 fixed-point
 // integers, so every total is independent of how the look-back grouped the
 // blocks.  A workgroup takes its router block from an atomic ticket, so every
 // block it waits for belongs to a workgroup that is already running and never
@@ -1192,11 +1192,6 @@ constexpr int kSpinLimit = 1 << 20;  // polls (~1 s)
 __global__ __launch_bounds__(256) void route_sync_clear_kernel(u32x4 *__restrict__ p, int64_t n16) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
     p[i] = u32x4{0, 0, 0, 0};
-}
-
-template <typename V>
-__device__ __forceinline__ void store_through(V *p, V v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // LDS of the single-pass tail (after the logit rows, which the epilogue
@@ -1266,15 +1261,14 @@ __device__ __forceinline__ void route_fused_tail(const FusedRouteArgs &a, int64_
     int32_t *rc = (blk == 0 ? a.inc_c : a.agg_c) + blk * Ns;
     int64_t *rp = (blk == 0 ? a.inc_p : a.agg_p) + blk * Ns;
     for (int e = tid; e < N; e += kThreads) {
-      store_through(rc + e, L.c[e]);
-      store_through(rp + e, L.p[e]);
+      rc[e] = L.c[e];
+      rp[e] = L.p[e];
       L.xc[e] = 0;
       L.xp[e] = 0;
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete
-  __syncthreads();
-  if (tid == 0) __hip_atomic_store(state + blk, blk == 0 ? 2 : 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();  // every thread's row stores happen before thread 0's release
+  if (tid == 0) __hip_atomic_store(state + blk, blk == 0 ? 2 : 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 
   // the dispatch copy's first kU pieces per thread, loaded now so that they
   // arrive while the block waits for the blocks before it
@@ -1297,6 +1291,10 @@ __device__ __forceinline__ void route_fused_tail(const FusedRouteArgs &a, int64_
     if (wave == 0) {
       bool found;
       const int n = lookback_window(state, lo, a.sync + 1, found);
+      // the states just read were stored with release semantics: this fence
+      // makes every row those blocks wrote before them visible to the reads
+      // below (the barrier orders the other waves' reads after it)
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (lane == 0) {
         L.win[0] = n;
         L.win[1] = found ? 1 : 0;
@@ -1327,12 +1325,11 @@ __device__ __forceinline__ void route_fused_tail(const FusedRouteArgs &a, int64_
   // 3. inclusive prefix of this block
   if (blk > 0) {
     for (int e = tid; e < N; e += kThreads) {
-      store_through(a.inc_c + blk * Ns + e, L.xc[e] + L.c[e]);
-      store_through(a.inc_p + blk * Ns + e, L.xp[e] + L.p[e]);
+      a.inc_c[blk * Ns + e] = L.xc[e] + L.c[e];
+      a.inc_p[blk * Ns + e] = L.xp[e] + L.p[e];
     }
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(state + blk, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(state + blk, 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // slots and drops
