@@ -20,8 +20,8 @@
  * ---------------------------------------
  * - Array arguments are DEVICE pointers owned by the caller; the library
  *   allocates and frees nothing, keeps no state between calls and never
- *   blocks the host (except switch_layer_forward_profiled).  All work is
- *   enqueued on `stream` (a hipStream_t passed as void*; NULL = null stream).
+ *   blocks the host (but see debug mode below).  All work is enqueued on
+ *   `stream` (a hipStream_t passed as void*; NULL = null stream).
  * - Layouts are dense row-major.  T tokens are the caller's [batch][seq]
  *   flattened in row-major order; that order is the "token order" that
  *   decides which tokens overflow an expert.
@@ -33,6 +33,12 @@
  *   anything: a call that returns an error has enqueued nothing and left
  *   every output untouched.  Device faults are asynchronous and surface at
  *   the caller's next synchronisation of the stream.
+ * - Debug mode: when the environment variable SMX_DEBUG_SYNC is set to a
+ *   value other than "" and "0" (read once per process), every entry point
+ *   waits for `stream` after each kernel it launches; when a wait reports an
+ *   error, the call launches nothing more and returns SWITCH_E_HIP with the
+ *   failing kernel's name in switch_last_error().  Kernels launched before
+ *   the failure stay enqueued; the outputs are then undefined.
  * - Outputs must not alias inputs or each other.  Calls on different streams
  *   with different buffers are independent; the library is reentrant.
  * - Alignment: x, W_in, W_out, dispatched, expert_out, y, x_residual, W_r
@@ -156,13 +162,22 @@ int switch_combine(const switch_shape *s, const void *expert_out, const int32_t 
                    const int32_t *slot, const uint8_t *dropped, const float *gate, const void *x_residual,
                    void *y, void *stream);
 
-/* The whole layer in one stream-ordered call: the results of switch_route,
+/* The whole Switch FFN layer ("The Architecture in Place": the Switch layer
+ * that takes the place of the dense FFN; its steps are those of "Switch
+ * Routing: From Top-k to k = 1" and "Expert Capacity and the Capacity
+ * Factor") in one stream-ordered call: the results of switch_route,
  * switch_dispatch, switch_expert_ffn and switch_combine, fused.  The expert
  * FFN reads each kept token's row of x directly (no dispatch copy) and
  * writes y[t] = gate[t] * E_e(x_t) (+ x_t) straight from its fp32
- * accumulators, so every output element is rounded once.  The workspace
- * holds the router's partial results, the hidden activations and the
- * slot -> token map.  add_residual != 0 returns y = x + layer output
+ * accumulators, so every output element is rounded once.  In bf16 with
+ * d_model 128 or 256, d_ff a multiple of 128 and capacity <= 160 (shapes
+ * where it was measured faster), the whole expert FFN is one kernel and the hidden activations
+ * ReLU(W_in x) never leave the chip (rounded to bf16 between the two
+ * products, as in switch_expert_ffn); other shapes run the up-projection
+ * into a workspace buffer, then the down-projection.  The workspace holds
+ * the router's partial results and the slot -> token map; it is NOT a valid
+ * forward workspace for switch_layer_backward, which needs the hidden
+ * activations that switch_layer_forward_train saves.  add_residual != 0 returns y = x + layer output
  * (dropped tokens then pass x through unchanged); 0 returns the bare layer
  * output (0 for dropped tokens).  Outputs as for switch_route plus y [T][d]. */
 int switch_layer_forward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
@@ -170,6 +185,42 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
                          int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
                          int32_t *expert_count, float *aux_loss, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/* The Switch layer followed by the block's Add + Normalize ("The
+ * Architecture in Place": the Switch FFN layer's output is added to its
+ * input x and normalized), in the layer call:
+ *   out[t] = (v - mean(v)) / sqrt(var(v) + eps) * gamma + beta,
+ *   v = x[t] + y_bare[t]   (y_bare = 0 for dropped tokens),
+ * mean and population variance over the d_model features of the row; gamma,
+ * beta [d_model] fp32 (device); eps host scalar, finite and >= 0.  fp32
+ * arithmetic from the layer's fp32 accumulators (y_bare is not rounded
+ * before the sum), one rounding of each output.  out [T][d] replaces y; the
+ * routing outputs and the workspace are those of switch_layer_forward.  Where
+ * switch_layer_forward runs one fused expert kernel the normalization is its
+ * epilogue (dropped rows: the assignment kernel); elsewhere the bare layer
+ * writes out, then switch_add_norm's kernel normalizes it in place.  Errors:
+ * as switch_layer_forward; SWITCH_E_INVALID for NULL / misaligned gamma or
+ * beta or a bad eps; SWITCH_E_UNSUPPORTED for d_model above switch_add_norm's
+ * limit. */
+int switch_layer_forward_add_norm(const switch_shape *s, const void *x, const float *w_router,
+                                  const float *router_bias, const void *w_in, const void *w_out, const float *gamma,
+                                  const float *beta, float eps, void *out, int32_t *expert_idx, float *gate,
+                                  int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* The layer forward of a training step: the same results as
+ * switch_layer_forward (bit for bit where both take the two-product path;
+ * elsewhere the same arithmetic in a different kernel, so y may differ in the
+ * last bf16 place), and the workspace then also holds what
+ * switch_layer_backward reads: the hidden activations H [N][C][d_ff] of the
+ * kept rows besides the slot maps ("The Core Idea": E(x) = W_out ReLU(W_in
+ * x); its gradient needs ReLU(W_in x)).  Same arguments, workspace size and
+ * errors as switch_layer_forward. */
+int switch_layer_forward_train(const switch_shape *s, const void *x, const float *w_router,
+                               const float *router_bias, const void *w_in, const void *w_out, int32_t add_residual,
+                               void *y, int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
+                               int32_t *expert_count, float *aux_loss, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /* switch_layer_forward for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
@@ -256,8 +307,9 @@ int switch_topk_layer_forward(const switch_shape *s, int32_t top_k, const void *
  *   dbias += dL/dh,  dx_t += W_r^T dL/dh;  with add_residual, dx_t += dy_t.
  * Inputs: the forward's shape, x, w_router, router_bias, w_in, w_out and
  * add_residual; its outputs expert_idx [T], dropped [T], expert_count [N];
- * fwd_workspace: the workspace the forward call used, unmodified since (it
- * holds the hidden activations H and the slot maps); dy [T][d] (activation
+ * fwd_workspace: the workspace of a switch_layer_forward_train call on the
+ * same inputs, unmodified since (it holds the hidden activations H and the
+ * slot maps; a switch_layer_forward workspace lacks H); dy [T][d] (activation
  * dtype); d_aux (host scalar, finite: the weight of aux_loss in L, e.g. the
  * alpha of the write-up).
  * Outputs (device, caller-owned, overwritten): dx [T][d] and dw_in

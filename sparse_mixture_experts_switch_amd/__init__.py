@@ -24,6 +24,8 @@ from .binding import (  # noqa: F401
     layer_forward,
     layer_forward_noalloc,
     layer_forward_profiled,
+    layer_forward_train,
+    layer_forward_add_norm,
     launch_names,
     load_library,
     noalloc_scratch_bytes,

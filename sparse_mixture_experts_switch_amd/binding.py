@@ -19,7 +19,7 @@ __all__ = [
     "expert_ffn", "combine", "layer_forward", "layer_forward_profiled", "launch_names", "add_norm",
     "topk_workspace_bytes", "topk_layer_forward", "backward_workspace_bytes", "layer_backward",
     "layer_backward_profiled", "BACKWARD_KERNELS", "combine_add_norm", "SWITCH_F32", "SWITCH_BF16",
-    "layer_forward_noalloc", "noalloc_scratch_bytes",
+    "layer_forward_noalloc", "noalloc_scratch_bytes", "layer_forward_train", "layer_forward_add_norm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswitchmoe.so")
@@ -34,7 +34,7 @@ EXPORTED = [
     "switch_launch_names", "switch_add_norm", "switch_topk_workspace_bytes", "switch_topk_layer_forward",
     "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
     "switch_combine_add_norm", "switch_route_dispatch", "switch_layer_forward_noalloc",
-    "switch_noalloc_scratch_bytes",
+    "switch_noalloc_scratch_bytes", "switch_layer_forward_train", "switch_layer_forward_add_norm",
 ]
 BACKWARD_KERNELS = ["bwd_dz", "bwd_dw_out", "bwd_dx", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
                     "bwd_router_w_sum"]
@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.switch_expert_ffn.argtypes = [sp] + [_P] * 6 + [sz, _P]
     lib.switch_combine.argtypes = [sp] + [_P] * 8
     lib.switch_layer_forward.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P]
+    lib.switch_layer_forward_train.argtypes = lib.switch_layer_forward.argtypes
+    lib.switch_layer_forward_add_norm.argtypes = [sp] + [_P] * 7 + [ctypes.c_float] + [_P] * 8 + [sz, _P]
     lib.switch_layer_forward_profiled.argtypes = (
         [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P, ctypes.c_int32, ctypes.c_int32,
                                                                ctypes.c_int32])
@@ -363,6 +365,34 @@ def layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Te
     return o
 
 
+def layer_forward_train(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None,
+                        w_in: torch.Tensor, w_out: torch.Tensor, capacity_: int, add_residual: bool = False,
+                        workspace: torch.Tensor | None = None, out: dict | None = None) -> dict:
+    """The layer forward of a training step (switch_layer_forward_train): the
+    results of layer_forward, and `workspace` then holds the hidden
+    activations that layer_backward reads."""
+    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
+    _check(load_library().switch_layer_forward_train(*args))
+    return o
+
+
+def layer_forward_add_norm(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None,
+                           w_in: torch.Tensor, w_out: torch.Tensor, capacity_: int, gamma: torch.Tensor,
+                           beta: torch.Tensor, eps: float, workspace: torch.Tensor | None = None,
+                           out: dict | None = None) -> dict:
+    """The layer and the block's Add + Normalize in one call
+    (switch_layer_forward_add_norm): o["y"] holds LayerNorm(x + y_bare) *
+    gamma + beta."""
+    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, False, workspace, out)
+    d = x.shape[1]
+    _expect(gamma, "gamma", (d,), torch.float32, x.device)
+    _expect(beta, "beta", (d,), torch.float32, x.device)
+    shape, xp, wr, wb, wi, wo, _res, y, *rest = args
+    _check(load_library().switch_layer_forward_add_norm(shape, xp, wr, wb, wi, wo, _ptr(gamma), _ptr(beta),
+                                                         float(eps), y, *rest))
+    return o
+
+
 def layer_forward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, first_kernel: int, last_kernel: int,
                            times: int = 1, add_residual=False, workspace=None, out=None) -> dict:
     """Kernels first_kernel..last_kernel of layer_forward only, each launched
@@ -499,7 +529,8 @@ def layer_backward(x, w_router, router_bias, w_in, w_out, capacity_: int, fwd: d
                    dy: torch.Tensor, d_aux: float, add_residual: bool = False, workspace=None, out=None) -> dict:
     """Gradients of <dy, y> + d_aux aux_loss for the routing of the forward
     call whose outputs are `fwd` and whose workspace is `fwd_workspace`
-    (switch_layer_backward)."""
+    (switch_layer_backward); that forward must be layer_forward_train, which
+    leaves the hidden activations in its workspace."""
     o, args = _bwd_args(x, w_router, router_bias, w_in, w_out, capacity_, fwd, fwd_workspace, dy, d_aux,
                         add_residual, workspace, out)
     _check(load_library().switch_layer_backward(*args))

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <mutex>
@@ -42,6 +43,28 @@ int fail(int code, const char *fmt, ...) {
 
 int hip_fail(hipError_t e, const char *what) {
   return fail(SWITCH_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+// Debug mode: with the environment variable SMX_DEBUG_SYNC set to anything
+// but "" or "0" (read once, at the first launch), every entry point waits for
+// its stream after each kernel it launches and fails with that kernel's name
+// when the wait reports an error, so a fault is pinned to the kernel that
+// raised it instead of surfacing at some later call.
+bool debug_sync() {
+  static const bool on = [] {
+    const char *v = std::getenv("SMX_DEBUG_SYNC");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+// Result of a single-kernel entry point: the launch status, then, in debug
+// mode, the status of a wait for the stream.
+int launched(hipError_t e, const char *what, void *stream) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (debug_sync() && (e = hipStreamSynchronize((hipStream_t)stream)) != hipSuccess)
+    return fail(SWITCH_E_HIP, "%s (SMX_DEBUG_SYNC wait): %s (%d)", what, hipGetErrorString(e), (int)e);
+  return SWITCH_OK;
 }
 
 // Device address of `scratch` on the current device, looked up once per
@@ -226,15 +249,33 @@ int check_ws(void *ws, size_t ws_bytes, size_t need) {
 // the kernels numbered first..last, each `times` times back to back (every
 // kernel of the layer reads only what earlier kernels wrote and never its own
 // outputs, so a repeat or a rerun on the same workspace changes no result).
+// In debug mode each mark also waits for the stream; after a failed wait no
+// further kernel is issued and done() turns the call's result into the error.
 struct Timer {
   int first = 0, last = 1 << 30;
   int times = 1;
   int n = 0;  // kernels of this call passed so far
   const char *names[16] = {};
-  int reps() const { return (n >= first && n <= last) ? times : 0; }
+  hipStream_t st = nullptr;
+  hipError_t err = hipSuccess;  // debug mode: first failed wait
+  const char *bad = nullptr;    // debug mode: the kernel before it
+  explicit Timer(void *stream) : st((hipStream_t)stream) {}
+  int reps() const { return (err == hipSuccess && n >= first && n <= last) ? times : 0; }
   void mark(const char *name) {
     if (n < 16) names[n] = name;
     ++n;
+    if (err == hipSuccess && debug_sync()) {
+      hipError_t e = hipStreamSynchronize(st);
+      if (e != hipSuccess) {
+        err = e;
+        bad = name;
+      }
+    }
+  }
+  int done(int rc) const {
+    if (rc == SWITCH_OK && err != hipSuccess)
+      return fail(SWITCH_E_HIP, "kernel %s (SMX_DEBUG_SYNC wait): %s (%d)", bad, hipGetErrorString(err), (int)err);
+    return rc;
   }
 };
 
@@ -301,11 +342,26 @@ int run_route(const RouteArgs &a, hipStream_t st, Timer &tm, const LayerMaps &ma
 // The layer with k routes per token.  k = 1: the expert FFN's epilogue writes
 // y directly.  k = 2: it writes each kept route's gate-scaled output to row
 // r * T + t of a workspace buffer, and a last kernel adds the kept routes of
-// each token (and x with the residual) into y.
+// each token (and x with the residual) into y.  The expert FFN is one fused
+// kernel where the shape allows it, unless save_hidden asks for the hidden
+// activations H in the workspace (the backward reads them): then it is the
+// up-projection (writing H) and the down-projection with the combine.
+bool fused_ffn(const switch_shape *s, bool save_hidden) {
+  return !save_hidden && ffn_fused_eligible(s->dtype, s->d_model, s->d_ff, s->capacity);
+}
+
+// The block's Add + Normalize after the layer (k = 1): y then holds
+// (v - mean) / sqrt(var + eps) * gamma + beta with v = x + layer output.
+struct NormOpt {
+  const float *gamma, *beta;
+  float eps;
+};
+
 int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *w_router,
                   const float *router_bias, const void *w_in, const void *w_out, int32_t add_residual, void *y,
                   int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count,
-                  float *aux_loss, void *ws, size_t ws_bytes, void *stream, Timer &tm) {
+                  float *aux_loss, void *ws, size_t ws_bytes, void *stream, Timer &tm, bool save_hidden = false,
+                  const NormOpt *norm = nullptr) {
   int rc = check_shape(s);
   if (rc) return rc;
   if ((rc = check_topk(s, k))) return rc;
@@ -326,25 +382,55 @@ int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *
   maps.tok = (int32_t *)(w + L.lf_tok);
   maps.gmap = (float *)(w + L.lf_gmap);
   const void *xres = add_residual ? x : nullptr;
+  const bool fused = fused_ffn(s, save_hidden);
+  // normalization inside the fused kernel (kept rows) and the assignment
+  // (dropped rows); otherwise the bare layer, then the Add + Normalize kernel
+  const bool norm_fused = norm && fused;
   if (k == 1) {
-    maps.xres = xres;
+    maps.xres = norm ? (norm_fused ? x : nullptr) : xres;
     maps.y = y;
+    if (norm_fused) {
+      maps.gamma = norm->gamma;
+      maps.beta = norm->beta;
+      maps.eps = norm->eps;
+    }
   } else {
     maps.rows = (int32_t *)(w + L.lf_rows);
   }
   if ((rc = run_route(ra, st, tm, maps))) return rc;
   hipError_t e;
+  void *routed = k == 1 ? y : (void *)(w + L.lf_routed);
+  if (fused) {
+    // the whole expert FFN and the combine in one kernel
+    FusedFfnCall fc{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w_out, routed,
+                    expert_count, maps.tok, k == 1 ? nullptr : maps.rows, maps.gmap,
+                    k == 1 ? (norm_fused ? x : xres) : nullptr};
+    if (norm_fused) {
+      fc.gamma = norm->gamma;
+      fc.beta = norm->beta;
+      fc.eps = norm->eps;
+    }
+    for (int r = tm.reps(); r > 0; --r)
+      if ((e = launch_ffn_fused(fc, st)) != hipSuccess) return hip_fail(e, "ffn launch");
+    tm.mark("ffn");
+  } else {
   GemmCall up{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w + L.lf_hidden,
               expert_count, maps.tok, nullptr, nullptr, nullptr};
   for (int r = tm.reps(); r > 0; --r)
     if ((e = launch_ffn_up_gather(up, st)) != hipSuccess) return hip_fail(e, "ffn_up launch");
   tm.mark("ffn_up");
-  void *routed = k == 1 ? y : (void *)(w + L.lf_routed);
   GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, routed,
-                expert_count, k == 1 ? maps.tok : maps.rows, gate, maps.gmap, k == 1 ? xres : nullptr};
+                expert_count, k == 1 ? maps.tok : maps.rows, gate, maps.gmap, k == 1 && !norm ? xres : nullptr};
   for (int r = tm.reps(); r > 0; --r)
     if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
   tm.mark("ffn_down");
+  }
+  if (norm && !norm_fused && s->tokens > 0) {  // in place: y = Add + Normalize(x, y)
+    AddNormArgs an{s->dtype, s->tokens, s->d_model, x, y, norm->gamma, norm->beta, norm->eps, y, CombineRows{}};
+    for (int r = tm.reps(); r > 0; --r)
+      if ((e = launch_add_norm(an, st)) != hipSuccess) return hip_fail(e, "add_norm launch");
+    tm.mark("add_norm");
+  }
   if (k > 1) {
     TopkSumArgs sa{s->dtype, k, s->tokens, s->d_model, routed, dropped, xres, y};
     for (int r = tm.reps(); r > 0; --r)
@@ -526,8 +612,8 @@ int switch_route(const switch_shape *s, const void *x, const float *w_router, co
     if ((rc = route_args(s, x, w_router, router_bias, expert_idx, gate, slot, dropped, expert_count, aux_loss, ws,
                          ws_bytes, L, a)))
       return rc;
-    Timer tm;
-    return run_route(a, (hipStream_t)stream, tm);
+    Timer tm(stream);
+    return tm.done(run_route(a, (hipStream_t)stream, tm));
   })
 }
 
@@ -558,11 +644,11 @@ int switch_route_dispatch(const switch_shape *s, const void *x, const float *w_r
     a.agg_p = (int64_t *)(w + L.fz_aggp);
     a.inc_p = (int64_t *)(w + L.fz_incp);
     a.dispatched = s->capacity > 0 ? dispatched : nullptr;
-    Timer tm;
+    Timer tm(stream);
     LaunchMarks marks{[](void *ctx, const char *name) { static_cast<Timer *>(ctx)->mark(name); },
                       [](void *ctx) { return static_cast<Timer *>(ctx)->reps(); }, &tm};
     hipError_t e = launch_route_fused(a, (hipStream_t)stream, marks);
-    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "route_dispatch launch");
+    return tm.done(e == hipSuccess ? SWITCH_OK : hip_fail(e, "route_dispatch launch"));
   })
 }
 
@@ -581,7 +667,7 @@ int switch_dispatch(const switch_shape *s, const void *x, const int32_t *expert_
     DispatchArgs a{s->dtype, s->tokens, s->d_model, s->num_experts, s->capacity, x,
                    expert_idx, slot, dropped, dispatched};
     hipError_t e = launch_dispatch(a, (hipStream_t)stream);
-    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "dispatch launch");
+    return launched(e, "dispatch launch", stream);
   })
 }
 
@@ -603,10 +689,8 @@ int switch_expert_ffn(const switch_shape *s, const void *dispatched, const int32
     if ((rc = check_ws(ws, ws_bytes, L.ffn_end))) return rc;
     FfnArgs a{s->dtype, s->d_model, s->d_ff, s->num_experts, s->capacity, dispatched, expert_count,
               w_in, w_out, (char *)ws + L.ffn_hidden, expert_out};
-    hipError_t e = launch_ffn_up(a, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "ffn_up launch");
-    e = launch_ffn_down(a, (hipStream_t)stream);
-    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "ffn_down launch");
+    if ((rc = launched(launch_ffn_up(a, (hipStream_t)stream), "ffn_up launch", stream))) return rc;
+    return launched(launch_ffn_down(a, (hipStream_t)stream), "ffn_down launch", stream);
   })
 }
 
@@ -628,7 +712,7 @@ int switch_combine(const switch_shape *s, const void *expert_out, const int32_t 
     CombineArgs a{s->dtype, s->tokens, s->d_model, s->num_experts, s->capacity, expert_out,
                   expert_idx, slot, dropped, gate, x_residual, y};
     hipError_t e = launch_combine(a, (hipStream_t)stream);
-    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "combine launch");
+    return launched(e, "combine launch", stream);
   })
 }
 
@@ -650,7 +734,7 @@ int switch_add_norm(const switch_shape *s, const void *x, const void *y, const f
     }
     AddNormArgs a{s->dtype, s->tokens, s->d_model, x, y, gamma, beta, eps, out, CombineRows{}};
     hipError_t e = launch_add_norm(a, (hipStream_t)stream);
-    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "add_norm launch");
+    return launched(e, "add_norm launch", stream);
   })
 }
 
@@ -678,7 +762,7 @@ int switch_combine_add_norm(const switch_shape *s, const void *expert_out, const
     CombineRows rows{expert_idx, slot, dropped, gate, s->capacity};
     AddNormArgs a{s->dtype, s->tokens, s->d_model, x, expert_out, gamma, beta, eps, out, rows};
     hipError_t e = launch_add_norm(a, (hipStream_t)stream);
-    return e == hipSuccess ? SWITCH_OK : hip_fail(e, "combine_add_norm launch");
+    return launched(e, "combine_add_norm launch", stream);
   })
 }
 
@@ -687,9 +771,43 @@ int switch_layer_forward(const switch_shape *s, const void *x, const float *w_ro
                          float *gate, int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss,
                          void *ws, size_t ws_bytes, void *stream) {
   GUARD({
-    Timer tm;
-    return layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
-                         dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
+    Timer tm(stream);
+    return tm.done(layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate,
+                                 slot, dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm));
+  })
+}
+
+int switch_layer_forward_train(const switch_shape *s, const void *x, const float *w_router,
+                               const float *router_bias, const void *w_in, const void *w_out, int32_t add_residual,
+                               void *y, int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
+                               int32_t *expert_count, float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
+  GUARD({
+    Timer tm(stream);
+    return tm.done(layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate,
+                                 slot, dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm, true));
+  })
+}
+
+int switch_layer_forward_add_norm(const switch_shape *s, const void *x, const float *w_router,
+                                  const float *router_bias, const void *w_in, const void *w_out, const float *gamma,
+                                  const float *beta, float eps, void *out, int32_t *expert_idx, float *gate,
+                                  int32_t *slot, uint8_t *dropped, int32_t *expert_count, float *aux_loss, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  GUARD({
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(SWITCH_E_INVALID, "eps = %g: need a finite eps >= 0", eps);
+    if (s->d_model > add_norm_max_d(s->dtype))
+      return fail(SWITCH_E_UNSUPPORTED, "d_model = %d above %d for the normalization", s->d_model,
+                  add_norm_max_d(s->dtype));
+    if (s->tokens > 0) {
+      NEED(gamma, 4);
+      NEED(beta, 4);
+    }
+    const NormOpt norm{gamma, beta, eps};
+    Timer tm(stream);
+    return tm.done(layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, 0, out, expert_idx, gate, slot, dropped,
+                                 expert_count, aux_loss, ws, ws_bytes, stream, tm, false, &norm));
   })
 }
 
@@ -707,9 +825,9 @@ int switch_layer_forward_noalloc(const switch_shape *s, const void *x, const flo
                   L.total, kNoAllocScratchBytes);
     void *ws = scratch_address();
     if (!ws) return SWITCH_E_HIP;
-    Timer tm;
-    return layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
-                         dropped, expert_count, aux_loss, ws, kNoAllocScratchBytes, stream, tm);
+    Timer tm(stream);
+    return tm.done(layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate,
+                                 slot, dropped, expert_count, aux_loss, ws, kNoAllocScratchBytes, stream, tm));
   })
 }
 
@@ -731,12 +849,12 @@ int switch_layer_forward_profiled(const switch_shape *s, const void *x, const fl
     if (times < 1) return fail(SWITCH_E_INVALID, "times = %d < 1", times);
     if (first_kernel < 0 || last_kernel < first_kernel)
       return fail(SWITCH_E_INVALID, "kernel range %d..%d", first_kernel, last_kernel);
-    Timer tm;
+    Timer tm(stream);
     tm.first = first_kernel;
     tm.last = last_kernel;
     tm.times = times;
-    int rc = layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
-                           dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
+    int rc = tm.done(layer_forward(s, 1, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate,
+                                   slot, dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm));
     if (rc == SWITCH_OK && last_kernel >= tm.n)
       return fail(SWITCH_E_INVALID, "kernel range %d..%d: the call launches %d kernels", first_kernel, last_kernel,
                   tm.n);
@@ -762,9 +880,9 @@ int switch_topk_layer_forward(const switch_shape *s, int32_t top_k, const void *
                               void *y, int32_t *expert_idx, float *gate, int32_t *slot, uint8_t *dropped,
                               int32_t *expert_count, float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
   GUARD({
-    Timer tm;
-    return layer_forward(s, top_k, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate, slot,
-                         dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm);
+    Timer tm(stream);
+    return tm.done(layer_forward(s, top_k, x, w_router, router_bias, w_in, w_out, add_residual, y, expert_idx, gate,
+                                 slot, dropped, expert_count, aux_loss, ws, ws_bytes, stream, tm));
   })
 }
 
@@ -787,10 +905,10 @@ int switch_layer_backward(const switch_shape *s, const void *x, const float *w_r
                           float *d_router_bias, void *dw_in, void *dw_out, void *workspace, size_t workspace_bytes,
                           void *stream) {
   GUARD({
-    Timer tm;
-    return layer_backward(s, x, w_router, router_bias, w_in, w_out, add_residual, expert_idx, dropped, expert_count,
-                          fwd_workspace, fwd_workspace_bytes, dy, d_aux, dx, dw_router, d_router_bias, dw_in,
-                          dw_out, workspace, workspace_bytes, stream, tm);
+    Timer tm(stream);
+    return tm.done(layer_backward(s, x, w_router, router_bias, w_in, w_out, add_residual, expert_idx, dropped,
+                                  expert_count, fwd_workspace, fwd_workspace_bytes, dy, d_aux, dx, dw_router,
+                                  d_router_bias, dw_in, dw_out, workspace, workspace_bytes, stream, tm));
   })
 }
 
@@ -806,13 +924,13 @@ int switch_layer_backward_profiled(const switch_shape *s, const void *x, const f
     if (times < 1) return fail(SWITCH_E_INVALID, "times = %d < 1", times);
     if (first_kernel < 0 || last_kernel < first_kernel)
       return fail(SWITCH_E_INVALID, "kernel range %d..%d", first_kernel, last_kernel);
-    Timer tm;
+    Timer tm(stream);
     tm.first = first_kernel;
     tm.last = last_kernel;
     tm.times = times;
-    int rc = layer_backward(s, x, w_router, router_bias, w_in, w_out, add_residual, expert_idx, dropped,
-                            expert_count, fwd_workspace, fwd_workspace_bytes, dy, d_aux, dx, dw_router,
-                            d_router_bias, dw_in, dw_out, workspace, workspace_bytes, stream, tm);
+    int rc = tm.done(layer_backward(s, x, w_router, router_bias, w_in, w_out, add_residual, expert_idx, dropped,
+                                    expert_count, fwd_workspace, fwd_workspace_bytes, dy, d_aux, dx, dw_router,
+                                    d_router_bias, dw_in, dw_out, workspace, workspace_bytes, stream, tm));
     if (rc == SWITCH_OK && last_kernel >= tm.n)
       return fail(SWITCH_E_INVALID, "kernel range %d..%d: the call launches %d kernels", first_kernel, last_kernel,
                   tm.n);
@@ -835,8 +953,12 @@ int switch_launch_names(const switch_shape *s, const char **names, int32_t max_n
       seq[n++] = "assign_scan";
       seq[n++] = "assign_apply";
     }
-    seq[n++] = "ffn_up";
-    seq[n++] = "ffn_down";
+    if (fused_ffn(s, false)) {
+      seq[n++] = "ffn";
+    } else {
+      seq[n++] = "ffn_up";
+      seq[n++] = "ffn_down";
+    }
     for (int i = 0; i < n && i < max_names; ++i) names[i] = seq[i];
     *num_names = n;
     return SWITCH_OK;

@@ -136,19 +136,76 @@ __global__ __launch_bounds__(256) void assign_apply_kernel(
   if (blockIdx.x == 0) write_aux_loss(T, k, N, expert_count, psum, aux_loss);
 }
 
+// Output row of a dropped token whose layer output is 0, under the block's
+// Add + Normalize ("The Architecture in Place"): (x - mean) / sqrt(var + eps)
+// * gamma + beta over the row's d = 8 * row16 (bf16) or 4 * row16 (fp32)
+// values, by one wave: per-lane partial sums in piece order, then fixed-order
+// butterflies, so every run gives the same bits.  The row is read three
+// times (sum, squared deviations, output); it is 16 * row16 bytes.
+__device__ __forceinline__ void norm_row_wave(const u32x4 *__restrict__ xrow, u32x4 *__restrict__ orow, int row16,
+                                              bool bf16_, const float *__restrict__ gamma,
+                                              const float *__restrict__ beta, float eps, int lane) {
+  const int per = bf16_ ? 8 : 4;
+  const int d = row16 * per;
+  auto val = [&](const u32x4 &v, int k) {
+    return bf16_ ? (float)as_bf16x8(v)[k] : __builtin_bit_cast(f32x4, v)[k & 3];
+  };
+  float s = 0.f;
+  for (int c = lane; c < row16; c += kWave) {
+    const u32x4 v = xrow[c];
+    for (int k = 0; k < per; ++k) s += val(v, k);
+  }
+  const float mean = wave_sum(s) / (float)d;
+  float q = 0.f;
+  for (int c = lane; c < row16; c += kWave) {
+    const u32x4 v = xrow[c];
+    for (int k = 0; k < per; ++k) {
+      const float dv = val(v, k) - mean;
+      q += dv * dv;
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+  for (int c = lane; c < row16; c += kWave) {
+    const u32x4 v = xrow[c];
+    u32x4 o;
+    if (bf16_) {
+      bf16x8 r;
+      for (int k = 0; k < 8; ++k) r[k] = (bf16)((val(v, k) - mean) * rstd * gamma[c * 8 + k] + beta[c * 8 + k]);
+      o = as_u32x4(r);
+    } else {
+      f32x4 r;
+      for (int k = 0; k < 4; ++k) r[k] = (val(v, k) - mean) * rstd * gamma[c * 4 + k] + beta[c * 4 + k];
+      o = __builtin_bit_cast(u32x4, r);
+    }
+    orow[c] = o;
+  }
+}
+
 // Layer path variant of the apply step: besides slot and dropped it records
 // which token sits in each live slot (tok[e][slot] = t), the route's output
 // row (rows[e][slot], when rows is set) and its gate (gmap[e][slot]) for the
 // expert FFN to gather from and scatter to, and, when y is set (one route per
 // token), writes the output rows of dropped tokens (their computation is
-// skipped: 0, or x when a residual is added).
+// skipped: 0, or x when a residual is added, or the Add + Normalize of x).
+struct DropRows {
+  const u32x4 *xres;
+  u32x4 *y;
+  int row16;
+  bool bf16_;
+  const float *gamma, *beta;  // set: normalized rows
+  float eps;
+};
+
 __global__ __launch_bounds__(256) void assign_apply_layer_kernel(
     const int32_t *__restrict__ expert_idx, const int32_t *__restrict__ rank, int32_t *__restrict__ slot,
     uint8_t *__restrict__ dropped,
     const int32_t *__restrict__ boff, int64_t T, int64_t Tp, int k, int N, int C,
     const int32_t *__restrict__ expert_count, const float *__restrict__ psum, float *__restrict__ aux_loss,
     int32_t *__restrict__ tok, int32_t *__restrict__ rows, float *__restrict__ gmap, const float *__restrict__ gate,
-    const u32x4 *__restrict__ xres, u32x4 *__restrict__ y, int row16) {
+    const DropRows dr) {
+  const u32x4 *__restrict__ xres = dr.xres;
+  u32x4 *__restrict__ y = dr.y;
+  const int row16 = dr.row16;
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int lane = threadIdx.x % kWave;
   bool drop = false;
@@ -171,8 +228,11 @@ __global__ __launch_bounds__(256) void assign_apply_layer_kernel(
       const int b = __ffsll(mask) - 1;
       mask &= mask - 1;
       const int64_t tt = j - lane + b;
-      for (int c = lane; c < row16; c += kWave)
-        y[tt * row16 + c] = xres ? xres[tt * row16 + c] : u32x4{0, 0, 0, 0};
+      if (dr.gamma)
+        norm_row_wave(xres + tt * row16, y + tt * row16, row16, dr.bf16_, dr.gamma, dr.beta, dr.eps, lane);
+      else
+        for (int c = lane; c < row16; c += kWave)
+          y[tt * row16 + c] = xres ? xres[tt * row16 + c] : u32x4{0, 0, 0, 0};
     }
   }
   if (blockIdx.x == 0) write_aux_loss(T, k, N, expert_count, psum, aux_loss);
@@ -222,6 +282,9 @@ struct AssignArgs {
   const u32x4 *xres;
   u32x4 *y;       // layer path with k = 1, or null
   int row16;
+  bool bf16_;
+  const float *gamma, *beta;  // set: dropped rows are the Add + Normalize of x
+  float eps;
 };
 
 size_t assign_one_smem(int N) {
@@ -348,10 +411,17 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
     }
     __syncthreads();
     const int nd = s_nd;
-    for (int it = tid; it < nd * p.row16; it += kAsThreads) {
-      const int r = it / p.row16, c = it - r * p.row16;
-      const int64_t tt = s_drop[r];
-      p.y[tt * p.row16 + c] = p.xres ? p.xres[tt * p.row16 + c] : u32x4{0, 0, 0, 0};
+    if (p.gamma) {  // one wave per row
+      for (int r = tid / kWave; r < nd; r += kAsThreads / kWave) {
+        const int64_t tt = s_drop[r];
+        norm_row_wave(p.xres + tt * p.row16, p.y + tt * p.row16, p.row16, p.bf16_, p.gamma, p.beta, p.eps, lane);
+      }
+    } else {
+      for (int it = tid; it < nd * p.row16; it += kAsThreads) {
+        const int r = it / p.row16, c = it - r * p.row16;
+        const int64_t tt = s_drop[r];
+        p.y[tt * p.row16 + c] = p.xres ? p.xres[tt * p.row16 + c] : u32x4{0, 0, 0, 0};
+      }
     }
   }
 
@@ -396,7 +466,8 @@ hipError_t launch_assign(const RouteArgs &a, const LayerMaps &m, hipStream_t st,
   u32x4 *y = a.k == 1 ? (u32x4 *)m.y : nullptr;
   if (assign_single_launch(nb, a.N)) {
     AssignArgs p{a.expert_idx, a.rank, a.slot, a.dropped, a.bcount, a.ppart, a.T, Tp, nb, a.k, a.N, a.C,
-                 a.expert_count, a.psum, a.aux_loss, a.gate, m.tok, m.rows, m.gmap, (const u32x4 *)m.xres, y, row16};
+                 a.expert_count, a.psum, a.aux_loss, a.gate, m.tok, m.rows, m.gmap, (const u32x4 *)m.xres, y, row16,
+                 a.dtype == kBF16, m.gamma, m.beta, m.eps};
     for (int r = reps(); r > 0; --r)
       assign_one_kernel<<<dim3((unsigned)ceil_div(nb, kAsBlocks)), dim3(kAsThreads), assign_one_smem(a.N), st>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -413,7 +484,8 @@ hipError_t launch_assign(const RouteArgs &a, const LayerMaps &m, hipStream_t st,
     if (m.tok)
       assign_apply_layer_kernel<<<grid, dim3(256), 0, st>>>(
           a.expert_idx, a.rank, a.slot, a.dropped, a.boff, a.T, Tp, a.k, a.N, a.C, a.expert_count, a.psum,
-          a.aux_loss, m.tok, m.rows, m.gmap, a.gate, (const u32x4 *)m.xres, y, row16);
+          a.aux_loss, m.tok, m.rows, m.gmap, a.gate,
+          DropRows{(const u32x4 *)m.xres, y, row16, a.dtype == kBF16, m.gamma, m.beta, m.eps});
     else
       assign_apply_kernel<<<grid, dim3(256), 0, st>>>(a.expert_idx, a.rank, a.slot, a.dropped, a.boff, a.T, Tp,
                                                       a.k, a.N, a.C, a.expert_count, a.psum, a.aux_loss);

@@ -998,11 +998,8 @@ hipError_t run_bf16(const BwdArgs<bf16> &a, hipStream_t st) {
 // Resident operand rows R (through the slot -> token map, width d), streamed
 // rows S ([N][C][d_ff]), output [N][d][d_ff] or [N][d_ff][d].
 int wgrad_grid_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-    cus = 256;
-  return cus;
+  const int cus = device_cus();
+  return cus < 8 ? 256 : cus;
 }
 
 // Resident operand rows R (through the slot -> token map, width d), streamed

@@ -30,8 +30,20 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace smx {
+
+int device_cus() {
+  static std::atomic<int> cache[kMaxDeviceCache];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool cached = dev >= 0 && dev < kMaxDeviceCache;
+  if (cached && (cus = cache[dev].load(std::memory_order_relaxed)) > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  if (cached) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 constexpr int kFfnThreads = 256;  // fp32 kernel: 4 waves
 constexpr int kKC = 64;           // contraction chunk
@@ -436,13 +448,19 @@ inline unsigned grid_of(int ntiles) { return (unsigned)(ceil_div(ntiles, 8) * 8)
 // that spreads the output features more evenly over the CUs.
 constexpr int kWaves = 8;
 
-// Resident workgroups for a persistent launch: CUs x workgroups per CU.
+// Resident workgroups for a persistent launch: CUs x workgroups per CU (the
+// occupancy of each kernel queried once per device).
 template <typename Kern>
 unsigned persistent_grid(Kern kern, int ntiles) {
-  int dev = 0, cus = 0, occ = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kWaves * 64, 0) != hipSuccess || occ < 1) occ = 1;
+  static std::atomic<int> occ_cache[kMaxDeviceCache];
+  const int cus = device_cus();
+  int dev = 0, occ = 0;
+  const bool cached = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDeviceCache;
+  if (cached) occ = occ_cache[dev].load(std::memory_order_relaxed);
+  if (occ < 1) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kWaves * 64, 0) != hipSuccess || occ < 1) occ = 1;
+    if (cached) occ_cache[dev].store(occ, std::memory_order_relaxed);
+  }
   const int64_t want = std::min<int64_t>((int64_t)cus * occ, ceil_div(ntiles, 8) * 8);
   return (unsigned)std::max<int64_t>(8, ceil_div(want, 8) * 8);
 }
@@ -462,10 +480,7 @@ hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
 // 4 tiles of 256 give every CU the same).  Ties keep the wider tile, which
 // re-reads each expert's activation rows fewer times.
 int pick_nbw(const GemmCall &c, int rows) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
+  const int cus = device_cus();
   auto span = [&](int nbw) {
     const int64_t cols = (int64_t)kWaves * 16 * nbw;
     const int64_t tiles = (int64_t)c.N * ceil_div(c.C, rows) * ceil_div(c.Nout, cols);

@@ -106,6 +106,11 @@ struct GemmCall {
   const void *xres;    // [T][Nout] residual rows (combine), may be null
 };
 
+// Compute units of the current device, queried once per device (256 when the
+// query fails); the launchers size persistent grids with it.
+constexpr int kMaxDeviceCache = 64;
+int device_cus();
+
 // Each launcher enqueues its kernels on `st` and returns the launch status.
 hipError_t launch_router(const RouteArgs &a, hipStream_t st);
 // Capacity assignment and loss after the router.  Small batches take one
@@ -131,6 +136,10 @@ struct LayerMaps {
   float *gmap = nullptr;    // [N][C] gate of each live slot
   const void *xres = nullptr;
   void *y = nullptr;
+  // with gamma set (and xres = x), the rows of dropped tokens are the block's
+  // Add + Normalize of x alone: (x - mean) / sqrt(var + eps) * gamma + beta
+  const float *gamma = nullptr, *beta = nullptr;
+  float eps = 0.f;
 };
 hipError_t launch_assign(const RouteArgs &a, const LayerMaps &m, hipStream_t st, LaunchMarks marks);
 
@@ -168,6 +177,26 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st);
 hipError_t launch_ffn_up(const FfnArgs &a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st);
 hipError_t launch_ffn_up_gather(const GemmCall &c, hipStream_t st);
+// Expert FFN and combine in one kernel (ffn_fused.hip): the hidden
+// activations stay on chip.  Taken by the layer call when
+// ffn_fused_eligible(dtype, d, d_ff, C).
+struct FusedFfnCall {
+  int dtype, N, C, d, dff;
+  const void *x;           // [T][d]
+  const void *w_in;        // [N][dff][d]
+  const void *w_out;       // [N][d][dff]
+  void *out;               // y [T][d], or the routed rows [k][T][d]
+  const int32_t *counts;
+  const int32_t *tok;      // [N][C]
+  const int32_t *rows;     // [N][C] output row of each live slot, or null (= tok)
+  const float *gmap;       // [N][C]
+  const void *xres;        // residual rows, or null
+  // set (k = 1, xres = x): write the block's Add + Normalize of x + y instead of y
+  const float *gamma = nullptr, *beta = nullptr;
+  float eps = 0.f;
+};
+bool ffn_fused_eligible(int dtype, int d, int dff, int C);
+hipError_t launch_ffn_fused(const FusedFfnCall &c, hipStream_t st);
 hipError_t launch_ffn_down_combine(const GemmCall &c, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_add_norm(const AddNormArgs &a, hipStream_t st);

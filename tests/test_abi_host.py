@@ -166,6 +166,11 @@ def test_launch_names_follow_the_shape():
     import torch
     base = B.make_shape(16384, 768, 3072, 128, 160, torch.bfloat16)
     assert smx.launch_names(base) == ["router", "assign", "ffn_up", "ffn_down"]
+    # bf16, d_model 128 or 256, capacity <= 160: the expert FFN is one kernel
+    narrow = B.make_shape(16384, 256, 1024, 128, 160, torch.bfloat16)
+    assert smx.launch_names(narrow) == ["router", "assign", "ffn"]
+    deep = B.make_shape(16384, 256, 1024, 128, 161, torch.bfloat16)
+    assert smx.launch_names(deep) == ["router", "assign", "ffn_up", "ffn_down"]
     # many router blocks x many experts: scan over blocks, then apply
     many = B.make_shape(32768, 2048, 6144, 2048, 16, torch.bfloat16)
     assert smx.launch_names(many) == ["router", "assign_scan", "assign_apply", "ffn_up", "ffn_down"]

@@ -60,8 +60,8 @@ def _run(cfg: LayerConfig, d_aux=0.5, add_residual=False, bias=None, capacity=No
     T, d = cfg.tokens, cfg.d_model
     shape = smx.binding.make_shape(T, d, cfg.d_ff, cfg.num_experts, C, cfg.torch_dtype)
     ws = torch.empty(max(smx.workspace_bytes(shape), 256), dtype=torch.uint8, device=DEV)
-    fwd = smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C,
-                            add_residual=add_residual, workspace=ws)
+    fwd = smx.layer_forward_train(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C,
+                                  add_residual=add_residual, workspace=ws)
     g = torch.Generator().manual_seed(seed)
     dy = torch.randn(T, d, generator=g).to(cfg.torch_dtype).to(DEV)
     grads = smx.layer_backward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C, fwd, ws,
@@ -245,7 +245,7 @@ def test_backward_empty_batch():
                     ("dropped", torch.uint8)):
         out[key] = torch.empty(0, dtype=dt, device=DEV)
     out["y"] = torch.empty(0, cfg.d_model, dtype=torch.bfloat16, device=DEV)
-    smx.layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], 0, workspace=ws, out=out)
+    smx.layer_forward_train(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], 0, workspace=ws, out=out)
     dy = torch.empty(0, cfg.d_model, dtype=torch.bfloat16, device=DEV)
     grads = smx.layer_backward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], 0, out, ws, dy, 1.0)
     torch.cuda.synchronize()
