@@ -11,6 +11,11 @@
         per kernel: MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES (summed over
         SIMDs) / (GRBM_GUI_ACTIVE / X x SIMDs) and bf16 MFMA flops per
         dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
+    python -m sparse_mixture_experts_switch_amd.profsummary counters DB OUT --kernels a,b --cmd "..." --source FILE
+        per listed kernel: the per-dispatch average of every counter the run
+        collected, and, when present, LDS bank-conflict cycles per LDS-active
+        cycle (SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS) and the fraction of
+        wave cycles spent waiting (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)
 
 Kernel names are the library's launch names: ffn_up / ffn_down are the
 grouped-GEMM instantiations that gather token rows (ReLU epilogue) and that
@@ -26,6 +31,7 @@ import sqlite3
 
 COPY_BYTES = 1 << 30
 KERNEL_KEYS = {
+    "ffn": ("ffn_fused_bf16_kernel", ""),
     "ffn_up": ("ffn_gemm_bf16_kernel", "Lb1ELi0E"),
     "ffn_down": ("ffn_gemm_bf16_kernel", "Lb0ELi2E"),
     "router": ("router_fwd_bf16_kernel", ""),
@@ -150,6 +156,35 @@ def mfma_summary(db: str, cmd: str, simds: int, xcds: int, source: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def counters_summary(db: str, kernels: list, cmd: str, source: str) -> str:
+    con = sqlite3.connect(db)
+    names = [r[0] for r in con.execute("select distinct counter_name from counters_collection")]
+    with open(source, "rb") as fh:
+        digest = hashlib.sha256(fh.read()).hexdigest()[:16]
+    lines = [f"# counters per dispatch (base workload), rocprofv3 --pmc", f"# command: {cmd}",
+             f"source_sha256 = {digest}"]
+    for short in kernels:
+        vals = {}
+        for cname in names:
+            agg = _counter(db, cname)
+            v = [x for name, xs in agg.items() if short_name(name) == short for x in xs]
+            if v:
+                vals[cname] = sum(v) / len(v)
+        if not vals:
+            lines.append(f"{short}: no dispatches")
+            continue
+        n = len([x for name, xs in _counter(db, names[0]).items() if short_name(name) == short for x in xs])
+        lines.append(f"[{short}] dispatches = {n}")
+        for cname in sorted(vals):
+            lines.append(f"{short}.{cname} = {vals[cname]:.6g}")
+        if vals.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in vals:
+            lines.append(f"{short}.lds_bank_conflict_per_lds_active_cycle = "
+                         f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_ACTIVE_INST_LDS']:.4f}")
+        if vals.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in vals:
+            lines.append(f"{short}.wait_fraction_of_wave_cycles = {vals['SQ_WAIT_INST_ANY'] / vals['SQ_WAVE_CYCLES']:.4f}")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -171,11 +206,19 @@ def main():
     m.add_argument("--simds", type=int, required=True)
     m.add_argument("--xcds", type=int, required=True)
     m.add_argument("--source", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("db")
+    k.add_argument("out")
+    k.add_argument("--kernels", required=True)
+    k.add_argument("--cmd", required=True)
+    k.add_argument("--source", required=True)
     a = ap.parse_args()
     if a.mode == "trace":
         text = trace_summary(a.db, a.cmd)
     elif a.mode == "traffic":
         text = traffic_summary(a.fetch_db, a.write_db, a.kernel, a.cmd, a.source)
+    elif a.mode == "counters":
+        text = counters_summary(a.db, a.kernels.split(","), a.cmd, a.source)
     else:
         text = mfma_summary(a.db, a.cmd, a.simds, a.xcds, a.source)
     with open(a.out, "w") as fh:
