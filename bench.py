@@ -250,18 +250,18 @@ def backward_bench(smx, torch, inp, out, ws, C, cfg, stream, steps: int) -> dict
                         for k, v in kern.items()}}
 
 
-def top2_bench(smx, torch, inp, cfg, stream, steps: int) -> dict:
+def top2_bench(smx, torch, inp, cfg, stream, steps: int, weights, tiled: bool) -> dict:
     """Classic top-2 routing on the same workload (switch_topk_layer_forward,
     capacity from 2 T so that both routes have room): whole-call time."""
     T, d, f, N = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts
     dev = inp["x"].device
     C2 = smx.capacity(2 * T, N, cfg.capacity_factor)
-    shape2 = smx.binding.make_shape(T, d, f, N, C2, cfg.torch_dtype)
+    shape2 = smx.binding.make_shape(T, d, f, N, C2, cfg.torch_dtype, tiled)
     ws2 = torch.empty(smx.topk_workspace_bytes(shape2, 2), dtype=torch.uint8, device=dev)
     out2 = smx.binding._route_outputs(T, N, dev, 2)
     out2["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
     call2 = lambda: smx.topk_layer_forward(inp["x"], inp["w_router"], inp["router_bias"],  # noqa: E731
-                                           inp["w_in"], inp["w_out"], C2, 2, workspace=ws2, out=out2)
+                                           *weights, C2, 2, workspace=ws2, out=out2, tiled=tiled)
     with torch.cuda.stream(stream):
         t_warm = time.perf_counter()
         while time.perf_counter() - t_warm < MIN_WARMUP_S:
@@ -282,7 +282,7 @@ def top2_bench(smx, torch, inp, cfg, stream, steps: int) -> dict:
             "ffn_tflop_per_s_whole_call": round(4.0 * kept2 * d * f / (ms2 * 1e-3) / 1e12, 1)}
 
 
-def mfma_diag_bench(smx, torch, cfg, stream, steps: int) -> dict:
+def mfma_diag_bench(smx, torch, cfg, stream, steps: int, tiled: bool) -> dict:
     """Unranked diagnostic of the expert FFN's matrix-core use: the same
     dimensions with 4x the tokens (512 per expert, capacity 640), where each
     weight byte feeds more multiply-adds than the HBM/MFMA ridge (~315 flop/B)
@@ -292,16 +292,19 @@ def mfma_diag_bench(smx, torch, cfg, stream, steps: int) -> dict:
     dcfg = cfg.with_(name="mfma_diag", tokens=4 * cfg.tokens)
     dev = torch.device("cuda:0")
     inp = make_inputs(dcfg, device=dev)
+    if tiled:
+        convert_in_place(smx, torch, inp["w_in"], True)
+        convert_in_place(smx, torch, inp["w_out"], True)
     T, d, f, N = dcfg.tokens, dcfg.d_model, dcfg.d_ff, dcfg.num_experts
     C = smx.capacity(T, N, dcfg.capacity_factor)
-    shape = smx.binding.make_shape(T, d, f, N, C, dcfg.torch_dtype)
+    shape = smx.binding.make_shape(T, d, f, N, C, dcfg.torch_dtype, tiled)
     ws = torch.empty(smx.workspace_bytes(shape), dtype=torch.uint8, device=dev)
     out = smx.binding._route_outputs(T, N, dev)
     out["y"] = torch.empty(T, d, dtype=dcfg.torch_dtype, device=dev)
     names = smx.launch_names(shape)
     part = lambda lo, hi: smx.layer_forward_profiled(  # noqa: E731
         inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C, first_kernel=lo,
-        last_kernel=hi, workspace=ws, out=out)
+        last_kernel=hi, workspace=ws, out=out, tiled=tiled)
     kern = {}
     with torch.cuda.stream(stream):
         t_warm = time.perf_counter()
@@ -331,19 +334,37 @@ def mfma_diag_bench(smx, torch, cfg, stream, steps: int) -> dict:
             "note": "unranked: 512 tokens per expert puts the expert FFN above the HBM/MFMA ridge"}
 
 
-def measure_layer(smx, torch, cfg, inp, stream, steps: int, warmup: int, kernels: bool = True) -> dict:
+def convert_in_place(smx, torch, w, to_tiled: bool, chunk: int = 8) -> None:
+    """Expert weights [N][rows][cols] between the row-major and the tiled
+    layout in their own memory, `chunk` experts at a time through a small
+    buffer (the many-expert workload's weights take 103 GB: no second copy)."""
+    tmp = torch.empty_like(w[:chunk])
+    fn = smx.tile_weights if to_tiled else smx.untile_weights
+    for i in range(0, w.shape[0], chunk):
+        j = min(i + chunk, w.shape[0])
+        fn(w[i:j], out=tmp[:j - i])
+        w[i:j].copy_(tmp[:j - i])
+    torch.cuda.synchronize()
+    del tmp
+
+
+def measure_layer(smx, torch, cfg, inp, stream, steps: int, warmup: int, kernels: bool = True,
+                  weights=None, tiled: bool = False) -> dict:
     """Times switch_layer_forward on one workload: `steps` back-to-back steps
     after the warmup, then `steps` cold-cache steps, then (kernels=True) each
-    kernel of the step bracketed by HIP events on the layer's stream."""
+    kernel of the step bracketed by HIP events on the layer's stream.
+    weights: (W_in, W_out) in the layout `tiled` declares (default: inp's,
+    row-major)."""
     dev = inp["x"].device
     T, d, f, N = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts
     C = smx.capacity(T, N, cfg.capacity_factor)
-    shape = smx.binding.make_shape(T, d, f, N, C, cfg.torch_dtype)
+    w_in, w_out = weights if weights is not None else (inp["w_in"], inp["w_out"])
+    shape = smx.binding.make_shape(T, d, f, N, C, cfg.torch_dtype, tiled)
     ws = torch.empty(smx.workspace_bytes(shape), dtype=torch.uint8, device=dev)
     out = smx.binding._route_outputs(T, N, dev)
     out["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
-    call = lambda: smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],  # noqa: E731
-                                     inp["w_out"], C, workspace=ws, out=out)
+    call = lambda: smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], w_in,  # noqa: E731
+                                     w_out, C, workspace=ws, out=out, tiled=tiled)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         # untimed warmup: at least W steps and at least MIN_WARMUP_S seconds
@@ -398,8 +419,8 @@ def measure_layer(smx, torch, cfg, inp, stream, steps: int, warmup: int, kernels
         names = smx.launch_names(shape)
         n_k = len(names)
         part = lambda lo, hi: smx.layer_forward_profiled(  # noqa: E731
-            inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C, first_kernel=lo,
-            last_kernel=hi, workspace=ws, out=out)
+            inp["x"], inp["w_router"], inp["router_bias"], w_in, w_out, C, first_kernel=lo,
+            last_kernel=hi, workspace=ws, out=out, tiled=tiled)
         with torch.cuda.stream(stream):
             for i, name in enumerate(names):
                 evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -537,7 +558,14 @@ def configs_bench(smx, torch, stream, steps: int, warmup: int, cpu: bool, names)
         es = 2 if cfg.dtype == "bf16" else 4
         log(f"bench: configs: generating {cfg}")
         inp = make_inputs(cfg, device=stream.device)
-        m = measure_layer(smx, torch, cfg, inp, stream, steps, warmup)
+        tiled = cfg.dtype == "bf16"  # bf16 layers run on tiled expert weights, converted before timing
+        if tiled:
+            convert_in_place(smx, torch, inp["w_in"], True)
+            convert_in_place(smx, torch, inp["w_out"], True)
+        m = measure_layer(smx, torch, cfg, inp, stream, steps, warmup, tiled=tiled)
+        if tiled:  # back to row-major for the oracle
+            convert_in_place(smx, torch, inp["w_in"], False)
+            convert_in_place(smx, torch, inp["w_out"], False)
         C, kern, counts = m["C"], m["kern"], m["counts"]
         kept = int(sum(min(int(c), C) for c in counts))
         per_kernel = {}
@@ -549,8 +577,9 @@ def configs_bench(smx, torch, stream, steps: int, warmup: int, cpu: bool, names)
         ffn_tflops = 4.0 * kept * d * f / (ffn_ms * 1e-3) / 1e12 if ffn_ms else 0.0
         peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS
         rec = {"workload": (f"{T} tokens, d_model {d}, d_ff {f}, {N} experts, capacity factor "
-                            f"{cfg.capacity_factor} (capacity {C}), {cfg.dtype} activations and expert weights, "
-                            f"fp32 router" + (f", Zipf({cfg.zipf_s}) router bias" if cfg.zipf_s else "")),
+                            f"{cfg.capacity_factor} (capacity {C}), {cfg.dtype} activations and expert weights"
+                            + (" (tiled layout)" if tiled else "") + ", fp32 router"
+                            + (f", Zipf({cfg.zipf_s}) router bias" if cfg.zipf_s else "")),
                "ms_per_step": round(m["ms_cold"], 4), "tokens_per_s": round(T / (m["ms_cold"] * 1e-3), 1),
                "ms_per_step_back_to_back": round(m["ms_warm"], 4),
                "tokens_per_s_back_to_back": round(T / (m["ms_warm"] * 1e-3), 1),
@@ -581,6 +610,9 @@ def main() -> int:
                          "configs")
     ap.add_argument("--configs", default="tiny,large,xxl,many",
                     help="workloads of the configs section")
+    ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
+                    help="expert weight layout of the timed forward calls (bf16): tiled (converted once before "
+                         "timing) or row-major")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -604,9 +636,22 @@ def main() -> int:
     # the layer runs on a stream of its own (the legacy default stream
     # synchronises with every other stream at each launch)
     stream = torch.cuda.Stream(device=dev)
-    m = measure_layer(smx, torch, cfg, inp, stream, args.steps, args.warmup)
+    # the expert weights in the layout the forward calls read: tiled (a copy
+    # converted once, before any timing: the parameters' storage format) or
+    # row-major; the backward reads row-major weights
+    tiled = args.weights == "tiled" and cfg.dtype == "bf16"
+    wts = (smx.tile_weights(inp["w_in"]), smx.tile_weights(inp["w_out"])) if tiled else (inp["w_in"], inp["w_out"])
+    torch.cuda.synchronize()
+    m = measure_layer(smx, torch, cfg, inp, stream, args.steps, args.warmup, weights=wts, tiled=tiled)
     C, shape, ws, out, kern = m["C"], m["shape"], m["ws"], m["out"], m["kern"]
     ms, ms_cold, counts, drop_rate = m["ms_warm"], m["ms_cold"], m["counts"], m["drop_rate"]
+    rows_rec = None
+    if tiled:  # the same step on row-major weights
+        mr = measure_layer(smx, torch, cfg, inp, stream, args.steps, 0, kernels=False)
+        rows_rec = {"ms_per_step": round(mr["ms_cold"], 4), "tokens_per_s": round(T / (mr["ms_cold"] * 1e-3), 1),
+                    "ms_per_step_back_to_back": round(mr["ms_warm"], 4),
+                    "note": "switch_layer_forward with row-major expert weights, cold-cache step as the headline"}
+        del mr
 
     # the stage entry points' data-movement kernels on the same routing (not
     # on the layer path, which gathers and scatters inside the expert FFN):
@@ -685,10 +730,10 @@ def main() -> int:
     if "stages" in sections:
         nout = {k: torch.empty_like(v) for k, v in out.items()}
         ncall = lambda: smx.layer_forward_add_norm(inp["x"], inp["w_router"], inp["router_bias"],  # noqa: E731
-                                                   inp["w_in"], inp["w_out"], C, gamma, beta, 1e-6,
-                                                   workspace=ws, out=nout)
-        bcall = lambda: smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],  # noqa: E731
-                                          inp["w_out"], C, workspace=ws, out=nout)
+                                                   *wts, C, gamma, beta, 1e-6, workspace=ws, out=nout,
+                                                   tiled=tiled)
+        bcall = lambda: smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], *wts,  # noqa: E731
+                                          C, workspace=ws, out=nout, tiled=tiled)
         times = {}
         with torch.cuda.stream(stream):
             for name, fn in (("bare", bcall), ("add_norm", ncall), ("bare2", bcall), ("add_norm2", ncall)):
@@ -709,11 +754,11 @@ def main() -> int:
                     "note": "switch_layer_forward_add_norm vs switch_layer_forward, back to back, best of two runs"}
         log(f"bench: layer + Add & Normalize {norm_ms:.4f} ms, bare layer {bare_ms:.4f} ms")
         del nout
-    top2 = top2_bench(smx, torch, inp, cfg, stream, args.steps) if "top2" in sections else None
+    top2 = top2_bench(smx, torch, inp, cfg, stream, args.steps, wts, tiled) if "top2" in sections else None
     # backward pass of the same step (switch_layer_backward on the forward's
     # routing and saved workspace; dy ~ N(0, 1), d_aux = 0.01): whole-call
     # time, then each kernel bracketed by events as for the forward
-    diag = mfma_diag_bench(smx, torch, cfg, stream, args.steps) if "mfma_diag" in sections else None
+    diag = mfma_diag_bench(smx, torch, cfg, stream, args.steps, tiled) if "mfma_diag" in sections else None
     bwd = None
     if "backward" in sections:
         bwd = backward_bench(smx, torch, inp, out, ws, C, cfg, stream, args.steps)
@@ -750,9 +795,10 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) tokens, truncated-normal 0.1-scale weights; no dataset)",
         "config": {"workload": f"{cfg.name}: {T} tokens (32 seqs x 512), d_model {d}, d_ff {f}, {N} experts, "
                                f"capacity factor {cfg.capacity_factor} (capacity {C}), bf16 activations and "
-                               f"expert weights, fp32 router",
+                               f"expert weights" + (" (tiled layout)" if tiled else "") + ", fp32 router",
                    "tokens": T, "d_model": d, "d_ff": f, "num_experts": N, "capacity": C,
-                   "drop_rate": round(drop_rate, 5)},
+                   "drop_rate": round(drop_rate, 5),
+                   "weight_layout": "tiled" if tiled else "row-major"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(dom, source_digest(FFN_SRC[dom]))},
@@ -770,9 +816,11 @@ def main() -> int:
                    "the MALL; the 1.2 GB of expert weights cannot)"),
         "back_to_back": {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
                          "wall_s_timed": round(m["t_wall"], 4)},
+        "row_major_weights": rows_rec,
         "train_forward": None if train_ms is None else {
             "ms_per_step": round(train_ms, 4), "tokens_per_s": round(T / (train_ms * 1e-3), 1),
-            "note": "switch_layer_forward_train, back to back: the expert FFN as two products with H saved"},
+            "note": ("switch_layer_forward_train, back to back, row-major expert weights (those the backward "
+                     "reads): the expert FFN as two products with H saved")},
         "layer_add_norm": norm_rec,
         "configs": None,
     }
@@ -790,7 +838,7 @@ def main() -> int:
     else:
         res["cpu_baseline"] = None
     if "configs" in sections:
-        del inp, m, ws, out
+        del inp, m, ws, out, wts
         torch.cuda.empty_cache()
         res["configs"] = configs_bench(smx, torch, stream, args.steps, args.warmup, not args.no_cpu_baseline,
                                        [c for c in args.configs.split(",") if c and c != args.config])

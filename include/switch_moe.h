@@ -22,9 +22,10 @@
  *   allocates and frees nothing, keeps no state between calls and never
  *   blocks the host (but see debug mode below).  All work is enqueued on
  *   `stream` (a hipStream_t passed as void*; NULL = null stream).
- * - Layouts are dense row-major.  T tokens are the caller's [batch][seq]
- *   flattened in row-major order; that order is the "token order" that
- *   decides which tokens overflow an expert.
+ * - Layouts are dense row-major, except the expert weights W_in and W_out
+ *   when s->weight_layout is SWITCH_WEIGHTS_TILED (see below).  T tokens are
+ *   the caller's [batch][seq] flattened in row-major order; that order is
+ *   the "token order" that decides which tokens overflow an expert.
  * - Activation dtype (s->dtype) applies to x, W_in, W_out, dispatched,
  *   expert_out and y: SWITCH_F32 (float) or SWITCH_BF16 (bfloat16, stored as
  *   16-bit words).  The router (W_r, bias, logits, softmax, gate) is always
@@ -46,7 +47,9 @@
  *   aligned (dropped: any).
  * - Supported shapes: d_model and d_ff multiples of 64; 0 <= tokens <= 2^31-1;
  *   num_experts >= 1; capacity >= 0.  Shapes outside that give
- *   SWITCH_E_UNSUPPORTED.
+ *   SWITCH_E_UNSUPPORTED, and so does SWITCH_WEIGHTS_TILED with fp32; a
+ *   weight_layout other than the two values below gives SWITCH_E_INVALID.
+ *   Every call that reads W_in / W_out reads them in s->weight_layout.
  */
 #ifndef SWITCH_MOE_H
 #define SWITCH_MOE_H
@@ -66,13 +69,33 @@ extern "C" {
 
 enum { SWITCH_F32 = 0, SWITCH_BF16 = 1 };
 
+/* Storage of the expert weights W_in [N][d_ff][d_model] and W_out
+ * [N][d_model][d_ff].  Each expert matrix has R rows and K columns, K being
+ * the contraction dimension (d_model for W_in, d_ff for W_out).
+ *   SWITCH_WEIGHTS_ROWS   row-major: element (r, k) of matrix m at
+ *                         (m R + r) K + k.
+ *   SWITCH_WEIGHTS_TILED  bf16 only: 16-row x 32-column blocks in row-major
+ *                         block order, each block as 64 groups of 8
+ *                         consecutive columns, group g = 16 (k % 32 / 8) +
+ *                         r % 16; element (r, k) of matrix m at
+ *                           ((m R/16 + r/16) K/32 + k/32) 512 + g 8 + k % 8.
+ *                         This is the operand order of the matrix cores'
+ *                         16x16x32 bf16 product, so a wave reads a block of
+ *                         weights as one contiguous 1 KB piece; the layer is
+ *                         faster and its results are bit-identical to those of
+ *                         the row-major layout.  switch_tile_weights converts.
+ * The same byte count either way.  The layout is not checked: weights in the
+ * other layout than the one declared give wrong results, not an error. */
+enum { SWITCH_WEIGHTS_ROWS = 0, SWITCH_WEIGHTS_TILED = 1 };
+
 typedef struct switch_shape {
-  int64_t tokens;      /* T: tokens per batch (capacity equation)                      */
-  int32_t d_model;     /* d: token width                                               */
-  int32_t d_ff;        /* expert hidden width                                          */
-  int32_t num_experts; /* N                                                            */
-  int32_t capacity;    /* C: per-expert buffer rows, normally from switch_capacity()   */
-  int32_t dtype;       /* SWITCH_F32 or SWITCH_BF16 (activations and expert weights)   */
+  int64_t tokens;        /* T: tokens per batch (capacity equation)                      */
+  int32_t d_model;       /* d: token width                                               */
+  int32_t d_ff;          /* expert hidden width                                          */
+  int32_t num_experts;   /* N                                                            */
+  int32_t capacity;      /* C: per-expert buffer rows, normally from switch_capacity()   */
+  int32_t dtype;         /* SWITCH_F32 or SWITCH_BF16 (activations and expert weights)   */
+  int32_t weight_layout; /* SWITCH_WEIGHTS_ROWS (0) or SWITCH_WEIGHTS_TILED: W_in, W_out */
 } switch_shape;
 
 /* Expert capacity, "Expert Capacity and the Capacity Factor" (capacity
@@ -323,7 +346,10 @@ int switch_topk_layer_forward(const switch_shape *s, int32_t top_k, const void *
  * result); dx summed in fp32 and rounded once.  Deterministic.
  * workspace: switch_backward_workspace_bytes bytes (256-byte aligned).
  * Errors: as switch_layer_forward; SWITCH_E_WORKSPACE if fwd_workspace_bytes
- * is below the forward's workspace size. */
+ * is below the forward's workspace size; SWITCH_E_UNSUPPORTED for
+ * s->weight_layout = SWITCH_WEIGHTS_TILED (the backward reads, and writes
+ * dw_in / dw_out, row-major: keep a row-major copy of the weights for
+ * training, or convert with switch_untile_weights). */
 int switch_backward_workspace_bytes(const switch_shape *s, size_t *bytes_out);
 int switch_layer_backward(const switch_shape *s, const void *x, const float *w_router, const float *router_bias,
                           const void *w_in, const void *w_out, int32_t add_residual, const int32_t *expert_idx,
@@ -383,6 +409,23 @@ int switch_layer_forward_profiled(const switch_shape *s, const void *x, const fl
  * "assign_apply", then "ffn_up", "ffn_down").  Up to max_names are stored in
  * names[]; *num_names receives their number (at most 5).  Host only. */
 int switch_launch_names(const switch_shape *s, const char **names, int32_t max_names, int32_t *num_names);
+
+/* Expert weights between the two layouts of SWITCH_WEIGHTS_ROWS and
+ * SWITCH_WEIGHTS_TILED (defined at switch_shape): count bf16 matrices of
+ * rows x cols (W_in: count = N, rows = d_ff, cols = d_model; W_out: rows =
+ * d_model, cols = d_ff), src -> dst, device pointers, 16-byte aligned, not
+ * overlapping, count * rows * cols * 2 bytes each.  A pure permutation of
+ * 16-byte pieces: untile(tile(w)) == w bit for bit.  A conversion of the
+ * parameters (after loading or updating them), not part of a layer call:
+ * the layer with tiled weights computes the same products in the same order
+ * as with row-major ones ("The Core Idea: Sparse Activation via Routing":
+ * each expert is an ordinary FFN; only its storage changes).  Enqueued on
+ * `stream`.
+ * Errors: SWITCH_E_INVALID (negative sizes, NULL / misaligned / overlapping
+ * pointers when there is anything to move), SWITCH_E_UNSUPPORTED (rows not a
+ * multiple of 16 or cols of 32, sizes overflowing), SWITCH_E_HIP. */
+int switch_tile_weights(int32_t count, int32_t rows, int32_t cols, const void *src, void *dst, void *stream);
+int switch_untile_weights(int32_t count, int32_t rows, int32_t cols, const void *src, void *dst, void *stream);
 
 #ifdef __cplusplus
 }

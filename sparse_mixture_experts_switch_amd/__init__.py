@@ -31,7 +31,9 @@ from .binding import (  # noqa: F401
     noalloc_scratch_bytes,
     route,
     route_dispatch,
+    tile_weights,
     topk_layer_forward,
     topk_workspace_bytes,
+    untile_weights,
     workspace_bytes,
 )

@@ -35,6 +35,7 @@ EXPORTED = [
     "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
     "switch_combine_add_norm", "switch_route_dispatch", "switch_layer_forward_noalloc",
     "switch_noalloc_scratch_bytes", "switch_layer_forward_train", "switch_layer_forward_add_norm",
+    "switch_tile_weights", "switch_untile_weights",
 ]
 BACKWARD_KERNELS = ["bwd_dz", "bwd_dw_out", "bwd_dx", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
                     "bwd_router_w_sum"]
@@ -50,6 +51,7 @@ class Shape(ctypes.Structure):
     _fields_ = [
         ("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
         ("num_experts", ctypes.c_int32), ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -94,6 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         [sp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8 + [sz, _P])
     lib.switch_layer_forward_noalloc.argtypes = [sp, _P, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 7 + [_P]
     lib.switch_noalloc_scratch_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
+    lib.switch_tile_weights.argtypes = [ctypes.c_int32] * 3 + [_P] * 3
+    lib.switch_untile_weights.argtypes = lib.switch_tile_weights.argtypes
     for name in EXPORTED:
         if name != "switch_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -192,8 +196,15 @@ def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def make_shape(tokens: int, d_model: int, d_ff: int, num_experts: int, capacity_: int, dtype: torch.dtype) -> Shape:
-    return Shape(tokens, d_model, d_ff, num_experts, capacity_, _dtype_code(dtype))
+WEIGHTS_ROWS, WEIGHTS_TILED = 0, 1
+
+
+def make_shape(tokens: int, d_model: int, d_ff: int, num_experts: int, capacity_: int, dtype: torch.dtype,
+               tiled: bool = False) -> Shape:
+    """The call's shape; tiled declares W_in / W_out in the tiled layout
+    (tile_weights), else row-major."""
+    return Shape(tokens, d_model, d_ff, num_experts, capacity_, _dtype_code(dtype),
+                 WEIGHTS_TILED if tiled else WEIGHTS_ROWS)
 
 
 def capacity(tokens: int, num_experts: int, capacity_factor: float) -> int:
@@ -294,7 +305,8 @@ def dispatch(x: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tensor, drop
 
 
 def expert_ffn(dispatched: torch.Tensor, expert_count: torch.Tensor, w_in: torch.Tensor, w_out: torch.Tensor,
-               workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+               workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               tiled: bool = False) -> torch.Tensor:
     """expert_out[i][r] = W_out,i ReLU(W_in,i dispatched[i][r]) (switch_expert_ffn)."""
     if not isinstance(dispatched, torch.Tensor) or dispatched.dim() != 3:
         raise ValueError("dispatched must be a 3-D tensor [num_experts][capacity][d_model]")
@@ -302,7 +314,7 @@ def expert_ffn(dispatched: torch.Tensor, expert_count: torch.Tensor, w_in: torch
     dev = _check_acts(dispatched.reshape(N * C, d), "dispatched")
     _expect(expert_count, "expert_count", (N,), torch.int32, dev)
     _check_experts(w_in, w_out, N, d, dispatched.dtype, dev)
-    shape = make_shape(0, d, w_in.shape[1], N, C, dispatched.dtype)
+    shape = make_shape(0, d, w_in.shape[1], N, C, dispatched.dtype, tiled)
     eo = out if out is not None else torch.empty_like(dispatched)
     _expect(eo, "out", (N, C, d), dispatched.dtype, dev)
     ws = workspace
@@ -338,11 +350,11 @@ def combine(expert_out: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tens
     return y
 
 
-def _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out):
+def _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out, tiled=False):
     _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
     T, d = x.shape
     N, f = w_in.shape[0], w_in.shape[1]
-    shape = make_shape(T, d, f, N, capacity_, x.dtype)
+    shape = make_shape(T, d, f, N, capacity_, x.dtype, tiled)
     dev = x.device
     o = out if out is not None else _route_outputs(T, N, dev)
     if "y" not in o:
@@ -358,20 +370,22 @@ def _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, wor
 
 def layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None, w_in: torch.Tensor,
                   w_out: torch.Tensor, capacity_: int, add_residual: bool = False,
-                  workspace: torch.Tensor | None = None, out: dict | None = None) -> dict:
-    """The whole Switch layer forward (switch_layer_forward)."""
-    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
+                  workspace: torch.Tensor | None = None, out: dict | None = None, tiled: bool = False) -> dict:
+    """The whole Switch layer forward (switch_layer_forward); tiled: W_in and
+    W_out are in the tiled layout (tile_weights)."""
+    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out, tiled)
     _check(load_library().switch_layer_forward(*args))
     return o
 
 
 def layer_forward_train(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None,
                         w_in: torch.Tensor, w_out: torch.Tensor, capacity_: int, add_residual: bool = False,
-                        workspace: torch.Tensor | None = None, out: dict | None = None) -> dict:
+                        workspace: torch.Tensor | None = None, out: dict | None = None,
+                        tiled: bool = False) -> dict:
     """The layer forward of a training step (switch_layer_forward_train): the
     results of layer_forward, and `workspace` then holds the hidden
     activations that layer_backward reads."""
-    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
+    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out, tiled)
     _check(load_library().switch_layer_forward_train(*args))
     return o
 
@@ -379,11 +393,11 @@ def layer_forward_train(x: torch.Tensor, w_router: torch.Tensor, router_bias: to
 def layer_forward_add_norm(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None,
                            w_in: torch.Tensor, w_out: torch.Tensor, capacity_: int, gamma: torch.Tensor,
                            beta: torch.Tensor, eps: float, workspace: torch.Tensor | None = None,
-                           out: dict | None = None) -> dict:
+                           out: dict | None = None, tiled: bool = False) -> dict:
     """The layer and the block's Add + Normalize in one call
     (switch_layer_forward_add_norm): o["y"] holds LayerNorm(x + y_bare) *
     gamma + beta."""
-    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, False, workspace, out)
+    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, False, workspace, out, tiled)
     d = x.shape[1]
     _expect(gamma, "gamma", (d,), torch.float32, x.device)
     _expect(beta, "beta", (d,), torch.float32, x.device)
@@ -394,10 +408,10 @@ def layer_forward_add_norm(x: torch.Tensor, w_router: torch.Tensor, router_bias:
 
 
 def layer_forward_profiled(x, w_router, router_bias, w_in, w_out, capacity_, first_kernel: int, last_kernel: int,
-                           times: int = 1, add_residual=False, workspace=None, out=None) -> dict:
+                           times: int = 1, add_residual=False, workspace=None, out=None, tiled=False) -> dict:
     """Kernels first_kernel..last_kernel of layer_forward only, each launched
     `times` times back to back (switch_layer_forward_profiled); asynchronous."""
-    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out)
+    _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out, tiled)
     _check(load_library().switch_layer_forward_profiled(*args, int(first_kernel), int(last_kernel), int(times)))
     return o
 
@@ -411,7 +425,7 @@ def noalloc_scratch_bytes() -> int:
 
 def layer_forward_noalloc(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None,
                           w_in: torch.Tensor, w_out: torch.Tensor, capacity_: int, add_residual: bool = False,
-                          out: dict | None = None) -> dict:
+                          out: dict | None = None, tiled: bool = False) -> dict:
     """The layer forward on the library's static workspace
     (switch_layer_forward_noalloc): no device memory is allocated by the call.
     `out` holds the output tensors (expert_idx, gate, slot, dropped,
@@ -419,7 +433,7 @@ def layer_forward_noalloc(x: torch.Tensor, w_router: torch.Tensor, router_bias: 
     the caller's side, before the call."""
     T, d = x.shape
     N, f = w_in.shape[0], w_in.shape[1]
-    shape = make_shape(T, d, f, N, capacity_, x.dtype)
+    shape = make_shape(T, d, f, N, capacity_, x.dtype, tiled)
     dev = x.device
     _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
     o = out if out is not None else _route_outputs(T, N, dev)
@@ -461,13 +475,13 @@ def topk_workspace_bytes(shape: Shape, top_k: int) -> int:
 def topk_layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None,
                        w_in: torch.Tensor, w_out: torch.Tensor, capacity_: int, top_k: int,
                        add_residual: bool = False, workspace: torch.Tensor | None = None,
-                       out: dict | None = None) -> dict:
+                       out: dict | None = None, tiled: bool = False) -> dict:
     """Classic top-k MoE layer, k = 1 or 2 (switch_topk_layer_forward); the
     routing outputs are [top_k][T]."""
     _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
     T, d = x.shape
     N, f = w_in.shape[0], w_in.shape[1]
-    shape = make_shape(T, d, f, N, capacity_, x.dtype)
+    shape = make_shape(T, d, f, N, capacity_, x.dtype, tiled)
     dev = x.device
     o = out if out is not None else _route_outputs(T, N, dev, top_k)
     if "y" not in o:
@@ -483,6 +497,32 @@ def topk_layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: tor
         1 if add_residual else 0, _ptr(o["y"]), _ptr(o["expert_idx"]), _ptr(o["gate"]), _ptr(o["slot"]),
         _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]), _ptr(ws), ws.numel(), _stream(dev)))
     return o
+
+
+def _tile_call(fn, w: torch.Tensor, out: torch.Tensor | None) -> torch.Tensor:
+    if not isinstance(w, torch.Tensor) or w.dim() != 3 or w.dtype != torch.bfloat16:
+        raise ValueError("expert weights must be a 3-D bfloat16 tensor [count][rows][cols]")
+    if not w.is_contiguous():
+        raise ValueError("expert weights must be contiguous")
+    dev = w.device
+    o = out if out is not None else torch.empty_like(w)
+    _expect(o, "out", tuple(w.shape), torch.bfloat16, dev)
+    cnt, rows, cols = w.shape
+    _check(fn(int(cnt), int(rows), int(cols), _ptr(w), _ptr(o), _stream(dev)))
+    return o
+
+
+def tile_weights(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major expert weights [count][rows][cols] (W_in [N][d_ff][d_model]
+    or W_out [N][d_model][d_ff], bf16) -> the tiled layout that the layer
+    calls read with tiled=True (switch_tile_weights).  Same shape and dtype;
+    asynchronous on the current stream."""
+    return _tile_call(load_library().switch_tile_weights, w, out)
+
+
+def untile_weights(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Tiled expert weights -> row-major (switch_untile_weights)."""
+    return _tile_call(load_library().switch_untile_weights, w, out)
 
 
 def backward_workspace_bytes(shape: Shape) -> int:

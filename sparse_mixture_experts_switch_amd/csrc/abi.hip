@@ -138,8 +138,14 @@ int check_shape(const switch_shape *s) {
     return fail(SWITCH_E_UNSUPPORTED, "tokens = %lld above 2^31-1", (long long)s->tokens);
   if (s->d_model % 64 || s->d_ff % 64)
     return fail(SWITCH_E_UNSUPPORTED, "d_model = %d and d_ff = %d must be multiples of 64", s->d_model, s->d_ff);
+  if (s->weight_layout != SWITCH_WEIGHTS_ROWS && s->weight_layout != SWITCH_WEIGHTS_TILED)
+    return fail(SWITCH_E_INVALID, "weight_layout = %d", s->weight_layout);
+  if (s->weight_layout == SWITCH_WEIGHTS_TILED && s->dtype != SWITCH_BF16)
+    return fail(SWITCH_E_UNSUPPORTED, "tiled expert weights are bf16 only");
   return SWITCH_OK;
 }
+
+bool tiled(const switch_shape *s) { return s->weight_layout == SWITCH_WEIGHTS_TILED; }
 
 // Workspace of a call with k routes per token: the router's per-block
 // partials (k blocks per router block), the route ranks, the logits rows when
@@ -405,6 +411,7 @@ int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *
     FusedFfnCall fc{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w_out, routed,
                     expert_count, maps.tok, k == 1 ? nullptr : maps.rows, maps.gmap,
                     k == 1 ? (norm_fused ? x : xres) : nullptr};
+    fc.tiled = tiled(s);
     if (norm_fused) {
       fc.gamma = norm->gamma;
       fc.beta = norm->beta;
@@ -415,12 +422,13 @@ int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *
     tm.mark("ffn");
   } else {
   GemmCall up{s->dtype, s->num_experts, s->capacity, s->d_model, s->d_ff, x, w_in, w + L.lf_hidden,
-              expert_count, maps.tok, nullptr, nullptr, nullptr};
+              expert_count, maps.tok, nullptr, nullptr, nullptr, tiled(s)};
   for (int r = tm.reps(); r > 0; --r)
     if ((e = launch_ffn_up_gather(up, st)) != hipSuccess) return hip_fail(e, "ffn_up launch");
   tm.mark("ffn_up");
   GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, routed,
-                expert_count, k == 1 ? maps.tok : maps.rows, gate, maps.gmap, k == 1 && !norm ? xres : nullptr};
+                expert_count, k == 1 ? maps.tok : maps.rows, gate, maps.gmap, k == 1 && !norm ? xres : nullptr,
+                tiled(s)};
   for (int r = tm.reps(); r > 0; --r)
     if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
   tm.mark("ffn_down");
@@ -496,6 +504,7 @@ int layer_backward(const switch_shape *s, const void *x, const float *w_router, 
                    void *dw_out, void *ws, size_t ws_bytes, void *stream, Timer &tm) {
   int rc = check_shape(s);
   if (rc) return rc;
+  if (tiled(s)) return fail(SWITCH_E_UNSUPPORTED, "the backward reads row-major expert weights");
   if (!std::isfinite(d_aux)) return fail(SWITCH_E_INVALID, "d_aux = %g is not finite", d_aux);
   Layout L;
   if ((rc = layout(s, L))) return rc;
@@ -541,6 +550,25 @@ int layer_backward(const switch_shape *s, const void *x, const float *w_router, 
                    w + B.bplanes, B.kp};
   if ((e = launch_router_bwd(ra, st, marks)) != hipSuccess) return hip_fail(e, "backward router launch");
   return SWITCH_OK;
+}
+
+// Between the two expert weight layouts (tile.hip); both directions share
+// the checks.
+int tile_call(int32_t count, int32_t rows, int32_t cols, const void *src, void *dst, void *stream,
+              bool to_tiled) {
+  if (count < 0 || rows < 0 || cols < 0)
+    return fail(SWITCH_E_INVALID, "count = %d, rows = %d, cols = %d must be >= 0", count, rows, cols);
+  if (rows % 16 || cols % 32)
+    return fail(SWITCH_E_UNSUPPORTED, "rows = %d must be a multiple of 16 and cols = %d of 32", rows, cols);
+  size_t bytes;
+  if (!mul(bytes, {count, rows, cols, 2})) return fail(SWITCH_E_UNSUPPORTED, "matrix sizes overflow");
+  if (bytes == 0) return SWITCH_OK;
+  NEED(src, 16);
+  NEED(dst, 16);
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return fail(SWITCH_E_INVALID, "src and dst overlap");
+  TileArgs t{count, rows, cols, src, dst, to_tiled};
+  return launched(launch_tile_weights(t, (hipStream_t)stream), to_tiled ? "tile launch" : "untile launch", stream);
 }
 
 }  // namespace
@@ -688,7 +716,7 @@ int switch_expert_ffn(const switch_shape *s, const void *dispatched, const int32
     }
     if ((rc = check_ws(ws, ws_bytes, L.ffn_end))) return rc;
     FfnArgs a{s->dtype, s->d_model, s->d_ff, s->num_experts, s->capacity, dispatched, expert_count,
-              w_in, w_out, (char *)ws + L.ffn_hidden, expert_out};
+              w_in, w_out, (char *)ws + L.ffn_hidden, expert_out, tiled(s)};
     if ((rc = launched(launch_ffn_up(a, (hipStream_t)stream), "ffn_up launch", stream))) return rc;
     return launched(launch_ffn_down(a, (hipStream_t)stream), "ffn_down launch", stream);
   })
@@ -936,6 +964,14 @@ int switch_layer_backward_profiled(const switch_shape *s, const void *x, const f
                   tm.n);
     return rc;
   })
+}
+
+int switch_tile_weights(int32_t count, int32_t rows, int32_t cols, const void *src, void *dst, void *stream) {
+  GUARD({ return tile_call(count, rows, cols, src, dst, stream, true); })
+}
+
+int switch_untile_weights(int32_t count, int32_t rows, int32_t cols, const void *src, void *dst, void *stream) {
+  GUARD({ return tile_call(count, rows, cols, src, dst, stream, false); })
 }
 
 int switch_launch_names(const switch_shape *s, const char **names, int32_t max_names, int32_t *num_names) {

@@ -92,7 +92,12 @@ __device__ __forceinline__ int xcd_tile(int b, int grid) {
 // per workgroup (kCols = WAVES * 16 * NBW).  Operand layout: lane l supplies
 // row (l % 16) and 8 consecutive k starting at 8 * (l / 16); result lane l
 // holds column (l % 16), rows 4 * (l / 16) + i.
-template <int MB, int NBW, int WAVES, bool kGather, int kEpi, bool kSkipDead = true>
+//
+// kTiled: the weights are stored in that operand order (16-row x 32-column
+// blocks, each 64 lanes x 16 bytes), so a wave's weight load of one block
+// is one contiguous 1 KB piece; row-major weights make every load touch 16
+// rows, which costs the vector memory path several times the cycles.
+template <int MB, int NBW, int WAVES, bool kGather, int kEpi, bool kTiled, bool kSkipDead = true>
 __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArgs<bf16> p) {
   constexpr int kThreads = WAVES * 64;
   constexpr int kRows = MB * 16;
@@ -186,10 +191,17 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
     }
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
-      const int n = min(t.n0 + wave * NBW * 16 + nb * 16 + r16, Nout - 1);
-      const bf16 *bp = p.B + ((int64_t)t.e * Nout + n) * K + kq + k0;
+      if (kTiled) {
+        const int blk = min((t.n0 + wave * NBW * 16 + nb * 16) / 16, Nout / 16 - 1);
+        const bf16 *bp = p.B + (((int64_t)t.e * (Nout / 16) + blk) * (K / 32) + k0 / 32) * 512 + lane * 8;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) breg[slot][s][nb] = *(const u32x4 *)(bp + s * 32);
+        for (int s = 0; s < 2; ++s) breg[slot][s][nb] = *(const u32x4 *)(bp + s * 512);
+      } else {
+        const int n = min(t.n0 + wave * NBW * 16 + nb * 16 + r16, Nout - 1);
+        const bf16 *bp = p.B + ((int64_t)t.e * Nout + n) * K + kq + k0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) breg[slot][s][nb] = *(const u32x4 *)(bp + s * 32);
+      }
     }
   };
   auto store_a = [&](int slot, int buf) {
@@ -448,11 +460,12 @@ inline unsigned grid_of(int ntiles) { return (unsigned)(ceil_div(ntiles, 8) * 8)
 // that spreads the output features more evenly over the CUs.
 constexpr int kWaves = 8;
 
-// Resident workgroups for a persistent launch: CUs x workgroups per CU (the
-// occupancy of each kernel queried once per device).
+// Resident workgroups for a persistent launch: CUs x workgroups per CU.  The
+// occupancy is queried once per device and kernel: occ_cache belongs to the
+// calling instantiation (all the kernels share one function type, so a
+// static here would be shared by every tile shape).
 template <typename Kern>
-unsigned persistent_grid(Kern kern, int ntiles) {
-  static std::atomic<int> occ_cache[kMaxDeviceCache];
+unsigned persistent_grid(Kern kern, int ntiles, std::atomic<int> (&occ_cache)[kMaxDeviceCache]) {
   const int cus = device_cus();
   int dev = 0, occ = 0;
   const bool cached = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDeviceCache;
@@ -465,12 +478,18 @@ unsigned persistent_grid(Kern kern, int ntiles) {
   return (unsigned)std::max<int64_t>(8, ceil_div(want, 8) * 8);
 }
 
+template <int MB, int NBW, bool kGather, int kEpi, bool kTiled>
+hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
+  static std::atomic<int> occ[kMaxDeviceCache];
+  auto g = make_args<bf16>(c, MB * 16, kWaves * 16 * NBW);
+  auto kern = ffn_gemm_bf16_kernel<MB, NBW, kWaves, kGather, kEpi, kTiled>;
+  kern<<<dim3(persistent_grid(kern, g.ntiles, occ)), dim3(kWaves * 64), 0, st>>>(g);
+  return hipGetLastError();
+}
+
 template <int MB, int NBW, bool kGather, int kEpi>
 hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
-  auto g = make_args<bf16>(c, MB * 16, kWaves * 16 * NBW);
-  auto kern = ffn_gemm_bf16_kernel<MB, NBW, kWaves, kGather, kEpi>;
-  kern<<<dim3(persistent_grid(kern, g.ntiles)), dim3(kWaves * 64), 0, st>>>(g);
-  return hipGetLastError();
+  return c.tiled ? run_bf16<MB, NBW, kGather, kEpi, true>(c, st) : run_bf16<MB, NBW, kGather, kEpi, false>(c, st);
 }
 
 // Column blocks per wave.  Both widths stream every weight byte once and run
@@ -517,13 +536,13 @@ hipError_t gemm(const GemmCall &c, hipStream_t st) {
 // Stage call: dispatched buffer -> H -> expert_out buffer.
 hipError_t launch_ffn_up(const FfnArgs &a, hipStream_t st) {
   GemmCall c{a.dtype, a.N, a.C, a.d, a.dff, a.dispatched, a.w_in, a.hidden, a.expert_count,
-             nullptr, nullptr, nullptr, nullptr};
+             nullptr, nullptr, nullptr, nullptr, a.tiled};
   return gemm<false, kEpiRelu>(c, st);
 }
 
 hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st) {
   GemmCall c{a.dtype, a.N, a.C, a.dff, a.d, a.hidden, a.w_out, a.expert_out, a.expert_count,
-             nullptr, nullptr, nullptr, nullptr};
+             nullptr, nullptr, nullptr, nullptr, a.tiled};
   return gemm<false, kEpiPlain>(c, st);
 }
 

@@ -71,6 +71,7 @@ struct FusedArgs {
   const float *gamma, *beta;  // Add + Normalize epilogue (with xres = x)
   float eps;
   int C, f, m_tiles, ntiles;
+  bool tiled;           // w_in / w_out in MFMA operand order (16 x 32 blocks of 64 lanes x 16 bytes)
 };
 
 // LDS-only barrier: waits for this wave's LDS operations, not for its
@@ -84,7 +85,7 @@ __device__ __forceinline__ void fz_pin() { __builtin_amdgcn_sched_barrier(0); }
 // Each of the four waves computes CB = 2 column blocks of 16 of the chunk's H.
 constexpr int kFzWaves = 4;
 
-template <int MB, int NB, int RING, bool kNorm>
+template <int MB, int NB, int RING, bool kNorm, bool kTiled>
 __global__ __launch_bounds__(kFzWaves * 64) void ffn_fused_bf16_kernel(const FusedArgs p) {
   constexpr int CB = kFzChunk / 16 / kFzWaves;
   constexpr int D = NB * 16 * kFzWaves;     // d_model
@@ -129,17 +130,23 @@ __global__ __launch_bounds__(kFzWaves * 64) void ffn_fused_bf16_kernel(const Fus
   //   columns 32 s + kq
   // down, load (ks, nb) of chunk c: W_out row e*D + wave*NB*16 + nb*16 + r16,
   //   columns c*128 + 32 ks + kq
-  const bf16 *win = p.w_in + ((int64_t)e * f + 16 * CB * wave + r16) * D + kq;
-  const bf16 *wout = p.w_out + ((int64_t)e * D + wave * NB * 16 + r16) * f + kq;
+  // (tiled weights: the same operands as whole 1 KB blocks, block
+  // (row / 16, column / 32) of the expert's matrix)
+  const bf16 *win = kTiled ? p.w_in + ((int64_t)e * (f / 16) + CB * wave) * (D / 32) * 512 + lane * 8
+                           : p.w_in + ((int64_t)e * f + 16 * CB * wave + r16) * D + kq;
+  const bf16 *wout = kTiled ? p.w_out + ((int64_t)e * (D / 16) + wave * NB) * (f / 32) * 512 + lane * 8
+                            : p.w_out + ((int64_t)e * D + wave * NB * 16 + r16) * f + kq;
   u32x4 ring[RING];
   auto load = [&](int i, int c) {  // load i (compile-time after unrolling) of chunk c
     const int cc = min(c, nch - 1);  // past the last chunk: re-read it (never consumed)
     if (i < LU) {
       const int s = i / CB, cb = i % CB;
-      ring[i % RING] = *(const u32x4 *)(win + ((int64_t)cc * kFzChunk + 16 * cb) * D + 32 * s);
+      ring[i % RING] = kTiled ? *(const u32x4 *)(win + ((int64_t)(cc * (kFzChunk / 16) + cb) * (D / 32) + s) * 512)
+                              : *(const u32x4 *)(win + ((int64_t)cc * kFzChunk + 16 * cb) * D + 32 * s);
     } else {
       const int u = i - LU, ks = u / NB, nb = u % NB;
-      ring[i % RING] = *(const u32x4 *)(wout + (int64_t)nb * 16 * f + cc * kFzChunk + 32 * ks);
+      ring[i % RING] = kTiled ? *(const u32x4 *)(wout + ((int64_t)nb * (f / 32) + cc * (kFzChunk / 32) + ks) * 512)
+                              : *(const u32x4 *)(wout + (int64_t)nb * 16 * f + cc * kFzChunk + 32 * ks);
     }
   };
   // issue the load RING places ahead of load i of chunk c
@@ -379,10 +386,11 @@ hipError_t run_fused(const FusedArgs &a, hipStream_t st) {
   constexpr int L = 2 * (D / 32) + 4 * NB;                // weight loads per chunk per wave
   constexpr int RING = L % 32 == 0 ? 32 : (L % 16 == 0 ? 16 : 8);
   const unsigned grid = (unsigned)(ceil_div(a.ntiles, 8) * 8);
-  if (a.gamma)
-    ffn_fused_bf16_kernel<MB, NB, RING, true><<<dim3(grid), dim3(kFzWaves * 64), 0, st>>>(a);
-  else
-    ffn_fused_bf16_kernel<MB, NB, RING, false><<<dim3(grid), dim3(kFzWaves * 64), 0, st>>>(a);
+  auto kern = a.gamma ? (a.tiled ? ffn_fused_bf16_kernel<MB, NB, RING, true, true>
+                                 : ffn_fused_bf16_kernel<MB, NB, RING, true, false>)
+                      : (a.tiled ? ffn_fused_bf16_kernel<MB, NB, RING, false, true>
+                                 : ffn_fused_bf16_kernel<MB, NB, RING, false, false>);
+  kern<<<dim3(grid), dim3(kFzWaves * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -414,7 +422,7 @@ hipError_t launch_ffn_fused(const FusedFfnCall &c, hipStream_t st) {
   if (c.gamma && (c.rows || !c.xres)) return hipErrorInvalidValue;  // normalization: one route per token, x given
   FusedArgs a{(const bf16 *)c.x, (const bf16 *)c.w_in, (const bf16 *)c.w_out, (bf16 *)c.out, c.counts, c.tok,
               c.rows, c.gmap, (const bf16 *)c.xres, c.gamma, c.beta, c.eps, c.C, c.dff,
-              (int)ceil_div(c.C, mb * 16), 0};
+              (int)ceil_div(c.C, mb * 16), 0, c.tiled};
   a.ntiles = c.N * a.m_tiles;
   return c.d == 128 ? run_fused_mb<128>(a, mb, st) : run_fused_mb<256>(a, mb, st);
 }

@@ -59,6 +59,7 @@ struct FfnArgs {
   const void *w_out;  // [N][d][dff]
   void *hidden;       // [N][C][dff] scratch
   void *expert_out;   // [N][C][d]
+  bool tiled = false; // weights in MFMA operand order (bf16), see tile_weights
 };
 
 struct CombineArgs {
@@ -104,6 +105,7 @@ struct GemmCall {
   const float *gate;   // [T] (combine, fp32 path)
   const float *gmap;   // [N][C]: gate of the token in each live slot (combine)
   const void *xres;    // [T][Nout] residual rows (combine), may be null
+  bool tiled = false;  // B in MFMA operand order (bf16), see tile_weights
 };
 
 // Compute units of the current device, queried once per device (256 when the
@@ -173,6 +175,18 @@ struct TopkSumArgs {
   void *y;
 };
 hipError_t launch_topk_sum(const TopkSumArgs &a, hipStream_t st);
+// Expert weights [count][rows][cols] bf16 between row-major and the tiled
+// layout (to_tiled) or back: element (r, c) of matrix m sits at
+//   ((m (rows/16) + r/16) (cols/32) + c/32) 512 + (16 ((c % 32)/8) + r % 16) 8 + c % 8.
+// rows % 16 == 0, cols % 32 == 0; src and dst do not overlap.
+struct TileArgs {
+  int64_t count;
+  int rows, cols;
+  const void *src;
+  void *dst;
+  bool to_tiled;
+};
+hipError_t launch_tile_weights(const TileArgs &a, hipStream_t st);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t st);
 hipError_t launch_ffn_up(const FfnArgs &a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs &a, hipStream_t st);
@@ -194,6 +208,7 @@ struct FusedFfnCall {
   // set (k = 1, xres = x): write the block's Add + Normalize of x + y instead of y
   const float *gamma = nullptr, *beta = nullptr;
   float eps = 0.f;
+  bool tiled = false;      // w_in / w_out in MFMA operand order, see tile_weights
 };
 bool ffn_fused_eligible(int dtype, int d, int dff, int C);
 hipError_t launch_ffn_fused(const FusedFfnCall &c, hipStream_t st);

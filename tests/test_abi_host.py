@@ -86,7 +86,8 @@ def test_workspace_bytes_layout():
     ("tokens", -1, B.SWITCH_E_INVALID), ("d_model", 0, B.SWITCH_E_INVALID), ("d_ff", -64, B.SWITCH_E_INVALID),
     ("num_experts", 0, B.SWITCH_E_INVALID), ("capacity", -1, B.SWITCH_E_INVALID), ("dtype", 7, B.SWITCH_E_INVALID),
     ("d_model", 96, B.SWITCH_E_UNSUPPORTED), ("d_ff", 100, B.SWITCH_E_UNSUPPORTED),
-    ("tokens", 2 ** 31, B.SWITCH_E_UNSUPPORTED),
+    ("tokens", 2 ** 31, B.SWITCH_E_UNSUPPORTED), ("weight_layout", 2, B.SWITCH_E_INVALID),
+    ("weight_layout", -1, B.SWITCH_E_INVALID), ("weight_layout", B.WEIGHTS_TILED, B.SWITCH_OK),
 ])
 def test_shape_validation(field, value, code):
     import torch
@@ -160,6 +161,35 @@ def test_entry_points_reject_before_launch():
         rc = lib.switch_layer_forward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good,
                                                good, good, good, good, good, 1 << 30, None, first, last, times)
         assert rc == B.SWITCH_E_INVALID
+
+
+def test_tiled_weights_validation():
+    """The tiled expert-weight layout: bf16 only, and the conversion calls
+    check sizes, pointers and overlap on the host; an empty conversion is a
+    no-op that needs no pointers."""
+    import torch
+    lib = smx.load_library()
+    out = ctypes.c_size_t()
+    s = B.make_shape(1024, 128, 256, 8, 128, torch.float32, tiled=True)
+    assert lib.switch_workspace_bytes(ctypes.byref(s), ctypes.byref(out)) == B.SWITCH_E_UNSUPPORTED
+    assert b"bf16" in lib.switch_last_error()
+    P = ctypes.c_void_p
+    good, other, odd = P(1 << 20), P(1 << 30), P((1 << 20) + 8)
+    for fn in (lib.switch_tile_weights, lib.switch_untile_weights):
+        assert fn(-1, 64, 128, good, other, None) == B.SWITCH_E_INVALID
+        assert fn(2, 24, 128, good, other, None) == B.SWITCH_E_UNSUPPORTED  # rows % 16
+        assert fn(2, 64, 48, good, other, None) == B.SWITCH_E_UNSUPPORTED   # cols % 32
+        assert fn(2, 64, 128, None, other, None) == B.SWITCH_E_INVALID
+        assert fn(2, 64, 128, odd, other, None) == B.SWITCH_E_INVALID
+        # dst starts inside src's 32 KB
+        assert fn(2, 64, 128, good, P((1 << 20) + 16 * 1024), None) == B.SWITCH_E_INVALID
+        assert b"overlap" in lib.switch_last_error()
+        assert fn(0, 64, 128, None, None, None) == B.SWITCH_OK
+        assert fn(3, 0, 128, None, None, None) == B.SWITCH_OK
+    with pytest.raises(ValueError):
+        smx.tile_weights(torch.zeros(2, 16, 32))  # fp32
+    with pytest.raises(ValueError):
+        smx.tile_weights(torch.zeros(2, 16, 32, dtype=torch.bfloat16))  # not on a GPU
 
 
 def test_launch_names_follow_the_shape():
@@ -241,6 +271,10 @@ def test_backward_rejects_before_launch():
     assert call(d_aux=float("nan")) == B.SWITCH_E_INVALID
     assert call(dx=odd) == B.SWITCH_E_INVALID
     assert call(ws_bytes=bwd_need - 1) == B.SWITCH_E_WORKSPACE
+    # the backward reads row-major expert weights only
+    s.weight_layout = B.WEIGHTS_TILED
+    assert call() == B.SWITCH_E_UNSUPPORTED and b"row-major" in lib.switch_last_error()
+    s.weight_layout = B.WEIGHTS_ROWS
     rc = lib.switch_layer_backward_profiled(ctypes.byref(s), good, good, None, good, good, 0, good, good, good, good,
                                             fwd_need, good, 0.5, good, good, None, good, good, good, bwd_need, None,
                                             2, 1, 1)

@@ -3,9 +3,9 @@ random small shapes, each checked against the oracle under the parity
 tolerances of parity_lib.
 
 Shapes: T in [0, 700], d_model and d_ff multiples of 64, N in
-{1, 2, 3, 8, 128, 2048}, capacity factor in {0.5, 1, 1.25, N}, fp32 or bf16,
-router bias absent, Zipf-skewed or pinned to one expert, with or without the
-residual.  The sweep is derandomized (the same cases on every run) and makes
+{1, 2, 3, 8, 128, 2048}, capacity factor in {0.5, 1, 1.25, N}, fp32 or bf16
+(bf16 with row-major or tiled expert weights), router bias absent,
+Zipf-skewed or pinned to one expert, with or without the residual.  The sweep is derandomized (the same cases on every run) and makes
 one pass without shrinking: it stops at the first failing case and prints it.
 """
 
@@ -36,24 +36,28 @@ def layer_case(draw):
     bias = draw(st.sampled_from(["none", "zipf", "hot"]))
     residual = draw(st.booleans())
     seed = draw(st.integers(0, 1000))
+    tiled = dtype == "bf16" and draw(st.booleans())
     cfg = LayerConfig("prop", T, d, f, N, cf, dtype, zipf_s=1.1 if bias == "zipf" else None, seed=seed)
-    return cfg, bias, residual
+    return cfg, bias, residual, tiled
 
 
 @settings(max_examples=40, deadline=None, derandomize=True, database=None, phases=(Phase.explicit, Phase.generate),
           suppress_health_check=list(HealthCheck))
 @given(layer_case())
 def test_layer_forward_matches_oracle_on_random_shapes(case):
-    cfg, bias, residual = case
-    say(f"property case {cfg} bias={bias} residual={residual}")
+    cfg, bias, residual, tiled = case
+    say(f"property case {cfg} bias={bias} residual={residual} tiled={tiled}")
     inp = make_inputs(cfg, device=DEV)
     if bias == "hot":
         b = torch.zeros(cfg.num_experts)
         b[cfg.seed % cfg.num_experts] = 30.0
         inp["router_bias"] = b.to(DEV)
     C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
-    o = smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C,
-                          add_residual=residual)
+    w_in, w_out = inp["w_in"], inp["w_out"]
+    if tiled:
+        w_in, w_out = smx.tile_weights(w_in), smx.tile_weights(w_out)
+    o = smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], w_in, w_out, C, add_residual=residual,
+                          tiled=tiled)
     torch.cuda.synchronize()
     g = gpu_outputs_numpy(o)
     own = oracle_run(inp, C, experts=[])
