@@ -194,8 +194,12 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
       if (kTiled) {
         const int blk = min((t.n0 + wave * NBW * 16 + nb * 16) / 16, Nout / 16 - 1);
         const bf16 *bp = p.B + (((int64_t)t.e * (Nout / 16) + blk) * (K / 32) + k0 / 32) * 512 + lane * 8;
+        // nontemporal: every weight byte is read once per call, and streaming
+        // it past the caches leaves the 256 MB last-level cache to the
+        // hidden activations and token rows that the other product re-reads
+        // (measured on both products together; either alone gains nothing)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) breg[slot][s][nb] = *(const u32x4 *)(bp + s * 512);
+        for (int s = 0; s < 2; ++s) breg[slot][s][nb] = __builtin_nontemporal_load((const u32x4 *)(bp + s * 512));
       } else {
         const int n = min(t.n0 + wave * NBW * 16 + nb * 16 + r16, Nout - 1);
         const bf16 *bp = p.B + ((int64_t)t.e * Nout + n) * K + kq + k0;
