@@ -97,7 +97,15 @@ __device__ __forceinline__ int xcd_tile(int b, int grid) {
 // blocks, each 64 lanes x 16 bytes), so a wave's weight load of one block
 // is one contiguous 1 KB piece; row-major weights make every load touch 16
 // rows, which costs the vector memory path several times the cycles.
-template <int MB, int NBW, int WAVES, bool kGather, int kEpi, bool kTiled, bool kSkipDead = true>
+// kStream (one row tile per expert, so every weight byte is read once):
+// tiled weights are loaded nontemporally, leaving the 256 MB last-level
+// cache to the hidden activations and token rows that the other product
+// re-reads (measured on both products together; either alone gains
+// nothing), and the results are stored nontemporally, written back as they
+// go instead of left dirty in L2 for the next kernel to wait behind.  With
+// several row tiles per expert the tiles re-read the expert's weights and
+// the down-projection re-reads H from cache: ordinary loads and stores.
+template <int MB, int NBW, int WAVES, bool kGather, int kEpi, bool kTiled, bool kStream, bool kSkipDead = true>
 __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArgs<bf16> p) {
   constexpr int kThreads = WAVES * 64;
   constexpr int kRows = MB * 16;
@@ -194,12 +202,10 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
       if (kTiled) {
         const int blk = min((t.n0 + wave * NBW * 16 + nb * 16) / 16, Nout / 16 - 1);
         const bf16 *bp = p.B + (((int64_t)t.e * (Nout / 16) + blk) * (K / 32) + k0 / 32) * 512 + lane * 8;
-        // nontemporal: every weight byte is read once per call, and streaming
-        // it past the caches leaves the 256 MB last-level cache to the
-        // hidden activations and token rows that the other product re-reads
-        // (measured on both products together; either alone gains nothing)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) breg[slot][s][nb] = __builtin_nontemporal_load((const u32x4 *)(bp + s * 512));
+        for (int s = 0; s < 2; ++s)
+          breg[slot][s][nb] = kStream ? __builtin_nontemporal_load((const u32x4 *)(bp + s * 512))
+                                      : *(const u32x4 *)(bp + s * 512);
       } else {
         const int n = min(t.n0 + wave * NBW * 16 + nb * 16 + r16, Nout - 1);
         const bf16 *bp = p.B + ((int64_t)t.e * Nout + n) * K + kq + k0;
@@ -286,6 +292,12 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
 
     // ---- epilogue of `cur`: each wave stages 16-row blocks of its columns
     // in its own LDS region and writes whole 16-byte row pieces ----
+    auto put = [&](bf16 *dst, const bf16x8 &o) {
+      if (kStream)
+        __builtin_nontemporal_store(as_u32x4(o), (u32x4 *)dst);
+      else
+        *(u32x4 *)dst = as_u32x4(o);
+    };
     float *stg = sStage + wave * 16 * kEStride;
     const int ncol0 = cur.n0 + wave * NBW * 16;
 #pragma clang loop unroll(full)
@@ -313,11 +325,11 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
             if (p.xres) xv = as_bf16x8(*(const u32x4 *)(p.xres + (int64_t)t * Nout + n));
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = (bf16)(p.xres ? (float)xv[i] + g * v[i] : g * v[i]);
-            *(u32x4 *)(p.Out + (int64_t)t * Nout + n) = as_u32x4(o);
+            put(p.Out + (int64_t)t * Nout + n, o);
           } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = (bf16)(kEpi == kEpiRelu ? fmaxf(v[i], 0.f) : v[i]);
-            *(u32x4 *)(p.Out + ((int64_t)cur.e * C + cur.m0 + m) * Nout + n) = as_u32x4(o);
+            put(p.Out + ((int64_t)cur.e * C + cur.m0 + m) * Nout + n, o);
           }
         }
       }
@@ -482,18 +494,29 @@ unsigned persistent_grid(Kern kern, int ntiles, std::atomic<int> (&occ_cache)[kM
   return (unsigned)std::max<int64_t>(8, ceil_div(want, 8) * 8);
 }
 
-template <int MB, int NBW, bool kGather, int kEpi, bool kTiled>
+template <int MB, int NBW, bool kGather, int kEpi, bool kTiled, bool kStream>
 hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
   static std::atomic<int> occ[kMaxDeviceCache];
   auto g = make_args<bf16>(c, MB * 16, kWaves * 16 * NBW);
-  auto kern = ffn_gemm_bf16_kernel<MB, NBW, kWaves, kGather, kEpi, kTiled>;
+  auto kern = ffn_gemm_bf16_kernel<MB, NBW, kWaves, kGather, kEpi, kTiled, kStream>;
   kern<<<dim3(persistent_grid(kern, g.ntiles, occ)), dim3(kWaves * 64), 0, st>>>(g);
   return hipGetLastError();
 }
 
+// Row tiles per expert: one unless the capacity exceeds the largest tile
+// (MB = kMaxMB); only then are the weights re-read (measured at 16384 tokens,
+// d_model 768, d_ff 3072, 128 experts, tiled weights: streaming takes the
+// layer from 316 to 290 us at capacity 160, and would take the top-2 layer
+// at capacity 320 from 504 to 577 us).
 template <int MB, int NBW, bool kGather, int kEpi>
 hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
-  return c.tiled ? run_bf16<MB, NBW, kGather, kEpi, true>(c, st) : run_bf16<MB, NBW, kGather, kEpi, false>(c, st);
+  bool stream = true;
+  if constexpr (MB == kMaxMB) stream = ceil_div(c.C, MB * 16) == 1;
+  if (c.tiled)
+    return stream ? run_bf16<MB, NBW, kGather, kEpi, true, true>(c, st)
+                  : run_bf16<MB, NBW, kGather, kEpi, true, false>(c, st);
+  return stream ? run_bf16<MB, NBW, kGather, kEpi, false, true>(c, st)
+                : run_bf16<MB, NBW, kGather, kEpi, false, false>(c, st);
 }
 
 // Column blocks per wave.  Both widths stream every weight byte once and run
