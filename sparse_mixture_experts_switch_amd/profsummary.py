@@ -19,7 +19,8 @@
 
 Kernel names are the library's launch names: ffn_up / ffn_down are the
 grouped-GEMM instantiations that gather token rows (ReLU epilogue) and that
-scatter through the combine epilogue.
+scatter through the combine epilogue, reading tiled expert weights;
+ffn_up_rows / ffn_down_rows the same on row-major weights.
 """
 
 from __future__ import annotations
@@ -32,8 +33,11 @@ import sqlite3
 COPY_BYTES = 1 << 30
 KERNEL_KEYS = {
     "ffn": ("ffn_fused_bf16_kernel", ""),
-    "ffn_up": ("ffn_gemm_bf16_kernel", "Lb1ELi0E"),
-    "ffn_down": ("ffn_gemm_bf16_kernel", "Lb0ELi2E"),
+    # <MB, NBW, waves, gather, epilogue, tiled, ...>, mangled or demangled
+    "ffn_up": ("ffn_gemm_bf16_kernel", ("Lb1ELi0ELb1E", "true, 0, true")),
+    "ffn_down": ("ffn_gemm_bf16_kernel", ("Lb0ELi2ELb1E", "false, 2, true")),
+    "ffn_up_rows": ("ffn_gemm_bf16_kernel", ("Lb1ELi0ELb0E", "true, 0, false")),
+    "ffn_down_rows": ("ffn_gemm_bf16_kernel", ("Lb0ELi2ELb0E", "false, 2, false")),
     "router": ("router_fwd_bf16_kernel", ""),
     "router_planes": ("router_wplanes_kernel", ""),
     "assign": ("assign_one_kernel", ""),
