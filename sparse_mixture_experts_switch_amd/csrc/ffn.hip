@@ -115,10 +115,16 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
   constexpr int kAStage = kRows * kLdsStride;  // bf16 per LDS buffer
   constexpr int kEStride = NBW * 16 + 4;       // fp32 staging row (per wave)
   constexpr int kPieces = NBW * 2;             // 8-column pieces per staged row
+  // Output rows of the expert buffer (not the combine): 16-row blocks of the
+  // whole tile are staged (double-buffered) and written in whole rows
+  constexpr bool kWholeRows = kEpi != kEpiCombine;
+  constexpr int kWStride = kCols + 16;         // fp32 staging row of the whole tile
+  constexpr int kRowPieces = kCols / 8;        // 8-column pieces per tile row
+  constexpr int kStageFloats = kWholeRows ? 2 * 16 * kWStride : WAVES * 16 * kEStride;
   constexpr bool kTok = kGather || kEpi == kEpiCombine;
   static_assert(kRows <= kThreads, "one row per thread for the tile's token map");
   __shared__ __attribute__((aligned(16))) bf16 sA[2 * kAStage];
-  __shared__ __attribute__((aligned(16))) float sStage[WAVES * 16 * kEStride];
+  __shared__ __attribute__((aligned(16))) float sStage[kStageFloats];
   __shared__ int s_tok[2][kRows];
   __shared__ float s_gate[2][kRows];
 
@@ -290,51 +296,87 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
       }
     }
 
-    // ---- epilogue of `cur`: each wave stages 16-row blocks of its columns
-    // in its own LDS region and writes whole 16-byte row pieces ----
+    // ---- epilogue of `cur` ----
     auto put = [&](bf16 *dst, const bf16x8 &o) {
       if (kStream)
         __builtin_nontemporal_store(as_u32x4(o), (u32x4 *)dst);
       else
         *(u32x4 *)dst = as_u32x4(o);
     };
-    float *stg = sStage + wave * 16 * kEStride;
-    const int ncol0 = cur.n0 + wave * NBW * 16;
+    if (kWholeRows) {
+      // Rows of the [N][C][Nout] buffer: each 16-row block of the tile is
+      // staged for the whole workgroup, and consecutive threads write
+      // consecutive 16-byte pieces of whole tile rows, so every wave stores
+      // whole cache lines (per-wave pieces of 96 bytes leave lines to be
+      // written back in parts: 135 MB written for 101 MB of H).  Two staging
+      // buffers, one LDS-only barrier per block: a wave overwrites a buffer
+      // only after the next block's barrier, which every wave reaches after
+      // its reads of it.  Measured at 16384 tokens, d_model 768, d_ff 3072,
+      // 128 experts: the up-projection 140.7 -> 132.6 us.
+      int sb = 0;
 #pragma clang loop unroll(full)
-    for (int mb = 0; mb < MB; ++mb) {
-      if (mb >= mlive) continue;
+      for (int mb = 0; mb < MB; ++mb) {
+        if (mb >= mlive) continue;
+        float *stg = sStage + sb * 16 * kWStride;
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
+        for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) stg[((lane / 16) * 4 + i) * kEStride + nb * 16 + r16] = acc[mb][nb][i];
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes landed
-      __builtin_amdgcn_wave_barrier();
-      for (int c = lane; c < 16 * kPieces; c += kWave) {
-        const int rr = c / kPieces, pc = c % kPieces;
-        const int m = mb * 16 + rr;
-        const int n = ncol0 + pc * 8;
-        if (m < cur.mrows && n < Nout) {
-          const f32x4 v0 = *(const f32x4 *)&stg[rr * kEStride + pc * 8];
-          const f32x4 v1 = *(const f32x4 *)&stg[rr * kEStride + pc * 8 + 4];
-          const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          bf16x8 o;
-          if (kEpi == kEpiCombine) {
-            const int t = s_tok[cb][m];
-            const float g = s_gate[cb][m];
-            bf16x8 xv{};
-            if (p.xres) xv = as_bf16x8(*(const u32x4 *)(p.xres + (int64_t)t * Nout + n));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (bf16)(p.xres ? (float)xv[i] + g * v[i] : g * v[i]);
-            put(p.Out + (int64_t)t * Nout + n, o);
-          } else {
+          for (int i = 0; i < 4; ++i)
+            stg[((lane / 16) * 4 + i) * kWStride + wave * NBW * 16 + nb * 16 + r16] = acc[mb][nb][i];
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only: stores keep going
+        for (int c = tid; c < 16 * kRowPieces; c += kThreads) {
+          const int rr = c / kRowPieces, pc = c % kRowPieces;
+          const int m = mb * 16 + rr;
+          const int n = cur.n0 + pc * 8;
+          if (m < cur.mrows && n < Nout) {
+            const f32x4 v0 = *(const f32x4 *)&stg[rr * kWStride + pc * 8];
+            const f32x4 v1 = *(const f32x4 *)&stg[rr * kWStride + pc * 8 + 4];
+            const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            bf16x8 o;
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = (bf16)(kEpi == kEpiRelu ? fmaxf(v[i], 0.f) : v[i]);
             put(p.Out + ((int64_t)cur.e * C + cur.m0 + m) * Nout + n, o);
           }
         }
+        sb ^= 1;
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // staging reads done before the next block overwrites
-      __builtin_amdgcn_wave_barrier();
+      // the next tile's epilogue reuses the buffers after its chunk barriers
+    } else {
+      // The combine: rows go to scattered tokens of y; each wave stages
+      // 16-row blocks of its columns in its own LDS region and writes whole
+      // 16-byte row pieces (staging the whole tile as above measured no
+      // faster here)
+      float *stg = sStage + wave * 16 * kEStride;
+      const int ncol0 = cur.n0 + wave * NBW * 16;
+#pragma clang loop unroll(full)
+      for (int mb = 0; mb < MB; ++mb) {
+        if (mb >= mlive) continue;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) stg[((lane / 16) * 4 + i) * kEStride + nb * 16 + r16] = acc[mb][nb][i];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes landed
+        __builtin_amdgcn_wave_barrier();
+        for (int c = lane; c < 16 * kPieces; c += kWave) {
+          const int rr = c / kPieces, pc = c % kPieces;
+          const int m = mb * 16 + rr;
+          const int n = ncol0 + pc * 8;
+          if (m < cur.mrows && n < Nout) {
+            const f32x4 v0 = *(const f32x4 *)&stg[rr * kEStride + pc * 8];
+            const f32x4 v1 = *(const f32x4 *)&stg[rr * kEStride + pc * 8 + 4];
+            const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            const int t = s_tok[cb][m];
+            const float g = s_gate[cb][m];
+            bf16x8 xv{}, o;
+            if (p.xres) xv = as_bf16x8(*(const u32x4 *)(p.xres + (int64_t)t * Nout + n));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (bf16)(p.xres ? (float)xv[i] + g * v[i] : g * v[i]);
+            put(p.Out + (int64_t)t * Nout + n, o);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // staging reads done before the next block overwrites
+        __builtin_amdgcn_wave_barrier();
+      }
     }
 
     if (!have_nxt) break;
