@@ -403,11 +403,15 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
   }
 }
 
-// fp32 grouped GEMM on the vector ALUs: 64 x 64 output tiles, 16-deep
-// contraction slices staged in LDS, 4 x 4 outputs per thread.
+// fp32 grouped GEMM on the vector ALUs: 64 x 64 output tiles, 32-deep
+// contraction slices staged in LDS, 4 x 4 outputs per thread.  The next
+// slice is loaded into registers while the current one is multiplied, so a
+// tile pays one global-load round trip, not one per slice (small fp32 layers
+// have few tiles, and each tile's slices ran in sequence).
 template <bool kGather, int kEpi>
 __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_f32_kernel(const GemmArgs<float> p) {
-  constexpr int kT = 64, kKs = 16;
+  constexpr int kT = 64, kKs = 32;
+  constexpr int kLd = kT * kKs / kFfnThreads;  // elements of each operand per thread and slice
   __shared__ float sA[kKs][kT + 1], sB[kKs][kT + 1];
   __shared__ int s_tok[kT];
   __shared__ float s_gate[kT];
@@ -432,17 +436,29 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_f32_kernel(const GemmArg
   }
   const float *Aexp = p.A + (int64_t)e * p.C * K;
   const float *Bexp = p.B + (int64_t)e * Nout * K;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += kKs) {
-    for (int i = tid; i < kT * kKs; i += kFfnThreads) {
+  float ra[kLd], rb[kLd];
+  auto load = [&](int k0) {  // K is a multiple of 64: every slice is whole
+#pragma unroll
+    for (int q = 0; q < kLd; ++q) {
+      const int i = tid + q * kFfnThreads;
       const int r = i / kKs, k = i % kKs;
       const int m = m0 + r, n = n0 + r;
-      float av = 0.f;
-      if (m < M) av = kGather ? p.A[(int64_t)s_tok[r] * K + k0 + k] : Aexp[(int64_t)m * K + k0 + k];
-      sA[k][r] = av;
-      sB[k][r] = (n < Nout) ? Bexp[(int64_t)n * K + k0 + k] : 0.f;
+      ra[q] = m < M ? (kGather ? p.A[(int64_t)s_tok[r] * K + k0 + k] : Aexp[(int64_t)m * K + k0 + k]) : 0.f;
+      rb[q] = n < Nout ? Bexp[(int64_t)n * K + k0 + k] : 0.f;
+    }
+  };
+  float acc[4][4] = {};
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += kKs) {
+    __syncthreads();  // the previous slice's products are done with the LDS tiles
+#pragma unroll
+    for (int q = 0; q < kLd; ++q) {
+      const int i = tid + q * kFfnThreads;
+      sA[i % kKs][i / kKs] = ra[q];
+      sB[i % kKs][i / kKs] = rb[q];
     }
     __syncthreads();
+    if (k0 + kKs < K) load(k0 + kKs);
 #pragma unroll
     for (int k = 0; k < kKs; ++k) {
       float a[4], b[4];
@@ -456,7 +472,6 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_f32_kernel(const GemmArg
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

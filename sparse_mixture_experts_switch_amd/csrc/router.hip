@@ -761,8 +761,13 @@ __device__ __forceinline__ LogitRows<kLds> router_contract_f32(
     lg.base = logits_g + t0 * N;
     lg.stride = N;
   }
-  constexpr int kPer = kRouterTokens * kRouterChunk / kRouterThreads;  // pairs per thread
+  constexpr int kPer = kRouterTokens * kRouterChunk / kRouterThreads;  // pairs per thread, at most
   for (int c0 = 0; c0 < N; c0 += kRouterChunk) {
+    // the chunk's (token, expert) pairs over its live experts only, spread
+    // over all threads (with few experts, pairs over the whole chunk width
+    // would leave most threads idle and the rest in long serial chains)
+    const int nc = min(kRouterChunk, N - c0);
+    const int npairs = kRouterTokens * nc;
     float acc[kPer];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) acc[q] = 0.f;
@@ -776,12 +781,14 @@ __device__ __forceinline__ LogitRows<kLds> router_contract_f32(
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int pair = tid + q * kRouterThreads;
-        const int t = pair / kRouterChunk, j = c0 + pair % kRouterChunk;
-        if (j < N) {
+        if (pair < npairs) {
+          const int t = pair / nc, j = c0 + pair % nc;
           const float *w = w_r + (int64_t)j * d + k0;
-          const int kn = min(kKc, d - k0);
           float a = acc[q];
-          for (int k = 0; k < kn; ++k) a = __builtin_fmaf(s_x[t][k], w[k], a);
+          // d is a multiple of 64: whole slices, so the W_r loads go out 16 at
+          // a time instead of one round trip per multiply-add
+#pragma unroll 16
+          for (int k = 0; k < kKc; ++k) a = __builtin_fmaf(s_x[t][k], w[k], a);
           acc[q] = a;
         }
       }
@@ -789,8 +796,10 @@ __device__ __forceinline__ LogitRows<kLds> router_contract_f32(
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int pair = tid + q * kRouterThreads;
-      const int t = pair / kRouterChunk, j = c0 + pair % kRouterChunk;
-      if (j < N && t < nt) lg.at(t, kLds ? j - c0 : j) = acc[q] + (bias ? bias[j] : 0.f);
+      if (pair < npairs) {
+        const int t = pair / nc, j = c0 + pair % nc;
+        if (t < nt) lg.at(t, kLds ? j - c0 : j) = acc[q] + (bias ? bias[j] : 0.f);
+      }
     }
     if (kLds) break;
   }
