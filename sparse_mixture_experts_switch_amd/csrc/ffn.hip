@@ -17,7 +17,9 @@
 // every weight byte once: a workgroup owns every live row of one expert (up
 // to 16 * MB) and a band of output features; the expert's activation rows
 // pass through LDS chunk by chunk while its weight rows stream from global
-// memory straight into MFMA operand registers, DEPTH chunks ahead.
+// memory straight into MFMA operand registers, two chunks ahead.  The
+// weights are either row-major or tiled (stored in MFMA operand order, see
+// tile.hip); both give the same operands in the same lanes.
 //
 // Row sources and sinks:
 //   A rows come from the [N][C][K] expert buffer, or (gather) from token rows
