@@ -2,11 +2,14 @@
 random small shapes, each checked against the oracle under the parity
 tolerances of parity_lib.
 
-Shapes: T in [0, 700], d_model and d_ff multiples of 64, N in
-{1, 2, 3, 8, 128, 2048}, capacity factor in {0.5, 1, 1.25, N}, fp32 or bf16
-(bf16 with row-major or tiled expert weights), router bias absent,
-Zipf-skewed or pinned to one expert, with or without the residual.  The sweep is derandomized (the same cases on every run) and makes
-one pass without shrinking: it stops at the first failing case and prints it.
+Shapes: T in [0, 700], d_model in {64, 128, 192, 256, 768} and d_ff in
+{64, 128, 256, 384} (the streaming expert kernels, and the fused one at
+d_model 128 / 256), N in {1, 2, 3, 8, 128, 2048}, capacity factor in
+{0.5, 1, 1.25, N}, fp32 or bf16 (bf16 with row-major or tiled expert
+weights), router bias absent, Zipf-skewed or pinned to one expert, with or
+without the residual.  The sweep is derandomized (the same cases on every
+run) and makes one pass without shrinking: it stops at the first failing
+case and prints it.
 """
 
 from __future__ import annotations
@@ -29,8 +32,8 @@ DEV = "cuda:0"
 def layer_case(draw):
     N = draw(st.sampled_from([1, 2, 3, 8, 128, 2048]))
     T = draw(st.integers(0, 700))
-    d = draw(st.sampled_from([64, 128, 192]))
-    f = draw(st.sampled_from([64, 128, 256]))
+    d = draw(st.sampled_from([64, 128, 192, 256, 768]))
+    f = draw(st.sampled_from([64, 128, 256, 384]))
     cf = draw(st.sampled_from([0.5, 1.0, 1.25, float(N)]))
     dtype = draw(st.sampled_from(["bf16", "f32"]))
     bias = draw(st.sampled_from(["none", "zipf", "hot"]))
