@@ -170,3 +170,29 @@ def test_layer_tiled_against_oracle():
     assert g["dropped"].any()
     check_y(g["y"], fed, cfg.torch_dtype, "tiled", expect_rows=int((~fed["dropped"]).sum()))
     assert f64(o["y"]).shape == (cfg.tokens, cfg.d_model)
+
+
+@pytest.mark.parametrize("name,cfg,cap", [
+    # capacity 160: one row tile per expert, weights and results streamed
+    ("stream_capacity_160", SMALL.with_(d_model=768, d_ff=384, tokens=1280, num_experts=8), 160),
+    # capacity 161: two row tiles, ordinary loads and stores
+    ("stream_capacity_161", SMALL.with_(d_model=768, d_ff=384, tokens=1280, num_experts=8), 161),
+    # the smallest tiled matrices: 4 column blocks, tiles wider than the matrix
+    ("d64_f64", SMALL.with_(d_model=64, d_ff=64, tokens=333, num_experts=3), None),
+    ("one_expert", SMALL.with_(d_model=192, d_ff=128, tokens=257, num_experts=1, capacity_factor=0.5), None),
+])
+def test_layer_tiled_edges(name, cfg, cap):
+    """Edges of the tiled path, each bit-identical to row-major weights:
+    the capacity where the expert kernels switch from streaming (one row
+    tile per expert, nontemporal weights and results) to several row tiles,
+    matrices narrower than one tile, and a single expert."""
+    say(f"tiled edge {name}: {cfg} capacity {cap}")
+    inp = make_inputs(cfg, device=DEV)
+    C = cap if cap is not None else smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+    wi, wo = _tiled(inp)
+    args = (inp["x"], inp["w_router"], inp["router_bias"])
+    a = smx.layer_forward(*args, inp["w_in"], inp["w_out"], C, add_residual=True)
+    b = smx.layer_forward(*args, wi, wo, C, add_residual=True, tiled=True)
+    torch.cuda.synchronize()
+    _same(a, b, ROUTE_KEYS + ("y",), name)
+    assert int(a["expert_count"].max()) > 0
