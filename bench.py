@@ -260,8 +260,9 @@ def top2_bench(smx, torch, inp, cfg, stream, steps: int, weights, tiled: bool) -
     ws2 = torch.empty(smx.topk_workspace_bytes(shape2, 2), dtype=torch.uint8, device=dev)
     out2 = smx.binding._route_outputs(T, N, dev, 2)
     out2["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
-    call2 = lambda: smx.topk_layer_forward(inp["x"], inp["w_router"], inp["router_bias"],  # noqa: E731
-                                           *weights, C2, 2, workspace=ws2, out=out2, tiled=tiled)
+    w_r, w_in, w_out = weights
+    call2 = lambda: smx.topk_layer_forward(inp["x"], w_r, inp["router_bias"], w_in, w_out,  # noqa: E731
+                                           C2, 2, workspace=ws2, out=out2, tiled=tiled)
     with torch.cuda.stream(stream):
         t_warm = time.perf_counter()
         while time.perf_counter() - t_warm < MIN_WARMUP_S:
@@ -292,7 +293,9 @@ def mfma_diag_bench(smx, torch, cfg, stream, steps: int, tiled: bool) -> dict:
     dcfg = cfg.with_(name="mfma_diag", tokens=4 * cfg.tokens)
     dev = torch.device("cuda:0")
     inp = make_inputs(dcfg, device=dev)
+    w_r = inp["w_router"]
     if tiled:
+        w_r = smx.tile_router(w_r)
         convert_in_place(smx, torch, inp["w_in"], True)
         convert_in_place(smx, torch, inp["w_out"], True)
     T, d, f, N = dcfg.tokens, dcfg.d_model, dcfg.d_ff, dcfg.num_experts
@@ -303,7 +306,7 @@ def mfma_diag_bench(smx, torch, cfg, stream, steps: int, tiled: bool) -> dict:
     out["y"] = torch.empty(T, d, dtype=dcfg.torch_dtype, device=dev)
     names = smx.launch_names(shape)
     part = lambda lo, hi: smx.layer_forward_profiled(  # noqa: E731
-        inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C, first_kernel=lo,
+        inp["x"], w_r, inp["router_bias"], inp["w_in"], inp["w_out"], C, first_kernel=lo,
         last_kernel=hi, workspace=ws, out=out, tiled=tiled)
     kern = {}
     with torch.cuda.stream(stream):
@@ -353,17 +356,17 @@ def measure_layer(smx, torch, cfg, inp, stream, steps: int, warmup: int, kernels
     """Times switch_layer_forward on one workload: `steps` back-to-back steps
     after the warmup, then `steps` cold-cache steps, then (kernels=True) each
     kernel of the step bracketed by HIP events on the layer's stream.
-    weights: (W_in, W_out) in the layout `tiled` declares (default: inp's,
-    row-major)."""
+    weights: (W_r, W_in, W_out) in the layout `tiled` declares (default:
+    inp's, row-major)."""
     dev = inp["x"].device
     T, d, f, N = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts
     C = smx.capacity(T, N, cfg.capacity_factor)
-    w_in, w_out = weights if weights is not None else (inp["w_in"], inp["w_out"])
+    w_r, w_in, w_out = weights if weights is not None else (inp["w_router"], inp["w_in"], inp["w_out"])
     shape = smx.binding.make_shape(T, d, f, N, C, cfg.torch_dtype, tiled)
     ws = torch.empty(smx.workspace_bytes(shape), dtype=torch.uint8, device=dev)
     out = smx.binding._route_outputs(T, N, dev)
     out["y"] = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
-    call = lambda: smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], w_in,  # noqa: E731
+    call = lambda: smx.layer_forward(inp["x"], w_r, inp["router_bias"], w_in,  # noqa: E731
                                      w_out, C, workspace=ws, out=out, tiled=tiled)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
@@ -419,7 +422,7 @@ def measure_layer(smx, torch, cfg, inp, stream, steps: int, warmup: int, kernels
         names = smx.launch_names(shape)
         n_k = len(names)
         part = lambda lo, hi: smx.layer_forward_profiled(  # noqa: E731
-            inp["x"], inp["w_router"], inp["router_bias"], w_in, w_out, C, first_kernel=lo,
+            inp["x"], w_r, inp["router_bias"], w_in, w_out, C, first_kernel=lo,
             last_kernel=hi, workspace=ws, out=out, tiled=tiled)
         with torch.cuda.stream(stream):
             for i, name in enumerate(names):
@@ -558,11 +561,15 @@ def configs_bench(smx, torch, stream, steps: int, warmup: int, cpu: bool, names)
         es = 2 if cfg.dtype == "bf16" else 4
         log(f"bench: configs: generating {cfg}")
         inp = make_inputs(cfg, device=stream.device)
-        tiled = cfg.dtype == "bf16"  # bf16 layers run on tiled expert weights, converted before timing
+        tiled = cfg.dtype == "bf16"  # bf16 layers run on tiled weights, converted before timing
+        w_r = inp["w_router"]
         if tiled:
+            w_r = smx.tile_router(w_r)
             convert_in_place(smx, torch, inp["w_in"], True)
             convert_in_place(smx, torch, inp["w_out"], True)
-        m = measure_layer(smx, torch, cfg, inp, stream, steps, warmup, tiled=tiled)
+        m = measure_layer(smx, torch, cfg, inp, stream, steps, warmup, weights=(w_r, inp["w_in"], inp["w_out"]),
+                          tiled=tiled)
+        del w_r
         if tiled:  # back to row-major for the oracle
             convert_in_place(smx, torch, inp["w_in"], False)
             convert_in_place(smx, torch, inp["w_out"], False)
@@ -578,7 +585,7 @@ def configs_bench(smx, torch, stream, steps: int, warmup: int, cpu: bool, names)
         peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS
         rec = {"workload": (f"{T} tokens, d_model {d}, d_ff {f}, {N} experts, capacity factor "
                             f"{cfg.capacity_factor} (capacity {C}), {cfg.dtype} activations and expert weights"
-                            + (" (tiled layout)" if tiled else "") + ", fp32 router"
+                            + (" (tiled layout, router planes)" if tiled else "") + ", fp32 router"
                             + (f", Zipf({cfg.zipf_s}) router bias" if cfg.zipf_s else "")),
                "ms_per_step": round(m["ms_cold"], 4), "tokens_per_s": round(T / (m["ms_cold"] * 1e-3), 1),
                "ms_per_step_back_to_back": round(m["ms_warm"], 4),
@@ -636,11 +643,13 @@ def main() -> int:
     # the layer runs on a stream of its own (the legacy default stream
     # synchronises with every other stream at each launch)
     stream = torch.cuda.Stream(device=dev)
-    # the expert weights in the layout the forward calls read: tiled (a copy
-    # converted once, before any timing: the parameters' storage format) or
-    # row-major; the backward reads row-major weights
+    # the weights in the layout the forward calls read: tiled (W_r's planes
+    # and the expert matrices in operand order, a copy converted once, before
+    # any timing: the parameters' storage format) or row-major; the backward
+    # reads row-major weights
     tiled = args.weights == "tiled" and cfg.dtype == "bf16"
-    wts = (smx.tile_weights(inp["w_in"]), smx.tile_weights(inp["w_out"])) if tiled else (inp["w_in"], inp["w_out"])
+    wts = ((smx.tile_router(inp["w_router"]), smx.tile_weights(inp["w_in"]), smx.tile_weights(inp["w_out"]))
+           if tiled else (inp["w_router"], inp["w_in"], inp["w_out"]))
     torch.cuda.synchronize()
     m = measure_layer(smx, torch, cfg, inp, stream, args.steps, args.warmup, weights=wts, tiled=tiled)
     C, shape, ws, out, kern = m["C"], m["shape"], m["ws"], m["out"], m["kern"]
@@ -676,9 +685,10 @@ def main() -> int:
         # routing alone (router + assignment), and routing with the dispatch
         # copy in one pass over x (its workspace's ordering state is cleared
         # by a small kernel inside each call)
-        ("route", lambda: smx.route(inp["x"], inp["w_router"], inp["router_bias"], C, workspace=ws, out=rstage)),
-        ("route_dispatch", lambda: smx.route_dispatch(inp["x"], inp["w_router"], inp["router_bias"], C,
-                                                      workspace=ws, out=rstage, dispatched=disp)))
+        ("route", lambda: smx.route(inp["x"], wts[0], inp["router_bias"], C, workspace=ws, out=rstage,
+                                    tiled=tiled, num_experts=N)),
+        ("route_dispatch", lambda: smx.route_dispatch(inp["x"], wts[0], inp["router_bias"], C, workspace=ws,
+                                                      out=rstage, dispatched=disp, tiled=tiled, num_experts=N)))
     with torch.cuda.stream(stream):
         for name, fn in stage_fns:
             fn()
@@ -729,10 +739,10 @@ def main() -> int:
     norm_rec = None
     if "stages" in sections:
         nout = {k: torch.empty_like(v) for k, v in out.items()}
-        ncall = lambda: smx.layer_forward_add_norm(inp["x"], inp["w_router"], inp["router_bias"],  # noqa: E731
-                                                   *wts, C, gamma, beta, 1e-6, workspace=ws, out=nout,
+        ncall = lambda: smx.layer_forward_add_norm(inp["x"], wts[0], inp["router_bias"],  # noqa: E731
+                                                   wts[1], wts[2], C, gamma, beta, 1e-6, workspace=ws, out=nout,
                                                    tiled=tiled)
-        bcall = lambda: smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], *wts,  # noqa: E731
+        bcall = lambda: smx.layer_forward(inp["x"], wts[0], inp["router_bias"], wts[1], wts[2],  # noqa: E731
                                           C, workspace=ws, out=nout, tiled=tiled)
         times = {}
         with torch.cuda.stream(stream):
@@ -795,7 +805,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) tokens, truncated-normal 0.1-scale weights; no dataset)",
         "config": {"workload": f"{cfg.name}: {T} tokens (32 seqs x 512), d_model {d}, d_ff {f}, {N} experts, "
                                f"capacity factor {cfg.capacity_factor} (capacity {C}), bf16 activations and "
-                               f"expert weights" + (" (tiled layout)" if tiled else "") + ", fp32 router",
+                               f"expert weights" + (" (tiled layout, router planes)" if tiled else "") + ", fp32 router",
                    "tokens": T, "d_model": d, "d_ff": f, "num_experts": N, "capacity": C,
                    "drop_rate": round(drop_rate, 5),
                    "weight_layout": "tiled" if tiled else "row-major"},

@@ -22,7 +22,7 @@
  *   allocates and frees nothing, keeps no state between calls and never
  *   blocks the host (but see debug mode below).  All work is enqueued on
  *   `stream` (a hipStream_t passed as void*; NULL = null stream).
- * - Layouts are dense row-major, except the expert weights W_in and W_out
+ * - Layouts are dense row-major, except the weights W_r, W_in and W_out
  *   when s->weight_layout is SWITCH_WEIGHTS_TILED (see below).  T tokens are
  *   the caller's [batch][seq] flattened in row-major order; that order is
  *   the "token order" that decides which tokens overflow an expert.
@@ -49,7 +49,7 @@
  *   num_experts >= 1; capacity >= 0.  Shapes outside that give
  *   SWITCH_E_UNSUPPORTED, and so does SWITCH_WEIGHTS_TILED with fp32; a
  *   weight_layout other than the two values below gives SWITCH_E_INVALID.
- *   Every call that reads W_in / W_out reads them in s->weight_layout.
+ *   Every call that reads W_r, W_in or W_out reads them in s->weight_layout.
  */
 #ifndef SWITCH_MOE_H
 #define SWITCH_MOE_H
@@ -69,9 +69,9 @@ extern "C" {
 
 enum { SWITCH_F32 = 0, SWITCH_BF16 = 1 };
 
-/* Storage of the expert weights W_in [N][d_ff][d_model] and W_out
- * [N][d_model][d_ff].  Each expert matrix has R rows and K columns, K being
- * the contraction dimension (d_model for W_in, d_ff for W_out).
+/* Storage of the weights.  The expert weights W_in [N][d_ff][d_model] and
+ * W_out [N][d_model][d_ff]: each expert matrix has R rows and K columns, K
+ * being the contraction dimension (d_model for W_in, d_ff for W_out).
  *   SWITCH_WEIGHTS_ROWS   row-major: element (r, k) of matrix m at
  *                         (m R + r) K + k.
  *   SWITCH_WEIGHTS_TILED  bf16 only: 16-row x 32-column blocks in row-major
@@ -84,8 +84,16 @@ enum { SWITCH_F32 = 0, SWITCH_BF16 = 1 };
  *                         weights as one contiguous 1 KB piece; the layer is
  *                         faster and its results are bit-identical to those of
  *                         the row-major layout.  switch_tile_weights converts.
- * The same byte count either way.  The layout is not checked: weights in the
- * other layout than the one declared give wrong results, not an error. */
+ *                         The same byte count either way.
+ * The router weights W_r: fp32 [N][d_model] row-major with SWITCH_WEIGHTS_ROWS;
+ * with SWITCH_WEIGHTS_TILED the argument w_router instead points at W_r's
+ * exact three-way bf16 split in the router's matrix-core operand order, as
+ * switch_tile_router writes it (switch_tiled_router_bytes bytes).  That is
+ * the form the router's products read: with row-major W_r a bf16 layer call
+ * first writes it into its workspace, a pass the tiled form skips.  The
+ * router computes the same fp32 logits either way.
+ * The layout is not checked: weights in the other layout than the one
+ * declared give wrong results, not an error. */
 enum { SWITCH_WEIGHTS_ROWS = 0, SWITCH_WEIGHTS_TILED = 1 };
 
 typedef struct switch_shape {
@@ -95,7 +103,7 @@ typedef struct switch_shape {
   int32_t num_experts;   /* N                                                            */
   int32_t capacity;      /* C: per-expert buffer rows, normally from switch_capacity()   */
   int32_t dtype;         /* SWITCH_F32 or SWITCH_BF16 (activations and expert weights)   */
-  int32_t weight_layout; /* SWITCH_WEIGHTS_ROWS (0) or SWITCH_WEIGHTS_TILED: W_in, W_out */
+  int32_t weight_layout; /* SWITCH_WEIGHTS_ROWS (0) or SWITCH_WEIGHTS_TILED: W_r, W_in, W_out */
 } switch_shape;
 
 /* Expert capacity, "Expert Capacity and the Capacity Factor" (capacity
@@ -119,7 +127,7 @@ const char *switch_last_error(void);
  * assignment and the load-balancing loss ("Switch Routing", "Expert
  * Capacity", "The Load-Balancing Loss").
  *   x            [T][d]    activation dtype
- *   w_router     [N][d]    fp32
+ *   w_router     [N][d]    fp32 (tiled layout: switch_tile_router's planes)
  *   router_bias  [N] fp32 or NULL (added to the logits)
  * Outputs:
  *   expert_idx   [T] int32  argmax of the logits; ties go to the lowest index
@@ -426,6 +434,25 @@ int switch_launch_names(const switch_shape *s, const char **names, int32_t max_n
  * multiple of 16 or cols of 32, sizes overflowing), SWITCH_E_HIP. */
 int switch_tile_weights(int32_t count, int32_t rows, int32_t cols, const void *src, void *dst, void *stream);
 int switch_untile_weights(int32_t count, int32_t rows, int32_t cols, const void *src, void *dst, void *stream);
+
+/* Router weights in the form SWITCH_WEIGHTS_TILED reads (defined at
+ * switch_shape).  w_router: W_r [num_experts][d_model] fp32, row-major.
+ * planes: switch_tiled_router_bytes(num_experts, d_model) bytes =
+ * ceil(num_experts / 16) x d_model / 32 x 3 KB: for each tile of 16 experts
+ * and 32 columns, three 1 KB pieces (the hi, mid and lo bf16 planes, each
+ * taking the next 8 significant bits of every value, so hi + mid + lo is the
+ * fp32 value exactly), each piece 64 lanes x 8 bf16 with lane l holding
+ * expert 16 tile + l % 16 (zeros past num_experts) at columns 8 (l / 16) ..
+ * + 7 of the 32.  The router stays fp32 ("Making Sparse Training Stable",
+ * selective precision): every product of a bf16 token value with a plane is
+ * exact in fp32.  A conversion of the parameters, like
+ * switch_tile_weights; device pointers, 16-byte aligned, not overlapping;
+ * enqueued on `stream`.  Errors: SWITCH_E_INVALID (num_experts or d_model
+ * below 1, NULL / misaligned / overlapping pointers, NULL bytes_out),
+ * SWITCH_E_UNSUPPORTED (d_model not a multiple of 64, sizes overflowing),
+ * SWITCH_E_HIP. */
+int switch_tiled_router_bytes(int32_t num_experts, int32_t d_model, size_t *bytes_out);
+int switch_tile_router(int32_t num_experts, int32_t d_model, const float *w_router, void *planes, void *stream);
 
 #ifdef __cplusplus
 }

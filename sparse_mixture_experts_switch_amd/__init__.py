@@ -31,7 +31,10 @@ from .binding import (  # noqa: F401
     noalloc_scratch_bytes,
     route,
     route_dispatch,
+    tile_router,
     tile_weights,
+    tiled_router_bytes,
+    tiled_router_shape,
     topk_layer_forward,
     topk_workspace_bytes,
     untile_weights,

@@ -35,7 +35,7 @@ EXPORTED = [
     "switch_backward_workspace_bytes", "switch_layer_backward", "switch_layer_backward_profiled",
     "switch_combine_add_norm", "switch_route_dispatch", "switch_layer_forward_noalloc",
     "switch_noalloc_scratch_bytes", "switch_layer_forward_train", "switch_layer_forward_add_norm",
-    "switch_tile_weights", "switch_untile_weights",
+    "switch_tile_weights", "switch_untile_weights", "switch_tiled_router_bytes", "switch_tile_router",
 ]
 BACKWARD_KERNELS = ["bwd_dz", "bwd_dw_out", "bwd_dx", "bwd_dw_in", "bwd_router", "bwd_router_dx", "bwd_router_w",
                     "bwd_router_w_sum"]
@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.switch_noalloc_scratch_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
     lib.switch_tile_weights.argtypes = [ctypes.c_int32] * 3 + [_P] * 3
     lib.switch_untile_weights.argtypes = lib.switch_tile_weights.argtypes
+    lib.switch_tiled_router_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.switch_tile_router.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
     for name in EXPORTED:
         if name != "switch_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -143,14 +145,29 @@ def _check_acts(x, name: str = "x") -> torch.device:
     return x.device
 
 
-def _check_router(x, w_router, router_bias) -> None:
+def tiled_router_shape(num_experts: int, d_model: int) -> tuple:
+    """Shape of W_r in the tiled layout (tile_router), bf16: 16-expert tiles x
+    32-column steps x 3 planes x 64 lanes x 8 values."""
+    return ((num_experts + 15) // 16, d_model // 32, 3, 64, 8)
+
+
+def _check_router(x, w_router, router_bias, tiled: bool = False, num_experts: int | None = None) -> int:
+    """Checks the router's weights (fp32 [N][d], or with tiled the planes of
+    tile_router for num_experts experts) and bias; returns N."""
     dev = _check_acts(x)
-    if not isinstance(w_router, torch.Tensor) or w_router.dim() != 2:
-        raise ValueError("w_router must be a 2-D tensor [num_experts][d_model]")
-    N = w_router.shape[0]
-    _expect(w_router, "w_router", (N, x.shape[1]), torch.float32, dev)
+    if tiled:
+        if num_experts is None:
+            raise ValueError("tiled router weights need num_experts")
+        N = int(num_experts)
+        _expect(w_router, "w_router (tiled)", tiled_router_shape(N, x.shape[1]), torch.bfloat16, dev)
+    else:
+        if not isinstance(w_router, torch.Tensor) or w_router.dim() != 2:
+            raise ValueError("w_router must be a 2-D tensor [num_experts][d_model]")
+        N = w_router.shape[0]
+        _expect(w_router, "w_router", (N, x.shape[1]), torch.float32, dev)
     if router_bias is not None:
         _expect(router_bias, "router_bias", (N,), torch.float32, dev)
+    return N
 
 
 def _check_experts(w_in, w_out, N: int, d: int, dtype: torch.dtype, dev: torch.device) -> None:
@@ -161,9 +178,11 @@ def _check_experts(w_in, w_out, N: int, d: int, dtype: torch.dtype, dev: torch.d
     _expect(w_out, "w_out", (N, d, f), dtype, dev)
 
 
-def _check_layer_inputs(x, w_router, router_bias, w_in, w_out) -> None:
-    _check_router(x, w_router, router_bias)
-    _check_experts(w_in, w_out, w_router.shape[0], x.shape[1], x.dtype, x.device)
+def _check_layer_inputs(x, w_router, router_bias, w_in, w_out, tiled: bool = False) -> None:
+    if not isinstance(w_in, torch.Tensor) or w_in.dim() != 3:
+        raise ValueError("w_in must be a 3-D tensor [num_experts][d_ff][d_model]")
+    N = _check_router(x, w_router, router_bias, tiled, w_in.shape[0])
+    _check_experts(w_in, w_out, N, x.shape[1], x.dtype, x.device)
 
 
 def _check_route_outputs(o: dict, T: int, N: int, dev: torch.device, k: int | None = None) -> None:
@@ -247,17 +266,18 @@ def _shape_of(x, w_in, num_experts, capacity_, d_ff=None) -> Shape:
 
 
 def route(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None, capacity_: int,
-          workspace: torch.Tensor | None = None, out: dict | None = None) -> dict:
-    """Router, top-1, capacity assignment and aux loss (switch_route)."""
-    _check_router(x, w_router, router_bias)
+          workspace: torch.Tensor | None = None, out: dict | None = None, tiled: bool = False,
+          num_experts: int | None = None) -> dict:
+    """Router, top-1, capacity assignment and aux loss (switch_route); tiled:
+    w_router holds tile_router's planes of num_experts experts."""
+    N = _check_router(x, w_router, router_bias, tiled, num_experts)
     T, d = x.shape
-    N = w_router.shape[0]
-    shape = make_shape(T, d, 64, N, capacity_, x.dtype)
+    shape = make_shape(T, d, 64, N, capacity_, x.dtype, tiled)
     dev = x.device
     o = out if out is not None else _route_outputs(T, N, dev)
     _check_route_outputs(o, T, N, dev)
     # routing needs the workspace of the same shape without expert buffers
-    ws = _workspace(make_shape(T, d, 64, N, 0, x.dtype), dev, workspace)
+    ws = _workspace(make_shape(T, d, 64, N, 0, x.dtype, tiled), dev, workspace)
     _check(load_library().switch_route(
         ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(o["expert_idx"]), _ptr(o["gate"]),
         _ptr(o["slot"]), _ptr(o["dropped"]), _ptr(o["expert_count"]), _ptr(o["aux_loss"]), _ptr(ws),
@@ -267,17 +287,17 @@ def route(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | N
 
 def route_dispatch(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Tensor | None, capacity_: int,
                    workspace: torch.Tensor | None = None, out: dict | None = None,
-                   dispatched: torch.Tensor | None = None) -> dict:
+                   dispatched: torch.Tensor | None = None, tiled: bool = False,
+                   num_experts: int | None = None) -> dict:
     """Routing and dispatch in one pass over x (switch_route_dispatch): the
     outputs of route() plus o["dispatched"] [N][C][d]."""
-    _check_router(x, w_router, router_bias)
+    N = _check_router(x, w_router, router_bias, tiled, num_experts)
     T, d = x.shape
-    N = w_router.shape[0]
-    shape = make_shape(T, d, 64, N, capacity_, x.dtype)
+    shape = make_shape(T, d, 64, N, capacity_, x.dtype, tiled)
     dev = x.device
     o = out if out is not None else _route_outputs(T, N, dev)
     _check_route_outputs(o, T, N, dev)
-    ws = _workspace(make_shape(T, d, 64, N, 0, x.dtype), dev, workspace)
+    ws = _workspace(make_shape(T, d, 64, N, 0, x.dtype, tiled), dev, workspace)
     buf = dispatched if dispatched is not None else torch.empty(N, capacity_, d, dtype=x.dtype, device=dev)
     _expect(buf, "dispatched", (N, capacity_, d), x.dtype, dev)
     _check(load_library().switch_route_dispatch(
@@ -351,7 +371,7 @@ def combine(expert_out: torch.Tensor, expert_idx: torch.Tensor, slot: torch.Tens
 
 
 def _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out, tiled=False):
-    _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
+    _check_layer_inputs(x, w_router, router_bias, w_in, w_out, tiled)
     T, d = x.shape
     N, f = w_in.shape[0], w_in.shape[1]
     shape = make_shape(T, d, f, N, capacity_, x.dtype, tiled)
@@ -372,7 +392,8 @@ def layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: torch.Te
                   w_out: torch.Tensor, capacity_: int, add_residual: bool = False,
                   workspace: torch.Tensor | None = None, out: dict | None = None, tiled: bool = False) -> dict:
     """The whole Switch layer forward (switch_layer_forward); tiled: W_in and
-    W_out are in the tiled layout (tile_weights)."""
+    W_out are in the tiled layout (tile_weights) and w_router holds W_r's
+    planes (tile_router)."""
     _, o, args = _lf_args(x, w_router, router_bias, w_in, w_out, capacity_, add_residual, workspace, out, tiled)
     _check(load_library().switch_layer_forward(*args))
     return o
@@ -435,7 +456,7 @@ def layer_forward_noalloc(x: torch.Tensor, w_router: torch.Tensor, router_bias: 
     N, f = w_in.shape[0], w_in.shape[1]
     shape = make_shape(T, d, f, N, capacity_, x.dtype, tiled)
     dev = x.device
-    _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
+    _check_layer_inputs(x, w_router, router_bias, w_in, w_out, tiled)
     o = out if out is not None else _route_outputs(T, N, dev)
     if "y" not in o:
         o["y"] = torch.empty(T, d, dtype=x.dtype, device=dev)
@@ -478,7 +499,7 @@ def topk_layer_forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: tor
                        out: dict | None = None, tiled: bool = False) -> dict:
     """Classic top-k MoE layer, k = 1 or 2 (switch_topk_layer_forward); the
     routing outputs are [top_k][T]."""
-    _check_layer_inputs(x, w_router, router_bias, w_in, w_out)
+    _check_layer_inputs(x, w_router, router_bias, w_in, w_out, tiled)
     T, d = x.shape
     N, f = w_in.shape[0], w_in.shape[1]
     shape = make_shape(T, d, f, N, capacity_, x.dtype, tiled)
@@ -523,6 +544,30 @@ def tile_weights(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
 def untile_weights(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Tiled expert weights -> row-major (switch_untile_weights)."""
     return _tile_call(load_library().switch_untile_weights, w, out)
+
+
+def tiled_router_bytes(num_experts: int, d_model: int) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().switch_tiled_router_bytes(int(num_experts), int(d_model), ctypes.byref(out)))
+    return out.value
+
+
+def tile_router(w_router: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W_r [N][d_model] fp32 -> its exact three-way bf16 split in the router's
+    operand order, the form the layer calls read with tiled=True
+    (switch_tile_router); bf16, shape tiled_router_shape(N, d_model);
+    asynchronous on the current stream."""
+    if not isinstance(w_router, torch.Tensor) or w_router.dim() != 2 or w_router.dtype != torch.float32:
+        raise ValueError("w_router must be a 2-D float32 tensor [num_experts][d_model]")
+    if not w_router.is_contiguous():
+        raise ValueError("w_router must be contiguous")
+    N, d = w_router.shape
+    dev = w_router.device
+    shp = tiled_router_shape(N, d)
+    o = out if out is not None else torch.empty(shp, dtype=torch.bfloat16, device=dev)
+    _expect(o, "out", shp, torch.bfloat16, dev)
+    _check(load_library().switch_tile_router(int(N), int(d), _ptr(w_router), _ptr(o), _stream(dev)))
+    return o
 
 
 def backward_workspace_bytes(shape: Shape) -> int:

@@ -149,7 +149,8 @@ bool tiled(const switch_shape *s) { return s->weight_layout == SWITCH_WEIGHTS_TI
 
 // Workspace of a call with k routes per token: the router's per-block
 // partials (k blocks per router block), the route ranks, the logits rows when
-// the experts do not fit one chunk, W_r's bf16 planes (bf16 layers), then the
+// the experts do not fit one chunk, W_r's bf16 planes (bf16 layers with
+// row-major weights), then the
 // layer's hidden activations and
 // slot maps; k > 1 adds the slot -> output row map and the [k][T][d] buffer of
 // gate-scaled expert outputs per route.
@@ -158,7 +159,10 @@ int layout(const switch_shape *s, Layout &L, int k = 1) {
   const int64_t nb = router_blocks(T) * k, Tp = router_blocks(T) * kRouterTokens * k;
   const int es = esize(s->dtype);
   size_t bc, pp, ps, rk, lg = 0, hid, act, tk, rt = 0, sy, r32, r64;
-  const size_t wpl = s->dtype == SWITCH_BF16 ? (size_t)router_planes_bytes((int)N, (int)d) : 0;
+  // tiled weights: the caller's W_r argument already holds the planes
+  const size_t wpl =
+      s->dtype == SWITCH_BF16 && s->weight_layout != SWITCH_WEIGHTS_TILED ? (size_t)router_planes_bytes((int)N, (int)d)
+                                                                          : 0;
   const int64_t Np = count_stride((int)N), Ns = (N + 63) / 64 * 64;
   bool ok = mul(bc, {nb, Np, 4}) && mul(pp, {nb, Np, 4}) && mul(ps, {N, 4}) && mul(rk, {Tp, 4}) &&
             mul(sy, {nb + 4, 4}) && mul(r32, {nb, Ns, 4}) && mul(r64, {nb, Ns, 8}) &&
@@ -315,7 +319,8 @@ int route_args(const switch_shape *s, const void *x, const float *w_router, cons
   a.w_r = w_router;
   a.bias = router_bias;
   a.logits = (float *)(w + L.logits);
-  a.wplanes = w + L.wplanes;
+  a.wr_planes = tiled(s);  // W_r given as its planes (switch_tile_router)
+  a.wplanes = a.wr_planes ? (void *)w_router : (void *)(w + L.wplanes);
   a.expert_idx = expert_idx;
   a.gate = gate;
   a.slot = slot;
@@ -569,6 +574,30 @@ int tile_call(int32_t count, int32_t rows, int32_t cols, const void *src, void *
   if (a < b + bytes && b < a + bytes) return fail(SWITCH_E_INVALID, "src and dst overlap");
   TileArgs t{count, rows, cols, src, dst, to_tiled};
   return launched(launch_tile_weights(t, (hipStream_t)stream), to_tiled ? "tile launch" : "untile launch", stream);
+}
+
+// W_r [N][d] fp32 -> its three bf16 planes in the router's operand order.
+int tile_router_bytes(int32_t num_experts, int32_t d_model, size_t &bytes) {
+  if (num_experts < 1 || d_model < 1)
+    return fail(SWITCH_E_INVALID, "num_experts = %d and d_model = %d must be >= 1", num_experts, d_model);
+  if (d_model % 64) return fail(SWITCH_E_UNSUPPORTED, "d_model = %d must be a multiple of 64", d_model);
+  size_t wr;
+  if (!mul(wr, {num_experts, d_model, 4}) || !mul(bytes, {(num_experts + 15) / 16, d_model / 32, 3 * 64 * 16}))
+    return fail(SWITCH_E_UNSUPPORTED, "sizes overflow");
+  return SWITCH_OK;
+}
+
+int tile_router(int32_t num_experts, int32_t d_model, const float *w_router, void *planes, void *stream) {
+  size_t bytes;
+  int rc = tile_router_bytes(num_experts, d_model, bytes);
+  if (rc) return rc;
+  NEED(w_router, 16);
+  NEED(planes, 16);
+  const size_t wr = (size_t)num_experts * d_model * 4;
+  const uintptr_t a = (uintptr_t)w_router, b = (uintptr_t)planes;
+  if (a < b + bytes && b < a + wr) return fail(SWITCH_E_INVALID, "w_router and planes overlap");
+  return launched(launch_router_planes(w_router, num_experts, d_model, planes, (hipStream_t)stream),
+                  "tile_router launch", stream);
 }
 
 }  // namespace
@@ -972,6 +1001,17 @@ int switch_tile_weights(int32_t count, int32_t rows, int32_t cols, const void *s
 
 int switch_untile_weights(int32_t count, int32_t rows, int32_t cols, const void *src, void *dst, void *stream) {
   GUARD({ return tile_call(count, rows, cols, src, dst, stream, false); })
+}
+
+int switch_tiled_router_bytes(int32_t num_experts, int32_t d_model, size_t *bytes_out) {
+  GUARD({
+    if (!bytes_out) return fail(SWITCH_E_INVALID, "bytes_out is NULL");
+    return tile_router_bytes(num_experts, d_model, *bytes_out);
+  })
+}
+
+int switch_tile_router(int32_t num_experts, int32_t d_model, const float *w_router, void *planes, void *stream) {
+  GUARD({ return tile_router(num_experts, d_model, w_router, planes, stream); })
 }
 
 int switch_launch_names(const switch_shape *s, const char **names, int32_t max_names, int32_t *num_names) {

@@ -27,6 +27,7 @@ struct RouteArgs {
   const float *w_r, *bias;
   float *logits;  // [T][N] scratch, only used when N > kRouterChunk
   void *wplanes;  // bf16 layers: W_r split into bf16 planes in MFMA fragment order (router_planes_bytes)
+  bool wr_planes = false;  // wplanes is the caller's W_r already in that form (tiled weights): no split pass
   int32_t *expert_idx;
   float *gate;
   int32_t *slot;  // slot of each token (assignment output)
@@ -299,10 +300,14 @@ hipError_t launch_router_wgrad_bf16(const float *dh, const void *x, int64_t T, i
 __host__ __device__ inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
 // Bytes of W_r split into three bf16 planes, laid out in the order the bf16
 // router's MFMA waves load them: [ceil(N / 16)][d / 32][3 planes][64 lanes]
-// pieces of 16 bytes (the router writes them, then reads them, each call).
+// pieces of 16 bytes (written by a split pass before the router of each
+// call, or once by the caller for tiled weights).
 __host__ __device__ inline int64_t router_planes_bytes(int N, int d) {
   return (int64_t)((N + 15) / 16) * (d / 32) * 3 * 64 * 16;
 }
+// Writes those planes of W_r [N][d] fp32 (zeros for the experts past N in the
+// last 16-expert tile).
+hipError_t launch_router_planes(const float *w_r, int N, int d, void *wplanes, hipStream_t st);
 // Row stride (elements) of the per-block count and P-partial arrays: rows
 // start on 16-byte boundaries.
 __host__ __device__ inline int count_stride(int N) { return (N + 3) & ~3; }

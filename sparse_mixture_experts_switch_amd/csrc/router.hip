@@ -549,7 +549,7 @@ __device__ __forceinline__ LogitRows<kLds> router_fwd_contract_bf16(
 
 // W_r split into its three exact bf16 planes (hi + mid + lo, each taking the
 // next 8 significant bits) and laid out in MFMA fragment order, once per
-// call: piece (tile m, step g, plane p, lane l) holds the 8 values of expert
+// call (or once for good, when the caller keeps W_r in this form): piece (tile m, step g, plane p, lane l) holds the 8 values of expert
 // 16 m + l mod 16 (zeros past N) at contraction columns 32 g + 8 (l / 16) ..
 // + 8, so each router wave loads its operands of a step as three contiguous
 // 1 KB pieces (loads whose consecutive lanes read different rows of W_r
@@ -1145,8 +1145,10 @@ hipError_t run_router(const RouteArgs &a, hipStream_t st) {
   const bool lds = a.N <= kRouterChunk;
   const dim3 grid((unsigned)nb);
   if (a.dtype == kBF16) {
-    hipError_t e = launch_router_planes(a.w_r, a.N, a.d, a.wplanes, st);
-    if (e != hipSuccess) return e;
+    if (!a.wr_planes) {
+      hipError_t e = launch_router_planes(a.w_r, a.N, a.d, a.wplanes, st);
+      if (e != hipSuccess) return e;
+    }
     auto kern = lds ? router_fwd_bf16_kernel<true, kK> : router_fwd_bf16_kernel<false, kK>;
     kern<<<grid, dim3(kFwThreads), 0, st>>>((const bf16 *)a.x, (const u32x4 *)a.wplanes, a.bias, a.T, a.d, a.N,
                                             a.logits, a.expert_idx, a.gate, a.rank, a.bcount, a.ppart);
@@ -1460,8 +1462,10 @@ hipError_t launch_route_fused(const FusedRouteArgs &a, hipStream_t st, LaunchMar
     route_sync_clear_kernel<<<dim3((unsigned)std::min<int64_t>(ceil_div(n16, 256), 2048)), dim3(256), 0, st>>>(
         (u32x4 *)a.sync, n16);
     if (a.r.dtype == kBF16) {
-      hipError_t e = launch_router_planes(a.r.w_r, a.r.N, a.r.d, a.r.wplanes, st);
-      if (e != hipSuccess) return e;
+      if (!a.r.wr_planes) {
+        hipError_t e = launch_router_planes(a.r.w_r, a.r.N, a.r.d, a.r.wplanes, st);
+        if (e != hipSuccess) return e;
+      }
       auto kern = lds ? route_fused_bf16_kernel<true> : route_fused_bf16_kernel<false>;
       kern<<<dim3((unsigned)nb), dim3(kFwThreads), 0, st>>>(a);
     } else {

@@ -11,6 +11,7 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle.switch_oracle as so
@@ -190,6 +191,51 @@ def test_tiled_weights_validation():
         smx.tile_weights(torch.zeros(2, 16, 32))  # fp32
     with pytest.raises(ValueError):
         smx.tile_weights(torch.zeros(2, 16, 32, dtype=torch.bfloat16))  # not on a GPU
+
+
+def test_tiled_router_validation():
+    """W_r's tiled form: its byte count from the header's definition, the
+    conversion's host checks (sizes, pointers, overlap), and a tiled layer
+    call's workspace without the split planes a row-major call keeps."""
+    import torch
+    lib = smx.load_library()
+    out = ctypes.c_size_t()
+    for N, d in ((1, 64), (16, 64), (17, 128), (128, 768), (2048, 2048)):
+        assert lib.switch_tiled_router_bytes(N, d, ctypes.byref(out)) == B.SWITCH_OK
+        assert out.value == -(-N // 16) * (d // 32) * 3 * 1024 == 2 * int(np.prod(smx.tiled_router_shape(N, d)))
+    assert lib.switch_tiled_router_bytes(0, 64, ctypes.byref(out)) == B.SWITCH_E_INVALID
+    assert lib.switch_tiled_router_bytes(8, 0, ctypes.byref(out)) == B.SWITCH_E_INVALID
+    assert lib.switch_tiled_router_bytes(8, 96, ctypes.byref(out)) == B.SWITCH_E_UNSUPPORTED
+    assert lib.switch_tiled_router_bytes(8, 64, None) == B.SWITCH_E_INVALID
+    P = ctypes.c_void_p
+    good, other, odd = P(1 << 20), P(1 << 30), P((1 << 20) + 8)
+    fn = lib.switch_tile_router
+    assert fn(0, 64, good, other, None) == B.SWITCH_E_INVALID
+    assert fn(8, 96, good, other, None) == B.SWITCH_E_UNSUPPORTED
+    assert fn(8, 64, None, other, None) == B.SWITCH_E_INVALID
+    assert fn(8, 64, odd, other, None) == B.SWITCH_E_INVALID
+    assert fn(8, 64, good, None, None) == B.SWITCH_E_INVALID
+    # W_r of 8 x 64 fp32 is 2 KB; planes of one 16-expert tile 6 KB
+    assert fn(8, 64, good, P((1 << 20) + 1024), None) == B.SWITCH_E_INVALID
+    assert b"overlap" in lib.switch_last_error()
+    assert fn(8, 64, P((1 << 20) + 4096), good, None) == B.SWITCH_E_INVALID  # W_r inside the planes
+    with pytest.raises(ValueError):
+        smx.tile_router(torch.zeros(8, 64, dtype=torch.bfloat16))  # not fp32
+    with pytest.raises(ValueError):
+        smx.tile_router(torch.zeros(8, 64))  # not on a GPU
+    # the layer's workspace: the split planes only for row-major W_r
+    rows = B.make_shape(16384, 768, 3072, 128, 160, torch.bfloat16)
+    tiled = B.make_shape(16384, 768, 3072, 128, 160, torch.bfloat16, tiled=True)
+    planes = -(-128 // 16) * (768 // 32) * 3 * 1024
+    assert smx.workspace_bytes(rows) - smx.workspace_bytes(tiled) == planes
+    # tiled layer calls check W_r's planes in the binding
+    x = torch.zeros(64, 128, dtype=torch.bfloat16)
+    w_in = torch.zeros(8, 64, 128, dtype=torch.bfloat16)
+    w_out = torch.zeros(8, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="tiled"):
+        smx.layer_forward(x, torch.zeros(8, 128), None, w_in, w_out, 16, tiled=True)  # fp32 W_r
+    with pytest.raises(ValueError, match="num_experts"):
+        smx.route(x, torch.zeros(smx.tiled_router_shape(8, 128), dtype=torch.bfloat16), None, 16, tiled=True)
 
 
 def test_launch_names_follow_the_shape():

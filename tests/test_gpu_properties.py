@@ -5,8 +5,8 @@ tolerances of parity_lib.
 Shapes: T in [0, 700], d_model in {64, 128, 192, 256, 768} and d_ff in
 {64, 128, 256, 384} (the streaming expert kernels, and the fused one at
 d_model 128 / 256), N in {1, 2, 3, 8, 128, 2048}, capacity factor in
-{0.5, 1, 1.25, N}, fp32 or bf16 (bf16 with row-major or tiled expert
-weights), router bias absent, Zipf-skewed or pinned to one expert, with or
+{0.5, 1, 1.25, N}, fp32 or bf16 (bf16 with row-major or tiled weights:
+the router's planes and the expert matrices), router bias absent, Zipf-skewed or pinned to one expert, with or
 without the residual.  The sweep is derandomized (the same cases on every
 run) and makes one pass without shrinking: it stops at the first failing
 case and prints it.
@@ -56,11 +56,10 @@ def test_layer_forward_matches_oracle_on_random_shapes(case):
         b[cfg.seed % cfg.num_experts] = 30.0
         inp["router_bias"] = b.to(DEV)
     C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
-    w_in, w_out = inp["w_in"], inp["w_out"]
+    w_r, w_in, w_out = inp["w_router"], inp["w_in"], inp["w_out"]
     if tiled:
-        w_in, w_out = smx.tile_weights(w_in), smx.tile_weights(w_out)
-    o = smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], w_in, w_out, C, add_residual=residual,
-                          tiled=tiled)
+        w_r, w_in, w_out = smx.tile_router(w_r), smx.tile_weights(w_in), smx.tile_weights(w_out)
+    o = smx.layer_forward(inp["x"], w_r, inp["router_bias"], w_in, w_out, C, add_residual=residual, tiled=tiled)
     torch.cuda.synchronize()
     g = gpu_outputs_numpy(o)
     own = oracle_run(inp, C, experts=[])

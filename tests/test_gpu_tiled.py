@@ -1,9 +1,14 @@
-"""GPU checks of the tiled expert-weight layout (switch_tile_weights /
-switch_untile_weights, and every layer call with weight_layout tiled).
+"""GPU checks of the tiled weight layout (switch_tile_weights /
+switch_untile_weights, switch_tile_router, and every layer call with
+weight_layout tiled).
 
 * The conversion against the layout's definition in include/switch_moe.h,
   computed here in numpy element by element: bit-exact; and the round trip
   untile(tile(w)) == w.
+* The router's planes: in numpy, each piece's 8 values at the position the
+  header defines, each plane a bf16 value with at most 8 significant bits
+  of the remainder left by the planes before it, hi + mid + lo == W_r
+  exactly (in float64), zeros for the padding experts.
 * The layer with tiled weights against the same call with row-major weights
   on the same inputs: every output bit-identical (the tiled layout only moves
   each weight to where the same matrix-core operand lane reads it), on the
@@ -91,7 +96,47 @@ CASES = {
 
 
 def _tiled(inp):
-    return smx.tile_weights(inp["w_in"]), smx.tile_weights(inp["w_out"])
+    """The three weights in the tiled layout: W_r's planes, W_in, W_out."""
+    return smx.tile_router(inp["w_router"]), smx.tile_weights(inp["w_in"]), smx.tile_weights(inp["w_out"])
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("N,d", [(1, 64), (16, 64), (20, 128), (128, 768), (2048, 2048)])
+def test_tile_router_matches_definition(N, d):
+    say(f"tile_router N={N} d={d}")
+    gen = torch.Generator().manual_seed(N * 31 + d)
+    w = torch.randn(N, d, generator=gen, dtype=torch.float64)
+    # values across many binades, exact zeros and a few tiny magnitudes
+    w = (w * torch.exp2(torch.randint(-30, 8, (N, d), generator=gen).double())).float()
+    w[0, :5] = 0.0
+    w = w.to(DEV)
+    planes = smx.tile_router(w)
+    torch.cuda.synchronize()
+    assert tuple(planes.shape) == smx.tiled_router_shape(N, d)
+    assert smx.tiled_router_bytes(N, d) == planes.numel() * 2
+    b = planes.view(torch.int16).cpu().numpy().view(np.uint16)  # [tiles][d/32][3][64][8]
+    # piece (m, g, plane, lane l) holds expert 16 m + l % 16, columns 32 g + 8 (l / 16) .. + 7
+    tiles, steps = b.shape[0], b.shape[1]
+    m = np.arange(tiles)[:, None, None, None]
+    g = np.arange(steps)[None, :, None, None]
+    lane = np.arange(64)[None, None, :, None]
+    k = np.arange(8)[None, None, None, :]
+    row = 16 * m + lane % 16
+    col = 32 * g + 8 * (lane // 16) + k
+    wr = w.double().cpu().numpy()
+    want = np.where(row < N, wr[np.minimum(row, N - 1), col], 0.0)
+    hi, mid, lo = (bf16_bits_to_f64(b[:, :, p]) for p in range(3))
+    assert np.array_equal(hi + mid + lo, want)  # exact: each sum below is exact in float64
+    # each plane holds the leading 8 significant bits of what the earlier planes left
+    for part, rest in ((hi, want), (mid, want - hi), (lo, want - hi - mid)):
+        nz = rest != 0
+        _, ex = np.frexp(np.where(nz, rest, 1.0))
+        # |rest - part| < one unit in the 8th significant bit of rest
+        assert np.all(np.abs(rest - part)[nz] < np.ldexp(1.0, ex[nz] - 8))
+        assert np.all(part[~nz] == 0)
 
 
 def _same(a: dict, b: dict, keys, label):
@@ -109,36 +154,49 @@ def test_layer_tiled_is_bit_identical(name):
     say(f"tiled layer {name}: {cfg}")
     inp = make_inputs(cfg, device=DEV)
     C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
-    wi, wo = _tiled(inp)
+    wr, wi, wo = _tiled(inp)
     args = (inp["x"], inp["w_router"], inp["router_bias"])
+    targs = (inp["x"], wr, inp["router_bias"])
     for res in (False, True):
         a = smx.layer_forward(*args, inp["w_in"], inp["w_out"], C, add_residual=res)
-        b = smx.layer_forward(*args, wi, wo, C, add_residual=res, tiled=True)
+        b = smx.layer_forward(*targs, wi, wo, C, add_residual=res, tiled=True)
         torch.cuda.synchronize()
         _same(a, b, ROUTE_KEYS + ("y",), f"{name} residual={res}")
     if name.startswith("fused") or name == "stream_ragged":
         a = smx.layer_forward_train(*args, inp["w_in"], inp["w_out"], C)
-        b = smx.layer_forward_train(*args, wi, wo, C, tiled=True)
+        b = smx.layer_forward_train(*targs, wi, wo, C, tiled=True)
         gamma = torch.linspace(0.5, 1.5, cfg.d_model, device=DEV)
         beta = torch.linspace(-0.1, 0.1, cfg.d_model, device=DEV)
         c = smx.layer_forward_add_norm(*args, inp["w_in"], inp["w_out"], C, gamma, beta, 1e-5)
-        d = smx.layer_forward_add_norm(*args, wi, wo, C, gamma, beta, 1e-5, tiled=True)
+        d = smx.layer_forward_add_norm(*targs, wi, wo, C, gamma, beta, 1e-5, tiled=True)
         torch.cuda.synchronize()
         _same(a, b, ("y",), f"{name} train")
         _same(c, d, ("y",), f"{name} add_norm")
     if name in ("base", "fused_d256_drops"):
         C2 = smx.capacity(2 * cfg.tokens, cfg.num_experts, cfg.capacity_factor)
         a = smx.topk_layer_forward(*args, inp["w_in"], inp["w_out"], C2, top_k=2)
-        b = smx.topk_layer_forward(*args, wi, wo, C2, top_k=2, tiled=True)
+        b = smx.topk_layer_forward(*targs, wi, wo, C2, top_k=2, tiled=True)
         torch.cuda.synchronize()
         _same(a, b, ROUTE_KEYS + ("y",), f"{name} top-2")
+    if name in ("base", "stream_d192_drops"):
+        # the stage calls that route: the same outputs from W_r's planes
+        N = cfg.num_experts
+        a = smx.route(*args, C)
+        b = smx.route(*targs, C, tiled=True, num_experts=N)
+        c = smx.route_dispatch(*args, C)
+        d = smx.route_dispatch(*targs, C, tiled=True, num_experts=N)
+        torch.cuda.synchronize()
+        _same(a, b, ROUTE_KEYS, f"{name} route")
+        _same(c, d, ROUTE_KEYS, f"{name} route_dispatch")
+        for e, n in enumerate(c["expert_count"].clamp(max=C).tolist()):  # live rows of the expert buffers
+            assert torch.equal(c["dispatched"][e, :n].view(torch.int16), d["dispatched"][e, :n].view(torch.int16))
 
 
 def test_expert_ffn_and_noalloc_tiled():
     cfg = CASES["stream_ragged"]
     inp = make_inputs(cfg, device=DEV)
     C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
-    wi, wo = _tiled(inp)
+    wr, wi, wo = _tiled(inp)
     r = smx.route(inp["x"], inp["w_router"], inp["router_bias"], C)
     disp = smx.dispatch(inp["x"], r["expert_idx"], r["slot"], r["dropped"], cfg.num_experts, C)
     a = smx.expert_ffn(disp, r["expert_count"], inp["w_in"], inp["w_out"])
@@ -150,7 +208,7 @@ def test_expert_ffn_and_noalloc_tiled():
     if smx.noalloc_scratch_bytes() >= smx.workspace_bytes(smx.binding.make_shape(
             cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts, C, cfg.torch_dtype)):
         c = smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C)
-        d = smx.layer_forward_noalloc(inp["x"], inp["w_router"], inp["router_bias"], wi, wo, C, tiled=True)
+        d = smx.layer_forward_noalloc(inp["x"], wr, inp["router_bias"], wi, wo, C, tiled=True)
         torch.cuda.synchronize()
         _same(c, d, ROUTE_KEYS + ("y",), "noalloc")
 
@@ -160,8 +218,8 @@ def test_layer_tiled_against_oracle():
     cfg = CASES["stream_d192_drops"]
     inp = make_inputs(cfg, device=DEV)
     C = smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
-    wi, wo = _tiled(inp)
-    o = smx.layer_forward(inp["x"], inp["w_router"], inp["router_bias"], wi, wo, C, tiled=True)
+    wr, wi, wo = _tiled(inp)
+    o = smx.layer_forward(inp["x"], wr, inp["router_bias"], wi, wo, C, tiled=True)
     torch.cuda.synchronize()
     g = gpu_outputs_numpy(o)
     own = oracle_run(inp, C, experts=[])
@@ -189,10 +247,10 @@ def test_layer_tiled_edges(name, cfg, cap):
     say(f"tiled edge {name}: {cfg} capacity {cap}")
     inp = make_inputs(cfg, device=DEV)
     C = cap if cap is not None else smx.capacity(cfg.tokens, cfg.num_experts, cfg.capacity_factor)
-    wi, wo = _tiled(inp)
+    wr, wi, wo = _tiled(inp)
     args = (inp["x"], inp["w_router"], inp["router_bias"])
     a = smx.layer_forward(*args, inp["w_in"], inp["w_out"], C, add_residual=True)
-    b = smx.layer_forward(*args, wi, wo, C, add_residual=True, tiled=True)
+    b = smx.layer_forward(inp["x"], wr, inp["router_bias"], wi, wo, C, add_residual=True, tiled=True)
     torch.cuda.synchronize()
     _same(a, b, ROUTE_KEYS + ("y",), name)
     assert int(a["expert_count"].max()) > 0
