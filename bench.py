@@ -191,11 +191,14 @@ def backward_alg_bytes(T: int, d: int, f: int, N: int, C: int, counts, splits: i
     }
 
 
-def backward_bench(smx, torch, inp, out, ws, C, cfg, stream, steps: int) -> dict:
+def backward_bench(smx, torch, inp, out, C, cfg, stream, steps: int) -> dict:
     T, d, f, N = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.num_experts
     dev = inp["x"].device
     shape = smx.binding.make_shape(T, d, f, N, C, cfg.torch_dtype)
     bws = torch.empty(smx.backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    # the training forward's own workspace: row-major weights (the layer
+    # timed above may run on tiled ones, whose workspace has no W_r planes)
+    ws = torch.empty(smx.workspace_bytes(shape), dtype=torch.uint8, device=dev)
     g = torch.Generator().manual_seed(5)
     dy = torch.randn(T, d, generator=g).to(cfg.torch_dtype).to(dev)
     grads = {}
@@ -717,7 +720,9 @@ def main() -> int:
     # FFN as two products, the hidden activations saved for the backward)
     train_ms = None
     if "stages" in sections:
-        tws = torch.empty_like(ws)
+        # row-major weights: the workspace also holds W_r's split planes
+        tws = torch.empty(smx.workspace_bytes(smx.binding.make_shape(T, d, f, N, C, cfg.torch_dtype)),
+                          dtype=torch.uint8, device=dev)
         tout = {k: torch.empty_like(v) for k, v in out.items()}
         tcall = lambda: smx.layer_forward_train(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"],  # noqa: E731
                                                 inp["w_out"], C, workspace=tws, out=tout)
@@ -771,7 +776,7 @@ def main() -> int:
     diag = mfma_diag_bench(smx, torch, cfg, stream, args.steps, tiled) if "mfma_diag" in sections else None
     bwd = None
     if "backward" in sections:
-        bwd = backward_bench(smx, torch, inp, out, ws, C, cfg, stream, args.steps)
+        bwd = backward_bench(smx, torch, inp, out, C, cfg, stream, args.steps)
         log("bench: backward " + f"{bwd['ms']:.4f} ms; per-kernel ms " +
             ", ".join(f"{k}={v['ms']:.4f}" for k, v in bwd["kernels"].items()))
     per_kernel = {}

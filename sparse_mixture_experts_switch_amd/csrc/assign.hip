@@ -245,23 +245,23 @@ __global__ void route_empty_kernel(int N, int32_t *__restrict__ expert_count, fl
 }
 
 // ---------------------------------------------------------------------------
-// One-launch assignment for batches whose block count is small: workgroup a
-// owns router block a (64 routes).  It sums the counts of all blocks before
-// its own (16-byte loads, kAsBatch rows in flight per thread, 16 row groups,
-// then the group sums in ascending order: exact integers) for its offsets,
-// and assigns its routes.  Workgroup 0, whose offsets are all zero, sums the
-// counts and the P partials of every block instead and forms the totals, the
-// P sums and the loss.  Every global load a workgroup makes (its routes'
-// expert, rank and gate, the rows it sums) is issued before its first
-// barrier, so it waits for memory once; the stores follow.  One router block
-// per workgroup: the busiest workgroup reads the same prefix as with larger
-// groups, and the route work (slots, maps, the rows of dropped tokens)
-// spreads over more CUs (base workload 11.5 -> 10.3 us, large-shaped with
-// 49% drops 21.5 -> 12.9 us, against four blocks per workgroup).
+// One-launch assignment for batches whose block count is small.  Workgroup a
+// owns router blocks [kAsBlocks a, kAsBlocks (a + 1)).  It sums the counts of
+// all blocks before its own (16-byte loads, kAsBatch rows in flight per
+// thread, 16 row groups, then the group sums in ascending order: exact
+// integers), adds its own blocks' counts one by one for the offsets of each,
+// and assigns its tokens.  One router block (64 tokens) per workgroup: the
+// busiest workgroup reads the same prefix as with larger groups, and the
+// token work (slots, maps, the rows of dropped tokens) spreads over four times
+// the CUs (base workload 11.5 -> 10.3 us, large-shaped with 49% drops 21.5 ->
+// 12.9 us, against four blocks per workgroup).  The workgroup holding the last block also reads the P
+// partials of every block and forms the totals, the P sums and the loss.
 // ---------------------------------------------------------------------------
 constexpr int kAsThreads = 512;
-constexpr int kAsGroups = kAsThreads / 32;  // row groups (32 lanes x 4 experts per row)
-constexpr int kAsChunk = 128;               // experts per pass
+constexpr int kAsBlocks = 1;                          // router blocks per workgroup
+constexpr int kAsTokens = kAsBlocks * kRouterTokens;  // tokens per workgroup
+constexpr int kAsGroups = kAsThreads / 32;            // row groups (32 lanes x 4 experts per row)
+constexpr int kAsChunk = 128;                         // experts per pass
 constexpr int kAsBatch = 16;
 
 struct AssignArgs {
@@ -288,69 +288,55 @@ struct AssignArgs {
 };
 
 size_t assign_one_smem(int N) {
-  return (size_t)N * 4 + (size_t)N * 4 + 2 * (size_t)kAsGroups * kAsChunk * 4 + kAsThreads * 8;
+  return (size_t)kAsBlocks * N * 4 + (size_t)N * 4 + 2 * (size_t)kAsGroups * kAsChunk * 4 + kAsThreads * 8;
 }
 
 __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs p) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const int N = p.N;
-  int *s_off = (int *)dsm;                                 // [N] offsets (workgroup 0: totals)
-  float *s_q = (float *)(s_off + N);                       // [N] workgroup 0: P sums
+  int *s_off = (int *)dsm;                                 // [kAsBlocks][N]
+  float *s_q = (float *)(s_off + kAsBlocks * N);           // [N] P partial sums of the blocks before r0
   int *s_part = (int *)(s_q + N);                          // [kAsGroups][kAsChunk]
   float *s_pq = (float *)(s_part + kAsGroups * kAsChunk);  // [kAsGroups][kAsChunk]
   double *s_acc = (double *)(s_pq + kAsGroups * kAsChunk); // [kAsThreads]
   const int tid = threadIdx.x, jq = tid % 32, rg = tid / 32;
   const int64_t Np = count_stride(N);
-  const int64_t r0 = blockIdx.x;
-  const bool totals = r0 == 0;           // sums every block, for the totals and the loss
-  const int64_t rows = totals ? p.nb : r0;  // rows summed: the prefix, or all
+  const int64_t r0 = (int64_t)blockIdx.x * kAsBlocks, r1 = min(r0 + kAsBlocks, p.nb);
+  const bool last = r1 == p.nb;
 
-  // 0. this workgroup's routes: expert, in-block rank and gate, loaded first
-  const int64_t j = r0 * kRouterTokens + tid;
-  int64_t t = 0, o = 0;
-  const bool mine = tid < kRouterTokens && j < p.nb * kRouterTokens && virt_token(j, p.T, p.Tp, p.k, t, o);
-  int e = 0, rk = 0;
-  float g = 0.f;
-  if (mine) {
-    e = p.expert_idx[o];
-    rk = p.rank[j];
-    if (p.tok) g = p.gate[o];
-  }
-
-  // 1. counts (and, for the totals, P partials) of the rows summed
+  // 1. counts (and, for the last group, P partials) of blocks [0, r0)
   for (int c0 = 0; c0 < N; c0 += kAsChunk) {
     const int j4 = c0 + 4 * jq;
     const bool act = j4 < N;  // Np % 4 == 0: the 4 columns from j4 lie inside the row
     int c[4] = {0, 0, 0, 0};
     float q[4] = {0.f, 0.f, 0.f, 0.f};
-    // kAsBatch rows per row group at a time, rows b, b + kAsGroups, ...
-    auto batch = [&](int64_t b) {
-      u32x4 cv[kAsBatch];
-      f32x4 pv[kAsBatch];
+    if (act) {
+      for (int64_t b = rg; b < r0; b += (int64_t)kAsGroups * kAsBatch) {
+        u32x4 cv[kAsBatch];
 #pragma unroll
-      for (int i = 0; i < kAsBatch; ++i)  // clamped past the rows: a row that exists, never added
-        cv[i] = *(const u32x4 *)(p.bcount + min(b + (int64_t)i * kAsGroups, rows - 1) * Np + j4);
-      if (totals) {
+        for (int i = 0; i < kAsBatch; ++i)  // clamped past r0: a row that exists, never added
+          cv[i] = *(const u32x4 *)(p.bcount + min(b + (int64_t)i * kAsGroups, r0 - 1) * Np + j4);
 #pragma unroll
         for (int i = 0; i < kAsBatch; ++i)
-          pv[i] = *(const f32x4 *)(p.ppart + min(b + (int64_t)i * kAsGroups, rows - 1) * Np + j4);
-      }
+          if (b + (int64_t)i * kAsGroups < r0) {
 #pragma unroll
-      for (int i = 0; i < kAsBatch; ++i)
-        if (b + (int64_t)i * kAsGroups < rows) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) c[k] += (int)cv[i][k];
-          if (totals) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) q[k] += pv[i][k];
+            for (int k = 0; k < 4; ++k) c[k] += (int)cv[i][k];
           }
+      }
+      if (last) {
+        for (int64_t b = rg; b < r0; b += (int64_t)kAsGroups * kAsBatch) {
+          f32x4 pv[kAsBatch];
+#pragma unroll
+          for (int i = 0; i < kAsBatch; ++i)
+            pv[i] = *(const f32x4 *)(p.ppart + min(b + (int64_t)i * kAsGroups, r0 - 1) * Np + j4);
+#pragma unroll
+          for (int i = 0; i < kAsBatch; ++i)
+            if (b + (int64_t)i * kAsGroups < r0) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) q[k] += pv[i][k];
+            }
         }
-    };
-    // the first batch outside the loop (the common case has one): at a loop
-    // head the compiler waits for every load in flight, the routes' included
-    if (act && rows > rg) {
-      batch(rg);
-      for (int64_t b = rg + (int64_t)kAsGroups * kAsBatch; b < rows; b += (int64_t)kAsGroups * kAsBatch) batch(b);
+      }
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -362,9 +348,9 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
       int off = 0;
       float qs = 0.f;
 #pragma unroll
-      for (int gg = 0; gg < kAsGroups; ++gg) {
-        off += s_part[gg * kAsChunk + tid];
-        qs += s_pq[gg * kAsChunk + tid];
+      for (int g = 0; g < kAsGroups; ++g) {
+        off += s_part[g * kAsChunk + tid];
+        qs += s_pq[g * kAsChunk + tid];
       }
       s_off[c0 + tid] = off;
       s_q[c0 + tid] = qs;
@@ -372,31 +358,40 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
     __syncthreads();
   }
 
-  // 2. the totals, the P sums and the loss's terms (workgroup 0)
-  if (totals) {
-    double acc = 0.0;
-    for (int jj = tid; jj < N; jj += kAsThreads) {
-      const int run = s_off[jj];
-      const float qs = s_q[jj];
-      p.expert_count[jj] = run;
-      p.psum[jj] = qs;
+  // 2. offsets of each of this group's blocks; the last group's totals
+  double acc = 0.0;
+  for (int j = tid; j < N; j += kAsThreads) {
+    int run = s_off[j];
+    float qs = s_q[j];
+    for (int64_t b = r0; b < r1; ++b) {
+      s_off[(b - r0) * N + j] = run;
+      run += p.bcount[b * Np + j];
+      if (last) qs += p.ppart[b * Np + j];
+    }
+    if (last) {
+      p.expert_count[j] = run;
+      p.psum[j] = qs;
       acc += (double)run * (double)qs;
     }
-    s_acc[tid] = acc;
   }
+  if (last) s_acc[tid] = acc;
+  __syncthreads();
 
-  // 3. routes: slot = offset of the block for the route's expert + in-block rank
+  // 3. routes: slot = offset of the route's block for its expert + in-block rank
+  const int64_t j = r0 * kRouterTokens + tid;
   const int lane = tid % kWave;
   bool drop = false;
-  if (mine) {
-    const int sl = (totals ? 0 : s_off[e]) + rk;
+  int64_t t, o;
+  if (tid < kAsTokens && j < p.nb * kRouterTokens && virt_token(j, p.T, p.Tp, p.k, t, o)) {
+    const int e = p.expert_idx[o];
+    const int sl = s_off[(tid / kRouterTokens) * N + e] + p.rank[j];
     p.slot[o] = sl;
     drop = sl >= p.C;
     p.dropped[o] = drop ? 1 : 0;
     if (!drop && p.tok) {
       p.tok[(int64_t)e * p.C + sl] = (int32_t)t;
       if (p.rows) p.rows[(int64_t)e * p.C + sl] = (int32_t)o;
-      p.gmap[(int64_t)e * p.C + sl] = g;
+      p.gmap[(int64_t)e * p.C + sl] = p.gate[o];
     }
   }
   if (p.y) {
@@ -431,8 +426,7 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
   }
 
   // 4. loss = N * sum_i (count_i / (k T)) (psum_i / T), reduced in double in a fixed order
-  if (totals) {
-    __syncthreads();
+  if (last) {
     for (int w = kAsThreads / 2; w > 0; w >>= 1) {
       if (tid < w) s_acc[tid] += s_acc[tid + w];
       __syncthreads();
@@ -448,7 +442,8 @@ __global__ __launch_bounds__(kAsThreads) void assign_one_kernel(const AssignArgs
 // One launch while the prefix rows all workgroups read stay below 64 MB in
 // total (base workload: 256 blocks x 128 experts, 16.8 MB).
 bool assign_single_launch(int64_t nb, int N) {
-  const double reads = 0.5 * (double)nb * (double)nb * (double)count_stride(N) * 4.0;
+  const int64_t groups = ceil_div(nb, kAsBlocks);
+  const double reads = 0.5 * (double)groups * (double)(groups * kAsBlocks) * (double)count_stride(N) * 4.0;
   return nb > 0 && reads <= 64.0 * (1 << 20) && assign_one_smem(N) <= 64 * 1024;
 }
 
@@ -474,7 +469,7 @@ hipError_t launch_assign(const RouteArgs &a, const LayerMaps &m, hipStream_t st,
                  a.expert_count, a.psum, a.aux_loss, a.gate, m.tok, m.rows, m.gmap, (const u32x4 *)m.xres, y, row16,
                  a.dtype == kBF16, m.gamma, m.beta, m.eps};
     for (int r = reps(); r > 0; --r)
-      assign_one_kernel<<<dim3((unsigned)nb), dim3(kAsThreads), assign_one_smem(a.N), st>>>(p);
+      assign_one_kernel<<<dim3((unsigned)ceil_div(nb, kAsBlocks)), dim3(kAsThreads), assign_one_smem(a.N), st>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     mark("assign");
     return hipSuccess;
