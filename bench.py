@@ -202,13 +202,15 @@ def backward_bench(smx, torch, inp, out, C, cfg, stream, steps: int) -> dict:
     g = torch.Generator().manual_seed(5)
     dy = torch.randn(T, d, generator=g).to(cfg.torch_dtype).to(dev)
     grads = {}
-    # the forward of a training step leaves the hidden activations that the
-    # backward reads in its workspace
-    smx.layer_forward_train(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C,
-                            workspace=ws, out=out)
     args = (inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C, out, ws, dy, 0.01)
     call = lambda: smx.layer_backward(*args, workspace=bws, out=grads)  # noqa: E731
+    torch.cuda.synchronize()  # dy's copy (default stream) is done before the stream reads it
     with torch.cuda.stream(stream):
+        # the forward of a training step, on the stream the backward runs on:
+        # it leaves the token maps and hidden activations that the backward
+        # reads in the workspace (allocated just above, so unwritten before)
+        smx.layer_forward_train(inp["x"], inp["w_router"], inp["router_bias"], inp["w_in"], inp["w_out"], C,
+                                workspace=ws, out=out)
         call()
         t_warm = time.perf_counter()
         while time.perf_counter() - t_warm < MIN_WARMUP_S:
@@ -312,6 +314,7 @@ def mfma_diag_bench(smx, torch, cfg, stream, steps: int, tiled: bool) -> dict:
         inp["x"], w_r, inp["router_bias"], inp["w_in"], inp["w_out"], C, first_kernel=lo,
         last_kernel=hi, workspace=ws, out=out, tiled=tiled)
     kern = {}
+    torch.cuda.synchronize()  # inputs made on the default stream are ready for the layer's stream
     with torch.cuda.stream(stream):
         t_warm = time.perf_counter()
         while time.perf_counter() - t_warm < MIN_WARMUP_S:
@@ -402,6 +405,7 @@ def measure_layer(smx, torch, cfg, inp, stream, steps: int, warmup: int, kernels
     # lines whose write-back the next step would pay); events bracket the
     # layer call only
     scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()  # filled (default stream) before the layer's stream reads it
     cold = []
     with torch.cuda.stream(stream):
         for _ in range(steps):
@@ -677,6 +681,7 @@ def main() -> int:
     ystage = torch.empty(T, d, dtype=cfg.torch_dtype, device=dev)
     rstage = {k: torch.empty_like(v) for k, v in out.items() if k != "y"}
     stage_ms = {}
+    torch.cuda.synchronize()  # gamma and beta (filled on the default stream) are ready
     stage_fns = () if "stages" not in sections else (
         ("dispatch", lambda: smx.dispatch(inp["x"], out["expert_idx"], out["slot"], out["dropped"], N, C,
                                           out=disp)),
