@@ -434,6 +434,7 @@ int layer_forward(const switch_shape *s, int32_t k, const void *x, const float *
   GemmCall down{s->dtype, s->num_experts, s->capacity, s->d_ff, s->d_model, w + L.lf_hidden, w_out, routed,
                 expert_count, k == 1 ? maps.tok : maps.rows, gate, maps.gmap, k == 1 && !norm ? xres : nullptr,
                 tiled(s)};
+  down.out_rows = (int64_t)k * s->tokens;
   for (int r = tm.reps(); r > 0; --r)
     if ((e = launch_ffn_down_combine(down, st)) != hipSuccess) return hip_fail(e, "ffn_down launch");
   tm.mark("ffn_down");

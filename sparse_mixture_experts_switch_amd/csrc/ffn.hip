@@ -103,11 +103,15 @@ __device__ __forceinline__ int xcd_tile(int b, int grid) {
 // tiled weights are loaded nontemporally, leaving the 256 MB last-level
 // cache to the hidden activations and token rows that the other product
 // re-reads (measured on both products together; either alone gains
-// nothing), and the results are stored nontemporally, written back as they
-// go instead of left dirty in L2 for the next kernel to wait behind.  With
-// several row tiles per expert the tiles re-read the expert's weights and
-// the down-projection re-reads H from cache: ordinary loads and stores.
-template <int MB, int NBW, int WAVES, bool kGather, int kEpi, bool kTiled, bool kStream, bool kSkipDead = true>
+// nothing).  kNtOut: the results are stored nontemporally, written back as
+// they go instead of left dirty in L2, whose evictions would then mix
+// write-backs into the weight stream (H, and y when it outgrows the L2s);
+// results that fit the L2s are better stored normally and written back in
+// one piece when the kernel ends.  With several row tiles per expert the
+// tiles re-read the expert's weights and the down-projection re-reads H
+// from cache: ordinary loads and stores.
+template <int MB, int NBW, int WAVES, bool kGather, int kEpi, bool kTiled, bool kStream, bool kNtOut,
+          bool kSkipDead = true>
 __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArgs<bf16> p) {
   constexpr int kThreads = WAVES * 64;
   constexpr int kRows = MB * 16;
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
 
     // ---- epilogue of `cur` ----
     auto put = [&](bf16 *dst, const bf16x8 &o) {
-      if (kStream)
+      if (kNtOut)
         __builtin_nontemporal_store(as_u32x4(o), (u32x4 *)dst);
       else
         *(u32x4 *)dst = as_u32x4(o);
@@ -553,13 +557,29 @@ unsigned persistent_grid(Kern kern, int ntiles, std::atomic<int> (&occ_cache)[kM
   return (unsigned)std::max<int64_t>(8, ceil_div(want, 8) * 8);
 }
 
-template <int MB, int NBW, bool kGather, int kEpi, bool kTiled, bool kStream>
+template <int MB, int NBW, bool kGather, int kEpi, bool kTiled, bool kStream, bool kNtOut>
 hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
   static std::atomic<int> occ[kMaxDeviceCache];
   auto g = make_args<bf16>(c, MB * 16, kWaves * 16 * NBW);
-  auto kern = ffn_gemm_bf16_kernel<MB, NBW, kWaves, kGather, kEpi, kTiled, kStream>;
+  auto kern = ffn_gemm_bf16_kernel<MB, NBW, kWaves, kGather, kEpi, kTiled, kStream, kNtOut>;
   kern<<<dim3(persistent_grid(kern, g.ntiles, occ)), dim3(kWaves * 64), 0, st>>>(g);
   return hipGetLastError();
+}
+
+// Rows of y that the combine stores normally when streaming: y of at most
+// 28 MiB fits the eight XCDs' 4 MiB L2s with room to spare.  Measured with
+// tiled weights, back to back / cold: 16384 tokens x d_model 768 (24 MiB of
+// y) 277 -> 273 / 283 -> 277.5 us with ordinary stores; 16384 x 1024 (32
+// MiB) 307 -> 310 / 311 -> 314 us and 8192 x 4096 (64 MiB) 2050 -> 2081 /
+// 2044 -> 2078 us, so nontemporal there.
+constexpr int64_t kKeepOutBytes = int64_t(28) << 20;
+
+template <int MB, int NBW, bool kGather, int kEpi, bool kTiled>
+hipError_t run_bf16_stream(const GemmCall &c, hipStream_t st) {
+  if constexpr (kEpi == kEpiCombine) {
+    if (c.out_rows * c.Nout * 2 <= kKeepOutBytes) return run_bf16<MB, NBW, kGather, kEpi, kTiled, true, false>(c, st);
+  }
+  return run_bf16<MB, NBW, kGather, kEpi, kTiled, true, true>(c, st);
 }
 
 // Row tiles per expert: one unless the capacity exceeds the largest tile
@@ -572,10 +592,10 @@ hipError_t run_bf16(const GemmCall &c, hipStream_t st) {
   bool stream = true;
   if constexpr (MB == kMaxMB) stream = ceil_div(c.C, MB * 16) == 1;
   if (c.tiled)
-    return stream ? run_bf16<MB, NBW, kGather, kEpi, true, true>(c, st)
-                  : run_bf16<MB, NBW, kGather, kEpi, true, false>(c, st);
-  return stream ? run_bf16<MB, NBW, kGather, kEpi, false, true>(c, st)
-                : run_bf16<MB, NBW, kGather, kEpi, false, false>(c, st);
+    return stream ? run_bf16_stream<MB, NBW, kGather, kEpi, true>(c, st)
+                  : run_bf16<MB, NBW, kGather, kEpi, true, false, false>(c, st);
+  return stream ? run_bf16_stream<MB, NBW, kGather, kEpi, false>(c, st)
+                : run_bf16<MB, NBW, kGather, kEpi, false, false, false>(c, st);
 }
 
 // Column blocks per wave.  Both widths stream every weight byte once and run

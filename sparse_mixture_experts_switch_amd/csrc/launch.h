@@ -107,6 +107,7 @@ struct GemmCall {
   const float *gmap;   // [N][C]: gate of the token in each live slot (combine)
   const void *xres;    // [T][Nout] residual rows (combine), may be null
   bool tiled = false;  // B in MFMA operand order (bf16), see tile_weights
+  int64_t out_rows = 0;  // combine: rows of y (its size decides the store policy)
 };
 
 // Compute units of the current device, queried once per device (256 when the

@@ -18,11 +18,11 @@ from sparse_mixture_experts_switch_amd import profsummary as ps
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# <MB, NBW, waves, gather, epilogue, tiled, stream, skip>: tiled weights; then row-major
-UP = "_ZN3smx20ffn_gemm_bf16_kernelILi10ELi3ELi8ELb1ELi0ELb1ELb1ELb1EEEvNS_8GemmArgsIDF16bEE"
-DOWN = "_ZN3smx20ffn_gemm_bf16_kernelILi10ELi3ELi8ELb0ELi2ELb1ELb1ELb1EEEvNS_8GemmArgsIDF16bEE"
-UP_ROWS = "_ZN3smx20ffn_gemm_bf16_kernelILi10ELi3ELi8ELb1ELi0ELb0ELb1ELb1EEEvNS_8GemmArgsIDF16bEE"
-DOWN_ROWS = "void smx::ffn_gemm_bf16_kernel<10, 3, 8, false, 2, false, true, true>(smx::GemmArgs<__bf16>)"
+# <MB, NBW, waves, gather, epilogue, tiled, stream, nontemporal results, skip>: tiled weights; then row-major
+UP = "_ZN3smx20ffn_gemm_bf16_kernelILi10ELi3ELi8ELb1ELi0ELb1ELb1ELb1ELb1EEEvNS_8GemmArgsIDF16bEE"
+DOWN = "_ZN3smx20ffn_gemm_bf16_kernelILi10ELi3ELi8ELb0ELi2ELb1ELb1ELb0ELb1EEEvNS_8GemmArgsIDF16bEE"
+UP_ROWS = "_ZN3smx20ffn_gemm_bf16_kernelILi10ELi3ELi8ELb1ELi0ELb0ELb1ELb1ELb1EEEvNS_8GemmArgsIDF16bEE"
+DOWN_ROWS = "void smx::ffn_gemm_bf16_kernel<10, 3, 8, false, 2, false, true, false, true>(smx::GemmArgs<__bf16>)"
 NORM = "_ZN3smx15add_norm_kernelIDF16bLi2ELb0EEEvPKDv4_jS3_PKfS5_fPS1_liNS_11CombineRowsE"
 NORM_C = "void smx::add_norm_kernel<bool _Accum, int, EL, bool, E>(unsigned int __vector(4) const*)"
 COPY = "__amd_rocclr_copyBuffer"
