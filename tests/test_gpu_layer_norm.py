@@ -3,9 +3,10 @@ block's Add + Normalize ("The Architecture in Place") in one call, against
 the oracle's layer normalisation of x + y_bare (y_bare from the oracle fed
 the GPU's routing), on shapes where the normalization is the fused expert
 kernel's epilogue (bf16, d_model 128 or 256) and on shapes that take the bare
-layer followed by the add_norm kernel (fp32, d_model 192 or 768, capacity
-above 160), with and without drops; the full base workload; and against the
-unfused calls.
+layer followed by the add_norm kernel (fp32; bf16 d_model 192 to 768, with
+ragged tiles, several row tiles per expert and more tiles than workgroups),
+with and without drops; the full base workload; and against the unfused
+calls.
 
 Tolerance (end to end), per element of row t:
     |out - ref| <= 2 rstd_t |gamma| dy_t + 2 u |ref| + 1e-5,
@@ -32,12 +33,20 @@ SMALL = LayerConfig("ln", 1000, 128, 256, 16, 1.0, "bf16")
 CASES = {
     "fused_d128": SMALL,
     "fused_d256_drops": SMALL.with_(d_model=256, d_ff=384, tokens=1500, capacity_factor=0.5),
-    "unfused_d768_ragged": SMALL.with_(d_model=768, d_ff=512, tokens=777, num_experts=8, capacity_factor=1.25),
     "fused_two_tiles": SMALL.with_(d_model=256, d_ff=256, tokens=2000, num_experts=16, capacity_factor=1.25),
+    "unfused_d768_ragged": SMALL.with_(d_model=768, d_ff=512, tokens=777, num_experts=8, capacity_factor=1.25),
+    # Zipf-skewed router bias: drops (capacity 100)
+    "unfused_d512_drops": SMALL.with_(d_model=512, d_ff=256, tokens=1600, num_experts=16, capacity_factor=1.0,
+                                   zipf_s=1.1),
+    "unfused_d384": SMALL.with_(d_model=384, d_ff=256, tokens=1900, num_experts=13, capacity_factor=1.0),
+    # three row tiles per expert (capacity 375)
+    "unfused_d768_row_tiles": SMALL.with_(d_model=768, d_ff=256, tokens=3000, num_experts=8, capacity_factor=1.0),
+    # 512 down-projection tiles: two per workgroup of the persistent grid
+    "unfused_two_tiles_per_workgroup": SMALL.with_(d_model=768, d_ff=256, tokens=25600, num_experts=256,
+                                                capacity_factor=1.0),
     "unfused_fp32": SMALL.with_(dtype="f32", d_model=64, d_ff=192, tokens=531, num_experts=5),
     "unfused_d192": SMALL.with_(d_model=192, d_ff=256, tokens=901, capacity_factor=0.5),
-    "unfused_capacity_above_160": SMALL.with_(d_model=128, d_ff=128, tokens=700, num_experts=2,
-                                              capacity_factor=1.0),
+    "unfused_capacity_above_160": SMALL.with_(d_model=128, d_ff=128, tokens=700, num_experts=2, capacity_factor=1.0),
 }
 
 
