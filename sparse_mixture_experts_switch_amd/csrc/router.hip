@@ -97,24 +97,45 @@ struct TopK {
 // bit.
 __device__ __forceinline__ int64_t p_fixed(float p) { return __double2ll_rn((double)p * 0x1p31); }
 
+// The best (and second best) logit of a lane and its expert.  Every update
+// is a select of values: conditional assignments through the references made
+// the compiler keep the four values of the top-2 epilogue in scratch memory
+// (a dependent chain of scratch accesses per logit).
 template <int kK>
 __device__ __forceinline__ void topk_take(float h, int j, float &b1, int &i1, float &b2, int &i2) {
   // ascending j within one lane: strict comparisons keep the lower index
-  if (h > b1) {
-    if (kK == 2) {
-      b2 = b1;
-      i2 = i1;
-    }
-    b1 = h;
-    i1 = j;
-  } else if (kK == 2 && h > b2) {
-    b2 = h;
-    i2 = j;
+  const bool g1 = h > b1;
+  if (kK == 2) {
+    const bool g2 = h > b2;
+    const float nb2 = g1 ? b1 : (g2 ? h : b2);
+    const int ni2 = g1 ? i1 : (g2 ? j : i2);
+    b2 = nb2;
+    i2 = ni2;
   }
+  b1 = g1 ? h : b1;
+  i1 = g1 ? j : i1;
 }
 
 __device__ __forceinline__ bool topk_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
+}
+
+// Merge another lane's ordered (best, second) into this lane's: the top two
+// of the union (larger logit first, the lower index on equal logits).
+template <int kK>
+__device__ __forceinline__ void topk_merge(float ov, int oi, float ov2, int oi2, float &best, int &bi, float &sec,
+                                           int &si) {
+  const bool theirs = topk_before(ov, oi, best, bi);
+  if (kK == 2) {
+    const bool mine2 = topk_before(best, bi, ov2, oi2);  // theirs first: second is my first or their second
+    const bool osec = topk_before(ov, oi, sec, si);      // mine first: second is their first or my second
+    const float ns = theirs ? (mine2 ? best : ov2) : (osec ? ov : sec);
+    const int nsi = theirs ? (mine2 ? bi : oi2) : (osec ? oi : si);
+    sec = ns;
+    si = nsi;
+  }
+  best = theirs ? ov : best;
+  bi = theirs ? oi : bi;
 }
 
 // With s_cnt set (one route per token) the block's counts and P partial sums
@@ -152,24 +173,9 @@ __device__ __forceinline__ void router_epilogue(const LogitRows<kLds> lg, int nt
     for (int off = 1; off < kLpt; off <<= 1) {
       const float ov = __shfl_xor(best, off, kWave);
       const int oi = __shfl_xor(bi, off, kWave);
-      if (kK == 2) {
-        // top two of the union of two ordered pairs
-        const float ov2 = __shfl_xor(sec, off, kWave);
-        const int oi2 = __shfl_xor(si, off, kWave);
-        if (topk_before(ov, oi, best, bi)) {  // theirs first; second: my first or their second
-          const bool mine = topk_before(best, bi, ov2, oi2);
-          sec = mine ? best : ov2;
-          si = mine ? bi : oi2;
-          best = ov;
-          bi = oi;
-        } else if (topk_before(ov, oi, sec, si)) {  // mine first; second: their first or my second
-          sec = ov;
-          si = oi;
-        }
-      } else if (topk_before(ov, oi, best, bi)) {
-        best = ov;
-        bi = oi;
-      }
+      const float ov2 = kK == 2 ? __shfl_xor(sec, off, kWave) : 0.f;
+      const int oi2 = kK == 2 ? __shfl_xor(si, off, kWave) : 0;
+      topk_merge<kK>(ov, oi, ov2, oi2, best, bi, sec, si);
     }
     float sum = 0.f;
     if (kLds) {
@@ -638,23 +644,7 @@ __device__ __forceinline__ void router_epilogue_lds(float *lg, RouterFwSmem &sm,
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) topk_take<kK>(h[4 * c + i], 32 * c + 4 * q + i, best, bi, sec, si);
-    auto merge = [&](float ov, int oi, float ov2, int oi2) {
-      if (kK == 2) {
-        if (topk_before(ov, oi, best, bi)) {  // theirs first; second: my first or their second
-          const bool mine = topk_before(best, bi, ov2, oi2);
-          sec = mine ? best : ov2;
-          si = mine ? bi : oi2;
-          best = ov;
-          bi = oi;
-        } else if (topk_before(ov, oi, sec, si)) {  // mine first; second: their first or my second
-          sec = ov;
-          si = oi;
-        }
-      } else if (topk_before(ov, oi, best, bi)) {
-        best = ov;
-        bi = oi;
-      }
-    };
+    auto merge = [&](float ov, int oi, float ov2, int oi2) { topk_merge<kK>(ov, oi, ov2, oi2, best, bi, sec, si); };
     merge(dpp8f<0>(best), dpp8<0>(bi), kK == 2 ? dpp8f<0>(sec) : 0.f, kK == 2 ? dpp8<0>(si) : 0);
     merge(dpp8f<1>(best), dpp8<1>(bi), kK == 2 ? dpp8f<1>(sec) : 0.f, kK == 2 ? dpp8<1>(si) : 0);
     merge(dpp8f<2>(best), dpp8<2>(bi), kK == 2 ? dpp8f<2>(sec) : 0.f, kK == 2 ? dpp8<2>(si) : 0);
