@@ -335,22 +335,30 @@ static_assert(kRouterLgBytes <= 2 * kFwBuf, "logit rows fit in the x buffers");
 // keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// 12 MFMAs of one 32-column step: 4 token tiles x 3 planes.
-__device__ __forceinline__ void fw_step_mfma(f32x4 (&acc)[3][kTokTiles], const bf16x8 (&a)[kTokTiles],
-                                             const bf16x8 (&pln)[3]) {
+// The MFMAs of one 32-column step: kTT token tiles x 3 planes.
+template <int kTT>
+__device__ __forceinline__ void fw_step_mfma(f32x4 (&acc)[3][kTT], const bf16x8 (&a)[kTT], const bf16x8 (&pln)[3]) {
 #pragma unroll
   for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
-    for (int tb = 0; tb < kTokTiles; ++tb)
+    for (int tb = 0; tb < kTT; ++tb)
       acc[pl][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], pln[pl], acc[pl][tb], 0, 0, 0);
 }
 
-template <bool kLds>
+// kTT: token tiles per MFMA wave.  With all 8 expert tiles of a chunk live
+// each wave multiplies its 16 experts for all 4 token tiles; with at most 4
+// (N <= 64) or 2 (N <= 32) expert tiles the waves split the block's token
+// tiles instead (2 or 4 waves per expert tile, 2 or 1 token tiles each), so
+// no wave repeats another's products, and the logit columns past the live
+// tiles are set to -inf.
+template <bool kLds, int kTT = kTokTiles>
 __device__ __forceinline__ LogitRows<kLds> router_fwd_contract_bf16(
     const bf16 *__restrict__ x, const u32x4 *__restrict__ wplanes, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int64_t blk, RouterFwSmem &sm) {
   static_assert(kFwStagePer * kFwStageThreads == kRouterTokens * kFwPieces, "staging plan");
   static_assert(kFwMfmaWaves * 16 == kRouterChunk, "16 experts per MFMA wave");
+  static_assert(kTT == kTokTiles || (kLds && (kTT == 2 || kTT == 1)), "token tiles per wave");
+  constexpr int kTileWaves = kFwMfmaWaves * kTT / kTokTiles;  // waves (= expert tiles) per token group
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -418,17 +426,23 @@ __device__ __forceinline__ LogitRows<kLds> router_fwd_contract_bf16(
     if (kLds) {       // clear the rank masks for the epilogue
       for (int i = tid - kFwMfmaWaves * kWave; i < 2 * kRouterChunk; i += kFwStageThreads)
         (&sm.mask[0][0])[i] = 0;
+      if (kTT < kTokTiles) {  // logit columns past the live expert tiles
+        constexpr int kCols = kRouterChunk - kTileWaves * 16;
+        for (int i = tid - kFwMfmaWaves * kWave; i < kRouterTokens * kCols; i += kFwStageThreads)
+          lg.at(i / kCols, kTileWaves * 16 + i % kCols) = -INFINITY;
+      }
     }
   } else {
     // ---- multiply
     const int r16 = lane % 16, kg = lane / 16;
-    f32x4 acc[3][kTokTiles];
+    const int mt = wave % kTileWaves, tb0 = (wave / kTileWaves) * kTT;  // expert tile, first token tile
+    f32x4 acc[3][kTT];
     u32x4 pring[kFwRing][3];
-    // planes of step g of expert chunk ec: tile ec * 8 + w (the last tile
+    // planes of step g of expert chunk ec: tile ec * 8 + mt (the last tile
     // again past the experts), three contiguous 1 KB pieces, 16 bytes a lane
     const int ntile = (N + 15) / 16;
     auto pl_ptr = [&](int ec, int g) -> const u32x4 * {
-      const int m = min(ec * 8 + wave, ntile - 1);
+      const int m = min(ec * 8 + mt, ntile - 1);
       return wplanes + ((int64_t)m * S + g) * 3 * kWave + lane;
     };
     auto pld = [&](int slot, const u32x4 *p) {
@@ -442,13 +456,13 @@ __device__ __forceinline__ LogitRows<kLds> router_fwd_contract_bf16(
     };
     auto write_logits = [&](int ec) {
       // chunk ec's logits (+ bias); in LDS, experts past N get -inf
-      const int j = ec * kRouterChunk + wave * 16 + r16;
+      const int j = ec * kRouterChunk + mt * 16 + r16;
       const float bj = bias && j < N ? bias[j] : 0.f;
 #pragma unroll
-      for (int tb = 0; tb < kTokTiles; ++tb)
+      for (int tb = 0; tb < kTT; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = tb * 16 + kg * 4 + i;
+          const int t = (tb0 + tb) * 16 + kg * 4 + i;
           const float v = acc[0][tb][i] + (acc[1][tb][i] + acc[2][tb][i]) + bj;
           if (kLds)
             lg.at(t, j) = j < N ? v : -INFINITY;
@@ -460,7 +474,7 @@ __device__ __forceinline__ LogitRows<kLds> router_fwd_contract_bf16(
 #pragma unroll
       for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
-        for (int tb = 0; tb < kTokTiles; ++tb) acc[pl][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tb = 0; tb < kTT; ++tb) acc[pl][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
     if (full) {
       // chunk q: expert chunk q / nkc, contraction chunk (q mod nkc + rot)
@@ -488,11 +502,11 @@ __device__ __forceinline__ LogitRows<kLds> router_fwd_contract_bf16(
           planes(s % kFwRing, pln);
           pld(s % kFwRing, s + kFwRing < 8 ? cur + (s + kFwRing) * kStep : nxt + (s + kFwRing - 8) * kStep);
           __builtin_amdgcn_sched_barrier(0);  // the refill issues here, 4 steps before its use
-          bf16x8 a[kTokTiles];
+          bf16x8 a[kTT];
 #pragma unroll
-          for (int tb = 0; tb < kTokTiles; ++tb)
-            a[tb] = as_bf16x8(*(const u32x4 *)(xb + (s * 4 * kFwPitch + tb * 16) * 16));
-          fw_step_mfma(acc, a, pln);
+          for (int tb = 0; tb < kTT; ++tb)
+            a[tb] = as_bf16x8(*(const u32x4 *)(xb + (s * 4 * kFwPitch + (tb0 + tb) * 16) * 16));
+          fw_step_mfma<kTT>(acc, a, pln);
         }
         cur = nxt;
         if (++kcw == nkc) {
@@ -533,10 +547,10 @@ __device__ __forceinline__ LogitRows<kLds> router_fwd_contract_bf16(
             planes(r, pln);
             fetch_next(r);
             const char *xb = sm.x + ((q - 1) & 1) * kFwBuf + (((g & 7) * 4 + kg) * kFwPitch + r16) * 16;
-            bf16x8 a[kTokTiles];
+            bf16x8 a[kTT];
 #pragma unroll
-            for (int tb = 0; tb < kTokTiles; ++tb) a[tb] = as_bf16x8(*(const u32x4 *)(xb + tb * 16 * 16));
-            fw_step_mfma(acc, a, pln);
+            for (int tb = 0; tb < kTT; ++tb) a[tb] = as_bf16x8(*(const u32x4 *)(xb + (tb0 + tb) * 16 * 16));
+            fw_step_mfma<kTT>(acc, a, pln);
             if (g == S - 1 && !kLds) write_logits(ec);
             if (++g == S) {
               g = 0;
@@ -710,7 +724,7 @@ __device__ __forceinline__ void router_epilogue_lds(float *lg, RouterFwSmem &sm,
   }
 }
 
-template <bool kLds, int kK>
+template <bool kLds, int kK, int kTT = kTokTiles>
 __global__ __launch_bounds__(kFwThreads) void router_fwd_bf16_kernel(
     const bf16 *__restrict__ x, const u32x4 *__restrict__ wplanes, const float *__restrict__ bias,
     int64_t T, int d, int N, float *__restrict__ logits_g, int32_t *__restrict__ expert_idx,
@@ -718,7 +732,7 @@ __global__ __launch_bounds__(kFwThreads) void router_fwd_bf16_kernel(
     float *__restrict__ ppart) {
   __shared__ RouterFwSmem sm;
   const int64_t blk = blockIdx.x;
-  const LogitRows<kLds> lg = router_fwd_contract_bf16<kLds>(x, wplanes, bias, T, d, N, logits_g, blk, sm);
+  const LogitRows<kLds> lg = router_fwd_contract_bf16<kLds, kTT>(x, wplanes, bias, T, d, N, logits_g, blk, sm);
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
   if (kLds)
@@ -1139,7 +1153,12 @@ hipError_t run_router(const RouteArgs &a, hipStream_t st) {
       hipError_t e = launch_router_planes(a.w_r, a.N, a.d, a.wplanes, st);
       if (e != hipSuccess) return e;
     }
-    auto kern = lds ? router_fwd_bf16_kernel<true, kK> : router_fwd_bf16_kernel<false, kK>;
+    // at most 2 or 4 live expert tiles: the waves split the token tiles
+    const int ntile = (a.N + 15) / 16;
+    auto kern = !lds       ? router_fwd_bf16_kernel<false, kK>
+                : ntile <= 2 ? router_fwd_bf16_kernel<true, kK, 1>
+                : ntile <= 4 ? router_fwd_bf16_kernel<true, kK, 2>
+                             : router_fwd_bf16_kernel<true, kK>;
     kern<<<grid, dim3(kFwThreads), 0, st>>>((const bf16 *)a.x, (const u32x4 *)a.wplanes, a.bias, a.T, a.d, a.N,
                                             a.logits, a.expert_idx, a.gate, a.rank, a.bcount, a.ppart);
   } else {

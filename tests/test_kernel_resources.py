@@ -8,19 +8,24 @@ four running values there and took 31 us instead of 22."""
 
 import glob
 import os
+import re
 
 import pytest
 
 from sparse_mixture_experts_switch_amd import build as B
 
-# router for N > 128 (logits in a [T][N] buffer): forward top-1 / top-2, the
-# backward's recompute, the single-pass routing
-ALLOWED = {
-    "_ZN3smx22router_fwd_bf16_kernelILb0ELi1EEEvPKDF16bPKDv4_jPKfliiPfPiS8_S9_S9_S8_",
-    "_ZN3smx22router_fwd_bf16_kernelILb0ELi2EEEvPKDF16bPKDv4_jPKfliiPfPiS8_S9_S9_S8_",
-    "_ZN3smx22router_bwd_bf16_kernelILb0EEEvNS_13RouterBwdArgsE",
-    "_ZN3smx23route_fused_bf16_kernelILb0EEEvNS_14FusedRouteArgsE",
-}
+# router for N > 128 (logits in a [T][N] buffer, template argument kLds =
+# false): forward top-1 / top-2, the backward's recompute, the single-pass
+# routing
+ALLOWED = (
+    re.compile(r"^_ZN3smx22router_fwd_bf16_kernelILb0ELi[12]E"),
+    re.compile(r"^_ZN3smx22router_bwd_bf16_kernelILb0EE"),
+    re.compile(r"^_ZN3smx23route_fused_bf16_kernelILb0EE"),
+)
+
+
+def allowed(name: str) -> bool:
+    return any(p.match(name) for p in ALLOWED)
 
 
 @pytest.fixture(scope="module")
@@ -44,11 +49,12 @@ def test_every_source_reports(resources):
 
 def test_no_scratch(resources):
     bad = {k: v.get("ScratchSize [bytes/lane]") for k, v in resources.items()
-           if k not in ALLOWED and (v.get("ScratchSize [bytes/lane]", 0) != 0 or v.get("Dynamic Stack") == "True")}
+           if not allowed(k) and (v.get("ScratchSize [bytes/lane]", 0) != 0 or v.get("Dynamic Stack") == "True")}
     assert not bad, f"kernels using scratch memory: {bad}"
 
 
 def test_allowed_spills_stay_small(resources):
-    for k in ALLOWED:
-        assert k in resources, k
+    names = [k for k in resources if allowed(k)]
+    assert len(names) == 4, names
+    for k in names:
         assert resources[k]["ScratchSize [bytes/lane]"] <= 128, (k, resources[k])
