@@ -66,6 +66,13 @@ EDGE = {
     "fp32_many_experts": SMALL.with_(dtype="f32", tokens=400, num_experts=300, d_model=128, d_ff=128,
                                      capacity_factor=3.0),
     "zipf_bias": SMALL.with_(zipf_s=1.1, tokens=2048, num_experts=32),
+    # at most 4 live expert tiles: the router's waves split the token tiles
+    # (2 per wave); d_model a multiple of 256 (whole chunks) or not
+    "router_33_experts": SMALL.with_(num_experts=33, tokens=999, d_model=256),
+    "router_48_experts_d320": SMALL.with_(num_experts=48, tokens=1111, d_model=320, capacity_factor=1.25),
+    "router_64_experts_d512": SMALL.with_(num_experts=64, tokens=700, d_model=512, d_ff=128),
+    # at most 2 live expert tiles (1 token tile per wave), d_model 768
+    "router_20_experts_d768": SMALL.with_(num_experts=20, tokens=640, d_model=768, d_ff=128),
     # block count x experts large enough for the two-launch assignment (scan, then apply)
     "scan_path_2048_experts": SMALL.with_(tokens=10000, num_experts=2048, d_model=64, d_ff=64,
                                           capacity_factor=2.0),

@@ -90,6 +90,8 @@ CASES = {
     "fp32_many_experts": SMALL.with_(dtype="f32", tokens=400, num_experts=300, d_model=128, d_ff=128,
                                      capacity_factor=3.0),
     "zipf_bias": SMALL.with_(zipf_s=1.1, tokens=2048, num_experts=32),
+    # the router's waves split the token tiles (at most 4 live expert tiles)
+    "router_40_experts_d320": SMALL.with_(num_experts=40, tokens=901, d_model=320),
     "scan_path_2048_experts": SMALL.with_(tokens=10000, num_experts=2048, d_model=64, d_ff=64,
                                           capacity_factor=2.0),
 }
