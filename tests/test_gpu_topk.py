@@ -164,3 +164,51 @@ def test_top2_empty_batch():
     smx.topk_layer_forward(inp["x"], inp["w_router"], None, inp["w_in"], inp["w_out"], 0, 2, out=out)
     torch.cuda.synchronize()
     assert out["expert_count"].sum().item() == 0 and out["aux_loss"].item() == 0.0
+
+
+@pytest.mark.parametrize("dtype,num_experts", [("bf16", 16), ("bf16", 128), ("f32", 16)])
+def test_exact_ties_lower_index_first(dtype, num_experts):
+    """Router rows 5, 9 and 12 copy row 2, so those experts' logits are
+    exactly equal for every token (the same products in the same order on
+    either router path).  Among equal logits the lower expert index comes
+    first ("Switch Routing": the top-k set; the tie rule is the oracle's
+    stable order), for k = 1 and 2: on every token whose k + 1 largest logits
+    are exactly equal or at least NEAR_TIE apart the choice must match the
+    oracle's exactly, and at least 5% of the tokens must have an exact tie
+    inside their chosen set or at its edge (the tied experts share a bias
+    that puts them first on most tokens).  With both routes in the tied group
+    the two gates are equal."""
+    cfg = SMALL.with_(name=f"exact_ties_{dtype}_{num_experts}", dtype=dtype, num_experts=num_experts, tokens=1000,
+                      d_model=128 if dtype == "bf16" else 64)
+    inp = make_inputs(cfg, device=DEV)
+    dups = (5, 9, 12)
+    wr = inp["w_router"].clone()
+    for r in dups:
+        wr[r] = wr[2]
+    # the same bias lifts the tied group above the others on most tokens
+    bias = torch.zeros(num_experts, dtype=torch.float32)
+    bias[[2, *dups]] = 0.5
+    bias = bias.to(DEV)
+    h = so.router_logits(f64(inp["x"]), f64(wr), f64(bias))
+    for r in dups:
+        h[:, r] = h[:, 2]  # exactly equal, as the arithmetic on identical rows makes them
+    for k in (1, 2):
+        C = smx.capacity(k * cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+        o = smx.topk_layer_forward(inp["x"], wr, bias, inp["w_in"], inp["w_out"], C, k)
+        torch.cuda.synchronize()
+        e = o["expert_idx"].cpu().numpy().astype(np.int64)
+        gate = o["gate"].cpu().numpy()
+        order = np.argsort(-h, axis=1, kind="stable")
+        want = order[:, :k].T
+        top = np.take_along_axis(h, order[:, :k + 1], axis=1)
+        gaps = top[:, :-1] - top[:, 1:]
+        strict = np.all((gaps == 0) | (gaps >= NEAR_TIE), axis=1)
+        tied = strict & np.any(gaps == 0, axis=1)
+        say(f"  k={k}: {int(strict.sum())} strict tokens, {int(tied.sum())} with an exact tie")
+        assert tied.sum() >= 0.05 * cfg.tokens, "too few exact ties for the test to mean anything"
+        bad = np.nonzero((e[:, strict] != want[:, strict]).any(axis=0))[0]
+        assert len(bad) == 0, f"k={k}: choice differs on tokens {np.nonzero(strict)[0][bad[:5]]}"
+        if k == 2:
+            both = strict & np.isin(want[0], (2,) + dups) & np.isin(want[1], (2,) + dups)
+            assert both.any()
+            assert np.array_equal(gate[0][both], gate[1][both]), "tied routes' gates differ"
