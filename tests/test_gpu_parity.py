@@ -137,6 +137,41 @@ def test_deterministic_across_runs_and_streams():
             assert torch.equal(o[k], ref[k]), f"run {i}: {k} differs"
 
 
+@pytest.mark.parametrize("name,tiled,k", [("fused_d128", False, 1), ("d768_two_products", False, 1),
+                                          ("d768_two_products", True, 1), ("fp32", False, 1),
+                                          ("d768_two_products", True, 2)])
+def test_doubling_w_out_doubles_y(name, tiled, k):
+    """The combine equation ("Switch Routing": y = p_e(x) E_e(x)) is linear
+    in W_out and a factor of two is exact in bf16 and fp32 (no overflow or
+    underflow at these scales): with 2 W_out every output element of the
+    bare layer is exactly twice the element with W_out, on every path (the
+    fused expert kernel, the two grouped products, tiled weights, fp32, the
+    sum of two routes), and the routing does not move.  Needs no oracle."""
+    base = {"fused_d128": SMALL.with_(tokens=1200),
+            "d768_two_products": SMALL.with_(d_model=768, d_ff=512, tokens=900, num_experts=8),
+            "fp32": SMALL.with_(dtype="f32", d_model=64, d_ff=192, tokens=531, num_experts=5)}[name]
+    cfg = base.with_(name=f"double_w_out_{name}")
+    inp = make_inputs(cfg, device=DEV)
+    C = smx.capacity(k * cfg.tokens, cfg.num_experts, cfg.capacity_factor)
+    w_r, w_in, w_out = inp["w_router"], inp["w_in"], inp["w_out"]
+    w_out2 = w_out * 2
+    if tiled:
+        w_r, w_in, w_out, w_out2 = (smx.tile_router(w_r), smx.tile_weights(w_in), smx.tile_weights(w_out),
+                                    smx.tile_weights(w_out2))
+    outs = []
+    for wo in (w_out, w_out2):
+        if k == 1:
+            outs.append(smx.layer_forward(inp["x"], w_r, None, w_in, wo, C, tiled=tiled))
+        else:
+            outs.append(smx.topk_layer_forward(inp["x"], w_r, None, w_in, wo, C, k, tiled=tiled))
+    torch.cuda.synchronize()
+    a, b = outs
+    for key in ("expert_idx", "gate", "slot", "dropped", "expert_count", "aux_loss"):
+        assert torch.equal(a[key], b[key]), f"{key} moved with W_out"
+    assert a["y"].abs().max().item() > 0
+    assert torch.equal(b["y"], a["y"] * 2), f"{cfg.name}: 2 W_out does not give exactly 2 y"
+
+
 # -------------------------------------------------------- stage-wise calls --
 def test_stages_match_layer_and_oracle():
     cfg = SMALL.with_(name="stages", tokens=1500, capacity_factor=0.75)
