@@ -442,41 +442,55 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_f32_kernel(const GemmArg
   }
   const float *Aexp = p.A + (int64_t)e * p.C * K;
   const float *Bexp = p.B + (int64_t)e * Nout * K;
-  float ra[kLd], rb[kLd];
-  auto load = [&](int k0) {  // K is a multiple of 64: every slice is whole
+  // slices s, s + 1, s + 2 in flight in a register ring (slot s mod 3; the
+  // loop is unrolled by the ring depth so that every slot index is a
+  // constant): small layers have short contractions, and one slice of
+  // products does not cover a global-load round trip
+  constexpr int kRing = 3;
+  float ra[kRing][kLd], rb[kRing][kLd];
+  auto load = [&](int slot, int k0) {  // K is a multiple of 64: every slice is whole
 #pragma unroll
     for (int q = 0; q < kLd; ++q) {
       const int i = tid + q * kFfnThreads;
       const int r = i / kKs, k = i % kKs;
       const int m = m0 + r, n = n0 + r;
-      ra[q] = m < M ? (kGather ? p.A[(int64_t)s_tok[r] * K + k0 + k] : Aexp[(int64_t)m * K + k0 + k]) : 0.f;
-      rb[q] = n < Nout ? Bexp[(int64_t)n * K + k0 + k] : 0.f;
+      ra[slot][q] = m < M ? (kGather ? p.A[(int64_t)s_tok[r] * K + k0 + k] : Aexp[(int64_t)m * K + k0 + k]) : 0.f;
+      rb[slot][q] = n < Nout ? Bexp[(int64_t)n * K + k0 + k] : 0.f;
     }
   };
   float acc[4][4] = {};
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += kKs) {
-    __syncthreads();  // the previous slice's products are done with the LDS tiles
+  const int ns = K / kKs;
 #pragma unroll
-    for (int q = 0; q < kLd; ++q) {
-      const int i = tid + q * kFfnThreads;
-      sA[i % kKs][i / kKs] = ra[q];
-      sB[i % kKs][i / kKs] = rb[q];
-    }
-    __syncthreads();
-    if (k0 + kKs < K) load(k0 + kKs);
+  for (int j = 0; j < kRing; ++j)
+    if (j < ns) load(j, j * kKs);
+  for (int s0 = 0; s0 < ns; s0 += kRing) {
 #pragma unroll
-    for (int k = 0; k < kKs; ++k) {
-      float a[4], b[4];
+    for (int j = 0; j < kRing; ++j) {
+      const int sl = s0 + j;
+      if (sl < ns) {
+        __syncthreads();  // the previous slice's products are done with the LDS tiles
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = sA[k][ty * 4 + i];
-        b[i] = sB[k][tx * 4 + i];
+        for (int q = 0; q < kLd; ++q) {
+          const int i = tid + q * kFfnThreads;
+          sA[i % kKs][i / kKs] = ra[j][q];
+          sB[i % kKs][i / kKs] = rb[j][q];
+        }
+        __syncthreads();
+        if (sl + kRing < ns) load(j, (sl + kRing) * kKs);
+#pragma unroll
+        for (int k = 0; k < kKs; ++k) {
+          float a[4], b[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a[i] = sA[k][ty * 4 + i];
+            b[i] = sB[k][tx * 4 + i];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[i][jj] = __builtin_fmaf(a[i], b[jj], acc[i][jj]);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
     }
   }
 #pragma unroll

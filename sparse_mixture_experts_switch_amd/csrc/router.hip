@@ -744,15 +744,16 @@ __global__ __launch_bounds__(kFwThreads) void router_fwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// fp32 activations: fp32 FMA.  The block's x rows are staged in LDS in
-// k-slices; each thread owns (token, expert) pairs of the current chunk.
+// fp32 activations: fp32 FMA.  The block's x rows and the chunk's W_r rows are
+// staged in LDS in k-slices; each thread owns (token, expert) pairs of the
+// current chunk.
 // ---------------------------------------------------------------------------
 // fp32 logits (+ bias) of block `blk` into `lg` (LDS rows s_lg when
 // N <= kRouterChunk, else the global scratch); ends with a barrier.
 template <bool kLds>
 __device__ __forceinline__ LogitRows<kLds> router_contract_f32(
     const float *__restrict__ x, const float *__restrict__ w_r, const float *__restrict__ bias, int64_t T, int d,
-    int N, float *__restrict__ logits_g, int64_t blk, float *s_lg, float (*s_x)[65]) {
+    int N, float *__restrict__ logits_g, int64_t blk, float *s_lg, float (*s_x)[65], float (*s_w)[65]) {
   constexpr int kKc = 64;  // contraction columns per LDS slice
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
@@ -777,22 +778,25 @@ __device__ __forceinline__ LogitRows<kLds> router_contract_f32(
     for (int q = 0; q < kPer; ++q) acc[q] = 0.f;
     for (int k0 = 0; k0 < d; k0 += kKc) {
       __syncthreads();
+      // the slice's x rows and W_r rows (d is a multiple of 64: whole
+      // slices), both with coalesced loads issued together
       for (int i = tid; i < kRouterTokens * kKc; i += kRouterThreads) {
         int t = i / kKc, k = i % kKc;
         s_x[t][k] = (t < nt && k0 + k < d) ? x[(t0 + t) * d + k0 + k] : 0.f;
+      }
+      for (int i = tid; i < nc * kKc; i += kRouterThreads) {
+        const int jj = i / kKc, k = i % kKc;
+        s_w[jj][k] = w_r[(int64_t)(c0 + jj) * d + k0 + k];
       }
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int pair = tid + q * kRouterThreads;
         if (pair < npairs) {
-          const int t = pair / nc, j = c0 + pair % nc;
-          const float *w = w_r + (int64_t)j * d + k0;
+          const int t = pair / nc, jj = pair % nc;
           float a = acc[q];
-          // d is a multiple of 64: whole slices, so the W_r loads go out 16 at
-          // a time instead of one round trip per multiply-add
 #pragma unroll 16
-          for (int k = 0; k < kKc; ++k) a = __builtin_fmaf(s_x[t][k], w[k], a);
+          for (int k = 0; k < kKc; ++k) a = __builtin_fmaf(s_x[t][k], s_w[jj][k], a);
           acc[q] = a;
         }
       }
@@ -819,12 +823,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
     float *__restrict__ ppart) {
   __shared__ float s_lg[kLds ? kRouterTokens * (kRouterChunk + 1) : 1];
   __shared__ float s_x[kRouterTokens][65];
+  __shared__ float s_w[kRouterChunk][65];  // W_r rows of the current slice
   __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
   __shared__ int s_e[kRouterTokens], s_e2[kRouterTokens];
   const int64_t blk = blockIdx.x;
   const int64_t t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
-  const LogitRows<kLds> lg = router_contract_f32<kLds>(x, w_r, bias, T, d, N, logits_g, blk, s_lg, s_x);
+  const LogitRows<kLds> lg = router_contract_f32<kLds>(x, w_r, bias, T, d, N, logits_g, blk, s_lg, s_x, s_w);
   router_epilogue<kRouterThreads, kLds, kK>(lg, nt, N, t0, blk, TopK{T, router_blocks(T)}, expert_idx, gate,
                                             slot_rank, bcount, ppart, s_max, s_inv, s_e, s_e2);
 }
@@ -1002,10 +1007,11 @@ template <bool kLds>
 __global__ __launch_bounds__(kRouterThreads) void router_bwd_f32_kernel(const RouterBwdArgs a) {
   __shared__ float s_lg[kLds ? kRouterTokens * (kRouterChunk + 1) : 1];
   __shared__ float s_x[kRouterTokens][65];
+  __shared__ float s_w[kRouterChunk][65];  // W_r rows of the current slice
   const int64_t blk = blockIdx.x, t0 = blk * kRouterTokens;
   const int nt = (int)min<int64_t>(kRouterTokens, a.T - t0);
   const LogitRows<kLds> lg =
-      router_contract_f32<kLds>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, s_lg, s_x);
+      router_contract_f32<kLds>((const float *)a.x, a.w_r, a.bias, a.T, a.d, a.N, a.logits, blk, s_lg, s_x, s_w);
   __shared__ __attribute__((aligned(16))) float s_extra[bwd_lds_floats<kRouterThreads>()];
   router_bwd_epilogue<float, kRouterThreads, kLds, true>(lg, nt, t0, a, s_extra);
 }
@@ -1443,6 +1449,7 @@ __global__ __launch_bounds__(kRouterThreads) void route_fused_f32_kernel(const F
   constexpr int kX = kRouterTokens * 65 * 4;
   constexpr int kTail = fused_tail_bytes(kFusedMaxExperts);
   __shared__ __attribute__((aligned(16))) char s_buf[kLg + (kX > kTail ? kX : kTail)];
+  __shared__ float s_w[kRouterChunk][65];  // W_r rows of the current slice
   __shared__ float s_max[kRouterTokens], s_inv[kRouterTokens];
   __shared__ int s_e[kRouterTokens], s_e2[kRouterTokens];
   __shared__ int s_blk;
@@ -1454,7 +1461,7 @@ __global__ __launch_bounds__(kRouterThreads) void route_fused_f32_kernel(const F
   const int nt = (int)min<int64_t>(kRouterTokens, T - t0);
   const LogitRows<kLds> lg = router_contract_f32<kLds>((const float *)a.r.x, a.r.w_r, a.r.bias, T, a.r.d, N,
                                                        a.r.logits, blk, (float *)s_buf,
-                                                       (float(*)[65])(s_buf + kLg));
+                                                       (float(*)[65])(s_buf + kLg), s_w);
   const TailLds L = tail_lds(s_buf + kLg, N);  // the x slices are dead after the contraction
   router_epilogue<kRouterThreads, kLds, 1>(lg, nt, N, t0, blk, TopK{T, nb}, a.r.expert_idx, a.r.gate, a.r.slot,
                                            a.r.bcount, a.r.ppart, s_max, s_inv, s_e, s_e2, L.c, L.p);
