@@ -411,9 +411,10 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_gemm_bf16_kernel(const GemmArg
 
 // fp32 grouped GEMM on the vector ALUs: 64 x 64 output tiles, 32-deep
 // contraction slices staged in LDS, 4 x 4 outputs per thread.  The next
-// slice is loaded into registers while the current one is multiplied, so a
-// tile pays one global-load round trip, not one per slice (small fp32 layers
-// have few tiles, and each tile's slices ran in sequence).
+// three slices are in registers while the current one is multiplied, so a
+// tile pays about one global-load round trip per three slices, not one per
+// slice (small fp32 layers have few tiles, and each tile's slices run in
+// sequence).
 template <bool kGather, int kEpi>
 __global__ __launch_bounds__(kFfnThreads) void ffn_gemm_f32_kernel(const GemmArgs<float> p) {
   constexpr int kT = 64, kKs = 32;

@@ -280,7 +280,8 @@ constexpr int kRouterLgBytes = kRouterTokens * kLgStride * 4;
 //    that it arrives first, then each thread keeps the next two chunks in
 //    registers);
 //  - waves 0..7 multiply: wave w owns experts [c0 + 16 w, c0 + 16 w + 16) of
-//    a 128-expert chunk for all 64 tokens.  Its W_r operands come straight
+//    a 128-expert chunk for all 64 tokens (with at most 4 or 2 live expert
+//    tiles, the waves share a tile and split the 64 tokens instead).  Its W_r operands come straight
 //    from global memory (the 393 KB of W_r stay in every XCD's L2) into
 //    registers, 8 fp32 per lane per 32-column step, four steps ahead, and
 //    are split there into the three bf16 planes; the x operands are 16-byte
