@@ -281,20 +281,20 @@ constexpr int kRouterLgBytes = kRouterTokens * kLgStride * 4;
 //    registers);
 //  - waves 0..7 multiply: wave w owns experts [c0 + 16 w, c0 + 16 w + 16) of
 //    a 128-expert chunk for all 64 tokens (with at most 4 or 2 live expert
-//    tiles, the waves share a tile and split the 64 tokens instead).  Its W_r operands come straight
-//    from global memory (the 393 KB of W_r stay in every XCD's L2) into
-//    registers, 8 fp32 per lane per 32-column step, four steps ahead, and
-//    are split there into the three bf16 planes; the x operands are 16-byte
-//    LDS reads.  Each plane has its own fp32 accumulator (the small planes
-//    accumulate apart from the large one) and the logit is
-//    hi + (mid + lo) at the end.
+//    tiles, the waves share a tile and split the 64 tokens instead).  Its
+//    operands of W_r's three exact bf16 planes (hi, mid, lo; fragment order,
+//    see router_wplanes_kernel) come straight from global memory (590 KB,
+//    held in every XCD's L2) into registers, three 1 KB pieces per wave and
+//    32-column step, four steps ahead; the x operands are 16-byte LDS reads.
+//    Each plane has its own fp32 accumulator (the small planes accumulate
+//    apart from the large one) and the logit is hi + (mid + lo) at the end.
 // x in LDS: piece-major ([32 pieces][64 tokens + 1] slots of 16 bytes), so
 // the 16 lanes of an MFMA row group read 256 contiguous bytes and the
 // staging stores of consecutive pieces fall on different banks.  One barrier
 // per chunk.  When d_model is a multiple of 256 every chunk is full: its 8
 // steps are unrolled without branches (the W_r operands 4 steps ahead come
 // from this chunk or, by fixed offsets, the next), so the compiler overlaps
-// one step's split and loads with the previous step's MFMAs; blocks on one
+// one step's loads with the previous step's MFMAs; blocks on one
 // XCD then also start their walk over the contraction at different chunks.
 // Other widths take a general loop.
 // MFMA operand layout (16x16x32 bf16): lane l supplies row (l % 16) and the 8
